@@ -1,0 +1,299 @@
+/*
+ * jbo.c -- fp64 sequential CPU oracle for the JetBlock token mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU library; it is built by gcc from this
+ * file alone.
+ *
+ * What it computes (one token at a time, every quantity in double):
+ *
+ *   Jet-Nemotron paper (Chinese translation, csdn page), section 2.4 "new
+ *   attention block design": a kernel generator takes the same input as the
+ *   Q/K/V projections, applies a reducing Linear layer, SiLU, and a final
+ *   Linear layer whose outputs are convolution-kernel weights; the dynamic
+ *   causal kernels are applied to the value tokens only; the static
+ *   convolutions on Q and K are removed; Gated DeltaNet does the time mixing.
+ *   The xugj520 blog page, section 2.2, lists kernel size 4 and generator
+ *   hidden width 32.
+ *
+ *   The Gated DeltaNet step with state S (dv x dk):
+ *       S_t = a_t * S_{t-1} (I - b_t k_t k_t^T) + b_t v'_t k_t^T,   o_t = S_t q_t
+ *   over L2-normalised q and k, where v'_t is the convolved value.
+ *   This oracle stores M = S^T (dk x dv, dv contiguous).
+ *
+ * Readings of points the pages leave open (each listed in the design notes):
+ *   - taps for token t come from x_t; tap j (0..3) multiplies v_{t-3+j}
+ *     (j = 3 is the current token); rows before the start come from the
+ *     conv cache (raw v rows, oldest first) or are zero;
+ *   - one tap set per head (4 taps per head, shared by all dv channels);
+ *   - L2 norm: x * (sum x^2 + eps)^(-1/2), eps = 1e-6;
+ *   - no 1/sqrt(dk) scaling of q; o uses the updated state S_t;
+ *   - generator biases are optional (NULL means zero).
+ *
+ * Inputs arrive as float arrays holding the exact values handed to the GPU
+ * (bf16 values are exactly representable in float); they are widened to
+ * double on use.
+ *
+ * Layouts (row-major, last index contiguous):
+ *   x [B][T][D]; q,k [B][T][H][dk]; v [B][T][H][dv]; alpha,beta [B][T][H]
+ *   W1 [G][D]; b1 [G]; W2 [H*K][G] (row h*K+j is tap j of head h); b2 [H*K]
+ *   S0, S_final [B][H][dk][dv]; conv_in, conv_out [B][K-1][H][dv]
+ *   o [B][T][H][dv]; taps [B][T][H][K]
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define JBO_EPS 1e-6
+
+/* ---------------------------------------------------------------- generator */
+
+/* taps for one token: hidden = SiLU(W1 x + b1), taps = W2 hidden + b2. */
+static void gen_one(int D, int G, int HK, const float* x, const float* W1,
+                    const float* b1, const float* W2, const float* b2,
+                    double* hidden, double* taps) {
+  for (int g = 0; g < G; ++g) {
+    double acc = b1 ? (double)b1[g] : 0.0;
+    const float* w = W1 + (int64_t)g * D;
+    for (int d = 0; d < D; ++d) acc += (double)w[d] * (double)x[d];
+    hidden[g] = acc / (1.0 + exp(-acc)); /* SiLU(h) = h * sigmoid(h) */
+  }
+  for (int r = 0; r < HK; ++r) {
+    double acc = b2 ? (double)b2[r] : 0.0;
+    const float* w = W2 + (int64_t)r * G;
+    for (int g = 0; g < G; ++g) acc += (double)w[g] * hidden[g];
+    taps[r] = acc;
+  }
+}
+
+typedef struct {
+  int64_t n0, n1;
+  int D, G, HK;
+  const float *x, *W1, *b1, *W2, *b2;
+  double* taps;
+} gen_job;
+
+static void* gen_worker(void* p) {
+  gen_job* j = (gen_job*)p;
+  double* hidden = (double*)malloc(sizeof(double) * (size_t)j->G);
+  for (int64_t n = j->n0; n < j->n1; ++n)
+    gen_one(j->D, j->G, j->HK, j->x + n * j->D, j->W1, j->b1, j->W2, j->b2,
+            hidden, j->taps + n * j->HK);
+  free(hidden);
+  return NULL;
+}
+
+/* Kernel generator over n_tokens rows of x.  taps: [n_tokens][H*K]. */
+int jbo_gen_taps(int64_t n_tokens, int D, int G, int H, int K, const float* x,
+                 const float* W1, const float* b1, const float* W2,
+                 const float* b2, double* taps, int nthreads) {
+  if (n_tokens < 0 || D <= 0 || G <= 0 || H <= 0 || K <= 0) return 1;
+  if (!x || !W1 || !W2 || !taps) return 1;
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > n_tokens) nthreads = n_tokens > 0 ? (int)n_tokens : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  gen_job* jobs = (gen_job*)malloc(sizeof(gen_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (gen_job){n_tokens * i / nthreads, n_tokens * (i + 1) / nthreads,
+                        D, G, H * K, x, W1, b1, W2, b2, taps};
+    if (nthreads == 1) gen_worker(&jobs[i]);
+    else pthread_create(&th[i], NULL, gen_worker, &jobs[i]);
+  }
+  if (nthreads > 1)
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
+
+/* --------------------------------------------------------------- L2 norm */
+
+/* out = x * (sum x^2 + eps)^(-1/2), row by row. */
+int jbo_l2norm(int64_t rows, int d, const float* x, double* out) {
+  if (rows < 0 || d <= 0 || !x || !out) return 1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) ss += (double)x[r * d + i] * (double)x[r * d + i];
+    double s = 1.0 / sqrt(ss + JBO_EPS);
+    for (int i = 0; i < d; ++i) out[r * d + i] = (double)x[r * d + i] * s;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------ dynamic causal conv */
+
+/* Raw value row for token t (may be negative: then it comes from the cache). */
+static const float* v_row(int t, int b, int h, int T, int H, int dv, int K,
+                          const float* v, const float* conv_in) {
+  if (t >= 0) return v + (((int64_t)b * T + t) * H + h) * dv;
+  if (!conv_in) return NULL;                /* zero padding */
+  int slot = (K - 1) + t;                   /* t = -1 -> newest cache row */
+  return conv_in + (((int64_t)b * (K - 1) + slot) * H + h) * dv;
+}
+
+/* v'[t][c] = sum_j taps[t][h][j] * v_{t-(K-1)+j}[c] for one (b, t, h). */
+static void conv_one(int b, int t, int h, int T, int H, int dv, int K,
+                     const double* taps_bth, const float* v,
+                     const float* conv_in, double* out) {
+  for (int c = 0; c < dv; ++c) out[c] = 0.0;
+  for (int j = 0; j < K; ++j) {
+    const float* row = v_row(t - (K - 1) + j, b, h, T, H, dv, K, v, conv_in);
+    if (!row) continue;
+    for (int c = 0; c < dv; ++c) out[c] += taps_bth[j] * (double)row[c];
+  }
+}
+
+/* Whole convolution: vconv [B][T][H][dv] from taps [B][T][H][K]. */
+int jbo_conv(int B, int T, int H, int dv, int K, const double* taps,
+             const float* v, const float* conv_in, double* vconv) {
+  if (B < 0 || T < 0 || H <= 0 || dv <= 0 || K <= 0) return 1;
+  if (!taps || !v || !vconv) return 1;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int h = 0; h < H; ++h) {
+        int64_t bth = ((int64_t)b * T + t) * H + h;
+        conv_one(b, t, h, T, H, dv, K, taps + bth * K, v, conv_in,
+                 vconv + bth * dv);
+      }
+  return 0;
+}
+
+/* ------------------------------------------------- gated delta-rule block */
+
+typedef struct {
+  int B, T, H, dk, dv, K;
+  const float *q, *k, *v, *alpha, *beta, *S0, *conv_in;
+  const double* taps;
+  double *o, *S_final;
+  int unit0, unit1; /* (b, h) units [unit0, unit1) */
+} rec_job;
+
+static void* rec_worker(void* p) {
+  rec_job* J = (rec_job*)p;
+  const int T = J->T, H = J->H, dk = J->dk, dv = J->dv, K = J->K;
+  double* M = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+  double* qh = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* vc = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* kM = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (int u = J->unit0; u < J->unit1; ++u) {
+    const int b = u / H, h = u % H;
+    const int64_t sbase = ((int64_t)b * H + h) * dk * dv;
+    for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+      M[i] = J->S0 ? (double)J->S0[sbase + i] : 0.0;
+    for (int t = 0; t < T; ++t) {
+      const int64_t bth = ((int64_t)b * T + t) * H + h;
+      /* value convolution with the per-token taps */
+      conv_one(b, t, h, T, H, dv, K, J->taps + bth * K, J->v, J->conv_in, vc);
+      /* L2-normalised query and key */
+      double sq = 0.0, sk = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        double a = J->q[bth * dk + i], c = J->k[bth * dk + i];
+        sq += a * a;
+        sk += c * c;
+      }
+      double rq = 1.0 / sqrt(sq + JBO_EPS), rk = 1.0 / sqrt(sk + JBO_EPS);
+      for (int i = 0; i < dk; ++i) {
+        qh[i] = (double)J->q[bth * dk + i] * rq;
+        kh[i] = (double)J->k[bth * dk + i] * rk;
+      }
+      const double a = J->alpha[bth], be = J->beta[bth];
+      /* S_t = a S_{t-1} (I - b k k^T) + b v' k^T, written for M = S^T:
+         M <- a (M - b k (k^T M)) + b k v'^T */
+      for (int c = 0; c < dv; ++c) {
+        double s = 0.0;
+        for (int i = 0; i < dk; ++i) s += kh[i] * M[(int64_t)i * dv + c];
+        kM[c] = s;
+      }
+      for (int i = 0; i < dk; ++i)
+        for (int c = 0; c < dv; ++c) {
+          double* m = &M[(int64_t)i * dv + c];
+          *m = a * (*m - be * kh[i] * kM[c]) + be * kh[i] * vc[c];
+        }
+      /* o_t = S_t q = M^T q */
+      double* ot = J->o + bth * dv;
+      for (int c = 0; c < dv; ++c) {
+        double s = 0.0;
+        for (int i = 0; i < dk; ++i) s += M[(int64_t)i * dv + c] * qh[i];
+        ot[c] = s;
+      }
+    }
+    if (J->S_final)
+      for (int64_t i = 0; i < (int64_t)dk * dv; ++i) J->S_final[sbase + i] = M[i];
+  }
+  free(M); free(qh); free(kh); free(vc); free(kM);
+  return NULL;
+}
+
+/*
+ * Full block over B sequences of T tokens.  taps_out (optional) receives the
+ * generator output [B][T][H][K].  conv_out (optional) receives the last K-1
+ * raw value rows (from v, or from conv_in when T < K-1).  Returns 0 on success.
+ */
+int jbo_prefill(int B, int T, int H, int dk, int dv, int D, int G, int K,
+                const float* x, const float* q, const float* k, const float* v,
+                const float* alpha, const float* beta, const float* W1,
+                const float* b1, const float* W2, const float* b2,
+                const float* S0, const float* conv_in, double* o,
+                double* S_final, float* conv_out, double* taps_out,
+                int nthreads) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || D <= 0 || G <= 0 || K < 1)
+    return 1;
+  if (!x || !q || !k || !v || !alpha || !beta || !W1 || !W2 || !o) return 1;
+  const int64_t n_tok = (int64_t)B * T;
+  double* taps = taps_out;
+  if (!taps) taps = (double*)malloc(sizeof(double) * (size_t)(n_tok * H * K + 1));
+  if (jbo_gen_taps(n_tok, D, G, H, K, x, W1, b1, W2, b2, taps, nthreads)) {
+    if (!taps_out) free(taps);
+    return 1;
+  }
+  const int units = B * H;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = units > 0 ? units : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  rec_job* jobs = (rec_job*)malloc(sizeof(rec_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (rec_job){B, T, H, dk, dv, K, q, k, v, alpha, beta, S0, conv_in,
+                        taps, o, S_final,
+                        (int)((int64_t)units * i / nthreads),
+                        (int)((int64_t)units * (i + 1) / nthreads)};
+    if (nthreads == 1) rec_worker(&jobs[i]);
+    else pthread_create(&th[i], NULL, rec_worker, &jobs[i]);
+  }
+  if (nthreads > 1)
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  if (conv_out) {
+    for (int b = 0; b < B; ++b)
+      for (int s = 0; s < K - 1; ++s)
+        for (int h = 0; h < H; ++h) {
+          const float* row = v_row(T - (K - 1) + s, b, h, T, H, dv, K, v, conv_in);
+          float* dst = conv_out + (((int64_t)b * (K - 1) + s) * H + h) * dv;
+          for (int c = 0; c < dv; ++c) dst[c] = row ? row[c] : 0.0f;
+        }
+  }
+  if (!taps_out) free(taps);
+  return 0;
+}
+
+/*
+ * One decode step for B sequences: the same block with T = 1.  S_in/S_out are
+ * [B][H][dk][dv] (S_out in double), cache_in/cache_out [B][K-1][H][dv],
+ * x_t [B][D], q_t,k_t [B][H][dk], v_t [B][H][dv], alpha_t,beta_t [B][H],
+ * o_t [B][H][dv].
+ */
+int jbo_decode_step(int B, int H, int dk, int dv, int D, int G, int K,
+                    const float* S_in, const float* cache_in,
+                    const float* x_t, const float* q_t, const float* k_t,
+                    const float* v_t, const float* alpha_t, const float* beta_t,
+                    const float* W1, const float* b1, const float* W2,
+                    const float* b2, double* o_t, double* S_out,
+                    float* cache_out, int nthreads) {
+  return jbo_prefill(B, 1, H, dk, dv, D, G, K, x_t, q_t, k_t, v_t, alpha_t,
+                     beta_t, W1, b1, W2, b2, S_in, cache_in, o_t, S_out,
+                     cache_out, NULL, nthreads);
+}
