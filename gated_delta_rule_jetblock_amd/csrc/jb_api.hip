@@ -1,0 +1,247 @@
+// jb_api.hip -- the C ABI of libjetblock (declared in include/jetblock.h):
+// host-side validation, workspace layout and kernel dispatch.  Validation is
+// complete before the first HIP call, so a rejected call touches no device
+// state; every entry point returns a jb_status and never throws.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/jetblock.h"
+#include "jb_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+jb_status fail(jb_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+jb_status ok() {
+  g_err[0] = 0;
+  return JB_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define JB_REQUIRE_PTR(p)                                                        \
+  do {                                                                           \
+    if (!(p)) return fail(JB_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);         \
+    if (!aligned16(p)) return fail(JB_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+#define JB_REQUIRE_SCALARS(p)                                                    \
+  do {                                                                           \
+    if (!(p)) return fail(JB_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);         \
+    if ((uintptr_t)(p) & 3u) return fail(JB_ERR_INVALID_ARG, "%s: %s is not 4-byte aligned", fn, #p); \
+  } while (0)
+#define JB_OPTIONAL_PTR(p)                                                       \
+  do {                                                                           \
+    if ((p) && !aligned16(p)) return fail(JB_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+// Shape checks common to every entry point; `decode` selects the T == 1 rules.
+jb_status check_shape(const char* fn, const jb_shape* s, bool decode) {
+  if (!s) return fail(JB_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  if (s->B < 1) return fail(JB_ERR_INVALID_ARG, "%s: B = %d must be >= 1", fn, s->B);
+  if (decode ? s->T != 1 : s->T < 0)
+    return fail(JB_ERR_INVALID_ARG, "%s: T = %d (%s)", fn, s->T, decode ? "decode needs T == 1" : "must be >= 0");
+  if (s->H < 1 || s->H > 32) return fail(JB_ERR_UNSUPPORTED, "%s: H = %d not in [1, 32]", fn, s->H);
+  if (s->dk != 32 && s->dk != 64 && s->dk != 96 && s->dk != 128)
+    return fail(JB_ERR_UNSUPPORTED, "%s: dk = %d not in {32, 64, 96, 128}", fn, s->dk);
+  if (s->dv != 64 && s->dv != 128 && s->dv != 256)
+    return fail(JB_ERR_UNSUPPORTED, "%s: dv = %d not in {64, 128, 256}", fn, s->dv);
+  if (s->d_model < 128 || s->d_model % 128)
+    return fail(JB_ERR_UNSUPPORTED, "%s: d_model = %d is not a positive multiple of 128", fn, s->d_model);
+  if (s->gen_hidden != 32) return fail(JB_ERR_UNSUPPORTED, "%s: gen_hidden = %d (must be 32)", fn, s->gen_hidden);
+  if (s->taps != 4) return fail(JB_ERR_UNSUPPORTED, "%s: taps = %d (must be 4)", fn, s->taps);
+  if (s->chunk != 0 && s->chunk != 64) return fail(JB_ERR_UNSUPPORTED, "%s: chunk = %d (must be 0 or 64)", fn, s->chunk);
+  if (s->io_dtype != JB_BF16 && s->io_dtype != JB_F32)
+    return fail(JB_ERR_INVALID_ARG, "%s: io_dtype = %d is not a jb_dtype", fn, s->io_dtype);
+  if (s->out_dtype != JB_BF16 && s->out_dtype != JB_F32)
+    return fail(JB_ERR_INVALID_ARG, "%s: out_dtype = %d is not a jb_dtype", fn, s->out_dtype);
+  const uint32_t extra = (uint32_t)s->flags & ~(0xffffu << 8);
+  if (extra) return fail(JB_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, extra);
+  if (decode && s->flags) return fail(JB_ERR_INVALID_ARG, "%s: flags must be 0 for decode", fn);
+  const int64_t tokens = (int64_t)s->B * s->T;
+  if (tokens * s->H * (int64_t)(s->dv > s->d_model ? s->dv : s->d_model) >= ((int64_t)1 << 40))
+    return fail(JB_ERR_UNSUPPORTED, "%s: tensor sizes exceed the supported range", fn);
+  return JB_OK;
+}
+
+int seg_flag(const jb_shape* s) { return (int)(((uint32_t)s->flags >> 8) & 0xffffu); }
+
+jb::PrefillPlan plan_of(const jb_shape* s) {
+  return jb::plan_prefill(s->B, s->T, s->H, s->dk, s->dv, s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16,
+                          s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16, seg_flag(s));
+}
+
+jb_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(JB_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t taps_bytes(const jb_shape* s) { return ((size_t)s->B * s->T * s->H * 4 * sizeof(float) + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* jb_status_string(jb_status st) {
+  switch (st) {
+    case JB_OK: return "JB_OK";
+    case JB_ERR_INVALID_ARG: return "JB_ERR_INVALID_ARG";
+    case JB_ERR_UNSUPPORTED: return "JB_ERR_UNSUPPORTED";
+    case JB_ERR_WORKSPACE: return "JB_ERR_WORKSPACE";
+    case JB_ERR_HIP: return "JB_ERR_HIP";
+  }
+  return "JB_ERR_UNKNOWN";
+}
+
+const char* jb_last_error(void) { return g_err; }
+
+int32_t jb_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+jb_status jb_prefill_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_prefill_workspace_size";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = jb::prefill_workspace_bytes(plan_of(s));
+  return ok();
+}
+
+jb_status jb_prefill(const jb_shape* s, const void* x, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const void* W1, const void* b1, const void* W2,
+                     const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
+                     void* conv_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_prefill";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  const jb::PrefillPlan p = plan_of(s);
+  if (!jb::prefill_supported(p))
+    return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built for io_dtype %d (the all-fp32 mode needs dk*dv <= 4096)",
+                fn, s->dk, s->dv, s->io_dtype);
+  if (seg_flag(s) < 0) return fail(JB_ERR_INVALID_ARG, "%s: bad segment flag", fn);
+  if (s->T > 0) {
+    JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v);
+    JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta); JB_REQUIRE_PTR(o);
+  }
+  JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_REQUIRE_PTR(S_final);
+  JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2); JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(conv_in);
+  JB_OPTIONAL_PTR(conv_out);
+  const size_t need = jb::prefill_workspace_bytes(p);
+  if (need && !workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if (workspace && ((uintptr_t)workspace & 255u))
+    return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  hipError_t e = hipSuccess;
+  if (s->T == 0) {
+    // empty sequence: the state and cache pass through
+    if (S0 && S0 != S_final)
+      e = hipMemcpyAsync(S_final, S0, (size_t)s->B * s->H * s->dk * s->dv * sizeof(float), hipMemcpyDeviceToDevice, hs);
+    else if (!S0)
+      e = jb::launch_fill_zero(S_final, (size_t)s->B * s->H * s->dk * s->dv, hs);
+    if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(io, s->B, 0, s->H, s->dv, v, conv_in, conv_out, hs);
+    return hip_status(fn, e);
+  }
+  float* taps = static_cast<float*>(workspace);
+  e = jb::launch_gen_taps(io, (int64_t)s->B * s->T, s->d_model, s->H, x, W1, b1, W2, b2, taps, hs);
+  if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, workspace, hs);
+  if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(io, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs);
+  return hip_status(fn, e);
+}
+
+jb_status jb_decode_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_decode_workspace_size";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = taps_bytes(s);
+  return ok();
+}
+
+jb_status jb_decode_step(const jb_shape* s, const float* S_in, float* S_out, const void* cache_in, void* cache_out,
+                         const void* x_t, const void* q_t, const void* k_t, const void* v_t, const float* alpha_t,
+                         const float* beta_t, const void* W1, const void* b1, const void* W2, const void* b2,
+                         void* o_t, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_decode_step";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (!jb::decode_supported(s->dk, s->dv)) return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built", fn, s->dk, s->dv);
+  JB_REQUIRE_PTR(S_in); JB_REQUIRE_PTR(S_out); JB_REQUIRE_PTR(cache_in); JB_REQUIRE_PTR(cache_out);
+  JB_REQUIRE_PTR(x_t); JB_REQUIRE_PTR(q_t); JB_REQUIRE_PTR(k_t); JB_REQUIRE_PTR(v_t);
+  JB_REQUIRE_SCALARS(alpha_t); JB_REQUIRE_SCALARS(beta_t); JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2);
+  JB_REQUIRE_PTR(o_t);
+  JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2);
+  const size_t need = taps_bytes(s);
+  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  float* taps = static_cast<float*>(workspace);
+  hipError_t e = jb::launch_gen_taps(io, s->B, s->d_model, s->H, x_t, W1, b1, W2, b2, taps, hs);
+  if (e == hipSuccess)
+    e = jb::launch_decode(io, out, s->B, s->H, s->dk, s->dv, S_in, S_out, cache_in, cache_out, q_t, k_t, v_t, alpha_t,
+                          beta_t, taps, o_t, hs);
+  return hip_status(fn, e);
+}
+
+jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
+                      float* taps, void* stream) {
+  const char* fn = "jb_gen_taps";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (s->T > 0) { JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(taps); }
+  JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  return hip_status(fn, jb::launch_gen_taps(io, (int64_t)s->B * s->T, s->d_model, s->H, x, W1, b1, W2, b2, taps,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+jb_status jb_gen_conv(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
+                      const void* v, const void* conv_in, float* taps, float* vconv, void* stream) {
+  const char* fn = "jb_gen_conv";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (s->T > 0) { JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(v); JB_REQUIRE_PTR(taps); JB_REQUIRE_PTR(vconv); }
+  JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2); JB_OPTIONAL_PTR(conv_in);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = jb::launch_gen_taps(io, (int64_t)s->B * s->T, s->d_model, s->H, x, W1, b1, W2, b2, taps, hs);
+  if (e == hipSuccess) e = jb::launch_conv(io, s->B, s->T, s->H, s->dv, taps, v, conv_in, vconv, hs);
+  return hip_status(fn, e);
+}
+
+jb_status jb_prologue(const jb_shape* s, const void* q, const void* k, const float* alpha, float* qhat, float* khat,
+                      float* g, void* stream) {
+  const char* fn = "jb_prologue";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (s->T > 0) {
+    JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_SCALARS(alpha);
+    JB_REQUIRE_PTR(qhat); JB_REQUIRE_PTR(khat); JB_REQUIRE_PTR(g);
+  }
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  return hip_status(fn, jb::launch_prologue(io, s->B, s->T, s->H, s->dk, q, k, alpha, qhat, khat, g,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+jb_status jb_probe_mfma(int32_t kind, const float* A, const float* B, float* D, void* stream) {
+  const char* fn = "jb_probe_mfma";
+  if (kind < 0 || kind > 2) return fail(JB_ERR_INVALID_ARG, "%s: kind = %d not in {0, 1, 2}", fn, kind);
+  JB_REQUIRE_PTR(A); JB_REQUIRE_PTR(B); JB_REQUIRE_PTR(D);
+  return hip_status(fn, jb::launch_probe_mfma(kind, A, B, D, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// jb_device.h -- device-side building blocks shared by the libjetblock kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Matrix-core operand placement used everywhere (16x16 output tiles):
+//   A (16 x K): lane l supplies row (l % 16); its lane group g = l / 16
+//               supplies a quarter of the K values.
+//   B (K x 16): lane l supplies column (l % 16), lane group g likewise.
+//   D (16x16):  lane l holds D[4g + i][l % 16] for i = 0..3.
+// A "fragment" is the 8 K-values one lane supplies for a 32-deep K block.
+// Because the contraction sums over K, any bijection between (g, j) and the
+// 32 K positions works as long as A and B use the same one.  Two orders are
+// used:
+//   kperm(g, j) = j < 4 ? 4g + j : 16 + 4g + (j - 4)
+//       -- the rows a lane already holds in the accumulators of a 32-row
+//          output block, so an accumulator block is a ready B fragment;
+//   8g + j
+//       -- contiguous, for operands streamed straight from memory.
+// For fp16 a fragment feeds one v_mfma_f32_16x16x32_f16; for fp32 it feeds
+// eight v_mfma_f32_16x16x4_f32, instruction j taking element j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jb {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bfloat16 bits in memory
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// round-to-nearest-even float -> bfloat16 (NaN stays NaN)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+template <> __device__ __forceinline__ float to_f32<_Float16>(_Float16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+
+// ------------------------------------------------------------- fragments
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+__host__ __device__ constexpr int kperm(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+template <typename OP> struct Frag { OP v[8]; };
+
+__device__ __forceinline__ void mma(f4_t& acc, const Frag<_Float16>& a, const Frag<_Float16>& b) {
+  half8_t av, bv;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { av[j] = a.v[j]; bv[j] = b.v[j]; }
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// A fragment (kperm order) from a row-major LDS tile: rows r0.., K offset k0.
+// Lane reads row r0 + l%16 at columns k0 + 4g..4g+3 and k0 + 16 + 4g..+3.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> lds_frag(const OP* base, int ld, int r0, int k0) {
+  const int l = lane_id(), m = l & 15, g = l >> 4;
+  const OP* p = base + (r0 + m) * ld + k0 + 4 * g;
+  Frag<OP> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { f.v[j] = p[j]; f.v[4 + j] = p[16 + j]; }
+  return f;
+}
+
+// B fragment (kperm order) from two accumulator tiles holding rows 0..15 and
+// 16..31 of a 32-row block, each row optionally scaled.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> acc_frag(const f4_t& lo, const f4_t& hi) {
+  Frag<OP> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { f.v[j] = from_f32<OP>(lo[j]); f.v[4 + j] = from_f32<OP>(hi[j]); }
+  return f;
+}
+
+__device__ __forceinline__ f4_t zero4() { return f4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// ----------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
+// sum over aligned groups of `n` consecutive lanes (n power of two <= 64)
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = N / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
+// inclusive prefix sum across the 64 lanes of a wave
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    float u = __shfl_up(v, off, WAVE);
+    if (l >= off) v += u;
+  }
+  return v;
+}
+
+// L2 normalisation factor (sum x^2 + 1e-6)^(-1/2)
+__device__ __forceinline__ float l2_scale(float sumsq) { return 1.0f / sqrtf(sumsq + 1e-6f); }
+
+}  // namespace jb

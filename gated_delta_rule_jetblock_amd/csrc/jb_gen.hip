@@ -1,0 +1,272 @@
+// jb_gen.hip -- kernel generator (x -> conv taps), the standalone dynamic
+// causal conv, the conv-cache tail copy and the matrix-core placement probe.
+//
+// Kernel generator (Jet-Nemotron csdn translation, section 2.4: it shares the
+// Q/K/V projections' input, reduces with a Linear layer, applies SiLU, and a
+// final Linear layer emits the conv-kernel weights; hidden width 32 and kernel
+// size 4 per the xugj520 blog, section 2.2):
+//     hidden = SiLU(W1 x + b1)   (32 units)     taps = W2 hidden + b2 (4 per head)
+// The first layer is a [tokens x d_model] x [d_model x 32] product on the
+// matrix cores (bf16 operands taken exactly from the inputs, fp32 accumulate;
+// fp32 operands in the all-fp32 mode); SiLU and the small second layer run in
+// fp32 on the vector ALUs.
+#include "jb_device.h"
+#include "jb_internal.h"
+
+namespace jb {
+
+constexpr int G = 32;        // generator hidden width
+constexpr int GEN_THR = 256; // 4 waves, each takes a quarter of d_model
+constexpr int MAX_HK = 128;  // up to 32 heads
+
+// Fragment of 8 contiguous K values (order 8g + j) straight from memory.
+__device__ __forceinline__ void load8(const bf16_t* p, bool valid, bf16x8_t& out) {
+  uint4 u = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+  out = *reinterpret_cast<bf16x8_t*>(&u);
+}
+__device__ __forceinline__ void load8(const float* p, bool valid, float (&out)[8]) {
+  float4 a = valid ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 b = valid ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+template <typename IO> struct GenFrag;
+template <> struct GenFrag<bf16_t> {
+  bf16x8_t v;
+  __device__ __forceinline__ void load(const bf16_t* p, bool valid) { load8(p, valid, v); }
+  __device__ __forceinline__ void mma(f4_t& acc, const GenFrag& b) const {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b.v, acc, 0, 0, 0);
+  }
+};
+template <> struct GenFrag<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p, bool valid) { load8(p, valid, v); }
+  __device__ __forceinline__ void mma(f4_t& acc, const GenFrag& b) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], b.v[j], acc, 0, 0, 0);
+  }
+};
+
+// One workgroup: 16*NT tokens.  hidden^T (32 x tokens) = W1 (32 x D) x^T;
+// wave w accumulates K range [w D/4, (w+1) D/4) and the partials meet in LDS.
+template <typename IO, int NT>
+__global__ __launch_bounds__(GEN_THR) void gen_kernel(int64_t n, int D, int HK, const IO* x, const IO* W1,
+                                                      const IO* b1, const IO* W2, const IO* b2, float* taps) {
+  constexpr int NTOK = 16 * NT;
+  __shared__ float red[4][G][NTOK];
+  __shared__ float hid[NTOK][G + 1];
+  __shared__ float w2s[MAX_HK][G + 1];
+  __shared__ float b2s[MAX_HK];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * NTOK;
+
+  f4_t acc[2][NT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[u][t] = zero4();
+
+  const int kq = D / 4;
+  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 32) {
+    GenFrag<IO> A[2], Bt[NT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) A[u].load(W1 + (int64_t)(u * 16 + m16) * D + k0 + 8 * g4, true);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t tok = n0 + t * 16 + m16;
+      Bt[t].load(x + tok * D + k0 + 8 * g4, tok < n);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) A[u].mma(acc[u][t], Bt[t]);
+  }
+  // lane holds hidden^T[u*16 + 4g + i][t*16 + m16]
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][u * 16 + 4 * g4 + i][t * 16 + m16] = acc[u][t][i];
+  for (int e = tid; e < HK * G; e += GEN_THR) w2s[e / G][e % G] = to_f32<IO>(W2[e]);
+  for (int e = tid; e < HK; e += GEN_THR) b2s[e] = b2 ? to_f32<IO>(b2[e]) : 0.f;
+  __syncthreads();
+  for (int e = tid; e < G * NTOK; e += GEN_THR) {
+    const int u = e / NTOK, t = e % NTOK;
+    float hsum = red[0][u][t] + red[1][u][t] + red[2][u][t] + red[3][u][t];
+    if (b1) hsum += to_f32<IO>(b1[u]);
+    hid[t][u] = hsum / (1.0f + expf(-hsum));  // SiLU
+  }
+  __syncthreads();
+  for (int e = tid; e < NTOK * HK; e += GEN_THR) {
+    const int t = e / HK, r = e % HK;
+    const int64_t tok = n0 + t;
+    if (tok >= n) continue;
+    float s = b2s[r];
+#pragma unroll
+    for (int u = 0; u < G; ++u) s += w2s[r][u] * hid[t][u];
+    taps[tok * HK + r] = s;
+  }
+}
+
+hipError_t launch_gen_taps(int io, int64_t n, int D, int H, const void* x, const void* W1, const void* b1,
+                           const void* W2, const void* b2, float* taps, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int HK = 4 * H;
+  // few rows (decode): 16 tokens per workgroup to spread the rows; else 64
+  if (n <= 4096) {
+    const dim3 grid((unsigned)((n + 15) / 16));
+    if (io == IO_BF16)
+      gen_kernel<bf16_t, 1><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const bf16_t*)x, (const bf16_t*)W1,
+                                                         (const bf16_t*)b1, (const bf16_t*)W2, (const bf16_t*)b2, taps);
+    else
+      gen_kernel<float, 1><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const float*)x, (const float*)W1,
+                                                        (const float*)b1, (const float*)W2, (const float*)b2, taps);
+  } else {
+    const dim3 grid((unsigned)((n + 63) / 64));
+    if (io == IO_BF16)
+      gen_kernel<bf16_t, 4><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const bf16_t*)x, (const bf16_t*)W1,
+                                                         (const bf16_t*)b1, (const bf16_t*)W2, (const bf16_t*)b2, taps);
+    else
+      gen_kernel<float, 4><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const float*)x, (const float*)W1,
+                                                        (const float*)b1, (const float*)W2, (const float*)b2, taps);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- standalone conv
+
+// one thread per (b, t, h, column): v'_t = sum_j taps_t[j] v_{t-3+j}
+template <typename IO>
+__global__ void conv_kernel(int B, int T, int H, int dv, const float* taps, const IO* v, const IO* conv_in,
+                            float* vconv) {
+  const int64_t total = (int64_t)B * T * H * dv;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e % dv);
+    const int64_t bth = e / dv;
+    const int h = (int)(bth % H);
+    const int64_t bt = bth / H;
+    const int t = (int)(bt % T);
+    const int b = (int)(bt / T);
+    const float* tp = taps + bth * 4;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = t - 3 + j;
+      float val = 0.f;
+      if (tt >= 0) val = to_f32<IO>(v[(((int64_t)b * T + tt) * H + h) * dv + c]);
+      else if (conv_in) val = to_f32<IO>(conv_in[(((int64_t)b * 3 + (3 + tt)) * H + h) * dv + c]);
+      s += tp[j] * val;
+    }
+    vconv[e] = s;
+  }
+}
+
+hipError_t launch_conv(int io, int B, int T, int H, int dv, const float* taps, const void* v, const void* conv_in,
+                       float* vconv, hipStream_t stream) {
+  const int64_t total = (int64_t)B * T * H * dv;
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  if (io == IO_BF16)
+    conv_kernel<bf16_t><<<blocks, 256, 0, stream>>>(B, T, H, dv, taps, (const bf16_t*)v, (const bf16_t*)conv_in, vconv);
+  else
+    conv_kernel<float><<<blocks, 256, 0, stream>>>(B, T, H, dv, taps, (const float*)v, (const float*)conv_in, vconv);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- conv cache tail
+
+// conv_out[b][s] = row T-3+s of [conv_in; v]; one thread per (b, h, c) reads
+// all three sources before writing, so conv_out may alias conv_in.
+template <typename IO>
+__global__ void conv_tail_kernel(int B, int T, int H, int dv, const IO* v, const IO* conv_in, IO* conv_out) {
+  const int64_t total = (int64_t)B * H * dv;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % dv);
+  const int h = (int)((e / dv) % H);
+  const int b = (int)(e / ((int64_t)dv * H));
+  IO vals[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int t = T - 3 + s;
+    if (t >= 0) vals[s] = v[(((int64_t)b * T + t) * H + h) * dv + c];
+    else if (conv_in) vals[s] = conv_in[(((int64_t)b * 3 + (3 + t)) * H + h) * dv + c];
+    else vals[s] = from_f32<IO>(0.f);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) conv_out[(((int64_t)b * 3 + s) * H + h) * dv + c] = vals[s];
+}
+
+hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v, const void* conv_in, void* conv_out,
+                            hipStream_t stream) {
+  const int64_t total = (int64_t)B * H * dv;
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)((total + 255) / 256);
+  if (io == IO_BF16)
+    conv_tail_kernel<bf16_t><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const bf16_t*)v, (const bf16_t*)conv_in,
+                                                         (bf16_t*)conv_out);
+  else
+    conv_tail_kernel<float><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const float*)v, (const float*)conv_in,
+                                                        (float*)conv_out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- zero fill
+
+__global__ void fill_zero_kernel(float* p, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+    p[e] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- placement probe
+
+__global__ __launch_bounds__(64) void probe_kernel(int kind, const float* A, const float* B, float* D) {
+  const int l = threadIdx.x, m = l & 15, g = l >> 4;
+  f4_t acc = zero4();
+  if (kind == 0) {
+    Frag<_Float16> a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a.v[j] = (_Float16)A[m * 32 + kperm(g, j)];
+      b.v[j] = (_Float16)B[kperm(g, j) * 16 + m];
+    }
+    mma(acc, a, b);
+  } else if (kind == 1) {
+    bf16_t ab[8], bb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ab[j] = f32_to_bf16(A[m * 32 + 8 * g + j]);
+      bb[j] = f32_to_bf16(B[(8 * g + j) * 16 + m]);
+    }
+    bf16x8_t av = *reinterpret_cast<bf16x8_t*>(ab), bv = *reinterpret_cast<bf16x8_t*>(bb);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  } else {
+    Frag<float> a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a.v[j] = A[m * 32 + kperm(g, j)];
+      b.v[j] = B[kperm(g, j) * 16 + m];
+    }
+    mma(acc, a, b);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) D[(4 * g + i) * 16 + m] = acc[i];
+}
+
+hipError_t launch_probe_mfma(int kind, const float* A, const float* B, float* D, hipStream_t stream) {
+  probe_kernel<<<1, 64, 0, stream>>>(kind, A, B, D);
+  return hipGetLastError();
+}
+
+}  // namespace jb

@@ -1,0 +1,61 @@
+// jb_internal.h -- host-side launchers shared between the libjetblock
+// translation units.  Each launcher enqueues kernels on `stream` and returns
+// the hipError_t of hipGetLastError() after the launch.  Arguments have been
+// validated by the C-ABI layer (jb_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jb {
+
+enum IoType { IO_BF16 = 0, IO_F32 = 1 };
+
+// Kernel generator over n rows of x [n][D] -> taps [n][H*4] f32.
+hipError_t launch_gen_taps(int io, int64_t n, int D, int H, const void* x, const void* W1,
+                           const void* b1, const void* W2, const void* b2, float* taps,
+                           hipStream_t stream);
+
+// Dynamic causal conv: vconv [B][T][H][dv] f32 from taps [B][T][H][4].
+hipError_t launch_conv(int io, int B, int T, int H, int dv, const float* taps, const void* v,
+                       const void* conv_in, float* vconv, hipStream_t stream);
+
+// Normalised q, k (f32) and chunk-local cumulative log-gate g.
+hipError_t launch_prologue(int io, int B, int T, int H, int dk, const void* q, const void* k,
+                           const float* alpha, float* qhat, float* khat, float* g,
+                           hipStream_t stream);
+
+// Copy of the last 3 raw value rows of [conv_in; v] into conv_out.
+hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v,
+                            const void* conv_in, void* conv_out, hipStream_t stream);
+
+// Chunked prefill (segment summaries, scan, outputs).
+struct PrefillPlan {
+  int B, T, H, dk, dv;
+  int io, out;       // IoType of inputs and of o
+  int nchunks;       // ceil(T / 64)
+  int seg_len;       // chunks per segment
+  int nseg;          // number of segments
+};
+PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, int seg_len);
+size_t prefill_workspace_bytes(const PrefillPlan& p);
+bool prefill_supported(const PrefillPlan& p);
+hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const float* taps,
+                          const void* conv_in, const float* S0, void* o, float* S_final,
+                          void* workspace, hipStream_t stream);
+
+// One decode step's state update (taps precomputed).
+bool decode_supported(int dk, int dv);
+hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const float* S_in,
+                         float* S_out, const void* cache_in, void* cache_out, const void* q_t,
+                         const void* k_t, const void* v_t, const float* alpha_t,
+                         const float* beta_t, const float* taps, void* o_t, hipStream_t stream);
+
+// Zero-fill n floats with a kernel (no memset node, safe under graph capture).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+
+hipError_t launch_probe_mfma(int kind, const float* A, const float* B, float* D, hipStream_t stream);
+
+}  // namespace jb

@@ -1,0 +1,695 @@
+// jb_prefill.hip -- chunked gated delta-rule prefill for gfx950.
+//
+// The recurrence (JetBlock time mixing is Gated DeltaNet: Jet-Nemotron csdn
+// translation, section 2.4) in the transposed state M = S^T (dk x dv):
+//     M_t = a_t (I - b_t k_t k_t^T) M_{t-1} + b_t k_t v'_t^T,   o_t = M_t^T q_t
+// with L2-normalised q, k.  Within a chunk of C = 64 tokens entering with M0
+// (local index i, g_i = sum_{j<=i} ln a_j, gamma_i = e^{g_i}):
+//     A_ij = b_i e^{g_i - g_j} k_i.k_j (j < i),   X = (I + A)^{-1}
+//     T1 = X diag(b),  T2 = X diag(b gamma)
+//     W = T2 K,  U0 = T1 V'                                   (WY/UT form)
+//     V_new = U0 - W M0
+//     O = diag(gamma) Q M0 + P V_new,  P_ij = e^{g_i - g_j} q_i.k_j (j <= i)
+//     M_C = gamma_C M0 + K^T diag(e^{g_C - g}) V_new
+// so a chunk maps M0 to Phi_c M0 + D_c.  A long sequence is cut into
+// segments of L chunks; three kernels then run:
+//   1. summary  (per segment but the last, in parallel): the segment's affine
+//      map (Phi_s, D_s), obtained by running the chunk loop from the zero
+//      state on the augmented columns [D | Phi] with Phi starting at I;
+//   2. scan     (per head and 16-column tile): M_{s+1} = Phi_s M_s + D_s;
+//   3. output   (per segment, in parallel): the chunk loop from the true M_s,
+//      writing o and, for the last segment, the final state.
+// With one segment only the output kernel runs.
+//
+// Matrix products run on the matrix cores: fp16 operands with fp32
+// accumulation for bfloat16 inputs (bf16 inputs convert to fp16 exactly in
+// the normal range), fp32 operands in the all-fp32 mode.  The state and every
+// accumulator stay fp32; scalars (norms, gates) are applied in fp32.
+//
+// Workgroup: 8 wavefronts.  Chunk-shared tiles (K, K^T, Q, A, X, T1, T2, W,
+// P, the value rows with their 3-row conv halo) live in LDS; each wave owns
+// whole 16-column tiles of the state and keeps them in accumulator registers
+// for the whole segment, so the state never leaves the compute unit.
+#include "jb_device.h"
+#include "jb_internal.h"
+
+namespace jb {
+
+constexpr int C = 64;        // chunk length
+constexpr int NWAVE = 8;     // wavefronts per chunk workgroup
+constexpr int NTHR = NWAVE * WAVE;
+constexpr int NCU = 256;     // compute units of one MI355X
+
+enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1 };
+
+struct ChunkArgs {
+  int T, H, nchunks, seg_len, nseg;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* taps;
+  const void* conv_in;
+  const float* S0;      // output kernel with one segment only
+  const float* Mstart;  // [B][H][nseg][DK][DV] start states (several segments)
+  float* Dsum;          // [B][H][nseg][DK][DV]
+  float* Phi;           // [B][H][nseg][DK][DK]
+  void* o;
+  float* S_final;
+};
+
+// ------------------------------------------------------------ LDS layout
+
+template <int DK, int DV, typename IO, typename OP, int MODE>
+struct Lds {
+  static constexpr int szKh = C * DK * (int)sizeof(OP);
+  static constexpr int szQh = MODE == MODE_OUTPUT ? C * DK * (int)sizeof(OP) : 0;
+  static constexpr int szV = (C + 3) * DV * (int)sizeof(IO);
+  static constexpr int szTap = C * 4 * 4;
+  static constexpr int szScal = 4 * C * 4;
+  static constexpr int szA = C * C * 4 > C * DK * (int)sizeof(OP) ? C * C * 4 : C * DK * (int)sizeof(OP);
+  static constexpr int szX = C * C * 4;
+  static constexpr int szT = 2 * C * C * (int)sizeof(OP) > 3 * 256 * 4 ? 2 * C * C * (int)sizeof(OP) : 3 * 256 * 4;
+  static constexpr int szP = MODE == MODE_OUTPUT ? C * C * (int)sizeof(OP) : 0;
+
+  static constexpr int oKh = 0;
+  static constexpr int oKt = oKh + szKh;
+  static constexpr int oQh = oKt + szKh;
+  static constexpr int oV = oQh + szQh;
+  static constexpr int oTap = oV + ((szV + 15) / 16) * 16;
+  static constexpr int oScal = oTap + szTap;
+  static constexpr int oA = oScal + szScal;   // A (f32), later W (OP)
+  static constexpr int oX = oA + szA;
+  static constexpr int oT = oX + szX;         // T1, T2 (OP); Y scratch (f32) before them
+  static constexpr int oP = oT + szT;
+  static constexpr int total = oP + szP;
+};
+
+// kind-of-tile tables for the lower-triangular 4x4 tile grid of a chunk
+__device__ __constant__ const int kLowI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__device__ __constant__ const int kLowJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+template <typename IO>
+__device__ __forceinline__ void load_row_part(const IO* src, float* dst, int n, bool valid);
+
+template <>
+__device__ __forceinline__ void load_row_part<bf16_t>(const bf16_t* src, float* dst, int n, bool valid) {
+  // n is a multiple of 4: 8-byte loads
+  for (int e = 0; e < n; e += 4) {
+    uint2 u = valid ? *reinterpret_cast<const uint2*>(src + e) : make_uint2(0u, 0u);
+    dst[e + 0] = __uint_as_float(u.x << 16);
+    dst[e + 1] = __uint_as_float(u.x & 0xffff0000u);
+    dst[e + 2] = __uint_as_float(u.y << 16);
+    dst[e + 3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_row_part<float>(const float* src, float* dst, int n, bool valid) {
+  for (int e = 0; e < n; e += 4) {
+    float4 u = valid ? *reinterpret_cast<const float4*>(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    dst[e + 0] = u.x;
+    dst[e + 1] = u.y;
+    dst[e + 2] = u.z;
+    dst[e + 3] = u.w;
+  }
+}
+
+// The gate and normalisation prologue for one chunk, as the 512 threads of a
+// chunk workgroup execute it: thread (row = tid/8, part = tid%8) normalises
+// DK/8 elements of q and k for token t0 + row; wave 0 additionally scans the
+// log-gates.  Rows at or beyond `n` (ragged tail) are neutral tokens: q = k =
+// 0, a = 1, b = 0.  Results are handed to the caller's sinks.
+template <int DK, typename IO>
+struct Prologue {
+  static constexpr int E = DK / 8;
+  float kv[E], qv[E];
+  int row, part;
+
+  __device__ __forceinline__ void normalise(const IO* q, const IO* k, int64_t row_base, int H,
+                                            int n, bool want_q) {
+    row = threadIdx.x >> 3;
+    part = threadIdx.x & 7;
+    const bool valid = row < n;
+    const int64_t off = (row_base + (int64_t)row * H) * DK + part * E;
+    load_row_part<IO>(k + off, kv, E, valid);
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) sk += kv[e] * kv[e];
+    sk = group_sum<8>(sk);
+    const float rk = l2_scale(sk);
+#pragma unroll
+    for (int e = 0; e < E; ++e) kv[e] *= rk;
+    if (want_q) {
+      load_row_part<IO>(q + off, qv, E, valid);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sq += qv[e] * qv[e];
+      sq = group_sum<8>(sq);
+      const float rq = l2_scale(sq);
+#pragma unroll
+      for (int e = 0; e < E; ++e) qv[e] *= rq;
+    }
+  }
+};
+
+// wave-0 part: g = inclusive cumsum of ln(alpha) over the chunk (lane = row)
+__device__ __forceinline__ float chunk_gate_scan(const float* alpha, int64_t idx, bool valid) {
+  const float la = valid ? logf(alpha[idx]) : 0.f;
+  return wave_inclusive_scan(la);
+}
+
+// ------------------------------------------------------------ chunk kernel
+
+template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE>
+__global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
+  using L = Lds<DK, DV, IO, OP, MODE>;
+  constexpr int NCT = MODE == MODE_SUMMARY ? (DV + DK) / 16 : DV / 16;  // column tiles
+  constexpr int CPW = (NCT + NWAVE - 1) / NWAVE;                        // tiles per wave (max)
+  constexpr int RT = DK / 16;                                           // row tiles of M
+  constexpr int KB = DK / 32;                                           // 32-deep blocks of dk
+  constexpr int VCT = DV / 16;                                          // value column tiles
+  static_assert(L::total <= 160 * 1024, "LDS budget of one CU exceeded");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::total];
+  OP* sKh = reinterpret_cast<OP*>(smem + L::oKh);      // [C][DK]   normalised k
+  OP* sKt = reinterpret_cast<OP*>(smem + L::oKt);      // [DK][C]   its transpose
+  OP* sQh = reinterpret_cast<OP*>(smem + L::oQh);      // [C][DK]   normalised q
+  IO* sV = reinterpret_cast<IO*>(smem + L::oV);        // [C+3][DV] raw v rows t0-3 ..
+  float* sTap = reinterpret_cast<float*>(smem + L::oTap);   // [C][4]
+  float* sG = reinterpret_cast<float*>(smem + L::oScal);    // [C] g
+  float* sGam = sG + C;                                      // [C] e^g
+  float* sBeta = sG + 2 * C;                                 // [C] b
+  float* sDec = sG + 3 * C;                                  // [C] e^{g_C - g}
+  float* sA = reinterpret_cast<float*>(smem + L::oA);        // [C][C]
+  OP* sW = reinterpret_cast<OP*>(smem + L::oA);              // [C][DK] -W (after A is dead)
+  float* sX = reinterpret_cast<float*>(smem + L::oX);        // [C][C]
+  OP* sT1 = reinterpret_cast<OP*>(smem + L::oT);             // [C][C]
+  OP* sT2 = sT1 + C * C;                                     // [C][C]
+  float* sY = reinterpret_cast<float*>(smem + L::oT);        // [3][16][16] scratch
+  OP* sP = reinterpret_cast<OP*>(smem + L::oP);              // [C][C]
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, H = a.H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const IO* q = reinterpret_cast<const IO*>(a.q);
+  const IO* k = reinterpret_cast<const IO*>(a.k);
+  const IO* v = reinterpret_cast<const IO*>(a.v);
+  const IO* cin = reinterpret_cast<const IO*>(a.conv_in);
+  const int64_t bh = (int64_t)b * H + h;
+
+  // ---- initial state (accumulator layout: lane holds M[rt*16+4g+i][ct*16+m16])
+  f4_t Macc[CPW][RT];
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      Macc[cw][rt] = zero4();
+      if (ct >= NCT) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        if (MODE == MODE_SUMMARY) {
+          if (ct >= VCT) Macc[cw][rt][i] = (row == (ct - VCT) * 16 + m16) ? 1.f : 0.f;
+        } else {
+          const int col = ct * 16 + m16;
+          const float* src = a.nseg > 1 ? a.Mstart + ((bh * a.nseg + s) * DK) * DV
+                                        : (a.S0 ? a.S0 + bh * DK * DV : nullptr);
+          Macc[cw][rt][i] = src ? src[row * DV + col] : 0.f;
+        }
+      }
+    }
+  }
+
+  // upper tiles of P are never written by the tile jobs: zero them once
+  if (MODE == MODE_OUTPUT) {
+    for (int e = tid; e < C * C; e += NTHR) {
+      const int r = e / C, c = e % C;
+      if ((c >> 4) > (r >> 4)) sP[e] = from_f32<OP>(0.f);
+    }
+  }
+
+  const int c_begin = s * a.seg_len;
+  const int c_end = min(a.nchunks, c_begin + a.seg_len);
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+
+    // ================= load + prologue =================
+    {
+      Prologue<DK, IO> pr;
+      pr.normalise(q, k, ((int64_t)b * T + t0) * H + h, H, n, MODE == MODE_OUTPUT);
+#pragma unroll
+      for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
+        const int d = pr.part * Prologue<DK, IO>::E + e;
+        const OP kh = from_f32<OP>(pr.kv[e]);
+        sKh[pr.row * DK + d] = kh;
+        sKt[d * C + pr.row] = kh;
+        if (MODE == MODE_OUTPUT) sQh[pr.row * DK + d] = from_f32<OP>(pr.qv[e]);
+      }
+    }
+    if (wave == 0) {
+      const int row = lane;
+      const bool valid = row < n;
+      const int64_t idx = ((int64_t)b * T + t0 + row) * H + h;
+      const float g = chunk_gate_scan(a.alpha, idx, valid);
+      const float gC = __shfl(g, C - 1, WAVE);
+      sG[row] = g;
+      sGam[row] = expf(g);
+      sBeta[row] = valid ? a.beta[idx] : 0.f;
+      sDec[row] = expf(gC - g);
+      const float4 tp = valid ? *reinterpret_cast<const float4*>(a.taps + idx * 4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(sTap + row * 4) = tp;
+    }
+    {
+      // value rows t0-3 .. t0+C-1 (16-byte pieces)
+      constexpr int PPR = DV * (int)sizeof(IO) / 16;
+      for (int e = tid; e < (C + 3) * PPR; e += NTHR) {
+        const int r = e / PPR, pc = e % PPR;
+        const int t = t0 - 3 + r;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (t >= 0 && t < T && r - 3 < n) {
+          val = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
+        } else if (t < 0 && cin) {
+          val = *reinterpret_cast<const uint4*>(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
+        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sV) + (size_t)e * 16) = val;
+      }
+    }
+    __syncthreads();
+
+    // ================= K K^T and Q K^T tiles =================
+    {
+      constexpr int NJOB = MODE == MODE_OUTPUT ? 20 : 10;
+      for (int job = wave; job < NJOB; job += NWAVE) {
+        const int which = job / 10, ti = kLowI[job % 10], tj = kLowJ[job % 10];
+        const OP* Asrc = which ? sQh : sKh;
+        f4_t acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mma(acc, lds_frag<OP>(Asrc, DK, ti * 16, kb * 32), lds_frag<OP>(sKh, DK, tj * 16, kb * 32));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+          if (which == 0) {
+            sA[r * C + cc] = cc < r ? sBeta[r] * expf(sG[r] - sG[cc]) * acc[i] : 0.f;
+          } else {
+            sP[r * C + cc] = from_f32<OP>(cc <= r ? expf(sG[r] - sG[cc]) * acc[i] : 0.f);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ================= X = (I + A)^{-1}, blocked =================
+    if (wave == 0) {
+      // four 16x16 diagonal blocks by forward substitution, one column per lane
+      const int base = (lane >> 4) * 16, jc = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == jc) ? 1.f : 0.f;
+        const float* arow = sA + (base + i) * C + base;
+#pragma unroll
+        for (int kk = 0; kk < i; ++kk) acc -= arow[kk] * x[kk];
+        x[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sX[(base + i) * C + base + jc] = x[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+      // blocks (i, j = i - d): Y = sum_{k=j}^{i-1} A_ik X_kj ; X_ij = -X_ii Y
+      const int nblk = 4 - d;
+      if (wave < nblk) {
+        const int bi = d + wave, bj = bi - d;
+        const int r = lane >> 2, c0 = (lane & 3) * 4;
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = bj; kb < bi; ++kb) {
+          const float* arow = sA + (bi * 16 + r) * C + kb * 16;
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
+            const float av = arow[kk];
+            const float4 xv = *reinterpret_cast<const float4*>(sX + (kb * 16 + kk) * C + bj * 16 + c0);
+            y[0] += av * xv.x; y[1] += av * xv.y; y[2] += av * xv.z; y[3] += av * xv.w;
+          }
+        }
+        *reinterpret_cast<float4*>(sY + wave * 256 + r * 16 + c0) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+      __syncthreads();
+      if (wave < nblk) {
+        const int bi = d + wave, bj = bi - d;
+        const int r = lane >> 2, c0 = (lane & 3) * 4;
+        float z[4] = {0.f, 0.f, 0.f, 0.f};
+        const float* xrow = sX + (bi * 16 + r) * C + bi * 16;
+        for (int kk = 0; kk <= r; ++kk) {
+          const float xv = xrow[kk];
+          const float4 yv = *reinterpret_cast<const float4*>(sY + wave * 256 + kk * 16 + c0);
+          z[0] -= xv * yv.x; z[1] -= xv * yv.y; z[2] -= xv * yv.z; z[3] -= xv * yv.w;
+        }
+        *reinterpret_cast<float4*>(sX + (bi * 16 + r) * C + bj * 16 + c0) = make_float4(z[0], z[1], z[2], z[3]);
+      }
+      __syncthreads();
+    }
+    // T1 = X diag(b), T2 = X diag(b gamma) (zero above the diagonal)
+    for (int e = tid; e < C * C; e += NTHR) {
+      const int r = e / C, cc = e % C;
+      const float xv = cc <= r ? sX[e] : 0.f;
+      sT1[e] = from_f32<OP>(xv * sBeta[cc]);
+      sT2[e] = from_f32<OP>(xv * sBeta[cc] * sGam[cc]);
+    }
+    __syncthreads();
+
+    // ================= -W = -(T2 K) =================
+    for (int job = wave; job < 4 * RT; job += NWAVE) {
+      const int rt = job / RT, ct = job % RT;
+      f4_t acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb * 32 <= rt * 16 + 15)
+          mma(acc, lds_frag<OP>(sT2, C, rt * 16, kb * 32), lds_frag<OP>(sKt, C, ct * 16, kb * 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sW[(rt * 16 + 4 * g4 + i) * DK + ct * 16 + m16] = from_f32<OP>(-acc[i]);
+    }
+    __syncthreads();
+
+    // ================= per-wave column tiles =================
+    const float gamC = sGam[C - 1];
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) {
+      const int ct = wave + cw * NWAVE;
+      if (ct >= NCT) continue;
+      const bool valcol = MODE == MODE_OUTPUT || ct < VCT;
+      f4_t U[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
+      if (valcol) {
+        // V' fragments: v'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
+        const int col = ct * 16 + m16;
+        Frag<OP> Vf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = kb * 32 + kperm(g4, j);
+            const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
+            const float vv = tp.x * to_f32<IO>(sV[(r + 0) * DV + col]) + tp.y * to_f32<IO>(sV[(r + 1) * DV + col]) +
+                             tp.z * to_f32<IO>(sV[(r + 2) * DV + col]) + tp.w * to_f32<IO>(sV[(r + 3) * DV + col]);
+            Vf[kb].v[j] = from_f32<OP>(vv);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb * 32 <= rt * 16 + 15) mma(U[rt], lds_frag<OP>(sT1, C, rt * 16, kb * 32), Vf[kb]);
+      }
+      // V_new = U0 - W M0
+      Frag<OP> Mf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) Mf[kb] = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) mma(U[rt], lds_frag<OP>(sW, DK, rt * 16, kb * 32), Mf[kb]);
+
+      if (MODE == MODE_OUTPUT) {
+        Frag<OP> Vn[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Vn[kb] = acc_frag<OP>(U[2 * kb], U[2 * kb + 1]);
+        OUT* o = reinterpret_cast<OUT*>(a.o);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          f4_t O = zero4();
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) mma(O, lds_frag<OP>(sQh, DK, rt * 16, kb * 32), Mf[kb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[i] *= sGam[rt * 16 + 4 * g4 + i];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb * 32 <= rt * 16 + 15) mma(O, lds_frag<OP>(sP, C, rt * 16, kb * 32), Vn[kb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = rt * 16 + 4 * g4 + i;
+            if (row < n) o[(((int64_t)b * T + t0 + row) * H + h) * DV + ct * 16 + m16] = from_f32<OUT>(O[i]);
+          }
+        }
+      }
+      // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
+      Frag<OP> Vd[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Vd[kb].v[j] = from_f32<OP>(U[2 * kb][j] * sDec[kb * 32 + 4 * g4 + j]);
+          Vd[kb].v[4 + j] = from_f32<OP>(U[2 * kb + 1][j] * sDec[kb * 32 + 16 + 4 * g4 + j]);
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma(Macc[cw][rt], lds_frag<OP>(sKt, C, rt * 16, kb * 32), Vd[kb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- results
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+    if (ct >= NCT) continue;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        if (MODE == MODE_OUTPUT) {
+          if (s == a.nseg - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+        } else if (ct < VCT) {
+          a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+        } else {
+          a.Phi[((bh * a.nseg + s) * DK + row) * DK + (ct - VCT) * 16 + m16] = Macc[cw][rt][i];
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------ segment scan
+
+// fp16 split products: x ~= hi + lo with both parts fp16, three products
+// keep about 22 bits of the fp32 operands.
+__device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const float* bv, _Float16) {
+  Frag<_Float16> ah, al, bh, bl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ah.v[j] = (_Float16)av[j];
+    al.v[j] = (_Float16)(av[j] - (float)ah.v[j]);
+    bh.v[j] = (_Float16)bv[j];
+    bl.v[j] = (_Float16)(bv[j] - (float)bh.v[j]);
+  }
+  mma(acc, ah, bh);
+  mma(acc, ah, bl);
+  mma(acc, al, bh);
+}
+
+__device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const float* bv, float) {
+  Frag<float> af, bf;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { af.v[j] = av[j]; bf.v[j] = bv[j]; }
+  mma(acc, af, bf);
+}
+
+// grid (DV/16, H, B), one wavefront: M_0 = S0 (or 0); M_{s+1} = Phi_s M_s + D_s.
+template <int DK, int DV, typename OP>
+__global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const float* S0, const float* Dsum,
+                                                    const float* Phi, float* Mstart) {
+  constexpr int RT = DK / 16, KB = DK / 32;
+  const int ct = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x, m16 = lane & 15, g4 = lane >> 4;
+  const int64_t bh = (int64_t)b * H + h;
+  const int col = ct * 16 + m16;
+  f4_t M[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[rt][i] = S0 ? S0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
+  for (int s = 0; s < nseg; ++s) {
+    float* dst = Mstart + (bh * nseg + s) * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[rt][i];
+    if (s == nseg - 1) break;
+    const float* D = Dsum + (bh * nseg + s) * DK * DV;
+    const float* P = Phi + (bh * nseg + s) * DK * DK;
+    float bv[KB][8];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { bv[kb][j] = M[2 * kb][j]; bv[kb][4 + j] = M[2 * kb + 1][j]; }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = D[(rt * 16 + 4 * g4 + i) * DV + col];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float av[8];
+        const float* prow = P + (rt * 16 + m16) * DK + kb * 32 + 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { av[j] = prow[j]; av[4 + j] = prow[16 + j]; }
+        split_mma(acc, av, bv[kb], OP());
+      }
+      M[rt] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------------ prologue hook
+
+// grid (nchunks, H, B), 512 threads: the chunk kernels' prologue on its own.
+template <int DK, typename IO>
+__global__ __launch_bounds__(NTHR) void prologue_kernel(int T, int H, const IO* q, const IO* k,
+                                                        const float* alpha, float* qhat, float* khat,
+                                                        float* gout) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t0 = c * C, n = min(C, T - t0);
+  Prologue<DK, IO> pr;
+  pr.normalise(q, k, ((int64_t)b * T + t0) * H + h, H, n, true);
+  if (pr.row < n) {
+    const int64_t off = (((int64_t)b * T + t0 + pr.row) * H + h) * DK + pr.part * Prologue<DK, IO>::E;
+#pragma unroll
+    for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
+      khat[off + e] = pr.kv[e];
+      qhat[off + e] = pr.qv[e];
+    }
+  }
+  if (threadIdx.x < WAVE) {
+    const int row = threadIdx.x;
+    const int64_t idx = ((int64_t)b * T + t0 + row) * H + h;
+    const float g = chunk_gate_scan(alpha, idx, row < n);
+    if (row < n) gout[idx] = g;
+  }
+}
+
+// ------------------------------------------------------------ host side
+
+PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, int seg_len) {
+  PrefillPlan p{};
+  p.B = B; p.T = T; p.H = H; p.dk = dk; p.dv = dv; p.io = io; p.out = out;
+  p.nchunks = (T + C - 1) / C;
+  if (p.nchunks == 0) { p.seg_len = 1; p.nseg = 0; return p; }
+  if (seg_len <= 0) {
+    const int64_t units = (int64_t)B * H;
+    int nseg = units >= NCU ? 1 : (int)(NCU / units);
+    if (nseg > p.nchunks) nseg = p.nchunks;
+    if (nseg < 1) nseg = 1;
+    seg_len = (p.nchunks + nseg - 1) / nseg;
+  }
+  p.seg_len = seg_len;
+  p.nseg = (p.nchunks + seg_len - 1) / seg_len;
+  return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prefill_workspace_bytes(const PrefillPlan& p) {
+  // taps, then (several segments) Mstart, Dsum, Phi
+  size_t bytes = align256((size_t)p.B * p.T * p.H * 4 * sizeof(float));
+  if (p.nseg > 1) {
+    const size_t st = (size_t)p.B * p.H * p.nseg;
+    bytes += 2 * align256(st * p.dk * p.dv * sizeof(float));
+    bytes += align256(st * p.dk * p.dk * sizeof(float));
+  }
+  return bytes;
+}
+
+template <int DK, int DV, typename IO, typename OP, typename OUT>
+static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
+  const dim3 blk(NTHR);
+  if (p.nseg > 1) {
+    chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
+    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(p.H, p.nseg, a.S0, a.Dsum, a.Phi,
+                                                                               const_cast<float*>(a.Mstart));
+  }
+  chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, typename IO, typename OP>
+static hipError_t run_prefill_out(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
+  return p.out == IO_F32 ? run_prefill<DK, DV, IO, OP, float>(p, a, stream)
+                         : run_prefill<DK, DV, IO, OP, bf16_t>(p, a, stream);
+}
+
+#define JB_PREFILL_BF16_CASES(X) \
+  X(32, 64) X(32, 128) X(32, 256) X(64, 64) X(64, 128) X(64, 256) \
+  X(96, 64) X(96, 128) X(96, 256) X(128, 64) X(128, 128) X(128, 256)
+#define JB_PREFILL_F32_CASES(X) X(32, 64) X(64, 64)
+
+bool prefill_supported(const PrefillPlan& p) {
+#define CASE(DK_, DV_) if (p.dk == DK_ && p.dv == DV_) return true;
+  if (p.io == IO_BF16) { JB_PREFILL_BF16_CASES(CASE) }
+  else { JB_PREFILL_F32_CASES(CASE) }
+#undef CASE
+  return false;
+}
+
+hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const float* taps,
+                          const void* conv_in, const float* S0, void* o, float* S_final,
+                          void* workspace, hipStream_t stream) {
+  if (p.nchunks == 0) return hipSuccess;
+  ChunkArgs a{};
+  a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
+  a.S0 = S0; a.o = o; a.S_final = S_final;
+  if (p.nseg > 1) {
+    char* ws = static_cast<char*>(workspace) + align256((size_t)p.B * p.T * p.H * 4 * sizeof(float));
+    const size_t st = (size_t)p.B * p.H * p.nseg;
+    a.Mstart = reinterpret_cast<float*>(ws);
+    ws += align256(st * p.dk * p.dv * sizeof(float));
+    a.Dsum = reinterpret_cast<float*>(ws);
+    ws += align256(st * p.dk * p.dv * sizeof(float));
+    a.Phi = reinterpret_cast<float*>(ws);
+  }
+#define CASE(DK_, DV_) \
+  if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16>(p, a, stream);
+  if (p.io == IO_BF16) { JB_PREFILL_BF16_CASES(CASE) }
+#undef CASE
+#define CASE(DK_, DV_) \
+  if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, float, float>(p, a, stream);
+  if (p.io == IO_F32) { JB_PREFILL_F32_CASES(CASE) }
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prologue(int io, int B, int T, int H, int dk, const void* q, const void* k,
+                           const float* alpha, float* qhat, float* khat, float* g, hipStream_t stream) {
+  const int nch = (T + C - 1) / C;
+  if (nch == 0 || B == 0) return hipSuccess;
+  const dim3 grid(nch, H, B), blk(NTHR);
+#define CASE(DK_)                                                                                   \
+  if (dk == DK_) {                                                                                  \
+    if (io == IO_BF16)                                                                              \
+      prologue_kernel<DK_, bf16_t><<<grid, blk, 0, stream>>>(T, H, (const bf16_t*)q, (const bf16_t*)k, \
+                                                             alpha, qhat, khat, g);                 \
+    else                                                                                            \
+      prologue_kernel<DK_, float><<<grid, blk, 0, stream>>>(T, H, (const float*)q, (const float*)k, \
+                                                            alpha, qhat, khat, g);                  \
+    return hipGetLastError();                                                                       \
+  }
+  CASE(32) CASE(64) CASE(96) CASE(128)
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace jb

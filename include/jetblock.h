@@ -1,0 +1,204 @@
+/*
+ * jetblock.h -- C ABI of libjetblock, the JetBlock token mixer on one AMD
+ * MI355X (gfx950).
+ *
+ * The block (Jet-Nemotron paper, Chinese translation on csdn, section 2.4
+ * "new attention block design"; parameters from the xugj520 blog, section
+ * 2.2): a kernel generator that shares the Q/K/V projections' input x
+ * (Linear -> SiLU -> Linear, hidden width 32) emits 4 causal conv taps per
+ * head for every token; the taps convolve the value tokens only (no static
+ * conv on Q or K); Gated DeltaNet mixes time.  With L2-normalised q, k and
+ * the convolved value v':
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v'_t k_t^T,   o_t = S_t q_t
+ *
+ * The library stores the state transposed, M = S^T, as [dk][dv] with dv
+ * contiguous ("dk x dv fp32 state per head").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer owned by the caller,
+ *     contiguous, row-major in the layout given, and 16-byte aligned (alpha
+ *     and beta: 4-byte aligned).  The library never allocates, frees or keeps
+ *     a pointer after a call returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  Inputs must stay valid until the work completes.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     an error nothing is written, a status is returned and jb_last_error()
+ *     names the offending argument.  No exception crosses the ABI.
+ *     JB_ERR_HIP reports a failed launch (hipGetLastError after enqueue).
+ *   - I/O dtype (shape.io_dtype) applies to x, q, k, v, W1, b1, W2, b2 and
+ *     the conv cache: JB_BF16 (bfloat16) or JB_F32.  alpha, beta, the state
+ *     and the taps are always float32.  o is shape.out_dtype.
+ *   - JB_F32 I/O selects the all-fp32 arithmetic mode (fp32 MFMA); JB_BF16
+ *     I/O selects fp16-operand MFMA with fp32 accumulation and fp32 state.
+ *
+ * Layouts (B sequences, T tokens, H heads, K = taps = 4, G = gen_hidden = 32)
+ *   x        [B][T][d_model]         q, k   [B][T][H][dk]
+ *   v        [B][T][H][dv]           alpha, beta [B][T][H]  (float32)
+ *   W1       [G][d_model]            b1     [G]          (nullable)
+ *   W2       [H*K][G]  row h*K+j is tap j of head h;  b2 [H*K] (nullable)
+ *   taps     [B][T][H][K] float32, tap j multiplies v_{t-(K-1)+j} (j = K-1
+ *            is the current token)
+ *   S0, S_final, decode state  [B][H][dk][dv] float32 (M = S^T)
+ *   conv cache [B][K-1][H][dv], the last K-1 raw value rows, oldest first
+ *   o        [B][T][H][dv]
+ *
+ * Supported shapes: dk in {32, 64, 96, 128}; dv in {64, 128, 256};
+ * gen_hidden == 32; taps == 4; chunk == 64 (0 selects 64); d_model a
+ * positive multiple of 128; B >= 1; T >= 0 for prefill, T == 1 for decode.
+ * The all-fp32 mode of jb_prefill additionally needs dk*dv <= 64*64 (its
+ * tiles must fit in the 160 KB of LDS of one compute unit).
+ */
+#ifndef JETBLOCK_H
+#define JETBLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JB_OK = 0,
+  JB_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment */
+  JB_ERR_UNSUPPORTED = 2,  /* valid but not built: shape or dtype combination */
+  JB_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  JB_ERR_HIP = 4           /* the HIP runtime reported an error on launch */
+} jb_status;
+
+typedef enum { JB_BF16 = 0, JB_F32 = 1 } jb_dtype;
+
+typedef struct {
+  int32_t B, T, H, dk, dv, d_model;
+  int32_t gen_hidden;   /* must be 32 */
+  int32_t taps;         /* must be 4 */
+  int32_t chunk;        /* 0 or 64 */
+  int32_t io_dtype;     /* jb_dtype of x, q, k, v, W1, b1, W2, b2, conv cache */
+  int32_t out_dtype;    /* jb_dtype of o */
+  int32_t flags;        /* 0, or JB_FLAG_SEGMENT(n) (jb_prefill only) */
+} jb_shape;
+
+/* Tuning knob for jb_prefill: split each sequence into segments of exactly
+ * n chunks (1 <= n <= 65535) instead of the automatic choice.  Results agree
+ * with any other segmentation up to rounding. */
+#define JB_FLAG_SEGMENT(n) ((int32_t)(((uint32_t)(n) & 0xffffu) << 8))
+
+/* Human-readable name of a status code (static string). */
+const char* jb_status_string(jb_status status);
+
+/* Message describing the last error raised on the calling thread ("" if
+ * none).  The string stays valid until the next call on that thread. */
+const char* jb_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t jb_version(void);
+
+/*
+ * Workspace bytes jb_prefill needs for `shape` (device memory, 256-byte
+ * aligned, contents ignored on entry).  Writes *bytes; returns JB_OK or a
+ * validation error.
+ */
+jb_status jb_prefill_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_prefill -- run the block over B sequences of T tokens.
+ *
+ * Computes, for every sequence and head, the generator taps from x
+ * (csdn section 2.4: Linear, SiLU, Linear emitting conv-kernel weights), the
+ * dynamic causal conv of v with those taps (rows before the start come from
+ * conv_in, or are zero when conv_in is NULL), and the gated delta-rule
+ * recurrence above from S0 (zero when NULL), writing every o_t and the final
+ * state.  The sequential recurrence is evaluated in chunks of 64 tokens with
+ * a WY/UT intra-chunk transform; long single sequences are split into
+ * segments whose transitions are composed by a scan, so results agree with
+ * the token-by-token definition up to rounding.
+ *
+ * Arguments: x, q, k, v, alpha, beta, W1, W2 required; b1, b2, S0, conv_in
+ * nullable; o required when T > 0; S_final required; conv_out nullable (the
+ * last K-1 raw value rows of [conv_in; v]).  S_final may alias S0 and
+ * conv_out may alias conv_in.  alpha should lie in (0, 1] and beta in
+ * [0, 1]; other values are not rejected but the result is then undefined
+ * in precision.  workspace must hold jb_prefill_workspace_size() bytes.
+ */
+jb_status jb_prefill(const jb_shape* shape, const void* x, const void* q, const void* k,
+                     const void* v, const float* alpha, const float* beta, const void* W1,
+                     const void* b1, const void* W2, const void* b2, const float* S0,
+                     const void* conv_in, void* o, float* S_final, void* conv_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes jb_decode_step needs for `shape` (shape.T must be 1). */
+jb_status jb_decode_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_decode_step -- one token for each of B sequences (shape.T == 1).
+ *
+ * The same block as jb_prefill for a single token: generator taps from x_t,
+ * v' from the conv cache and v_t, then with a = M^T k, c = M^T q (one read
+ * of the state): u = b (v' - alpha a), o_t = alpha c + (k.q) u,
+ * M' = alpha M + k u^T, written to S_out; the cache shifts in the raw v_t.
+ * Decode is bound by the state's HBM traffic (csdn section 2.5, finding 4:
+ * decoding is memory-bandwidth-bound), which this call reads and writes once.
+ *
+ * Layouts: S_in, S_out [B][H][dk][dv] f32 (S_out may alias S_in);
+ * cache_in, cache_out [B][K-1][H][dv] (may alias); x_t [B][d_model];
+ * q_t, k_t [B][H][dk]; v_t [B][H][dv]; alpha_t, beta_t [B][H] f32;
+ * o_t [B][H][dv] (out_dtype).  workspace must hold
+ * jb_decode_workspace_size() bytes.
+ */
+jb_status jb_decode_step(const jb_shape* shape, const float* S_in, float* S_out,
+                         const void* cache_in, void* cache_out, const void* x_t,
+                         const void* q_t, const void* k_t, const void* v_t,
+                         const float* alpha_t, const float* beta_t, const void* W1,
+                         const void* b1, const void* W2, const void* b2, void* o_t,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Single-stage entry points.  Each runs one stage of the path by itself so
+ * that it can be checked on its own; the two calls above fuse these stages.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * jb_gen_taps -- kernel generator (csdn section 2.4; hidden width 32 from
+ * the xugj520 blog, section 2.2) on the B*T rows of x:
+ * taps = W2 SiLU(W1 x + b1) + b2, written as taps [B][T][H][K] float32.
+ */
+jb_status jb_gen_taps(const jb_shape* shape, const void* x, const void* W1, const void* b1,
+                      const void* W2, const void* b2, float* taps, void* stream);
+
+/*
+ * jb_gen_conv -- kernel generator followed by the dynamic causal conv of v
+ * (csdn section 2.4: dynamic kernels applied to the value tokens):
+ * v'_t[h][c] = sum_j taps_t[h][j] v_{t-(K-1)+j}[h][c], rows before the start
+ * from conv_in or zero.  Writes taps (nullable) and vconv [B][T][H][dv]
+ * float32.
+ */
+jb_status jb_gen_conv(const jb_shape* shape, const void* x, const void* W1, const void* b1,
+                      const void* W2, const void* b2, const void* v, const void* conv_in,
+                      float* taps, float* vconv, void* stream);
+
+/*
+ * jb_prologue -- the gate and normalisation stage on its own:
+ * qhat = q (sum q^2 + 1e-6)^(-1/2), khat likewise (float32, [B][T][H][dk]),
+ * and g [B][T][H] float32, the inclusive cumulative sum of ln(alpha) within
+ * each 64-token chunk (the log of the chunk-local decay products).
+ */
+jb_status jb_prologue(const jb_shape* shape, const void* q, const void* k,
+                      const float* alpha, float* qhat, float* khat, float* g, void* stream);
+
+/*
+ * jb_probe_mfma -- runs one 16x16x32 matrix-core product D = A B on one
+ * wavefront with the operand placement the library's kernels assume
+ * (A [16][32], B [32][16], D [16][16], row-major float32 device buffers).
+ * kind 0: fp16 operands in the accumulator-chaining K order; kind 1: bf16
+ * operands in contiguous K order; kind 2: fp32 operands (eight 16x16x4
+ * products).  Operands are rounded to the operand type on load.  Exposed so
+ * that a test can check the placement against a host product.
+ */
+jb_status jb_probe_mfma(int32_t kind, const float* A, const float* B, float* D, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETBLOCK_H */

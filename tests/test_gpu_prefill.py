@@ -1,0 +1,185 @@
+"""GPU parity of jb_prefill against the fp64 oracle, on the named workloads,
+ragged and edge-case sequences, and the invariances the method must keep
+(segmentation, continuation, bf16 output rounding, prefill = decode loop)."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL_BF16, TOL_F32, oracle_prefill, rel_err, to_dev, to_np, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def jb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_jetblock_amd import jetblock
+    return jetblock
+
+
+def _run(jb, p, S0=None, conv_in=None, **kw):
+    d = to_dev(p)
+    r = jb.prefill(d["x"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["W1"], d["W2"],
+                   S0=None if S0 is None else S0.cuda(), conv_in=None if conv_in is None else conv_in.cuda(), **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _check(r, ref, tol, what=""):
+    eo = rel_err(r["o"], ref["o"])
+    es = rel_err(r["S_final"], ref["S_final"])
+    print(f"  {what} o_err={eo:.3e} S_err={es:.3e}", flush=True)
+    assert eo < tol, (what, "o", eo)
+    assert es < tol, (what, "S_final", es)
+
+
+def test_tiny_f32_workload(jb, oracle_mod):
+    """Tiny JetBlock in all-fp32 mode: B=1, T=256, H=2, dk=32, dv=64, d_model=128."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print("tiny f32 T=256", flush=True)
+    p = inputs.prefill_inputs(inputs.TINY_F32, seed=0)
+    ref = oracle_prefill(oracle_mod, p)
+    r = _run(jb, p)
+    _check(r, ref, TOL_F32, "tiny")
+    np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 3, 63, 64, 65, 200])
+def test_ragged_lengths_with_state(jb, oracle_mod, io, T):
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"ragged io={io} T={T}", flush=True)
+    s = inputs.Shape(B=2, T=T, H=2, dk=32, dv=64, d_model=128, io_dtype=io)
+    p = inputs.prefill_inputs(s, seed=T)
+    st = inputs.state_inputs(s, seed=T)
+    ref = oracle_prefill(oracle_mod, p, st["S"], st["cache"])
+    r = _run(jb, p, st["S"], st["cache"])
+    _check(r, ref, TOL_BF16 if io == "bf16" else TOL_F32, f"T={T}")
+    np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (64, 128), (96, 256), (128, 256), (128, 64), (96, 128)])
+def test_head_shapes_bf16(jb, oracle_mod, dk, dv):
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"shape dk={dk} dv={dv}", flush=True)
+    s = inputs.Shape(B=1, T=300, H=3, dk=dk, dv=dv, d_model=256)
+    p = inputs.prefill_inputs(s, seed=dk + dv)
+    st = inputs.state_inputs(s, seed=1)
+    ref = oracle_prefill(oracle_mod, p, st["S"], st["cache"])
+    r = _run(jb, p, st["S"], st["cache"])
+    _check(r, ref, TOL_BF16, f"dk={dk} dv={dv}")
+
+
+def test_jetblock2b_T4096(jb, oracle_mod):
+    """JetBlock 2B shape prefill: B=1, T=4096, H=12, dk=96, dv=256, d_model=1536."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print("2B T=4096", flush=True)
+    p = inputs.prefill_inputs(inputs.B2_T4096, seed=0)
+    ref = oracle_prefill(oracle_mod, p)
+    r = _run(jb, p)
+    _check(r, ref, TOL_BF16, "2B T=4096")
+
+
+@pytest.mark.parametrize("seg", [1, 2, 5, 64])
+def test_segmentation_invariance(jb, oracle_mod, seg):
+    """Any split into segments (1 chunk .. whole sequence) gives the oracle's result."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"segments of {seg} chunks", flush=True)
+    s = inputs.Shape(B=1, T=1000, H=2, dk=96, dv=256, d_model=256)
+    p = inputs.prefill_inputs(s, seed=11, alpha_mean=6.0)
+    st = inputs.state_inputs(s, seed=11)
+    ref = oracle_prefill(oracle_mod, p, st["S"], st["cache"])
+    r = _run(jb, p, st["S"], st["cache"], seg_len=seg)
+    _check(r, ref, TOL_BF16, f"seg={seg}")
+
+
+def test_long_memory_carry(jb, oracle_mod):
+    """alpha ~ sigmoid(N(9,1)), beta ~ sigmoid(N(-3,1)): the state decays little, so a
+    wrong carry between chunks or segments many chunks back shows in the output."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print("long memory T=4096", flush=True)
+    s = inputs.Shape(B=1, T=4096, H=2, dk=96, dv=256, d_model=256)
+    p = inputs.prefill_inputs(s, seed=21, alpha_mean=9.0, beta_mean=-3.0)
+    st = inputs.state_inputs(s, seed=21, state_std=1.0)
+    ref = oracle_prefill(oracle_mod, p, st["S"])
+    for seg in (None, 3):
+        r = _run(jb, p, st["S"], seg_len=seg)
+        _check(r, ref, TOL_BF16, f"long memory seg={seg}")
+
+
+def test_identity_gates_on_gpu(jb):
+    """alpha = 1, beta = 0: the state passes through unchanged (up to the ~2^-22 split-fp16
+    rounding of the segment scan) and o_t = S0^T qhat_t."""
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=1, T=130, H=2, dk=64, dv=128, d_model=128)
+    p = inputs.prefill_inputs(s, seed=2)
+    p["alpha"][:] = 1.0
+    p["beta"][:] = 0.0
+    st = inputs.state_inputs(s, seed=2)
+    r = _run(jb, p, st["S"])
+    assert rel_err(r["S_final"], to_np(st["S"])) < 1e-6
+    qh = to_np(p["q"]).astype(np.float64)
+    qh /= np.sqrt((qh * qh).sum(-1, keepdims=True) + 1e-6)
+    want = np.einsum("bthk,bhkv->bthv", qh, to_np(st["S"]).astype(np.float64))
+    assert rel_err(r["o"], want) < TOL_BF16
+
+
+def test_bf16_output_is_rounded_f32_output(jb):
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=1, T=500, H=2, dk=96, dv=256, d_model=256)
+    p = inputs.prefill_inputs(s, seed=8)
+    r32 = _run(jb, p)
+    r16 = _run(jb, p, out_dtype=torch.bfloat16)
+    assert r16["o"].dtype == torch.bfloat16
+    assert torch.equal(r16["o"].view(torch.int16), r32["o"].to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(r16["S_final"], r32["S_final"])
+
+
+def test_split_prefill_equals_full(jb, oracle_mod):
+    """Prefill [0, T1) then [T1, T) from (S_final, conv_out) = one prefill (continuation)."""
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=2, T=400, H=3, dk=64, dv=128, d_model=256)
+    p = inputs.prefill_inputs(s, seed=9)
+    ref = oracle_prefill(oracle_mod, p)
+    T1 = 150
+    pa = {k: (v[:, :T1].contiguous() if k in ("x", "q", "k", "v", "alpha", "beta") else v) for k, v in p.items()}
+    pb = {k: (v[:, T1:].contiguous() if k in ("x", "q", "k", "v", "alpha", "beta") else v) for k, v in p.items()}
+    ra = _run(jb, pa)
+    rb = _run(jb, pb, ra["S_final"].cpu(), ra["conv_out"].cpu())
+    o = torch.cat([ra["o"], rb["o"]], dim=1)
+    assert rel_err(o, ref["o"]) < TOL_BF16
+    assert rel_err(rb["S_final"], ref["S_final"]) < TOL_BF16
+
+
+def test_empty_sequence_passes_state(jb):
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=2, T=0, H=2, dk=32, dv=64, d_model=128)
+    p = inputs.prefill_inputs(s, seed=1)
+    st = inputs.state_inputs(s, seed=1)
+    r = _run(jb, p, st["S"], st["cache"])
+    assert torch.equal(r["S_final"].cpu(), st["S"])
+    assert torch.equal(r["conv_out"].cpu(), st["cache"])
+    r0 = _run(jb, p)
+    assert torch.count_nonzero(r0["S_final"]) == 0
+
+
+@pytest.mark.parametrize("case", ["tiny_alpha", "beta_one", "same_keys", "big_v"])
+def test_edge_values(jb, oracle_mod, case):
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"edge {case}", flush=True)
+    s = inputs.Shape(B=1, T=200, H=2, dk=64, dv=128, d_model=128)
+    p = inputs.prefill_inputs(s, seed=13)
+    if case == "tiny_alpha":
+        p["alpha"][:, ::7] = 1e-20
+    elif case == "beta_one":
+        p["beta"][:] = 1.0
+        p["alpha"][:] = 1.0
+    elif case == "same_keys":
+        p["k"][:, 64:128] = p["k"][:, 64:65]
+        p["beta"][:, 64:128] = 1.0
+    elif case == "big_v":
+        p["v"] = (p["v"].float() * 1000).to(p["v"].dtype)
+    ref = oracle_prefill(oracle_mod, p)
+    r = _run(jb, p)
+    _check(r, ref, TOL_BF16, case)
