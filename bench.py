@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of the JetBlock hot path (libjetblock) on one MI355X.
+
+One step = one JetBlock-2B-shape prefill of a 65,536-token sequence (B=1,
+H=12, dk=96, dv=256, d_model=1536, chunk 64) followed by 128 decode steps
+for 256 sequences of the same shape from seeded fp32 states.  Inputs are
+seeded synthetic tensors already resident in HBM.  value = tokens processed
+per second over the whole step (65,536 prefill + 32,768 decode tokens).
+
+The decode step inside the timed loop is the two launches jb_decode_step
+makes (jb_gen_taps on x_t, then jb_decode_update); HIP events on the
+launching stream bracket every jb_prefill call and every state-update launch,
+which gives the per-kernel averages the roofline figures use.
+
+Prints one JSON line on stdout; progress goes to stderr.
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2b|4b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 matrix peak, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops_per_token(s) -> float:
+    """Algorithmic flops per token of the chunked prefill (C = 64):
+    H (6 C dk + 4 C dv + 6 dk dv) + 2 D G + 2 G 4H + 8 H dv."""
+    C, G = 64, 32
+    return (s.H * (6 * C * s.dk + 4 * C * s.dv + 6 * s.dk * s.dv) + 2 * s.d_model * G + 2 * G * 4 * s.H
+            + 8 * s.H * s.dv)
+
+
+def prefill_bytes_per_token(s, out_bytes: int) -> float:
+    """Compulsory HBM bytes per token: x, q, k, v (bf16), alpha, beta (f32), o."""
+    return 2 * s.d_model + 2 * 2 * s.H * s.dk + 2 * s.H * s.dv + 8 * s.H + out_bytes * s.H * s.dv
+
+
+def decode_update_bytes_per_unit(s, out_bytes: int) -> float:
+    """Compulsory bytes of the decode state update per (sequence, head): fp32 state read
+    and written once, q, k, v_t, the 3-row cache read and written, alpha, beta, 4 taps, o."""
+    return (2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * s.dv * 2 + 8 + 16 + s.dv * out_bytes)
+
+
+def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
+    """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
+    import oracle
+    from gated_delta_rule_jetblock_amd import inputs
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    tp = budget_tokens
+    ps = shape_p.with_(T=tp)
+    p = inputs.prefill_inputs(ps, seed=0)
+    f = lambda t: t.float().numpy()
+    args = [f(p[k]) for k in ("x", "q", "k", "v", "alpha", "beta", "W1", "W2")]
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.prefill(*args, nthreads=threads)
+    t_pre = time.perf_counter() - t0
+    dsteps = 4
+    d = inputs.decode_inputs(shape_d, steps=dsteps, seed=0)
+    S, c = f(d["S"]), f(d["cache"])
+    t0 = time.perf_counter()
+    for t in range(dsteps):
+        r = oracle.decode_step(S, c, *(f(d[k][t]) for k in ("x", "q", "k", "v", "alpha", "beta")), f(d["W1"]),
+                               f(d["W2"]), nthreads=threads)
+        S, c = r["S"].astype("float32"), r["cache"]
+    t_dec = time.perf_counter() - t0
+    pre_rate = tp / t_pre
+    dec_rate = shape_d.B * dsteps / t_dec
+    step_s = prefill_tokens_per_step / pre_rate + decode_tokens_per_step / dec_rate
+    return dict(value=(prefill_tokens_per_step + decode_tokens_per_step) / step_s, unit="tokens/s", cores=threads,
+                kind="oracle",
+                sample=f"fp64 oracle: prefill of {tp} tokens (all {shape_p.H} heads) in {t_pre:.2f} s and "
+                       f"{dsteps} decode steps x {shape_d.B} sequences in {t_dec:.2f} s, scaled to one step",
+                prefill_tokens_per_s=pre_rate, decode_tokens_per_s=dec_rate)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=["2b", "4b"], default="2b")
+    ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_jetblock_amd import inputs, jetblock as jb
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "2b":
+        sp, sd = inputs.B2_T65536, inputs.B2_DECODE
+        wname = "JetBlock-2B shape: prefill B=1 T=65536 + decode B=256 x 128 steps"
+    else:
+        sp, sd = inputs.B4_T262144, inputs.B4_DECODE
+        wname = "JetBlock-4B shape: prefill B=1 T=262144 + decode B=128 x 128 steps"
+    out_dt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    out_bytes = 2 if args.out_dtype == "bf16" else 4
+    nsteps_dec = args.decode_steps
+
+    log(f"generating inputs on {dev} ...")
+    p = inputs.prefill_inputs(sp, seed=0, device=dev)
+    d = inputs.decode_inputs(sd, steps=nsteps_dec, seed=1, device=dev)
+    o = torch.empty((sp.B, sp.T, sp.H, sp.dv), dtype=out_dt, device=dev)
+    S_fin = torch.empty((sp.B, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+    conv_out = torch.empty((sp.B, 3, sp.H, sp.dv), dtype=torch.bfloat16, device=dev)
+    shp = jb.make_shape(sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.d_model, jb.JB_BF16,
+                        jb.JB_BF16 if out_dt == torch.bfloat16 else jb.JB_F32)
+    ws = jb.workspace(jb.prefill_workspace_size(shp), dev)
+    S = d["S"]
+    cache = d["cache"]
+    taps = torch.empty((sd.B, sd.H, 4), dtype=torch.float32, device=dev)
+    od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev_pre = []
+    ev_dec = []
+
+    def one_step(record: bool):
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        jb.prefill(p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"], p["W2"], out_dtype=out_dt,
+                   o=o, S_final=S_fin, conv_out=conv_out, ws=ws, stream=stream)
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            ev_pre.append((e0, e1))
+        for t in range(nsteps_dec):
+            jb.gen_taps(d["x"][t].view(sd.B, 1, sd.d_model), d["W1"], d["W2"], H=sd.H, out=taps, stream=stream)
+            if record:
+                a0 = torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+            jb.decode_update(S, cache, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], taps,
+                             d_model=sd.d_model, out_dtype=out_dt, o=od, stream=stream)
+            if record:
+                a1 = torch.cuda.Event(enable_timing=True)
+                a1.record(stream)
+                ev_dec.append((a0, a1))
+
+    log(f"warmup {args.warmup} steps ...")
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps ...")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        one_step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    pre_ms = sum(a.elapsed_time(b) for a, b in ev_pre) / len(ev_pre)
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev_dec) / len(ev_dec)
+    log(f"step {ms_step:.3f} ms: prefill {pre_ms:.3f} ms, decode update {dec_ms * 1e3:.1f} us x {nsteps_dec}")
+
+    tok_pre = sp.B * sp.T
+    tok_dec = sd.B * nsteps_dec
+    value = (tok_pre + tok_dec) / (ms_step * 1e-3)
+
+    # decode state update: the dominant kernel of the step
+    dec_bytes = decode_update_bytes_per_unit(sd, out_bytes) * sd.B * sd.H
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    roof = dict(kernel="decode_kernel (jb_decode_update)", bound="hbm", achieved=round(dec_gbs, 1),
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(dec_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                bytes_per_launch=dec_bytes, avg_launch_us=round(dec_ms * 1e3, 2))
+    pre_flops = prefill_flops_per_token(sp) * tok_pre
+    pre_tf = pre_flops / (pre_ms * 1e-3) / 1e12
+    pre_gbs = prefill_bytes_per_token(sp, out_bytes) * tok_pre / (pre_ms * 1e-3) / 1e9
+    roof_pre = dict(call="jb_prefill (generator, summary, scan, output kernels)", bound="mfma",
+                    achieved=round(pre_tf, 2), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4), hbm_GBs=round(pre_gbs, 1),
+                    hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4), flops_per_call=pre_flops,
+                    avg_call_ms=round(pre_ms, 4))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(sp, sd, tok_pre, tok_dec, args.cpu_tokens)
+        log(f"cpu oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "JetBlock tokens/s: prefill @T=64K (%MFMA peak) + decode B=256 (%HBM peak)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 I/O; fp16 MFMA operands, fp32 accumulate and state" if args.out_dtype == "bf16"
+        else "bf16 inputs, fp32 o; fp16 MFMA operands, fp32 accumulate and state",
+        "data": "synthetic (seeded)",
+        "config": {"workload": wname,
+                   "prefill": dict(B=sp.B, T=sp.T, H=sp.H, dk=sp.dk, dv=sp.dv, d_model=sp.d_model, chunk=64,
+                                   out=args.out_dtype),
+                   "decode": dict(B=sd.B, steps=nsteps_dec, H=sd.H, dk=sd.dk, dv=sd.dv, d_model=sd.d_model)},
+        "prefill": dict(tokens_per_s=round(tok_pre / (pre_ms * 1e-3), 1), ms=round(pre_ms, 4),
+                        mfma_frac=roof_pre["frac"], hbm_frac=roof_pre["hbm_frac"]),
+        "decode": dict(tokens_per_s=round(tok_dec / (dec_ms * nsteps_dec * 1e-3), 1),
+                       update_us=round(dec_ms * 1e3, 2), hbm_frac=roof["frac"]),
+        "roofline": roof,
+        "roofline_prefill": roof_pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -197,6 +197,22 @@ jb_status jb_decode_step(const jb_shape* s, const float* S_in, float* S_out, con
   return hip_status(fn, e);
 }
 
+jb_status jb_decode_update(const jb_shape* s, const float* S_in, float* S_out, const void* cache_in, void* cache_out,
+                           const void* q_t, const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
+                           const float* taps, void* o_t, void* stream) {
+  const char* fn = "jb_decode_update";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (!jb::decode_supported(s->dk, s->dv)) return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built", fn, s->dk, s->dv);
+  JB_REQUIRE_PTR(S_in); JB_REQUIRE_PTR(S_out); JB_REQUIRE_PTR(cache_in); JB_REQUIRE_PTR(cache_out);
+  JB_REQUIRE_PTR(q_t); JB_REQUIRE_PTR(k_t); JB_REQUIRE_PTR(v_t); JB_REQUIRE_SCALARS(alpha_t);
+  JB_REQUIRE_SCALARS(beta_t); JB_REQUIRE_PTR(taps); JB_REQUIRE_PTR(o_t);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  return hip_status(fn, jb::launch_decode(io, out, s->B, s->H, s->dk, s->dv, S_in, S_out, cache_in, cache_out, q_t,
+                                          k_t, v_t, alpha_t, beta_t, taps, o_t, static_cast<hipStream_t>(stream)));
+}
+
 jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
                       float* taps, void* stream) {
   const char* fn = "jb_gen_taps";

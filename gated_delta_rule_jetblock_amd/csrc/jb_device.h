@@ -100,6 +100,20 @@ __device__ __forceinline__ Frag<OP> acc_frag(const f4_t& lo, const f4_t& hi) {
 
 __device__ __forceinline__ f4_t zero4() { return f4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// ----------------------------------------------------------- buffer stores
+// A raw buffer resource over [base, base + bytes): stores beyond the range
+// are dropped by the hardware.  Offsets are a per-lane 32-bit VGPR plus a
+// wave-uniform SGPR, so a run of stores shares one address register.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, float v, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);  // bits, not a conversion
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, bf16_t v, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+}
+
 // ----------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ float wave_sum(float v) {

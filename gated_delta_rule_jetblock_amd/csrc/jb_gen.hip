@@ -16,7 +16,6 @@
 namespace jb {
 
 constexpr int G = 32;        // generator hidden width
-constexpr int GEN_THR = 256; // 4 waves, each takes a quarter of d_model
 constexpr int MAX_HK = 128;  // up to 32 heads
 
 // Fragment of 8 contiguous K values (order 8g + j) straight from memory.
@@ -48,13 +47,16 @@ template <> struct GenFrag<float> {
   }
 };
 
-// One workgroup: 16*NT tokens.  hidden^T (32 x tokens) = W1 (32 x D) x^T;
-// wave w accumulates K range [w D/4, (w+1) D/4) and the partials meet in LDS.
-template <typename IO, int NT>
-__global__ __launch_bounds__(GEN_THR) void gen_kernel(int64_t n, int D, int HK, const IO* x, const IO* W1,
+// One workgroup: 16*NT tokens, NW wavefronts.  hidden^T (32 x tokens) =
+// W1 (32 x D) x^T; wave w accumulates the K range [w D/NW, (w+1) D/NW) and
+// the partials meet in LDS.  Few tokens per workgroup (decode) use many waves
+// so that each wave's chain of dependent loads stays short.
+template <typename IO, int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, const IO* x, const IO* W1,
                                                       const IO* b1, const IO* W2, const IO* b2, float* taps) {
   constexpr int NTOK = 16 * NT;
-  __shared__ float red[4][G][NTOK];
+  constexpr int NTHREADS = NW * 64;
+  __shared__ float red[NW][G][NTOK];
   __shared__ float hid[NTOK][G + 1];
   __shared__ float w2s[MAX_HK][G + 1];
   __shared__ float b2s[MAX_HK];
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(GEN_THR) void gen_kernel(int64_t n, int D, int HK, 
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[u][t] = zero4();
 
-  const int kq = D / 4;
+  const int kq = D / NW;
+#pragma unroll 4
   for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 32) {
     GenFrag<IO> A[2], Bt[NT];
 #pragma unroll
@@ -91,17 +94,19 @@ __global__ __launch_bounds__(GEN_THR) void gen_kernel(int64_t n, int D, int HK, 
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][u * 16 + 4 * g4 + i][t * 16 + m16] = acc[u][t][i];
-  for (int e = tid; e < HK * G; e += GEN_THR) w2s[e / G][e % G] = to_f32<IO>(W2[e]);
-  for (int e = tid; e < HK; e += GEN_THR) b2s[e] = b2 ? to_f32<IO>(b2[e]) : 0.f;
+  for (int e = tid; e < HK * G; e += NTHREADS) w2s[e / G][e % G] = to_f32<IO>(W2[e]);
+  for (int e = tid; e < HK; e += NTHREADS) b2s[e] = b2 ? to_f32<IO>(b2[e]) : 0.f;
   __syncthreads();
-  for (int e = tid; e < G * NTOK; e += GEN_THR) {
+  for (int e = tid; e < G * NTOK; e += NTHREADS) {
     const int u = e / NTOK, t = e % NTOK;
-    float hsum = red[0][u][t] + red[1][u][t] + red[2][u][t] + red[3][u][t];
+    float hsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) hsum += red[w][u][t];
     if (b1) hsum += to_f32<IO>(b1[u]);
     hid[t][u] = hsum / (1.0f + expf(-hsum));  // SiLU
   }
   __syncthreads();
-  for (int e = tid; e < NTOK * HK; e += GEN_THR) {
+  for (int e = tid; e < NTOK * HK; e += NTHREADS) {
     const int t = e / HK, r = e % HK;
     const int64_t tok = n0 + t;
     if (tok >= n) continue;
@@ -112,28 +117,33 @@ __global__ __launch_bounds__(GEN_THR) void gen_kernel(int64_t n, int D, int HK, 
   }
 }
 
+template <typename IO, int NT, int NW>
+static void gen_launch(int64_t n, int D, int HK, const void* x, const void* W1, const void* b1, const void* W2,
+                       const void* b2, float* taps, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)));
+  gen_kernel<IO, NT, NW><<<grid, NW * 64, 0, stream>>>(n, D, HK, (const IO*)x, (const IO*)W1, (const IO*)b1,
+                                                      (const IO*)W2, (const IO*)b2, taps);
+}
+
+template <typename IO>
+static void gen_dispatch(int64_t n, int D, int HK, const void* x, const void* W1, const void* b1, const void* W2,
+                         const void* b2, float* taps, hipStream_t stream) {
+  // few rows (decode): 16 tokens per workgroup over as many waves as d_model
+  // allows, to spread the rows; many rows: 64 tokens per workgroup, 4 waves
+  if (n <= 4096) {
+    if ((D / 32) % 16 == 0) gen_launch<IO, 1, 16>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+    else if ((D / 32) % 8 == 0) gen_launch<IO, 1, 8>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+    else gen_launch<IO, 1, 4>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+  } else {
+    gen_launch<IO, 4, 4>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+  }
+}
+
 hipError_t launch_gen_taps(int io, int64_t n, int D, int H, const void* x, const void* W1, const void* b1,
                            const void* W2, const void* b2, float* taps, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int HK = 4 * H;
-  // few rows (decode): 16 tokens per workgroup to spread the rows; else 64
-  if (n <= 4096) {
-    const dim3 grid((unsigned)((n + 15) / 16));
-    if (io == IO_BF16)
-      gen_kernel<bf16_t, 1><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const bf16_t*)x, (const bf16_t*)W1,
-                                                         (const bf16_t*)b1, (const bf16_t*)W2, (const bf16_t*)b2, taps);
-    else
-      gen_kernel<float, 1><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const float*)x, (const float*)W1,
-                                                        (const float*)b1, (const float*)W2, (const float*)b2, taps);
-  } else {
-    const dim3 grid((unsigned)((n + 63) / 64));
-    if (io == IO_BF16)
-      gen_kernel<bf16_t, 4><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const bf16_t*)x, (const bf16_t*)W1,
-                                                         (const bf16_t*)b1, (const bf16_t*)W2, (const bf16_t*)b2, taps);
-    else
-      gen_kernel<float, 4><<<grid, GEN_THR, 0, stream>>>(n, D, HK, (const float*)x, (const float*)W1,
-                                                        (const float*)b1, (const float*)W2, (const float*)b2, taps);
-  }
+  if (io == IO_BF16) gen_dispatch<bf16_t>(n, D, 4 * H, x, W1, b1, W2, b2, taps, stream);
+  else gen_dispatch<float>(n, D, 4 * H, x, W1, b1, W2, b2, taps, stream);
   return hipGetLastError();
 }
 

@@ -5,9 +5,8 @@
 //     M_t = a_t (I - b_t k_t k_t^T) M_{t-1} + b_t k_t v'_t^T,   o_t = M_t^T q_t
 // with L2-normalised q, k.  Within a chunk of C = 64 tokens entering with M0
 // (local index i, g_i = sum_{j<=i} ln a_j, gamma_i = e^{g_i}):
-//     A_ij = b_i e^{g_i - g_j} k_i.k_j (j < i),   X = (I + A)^{-1}
-//     T1 = X diag(b),  T2 = X diag(b gamma)
-//     W = T2 K,  U0 = T1 V'                                   (WY/UT form)
+//     A_ij = b_i e^{g_i - g_j} k_i.k_j (j < i)
+//     W = (I + A)^{-1} diag(b gamma) K,  U0 = (I + A)^{-1} diag(b) V'   (WY/UT form)
 //     V_new = U0 - W M0
 //     O = diag(gamma) Q M0 + P V_new,  P_ij = e^{g_i - g_j} q_i.k_j (j <= i)
 //     M_C = gamma_C M0 + K^T diag(e^{g_C - g}) V_new
@@ -26,10 +25,15 @@
 // the normal range), fp32 operands in the all-fp32 mode.  The state and every
 // accumulator stay fp32; scalars (norms, gates) are applied in fp32.
 //
-// Workgroup: 8 wavefronts.  Chunk-shared tiles (K, K^T, Q, A, X, T1, T2, W,
-// P, the value rows with their 3-row conv halo) live in LDS; each wave owns
-// whole 16-column tiles of the state and keeps them in accumulator registers
-// for the whole segment, so the state never leaves the compute unit.
+// Workgroup: 16 wavefronts.  Chunk-shared tiles (K, K^T, Q, -A, the diagonal
+// blocks of A and their inverses, -W, P, the value rows with their 3-row conv
+// halo) live in LDS; each wave owns whole 16-column tiles of the state and
+// keeps them in accumulator registers for the whole segment, so the state
+// never leaves the compute unit.  (I + A)^{-1} is never formed: only its four
+// 16x16 diagonal blocks are inverted (fp32, forward substitution), and every
+// wave applies a blocked forward substitution on the matrix cores to its own
+// right-hand sides (its columns of diag(b) V', and one column tile of
+// diag(b gamma) K for the W tiles).
 #include "jb_device.h"
 #include "jb_internal.h"
 
@@ -38,6 +42,8 @@ namespace jb {
 constexpr int C = 64;        // chunk length
 constexpr int NWAVE = 8;     // wavefronts per chunk workgroup
 constexpr int NTHR = NWAVE * WAVE;
+constexpr int PRO_THR = 512; // threads of the prologue mapping: 64 rows x 8 parts
+constexpr int GATE_WAVE = 7; // the wave that loads and scans the gates
 constexpr int NCU = 256;     // compute units of one MI355X
 
 enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1 };
@@ -60,30 +66,45 @@ struct ChunkArgs {
 };
 
 // ------------------------------------------------------------ LDS layout
+//
+// Every tile row is padded by 4 elements: a fragment read has the 16 lanes of
+// a lane group walk 16 rows at one column, and an unpadded 128- or 192-byte
+// row stride would put all of them in one or two LDS banks.  With the pad the
+// row stride is 2 (mod 4) dwords for fp16 and 4 (mod 8) dwords for fp32
+// tiles, so the lanes of a group spread over distinct banks.
 
 template <int DK, int DV, typename IO, typename OP, int MODE>
 struct Lds {
-  static constexpr int szKh = C * DK * (int)sizeof(OP);
-  static constexpr int szQh = MODE == MODE_OUTPUT ? C * DK * (int)sizeof(OP) : 0;
-  static constexpr int szV = (C + 3) * DV * (int)sizeof(IO);
+  static constexpr int LDK = DK + 4;                     // [C][DK] tiles
+  static constexpr int LC = C + 4;                       // [*][C] tiles
+  static constexpr int LVB = DV * (int)sizeof(IO) + 16;  // bytes per value row
+  static constexpr int LAD = 16 + 4;                     // fp32 diagonal blocks of A
+  static constexpr int LLI = 32 + 4;                     // diagonal-block inverses (cols 16..31 zero)
+  static constexpr int szKh = C * LDK * (int)sizeof(OP);
+  static constexpr int szKt = DK * LC * (int)sizeof(OP);
+  static constexpr int szQh = MODE == MODE_OUTPUT ? C * LDK * (int)sizeof(OP) : 0;
+  static constexpr int szV = (C + 3) * LVB;
   static constexpr int szTap = C * 4 * 4;
   static constexpr int szScal = 4 * C * 4;
-  static constexpr int szA = C * C * 4 > C * DK * (int)sizeof(OP) ? C * C * 4 : C * DK * (int)sizeof(OP);
-  static constexpr int szX = C * C * 4;
-  static constexpr int szT = 2 * C * C * (int)sizeof(OP) > 3 * 256 * 4 ? 2 * C * C * (int)sizeof(OP) : 3 * 256 * 4;
-  static constexpr int szP = MODE == MODE_OUTPUT ? C * C * (int)sizeof(OP) : 0;
+  static constexpr int szW = C * LDK * (int)sizeof(OP);
+  static constexpr int szAn = C * LC * (int)sizeof(OP);
+  static constexpr int szAd = C * LAD * 4;
+  static constexpr int szLi = C * LLI * (int)sizeof(OP);
+  static constexpr int szP = MODE == MODE_OUTPUT ? C * LC * (int)sizeof(OP) : 0;
 
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int oKh = 0;
-  static constexpr int oKt = oKh + szKh;
-  static constexpr int oQh = oKt + szKh;
-  static constexpr int oV = oQh + szQh;
-  static constexpr int oTap = oV + ((szV + 15) / 16) * 16;
-  static constexpr int oScal = oTap + szTap;
-  static constexpr int oA = oScal + szScal;   // A (f32), later W (OP)
-  static constexpr int oX = oA + szA;
-  static constexpr int oT = oX + szX;         // T1, T2 (OP); Y scratch (f32) before them
-  static constexpr int oP = oT + szT;
-  static constexpr int total = oP + szP;
+  static constexpr int oKt = a16(oKh + szKh);
+  static constexpr int oQh = a16(oKt + szKt);
+  static constexpr int oV = a16(oQh + szQh);
+  static constexpr int oTap = a16(oV + szV);
+  static constexpr int oScal = a16(oTap + szTap);
+  static constexpr int oW = a16(oScal + szScal);
+  static constexpr int oAn = a16(oW + szW);
+  static constexpr int oAd = a16(oAn + szAn);
+  static constexpr int oLi = a16(oAd + szAd);
+  static constexpr int oP = a16(oLi + szLi);
+  static constexpr int total = a16(oP + szP);
 };
 
 // kind-of-tile tables for the lower-triangular 4x4 tile grid of a chunk
@@ -116,47 +137,72 @@ __device__ __forceinline__ void load_row_part<float>(const float* src, float* ds
   }
 }
 
-// The gate and normalisation prologue for one chunk, as the 512 threads of a
-// chunk workgroup execute it: thread (row = tid/8, part = tid%8) normalises
-// DK/8 elements of q and k for token t0 + row; wave 0 additionally scans the
-// log-gates.  Rows at or beyond `n` (ragged tail) are neutral tokens: q = k =
-// 0, a = 1, b = 0.  Results are handed to the caller's sinks.
+// The normalisation part of the prologue for one chunk, as the first 512
+// threads of a workgroup execute it: thread (row = tid/8, part = tid%8)
+// handles DK/8 elements of q and k for token t0 + row.  Rows at or beyond
+// `n` (ragged tail) are neutral tokens: q = k = 0 (and a = 1, b = 0).
+// load() only issues the global loads; finish() reduces and scales.
 template <int DK, typename IO>
 struct Prologue {
   static constexpr int E = DK / 8;
   float kv[E], qv[E];
   int row, part;
 
-  __device__ __forceinline__ void normalise(const IO* q, const IO* k, int64_t row_base, int H,
-                                            int n, bool want_q) {
+  __device__ __forceinline__ void load(const IO* q, const IO* k, int64_t row_base, int H, int n, bool want_q) {
     row = threadIdx.x >> 3;
     part = threadIdx.x & 7;
     const bool valid = row < n;
     const int64_t off = (row_base + (int64_t)row * H) * DK + part * E;
     load_row_part<IO>(k + off, kv, E, valid);
+    if (want_q) load_row_part<IO>(q + off, qv, E, valid);
+  }
+  __device__ __forceinline__ void finish(bool want_q) {
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) sk += kv[e] * kv[e];
-    sk = group_sum<8>(sk);
-    const float rk = l2_scale(sk);
+    const float rk = l2_scale(group_sum<8>(sk));
 #pragma unroll
     for (int e = 0; e < E; ++e) kv[e] *= rk;
     if (want_q) {
-      load_row_part<IO>(q + off, qv, E, valid);
 #pragma unroll
       for (int e = 0; e < E; ++e) sq += qv[e] * qv[e];
-      sq = group_sum<8>(sq);
-      const float rq = l2_scale(sq);
+      const float rq = l2_scale(group_sum<8>(sq));
 #pragma unroll
       for (int e = 0; e < E; ++e) qv[e] *= rq;
     }
   }
 };
 
-// wave-0 part: g = inclusive cumsum of ln(alpha) over the chunk (lane = row)
-__device__ __forceinline__ float chunk_gate_scan(const float* alpha, int64_t idx, bool valid) {
-  const float la = valid ? logf(alpha[idx]) : 0.f;
-  return wave_inclusive_scan(la);
+// g = inclusive cumsum of ln(alpha) over the chunk, lane = row (one wave)
+__device__ __forceinline__ float chunk_gate_scan(float alpha_or_one) {
+  return wave_inclusive_scan(logf(alpha_or_one));
+}
+
+// Y = (I + A)^{-1} R for a 64 x 16 right-hand side in accumulator layout
+// (Y[b] holds rows 16b..16b+15 of R on entry and of the solution on exit).
+// Blocked forward substitution: Y_b = Linv_b (R_b - sum_{k<b} A_bk Y_k), on
+// the matrix cores; sAn holds -A (row stride LC) and sLi the four diagonal
+// block inverses (row stride LLI, columns 16..31 zero).
+template <typename OP, int LC, int LLI>
+__device__ __forceinline__ void block_solve(f4_t (&Y)[4], const OP* sAn, const OP* sLi) {
+  const f4_t z = zero4();
+  f4_t t = zero4();
+  mma(t, lds_frag<OP>(sLi, LLI, 0, 0), acc_frag<OP>(Y[0], z));
+  Y[0] = t;
+  mma(Y[1], lds_frag<OP>(sAn, LC, 16, 0), acc_frag<OP>(Y[0], z));
+  t = zero4();
+  mma(t, lds_frag<OP>(sLi, LLI, 16, 0), acc_frag<OP>(Y[1], z));
+  Y[1] = t;
+  const Frag<OP> f01 = acc_frag<OP>(Y[0], Y[1]);
+  mma(Y[2], lds_frag<OP>(sAn, LC, 32, 0), f01);
+  mma(Y[3], lds_frag<OP>(sAn, LC, 48, 0), f01);
+  t = zero4();
+  mma(t, lds_frag<OP>(sLi, LLI, 32, 0), acc_frag<OP>(Y[2], z));
+  Y[2] = t;
+  mma(Y[3], lds_frag<OP>(sAn, LC, 48, 32), acc_frag<OP>(Y[2], z));
+  t = zero4();
+  mma(t, lds_frag<OP>(sLi, LLI, 48, 0), acc_frag<OP>(Y[3], z));
+  Y[3] = t;
 }
 
 // ------------------------------------------------------------ chunk kernel
@@ -164,30 +210,30 @@ __device__ __forceinline__ float chunk_gate_scan(const float* alpha, int64_t idx
 template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE>
 __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   using L = Lds<DK, DV, IO, OP, MODE>;
+  constexpr int LDK = L::LDK, LC = L::LC, LVB = L::LVB, LAD = L::LAD, LLI = L::LLI;
   constexpr int NCT = MODE == MODE_SUMMARY ? (DV + DK) / 16 : DV / 16;  // column tiles
   constexpr int CPW = (NCT + NWAVE - 1) / NWAVE;                        // tiles per wave (max)
   constexpr int RT = DK / 16;                                           // row tiles of M
   constexpr int KB = DK / 32;                                           // 32-deep blocks of dk
   constexpr int VCT = DV / 16;                                          // value column tiles
   static_assert(L::total <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(RT <= NWAVE, "one wave per W column tile");
 
   __shared__ __attribute__((aligned(16))) char smem[L::total];
-  OP* sKh = reinterpret_cast<OP*>(smem + L::oKh);      // [C][DK]   normalised k
-  OP* sKt = reinterpret_cast<OP*>(smem + L::oKt);      // [DK][C]   its transpose
-  OP* sQh = reinterpret_cast<OP*>(smem + L::oQh);      // [C][DK]   normalised q
-  IO* sV = reinterpret_cast<IO*>(smem + L::oV);        // [C+3][DV] raw v rows t0-3 ..
+  OP* sKh = reinterpret_cast<OP*>(smem + L::oKh);           // [C][LDK]  normalised k
+  OP* sKt = reinterpret_cast<OP*>(smem + L::oKt);           // [DK][LC]  its transpose
+  OP* sQh = reinterpret_cast<OP*>(smem + L::oQh);           // [C][LDK]  normalised q
+  char* sV = smem + L::oV;                                  // [C+3] rows of LVB bytes: raw v, t0-3 ..
   float* sTap = reinterpret_cast<float*>(smem + L::oTap);   // [C][4]
   float* sG = reinterpret_cast<float*>(smem + L::oScal);    // [C] g
-  float* sGam = sG + C;                                      // [C] e^g
-  float* sBeta = sG + 2 * C;                                 // [C] b
-  float* sDec = sG + 3 * C;                                  // [C] e^{g_C - g}
-  float* sA = reinterpret_cast<float*>(smem + L::oA);        // [C][C]
-  OP* sW = reinterpret_cast<OP*>(smem + L::oA);              // [C][DK] -W (after A is dead)
-  float* sX = reinterpret_cast<float*>(smem + L::oX);        // [C][C]
-  OP* sT1 = reinterpret_cast<OP*>(smem + L::oT);             // [C][C]
-  OP* sT2 = sT1 + C * C;                                     // [C][C]
-  float* sY = reinterpret_cast<float*>(smem + L::oT);        // [3][16][16] scratch
-  OP* sP = reinterpret_cast<OP*>(smem + L::oP);              // [C][C]
+  float* sGam = sG + C;                                     // [C] e^g
+  float* sBeta = sG + 2 * C;                                // [C] b
+  float* sDec = sG + 3 * C;                                 // [C] e^{g_C - g}
+  OP* sW = reinterpret_cast<OP*>(smem + L::oW);             // [C][LDK]  -W
+  OP* sAn = reinterpret_cast<OP*>(smem + L::oAn);           // [C][LC]   -A (lower tiles)
+  float* sAd = reinterpret_cast<float*>(smem + L::oAd);     // [C][LAD]  diagonal blocks of A
+  OP* sLi = reinterpret_cast<OP*>(smem + L::oLi);           // [C][LLI]  their inverses
+  OP* sP = reinterpret_cast<OP*>(smem + L::oP);             // [C][LC]   gated causal Q K^T
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
@@ -223,12 +269,12 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     }
   }
 
-  // upper tiles of P are never written by the tile jobs: zero them once
-  if (MODE == MODE_OUTPUT) {
-    for (int e = tid; e < C * C; e += NTHR) {
-      const int r = e / C, c = e % C;
-      if ((c >> 4) > (r >> 4)) sP[e] = from_f32<OP>(0.f);
-    }
+  // tiles the chunk loop never writes: P above its block diagonal, and the
+  // zero half of the diagonal-block inverse tiles
+  for (int e = tid; e < C * C; e += NTHR) {
+    const int r = e / C, c = e % C;
+    if (MODE == MODE_OUTPUT && (c >> 4) > (r >> 4)) sP[r * LC + c] = from_f32<OP>(0.f);
+    if (c >= 16 && c < 32) sLi[r * LLI + c] = from_f32<OP>(0.f);
   }
 
   const int c_begin = s * a.seg_len;
@@ -238,51 +284,64 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
 
-    // ================= load + prologue =================
+    // ================= loads (all issued before any is used) + prologue =================
     {
       Prologue<DK, IO> pr;
-      pr.normalise(q, k, ((int64_t)b * T + t0) * H + h, H, n, MODE == MODE_OUTPUT);
-#pragma unroll
-      for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
-        const int d = pr.part * Prologue<DK, IO>::E + e;
-        const OP kh = from_f32<OP>(pr.kv[e]);
-        sKh[pr.row * DK + d] = kh;
-        sKt[d * C + pr.row] = kh;
-        if (MODE == MODE_OUTPUT) sQh[pr.row * DK + d] = from_f32<OP>(pr.qv[e]);
+      if (tid < PRO_THR) pr.load(q, k, ((int64_t)b * T + t0) * H + h, H, n, MODE == MODE_OUTPUT);
+      float al = 1.f, be = 0.f;
+      float4 tp = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int64_t gidx = ((int64_t)b * T + t0 + lane) * H + h;
+      if (wave == GATE_WAVE && lane < n) {
+        al = a.alpha[gidx];
+        be = a.beta[gidx];
+        tp = *reinterpret_cast<const float4*>(a.taps + gidx * 4);
       }
-    }
-    if (wave == 0) {
-      const int row = lane;
-      const bool valid = row < n;
-      const int64_t idx = ((int64_t)b * T + t0 + row) * H + h;
-      const float g = chunk_gate_scan(a.alpha, idx, valid);
-      const float gC = __shfl(g, C - 1, WAVE);
-      sG[row] = g;
-      sGam[row] = expf(g);
-      sBeta[row] = valid ? a.beta[idx] : 0.f;
-      sDec[row] = expf(gC - g);
-      const float4 tp = valid ? *reinterpret_cast<const float4*>(a.taps + idx * 4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(sTap + row * 4) = tp;
-    }
-    {
-      // value rows t0-3 .. t0+C-1 (16-byte pieces)
+      // value rows t0-3 .. t0+C-1 in 16-byte pieces
       constexpr int PPR = DV * (int)sizeof(IO) / 16;
-      for (int e = tid; e < (C + 3) * PPR; e += NTHR) {
+      constexpr int NP = ((C + 3) * PPR + NTHR - 1) / NTHR;
+      uint4 val[NP];
+#pragma unroll
+      for (int it = 0; it < NP; ++it) {
+        const int e = tid + it * NTHR;
         const int r = e / PPR, pc = e % PPR;
         const int t = t0 - 3 + r;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (t >= 0 && t < T && r - 3 < n) {
-          val = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
-        } else if (t < 0 && cin) {
-          val = *reinterpret_cast<const uint4*>(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
+        val[it] = make_uint4(0u, 0u, 0u, 0u);
+        if (e < (C + 3) * PPR) {
+          if (t >= 0 && t < T && r - 3 < n)
+            val[it] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
+          else if (t < 0 && cin)
+            val[it] = *reinterpret_cast<const uint4*>(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
         }
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(sV) + (size_t)e * 16) = val;
+      }
+      if (tid < PRO_THR) {
+        pr.finish(MODE == MODE_OUTPUT);
+#pragma unroll
+        for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
+          const int d = pr.part * Prologue<DK, IO>::E + e;
+          const OP kh = from_f32<OP>(pr.kv[e]);
+          sKh[pr.row * LDK + d] = kh;
+          sKt[d * LC + pr.row] = kh;
+          if (MODE == MODE_OUTPUT) sQh[pr.row * LDK + d] = from_f32<OP>(pr.qv[e]);
+        }
+      }
+      if (wave == GATE_WAVE) {
+        const float g = chunk_gate_scan(al);
+        const float gC = __shfl(g, C - 1, WAVE);
+        sG[lane] = g;
+        sGam[lane] = expf(g);
+        sBeta[lane] = be;
+        sDec[lane] = expf(gC - g);
+        *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
+      }
+#pragma unroll
+      for (int it = 0; it < NP; ++it) {
+        const int e = tid + it * NTHR;
+        if (e < (C + 3) * PPR) *reinterpret_cast<uint4*>(sV + (e / PPR) * LVB + (e % PPR) * 16) = val[it];
       }
     }
     __syncthreads();
 
-    // ================= K K^T and Q K^T tiles =================
+    // ================= K K^T -> -A (and its diagonal blocks), Q K^T -> P =================
     {
       constexpr int NJOB = MODE == MODE_OUTPUT ? 20 : 10;
       for (int job = wave; job < NJOB; job += NWAVE) {
@@ -291,172 +350,169 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         f4_t acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          mma(acc, lds_frag<OP>(Asrc, DK, ti * 16, kb * 32), lds_frag<OP>(sKh, DK, tj * 16, kb * 32));
+          mma(acc, lds_frag<OP>(Asrc, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
           if (which == 0) {
-            sA[r * C + cc] = cc < r ? sBeta[r] * expf(sG[r] - sG[cc]) * acc[i] : 0.f;
+            const float av = cc < r ? sBeta[r] * expf(sG[r] - sG[cc]) * acc[i] : 0.f;
+            sAn[r * LC + cc] = from_f32<OP>(-av);
+            if (ti == tj) sAd[r * LAD + m16] = av;
           } else {
-            sP[r * C + cc] = from_f32<OP>(cc <= r ? expf(sG[r] - sG[cc]) * acc[i] : 0.f);
+            sP[r * LC + cc] = from_f32<OP>(cc <= r ? expf(sG[r] - sG[cc]) * acc[i] : 0.f);
           }
         }
       }
     }
     __syncthreads();
 
-    // ================= X = (I + A)^{-1}, blocked =================
+    // ================= diagonal-block inverses (wave 0) =================
+    f4_t O[CPW][4];
+    auto q_times_m = [&](int cw) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
+      if (MODE != MODE_OUTPUT) return;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mma(O[cw][rt], lds_frag<OP>(sQh, LDK, rt * 16, kb * 32), mf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[cw][rt][i] *= sGam[rt * 16 + 4 * g4 + i];
+    };
     if (wave == 0) {
-      // four 16x16 diagonal blocks by forward substitution, one column per lane
+      // four 16x16 blocks by forward substitution, one column per lane; rows
+      // are read as float4 and the scheduling fences keep the compiler from
+      // hoisting all 120 row values into registers at once
       const int base = (lane >> 4) * 16, jc = lane & 15;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float acc = (i == jc) ? 1.f : 0.f;
-        const float* arow = sA + (base + i) * C + base;
+        const float* arow = sAd + (base + i) * LAD;
 #pragma unroll
-        for (int kk = 0; kk < i; ++kk) acc -= arow[kk] * x[kk];
+        for (int k4 = 0; k4 < i; k4 += 4) {
+          const float4 av = *reinterpret_cast<const float4*>(arow + k4);
+          acc -= av.x * x[k4];
+          if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
+          if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
+          if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
+        }
         x[i] = acc;
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sX[(base + i) * C + base + jc] = x[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int d = 1; d <= 3; ++d) {
-      // blocks (i, j = i - d): Y = sum_{k=j}^{i-1} A_ik X_kj ; X_ij = -X_ii Y
-      const int nblk = 4 - d;
-      if (wave < nblk) {
-        const int bi = d + wave, bj = bi - d;
-        const int r = lane >> 2, c0 = (lane & 3) * 4;
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = bj; kb < bi; ++kb) {
-          const float* arow = sA + (bi * 16 + r) * C + kb * 16;
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) {
-            const float av = arow[kk];
-            const float4 xv = *reinterpret_cast<const float4*>(sX + (kb * 16 + kk) * C + bj * 16 + c0);
-            y[0] += av * xv.x; y[1] += av * xv.y; y[2] += av * xv.z; y[3] += av * xv.w;
-          }
-        }
-        *reinterpret_cast<float4*>(sY + wave * 256 + r * 16 + c0) = make_float4(y[0], y[1], y[2], y[3]);
-      }
-      __syncthreads();
-      if (wave < nblk) {
-        const int bi = d + wave, bj = bi - d;
-        const int r = lane >> 2, c0 = (lane & 3) * 4;
-        float z[4] = {0.f, 0.f, 0.f, 0.f};
-        const float* xrow = sX + (bi * 16 + r) * C + bi * 16;
-        for (int kk = 0; kk <= r; ++kk) {
-          const float xv = xrow[kk];
-          const float4 yv = *reinterpret_cast<const float4*>(sY + wave * 256 + kk * 16 + c0);
-          z[0] -= xv * yv.x; z[1] -= xv * yv.y; z[2] -= xv * yv.z; z[3] -= xv * yv.w;
-        }
-        *reinterpret_cast<float4*>(sX + (bi * 16 + r) * C + bj * 16 + c0) = make_float4(z[0], z[1], z[2], z[3]);
-      }
-      __syncthreads();
-    }
-    // T1 = X diag(b), T2 = X diag(b gamma) (zero above the diagonal)
-    for (int e = tid; e < C * C; e += NTHR) {
-      const int r = e / C, cc = e % C;
-      const float xv = cc <= r ? sX[e] : 0.f;
-      sT1[e] = from_f32<OP>(xv * sBeta[cc]);
-      sT2[e] = from_f32<OP>(xv * sBeta[cc] * sGam[cc]);
+      for (int i = 0; i < 16; ++i) sLi[(base + i) * LLI + jc] = from_f32<OP>(x[i]);
     }
     __syncthreads();
 
-    // ================= -W = -(T2 K) =================
-    for (int job = wave; job < 4 * RT; job += NWAVE) {
-      const int rt = job / RT, ct = job % RT;
-      f4_t acc = zero4();
+    // ================= per-wave solves: W tiles and U0 = (I+A)^{-1} diag(b) V' =================
+    if (wave < RT) {
+      // W = (I+A)^{-1} diag(b gamma) K, column tile `wave`; stored negated
+      f4_t Y[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        if (kb * 32 <= rt * 16 + 15)
-          mma(acc, lds_frag<OP>(sT2, C, rt * 16, kb * 32), lds_frag<OP>(sKt, C, ct * 16, kb * 32));
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sW[(rt * 16 + 4 * g4 + i) * DK + ct * 16 + m16] = from_f32<OP>(-acc[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = rb * 16 + 4 * g4 + i;
+          Y[rb][i] = sBeta[r] * sGam[r] * to_f32<OP>(sKh[r * LDK + wave * 16 + m16]);
+        }
+      block_solve<OP, LC, LLI>(Y, sAn, sLi);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sW[(rb * 16 + 4 * g4 + i) * LDK + wave * 16 + m16] = from_f32<OP>(-Y[rb][i]);
+    }
+    f4_t U[CPW][4];
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) {
+      const int ct = wave + cw * NWAVE;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) U[cw][rb] = zero4();
+      if (ct >= NCT || !(MODE == MODE_OUTPUT || ct < VCT)) continue;
+      // right-hand side diag(b) V', V'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
+      const int col = ct * 16 + m16;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rb * 16 + 4 * g4 + i;
+          const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
+          const IO* vcol = reinterpret_cast<const IO*>(sV + r * LVB) + col;
+          const float vv = tp.x * to_f32<IO>(vcol[0]) + tp.y * to_f32<IO>(vcol[LVB / sizeof(IO)]) +
+                           tp.z * to_f32<IO>(vcol[2 * LVB / sizeof(IO)]) + tp.w * to_f32<IO>(vcol[3 * LVB / sizeof(IO)]);
+          U[cw][rb][i] = sBeta[r] * vv;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
-    // ================= per-wave column tiles =================
+    // ================= state-dependent part, per column tile =================
     const float gamC = sGam[C - 1];
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
       const int ct = wave + cw * NWAVE;
       if (ct >= NCT) continue;
-      const bool valcol = MODE == MODE_OUTPUT || ct < VCT;
-      f4_t U[4];
+      // V_new = U0 - W M0
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) U[rt] = zero4();
-      if (valcol) {
-        // V' fragments: v'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
-        const int col = ct * 16 + m16;
-        Frag<OP> Vf[2];
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mma(U[cw][rt], lds_frag<OP>(sW, LDK, rt * 16, kb * 32), mf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (MODE == MODE_OUTPUT) {
+        // O = diag(gamma) Q M0 + P V_new
+        q_times_m(cw);
+        // rows of this chunk for head h: row r lives at r * H * DV elements from base
+        const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
+        const __amdgpu_buffer_rsrc_t orsrc =
+            make_rsrc(reinterpret_cast<OUT*>(a.o) + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
+        const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          const Frag<OP> vn = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = kb * 32 + kperm(g4, j);
-            const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
-            const float vv = tp.x * to_f32<IO>(sV[(r + 0) * DV + col]) + tp.y * to_f32<IO>(sV[(r + 1) * DV + col]) +
-                             tp.z * to_f32<IO>(sV[(r + 2) * DV + col]) + tp.w * to_f32<IO>(sV[(r + 3) * DV + col]);
-            Vf[kb].v[j] = from_f32<OP>(vv);
-          }
+          for (int rt = 0; rt < 4; ++rt)
+            if (kb * 32 <= rt * 16 + 15) mma(O[cw][rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (kb * 32 <= rt * 16 + 15) mma(U[rt], lds_frag<OP>(sT1, C, rt * 16, kb * 32), Vf[kb]);
-      }
-      // V_new = U0 - W M0
-      Frag<OP> Mf[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) Mf[kb] = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma(U[rt], lds_frag<OP>(sW, DK, rt * 16, kb * 32), Mf[kb]);
-
-      if (MODE == MODE_OUTPUT) {
-        Frag<OP> Vn[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Vn[kb] = acc_frag<OP>(U[2 * kb], U[2 * kb + 1]);
-        OUT* o = reinterpret_cast<OUT*>(a.o);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          f4_t O = zero4();
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mma(O, lds_frag<OP>(sQh, DK, rt * 16, kb * 32), Mf[kb]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[i] *= sGam[rt * 16 + 4 * g4 + i];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (kb * 32 <= rt * 16 + 15) mma(O, lds_frag<OP>(sP, C, rt * 16, kb * 32), Vn[kb]);
-#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = rt * 16 + 4 * g4 + i;
-            if (row < n) o[(((int64_t)b * T + t0 + row) * H + h) * DV + ct * 16 + m16] = from_f32<OUT>(O[i]);
+            // rows at or beyond n fall outside the resource and are dropped
+            buf_store(orsrc, from_f32<OUT>(O[cw][rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
           }
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
-      Frag<OP> Vd[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        Frag<OP> vd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          Vd[kb].v[j] = from_f32<OP>(U[2 * kb][j] * sDec[kb * 32 + 4 * g4 + j]);
-          Vd[kb].v[4 + j] = from_f32<OP>(U[2 * kb + 1][j] * sDec[kb * 32 + 16 + 4 * g4 + j]);
+          vd.v[j] = from_f32<OP>(U[cw][2 * kb][j] * sDec[kb * 32 + 4 * g4 + j]);
+          vd.v[4 + j] = from_f32<OP>(U[cw][2 * kb + 1][j] * sDec[kb * 32 + 16 + 4 * g4 + j]);
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          if (kb == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+          }
+          mma(Macc[cw][rt], lds_frag<OP>(sKt, LC, rt * 16, kb * 32), vd);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma(Macc[cw][rt], lds_frag<OP>(sKt, C, rt * 16, kb * 32), Vd[kb]);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
@@ -557,13 +613,14 @@ __global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const float
 
 // grid (nchunks, H, B), 512 threads: the chunk kernels' prologue on its own.
 template <int DK, typename IO>
-__global__ __launch_bounds__(NTHR) void prologue_kernel(int T, int H, const IO* q, const IO* k,
-                                                        const float* alpha, float* qhat, float* khat,
-                                                        float* gout) {
+__global__ __launch_bounds__(PRO_THR) void prologue_kernel(int T, int H, const IO* q, const IO* k,
+                                                           const float* alpha, float* qhat, float* khat,
+                                                           float* gout) {
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = c * C, n = min(C, T - t0);
   Prologue<DK, IO> pr;
-  pr.normalise(q, k, ((int64_t)b * T + t0) * H + h, H, n, true);
+  pr.load(q, k, ((int64_t)b * T + t0) * H + h, H, n, true);
+  pr.finish(true);
   if (pr.row < n) {
     const int64_t off = (((int64_t)b * T + t0 + pr.row) * H + h) * DK + pr.part * Prologue<DK, IO>::E;
 #pragma unroll
@@ -575,7 +632,7 @@ __global__ __launch_bounds__(NTHR) void prologue_kernel(int T, int H, const IO* 
   if (threadIdx.x < WAVE) {
     const int row = threadIdx.x;
     const int64_t idx = ((int64_t)b * T + t0 + row) * H + h;
-    const float g = chunk_gate_scan(alpha, idx, row < n);
+    const float g = chunk_gate_scan(row < n ? alpha[idx] : 1.f);
     if (row < n) gout[idx] = g;
   }
 }
@@ -676,7 +733,7 @@ hipError_t launch_prologue(int io, int B, int T, int H, int dk, const void* q, c
                            const float* alpha, float* qhat, float* khat, float* g, hipStream_t stream) {
   const int nch = (T + C - 1) / C;
   if (nch == 0 || B == 0) return hipSuccess;
-  const dim3 grid(nch, H, B), blk(NTHR);
+  const dim3 grid(nch, H, B), blk(PRO_THR);
 #define CASE(DK_)                                                                                   \
   if (dk == DK_) {                                                                                  \
     if (io == IO_BF16)                                                                              \

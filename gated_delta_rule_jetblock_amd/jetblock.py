@@ -62,8 +62,9 @@ _lib.jb_gen_taps.argtypes = [_S] + [_P] * 6 + [_P]
 _lib.jb_gen_conv.argtypes = [_S] + [_P] * 9 + [_P]
 _lib.jb_prologue.argtypes = [_S] + [_P] * 6 + [_P]
 _lib.jb_probe_mfma.argtypes = [ctypes.c_int32, _P, _P, _P, _P]
+_lib.jb_decode_update.argtypes = [_S] + [_P] * 11 + [_P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
-           "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma"):
+           "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -188,13 +189,30 @@ def decode_step(S, cache, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, W2, b1=None, 
     return dict(o=o, S=S_out, cache=cache_out)
 
 
-def gen_taps(x, W1, W2, b1=None, b2=None, H: int | None = None, *, stream=None):
-    """jb_gen_taps on x [B,T,D] -> taps [B,T,H,4] f32."""
+def decode_update(S, cache, q_t, k_t, v_t, alpha_t, beta_t, taps, *, d_model: int = 128,
+                  out_dtype=torch.float32, S_out=None, cache_out=None, o=None, stream=None):
+    """jb_decode_update: the state-update stage with taps [B,H,4] f32 precomputed.
+    In place on S and cache unless S_out/cache_out are given."""
+    B, H, dk = q_t.shape
+    dv = v_t.shape[2]
+    shape = make_shape(B, 1, H, dk, dv, d_model, _io_code(q_t), _DT[out_dtype])
+    S_out = S if S_out is None else S_out
+    cache_out = cache if cache_out is None else cache_out
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q_t.device)
+    _check(_lib.jb_decode_update(ctypes.byref(shape), _ptr(S), _ptr(S_out), _ptr(cache), _ptr(cache_out),
+                                 _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(alpha_t), _ptr(beta_t), _ptr(taps),
+                                 _ptr(o), _stream(stream)))
+    return dict(o=o, S=S_out, cache=cache_out)
+
+
+def gen_taps(x, W1, W2, b1=None, b2=None, H: int | None = None, *, out=None, stream=None):
+    """jb_gen_taps on x [B,T,D] -> taps [B,T,H,4] f32 (written into `out` when given)."""
     B, T, D = x.shape
     if H is None:
         H = W2.shape[0] // 4
     shape = make_shape(B, T, H, 32, 64, D, _io_code(x))
-    taps = torch.empty((B, T, H, 4), dtype=torch.float32, device=x.device)
+    taps = torch.empty((B, T, H, 4), dtype=torch.float32, device=x.device) if out is None else out
     _check(_lib.jb_gen_taps(ctypes.byref(shape), _ptr(x), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(taps),
                             _stream(stream)))
     return taps

@@ -187,6 +187,18 @@ jb_status jb_prologue(const jb_shape* shape, const void* q, const void* k,
                       const float* alpha, float* qhat, float* khat, float* g, void* stream);
 
 /*
+ * jb_decode_update -- the state-update stage of jb_decode_step on its own,
+ * with the taps [B][H][K] float32 already computed (e.g. by jb_gen_taps on
+ * x_t): conv of the cache and v_t, q/k normalisation, the one-pass update
+ * of the state (csdn section 2.5, finding 4: decode is bound by memory
+ * bandwidth) and the cache shift.  Arguments as in jb_decode_step.
+ */
+jb_status jb_decode_update(const jb_shape* shape, const float* S_in, float* S_out,
+                           const void* cache_in, void* cache_out, const void* q_t,
+                           const void* k_t, const void* v_t, const float* alpha_t,
+                           const float* beta_t, const float* taps, void* o_t, void* stream);
+
+/*
  * jb_probe_mfma -- runs one 16x16x32 matrix-core product D = A B on one
  * wavefront with the operand placement the library's kernels assume
  * (A [16][32], B [32][16], D [16][16], row-major float32 device buffers).
