@@ -7,10 +7,11 @@ for 256 sequences of the same shape from seeded fp32 states.  Inputs are
 seeded synthetic tensors already resident in HBM.  value = tokens processed
 per second over the whole step (65,536 prefill + 32,768 decode tokens).
 
-The decode step inside the timed loop is the two launches jb_decode_step
-makes (jb_gen_taps on x_t, then jb_decode_update); HIP events on the
-launching stream bracket every jb_prefill call and every state-update launch,
-which gives the per-kernel averages the roofline figures use.
+Each decode step is the two launches jb_decode_step makes, issued through
+their single-stage entry points so that the state update can be timed by
+itself: jb_gen_taps on x_t, then jb_decode_update.  HIP events on the
+launching stream bracket every jb_prefill call and every state-update
+launch, which gives the per-kernel averages the roofline figures use.
 
 Prints one JSON line on stdout; progress goes to stderr.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2b|4b]
@@ -47,10 +48,28 @@ def prefill_bytes_per_token(s, out_bytes: int) -> float:
     return 2 * s.d_model + 2 * 2 * s.H * s.dk + 2 * s.H * s.dv + 8 * s.H + out_bytes * s.H * s.dv
 
 
-def decode_update_bytes_per_unit(s, out_bytes: int) -> float:
-    """Compulsory bytes of the decode state update per (sequence, head): fp32 state read
-    and written once, q, k, v_t, the 3-row cache read and written, alpha, beta, 4 taps, o."""
-    return (2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * s.dv * 2 + 8 + 16 + s.dv * out_bytes)
+def decode_update_bytes(s, out_bytes: int) -> float:
+    """Compulsory HBM bytes of one decode state-update launch for B sequences: per (sequence,
+    head) the fp32 state read and written once, q, k, v_t (bf16), the 3-row cache read and
+    written, alpha, beta (f32), the 4 taps (f32) and o."""
+    per_unit = 2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * s.dv * 2 + 8 + 16 + s.dv * out_bytes
+    return s.B * s.H * per_unit
+
+
+def measured_traffic(profile: str, sources: list[str]):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain-copy calibration), or None when the
+    summary is missing or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in sources)).hexdigest()[:16]
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and line[:1].isalpha())
+    if fields.get("source_sha256_16", "").strip() != h:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
@@ -97,6 +116,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run three plain 256 MiB device-to-device copies, whose counter "
+                         "readings scale the HBM-traffic counters of a profiled run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -129,8 +151,8 @@ def main():
     ws = jb.workspace(jb.prefill_workspace_size(shp), dev)
     S = d["S"]
     cache = d["cache"]
-    taps = torch.empty((sd.B, sd.H, 4), dtype=torch.float32, device=dev)
     od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
+    taps = torch.empty((sd.B, 1, sd.H, 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     ev_pre = []
@@ -182,10 +204,14 @@ def main():
     value = (tok_pre + tok_dec) / (ms_step * 1e-3)
 
     # decode state update: the dominant kernel of the step
-    dec_bytes = decode_update_bytes_per_unit(sd, out_bytes) * sd.B * sd.H
+    dec_bytes = decode_update_bytes(sd, out_bytes)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = (measured_traffic("decode_kernel_jetblock2b_B256.md",
+                                ["gated_delta_rule_jetblock_amd/csrc/jb_decode.hip",
+                                 "gated_delta_rule_jetblock_amd/csrc/jb_device.h"])
+               if args.workload == "2b" and args.out_dtype == "bf16" else None)
     roof = dict(kernel="decode_kernel (jb_decode_update)", bound="hbm", achieved=round(dec_gbs, 1),
-                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(dec_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(dec_gbs / HBM_PEAK_GBS, 4), traffic=traffic,
                 bytes_per_launch=dec_bytes, avg_launch_us=round(dec_ms * 1e3, 2))
     pre_flops = prefill_flops_per_token(sp) * tok_pre
     pre_tf = pre_flops / (pre_ms * 1e-3) / 1e12
@@ -195,6 +221,13 @@ def main():
                     frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4), hbm_GBs=round(pre_gbs, 1),
                     hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4), flops_per_call=pre_flops,
                     avg_call_ms=round(pre_ms, 4))
+    if args.calibrate_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -214,8 +247,9 @@ def main():
                    "decode": dict(B=sd.B, steps=nsteps_dec, H=sd.H, dk=sd.dk, dv=sd.dv, d_model=sd.d_model)},
         "prefill": dict(tokens_per_s=round(tok_pre / (pre_ms * 1e-3), 1), ms=round(pre_ms, 4),
                         mfma_frac=roof_pre["frac"], hbm_frac=roof_pre["hbm_frac"]),
-        "decode": dict(tokens_per_s=round(tok_dec / (dec_ms * nsteps_dec * 1e-3), 1),
-                       update_us=round(dec_ms * 1e3, 2), hbm_frac=roof["frac"]),
+        "decode": dict(tokens_per_s=round(tok_dec / ((ms_step - pre_ms) * 1e-3), 1),
+                       update_us=round(dec_ms * 1e3, 2), step_us=round((ms_step - pre_ms) / nsteps_dec * 1e3, 2),
+                       hbm_frac=roof["frac"]),
         "roofline": roof,
         "roofline_prefill": roof_pre,
         "cpu_baseline": cpu,

@@ -60,10 +60,23 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
   __shared__ float hid[NTOK][G + 1];
   __shared__ float w2s[MAX_HK][G + 1];
   __shared__ float b2s[MAX_HK];
+  __shared__ float b1s[G];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * NTOK;
+
+  // second-layer weights and the biases first, so that their loads overlap
+  // the first layer's instead of forming a second round of memory latency
+  constexpr int WPT = (MAX_HK * G + NTHREADS - 1) / NTHREADS;
+  float w2r[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = tid + i * NTHREADS;
+    w2r[i] = e < HK * G ? to_f32<IO>(W2[e]) : 0.f;
+  }
+  const float b2r = (tid < HK && b2) ? to_f32<IO>(b2[tid]) : 0.f;
+  const float b1r = (tid < G && b1) ? to_f32<IO>(b1[tid]) : 0.f;
 
   f4_t acc[2][NT];
 #pragma unroll
@@ -94,15 +107,19 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][u * 16 + 4 * g4 + i][t * 16 + m16] = acc[u][t][i];
-  for (int e = tid; e < HK * G; e += NTHREADS) w2s[e / G][e % G] = to_f32<IO>(W2[e]);
-  for (int e = tid; e < HK; e += NTHREADS) b2s[e] = b2 ? to_f32<IO>(b2[e]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = tid + i * NTHREADS;
+    if (e < HK * G) w2s[e / G][e % G] = w2r[i];
+  }
+  if (tid < HK) b2s[tid] = b2r;
+  if (tid < G) b1s[tid] = b1r;
   __syncthreads();
   for (int e = tid; e < G * NTOK; e += NTHREADS) {
     const int u = e / NTOK, t = e % NTOK;
-    float hsum = 0.f;
+    float hsum = b1s[u];
 #pragma unroll
     for (int w = 0; w < NW; ++w) hsum += red[w][u][t];
-    if (b1) hsum += to_f32<IO>(b1[u]);
     hid[t][u] = hsum / (1.0f + expf(-hsum));  // SiLU
   }
   __syncthreads();

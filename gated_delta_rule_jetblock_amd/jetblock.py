@@ -180,12 +180,12 @@ def decode_step(S, cache, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, W2, b1=None, 
         cache_out = cache
     if o is None:
         o = torch.empty((B, H, dv), dtype=out_dtype, device=x_t.device)
-    if ws is None:
+    if ws is None and decode_workspace_size(shape) > 0:
         ws = workspace(decode_workspace_size(shape), x_t.device)
     _check(_lib.jb_decode_step(ctypes.byref(shape), _ptr(S), _ptr(S_out), _ptr(cache), _ptr(cache_out),
                                _ptr(x_t), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(alpha_t), _ptr(beta_t),
-                               _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(o), _ptr(ws), ws.numel(),
-                               _stream(stream)))
+                               _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(o), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))
     return dict(o=o, S=S_out, cache=cache_out)
 
 

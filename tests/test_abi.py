@@ -58,7 +58,7 @@ def test_workspace_sizes(jb):
     n = ctypes.c_size_t(0)
     assert jb.library().jb_decode_workspace_size(ctypes.byref(jb.make_shape(256, 1, 12, 96, 256, 1536)),
                                                  ctypes.byref(n)) == 0
-    assert n.value >= 256 * 12 * 16
+    assert n.value >= 256 * 12 * 16  # the taps of every (sequence, head)
     assert jb.library().jb_decode_workspace_size(ctypes.byref(jb.make_shape(4, 2, 12, 96, 256, 1536)),
                                                  ctypes.byref(n)) == 1
 
@@ -98,9 +98,18 @@ def test_decode_rejects_before_launch(jb):
     args = [fake] * 15
     a = list(args); a[0] = None  # S_in
     assert lib.jb_decode_step(ctypes.byref(s), *a, fake, 1 << 20, None) == 1
-    assert lib.jb_decode_step(ctypes.byref(s), *args, None, 1 << 20, None) == 3
+    assert "S_in is NULL" in jb.last_error()
+    a = list(args); a[8] = ctypes.c_void_p(0x10002)  # alpha_t only 2-byte aligned
+    assert lib.jb_decode_step(ctypes.byref(s), *a, None, 0, None) == 1
+    a = list(args); a[4] = ctypes.c_void_p(0x10008)  # x_t not 16-byte aligned
+    assert lib.jb_decode_step(ctypes.byref(s), *a, None, 0, None) == 1
+    assert lib.jb_decode_step(ctypes.byref(s), *args, None, 1 << 20, None) == 3  # no workspace
+    assert lib.jb_decode_step(ctypes.byref(s), *args, fake, 16, None) == 3      # too small
     s.T = 2
     assert lib.jb_decode_step(ctypes.byref(s), *args, fake, 1 << 20, None) == 1
+    s.T = 1
+    s.dk = 80
+    assert lib.jb_decode_step(ctypes.byref(s), *args, fake, 1 << 20, None) == 2
 
 
 def test_binding_refuses_host_tensors(jb):

@@ -25,13 +25,10 @@ def _decode_vs_oracle(jb, oracle_mod, shape, steps, sample_b, io_tol, seed=0, ou
     cache = d["cache"].cuda().clone()
     W1, W2 = d["W1"].cuda(), d["W2"].cuda()
     dev = {k: d[k].cuda() for k in ("x", "q", "k", "v", "alpha", "beta")}
-    ws = jb.workspace(jb.decode_workspace_size(jb.make_shape(shape.B, 1, shape.H, shape.dk, shape.dv,
-                                                             shape.d_model, 0 if shape.io_dtype == "bf16" else 1)),
-                      "cuda")
     outs = []
     for t in range(steps):
         r = jb.decode_step(S, cache, dev["x"][t], dev["q"][t], dev["k"][t], dev["v"][t], dev["alpha"][t],
-                           dev["beta"][t], W1, W2, ws=ws, out_dtype=out_dtype)
+                           dev["beta"][t], W1, W2, out_dtype=out_dtype)
         outs.append(r["o"].clone())
     torch.cuda.synchronize()
     # oracle on sampled sequences, step by step from the same seeded state
@@ -111,3 +108,28 @@ def test_prefill_equals_decode_loop(jb, oracle_mod):
     assert rel_err(o, to_np(r["o"]).astype(np.float64)) < TOL_BF16
     assert rel_err(S, to_np(r["S_final"]).astype(np.float64)) < TOL_BF16
     assert torch.equal(c, r["conv_out"])
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_update_with_given_taps(jb, oracle_mod, io):
+    """jb_gen_taps followed by jb_decode_update equals jb_decode_step (and the oracle)."""
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=6, T=1, H=3, dk=64, dv=128, d_model=256, io_dtype=io)
+    d = inputs.decode_inputs(s, steps=1, seed=17)
+    g = torch.Generator().manual_seed(3)
+    b1 = (torch.randn(32, generator=g) * 0.3).to(d["W1"].dtype).cuda()
+    b2 = (torch.randn(12, generator=g) * 0.3).to(d["W1"].dtype).cuda()
+    args = [d[k][0].cuda() for k in ("x", "q", "k", "v", "alpha", "beta")]
+    W1, W2 = d["W1"].cuda(), d["W2"].cuda()
+    S1, c1 = d["S"].cuda().clone(), d["cache"].cuda().clone()
+    S2, c2 = d["S"].cuda().clone(), d["cache"].cuda().clone()
+    r1 = jb.decode_step(S1, c1, *args, W1, W2, b1, b2)
+    taps = jb.gen_taps(args[0].view(6, 1, 256), W1, W2, b1, b2, H=3)
+    r2 = jb.decode_update(S2, c2, args[1], args[2], args[3], args[4], args[5], taps, d_model=256)
+    torch.cuda.synchronize()
+    ro = oracle_mod.decode_step(to_np(d["S"]), to_np(d["cache"]), *(to_np(a) for a in args), to_np(d["W1"]),
+                                to_np(d["W2"]), b1=to_np(b1), b2=to_np(b2))
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    assert rel_err(r1["o"], ro["o"]) < tol and rel_err(S1, ro["S"]) < tol
+    assert rel_err(r2["o"], ro["o"]) < tol and rel_err(S2, ro["S"]) < tol
+    assert torch.equal(c1, c2)
