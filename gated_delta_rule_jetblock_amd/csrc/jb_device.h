@@ -38,13 +38,8 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// round-to-nearest-even float -> bfloat16 (NaN stays NaN)
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// round-to-nearest-even float -> bfloat16 (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
@@ -140,6 +135,10 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   }
   return v;
 }
+
+// 2^x and log2(x) as single hardware instructions (1 ulp)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // L2 normalisation factor (sum x^2 + 1e-6)^(-1/2)
 __device__ __forceinline__ float l2_scale(float sumsq) { return 1.0f / sqrtf(sumsq + 1e-6f); }

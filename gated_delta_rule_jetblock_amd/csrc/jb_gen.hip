@@ -84,21 +84,30 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[u][t] = zero4();
 
-  const int kq = D / NW;
-#pragma unroll 4
-  for (int k0 = wave * kq; k0 < (wave + 1) * kq; k0 += 32) {
-    GenFrag<IO> A[2], Bt[NT];
+  // the wave's K range in blocks of KU 32-deep steps whose loads are all in
+  // flight before the first product (one memory latency per block, not per step)
+  constexpr int KU = NT == 1 ? 4 : 2;
+  const int kq = D / NW, kend = (wave + 1) * kq;
+  for (int k0 = wave * kq; k0 < kend; k0 += 32 * KU) {
+    GenFrag<IO> A[KU][2], Bt[KU][NT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) A[u].load(W1 + (int64_t)(u * 16 + m16) * D + k0 + 8 * g4, true);
+    for (int s = 0; s < KU; ++s) {
+      const int k = k0 + 32 * s;
+      const bool kv = k < kend;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t tok = n0 + t * 16 + m16;
-      Bt[t].load(x + tok * D + k0 + 8 * g4, tok < n);
+      for (int u = 0; u < 2; ++u) A[s][u].load(W1 + (int64_t)(u * 16 + m16) * D + k + 8 * g4, kv);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int64_t tok = n0 + t * 16 + m16;
+        Bt[s][t].load(x + tok * D + k + 8 * g4, kv && tok < n);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int s = 0; s < KU; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) A[u].mma(acc[u][t], Bt[t]);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) A[s][u].mma(acc[u][t], Bt[s][t]);  // zero fragments past kend add nothing
   }
   // lane holds hidden^T[u*16 + 4g + i][t*16 + m16]
 #pragma unroll

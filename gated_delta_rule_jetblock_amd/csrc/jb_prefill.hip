@@ -77,7 +77,7 @@ template <int DK, int DV, typename IO, typename OP, int MODE>
 struct Lds {
   static constexpr int LDK = DK + 4;                     // [C][DK] tiles
   static constexpr int LC = C + 4;                       // [*][C] tiles
-  static constexpr int LVB = DV * (int)sizeof(IO) + 16;  // bytes per value row
+  static constexpr int LVB = DV * (int)sizeof(IO);       // bytes per value row (DMA-filled, unpadded)
   static constexpr int LAD = 16 + 4;                     // fp32 diagonal blocks of A
   static constexpr int LLI = 32 + 4;                     // diagonal-block inverses (cols 16..31 zero)
   static constexpr int szKh = C * LDK * (int)sizeof(OP);
@@ -91,25 +91,39 @@ struct Lds {
   static constexpr int szAd = C * LAD * 4;
   static constexpr int szLi = C * LLI * (int)sizeof(OP);
   static constexpr int szP = MODE == MODE_OUTPUT ? C * LC * (int)sizeof(OP) : 0;
+  static constexpr int szRaw = C * DK * (int)sizeof(IO);                   // raw q or k rows of a chunk
+  static constexpr int szQraw = MODE == MODE_OUTPUT ? szRaw : 0;
+  static constexpr int szGraw = C * 4 * 2 + C * 16;                        // raw alpha, beta, taps
 
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
-  static constexpr int oKh = 0;
-  static constexpr int oKt = a16(oKh + szKh);
-  static constexpr int oQh = a16(oKt + szKt);
-  static constexpr int oV = a16(oQh + szQh);
-  static constexpr int oTap = a16(oV + szV);
+  // small per-row arrays first, then the raw q / k staging (the -A region
+  // doubles as raw k staging) and the tiles read with the C-element row
+  // stride: a ds_read immediate offset reaches 64 KB, so everything placed
+  // below that is addressed from one lane-dependent register per row stride
+  static constexpr int oGraw = 0;
+  static constexpr int oTap = a16(oGraw + szGraw);
   static constexpr int oScal = a16(oTap + szTap);
-  static constexpr int oW = a16(oScal + szScal);
-  static constexpr int oAn = a16(oW + szW);
+  static constexpr int oQraw = a16(oScal + szScal);
+  static constexpr int oAn = a16(oQraw + szQraw);
   static constexpr int oAd = a16(oAn + szAn);
   static constexpr int oLi = a16(oAd + szAd);
-  static constexpr int oP = a16(oLi + szLi);
-  static constexpr int total = a16(oP + szP);
+  static constexpr int oKt = a16(oLi + szLi);
+  static constexpr int oP = a16(oKt + szKt);
+  static constexpr int oW = a16(oP + szP);
+  static constexpr int oQh = a16(oW + szW);
+  static constexpr int oKh = a16(oQh + szQh);
+  static constexpr int oV = a16(oKh + szKh);
+  static constexpr int total = a16(oV + szV);
+  // raw k rows of the next chunk land in the -A / diagonal-block region, dead
+  // while a chunk's column phase runs and rewritten only after the prologue
+  static constexpr int oKraw = oAn;
+  static_assert(oLi + szLi - oAn >= szRaw, "raw k staging does not fit");
 };
 
-// kind-of-tile tables for the lower-triangular 4x4 tile grid of a chunk
-__device__ __constant__ const int kLowI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ __constant__ const int kLowJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// the lower-triangular tiles (i, j), j <= i, of a chunk's 4 x 4 tile grid in
+// row order, two bits per coordinate: tile t is ((kLowI >> 2t) & 3, (kLowJ >> 2t) & 3)
+constexpr uint32_t kLowI = 0xffa94u;  // rows    0 1 1 2 2 2 3 3 3 3
+constexpr uint32_t kLowJ = 0xe4910u;  // columns 0 0 1 0 1 2 0 1 2 3
 
 template <typename IO>
 __device__ __forceinline__ void load_row_part(const IO* src, float* dst, int n, bool valid);
@@ -173,9 +187,10 @@ struct Prologue {
   }
 };
 
-// g = inclusive cumsum of ln(alpha) over the chunk, lane = row (one wave)
+// g2 = inclusive cumsum of log2(alpha) over the chunk, lane = row (one wave).
+// The chunk kernels keep the gates in base 2: e^{g_i - g_j} = 2^{g2_i - g2_j}.
 __device__ __forceinline__ float chunk_gate_scan(float alpha_or_one) {
-  return wave_inclusive_scan(logf(alpha_or_one));
+  return wave_inclusive_scan(fast_log2(alpha_or_one));
 }
 
 // Y = (I + A)^{-1} R for a 64 x 16 right-hand side in accumulator layout
@@ -205,6 +220,20 @@ __device__ __forceinline__ void block_solve(f4_t (&Y)[4], const OP* sAn, const O
   Y[3] = t;
 }
 
+// ------------------------------------------------------------ LDS DMA
+
+// Direct global -> LDS loads (gfx950): one wave instruction moves a 16-byte
+// (or 4-byte) piece per active lane into consecutive LDS slots starting at the
+// wave-uniform address `lds`; lanes that skip the call write nothing.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
 // ------------------------------------------------------------ chunk kernel
 
 template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE>
@@ -225,7 +254,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   OP* sQh = reinterpret_cast<OP*>(smem + L::oQh);           // [C][LDK]  normalised q
   char* sV = smem + L::oV;                                  // [C+3] rows of LVB bytes: raw v, t0-3 ..
   float* sTap = reinterpret_cast<float*>(smem + L::oTap);   // [C][4]
-  float* sG = reinterpret_cast<float*>(smem + L::oScal);    // [C] g
+  float* sG = reinterpret_cast<float*>(smem + L::oScal);    // [C] g / ln 2
   float* sGam = sG + C;                                     // [C] e^g
   float* sBeta = sG + 2 * C;                                // [C] b
   float* sDec = sG + 3 * C;                                 // [C] e^{g_C - g}
@@ -234,10 +263,14 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   float* sAd = reinterpret_cast<float*>(smem + L::oAd);     // [C][LAD]  diagonal blocks of A
   OP* sLi = reinterpret_cast<OP*>(smem + L::oLi);           // [C][LLI]  their inverses
   OP* sP = reinterpret_cast<OP*>(smem + L::oP);             // [C][LC]   gated causal Q K^T
+  char* sKraw = smem + L::oKraw;                            // [C][DK] raw k of the next chunk
+  char* sQraw = smem + L::oQraw;                            // [C][DK] raw q of the next chunk
+  char* sGraw = smem + L::oGraw;                            // raw alpha [C], beta [C], taps [C][4]
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across a wave: keep it (and what derives from it) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const IO* q = reinterpret_cast<const IO*>(a.q);
   const IO* k = reinterpret_cast<const IO*>(a.k);
@@ -269,51 +302,83 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     }
   }
 
-  // tiles the chunk loop never writes: P above its block diagonal, and the
-  // zero half of the diagonal-block inverse tiles
-  for (int e = tid; e < C * C; e += NTHR) {
-    const int r = e / C, c = e % C;
-    if (MODE == MODE_OUTPUT && (c >> 4) > (r >> 4)) sP[r * LC + c] = from_f32<OP>(0.f);
-    if (c >= 16 && c < 32) sLi[r * LLI + c] = from_f32<OP>(0.f);
-  }
+  // P above its block diagonal is never written by the chunk loop
+  if (MODE == MODE_OUTPUT)
+    for (int e = tid; e < C * C; e += NTHR) {
+      const int r = e / C, c = e % C;
+      if ((c >> 4) > (r >> 4)) sP[r * LC + c] = from_f32<OP>(0.f);
+    }
 
   const int c_begin = s * a.seg_len;
   const int c_end = min(a.nchunks, c_begin + a.seg_len);
+
+  // Raw inputs of chunk cc straight into LDS: value rows t0-3 .. t0+63 into
+  // sV (zeros where neither v nor the conv cache has a row), raw k (and q)
+  // rows into their staging tiles, and the gates.  Rows at or beyond the
+  // sequence end are skipped; the prologue treats them as neutral tokens.
+  auto issue_chunk = [&](int cc) {
+    const int t0c = cc * C, nc = min(C, T - t0c);
+    constexpr int EP = 16 / (int)sizeof(IO);            // elements per 16-byte piece
+    constexpr int PPR = DV / EP;                        // pieces per value row
+    constexpr int NPV = (C + 3) * PPR;
+    for (int j = wave; j * 64 < NPV; j += NWAVE) {
+      const int p = j * 64 + lane;
+      if (p < NPV) {
+        const int r = p / PPR, pc = p % PPR, t = t0c - 3 + r;
+        if (t >= 0 && r - 3 < nc)
+          dma16(v + (((int64_t)b * T + t) * H + h) * DV + pc * EP, sV + j * 64 * 16);
+        else if (t < 0 && cin)
+          dma16(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * EP, sV + j * 64 * 16);
+        else
+          *reinterpret_cast<uint4*>(sV + p * 16) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    constexpr int PPK = DK / EP;                        // pieces per q or k row
+    for (int j = wave; j * 64 < C * PPK; j += NWAVE) {
+      const int p = j * 64 + lane;
+      const int r = p / PPK, pc = p % PPK;
+      if (p < C * PPK && r < nc) {
+        const int64_t off = (((int64_t)b * T + t0c + r) * H + h) * DK + pc * EP;
+        dma16(k + off, sKraw + j * 64 * 16);
+        if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+      }
+    }
+    if (wave == GATE_WAVE && lane < nc) {
+      const int64_t gidx = ((int64_t)b * T + t0c + lane) * H + h;
+      dma4(a.alpha + gidx, sGraw);
+      dma4(a.beta + gidx, sGraw + C * 4);
+      dma16(a.taps + gidx * 4, sGraw + C * 8);
+    }
+  };
+
+  // a column tile of outputs, rows t0 .. t0+n-1, straight from registers
+  auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n) {
+    const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(reinterpret_cast<OUT*>(a.o) + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
+    const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        // rows at or beyond n fall outside the resource and are dropped
+        buf_store(orsrc, from_f32<OUT>(Ot[rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
+  };
+
+  issue_chunk(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
 
-    // ================= loads (all issued before any is used) + prologue =================
+    // ================= prefetched inputs -> prologue =================
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA transfers have landed
+    __syncthreads();                // ... and every other wave's
     {
-      Prologue<DK, IO> pr;
-      if (tid < PRO_THR) pr.load(q, k, ((int64_t)b * T + t0) * H + h, H, n, MODE == MODE_OUTPUT);
-      float al = 1.f, be = 0.f;
-      float4 tp = make_float4(0.f, 0.f, 0.f, 0.f);
-      const int64_t gidx = ((int64_t)b * T + t0 + lane) * H + h;
-      if (wave == GATE_WAVE && lane < n) {
-        al = a.alpha[gidx];
-        be = a.beta[gidx];
-        tp = *reinterpret_cast<const float4*>(a.taps + gidx * 4);
-      }
-      // value rows t0-3 .. t0+C-1 in 16-byte pieces
-      constexpr int PPR = DV * (int)sizeof(IO) / 16;
-      constexpr int NP = ((C + 3) * PPR + NTHR - 1) / NTHR;
-      uint4 val[NP];
-#pragma unroll
-      for (int it = 0; it < NP; ++it) {
-        const int e = tid + it * NTHR;
-        const int r = e / PPR, pc = e % PPR;
-        const int t = t0 - 3 + r;
-        val[it] = make_uint4(0u, 0u, 0u, 0u);
-        if (e < (C + 3) * PPR) {
-          if (t >= 0 && t < T && r - 3 < n)
-            val[it] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
-          else if (t < 0 && cin)
-            val[it] = *reinterpret_cast<const uint4*>(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * (16 / (int)sizeof(IO)));
-        }
-      }
       if (tid < PRO_THR) {
+        Prologue<DK, IO> pr;
+        pr.load(reinterpret_cast<const IO*>(sQraw), reinterpret_cast<const IO*>(sKraw), 0, 1, n,
+                MODE == MODE_OUTPUT);
         pr.finish(MODE == MODE_OUTPUT);
 #pragma unroll
         for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
@@ -325,18 +390,17 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         }
       }
       if (wave == GATE_WAVE) {
+        const bool valid = lane < n;
+        const float al = valid ? reinterpret_cast<const float*>(sGraw)[lane] : 1.f;
+        const float be = valid ? reinterpret_cast<const float*>(sGraw + C * 4)[lane] : 0.f;
+        const float4 tp = valid ? reinterpret_cast<const float4*>(sGraw + C * 8)[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
         const float g = chunk_gate_scan(al);
         const float gC = __shfl(g, C - 1, WAVE);
         sG[lane] = g;
-        sGam[lane] = expf(g);
+        sGam[lane] = fast_exp2(g);
         sBeta[lane] = be;
-        sDec[lane] = expf(gC - g);
+        sDec[lane] = fast_exp2(gC - g);
         *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
-      }
-#pragma unroll
-      for (int it = 0; it < NP; ++it) {
-        const int e = tid + it * NTHR;
-        if (e < (C + 3) * PPR) *reinterpret_cast<uint4*>(sV + (e / PPR) * LVB + (e % PPR) * 16) = val[it];
       }
     }
     __syncthreads();
@@ -345,7 +409,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     {
       constexpr int NJOB = MODE == MODE_OUTPUT ? 20 : 10;
       for (int job = wave; job < NJOB; job += NWAVE) {
-        const int which = job / 10, ti = kLowI[job % 10], tj = kLowJ[job % 10];
+        const int which = job >= 10, t = job - 10 * which;
+        const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
         const OP* Asrc = which ? sQh : sKh;
         f4_t acc = zero4();
 #pragma unroll
@@ -355,11 +420,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
           if (which == 0) {
-            const float av = cc < r ? sBeta[r] * expf(sG[r] - sG[cc]) * acc[i] : 0.f;
+            const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
             sAn[r * LC + cc] = from_f32<OP>(-av);
             if (ti == tj) sAd[r * LAD + m16] = av;
           } else {
-            sP[r * LC + cc] = from_f32<OP>(cc <= r ? expf(sG[r] - sG[cc]) * acc[i] : 0.f);
+            sP[r * LC + cc] = from_f32<OP>(cc <= r ? fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f);
           }
         }
       }
@@ -367,23 +432,6 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
 
     // ================= diagonal-block inverses (wave 0) =================
-    f4_t O[CPW][4];
-    auto q_times_m = [&](int cw) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
-      if (MODE != MODE_OUTPUT) return;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mma(O[cw][rt], lds_frag<OP>(sQh, LDK, rt * 16, kb * 32), mf);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[cw][rt][i] *= sGam[rt * 16 + 4 * g4 + i];
-    };
     if (wave == 0) {
       // four 16x16 blocks by forward substitution, one column per lane; rows
       // are read as float4 and the scheduling fences keep the compiler from
@@ -406,7 +454,10 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sLi[(base + i) * LLI + jc] = from_f32<OP>(x[i]);
+      for (int i = 0; i < 16; ++i) {
+        sLi[(base + i) * LLI + jc] = from_f32<OP>(x[i]);
+        sLi[(base + i) * LLI + 16 + jc] = from_f32<OP>(0.f);  // the zero half a 32-deep fragment reads
+      }
     }
     __syncthreads();
 
@@ -422,7 +473,6 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
           Y[rb][i] = sBeta[r] * sGam[r] * to_f32<OP>(sKh[r * LDK + wave * 16 + m16]);
         }
       block_solve<OP, LC, LLI>(Y, sAn, sLi);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -447,51 +497,51 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
           const float vv = tp.x * to_f32<IO>(vcol[0]) + tp.y * to_f32<IO>(vcol[LVB / sizeof(IO)]) +
                            tp.z * to_f32<IO>(vcol[2 * LVB / sizeof(IO)]) + tp.w * to_f32<IO>(vcol[3 * LVB / sizeof(IO)]);
           U[cw][rb][i] = sBeta[r] * vv;
-          __builtin_amdgcn_sched_barrier(0);
+          if (i == 3) __builtin_amdgcn_sched_barrier(0);
         }
       block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
-      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
     // ================= state-dependent part, per column tile =================
+    // the value rows, -A, its diagonal blocks and inverses, and the taps are
+    // dead from here on: the next chunk's raw inputs can stream in now
+    if (c + 1 < c_end) issue_chunk(c + 1);
     const float gamC = sGam[C - 1];
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
       const int ct = wave + cw * NWAVE;
       if (ct >= NCT) continue;
-      // V_new = U0 - W M0
+      // V_new = U0 - W M0 and (outputs) Q M0, sharing each M0 fragment
+      f4_t O[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[rt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) mma(U[cw][rt], lds_frag<OP>(sW, LDK, rt * 16, kb * 32), mf);
+        if (MODE == MODE_OUTPUT) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) mma(O[rt], lds_frag<OP>(sQh, LDK, rt * 16, kb * 32), mf);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (MODE == MODE_OUTPUT) {
         // O = diag(gamma) Q M0 + P V_new
-        q_times_m(cw);
-        // rows of this chunk for head h: row r lives at r * H * DV elements from base
-        const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
-        const __amdgpu_buffer_rsrc_t orsrc =
-            make_rsrc(reinterpret_cast<OUT*>(a.o) + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
-        const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[rt][i] *= sGam[rt * 16 + 4 * g4 + i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const Frag<OP> vn = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            if (kb * 32 <= rt * 16 + 15) mma(O[cw][rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
+            if (kb * 32 <= rt * 16 + 15) mma(O[rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // rows at or beyond n fall outside the resource and are dropped
-            buf_store(orsrc, from_f32<OUT>(O[cw][rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
-          }
-        __builtin_amdgcn_sched_barrier(0);
+        store_o(O, ct, t0, n);
       }
       // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
 #pragma unroll
@@ -514,7 +564,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    // (no barrier here: the next chunk's first LDS write follows the barrier
+    // at the top of the loop, which every wave reaches only after its column phase)
   }
 
   // ---- results
@@ -633,7 +684,7 @@ __global__ __launch_bounds__(PRO_THR) void prologue_kernel(int T, int H, const I
     const int row = threadIdx.x;
     const int64_t idx = ((int64_t)b * T + t0 + row) * H + h;
     const float g = chunk_gate_scan(row < n ? alpha[idx] : 1.f);
-    if (row < n) gout[idx] = g;
+    if (row < n) gout[idx] = g * 0.69314718055994531f;  // back to natural log
   }
 }
 
