@@ -7,11 +7,12 @@ for 256 sequences of the same shape from seeded fp32 states.  Inputs are
 seeded synthetic tensors already resident in HBM.  value = tokens processed
 per second over the whole step (65,536 prefill + 32,768 decode tokens).
 
-Each decode step is the two launches jb_decode_step makes, issued through
-their single-stage entry points so that the state update can be timed by
-itself: jb_gen_taps on x_t, then jb_decode_update.  HIP events on the
-launching stream bracket every jb_prefill call and every state-update
-launch, which gives the per-kernel averages the roofline figures use.
+Each decode step is one jb_decode_step call, a single kernel launch
+(generator, conv and state update fused).  HIP events on the launching
+stream bracket every jb_prefill call and every 16th decode launch
+(--event-every; recording events costs the stream a few microseconds, so a
+pair around every launch would slow the timed loop), which gives the
+per-kernel averages the roofline figures use.
 
 Prints one JSON line on stdout; progress goes to stderr.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2b|4b]
@@ -48,12 +49,12 @@ def prefill_bytes_per_token(s, out_bytes: int) -> float:
     return 2 * s.d_model + 2 * 2 * s.H * s.dk + 2 * s.H * s.dv + 8 * s.H + out_bytes * s.H * s.dv
 
 
-def decode_update_bytes(s, out_bytes: int) -> float:
-    """Compulsory HBM bytes of one decode state-update launch for B sequences: per (sequence,
-    head) the fp32 state read and written once, q, k, v_t (bf16), the 3-row cache read and
-    written, alpha, beta (f32), the 4 taps (f32) and o."""
-    per_unit = 2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * s.dv * 2 + 8 + 16 + s.dv * out_bytes
-    return s.B * s.H * per_unit
+def decode_step_bytes(s, out_bytes: int) -> float:
+    """Compulsory HBM bytes of one jb_decode_step launch for B sequences: per (sequence, head)
+    the fp32 state read and written once, q, k, v_t (bf16), the 3-row cache read and written,
+    alpha, beta (f32) and o; per sequence x_t (bf16); once, the generator weights W1, W2."""
+    per_unit = 2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * s.dv * 2 + 8 + s.dv * out_bytes
+    return s.B * s.H * per_unit + s.B * s.d_model * 2 + (32 * s.d_model + 4 * s.H * 32) * 2
 
 
 def measured_traffic(profile: str, sources: list[str]):
@@ -114,6 +115,8 @@ def main():
     ap.add_argument("--workload", choices=["2b", "4b"], default="2b")
     ap.add_argument("--out-dtype", choices=["bf16", "f32"], default="bf16")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--event-every", type=int, default=16,
+                    help="bracket every N-th decode state-update launch with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -152,7 +155,6 @@ def main():
     S = d["S"]
     cache = d["cache"]
     od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
-    taps = torch.empty((sd.B, 1, sd.H, 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     ev_pre = []
@@ -169,13 +171,13 @@ def main():
             e1.record(stream)
             ev_pre.append((e0, e1))
         for t in range(nsteps_dec):
-            jb.gen_taps(d["x"][t].view(sd.B, 1, sd.d_model), d["W1"], d["W2"], H=sd.H, out=taps, stream=stream)
-            if record:
+            rec_t = record and t % args.event_every == 0
+            if rec_t:
                 a0 = torch.cuda.Event(enable_timing=True)
                 a0.record(stream)
-            jb.decode_update(S, cache, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], taps,
-                             d_model=sd.d_model, out_dtype=out_dt, o=od, stream=stream)
-            if record:
+            jb.decode_step(S, cache, d["x"][t], d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t],
+                           d["W1"], d["W2"], out_dtype=out_dt, o=od, stream=stream)
+            if rec_t:
                 a1 = torch.cuda.Event(enable_timing=True)
                 a1.record(stream)
                 ev_dec.append((a0, a1))
@@ -197,20 +199,20 @@ def main():
     ms_step = total_ms / args.steps
     pre_ms = sum(a.elapsed_time(b) for a, b in ev_pre) / len(ev_pre)
     dec_ms = sum(a.elapsed_time(b) for a, b in ev_dec) / len(ev_dec)
-    log(f"step {ms_step:.3f} ms: prefill {pre_ms:.3f} ms, decode update {dec_ms * 1e3:.1f} us x {nsteps_dec}")
+    log(f"step {ms_step:.3f} ms: prefill {pre_ms:.3f} ms, decode step {dec_ms * 1e3:.1f} us x {nsteps_dec}")
 
     tok_pre = sp.B * sp.T
     tok_dec = sd.B * nsteps_dec
     value = (tok_pre + tok_dec) / (ms_step * 1e-3)
 
-    # decode state update: the dominant kernel of the step
-    dec_bytes = decode_update_bytes(sd, out_bytes)
+    # decode step: the dominant kernel of the step
+    dec_bytes = decode_step_bytes(sd, out_bytes)
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
-    traffic = (measured_traffic("decode_kernel_jetblock2b_B256.md",
+    traffic = (measured_traffic("decode_step_jetblock2b_B256.md",
                                 ["gated_delta_rule_jetblock_amd/csrc/jb_decode.hip",
                                  "gated_delta_rule_jetblock_amd/csrc/jb_device.h"])
                if args.workload == "2b" and args.out_dtype == "bf16" else None)
-    roof = dict(kernel="decode_kernel (jb_decode_update)", bound="hbm", achieved=round(dec_gbs, 1),
+    roof = dict(kernel="decode_seq_kernel (jb_decode_step)", bound="hbm", achieved=round(dec_gbs, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(dec_gbs / HBM_PEAK_GBS, 4), traffic=traffic,
                 bytes_per_launch=dec_bytes, avg_launch_us=round(dec_ms * 1e3, 2))
     pre_flops = prefill_flops_per_token(sp) * tok_pre
@@ -248,7 +250,7 @@ def main():
         "prefill": dict(tokens_per_s=round(tok_pre / (pre_ms * 1e-3), 1), ms=round(pre_ms, 4),
                         mfma_frac=roof_pre["frac"], hbm_frac=roof_pre["hbm_frac"]),
         "decode": dict(tokens_per_s=round(tok_dec / ((ms_step - pre_ms) * 1e-3), 1),
-                       update_us=round(dec_ms * 1e3, 2), step_us=round((ms_step - pre_ms) / nsteps_dec * 1e3, 2),
+                       launch_us=round(dec_ms * 1e3, 2), step_us=round((ms_step - pre_ms) / nsteps_dec * 1e3, 2),
                        hbm_frac=roof["frac"]),
         "roofline": roof,
         "roofline_prefill": roof_pre,

@@ -84,7 +84,6 @@ jb_status hip_status(const char* fn, hipError_t e) {
   return ok();
 }
 
-size_t taps_bytes(const jb_shape* s) { return ((size_t)s->B * s->T * s->H * 4 * sizeof(float) + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -164,7 +163,7 @@ jb_status jb_decode_workspace_size(const jb_shape* s, size_t* bytes) {
   jb_status st = check_shape(fn, s, true);
   if (st) return st;
   if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
-  *bytes = taps_bytes(s);
+  *bytes = 0;  // the fused step keeps its intermediates on chip
   return ok();
 }
 
@@ -181,20 +180,13 @@ jb_status jb_decode_step(const jb_shape* s, const float* S_in, float* S_out, con
   JB_REQUIRE_SCALARS(alpha_t); JB_REQUIRE_SCALARS(beta_t); JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2);
   JB_REQUIRE_PTR(o_t);
   JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2);
-  const size_t need = taps_bytes(s);
-  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
-  if (workspace_bytes < need)
-    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
-  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)workspace;
+  (void)workspace_bytes;
   const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
   const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
-  float* taps = static_cast<float*>(workspace);
-  hipError_t e = jb::launch_gen_taps(io, s->B, s->d_model, s->H, x_t, W1, b1, W2, b2, taps, hs);
-  if (e == hipSuccess)
-    e = jb::launch_decode(io, out, s->B, s->H, s->dk, s->dv, S_in, S_out, cache_in, cache_out, q_t, k_t, v_t, alpha_t,
-                          beta_t, taps, o_t, hs);
-  return hip_status(fn, e);
+  return hip_status(fn, jb::launch_decode_step(io, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
+                                               cache_out, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, b1, W2, b2, o_t,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 jb_status jb_decode_update(const jb_shape* s, const float* S_in, float* S_out, const void* cache_in, void* cache_out,

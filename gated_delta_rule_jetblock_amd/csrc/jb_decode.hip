@@ -149,6 +149,301 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, const float* S_in, f
   }
 }
 
+// ------------------------------------------------------- fused decode step
+//
+// jb_decode_step in one launch, with no communication between workgroups.
+// A workgroup of 16 waves owns one sequence b and a group of HPG of its
+// heads (HPG = H when the sequences alone fill the GPU).  It computes the
+// token's generator hidden layer once, then the taps, v' and the normalised
+// q and k of its heads into LDS, and then streams the heads' states.  Even
+// heads use one register tile and odd heads the other: head j+1's tile is in
+// flight while head j is processed, and the barriers between phases order
+// LDS only, so state loads and stores keep streaming across them.  Issue
+// order matters because the hardware counts outstanding memory operations
+// in order: the generator's loads go out before the state tiles, and each
+// head's tile before the previous head's stores, so that no wait for a
+// needed value also waits for a later, larger transfer.
+constexpr int SEQ_NW = 16;      // waves per workgroup
+constexpr int SEQ_MAXHPG = 16;  // heads per workgroup at most
+
+template <int DK, int DV>
+struct SeqSmem {
+  float sk[SEQ_MAXHPG][DK], sq[SEQ_MAXHPG][DK];  // normalised k and q
+  float sv[SEQ_MAXHPG][DV];                       // v'
+  float sred[2][SEQ_NW][DV];                      // per-wave column sums of M^T k and M^T q
+  float su[DV];                                   // u of the current head
+  float shraw[32], shid[32];                      // generator hidden layer before / after SiLU
+  float sw2[SEQ_MAXHPG * 4][33];                  // second-layer rows of the group's taps
+  float staps[SEQ_MAXHPG][4];
+  float sal[SEQ_MAXHPG], sbe[SEQ_MAXHPG], skq[SEQ_MAXHPG];
+};
+
+// 16 bytes of IO elements from global memory (zeros when !valid)
+template <typename IO>
+__device__ __forceinline__ uint4 ld16(const IO* p, bool valid) {
+  return valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+}
+// dot product of two 16-byte pieces of IO elements, accumulated in fp32
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, bf16_t) {
+  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
+    acc += __uint_as_float(av[i] & 0xffff0000u) * __uint_as_float(bv[i] & 0xffff0000u);
+  }
+  return acc;
+}
+__device__ __forceinline__ float dot16(uint4 a, uint4 b, float acc, float) {
+  acc += __uint_as_float(a.x) * __uint_as_float(b.x);
+  acc += __uint_as_float(a.y) * __uint_as_float(b.y);
+  acc += __uint_as_float(a.z) * __uint_as_float(b.z);
+  acc += __uint_as_float(a.w) * __uint_as_float(b.w);
+  return acc;
+}
+
+// two adjacent IO elements as one register-sized load
+template <typename IO> struct Two;
+template <> struct Two<bf16_t> {
+  uint32_t v;
+  __device__ __forceinline__ float lo() const { return __uint_as_float(v << 16); }
+  __device__ __forceinline__ float hi() const { return __uint_as_float(v & 0xffff0000u); }
+};
+template <> struct Two<float> {
+  float2 v;
+  __device__ __forceinline__ float lo() const { return v.x; }
+  __device__ __forceinline__ float hi() const { return v.y; }
+};
+
+template <int DK, int DV, typename IO, typename OUT>
+__global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG, int D, const float* S_in,
+                                                                 float* S_out, const IO* cache_in, IO* cache_out,
+                                                                 const IO* x_t, const IO* q_t, const IO* k_t,
+                                                                 const IO* v_t, const float* alpha_t,
+                                                                 const float* beta_t, const IO* W1, const IO* b1,
+                                                                 const IO* W2, const IO* b2, OUT* o_t) {
+  constexpr int NT = SEQ_NW * 64;
+  constexpr int RPW = DK / SEQ_NW;               // state rows per wave
+  constexpr int CPL = DV / 64;                   // state columns per lane
+  constexpr int EPC = 16 / (int)sizeof(IO);      // elements per 16-byte piece
+  constexpr int GU = sizeof(IO) == 2 ? 4 : 2;    // generator pieces per lane in flight
+  constexpr int NPAIR = (SEQ_MAXHPG * DV / 2 + NT - 1) / NT;  // (head, column pair) conv items per thread, at most
+  constexpr bool EARLY_B = 2 * RPW * CPL <= 48;  // second state tile in flight during the generator
+  __shared__ SeqSmem<DK, DV> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.y, h0 = blockIdx.x * HPG;
+  const int64_t bh0 = (int64_t)b * H + h0;
+
+  auto load_tile = [&](float (&m)[RPW][CPL], int j) {
+    const float* p = S_in + (bh0 + j) * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) ld<CPL>(p + (int64_t)r * DV, m[r]);
+  };
+
+  // ---- issue: generator pieces (wave w owns hidden units 2w and 2w+1, its
+  // lanes split d_model), q and k, the conv rows, then the state tiles
+  const int npc = (D + 64 * EPC - 1) / (64 * EPC);  // pieces per lane over d_model
+  uint4 gx[GU], gw0[GU], gw1[GU];
+#pragma unroll
+  for (int g = 0; g < GU; ++g) {
+    const int e = (g * 64 + lane) * EPC;
+    const bool ok = g < npc && e < D;
+    gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
+    gw0[g] = ld16(W1 + (int64_t)(2 * wave) * D + e, ok);
+    gw1[g] = ld16(W1 + (int64_t)(2 * wave + 1) * D + e, ok);
+  }
+  float kx[2] = {0.f, 0.f}, qx[2] = {0.f, 0.f};
+  if (wave < HPG) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < DK) {
+        kx[e] = to_f32<IO>(k_t[(bh0 + wave) * DK + d]);
+        qx[e] = to_f32<IO>(q_t[(bh0 + wave) * DK + d]);
+      }
+    }
+  }
+  Two<IO> raw[NPAIR][4];  // columns c, c+1 of the three cached rows and v_t
+#pragma unroll
+  for (int i = 0; i < NPAIR; ++i) {
+    const int pr = tid + i * NT, j = pr / (DV / 2), c = 2 * (pr % (DV / 2));
+    if (j < HPG) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        raw[i][t] = *reinterpret_cast<const Two<IO>*>(cache_in + ((int64_t)b * 3 + t) * H * DV + (int64_t)(h0 + j) * DV + c);
+      raw[i][3] = *reinterpret_cast<const Two<IO>*>(v_t + (bh0 + j) * DV + c);
+    }
+  }
+  float ma[RPW][CPL], mb[RPW][CPL];
+  load_tile(ma, 0);
+  if (EARLY_B && HPG > 1) load_tile(mb, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- generator hidden layer (pre-activation), q / k normalisation, cache shift
+  float h0acc = 0.f, h1acc = 0.f;
+#pragma unroll
+  for (int g = 0; g < GU; ++g) {
+    h0acc = dot16(gw0[g], gx[g], h0acc, IO());
+    h1acc = dot16(gw1[g], gx[g], h1acc, IO());
+  }
+  for (int p0 = GU; p0 < npc; p0 += GU) {  // d_model beyond one round of pieces
+#pragma unroll
+    for (int g = 0; g < GU; ++g) {
+      const int e = ((p0 + g) * 64 + lane) * EPC;
+      const bool ok = p0 + g < npc && e < D;
+      gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
+      gw0[g] = ld16(W1 + (int64_t)(2 * wave) * D + e, ok);
+      gw1[g] = ld16(W1 + (int64_t)(2 * wave + 1) * D + e, ok);
+    }
+#pragma unroll
+    for (int g = 0; g < GU; ++g) {
+      h0acc = dot16(gw0[g], gx[g], h0acc, IO());
+      h1acc = dot16(gw1[g], gx[g], h1acc, IO());
+    }
+  }
+  h0acc = wave_sum(h0acc);
+  h1acc = wave_sum(h1acc);
+  if (lane == 0) {
+    sm.shraw[2 * wave] = h0acc;
+    sm.shraw[2 * wave + 1] = h1acc;
+  }
+  if (wave < HPG) {
+    float sk2 = kx[0] * kx[0] + kx[1] * kx[1], sq2 = qx[0] * qx[0] + qx[1] * qx[1];
+    const float rk = l2_scale(wave_sum(sk2)), rq = l2_scale(wave_sum(sq2));
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < DK) {
+        sm.sk[wave][d] = kx[e] * rk;
+        sm.sq[wave][d] = qx[e] * rq;
+        kq += kx[e] * rk * qx[e] * rq;
+      }
+    }
+    kq = wave_sum(kq);
+    if (lane == 0) {
+      sm.skq[wave] = kq;
+      sm.sal[wave] = alpha_t[bh0 + wave];
+      sm.sbe[wave] = beta_t[bh0 + wave];
+    }
+  }
+  for (int e = tid; e < HPG * 4 * 32; e += NT) sm.sw2[e / 32][e % 32] = to_f32<IO>(W2[(int64_t)h0 * 4 * 32 + e]);
+  // shift the conv cache; the thread that read a (head, column) writes it,
+  // so cache_out may alias cache_in
+#pragma unroll
+  for (int i = 0; i < NPAIR; ++i) {
+    const int pr = tid + i * NT, j = pr / (DV / 2), c = 2 * (pr % (DV / 2));
+    if (j < HPG) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        *reinterpret_cast<Two<IO>*>(cache_out + ((int64_t)b * 3 + t) * H * DV + (int64_t)(h0 + j) * DV + c) = raw[i][t + 1];
+    }
+  }
+  if (!EARLY_B && HPG > 1) load_tile(mb, 1);
+  lds_barrier();
+
+  // ---- SiLU, second layer (the group's taps), conv
+  if (tid < 32) {
+    const float hv = sm.shraw[tid] + (b1 ? to_f32<IO>(b1[tid]) : 0.f);
+    sm.shid[tid] = hv / (1.0f + expf(-hv));
+  }
+  lds_barrier();
+  if (tid < 4 * HPG) {
+    float t = b2 ? to_f32<IO>(b2[h0 * 4 + tid]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) t += sm.sw2[tid][u] * sm.shid[u];
+    sm.staps[tid / 4][tid % 4] = t;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < NPAIR; ++i) {
+    const int pr = tid + i * NT, j = pr / (DV / 2), c = 2 * (pr % (DV / 2));
+    if (j < HPG) {
+      const float t0 = sm.staps[j][0], t1 = sm.staps[j][1], t2 = sm.staps[j][2], t3 = sm.staps[j][3];
+      sm.sv[j][c] = t0 * raw[i][0].lo() + t1 * raw[i][1].lo() + t2 * raw[i][2].lo() + t3 * raw[i][3].lo();
+      sm.sv[j][c + 1] = t0 * raw[i][0].hi() + t1 * raw[i][1].hi() + t2 * raw[i][2].hi() + t3 * raw[i][3].hi();
+    }
+  }
+  lds_barrier();
+
+  // ---- the heads' state updates
+  auto process = [&](float (&m)[RPW][CPL], int j) {
+    const int64_t bh = bh0 + j;
+    float pa[CPL], pc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) { pa[i] = 0.f; pc[i] = 0.f; }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float kr = sm.sk[j][wave * RPW + r], qr = sm.sq[j][wave * RPW + r];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { pa[i] += m[r][i] * kr; pc[i] += m[r][i] * qr; }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      sm.sred[0][wave][lane * CPL + i] = pa[i];
+      sm.sred[1][wave][lane * CPL + i] = pc[i];
+    }
+    lds_barrier();
+    const float al = sm.sal[j];
+    if (tid < DV) {
+      float av = 0.f, cv = 0.f;
+#pragma unroll
+      for (int w = 0; w < SEQ_NW; ++w) { av += sm.sred[0][w][tid]; cv += sm.sred[1][w][tid]; }
+      const float u = sm.sbe[j] * (sm.sv[j][tid] - al * av);
+      sm.su[tid] = u;
+      o_t[bh * DV + tid] = from_f32<OUT>(al * cv + sm.skq[j] * u);
+    }
+    lds_barrier();
+    float* Mo = S_out + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+    float uu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) uu[i] = sm.su[lane * CPL + i];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float kr = sm.sk[j][wave * RPW + r];
+      float nm[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) nm[i] = al * m[r][i] + kr * uu[i];
+      st<CPL>(Mo + (int64_t)r * DV, nm);
+    }
+  };
+  for (int j = 0; j < HPG; j += 2) {
+    process(ma, j);
+    if (j + 2 < HPG) load_tile(ma, j + 2);
+    if (j + 1 < HPG) {
+      process(mb, j + 1);
+      if (j + 3 < HPG) load_tile(mb, j + 3);
+    }
+  }
+}
+
+// heads per workgroup: the fewest groups per sequence that fill the GPU with
+// at most SEQ_MAXHPG heads each (a divisor of H)
+int decode_seq_heads_per_group(int B, int H) {
+  for (int ng = 1; ng <= H; ++ng)
+    if (H % ng == 0 && H / ng <= SEQ_MAXHPG && (int64_t)B * ng >= 256) return H / ng;
+  return 1;
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t run_decode_seq(int out, int B, int H, int D, const float* S_in, float* S_out, const void* cache_in,
+                                 void* cache_out, const void* x_t, const void* q_t, const void* k_t, const void* v_t,
+                                 const float* alpha_t, const float* beta_t, const void* W1, const void* b1,
+                                 const void* W2, const void* b2, void* o_t, hipStream_t stream) {
+  const int hpg = decode_seq_heads_per_group(B, H);
+  const dim3 grid(H / hpg, B);
+#define JB_SEQ_ARGS(OUT_)                                                                                       \
+  H, hpg, D, S_in, S_out, (const IO*)cache_in, (IO*)cache_out, (const IO*)x_t, (const IO*)q_t, (const IO*)k_t, \
+      (const IO*)v_t, alpha_t, beta_t, (const IO*)W1, (const IO*)b1, (const IO*)W2, (const IO*)b2, (OUT_*)o_t
+  if (out == IO_F32)
+    decode_seq_kernel<DK, DV, IO, float><<<grid, SEQ_NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
+  else
+    decode_seq_kernel<DK, DV, IO, bf16_t><<<grid, SEQ_NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
+#undef JB_SEQ_ARGS
+  return hipGetLastError();
+}
+
 #define JB_DECODE_CASES(X) \
   X(32, 64) X(32, 128) X(32, 256) X(64, 64) X(64, 128) X(64, 256) \
   X(96, 64) X(96, 128) X(96, 256) X(128, 64) X(128, 128) X(128, 256)
@@ -188,6 +483,25 @@ hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const fl
                                           beta_t, taps, o_t, stream);                                         \
     return run_decode<DK_, DV_, float>(out, B, H, S_in, S_out, cache_in, cache_out, q_t, k_t, v_t, alpha_t,    \
                                        beta_t, taps, o_t, stream);                                            \
+  }
+  JB_DECODE_CASES(CASE)
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int D, const float* S_in, float* S_out,
+                              const void* cache_in, void* cache_out, const void* x_t, const void* q_t,
+                              const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
+                              const void* W1, const void* b1, const void* W2, const void* b2, void* o_t,
+                              hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+#define CASE(DK_, DV_)                                                                                         \
+  if (dk == DK_ && dv == DV_) {                                                                                \
+    if (io == IO_BF16)                                                                                         \
+      return run_decode_seq<DK_, DV_, bf16_t>(out, B, H, D, S_in, S_out, cache_in, cache_out, x_t, q_t, k_t, v_t, \
+                                              alpha_t, beta_t, W1, b1, W2, b2, o_t, stream);                   \
+    return run_decode_seq<DK_, DV_, float>(out, B, H, D, S_in, S_out, cache_in, cache_out, x_t, q_t, k_t, v_t,    \
+                                           alpha_t, beta_t, W1, b1, W2, b2, o_t, stream);                      \
   }
   JB_DECODE_CASES(CASE)
 #undef CASE

@@ -136,6 +136,16 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   return v;
 }
 
+// Workgroup barrier ordering LDS only.  __syncthreads() also waits for the
+// calling wave's outstanding global loads and stores; this one leaves them
+// in flight, so prefetches and stores overlap the next phase.  Global data
+// exchanged between waves still needs __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 2^x and log2(x) as single hardware instructions (1 ulp)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -53,6 +53,15 @@ hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const fl
                          const void* k_t, const void* v_t, const float* alpha_t,
                          const float* beta_t, const float* taps, void* o_t, hipStream_t stream);
 
+// One whole decode step in one launch (generator taps, conv and state update
+// for B tokens); no workspace.
+int decode_seq_heads_per_group(int B, int H);
+hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int D, const float* S_in, float* S_out,
+                              const void* cache_in, void* cache_out, const void* x_t, const void* q_t,
+                              const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
+                              const void* W1, const void* b1, const void* W2, const void* b2, void* o_t,
+                              hipStream_t stream);
+
 // Zero-fill n floats with a kernel (no memset node, safe under graph capture).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 

@@ -127,7 +127,8 @@ jb_status jb_prefill(const jb_shape* shape, const void* x, const void* q, const 
                      const void* conv_in, void* o, float* S_final, void* conv_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes jb_decode_step needs for `shape` (shape.T must be 1). */
+/* Workspace bytes jb_decode_step needs for `shape` (shape.T must be 1).
+ * Currently 0: the step keeps its intermediates on chip. */
 jb_status jb_decode_workspace_size(const jb_shape* shape, size_t* bytes);
 
 /*
@@ -140,11 +141,16 @@ jb_status jb_decode_workspace_size(const jb_shape* shape, size_t* bytes);
  * Decode is bound by the state's HBM traffic (csdn section 2.5, finding 4:
  * decoding is memory-bandwidth-bound), which this call reads and writes once.
  *
+ * One launch: each workgroup takes one sequence (or a group of its heads),
+ * computes that token's generator hidden layer once, and streams the heads'
+ * states through registers.
+ *
  * Layouts: S_in, S_out [B][H][dk][dv] f32 (S_out may alias S_in);
  * cache_in, cache_out [B][K-1][H][dv] (may alias); x_t [B][d_model];
  * q_t, k_t [B][H][dk]; v_t [B][H][dv]; alpha_t, beta_t [B][H] f32;
- * o_t [B][H][dv] (out_dtype).  workspace must hold
- * jb_decode_workspace_size() bytes.
+ * o_t [B][H][dv] (out_dtype).  workspace may be NULL when
+ * jb_decode_workspace_size() reports 0; it is accepted for the signature's
+ * stability and not touched.
  */
 jb_status jb_decode_step(const jb_shape* shape, const float* S_in, float* S_out,
                          const void* cache_in, void* cache_out, const void* x_t,

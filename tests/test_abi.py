@@ -58,7 +58,7 @@ def test_workspace_sizes(jb):
     n = ctypes.c_size_t(0)
     assert jb.library().jb_decode_workspace_size(ctypes.byref(jb.make_shape(256, 1, 12, 96, 256, 1536)),
                                                  ctypes.byref(n)) == 0
-    assert n.value >= 256 * 12 * 16  # the taps of every (sequence, head)
+    assert n.value == 0  # the fused decode step keeps its intermediates on chip
     assert jb.library().jb_decode_workspace_size(ctypes.byref(jb.make_shape(4, 2, 12, 96, 256, 1536)),
                                                  ctypes.byref(n)) == 1
 
@@ -103,8 +103,6 @@ def test_decode_rejects_before_launch(jb):
     assert lib.jb_decode_step(ctypes.byref(s), *a, None, 0, None) == 1
     a = list(args); a[4] = ctypes.c_void_p(0x10008)  # x_t not 16-byte aligned
     assert lib.jb_decode_step(ctypes.byref(s), *a, None, 0, None) == 1
-    assert lib.jb_decode_step(ctypes.byref(s), *args, None, 1 << 20, None) == 3  # no workspace
-    assert lib.jb_decode_step(ctypes.byref(s), *args, fake, 16, None) == 3      # too small
     s.T = 2
     assert lib.jb_decode_step(ctypes.byref(s), *args, fake, 1 << 20, None) == 1
     s.T = 1

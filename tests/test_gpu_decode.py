@@ -133,3 +133,13 @@ def test_decode_update_with_given_taps(jb, oracle_mod, io):
     assert rel_err(r1["o"], ro["o"]) < tol and rel_err(S1, ro["S"]) < tol
     assert rel_err(r2["o"], ro["o"]) < tol and rel_err(S2, ro["S"]) < tol
     assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("B,H,dk,dv", [(64, 12, 96, 256), (32, 16, 64, 128), (256, 20, 32, 64), (16, 5, 128, 256)])
+def test_decode_head_groups(jb, oracle_mod, B, H, dk, dv):
+    """jb_decode_step gives each workgroup one sequence and a group of its heads: groups
+    of 3 (odd), 2, 10 (H = 20 split in two) and 1 head, against the oracle."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"decode groups B={B} H={H} dk={dk} dv={dv}", flush=True)
+    s = inputs.Shape(B=B, T=1, H=H, dk=dk, dv=dv, d_model=512)
+    _decode_vs_oracle(jb, oracle_mod, s, 3, [0, B // 2, B - 1], TOL_BF16, seed=B + H)
