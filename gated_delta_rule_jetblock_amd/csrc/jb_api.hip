@@ -47,6 +47,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 jb_status check_shape(const char* fn, const jb_shape* s, bool decode) {
   if (!s) return fail(JB_ERR_INVALID_ARG, "%s: shape is NULL", fn);
   if (s->B < 1) return fail(JB_ERR_INVALID_ARG, "%s: B = %d must be >= 1", fn, s->B);
+  if (s->B > 65535) return fail(JB_ERR_UNSUPPORTED, "%s: B = %d exceeds 65535 (one grid dimension)", fn, s->B);
   if (decode ? s->T != 1 : s->T < 0)
     return fail(JB_ERR_INVALID_ARG, "%s: T = %d (%s)", fn, s->T, decode ? "decode needs T == 1" : "must be >= 0");
   if (s->H < 1 || s->H > 32) return fail(JB_ERR_UNSUPPORTED, "%s: H = %d not in [1, 32]", fn, s->H);

@@ -45,7 +45,8 @@
  *
  * Supported shapes: dk in {32, 64, 96, 128}; dv in {64, 128, 256};
  * gen_hidden == 32; taps == 4; chunk == 64 (0 selects 64); d_model a
- * positive multiple of 128; B >= 1; T >= 0 for prefill, T == 1 for decode.
+ * positive multiple of 128; 1 <= B <= 65535; H <= 32; T >= 0 for prefill,
+ * T == 1 for decode.
  * The all-fp32 mode of jb_prefill additionally needs dk*dv <= 64*64 (its
  * tiles must fit in the 160 KB of LDS of one compute unit).
  */

@@ -40,7 +40,8 @@ def _ws(jb, shape):
 
 @pytest.mark.parametrize("field,value,status", [
     ("dk", 48, 2), ("dv", 96, 2), ("gen_hidden", 16, 2), ("taps", 3, 2), ("chunk", 32, 2),
-    ("d_model", 100, 2), ("H", 0, 2), ("B", 0, 1), ("T", -1, 1), ("io_dtype", 7, 1), ("flags", 1, 1),
+    ("d_model", 100, 2), ("H", 0, 2), ("H", 33, 2), ("B", 0, 1), ("B", 65536, 2), ("T", -1, 1), ("io_dtype", 7, 1),
+    ("flags", 1, 1),
 ])
 def test_shape_validation(jb, field, value, status):
     s = jb.make_shape(1, 100, 2, 32, 64, 128)
