@@ -163,14 +163,14 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, const float* S_in, f
 // in order: the generator's loads go out before the state tiles, and each
 // head's tile before the previous head's stores, so that no wait for a
 // needed value also waits for a later, larger transfer.
-constexpr int SEQ_NW = 16;      // waves per workgroup
+constexpr int SEQ_NW = 8;       // waves per workgroup (two workgroups per CU)
 constexpr int SEQ_MAXHPG = 16;  // heads per workgroup at most
 
-template <int DK, int DV>
+template <int DK, int DV, int NW>
 struct SeqSmem {
   float sk[SEQ_MAXHPG][DK], sq[SEQ_MAXHPG][DK];  // normalised k and q
   float sv[SEQ_MAXHPG][DV];                       // v'
-  float sred[2][SEQ_NW][DV];                      // per-wave column sums of M^T k and M^T q
+  float sred[2][NW][DV];                          // per-wave column sums of M^T k and M^T q
   float su[DV];                                   // u of the current head
   float shraw[32], shid[32];                      // generator hidden layer before / after SiLU
   float sw2[SEQ_MAXHPG * 4][33];                  // second-layer rows of the group's taps
@@ -214,21 +214,22 @@ template <> struct Two<float> {
   __device__ __forceinline__ float hi() const { return v.y; }
 };
 
-template <int DK, int DV, typename IO, typename OUT>
-__global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG, int D, const float* S_in,
+template <int DK, int DV, typename IO, typename OUT, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int D, const float* S_in,
                                                                  float* S_out, const IO* cache_in, IO* cache_out,
                                                                  const IO* x_t, const IO* q_t, const IO* k_t,
                                                                  const IO* v_t, const float* alpha_t,
                                                                  const float* beta_t, const IO* W1, const IO* b1,
                                                                  const IO* W2, const IO* b2, OUT* o_t) {
-  constexpr int NT = SEQ_NW * 64;
-  constexpr int RPW = DK / SEQ_NW;               // state rows per wave
+  constexpr int NT = NW * 64;
+  constexpr int RPW = DK / NW;                   // state rows per wave
+  constexpr int UPW = 32 / NW;                   // generator hidden units per wave
   constexpr int CPL = DV / 64;                   // state columns per lane
   constexpr int EPC = 16 / (int)sizeof(IO);      // elements per 16-byte piece
-  constexpr int GU = sizeof(IO) == 2 ? 4 : 2;    // generator pieces per lane in flight
+  constexpr int GU = (sizeof(IO) == 2 ? 8 : 4) / UPW;  // generator pieces per lane in flight
   constexpr int NPAIR = (SEQ_MAXHPG * DV / 2 + NT - 1) / NT;  // (head, column pair) conv items per thread, at most
   constexpr bool EARLY_B = 2 * RPW * CPL <= 48;  // second state tile in flight during the generator
-  __shared__ SeqSmem<DK, DV> sm;
+  __shared__ SeqSmem<DK, DV, NW> sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -241,29 +242,31 @@ __global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG,
     for (int r = 0; r < RPW; ++r) ld<CPL>(p + (int64_t)r * DV, m[r]);
   };
 
-  // ---- issue: generator pieces (wave w owns hidden units 2w and 2w+1, its
-  // lanes split d_model), q and k, the conv rows, then the state tiles
+  // ---- issue: generator pieces (wave w owns hidden units UPW w .. UPW w +
+  // UPW-1, its lanes split d_model), the conv rows, then the state tiles
   const int npc = (D + 64 * EPC - 1) / (64 * EPC);  // pieces per lane over d_model
-  uint4 gx[GU], gw0[GU], gw1[GU];
+  uint4 gx[GU], gw[UPW][GU];
 #pragma unroll
   for (int g = 0; g < GU; ++g) {
     const int e = (g * 64 + lane) * EPC;
     const bool ok = g < npc && e < D;
     gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
-    gw0[g] = ld16(W1 + (int64_t)(2 * wave) * D + e, ok);
-    gw1[g] = ld16(W1 + (int64_t)(2 * wave + 1) * D + e, ok);
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) gw[u][g] = ld16(W1 + (int64_t)(UPW * wave + u) * D + e, ok);
   }
+  // q and k of the wave's first head (each lane holds up to two elements)
   float kx[2] = {0.f, 0.f}, qx[2] = {0.f, 0.f};
-  if (wave < HPG) {
+  auto load_qk = [&](int jw) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = lane + 64 * e;
       if (d < DK) {
-        kx[e] = to_f32<IO>(k_t[(bh0 + wave) * DK + d]);
-        qx[e] = to_f32<IO>(q_t[(bh0 + wave) * DK + d]);
+        kx[e] = to_f32<IO>(k_t[(bh0 + jw) * DK + d]);
+        qx[e] = to_f32<IO>(q_t[(bh0 + jw) * DK + d]);
       }
     }
-  }
+  };
+  if (wave < HPG) load_qk(wave);
   Two<IO> raw[NPAIR][4];  // columns c, c+1 of the three cached rows and v_t
 #pragma unroll
   for (int i = 0; i < NPAIR; ++i) {
@@ -281,34 +284,35 @@ __global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG,
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- generator hidden layer (pre-activation), q / k normalisation, cache shift
-  float h0acc = 0.f, h1acc = 0.f;
+  float hacc[UPW];
 #pragma unroll
-  for (int g = 0; g < GU; ++g) {
-    h0acc = dot16(gw0[g], gx[g], h0acc, IO());
-    h1acc = dot16(gw1[g], gx[g], h1acc, IO());
-  }
+  for (int u = 0; u < UPW; ++u) hacc[u] = 0.f;
+#pragma unroll
+  for (int g = 0; g < GU; ++g)
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) hacc[u] = dot16(gw[u][g], gx[g], hacc[u], IO());
   for (int p0 = GU; p0 < npc; p0 += GU) {  // d_model beyond one round of pieces
 #pragma unroll
     for (int g = 0; g < GU; ++g) {
       const int e = ((p0 + g) * 64 + lane) * EPC;
       const bool ok = p0 + g < npc && e < D;
       gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
-      gw0[g] = ld16(W1 + (int64_t)(2 * wave) * D + e, ok);
-      gw1[g] = ld16(W1 + (int64_t)(2 * wave + 1) * D + e, ok);
+#pragma unroll
+      for (int u = 0; u < UPW; ++u) gw[u][g] = ld16(W1 + (int64_t)(UPW * wave + u) * D + e, ok);
     }
 #pragma unroll
-    for (int g = 0; g < GU; ++g) {
-      h0acc = dot16(gw0[g], gx[g], h0acc, IO());
-      h1acc = dot16(gw1[g], gx[g], h1acc, IO());
-    }
+    for (int g = 0; g < GU; ++g)
+#pragma unroll
+      for (int u = 0; u < UPW; ++u) hacc[u] = dot16(gw[u][g], gx[g], hacc[u], IO());
   }
-  h0acc = wave_sum(h0acc);
-  h1acc = wave_sum(h1acc);
-  if (lane == 0) {
-    sm.shraw[2 * wave] = h0acc;
-    sm.shraw[2 * wave + 1] = h1acc;
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    const float hs = wave_sum(hacc[u]);
+    if (lane == 0) sm.shraw[UPW * wave + u] = hs;
   }
-  if (wave < HPG) {
+  for (int jw = wave; jw < HPG; jw += NW) {
+    // normalise q and k of head jw (loaded above for the first)
+    if (jw != wave) load_qk(jw);
     float sk2 = kx[0] * kx[0] + kx[1] * kx[1], sq2 = qx[0] * qx[0] + qx[1] * qx[1];
     const float rk = l2_scale(wave_sum(sk2)), rq = l2_scale(wave_sum(sq2));
     float kq = 0.f;
@@ -316,16 +320,16 @@ __global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG,
     for (int e = 0; e < 2; ++e) {
       const int d = lane + 64 * e;
       if (d < DK) {
-        sm.sk[wave][d] = kx[e] * rk;
-        sm.sq[wave][d] = qx[e] * rq;
+        sm.sk[jw][d] = kx[e] * rk;
+        sm.sq[jw][d] = qx[e] * rq;
         kq += kx[e] * rk * qx[e] * rq;
       }
     }
     kq = wave_sum(kq);
     if (lane == 0) {
-      sm.skq[wave] = kq;
-      sm.sal[wave] = alpha_t[bh0 + wave];
-      sm.sbe[wave] = beta_t[bh0 + wave];
+      sm.skq[jw] = kq;
+      sm.sal[jw] = alpha_t[bh0 + jw];
+      sm.sbe[jw] = beta_t[bh0 + jw];
     }
   }
   for (int e = tid; e < HPG * 4 * 32; e += NT) sm.sw2[e / 32][e % 32] = to_f32<IO>(W2[(int64_t)h0 * 4 * 32 + e]);
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG,
     if (tid < DV) {
       float av = 0.f, cv = 0.f;
 #pragma unroll
-      for (int w = 0; w < SEQ_NW; ++w) { av += sm.sred[0][w][tid]; cv += sm.sred[1][w][tid]; }
+      for (int w = 0; w < NW; ++w) { av += sm.sred[0][w][tid]; cv += sm.sred[1][w][tid]; }
       const float u = sm.sbe[j] * (sm.sv[j][tid] - al * av);
       sm.su[tid] = u;
       o_t[bh * DV + tid] = from_f32<OUT>(al * cv + sm.skq[j] * u);
@@ -418,11 +422,12 @@ __global__ __launch_bounds__(SEQ_NW * 64) void decode_seq_kernel(int H, int HPG,
   }
 }
 
-// heads per workgroup: the fewest groups per sequence that fill the GPU with
-// at most SEQ_MAXHPG heads each (a divisor of H)
-int decode_seq_heads_per_group(int B, int H) {
+// heads per workgroup: the fewest groups per sequence that give every CU
+// 16 waves (256 CUs) with at most SEQ_MAXHPG heads each (a divisor of H)
+int decode_seq_heads_per_group(int B, int H, int nw) {
+  const int64_t want = 256 * (16 / nw);
   for (int ng = 1; ng <= H; ++ng)
-    if (H % ng == 0 && H / ng <= SEQ_MAXHPG && (int64_t)B * ng >= 256) return H / ng;
+    if (H % ng == 0 && H / ng <= SEQ_MAXHPG && (int64_t)B * ng >= want) return H / ng;
   return 1;
 }
 
@@ -431,15 +436,16 @@ static hipError_t run_decode_seq(int out, int B, int H, int D, const float* S_in
                                  void* cache_out, const void* x_t, const void* q_t, const void* k_t, const void* v_t,
                                  const float* alpha_t, const float* beta_t, const void* W1, const void* b1,
                                  const void* W2, const void* b2, void* o_t, hipStream_t stream) {
-  const int hpg = decode_seq_heads_per_group(B, H);
+  constexpr int NW = SEQ_NW;
+  const int hpg = decode_seq_heads_per_group(B, H, NW);
   const dim3 grid(H / hpg, B);
 #define JB_SEQ_ARGS(OUT_)                                                                                       \
   H, hpg, D, S_in, S_out, (const IO*)cache_in, (IO*)cache_out, (const IO*)x_t, (const IO*)q_t, (const IO*)k_t, \
       (const IO*)v_t, alpha_t, beta_t, (const IO*)W1, (const IO*)b1, (const IO*)W2, (const IO*)b2, (OUT_*)o_t
   if (out == IO_F32)
-    decode_seq_kernel<DK, DV, IO, float><<<grid, SEQ_NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
+    decode_seq_kernel<DK, DV, IO, float, NW><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
   else
-    decode_seq_kernel<DK, DV, IO, bf16_t><<<grid, SEQ_NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
+    decode_seq_kernel<DK, DV, IO, bf16_t, NW><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
 #undef JB_SEQ_ARGS
   return hipGetLastError();
 }

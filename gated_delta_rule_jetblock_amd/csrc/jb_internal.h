@@ -55,7 +55,7 @@ hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const fl
 
 // One whole decode step in one launch (generator taps, conv and state update
 // for B tokens); no workspace.
-int decode_seq_heads_per_group(int B, int H);
+int decode_seq_heads_per_group(int B, int H, int nw);
 hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int D, const float* S_in, float* S_out,
                               const void* cache_in, void* cache_out, const void* x_t, const void* q_t,
                               const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
