@@ -94,6 +94,10 @@ struct Lds {
   static constexpr int szRaw = C * DK * (int)sizeof(IO);                   // raw q or k rows of a chunk
   static constexpr int szQraw = MODE == MODE_OUTPUT ? szRaw : 0;
   static constexpr int szGraw = C * 4 * 2 + C * 16;                        // raw alpha, beta, taps
+  // bf16 inputs: the band T of the right-hand side diag(b) V' = T V_ext, as
+  // [hi, lo][row tile][16 rows][LT] bf16 (32 columns used)
+  static constexpr int LT = 32 + 8;
+  static constexpr int szT = sizeof(IO) == 2 ? 2 * 4 * 16 * LT * 2 : 0;
 
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   // small per-row arrays first, then the raw q / k staging (the -A region
@@ -113,7 +117,8 @@ struct Lds {
   static constexpr int oQh = a16(oW + szW);
   static constexpr int oKh = a16(oQh + szQh);
   static constexpr int oV = a16(oKh + szKh);
-  static constexpr int total = a16(oV + szV);
+  static constexpr int oT = a16(oV + szV);
+  static constexpr int total = a16(oT + szT);
   // raw k rows of the next chunk land in the -A / diagonal-block region, dead
   // while a chunk's column phase runs and rewritten only after the prologue
   static constexpr int oKraw = oAn;
@@ -266,6 +271,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   char* sKraw = smem + L::oKraw;                            // [C][DK] raw k of the next chunk
   char* sQraw = smem + L::oQraw;                            // [C][DK] raw q of the next chunk
   char* sGraw = smem + L::oGraw;                            // raw alpha [C], beta [C], taps [C][4]
+  bf16_t* sT = reinterpret_cast<bf16_t*>(smem + L::oT);     // bf16 inputs: band T, hi then lo
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
@@ -365,6 +371,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         buf_store(orsrc, from_f32<OUT>(Ot[rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
   };
 
+  // T is zero outside its band; the band is rewritten every chunk
+  for (int e = tid; e < L::szT / 16; e += NTHR) reinterpret_cast<uint4*>(smem + L::oT)[e] = make_uint4(0u, 0u, 0u, 0u);
   issue_chunk(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
@@ -401,6 +409,23 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         sBeta[lane] = be;
         sDec[lane] = fast_exp2(gC - g);
         *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
+        if constexpr (sizeof(IO) == 2) {
+          // row `lane` of the band T with T[r][r + j] = b_r tap_r[j], so that the
+          // right-hand side diag(b) V' = T V_ext runs on the matrix cores; row
+          // tile rt multiplies the 32 staged value rows from 16 rt (from 35 for
+          // the last tile, which keeps the window inside the C + 3 rows), and
+          // each coefficient is split into bf16 hi + lo
+          const int rt = lane >> 4, m = lane & 15, k0 = (rt < 3 ? 0 : 16 * rt - (C + 3 - 32)) + m;
+          const float cf[4] = {be * tp.x, be * tp.y, be * tp.z, be * tp.w};
+          bf16_t* th = sT + (rt * 16 + m) * L::LT + k0;
+          bf16_t* tl = th + 4 * 16 * L::LT;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16_t hi = f32_to_bf16(cf[j]);
+            th[j] = hi;
+            tl[j] = f32_to_bf16(cf[j] - bf16_to_f32(hi));
+          }
+        }
       }
     }
     __syncthreads();
@@ -487,18 +512,35 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       if (ct >= NCT || !(MODE == MODE_OUTPUT || ct < VCT)) continue;
       // right-hand side diag(b) V', V'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
       const int col = ct * 16 + m16;
+      if constexpr (sizeof(IO) == 2) {
+        // on the matrix cores: U0 tile rt = (T_hi + T_lo) V_ext[window rows][this column tile],
+        // the value rows taken exactly as bf16 operands (K order 8g + j on both sides)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+        for (int rt = 0; rt < 4; ++rt) {
+          const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
+          const bf16_t* vcol = reinterpret_cast<const bf16_t*>(sV + (s0 + 8 * g4) * L::LVB) + col;
+          bf16x8_t vb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rb * 16 + 4 * g4 + i;
-          const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
-          const IO* vcol = reinterpret_cast<const IO*>(sV + r * LVB) + col;
-          const float vv = tp.x * to_f32<IO>(vcol[0]) + tp.y * to_f32<IO>(vcol[LVB / sizeof(IO)]) +
-                           tp.z * to_f32<IO>(vcol[2 * LVB / sizeof(IO)]) + tp.w * to_f32<IO>(vcol[3 * LVB / sizeof(IO)]);
-          U[cw][rb][i] = sBeta[r] * vv;
-          if (i == 3) __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < 8; ++j) vb[j] = __builtin_bit_cast(__bf16, vcol[j * (L::LVB / 2)]);
+          const bf16x8_t th = *reinterpret_cast<const bf16x8_t*>(sT + (rt * 16 + m16) * L::LT + 8 * g4);
+          const bf16x8_t tl = *reinterpret_cast<const bf16x8_t*>(sT + ((4 + rt) * 16 + m16) * L::LT + 8 * g4);
+          const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
+          U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
         }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = rb * 16 + 4 * g4 + i;
+            const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
+            const IO* vcol = reinterpret_cast<const IO*>(sV + r * LVB) + col;
+            const float vv = tp.x * to_f32<IO>(vcol[0]) + tp.y * to_f32<IO>(vcol[LVB / sizeof(IO)]) +
+                             tp.z * to_f32<IO>(vcol[2 * LVB / sizeof(IO)]) + tp.w * to_f32<IO>(vcol[3 * LVB / sizeof(IO)]);
+            U[cw][rb][i] = sBeta[r] * vv;
+            if (i == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+      }
       block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
     }
     __syncthreads();
