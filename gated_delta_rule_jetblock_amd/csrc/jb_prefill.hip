@@ -550,22 +550,93 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     // dead from here on: the next chunk's raw inputs can stream in now
     if (c + 1 < c_end) issue_chunk(c + 1);
     const float gamC = sGam[C - 1];
+    if constexpr (CPW == 1) {
+      // one column tile per wave
 #pragma unroll
-    for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = wave + cw * NWAVE;
-      if (ct >= NCT) continue;
-      // V_new = U0 - W M0 and (outputs) Q M0, sharing each M0 fragment
-      f4_t O[4];
+      for (int cw = 0; cw < CPW; ++cw) {
+        const int ct = wave + cw * NWAVE;
+        if (ct >= NCT) continue;
+        // V_new = U0 - W M0 and (outputs) Q M0, sharing each M0 fragment
+        f4_t O[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) O[rt] = zero4();
+        for (int rt = 0; rt < 4; ++rt) O[rt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) mma(U[cw][rt], lds_frag<OP>(sW, LDK, rt * 16, kb * 32), mf);
+          if (MODE == MODE_OUTPUT) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) mma(O[rt], lds_frag<OP>(sQh, LDK, rt * 16, kb * 32), mf);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (MODE == MODE_OUTPUT) {
+          // O = diag(gamma) Q M0 + P V_new
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[rt][i] *= sGam[rt * 16 + 4 * g4 + i];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const Frag<OP> vn = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+              if (kb * 32 <= rt * 16 + 15) mma(O[rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          store_o(O, ct, t0, n);
+        }
+        // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<OP> vd;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vd.v[j] = from_f32<OP>(U[cw][2 * kb][j] * sDec[kb * 32 + 4 * g4 + j]);
+            vd.v[4 + j] = from_f32<OP>(U[cw][2 * kb + 1][j] * sDec[kb * 32 + 16 + 4 * g4 + j]);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            if (kb == 0) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+            }
+            mma(Macc[cw][rt], lds_frag<OP>(sKt, LC, rt * 16, kb * 32), vd);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // Each A fragment (rows of W, Q, P, K^T) is read from LDS once and applied
+      // to all of the wave's column tiles.
+      bool has[CPW];  // the wave owns column tile wave + cw * NWAVE
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw) has[cw] = wave + cw * NWAVE < NCT;
+      // V_new = U0 - W M0 and (outputs) Q M0
+      f4_t O[MODE == MODE_OUTPUT ? CPW : 1][4];
+#pragma unroll
+      for (int cw = 0; cw < (MODE == MODE_OUTPUT ? CPW : 1); ++cw)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const Frag<OP> mf = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+        Frag<OP> mf[CPW];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mma(U[cw][rt], lds_frag<OP>(sW, LDK, rt * 16, kb * 32), mf);
-        if (MODE == MODE_OUTPUT) {
+        for (int cw = 0; cw < CPW; ++cw) mf[cw] = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) mma(O[rt], lds_frag<OP>(sQh, LDK, rt * 16, kb * 32), mf);
+        for (int rt = 0; rt < 4; ++rt) {
+          const Frag<OP> aw = lds_frag<OP>(sW, LDK, rt * 16, kb * 32);
+#pragma unroll
+          for (int cw = 0; cw < CPW; ++cw)
+            if (has[cw]) mma(U[cw][rt], aw, mf[cw]);
+          if (MODE == MODE_OUTPUT) {
+            const Frag<OP> aq = lds_frag<OP>(sQh, LDK, rt * 16, kb * 32);
+#pragma unroll
+            for (int cw = 0; cw < CPW; ++cw)
+              if (has[cw]) mma(O[cw][rt], aq, mf[cw]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -574,37 +645,58 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[rt][i] *= sGam[rt * 16 + 4 * g4 + i];
+          for (int i = 0; i < 4; ++i) {
+            const float gm = sGam[rt * 16 + 4 * g4 + i];
+#pragma unroll
+            for (int cw = 0; cw < CPW; ++cw) O[cw][rt][i] *= gm;
+          }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const Frag<OP> vn = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
+          Frag<OP> vn[CPW];
+#pragma unroll
+          for (int cw = 0; cw < CPW; ++cw) vn[cw] = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            if (kb * 32 <= rt * 16 + 15) mma(O[rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
+            if (kb * 32 <= rt * 16 + 15) {
+              const Frag<OP> ap = lds_frag<OP>(sP, LC, rt * 16, kb * 32);
+#pragma unroll
+              for (int cw = 0; cw < CPW; ++cw)
+                if (has[cw]) mma(O[cw][rt], ap, vn[cw]);
+            }
           __builtin_amdgcn_sched_barrier(0);
         }
-        store_o(O, ct, t0, n);
+#pragma unroll
+        for (int cw = 0; cw < CPW; ++cw)
+          if (has[cw]) store_o(O[cw], wave + cw * NWAVE, t0, n);
       }
       // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        Frag<OP> vd;
+        Frag<OP> vd[CPW];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          vd.v[j] = from_f32<OP>(U[cw][2 * kb][j] * sDec[kb * 32 + 4 * g4 + j]);
-          vd.v[4 + j] = from_f32<OP>(U[cw][2 * kb + 1][j] * sDec[kb * 32 + 16 + 4 * g4 + j]);
+          const float d0 = sDec[kb * 32 + 4 * g4 + j], d1 = sDec[kb * 32 + 16 + 4 * g4 + j];
+#pragma unroll
+          for (int cw = 0; cw < CPW; ++cw) {
+            vd[cw].v[j] = from_f32<OP>(U[cw][2 * kb][j] * d0);
+            vd[cw].v[4 + j] = from_f32<OP>(U[cw][2 * kb + 1][j] * d1);
+          }
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          if (kb == 0) {
+          const Frag<OP> ak = lds_frag<OP>(sKt, LC, rt * 16, kb * 32);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
-          }
-          mma(Macc[cw][rt], lds_frag<OP>(sKt, LC, rt * 16, kb * 32), vd);
+          for (int cw = 0; cw < CPW; ++cw)
+            if (has[cw]) {
+              if (kb == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+              }
+              mma(Macc[cw][rt], ak, vd[cw]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     // (no barrier here: the next chunk's first LDS write follows the barrier
     // at the top of the loop, which every wave reaches only after its column phase)
