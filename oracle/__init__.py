@@ -52,6 +52,10 @@ def _load():
         _lib.jbo_conv.restype = I
         _lib.jbo_l2norm.argtypes = [L, I, P, P]
         _lib.jbo_l2norm.restype = I
+        _lib.jbo_project.argtypes = [L, I, I, I, I] + [P] * 16 + [I]
+        _lib.jbo_project.restype = I
+        _lib.jbo_bf16_round.argtypes = [ctypes.c_double]
+        _lib.jbo_bf16_round.restype = ctypes.c_double
     return _lib
 
 
@@ -171,3 +175,50 @@ def l2norm(x):
     if rc != 0:
         raise ValueError("jbo_l2norm rejected its arguments")
     return out
+
+
+def bf16_round(value: float) -> float:
+    """Nearest bf16 of a double, ties to even (jbo_bf16_round)."""
+    return _load().jbo_bf16_round(float(value))
+
+
+def project(x, Wq, Wk, Wv, Wa, Wb, bq=None, bk=None, bv=None, ba=None, bb=None,
+            nthreads: int | None = None):
+    """The input projections of the block (jbo_project) for x [B,T,D]:
+    Wq, Wk [H*dk, D], Wv [H*dv, D], Wa, Wb [H, D], biases optional.
+
+    Returns dict(q, k [B,T,H,dk], v [B,T,H,dv] float32 holding bf16 values,
+    alpha, beta [B,T,H] float64)."""
+    x = _f32(x)
+    Wq, Wk, Wv, Wa, Wb = _f32(Wq), _f32(Wk), _f32(Wv), _f32(Wa), _f32(Wb)
+    bq, bk, bv, ba, bb = _f32(bq), _f32(bk), _f32(bv), _f32(ba), _f32(bb)
+    B, T, D = x.shape
+    H = Wa.shape[0]
+    dk = Wq.shape[0] // H
+    dv = Wv.shape[0] // H
+    assert Wq.shape == (H * dk, D) and Wk.shape == (H * dk, D) and Wv.shape == (H * dv, D)
+    assert Wa.shape == (H, D) and Wb.shape == (H, D)
+    n = B * T
+    q = np.empty((B, T, H, dk), np.float32)
+    k = np.empty((B, T, H, dk), np.float32)
+    v = np.empty((B, T, H, dv), np.float32)
+    alpha = np.empty((B, T, H), np.float64)
+    beta = np.empty((B, T, H), np.float64)
+    rc = _load().jbo_project(n, D, H, dk, dv, _p(x), _p(Wq), _p(bq), _p(Wk), _p(bk), _p(Wv), _p(bv),
+                             _p(Wa), _p(ba), _p(Wb), _p(bb), _p(q), _p(k), _p(v), _p(alpha), _p(beta),
+                             nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("jbo_project rejected its arguments")
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
+
+
+def prefill_from_x(x, Wq, Wk, Wv, Wa, Wb, W1, W2, bq=None, bk=None, bv=None, ba=None, bb=None,
+                   b1=None, b2=None, S0=None, conv_in=None, nthreads: int | None = None):
+    """The block from its input x: project() and then prefill().  The gates
+    cross into the block as float32, its boundary type; q, k, v as the bf16
+    values project() returns."""
+    pr = project(x, Wq, Wk, Wv, Wa, Wb, bq, bk, bv, ba, bb, nthreads)
+    r = prefill(x, pr["q"], pr["k"], pr["v"], pr["alpha"].astype(np.float32), pr["beta"].astype(np.float32),
+                W1, W2, b1=b1, b2=b2, S0=S0, conv_in=conv_in, nthreads=nthreads)
+    r["proj"] = pr
+    return r

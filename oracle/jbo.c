@@ -297,3 +297,93 @@ int jbo_decode_step(int B, int H, int dk, int dv, int D, int G, int K,
                      beta_t, W1, b1, W2, b2, S_in, cache_in, o_t, S_out,
                      cache_out, NULL, nthreads);
 }
+
+/* ------------------------------------------------------- input projections */
+/*
+ * The Linear layers that feed the block.  The csdn translation, section 2.4,
+ * says the kernel generator takes the same input as the Q/K/V projection
+ * layers; per token x (length D):
+ *     q = Wq x + bq,  k = Wk x + bk,  v = Wv x + bv
+ *     alpha = sigmoid(Wa x + ba),  beta = sigmoid(Wb x + bb)   (one per head)
+ * Readings (the pages describe neither the gate projections nor the
+ * activation precision): both gates pass through a sigmoid, which keeps them
+ * in (0, 1) as the recurrence needs; q, k and v leave the projections as
+ * bf16 activations, the block's input type, i.e. the exact value rounded to
+ * the nearest bf16 with ties to even.  Every bias is optional (NULL = 0).
+ *
+ * Layouts: x [n][D]; Wq, Wk [H*dk][D]; Wv [H*dv][D]; Wa, Wb [H][D];
+ * q, k [n][H*dk]; v [n][H*dv]; alpha, beta [n][H].
+ */
+
+/* nearest bf16 (8 significant bits, ties to even) of a double, from the
+ * definition: scale the value so that the 8 bits are its integer part, round
+ * to the nearest integer (the default rounding mode breaks ties to even) and
+ * scale back.  Below the smallest normal bf16 (2^-126) the spacing stays
+ * 2^-133. */
+double jbo_bf16_round(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  frexp(v, &e); /* |v| = f 2^e with f in [0.5, 1) */
+  const int sh = e < -125 ? 133 : 8 - e;
+  return ldexp(nearbyint(ldexp(v, sh)), -sh);
+}
+
+typedef struct {
+  int64_t n0, n1;
+  int D, H, dk, dv;
+  const float *x, *Wq, *bq, *Wk, *bk, *Wv, *bv, *Wa, *ba, *Wb, *bb;
+  float *q, *k, *v;
+  double *alpha, *beta;
+} proj_job;
+
+static double dot_row(const float* w, const float* x, int D) {
+  double acc = 0.0;
+  for (int i = 0; i < D; ++i) acc += (double)w[i] * (double)x[i];
+  return acc;
+}
+
+static void* proj_worker(void* p) {
+  const proj_job* j = (const proj_job*)p;
+  const int D = j->D, nqk = j->H * j->dk, nv = j->H * j->dv;
+  for (int64_t n = j->n0; n < j->n1; ++n) {
+    const float* x = j->x + n * D;
+    for (int r = 0; r < nqk; ++r) {
+      j->q[n * nqk + r] = (float)jbo_bf16_round(dot_row(j->Wq + (int64_t)r * D, x, D) + (j->bq ? j->bq[r] : 0.0));
+      j->k[n * nqk + r] = (float)jbo_bf16_round(dot_row(j->Wk + (int64_t)r * D, x, D) + (j->bk ? j->bk[r] : 0.0));
+    }
+    for (int r = 0; r < nv; ++r)
+      j->v[n * nv + r] = (float)jbo_bf16_round(dot_row(j->Wv + (int64_t)r * D, x, D) + (j->bv ? j->bv[r] : 0.0));
+    for (int h = 0; h < j->H; ++h) {
+      const double za = dot_row(j->Wa + (int64_t)h * D, x, D) + (j->ba ? j->ba[h] : 0.0);
+      const double zb = dot_row(j->Wb + (int64_t)h * D, x, D) + (j->bb ? j->bb[h] : 0.0);
+      j->alpha[n * j->H + h] = 1.0 / (1.0 + exp(-za));
+      j->beta[n * j->H + h] = 1.0 / (1.0 + exp(-zb));
+    }
+  }
+  return NULL;
+}
+
+int jbo_project(int64_t n_tokens, int D, int H, int dk, int dv, const float* x,
+                const float* Wq, const float* bq, const float* Wk, const float* bk,
+                const float* Wv, const float* bv, const float* Wa, const float* ba,
+                const float* Wb, const float* bb, float* q, float* k, float* v,
+                double* alpha, double* beta, int nthreads) {
+  if (n_tokens < 0 || D < 1 || H < 1 || dk < 1 || dv < 1 || !x || !Wq || !Wk || !Wv || !Wa || !Wb ||
+      !q || !k || !v || !alpha || !beta)
+    return 1;
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > n_tokens) nthreads = n_tokens > 0 ? (int)n_tokens : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  proj_job* jobs = (proj_job*)malloc(sizeof(proj_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (proj_job){n_tokens * i / nthreads, n_tokens * (i + 1) / nthreads, D, H, dk, dv,
+                         x, Wq, bq, Wk, bk, Wv, bv, Wa, ba, Wb, bb, q, k, v, alpha, beta};
+    if (nthreads == 1) proj_worker(&jobs[i]);
+    else pthread_create(&th[i], NULL, proj_worker, &jobs[i]);
+  }
+  if (nthreads > 1)
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
