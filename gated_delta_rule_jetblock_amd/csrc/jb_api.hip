@@ -206,6 +206,128 @@ jb_status jb_decode_update(const jb_shape* s, const float* S_in, float* S_out, c
                                           k_t, v_t, alpha_t, beta_t, taps, o_t, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// bytes of q, k, v (bf16) and alpha, beta (fp32) for the tokens of `s`
+size_t qkvab_bytes(const jb_shape* s) {
+  const size_t n = (size_t)s->B * s->T;
+  return 2 * a256(n * s->H * s->dk * 2) + a256(n * s->H * s->dv * 2) + 2 * a256(n * s->H * sizeof(float));
+}
+
+jb_status check_projection_args(const char* fn, const jb_shape* s) {
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the projections take bf16 inputs only", fn);
+  return JB_OK;
+}
+
+}  // namespace
+
+jb_status jb_project_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_project_workspace_size";
+  jb_status st = check_projection_args(fn, s);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = jb::project_workspace_bytes((int64_t)s->B * s->T, s->H, s->d_model);
+  return ok();
+}
+
+#define JB_PROJECTION_PTRS()                                                                                \
+  JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(Wq); JB_REQUIRE_PTR(Wk); JB_REQUIRE_PTR(Wv); JB_REQUIRE_PTR(Wa);       \
+  JB_REQUIRE_PTR(Wb); JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_OPTIONAL_PTR(ba); JB_OPTIONAL_PTR(bb);    \
+  JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2)
+
+jb_status jb_project(const jb_shape* s, const void* x, const void* Wq, const void* Wk, const void* Wv,
+                     const void* Wa, const void* ba, const void* Wb, const void* bb,
+                     const void* W1, const void* b1, const void* W2, const void* b2, void* q, void* k, void* v,
+                     float* alpha, float* beta, float* taps, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_project";
+  jb_status st = check_projection_args(fn, s);
+  if (st) return st;
+  if (s->T == 0) return ok();
+  JB_PROJECTION_PTRS();
+  JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v); JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta);
+  JB_REQUIRE_PTR(taps);
+  const size_t need = jb::project_workspace_bytes((int64_t)s->B * s->T, s->H, s->d_model);
+  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  return hip_status(fn, jb::launch_project((int64_t)s->B * s->T, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa,
+                                           ba, Wb, bb, W1, b1, W2, b2, q, k, v, alpha, beta, taps,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+jb_status jb_prefill_from_x_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_prefill_from_x_workspace_size";
+  jb_status st = check_projection_args(fn, s);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = a256(jb::prefill_workspace_bytes(plan_of(s))) + qkvab_bytes(s) +
+           jb::project_workspace_bytes((int64_t)s->B * s->T, s->H, s->d_model);
+  return ok();
+}
+
+jb_status jb_prefill_from_x(const jb_shape* s, const void* x, const void* Wq, const void* Wk, const void* Wv,
+                            const void* Wa, const void* ba, const void* Wb, const void* bb, const void* W1,
+                            const void* b1, const void* W2,
+                            const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
+                            void* conv_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_prefill_from_x";
+  jb_status st = check_projection_args(fn, s);
+  if (st) return st;
+  const jb::PrefillPlan p = plan_of(s);
+  if (!jb::prefill_supported(p)) return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built", fn, s->dk, s->dv);
+  if (seg_flag(s) < 0) return fail(JB_ERR_INVALID_ARG, "%s: bad segment flag", fn);
+  if (s->T > 0) {
+    JB_PROJECTION_PTRS();
+    JB_REQUIRE_PTR(o);
+  }
+  JB_REQUIRE_PTR(S_final); JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(conv_in); JB_OPTIONAL_PTR(conv_out);
+  size_t need = 0;
+  jb_prefill_from_x_workspace_size(s, &need);
+  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (s->T == 0) {
+    // empty sequence: the state and cache pass through
+    if (S0 && S0 != S_final)
+      e = hipMemcpyAsync(S_final, S0, (size_t)s->B * s->H * s->dk * s->dv * sizeof(float), hipMemcpyDeviceToDevice, hs);
+    else if (!S0)
+      e = jb::launch_fill_zero(S_final, (size_t)s->B * s->H * s->dk * s->dv, hs);
+    if (e == hipSuccess && conv_out)
+      e = jb::launch_conv_tail(jb::IO_BF16, s->B, 0, s->H, s->dv, nullptr, conv_in, conv_out, hs);
+    return hip_status(fn, e);
+  }
+  // workspace: the prefill's own (taps first), then q, k, v, alpha, beta, then the projections'
+  const size_t n = (size_t)s->B * s->T;
+  char* ws = static_cast<char*>(workspace);
+  float* taps = reinterpret_cast<float*>(ws);
+  char* pre_ws = ws;
+  ws += a256(jb::prefill_workspace_bytes(p));
+  void* q = ws;
+  ws += a256(n * s->H * s->dk * 2);
+  void* k = ws;
+  ws += a256(n * s->H * s->dk * 2);
+  void* v = ws;
+  ws += a256(n * s->H * s->dv * 2);
+  float* alpha = reinterpret_cast<float*>(ws);
+  ws += a256(n * s->H * sizeof(float));
+  float* beta = reinterpret_cast<float*>(ws);
+  ws += a256(n * s->H * sizeof(float));
+  e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa, ba, Wb, bb, W1, b1, W2, b2, q,
+                         k, v, alpha, beta, taps, ws, hs);
+  if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, pre_ws, hs);
+  if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(jb::IO_BF16, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs);
+  return hip_status(fn, e);
+}
+
 jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
                       float* taps, void* stream) {
   const char* fn = "jb_gen_taps";

@@ -62,6 +62,16 @@ hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int
                               const void* W1, const void* b1, const void* W2, const void* b2, void* o_t,
                               hipStream_t stream);
 
+// The input projections (q, k, v, gates) and the generator taps from x
+// (bf16 inputs only); workspace of project_workspace_bytes(n, H, D).
+size_t project_gemm_workspace_bytes();
+size_t project_workspace_bytes(int64_t n, int H, int D);
+hipError_t launch_project(int64_t n, int H, int dk, int dv, int D, const void* x, const void* Wq, const void* Wk,
+                          const void* Wv, const void* Wa, const void* ba, const void* Wb, const void* bb,
+                          const void* W1, const void* b1,
+                          const void* W2, const void* b2, void* q, void* k, void* v, float* alpha, float* beta,
+                          float* taps, void* workspace, hipStream_t stream);
+
 // Zero-fill n floats with a kernel (no memset node, safe under graph capture).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 

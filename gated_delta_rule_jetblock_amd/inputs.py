@@ -24,6 +24,7 @@ the I/O dtype is bfloat16; alpha, beta and the state are always float32.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, replace
 
 import torch
@@ -139,4 +140,32 @@ def decode_inputs(shape: Shape, steps: int = DECODE_STEPS, seed: int = 0, device
     out["v"] = _normal(g, (steps, s.B, s.H, s.dv), 0.0, 1.0, device, io)
     out["alpha"] = torch.sigmoid(_normal(g, (steps, s.B, s.H), 3.0, 1.0, device, torch.float32))
     out["beta"] = torch.sigmoid(_normal(g, (steps, s.B, s.H), 0.0, 1.0, device, torch.float32))
+    return out
+
+
+def projection_inputs(shape: Shape, seed: int = 0, device="cpu", alpha_mean: float = 3.0,
+                      beta_mean: float = 0.0):
+    """Inputs of the block from its layer input: x [B,T,D] ~ N(0,1) and bf16 weights.
+
+    Wq, Wk [H*dk, D], Wv [H*dv, D] ~ N(0, 1/D), so q, k, v come out ~ N(0, 1) like the
+    direct-input workloads; Wa, Wb [H, D] ~ N(0, 1/D) with biases ba = alpha_mean,
+    bb = beta_mean, so the gate logits are ~ N(mean, 1) as there; W1, W2 as for prefill.
+    with_qkv_bias adds bq, bk, bv ~ N(0, 0.1).
+    """
+    s = shape
+    io = torch.bfloat16
+    g = _gen(seed, device)
+    ws = 1.0 / math.sqrt(s.d_model)
+    out = dict(
+        x=_normal(g, (s.B, s.T, s.d_model), 0.0, 1.0, device, io),
+        Wq=_normal(g, (s.H * s.dk, s.d_model), 0.0, ws, device, io),
+        Wk=_normal(g, (s.H * s.dk, s.d_model), 0.0, ws, device, io),
+        Wv=_normal(g, (s.H * s.dv, s.d_model), 0.0, ws, device, io),
+        Wa=_normal(g, (s.H, s.d_model), 0.0, ws, device, io),
+        Wb=_normal(g, (s.H, s.d_model), 0.0, ws, device, io),
+        ba=torch.full((s.H,), alpha_mean, device=device).to(io),
+        bb=torch.full((s.H,), beta_mean, device=device).to(io),
+        W1=_normal(g, (s.gen_hidden, s.d_model), 0.0, 0.02, device, io),
+        W2=_normal(g, (s.H * s.taps, s.gen_hidden), 0.0, 0.02, device, io),
+    )
     return out

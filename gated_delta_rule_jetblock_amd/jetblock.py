@@ -63,8 +63,13 @@ _lib.jb_gen_conv.argtypes = [_S] + [_P] * 9 + [_P]
 _lib.jb_prologue.argtypes = [_S] + [_P] * 6 + [_P]
 _lib.jb_probe_mfma.argtypes = [ctypes.c_int32, _P, _P, _P, _P]
 _lib.jb_decode_update.argtypes = [_S] + [_P] * 11 + [_P]
+_lib.jb_project_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
+_lib.jb_prefill_from_x_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
+_lib.jb_project.argtypes = [_S] + [_P] * 18 + [_P, _SZ, _P]
+_lib.jb_prefill_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
-           "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update"):
+           "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
+           "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -247,3 +252,67 @@ def probe_mfma(kind: int, A, B, *, stream=None):
     D = torch.empty((16, 16), dtype=torch.float32, device=A.device)
     _check(_lib.jb_probe_mfma(int(kind), _ptr(A), _ptr(B), _ptr(D), _stream(stream)))
     return D
+
+
+def project_workspace_size(shape: Shape) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_project_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def prefill_from_x_workspace_size(shape: Shape) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_prefill_from_x_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def _proj_shape(x, Wq, Wv, Wa, seg_len=None, out_dtype=torch.float32):
+    B, T, D = x.shape
+    H = Wa.shape[0]
+    dk = Wq.shape[0] // H
+    dv = Wv.shape[0] // H
+    return make_shape(B, T, H, dk, dv, D, JB_BF16, _DT[out_dtype],
+                      flags=flag_segment(seg_len) if seg_len else 0)
+
+
+def project(x, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=None, *, ws=None, stream=None):
+    """jb_project.  x [B,T,D] bf16; Wq, Wk [H*dk,D], Wv [H*dv,D], Wa, Wb [H,D], W1 [32,D], W2 [4H,32]
+    bf16.  Returns dict(q, k [B,T,H,dk], v [B,T,H,dv] bf16, alpha, beta [B,T,H], taps [B,T,H,4] f32)."""
+    shape = _proj_shape(x, Wq, Wv, Wa)
+    B, T, H, dk, dv = shape.B, shape.T, shape.H, shape.dk, shape.dv
+    dev = x.device
+    q = torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    alpha = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(alpha)
+    taps = torch.empty((B, T, H, 4), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(project_workspace_size(shape), dev)
+    _check(_lib.jb_project(ctypes.byref(shape), _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wa), _ptr(ba),
+                           _ptr(Wb), _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2),
+                           _ptr(b2), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(taps), _ptr(ws),
+                           ws.numel(), _stream(stream)))
+    return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, taps=taps)
+
+
+def prefill_from_x(x, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=None, S0=None, conv_in=None, *, out_dtype=torch.float32, seg_len: int | None = None,
+                   o=None, S_final=None, conv_out=None, want_conv_out=True, ws=None, stream=None):
+    """jb_prefill_from_x: the block from its layer input x (projections, generator, recurrence).
+    Returns dict(o, S_final, conv_out)."""
+    shape = _proj_shape(x, Wq, Wv, Wa, seg_len, out_dtype)
+    B, T, H, dk, dv = shape.B, shape.T, shape.H, shape.dk, shape.dv
+    dev = x.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv_out:
+        conv_out = torch.empty((B, 3, H, dv), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(prefill_from_x_workspace_size(shape), dev)
+    _check(_lib.jb_prefill_from_x(ctypes.byref(shape), _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wa), _ptr(ba),
+                                  _ptr(Wb), _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2),
+                                  _ptr(b2), _ptr(S0), _ptr(conv_in), _ptr(o), _ptr(S_final), _ptr(conv_out),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return dict(o=o, S_final=S_final, conv_out=conv_out)

@@ -161,6 +161,52 @@ jb_status jb_decode_step(const jb_shape* shape, const float* S_in, float* S_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The block from its layer input x.  The kernel generator takes the same
+ * input as the Q/K/V projection layers (csdn translation, section 2.4), so the
+ * projections and the generator's first layer share one pass over x:
+ *   q = Wq x, k = Wk x, v = Wv x     (bf16, nearest-even from the fp32 sum)
+ *   alpha = sigmoid(Wa x + ba), beta = sigmoid(Wb x + bb)   (fp32, per head)
+ *   taps  = W2 SiLU(W1 x + b1) + b2                          (fp32, 4 per head)
+ * The pages do not describe the gate projections; a sigmoid keeps both
+ * gates in (0, 1).  bf16 inputs only (shape.io_dtype == JB_BF16); other
+ * dtypes return JB_ERR_UNSUPPORTED.
+ *
+ * Weights (bf16, row-major, caller-owned): Wq, Wk [H*dk][d_model];
+ * Wv [H*dv][d_model]; Wa, Wb [H][d_model]; W1 [32][d_model]; W2 [4H][32].
+ * The Q/K/V layers take no bias; the biases ba, bb [H], b1 [32], b2 [4H] are
+ * nullable (NULL means zero).  All pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of jb_project for `shape` (B*T tokens). */
+jb_status jb_project_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_project -- the projections above for the B*T rows of x [B][T][d_model]:
+ * writes q, k [B][T][H][dk] and v [B][T][H][dv] (bf16), alpha, beta
+ * [B][T][H] and taps [B][T][H][4] (fp32).  The three large products run as
+ * library GEMMs (bf16 operands, fp32 accumulation); W1, Wa, Wb form one more.
+ */
+jb_status jb_project(const jb_shape* shape, const void* x, const void* Wq, const void* Wk,
+                     const void* Wv, const void* Wa, const void* ba, const void* Wb, const void* bb,
+                     const void* W1, const void* b1, const void* W2, const void* b2,
+                     void* q, void* k, void* v, float* alpha, float* beta, float* taps,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of jb_prefill_from_x for `shape`. */
+jb_status jb_prefill_from_x_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_prefill_from_x -- jb_project followed by jb_prefill's recurrence: the
+ * block over B sequences of T tokens from x.  q, k, v and the gates live in
+ * the workspace.  S0, conv_in, o, S_final, conv_out as in jb_prefill.
+ */
+jb_status jb_prefill_from_x(const jb_shape* shape, const void* x, const void* Wq, const void* Wk,
+                            const void* Wv, const void* Wa, const void* ba, const void* Wb, const void* bb,
+                            const void* W1, const void* b1, const void* W2, const void* b2,
+                            const float* S0, const void* conv_in, void* o, float* S_final,
+                            void* conv_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single-stage entry points.  Each runs one stage of the path by itself so
  * that it can be checked on its own; the two calls above fuse these stages.
  * ------------------------------------------------------------------------- */

@@ -15,7 +15,8 @@ def jb():
 def test_exports_every_declared_function(jb):
     names = jb.declared_functions()
     assert {"jb_prefill", "jb_decode_step", "jb_prefill_workspace_size", "jb_decode_workspace_size",
-            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_decode_update"} <= set(names)
+            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_decode_update", "jb_project",
+            "jb_project_workspace_size", "jb_prefill_from_x", "jb_prefill_from_x_workspace_size"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", jb.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     missing = [n for n in names if n not in exported]
@@ -116,3 +117,24 @@ def test_binding_refuses_host_tensors(jb):
     x = torch.zeros(1, 4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         jb.gen_taps(x, torch.zeros(32, 128, dtype=torch.bfloat16), torch.zeros(8, 32, dtype=torch.bfloat16), H=2)
+
+
+def test_projection_entries_reject_before_launch(jb):
+    lib = jb.library()
+    n = ctypes.c_size_t(0)
+    s = jb.make_shape(1, 64, 2, 32, 64, 128)
+    assert lib.jb_project_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0 and n.value > 64 * 34 * 4
+    assert lib.jb_prefill_from_x_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    s32 = jb.make_shape(1, 64, 2, 32, 64, 128, io_dtype=jb.JB_F32)
+    assert lib.jb_project_workspace_size(ctypes.byref(s32), ctypes.byref(n)) == 2  # bf16 inputs only
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 18
+    a = list(args); a[0] = None  # x
+    assert lib.jb_project(ctypes.byref(s), *a, fake, 1 << 30, None) == 1
+    assert "x is NULL" in jb.last_error()
+    a = list(args); a[2] = ctypes.c_void_p(0x10008)  # Wk misaligned
+    assert lib.jb_project(ctypes.byref(s), *a, fake, 1 << 30, None) == 1
+    assert lib.jb_project(ctypes.byref(s), *args, fake, 16, None) == 3  # workspace too small
+    pargs = [fake] * 17
+    assert lib.jb_prefill_from_x(ctypes.byref(s), *pargs, fake, 16, None) == 3
+    assert lib.jb_prefill_from_x(ctypes.byref(s32), *pargs, fake, 1 << 30, None) == 2
