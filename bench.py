@@ -73,6 +73,50 @@ def measured_traffic(profile: str, sources: list[str]):
     return float(fields["traffic_bytes_per_launch"])
 
 
+def projection_flops_per_token(s) -> float:
+    """Matrix flops per token of the input projections: 2 D (2 H dk + H dv + 32 + 2 H)."""
+    return 2.0 * s.d_model * (2 * s.H * s.dk + s.H * s.dv + 32 + 2 * s.H)
+
+
+def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
+    """The block from its layer input x at the prefill shape (outside the timed step):
+    jb_project alone and jb_prefill_from_x, each averaged over `reps` calls bracketed by
+    HIP events on the launching stream."""
+    dev = torch.device("cuda:0")
+    p = inputs.projection_inputs(sp, seed=2, device=dev)
+    stream = torch.cuda.current_stream()
+    pshape = jb.make_shape(sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.d_model, jb.JB_BF16,
+                           jb.JB_BF16 if out_dt == torch.bfloat16 else jb.JB_F32)
+    ws_p = jb.workspace(jb.project_workspace_size(pshape), dev)
+    ws_x = jb.workspace(jb.prefill_from_x_workspace_size(pshape), dev)
+    o = torch.empty((sp.B, sp.T, sp.H, sp.dv), dtype=out_dt, device=dev)
+    S = torch.empty((sp.B, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_proj = timed(lambda: jb.project(**p, ws=ws_p, stream=stream))
+    ms_x = timed(lambda: jb.prefill_from_x(**p, out_dtype=out_dt, o=o, S_final=S, want_conv_out=False, ws=ws_x,
+                                           stream=stream))
+    tok = sp.B * sp.T
+    proj_tf = projection_flops_per_token(sp) * tok / (ms_proj * 1e-3) / 1e12
+    return dict(call="jb_prefill_from_x (projections from x, generator, recurrence)", tokens=tok,
+                ms=round(ms_x, 4), tokens_per_s=round(tok / (ms_x * 1e-3), 1),
+                project=dict(call="jb_project (q, k, v, gates, taps from x)", ms=round(ms_proj, 4), bound="mfma",
+                             achieved=round(proj_tf, 2), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(proj_tf / MFMA_PEAK_TFLOPS, 4),
+                             flops_per_call=projection_flops_per_token(sp) * tok))
+
+
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
     """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
     import oracle
@@ -118,6 +162,7 @@ def main():
     ap.add_argument("--event-every", type=int, default=16,
                     help="bracket every N-th decode state-update launch with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-from-x", action="store_true", help="skip the measurement of the block from x")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run three plain 256 MiB device-to-device copies, whose counter "
@@ -223,6 +268,12 @@ def main():
                     frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4), hbm_GBs=round(pre_gbs, 1),
                     hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4), flops_per_call=pre_flops,
                     avg_call_ms=round(pre_ms, 4))
+    from_x = None
+    if not args.no_from_x:
+        log("timing the block from its layer input x ...")
+        from_x = measure_from_x(jb, inputs, torch, sp, out_dt)
+        log(f"from x: {from_x['ms']:.3f} ms per prefill, projections {from_x['project']['ms']:.3f} ms "
+            f"({from_x['project']['frac'] * 100:.1f}% of the MFMA peak)")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -255,6 +306,7 @@ def main():
         "roofline": roof,
         "roofline_prefill": roof_pre,
         "cpu_baseline": cpu,
+        "from_x": from_x,
     }
     print(json.dumps(line), flush=True)
 
