@@ -328,6 +328,61 @@ jb_status jb_prefill_from_x(const jb_shape* s, const void* x, const void* Wq, co
   return hip_status(fn, e);
 }
 
+jb_status jb_decode_step_from_x_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_decode_step_from_x_workspace_size";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the projections take bf16 inputs only", fn);
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  // q, k, v, alpha, beta and the (unused) taps of the B tokens, then the projections' own
+  *bytes = qkvab_bytes(s) + a256((size_t)s->B * s->H * 4 * sizeof(float)) +
+           jb::project_workspace_bytes(s->B, s->H, s->d_model);
+  return ok();
+}
+
+jb_status jb_decode_step_from_x(const jb_shape* s, const float* S_in, float* S_out, const void* cache_in,
+                                void* cache_out, const void* x, const void* Wq, const void* Wk, const void* Wv,
+                                const void* Wa, const void* ba, const void* Wb, const void* bb, const void* W1,
+                                const void* b1, const void* W2, const void* b2, void* o_t, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_decode_step_from_x";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the projections take bf16 inputs only", fn);
+  if (!jb::decode_supported(s->dk, s->dv)) return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built", fn, s->dk, s->dv);
+  JB_PROJECTION_PTRS();
+  JB_REQUIRE_PTR(S_in); JB_REQUIRE_PTR(S_out); JB_REQUIRE_PTR(cache_in); JB_REQUIRE_PTR(cache_out);
+  JB_REQUIRE_PTR(o_t);
+  size_t need = 0;
+  jb_decode_step_from_x_workspace_size(s, &need);
+  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)s->B;
+  char* ws = static_cast<char*>(workspace);
+  void* q = ws;
+  ws += a256(n * s->H * s->dk * 2);
+  void* k = ws;
+  ws += a256(n * s->H * s->dk * 2);
+  void* v = ws;
+  ws += a256(n * s->H * s->dv * 2);
+  float* alpha = reinterpret_cast<float*>(ws);
+  ws += a256(n * s->H * sizeof(float));
+  float* beta = reinterpret_cast<float*>(ws);
+  ws += a256(n * s->H * sizeof(float));
+  float* taps = reinterpret_cast<float*>(ws);  // the step computes its own; the projection writes them here
+  ws += a256(n * s->H * 4 * sizeof(float));
+  const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  hipError_t e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa, ba, Wb, bb, W1, b1,
+                                    W2, b2, q, k, v, alpha, beta, taps, ws, hs);
+  if (e == hipSuccess)
+    e = jb::launch_decode_step(jb::IO_BF16, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
+                               cache_out, x, q, k, v, alpha, beta, W1, b1, W2, b2, o_t, hs);
+  return hip_status(fn, e);
+}
+
 jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
                       float* taps, void* stream) {
   const char* fn = "jb_gen_taps";

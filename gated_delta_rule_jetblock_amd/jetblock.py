@@ -67,9 +67,12 @@ _lib.jb_project_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_prefill_from_x_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_project.argtypes = [_S] + [_P] * 18 + [_P, _SZ, _P]
 _lib.jb_prefill_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
+_lib.jb_decode_step_from_x_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
+_lib.jb_decode_step_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
-           "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x"):
+           "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x",
+           "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -316,3 +319,26 @@ def prefill_from_x(x, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=
                                   _ptr(b2), _ptr(S0), _ptr(conv_in), _ptr(o), _ptr(S_final), _ptr(conv_out),
                                   _ptr(ws), ws.numel(), _stream(stream)))
     return dict(o=o, S_final=S_final, conv_out=conv_out)
+
+
+def decode_step_from_x(S, cache, x_t, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=None, *,
+                       out_dtype=torch.float32, S_out=None, cache_out=None, o=None, ws=None, stream=None):
+    """jb_decode_step_from_x: one decode step from the layer input x_t [B,D].  In place on S
+    and cache unless S_out/cache_out are given.  Returns dict(o, S, cache)."""
+    B, D = x_t.shape
+    H = Wa.shape[0]
+    dk, dv = Wq.shape[0] // H, Wv.shape[0] // H
+    shape = make_shape(B, 1, H, dk, dv, D, JB_BF16, _DT[out_dtype])
+    S_out = S if S_out is None else S_out
+    cache_out = cache if cache_out is None else cache_out
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=x_t.device)
+    if ws is None:
+        n = _SZ(0)
+        _check(_lib.jb_decode_step_from_x_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+        ws = workspace(n.value, x_t.device)
+    _check(_lib.jb_decode_step_from_x(ctypes.byref(shape), _ptr(S), _ptr(S_out), _ptr(cache), _ptr(cache_out),
+                                      _ptr(x_t), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wa), _ptr(ba), _ptr(Wb),
+                                      _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(o), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
+    return dict(o=o, S=S_out, cache=cache_out)

@@ -206,6 +206,22 @@ jb_status jb_prefill_from_x(const jb_shape* shape, const void* x, const void* Wq
                             const float* S0, const void* conv_in, void* o, float* S_final,
                             void* conv_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of jb_decode_step_from_x for `shape` (shape.T must be 1). */
+jb_status jb_decode_step_from_x_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_decode_step_from_x -- one decode step for B sequences from the layer
+ * input x_t [B][d_model]: jb_project on the B tokens (q, k, v and the gates
+ * into the workspace) and then jb_decode_step.  S_in, S_out, cache_in,
+ * cache_out, o_t as in jb_decode_step.
+ */
+jb_status jb_decode_step_from_x(const jb_shape* shape, const float* S_in, float* S_out,
+                                const void* cache_in, void* cache_out, const void* x_t,
+                                const void* Wq, const void* Wk, const void* Wv, const void* Wa,
+                                const void* ba, const void* Wb, const void* bb, const void* W1,
+                                const void* b1, const void* W2, const void* b2, void* o_t,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Single-stage entry points.  Each runs one stage of the path by itself so
  * that it can be checked on its own; the two calls above fuse these stages.

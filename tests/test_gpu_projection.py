@@ -108,3 +108,45 @@ def test_prefill_from_x_empty_sequence_passes_state(jb):
     r = jb.prefill_from_x(**p, S0=S0, conv_in=cache)
     torch.cuda.synchronize()
     assert torch.equal(r["S_final"], S0) and torch.equal(r["conv_out"], cache)
+
+
+@pytest.mark.parametrize("B,H,dk,dv,D", [(256, 12, 96, 256, 1536), (5, 3, 64, 128, 256)])
+def test_decode_step_from_x_vs_oracle(jb, oracle_mod, B, H, dk, dv, D):
+    """Three decode steps from x_t (2B decode shape and a small one) against the oracle's
+    projections + block step, on sampled sequences; and bitwise equal to jb_project followed
+    by jb_decode_step."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"decode_step_from_x B={B} H={H} dk={dk} dv={dv} D={D}", flush=True)
+    s = inputs.Shape(B=B, T=3, H=H, dk=dk, dv=dv, d_model=D)
+    p = inputs.projection_inputs(s, seed=B + D)          # x [B, 3, D]: three steps of x_t
+    st = inputs.state_inputs(s, seed=B)
+    d = {k: v.cuda() for k, v in p.items()}
+    W = {k: d[k] for k in ("Wq", "Wk", "Wv", "Wa", "Wb", "W1", "W2", "ba", "bb")}
+    S, cache = st["S"].cuda().clone(), st["cache"].cuda().clone()
+    S2, cache2 = S.clone(), cache.clone()
+    outs = []
+    for t in range(3):
+        xt = d["x"][:, t].contiguous()
+        r = jb.decode_step_from_x(S, cache, xt, **W)
+        outs.append(r["o"].clone())
+        pr = jb.project(xt.view(B, 1, D), **W)
+        r2 = jb.decode_step(S2, cache2, xt, pr["q"].view(B, H, dk), pr["k"].view(B, H, dk), pr["v"].view(B, H, dv),
+                            pr["alpha"].view(B, H), pr["beta"].view(B, H), W["W1"], W["W2"])
+        assert torch.equal(r["o"], r2["o"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, S2) and torch.equal(cache, cache2)
+    bs = np.array(sorted({0, B // 2, B - 1}))
+    a = _oracle_args(p)
+    So, co = to_np(st["S"])[bs], to_np(st["cache"])[bs]
+    worst = 0.0
+    for t in range(3):
+        xt = a["x"][bs, t:t + 1]
+        pr = oracle_mod.project(xt, a["Wq"], a["Wk"], a["Wv"], a["Wa"], a["Wb"], ba=a["ba"], bb=a["bb"])
+        ro = oracle_mod.decode_step(So, co, xt[:, 0], pr["q"][:, 0], pr["k"][:, 0], pr["v"][:, 0],
+                                    pr["alpha"][:, 0].astype(np.float32), pr["beta"][:, 0].astype(np.float32),
+                                    a["W1"], a["W2"])
+        worst = max(worst, rel_err(outs[t][bs], ro["o"]))
+        So, co = ro["S"], ro["cache"]
+    es = rel_err(S[bs], So)
+    print(f"  o_err={worst:.3e} S_err={es:.3e}", flush=True)
+    assert worst < TOL_BF16 and es < TOL_BF16
