@@ -79,9 +79,9 @@ def projection_flops_per_token(s) -> float:
 
 
 def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
-    """The block from its layer input x at the prefill shape (outside the timed step):
-    jb_project alone and jb_prefill_from_x, each averaged over `reps` calls bracketed by
-    HIP events on the launching stream."""
+    """The block from its layer input x (outside the timed step): jb_project alone and
+    jb_prefill_from_x at the prefill shape, jb_decode_step_from_x at the decode shape, each
+    averaged over `reps` calls bracketed by HIP events on the launching stream."""
     dev = torch.device("cuda:0")
     p = inputs.projection_inputs(sp, seed=2, device=dev)
     stream = torch.cuda.current_stream()
@@ -105,12 +105,25 @@ def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
         return e0.elapsed_time(e1) / reps
 
     ms_proj = timed(lambda: jb.project(**p, ws=ws_p, stream=stream))
+    # one decode step from x_t at the decode shape (projections over the batch + the step)
+    sd = inputs.B2_DECODE if sp.H == inputs.B2_DECODE.H else inputs.B4_DECODE
+    pd = inputs.projection_inputs(sd, seed=3, device=dev)
+    Wd = {k: pd[k] for k in ("Wq", "Wk", "Wv", "Wa", "Wb", "W1", "W2", "ba", "bb")}
+    st = inputs.state_inputs(sd, seed=3, device=dev)
+    xt = pd["x"][:, 0].contiguous()
+    od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
+    dshape = jb.make_shape(sd.B, 1, sd.H, sd.dk, sd.dv, sd.d_model)
+    ws_d = jb.workspace(jb.decode_step_from_x_workspace_size(dshape), dev)
+    us_dec = 1e3 * timed(lambda: jb.decode_step_from_x(st["S"], st["cache"], xt, **Wd, out_dtype=out_dt, o=od,
+                                                       ws=ws_d, stream=stream))
     ms_x = timed(lambda: jb.prefill_from_x(**p, out_dtype=out_dt, o=o, S_final=S, want_conv_out=False, ws=ws_x,
                                            stream=stream))
     tok = sp.B * sp.T
     proj_tf = projection_flops_per_token(sp) * tok / (ms_proj * 1e-3) / 1e12
     return dict(call="jb_prefill_from_x (projections from x, generator, recurrence)", tokens=tok,
                 ms=round(ms_x, 4), tokens_per_s=round(tok / (ms_x * 1e-3), 1),
+                decode_step_from_x=dict(call="jb_decode_step_from_x", B=sd.B, us=round(us_dec, 2),
+                                        tokens_per_s=round(sd.B / (us_dec * 1e-6), 1)),
                 project=dict(call="jb_project (q, k, v, gates, taps from x)", ms=round(ms_proj, 4), bound="mfma",
                              achieved=round(proj_tf, 2), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                              frac=round(proj_tf / MFMA_PEAK_TFLOPS, 4),
@@ -273,7 +286,8 @@ def main():
         log("timing the block from its layer input x ...")
         from_x = measure_from_x(jb, inputs, torch, sp, out_dt)
         log(f"from x: {from_x['ms']:.3f} ms per prefill, projections {from_x['project']['ms']:.3f} ms "
-            f"({from_x['project']['frac'] * 100:.1f}% of the MFMA peak)")
+            f"({from_x['project']['frac'] * 100:.1f}% of the MFMA peak), decode step from x "
+            f"{from_x['decode_step_from_x']['us']:.1f} us")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)

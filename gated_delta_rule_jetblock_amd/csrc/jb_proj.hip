@@ -37,15 +37,61 @@ size_t project_gemm_workspace_bytes() { return kGemmWorkspace; }
 
 namespace {
 
+// A GEMM plan: descriptors and the chosen algorithm for one shape, built on
+// first use and kept for the life of the process (creating them per call
+// cost more host time than a small GEMM takes on the GPU).
+struct GemmPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+};
+
 struct LtState {
   std::mutex mu;
   std::map<int, hipblasLtHandle_t> handles;  // per device
-  // (device, M, N, K, out f32) -> chosen algorithm
-  std::map<std::tuple<int, int64_t, int, int, bool>, hipblasLtMatmulAlgo_t> algos;
+  // (device, M, N, K, out f32) -> plan
+  std::map<std::tuple<int, int64_t, int, int, bool>, GemmPlan> plans;
 };
 LtState& lt() {
   static LtState s;
   return s;
+}
+
+hipError_t make_plan(hipblasLtHandle_t handle, int64_t M, int N, int K, bool y_f32, size_t ws_bytes, GemmPlan& p) {
+  const hipDataType ytype = y_f32 ? HIP_R_32F : HIP_R_16BF;
+  const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+  const uint64_t wsb = ws_bytes;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  hipError_t out = hipSuccess;
+  if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, K) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.ld, ytype, N, M, N) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) !=
+          HIPBLAS_STATUS_SUCCESS) {
+    out = hipErrorInvalidValue;
+  } else {
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int n = 0;
+    if (hipblasLtMatmulAlgoGetHeuristic(handle, p.desc, p.la, p.lb, p.ld, p.ld, pref, 1, res, &n) !=
+            HIPBLAS_STATUS_SUCCESS ||
+        n < 1)
+      out = hipErrorNotSupported;
+    else
+      p.algo = res[0].algo;
+  }
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (out != hipSuccess) {
+    if (p.ld) hipblasLtMatrixLayoutDestroy(p.ld);
+    if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+    if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+    p = GemmPlan{};
+  }
+  return out;
 }
 
 }  // namespace
@@ -53,8 +99,8 @@ LtState& lt() {
 // y[M][N] = x[M][K] W[N][K]^T, x and W bf16 row-major, y bf16 or fp32
 // row-major.  In the library's column-major terms: D[N x M] = op_T(W) B with
 // B = x^T [K x M].
-hipError_t gemm_xwt(int64_t M, int N, int K, const void* x, const void* W, void* y, bool y_f32,
-                    void* ws, size_t ws_bytes, hipStream_t stream) {
+hipError_t gemm_xwt(int64_t M, int N, int K, const void* x, const void* W, void* y, bool y_f32, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -67,57 +113,20 @@ hipError_t gemm_xwt(int64_t M, int N, int K, const void* x, const void* W, void*
     if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return hipErrorInitializationError;
     hit = s.handles.emplace(dev, h).first;
   }
-  hipblasLtHandle_t handle = hit->second;
-
-  hipblasLtMatmulDesc_t desc = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  hipError_t out = hipSuccess;
-  const hipDataType ytype = y_f32 ? HIP_R_32F : HIP_R_16BF;
-  const hipblasOperation_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-  const uint64_t wsb = ws_bytes;
-  do {
-    if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)) != HIPBLAS_STATUS_SUCCESS) {
-      out = hipErrorInvalidValue;
-      break;
-    }
-    if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, K, N, K) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, M, K) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&ld, ytype, N, M, N) != HIPBLAS_STATUS_SUCCESS) {
-      out = hipErrorInvalidValue;
-      break;
-    }
-    const auto key = std::make_tuple(dev, M, N, K, y_f32);
-    auto ait = s.algos.find(key);
-    if (ait == s.algos.end()) {
-      if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS ||
-          hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) !=
-              HIPBLAS_STATUS_SUCCESS) {
-        out = hipErrorInvalidValue;
-        break;
-      }
-      hipblasLtMatmulHeuristicResult_t res[1];
-      int n = 0;
-      if (hipblasLtMatmulAlgoGetHeuristic(handle, desc, la, lb, ld, ld, pref, 1, res, &n) != HIPBLAS_STATUS_SUCCESS ||
-          n < 1) {
-        out = hipErrorNotSupported;
-        break;
-      }
-      ait = s.algos.emplace(key, res[0].algo).first;
-    }
-    const float one = 1.f, zero = 0.f;
-    if (hipblasLtMatmul(handle, desc, &one, W, la, x, lb, &zero, y, ld, y, ld, &ait->second, ws, ws_bytes, stream) !=
-        HIPBLAS_STATUS_SUCCESS)
-      out = hipErrorLaunchFailure;
-  } while (false);
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (ld) hipblasLtMatrixLayoutDestroy(ld);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (desc) hipblasLtMatmulDescDestroy(desc);
-  return out;
+  const auto key = std::make_tuple(dev, M, N, K, y_f32);
+  auto pit = s.plans.find(key);
+  if (pit == s.plans.end()) {
+    GemmPlan p;
+    e = make_plan(hit->second, M, N, K, y_f32, ws_bytes, p);
+    if (e != hipSuccess) return e;
+    pit = s.plans.emplace(key, p).first;
+  }
+  const GemmPlan& p = pit->second;
+  const float one = 1.f, zero = 0.f;
+  if (hipblasLtMatmul(hit->second, p.desc, &one, W, p.la, x, p.lb, &zero, y, p.ld, y, p.ld, &p.algo, ws, ws_bytes,
+                      stream) != HIPBLAS_STATUS_SUCCESS)
+    return hipErrorLaunchFailure;
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------ epilogue

@@ -321,6 +321,12 @@ def prefill_from_x(x, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=
     return dict(o=o, S_final=S_final, conv_out=conv_out)
 
 
+def decode_step_from_x_workspace_size(shape: Shape) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_decode_step_from_x_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
 def decode_step_from_x(S, cache, x_t, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=None, *,
                        out_dtype=torch.float32, S_out=None, cache_out=None, o=None, ws=None, stream=None):
     """jb_decode_step_from_x: one decode step from the layer input x_t [B,D].  In place on S
@@ -334,9 +340,7 @@ def decode_step_from_x(S, cache, x_t, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=No
     if o is None:
         o = torch.empty((B, H, dv), dtype=out_dtype, device=x_t.device)
     if ws is None:
-        n = _SZ(0)
-        _check(_lib.jb_decode_step_from_x_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
-        ws = workspace(n.value, x_t.device)
+        ws = workspace(decode_step_from_x_workspace_size(shape), x_t.device)
     _check(_lib.jb_decode_step_from_x(ctypes.byref(shape), _ptr(S), _ptr(S_out), _ptr(cache), _ptr(cache_out),
                                       _ptr(x_t), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wa), _ptr(ba), _ptr(Wb),
                                       _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(o), _ptr(ws),
