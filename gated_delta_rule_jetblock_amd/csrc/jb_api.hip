@@ -186,7 +186,7 @@ jb_status jb_decode_step(const jb_shape* s, const float* S_in, float* S_out, con
   const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
   const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
   return hip_status(fn, jb::launch_decode_step(io, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
-                                               cache_out, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, b1, W2, b2, o_t,
+                                               cache_out, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, b1, W2, b2, nullptr, nullptr, nullptr, nullptr, o_t,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -334,9 +334,8 @@ jb_status jb_decode_step_from_x_workspace_size(const jb_shape* s, size_t* bytes)
   if (st) return st;
   if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the projections take bf16 inputs only", fn);
   if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
-  // q, k, v, alpha, beta and the (unused) taps of the B tokens, then the projections' own
-  *bytes = qkvab_bytes(s) + a256((size_t)s->B * s->H * 4 * sizeof(float)) +
-           jb::project_workspace_bytes(s->B, s->H, s->d_model);
+  // q, k, v of the B tokens, then the projections' own
+  *bytes = qkvab_bytes(s) + jb::project_workspace_bytes(s->B, s->H, s->d_model);
   return ok();
 }
 
@@ -368,18 +367,15 @@ jb_status jb_decode_step_from_x(const jb_shape* s, const float* S_in, float* S_o
   ws += a256(n * s->H * s->dk * 2);
   void* v = ws;
   ws += a256(n * s->H * s->dv * 2);
-  float* alpha = reinterpret_cast<float*>(ws);
-  ws += a256(n * s->H * sizeof(float));
-  float* beta = reinterpret_cast<float*>(ws);
-  ws += a256(n * s->H * sizeof(float));
-  float* taps = reinterpret_cast<float*>(ws);  // the step computes its own; the projection writes them here
-  ws += a256(n * s->H * 4 * sizeof(float));
   const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
-  hipError_t e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa, ba, Wb, bb, W1, b1,
-                                    W2, b2, q, k, v, alpha, beta, taps, ws, hs);
+  // q, k, v as GEMMs over the batch; the step itself forms the taps and the
+  // gates from x (its workgroups hold x_t of their sequence)
+  hipError_t e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, nullptr, nullptr,
+                                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, q, k, v, nullptr, nullptr,
+                                    nullptr, ws, hs);
   if (e == hipSuccess)
     e = jb::launch_decode_step(jb::IO_BF16, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
-                               cache_out, x, q, k, v, alpha, beta, W1, b1, W2, b2, o_t, hs);
+                               cache_out, x, q, k, v, nullptr, nullptr, W1, b1, W2, b2, Wa, ba, Wb, bb, o_t, hs);
   return hip_status(fn, e);
 }
 

@@ -56,14 +56,17 @@ hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const fl
 // One whole decode step in one launch (generator taps, conv and state update
 // for B tokens); no workspace.
 int decode_seq_heads_per_group(int B, int H, int nw);
+// With alpha_t == NULL the gates come from x: alpha = sigmoid(Wa x + ba),
+// beta = sigmoid(Wb x + bb) (bf16 inputs only).
 hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int D, const float* S_in, float* S_out,
                               const void* cache_in, void* cache_out, const void* x_t, const void* q_t,
                               const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
-                              const void* W1, const void* b1, const void* W2, const void* b2, void* o_t,
-                              hipStream_t stream);
+                              const void* W1, const void* b1, const void* W2, const void* b2, const void* Wa,
+                              const void* ba, const void* Wb, const void* bb, void* o_t, hipStream_t stream);
 
 // The input projections (q, k, v, gates) and the generator taps from x
-// (bf16 inputs only); workspace of project_workspace_bytes(n, H, D).
+// (bf16 inputs only); workspace of project_workspace_bytes(n, H, D).  With
+// W1 == NULL only q, k, v are formed.
 size_t project_gemm_workspace_bytes();
 size_t project_workspace_bytes(int64_t n, int H, int D);
 hipError_t launch_project(int64_t n, int H, int dk, int dv, int D, const void* x, const void* Wq, const void* Wk,

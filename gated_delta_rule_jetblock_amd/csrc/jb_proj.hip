@@ -200,12 +200,13 @@ hipError_t launch_project(int64_t n, int H, int dk, int dv, int D, const void* x
   hipError_t e = hipSuccess;
   void* gws = ws;
   const size_t rowb = (size_t)D * 2;
+  e = gemm_xwt(n, H * dk, D, x, Wq, q, false, gws, kGemmWorkspace, stream);
+  if (e == hipSuccess) e = gemm_xwt(n, H * dk, D, x, Wk, k, false, gws, kGemmWorkspace, stream);
+  if (e == hipSuccess) e = gemm_xwt(n, H * dv, D, x, Wv, v, false, gws, kGemmWorkspace, stream);
+  if (e != hipSuccess || !W1) return e;  // q, k, v only
   e = hipMemcpyAsync(wg, W1, 32 * rowb, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(wg + 32 * rowb, Wa, H * rowb, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(wg + (32 + H) * rowb, Wb, H * rowb, hipMemcpyDeviceToDevice, stream);
-  if (e == hipSuccess) e = gemm_xwt(n, H * dk, D, x, Wq, q, false, gws, kGemmWorkspace, stream);
-  if (e == hipSuccess) e = gemm_xwt(n, H * dk, D, x, Wk, k, false, gws, kGemmWorkspace, stream);
-  if (e == hipSuccess) e = gemm_xwt(n, H * dv, D, x, Wv, v, false, gws, kGemmWorkspace, stream);
   if (e == hipSuccess) e = gemm_xwt(n, NZ, D, x, wg, z, true, gws, kGemmWorkspace, stream);
   if (e != hipSuccess) return e;
   proj_epilogue_kernel<<<(unsigned)((n + EP_TOK - 1) / EP_TOK), EP_THR, 0, stream>>>(

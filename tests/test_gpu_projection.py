@@ -113,8 +113,9 @@ def test_prefill_from_x_empty_sequence_passes_state(jb):
 @pytest.mark.parametrize("B,H,dk,dv,D", [(256, 12, 96, 256, 1536), (5, 3, 64, 128, 256)])
 def test_decode_step_from_x_vs_oracle(jb, oracle_mod, B, H, dk, dv, D):
     """Three decode steps from x_t (2B decode shape and a small one) against the oracle's
-    projections + block step, on sampled sequences; and bitwise equal to jb_project followed
-    by jb_decode_step."""
+    projections + block step, on sampled sequences; and against jb_project followed by
+    jb_decode_step (the step from x forms its gates inside the decode kernel, in another
+    summation order than the projection GEMM, so the two agree to fp32 rounding)."""
     from gated_delta_rule_jetblock_amd import inputs
     print(f"decode_step_from_x B={B} H={H} dk={dk} dv={dv} D={D}", flush=True)
     s = inputs.Shape(B=B, T=3, H=H, dk=dk, dv=dv, d_model=D)
@@ -132,9 +133,9 @@ def test_decode_step_from_x_vs_oracle(jb, oracle_mod, B, H, dk, dv, D):
         pr = jb.project(xt.view(B, 1, D), **W)
         r2 = jb.decode_step(S2, cache2, xt, pr["q"].view(B, H, dk), pr["k"].view(B, H, dk), pr["v"].view(B, H, dv),
                             pr["alpha"].view(B, H), pr["beta"].view(B, H), W["W1"], W["W2"])
-        assert torch.equal(r["o"], r2["o"])
+        assert rel_err(r["o"], to_np(r2["o"])) < 1e-5
     torch.cuda.synchronize()
-    assert torch.equal(S, S2) and torch.equal(cache, cache2)
+    assert rel_err(S, to_np(S2)) < 1e-5 and torch.equal(cache, cache2)
     bs = np.array(sorted({0, B // 2, B - 1}))
     a = _oracle_args(p)
     So, co = to_np(st["S"])[bs], to_np(st["cache"])[bs]
