@@ -53,6 +53,8 @@ def _load():
         _lib.jbo_l2norm.argtypes = [L, I, P, P]
         _lib.jbo_l2norm.restype = I
         _lib.jbo_project.argtypes = [L, I, I, I, I] + [P] * 16 + [I]
+        _lib.jbo_prefill_static.argtypes = [I] * 6 + [P] * 17 + [I]
+        _lib.jbo_prefill_static.restype = I
         _lib.jbo_project.restype = I
         _lib.jbo_bf16_round.argtypes = [ctypes.c_double]
         _lib.jbo_bf16_round.restype = ctypes.c_double
@@ -222,3 +224,39 @@ def prefill_from_x(x, Wq, Wk, Wv, Wa, Wb, W1, W2, bq=None, bk=None, bv=None, ba=
                 W1, W2, b1=b1, b2=b2, S0=S0, conv_in=conv_in, nthreads=nthreads)
     r["proj"] = pr
     return r
+
+
+def prefill_static(q, k, v, alpha, beta, wq, wk, wv, S0=None, cache_q=None, cache_k=None, cache_v=None,
+                   nthreads: int | None = None):
+    """The static-conv Gated DeltaNet block (jbo_prefill_static): per-channel causal convs of
+    size K with fixed weights wq, wk [H*dk, K], wv [H*dv, K] on q, k, v, then the recurrence.
+
+    Returns dict(o [B,T,H,dv] f64, S_final f64, cache_q, cache_k, cache_v [B,K-1,H,d] f32)."""
+    q, k, v, alpha, beta = _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(beta)
+    wq, wk, wv, S0 = _f32(wq), _f32(wk), _f32(wv), _f32(S0)
+    cache_q, cache_k, cache_v = _f32(cache_q), _f32(cache_k), _f32(cache_v)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    K = wq.shape[1]
+    assert wq.shape == (H * dk, K) and wk.shape == (H * dk, K) and wv.shape == (H * dv, K)
+    o = np.empty((B, T, H, dv), np.float64)
+    S = np.empty((B, H, dk, dv), np.float64)
+    cq = np.empty((B, K - 1, H, dk), np.float32)
+    ck = np.empty((B, K - 1, H, dk), np.float32)
+    cv = np.empty((B, K - 1, H, dv), np.float32)
+    rc = _load().jbo_prefill_static(B, T, H, dk, dv, K, _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(wq),
+                                    _p(wk), _p(wv), _p(S0), _p(cache_q), _p(cache_k), _p(cache_v), _p(o), _p(S),
+                                    _p(cq), _p(ck), _p(cv), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("jbo_prefill_static rejected its arguments")
+    return dict(o=o, S_final=S, cache_q=cq, cache_k=ck, cache_v=cv)
+
+
+def decode_step_static(S, cache_q, cache_k, cache_v, q_t, k_t, v_t, alpha_t, beta_t, wq, wk, wv,
+                       nthreads: int | None = None):
+    """One decode step of the static-conv block (prefill_static with T = 1); q_t, k_t [B,H,dk],
+    v_t [B,H,dv], alpha_t, beta_t [B,H].  Returns dict(o [B,H,dv], S, cache_q, cache_k, cache_v)."""
+    r = prefill_static(np.asarray(q_t)[:, None], np.asarray(k_t)[:, None], np.asarray(v_t)[:, None],
+                       np.asarray(alpha_t)[:, None], np.asarray(beta_t)[:, None], wq, wk, wv, S0=S,
+                       cache_q=cache_q, cache_k=cache_k, cache_v=cache_v, nthreads=nthreads)
+    return dict(o=r["o"][:, 0], S=r["S_final"], cache_q=r["cache_q"], cache_k=r["cache_k"], cache_v=r["cache_v"])

@@ -171,6 +171,36 @@ typedef struct {
   int unit0, unit1; /* (b, h) units [unit0, unit1) */
 } rec_job;
 
+/* L2 normalisation of one row: out = x (sum x^2 + eps)^(-1/2) */
+static void l2n_row(const double* x, int n, double* out) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += x[i] * x[i];
+  const double r = 1.0 / sqrt(s + JBO_EPS);
+  for (int i = 0; i < n; ++i) out[i] = x[i] * r;
+}
+
+/* One token of the recurrence on normalised qh, kh and the convolved value vc:
+     S_t = a S_{t-1} (I - b k k^T) + b v' k^T, written for M = S^T:
+     M <- a (M - b k (k^T M)) + b k v'^T,   o_t = S_t q = M^T q. */
+static void rec_step(double* M, const double* qh, const double* kh, const double* vc,
+                     double a, double be, int dk, int dv, double* kM, double* ot) {
+  for (int c = 0; c < dv; ++c) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += kh[i] * M[(int64_t)i * dv + c];
+    kM[c] = s;
+  }
+  for (int i = 0; i < dk; ++i)
+    for (int c = 0; c < dv; ++c) {
+      double* m = &M[(int64_t)i * dv + c];
+      *m = a * (*m - be * kh[i] * kM[c]) + be * kh[i] * vc[c];
+    }
+  for (int c = 0; c < dv; ++c) {
+    double s = 0.0;
+    for (int i = 0; i < dk; ++i) s += M[(int64_t)i * dv + c] * qh[i];
+    ot[c] = s;
+  }
+}
+
 static void* rec_worker(void* p) {
   rec_job* J = (rec_job*)p;
   const int T = J->T, H = J->H, dk = J->dk, dv = J->dv, K = J->K;
@@ -189,37 +219,13 @@ static void* rec_worker(void* p) {
       /* value convolution with the per-token taps */
       conv_one(b, t, h, T, H, dv, K, J->taps + bth * K, J->v, J->conv_in, vc);
       /* L2-normalised query and key */
-      double sq = 0.0, sk = 0.0;
       for (int i = 0; i < dk; ++i) {
-        double a = J->q[bth * dk + i], c = J->k[bth * dk + i];
-        sq += a * a;
-        sk += c * c;
+        qh[i] = (double)J->q[bth * dk + i];
+        kh[i] = (double)J->k[bth * dk + i];
       }
-      double rq = 1.0 / sqrt(sq + JBO_EPS), rk = 1.0 / sqrt(sk + JBO_EPS);
-      for (int i = 0; i < dk; ++i) {
-        qh[i] = (double)J->q[bth * dk + i] * rq;
-        kh[i] = (double)J->k[bth * dk + i] * rk;
-      }
-      const double a = J->alpha[bth], be = J->beta[bth];
-      /* S_t = a S_{t-1} (I - b k k^T) + b v' k^T, written for M = S^T:
-         M <- a (M - b k (k^T M)) + b k v'^T */
-      for (int c = 0; c < dv; ++c) {
-        double s = 0.0;
-        for (int i = 0; i < dk; ++i) s += kh[i] * M[(int64_t)i * dv + c];
-        kM[c] = s;
-      }
-      for (int i = 0; i < dk; ++i)
-        for (int c = 0; c < dv; ++c) {
-          double* m = &M[(int64_t)i * dv + c];
-          *m = a * (*m - be * kh[i] * kM[c]) + be * kh[i] * vc[c];
-        }
-      /* o_t = S_t q = M^T q */
-      double* ot = J->o + bth * dv;
-      for (int c = 0; c < dv; ++c) {
-        double s = 0.0;
-        for (int i = 0; i < dk; ++i) s += M[(int64_t)i * dv + c] * qh[i];
-        ot[c] = s;
-      }
+      l2n_row(qh, dk, qh);
+      l2n_row(kh, dk, kh);
+      rec_step(M, qh, kh, vc, J->alpha[bth], J->beta[bth], dk, dv, kM, J->o + bth * dv);
     }
     if (J->S_final)
       for (int64_t i = 0; i < (int64_t)dk * dv; ++i) J->S_final[sbase + i] = M[i];
@@ -385,5 +391,115 @@ int jbo_project(int64_t n_tokens, int D, int H, int dk, int dv, const float* x,
     for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
   free(th);
   free(jobs);
+  return 0;
+}
+
+/* ------------------------------------------- static-conv Gated DeltaNet block */
+/*
+ * The block JetBlock replaces (csdn translation, section 2.4: earlier linear
+ * attention blocks use static convolution kernels; JetBlock applies a
+ * dynamic kernel to V and drops the static ones on Q and K).  Readings (the
+ * pages give no detail): a depthwise causal convolution of size K per
+ * channel with fixed weights on each of q, k and v, tap j (0..K-1)
+ * multiplying token t-(K-1)+j, no activation; q and k are L2-normalised after
+ * their convolution; the recurrence is the same.  Rows before the start come
+ * from each tensor's own cache (raw rows, oldest first) or are zero.
+ *
+ * Layouts: q, k [B][T][H][dk]; v [B][T][H][dv]; wq, wk [H*dk][K];
+ * wv [H*dv][K]; cq, ck [B][K-1][H][dk]; cv [B][K-1][H][dv] (in and out).
+ */
+
+/* raw row of a [B][T][H][d] tensor for token t, or of its cache when t < 0 */
+static const float* raw_row(int t, int b, int h, int T, int H, int d, int K, const float* x,
+                            const float* cache) {
+  if (t >= 0) return x + (((int64_t)b * T + t) * H + h) * d;
+  if (!cache) return NULL;
+  return cache + (((int64_t)b * (K - 1) + (K - 1) + t) * H + h) * d;
+}
+
+/* out[c] = sum_j w[c][j] x_{t-(K-1)+j}[c] for one (b, t, h) */
+static void static_conv_one(int b, int t, int h, int T, int H, int d, int K, const float* x,
+                            const float* cache, const float* w, double* out) {
+  for (int c = 0; c < d; ++c) out[c] = 0.0;
+  for (int j = 0; j < K; ++j) {
+    const float* row = raw_row(t - (K - 1) + j, b, h, T, H, d, K, x, cache);
+    if (!row) continue;
+    for (int c = 0; c < d; ++c) out[c] += (double)w[((int64_t)h * d + c) * K + j] * (double)row[c];
+  }
+}
+
+typedef struct {
+  int B, T, H, dk, dv, K;
+  const float *q, *k, *v, *alpha, *beta, *wq, *wk, *wv, *S0, *cq, *ck, *cv;
+  double *o, *S_final;
+  int unit0, unit1;
+} rec_static_job;
+
+static void* rec_static_worker(void* p) {
+  rec_static_job* J = (rec_static_job*)p;
+  const int T = J->T, H = J->H, dk = J->dk, dv = J->dv, K = J->K;
+  double* M = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+  double* qh = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+  double* vc = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* kM = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (int u = J->unit0; u < J->unit1; ++u) {
+    const int b = u / H, h = u % H;
+    const int64_t sbase = ((int64_t)b * H + h) * dk * dv;
+    for (int64_t i = 0; i < (int64_t)dk * dv; ++i) M[i] = J->S0 ? (double)J->S0[sbase + i] : 0.0;
+    for (int t = 0; t < T; ++t) {
+      const int64_t bth = ((int64_t)b * T + t) * H + h;
+      static_conv_one(b, t, h, T, H, dk, K, J->q, J->cq, J->wq, qh);
+      static_conv_one(b, t, h, T, H, dk, K, J->k, J->ck, J->wk, kh);
+      static_conv_one(b, t, h, T, H, dv, K, J->v, J->cv, J->wv, vc);
+      l2n_row(qh, dk, qh);
+      l2n_row(kh, dk, kh);
+      rec_step(M, qh, kh, vc, J->alpha[bth], J->beta[bth], dk, dv, kM, J->o + bth * dv);
+    }
+    if (J->S_final)
+      for (int64_t i = 0; i < (int64_t)dk * dv; ++i) J->S_final[sbase + i] = M[i];
+  }
+  free(M); free(qh); free(kh); free(vc); free(kM);
+  return NULL;
+}
+
+/* the last K-1 raw rows of [cache; x] into cache_out */
+static void tail_rows(int B, int T, int H, int d, int K, const float* x, const float* cache,
+                      float* out) {
+  for (int b = 0; b < B; ++b)
+    for (int s = 0; s < K - 1; ++s)
+      for (int h = 0; h < H; ++h) {
+        const float* row = raw_row(T - (K - 1) + s, b, h, T, H, d, K, x, cache);
+        float* dst = out + (((int64_t)b * (K - 1) + s) * H + h) * d;
+        for (int c = 0; c < d; ++c) dst[c] = row ? row[c] : 0.0f;
+      }
+}
+
+int jbo_prefill_static(int B, int T, int H, int dk, int dv, int K, const float* q, const float* k,
+                       const float* v, const float* alpha, const float* beta, const float* wq,
+                       const float* wk, const float* wv, const float* S0, const float* cq_in,
+                       const float* ck_in, const float* cv_in, double* o, double* S_final,
+                       float* cq_out, float* ck_out, float* cv_out, int nthreads) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || K < 1) return 1;
+  if (!q || !k || !v || !alpha || !beta || !wq || !wk || !wv || !o) return 1;
+  const int units = B * H;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = units > 0 ? units : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  rec_static_job* jobs = (rec_static_job*)malloc(sizeof(rec_static_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (rec_static_job){B, T, H, dk, dv, K, q, k, v, alpha, beta, wq, wk, wv, S0, cq_in, ck_in, cv_in,
+                               o, S_final, (int)((int64_t)units * i / nthreads),
+                               (int)((int64_t)units * (i + 1) / nthreads)};
+    if (nthreads == 1) rec_static_worker(&jobs[i]);
+    else pthread_create(&th[i], NULL, rec_static_worker, &jobs[i]);
+  }
+  if (nthreads > 1)
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  if (cq_out) tail_rows(B, T, H, dk, K, q, cq_in, cq_out);
+  if (ck_out) tail_rows(B, T, H, dk, K, k, ck_in, ck_out);
+  if (cv_out) tail_rows(B, T, H, dv, K, v, cv_in, cv_out);
   return 0;
 }
