@@ -379,6 +379,101 @@ jb_status jb_decode_step_from_x(const jb_shape* s, const float* S_in, float* S_o
   return hip_status(fn, e);
 }
 
+namespace {
+
+jb_status check_static_prefill(const char* fn, const jb_shape* s, jb::PrefillPlan* p) {
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  *p = plan_of(s);
+  if (!jb::prefill_static_supported(*p))
+    return fail(JB_ERR_UNSUPPORTED,
+                "%s: the static-conv prefill is built for bf16 inputs and (dk, dv) in {(32,64), (64,128), (96,256), "
+                "(128,256)}; got io_dtype %d, dk=%d dv=%d", fn, s->io_dtype, s->dk, s->dv);
+  if (seg_flag(s) < 0) return fail(JB_ERR_INVALID_ARG, "%s: bad segment flag", fn);
+  return JB_OK;
+}
+
+}  // namespace
+
+jb_status jb_prefill_static_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_prefill_static_workspace_size";
+  jb::PrefillPlan p;
+  jb_status st = check_static_prefill(fn, s, &p);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = jb::prefill_static_workspace_bytes(p);
+  return ok();
+}
+
+jb_status jb_prefill_static(const jb_shape* s, const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* wq, const float* wk, const float* wv, const float* S0,
+                            const void* cache_q_in, const void* cache_k_in, const void* cache_v_in, void* o,
+                            float* S_final, void* cache_q_out, void* cache_k_out, void* cache_v_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_prefill_static";
+  jb::PrefillPlan p;
+  jb_status st = check_static_prefill(fn, s, &p);
+  if (st) return st;
+  if (s->T > 0) {
+    JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v);
+    JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta); JB_REQUIRE_PTR(o);
+  }
+  JB_REQUIRE_PTR(wq); JB_REQUIRE_PTR(wk); JB_REQUIRE_PTR(wv); JB_REQUIRE_PTR(S_final);
+  JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(cache_q_in); JB_OPTIONAL_PTR(cache_k_in); JB_OPTIONAL_PTR(cache_v_in);
+  JB_OPTIONAL_PTR(cache_q_out); JB_OPTIONAL_PTR(cache_k_out); JB_OPTIONAL_PTR(cache_v_out);
+  if (!cache_q_in != !cache_k_in || !cache_q_in != !cache_v_in)
+    return fail(JB_ERR_INVALID_ARG, "%s: cache_q_in, cache_k_in and cache_v_in must be all set or all NULL", fn);
+  const size_t need = jb::prefill_static_workspace_bytes(p);
+  if (need && !workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if (workspace && ((uintptr_t)workspace & 255u))
+    return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (s->T == 0) {
+    if (S0 && S0 != S_final)
+      e = hipMemcpyAsync(S_final, S0, (size_t)s->B * s->H * s->dk * s->dv * sizeof(float), hipMemcpyDeviceToDevice, hs);
+    else if (!S0)
+      e = jb::launch_fill_zero(S_final, (size_t)s->B * s->H * s->dk * s->dv, hs);
+  } else {
+    e = jb::launch_prefill_static(p, q, k, v, alpha, beta, wq, wk, wv, cache_q_in, cache_k_in, cache_v_in, S0, o,
+                                  S_final, workspace, hs);
+  }
+  // the caches' tails after the chunk kernels, which read the incoming caches
+  if (e == hipSuccess && cache_q_out)
+    e = jb::launch_conv_tail(jb::IO_BF16, s->B, s->T, s->H, s->dk, q, cache_q_in, cache_q_out, hs);
+  if (e == hipSuccess && cache_k_out)
+    e = jb::launch_conv_tail(jb::IO_BF16, s->B, s->T, s->H, s->dk, k, cache_k_in, cache_k_out, hs);
+  if (e == hipSuccess && cache_v_out)
+    e = jb::launch_conv_tail(jb::IO_BF16, s->B, s->T, s->H, s->dv, v, cache_v_in, cache_v_out, hs);
+  return hip_status(fn, e);
+}
+
+jb_status jb_decode_step_static(const jb_shape* s, const float* S_in, float* S_out, const void* cache_q_in,
+                                const void* cache_k_in, const void* cache_v_in, void* cache_q_out, void* cache_k_out,
+                                void* cache_v_out, const void* q_t, const void* k_t, const void* v_t,
+                                const float* alpha_t, const float* beta_t, const float* wq, const float* wk,
+                                const float* wv, void* o_t, void* stream) {
+  const char* fn = "jb_decode_step_static";
+  jb_status st = check_shape(fn, s, true);
+  if (st) return st;
+  if (!jb::decode_supported(s->dk, s->dv)) return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built", fn, s->dk, s->dv);
+  JB_REQUIRE_PTR(S_in); JB_REQUIRE_PTR(S_out);
+  JB_REQUIRE_PTR(cache_q_in); JB_REQUIRE_PTR(cache_k_in); JB_REQUIRE_PTR(cache_v_in);
+  JB_REQUIRE_PTR(cache_q_out); JB_REQUIRE_PTR(cache_k_out); JB_REQUIRE_PTR(cache_v_out);
+  JB_REQUIRE_PTR(q_t); JB_REQUIRE_PTR(k_t); JB_REQUIRE_PTR(v_t);
+  JB_REQUIRE_SCALARS(alpha_t); JB_REQUIRE_SCALARS(beta_t);
+  JB_REQUIRE_PTR(wq); JB_REQUIRE_PTR(wk); JB_REQUIRE_PTR(wv); JB_REQUIRE_PTR(o_t);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  return hip_status(fn, jb::launch_decode_static(io, out, s->B, s->H, s->dk, s->dv, S_in, S_out, cache_q_in,
+                                                 cache_k_in, cache_v_in, cache_q_out, cache_k_out, cache_v_out, q_t,
+                                                 k_t, v_t, alpha_t, beta_t, wq, wk, wv, o_t,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
                       float* taps, void* stream) {
   const char* fn = "jb_gen_taps";

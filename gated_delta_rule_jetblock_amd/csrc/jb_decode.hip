@@ -47,6 +47,59 @@ __device__ __forceinline__ void st(float* p, const float (&o)[CPL]) {
   *reinterpret_cast<V*>(p) = t;
 }
 
+// The part of a decode step after staging, for the 4 waves of a (head,
+// sequence) workgroup: wave `wave` holds rows wave*DK/4 .. of M in m, and
+// sk, sq (normalised k, q) and sv (v') are in LDS behind a barrier.
+template <int DK, int DV, typename OUT>
+__device__ __forceinline__ void decode_update(float (&m)[DK / 4][DV / 64], const float* sk, const float* sq,
+                                              const float* sv, float (&sred)[2][4][DV], float al, float be,
+                                              int64_t bh, OUT* o_t, float* Mout, int wave, int lane) {
+  constexpr int RPW = DK / 4;   // rows per wave
+  constexpr int CPL = DV / 64;  // columns per lane
+  // partial column sums over this wave's rows
+  float pa[CPL], pc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) { pa[i] = 0.f; pc[i] = 0.f; }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float kr = sk[wave * RPW + r], qr = sq[wave * RPW + r];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) { pa[i] += m[r][i] * kr; pc[i] += m[r][i] * qr; }
+  }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    sred[0][wave][lane * CPL + i] = pa[i];
+    sred[1][wave][lane * CPL + i] = pc[i];
+  }
+  // k.q for the output term (every wave computes it from LDS)
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int d = lane + 64 * e;
+    if (d < DK) kq += sk[d] * sq[d];
+  }
+  kq = wave_sum(kq);
+  __syncthreads();
+
+  float u[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane * CPL + i;
+    const float av = sred[0][0][c] + sred[0][1][c] + sred[0][2][c] + sred[0][3][c];
+    const float cv = sred[1][0][c] + sred[1][1][c] + sred[1][2][c] + sred[1][3][c];
+    u[i] = be * (sv[c] - al * av);
+    if (wave == 0) o_t[bh * DV + c] = from_f32<OUT>(al * cv + kq * u[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float kr = sk[wave * RPW + r];
+    float nm[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) nm[i] = al * m[r][i] + kr * u[i];
+    st<CPL>(Mout + (int64_t)r * DV, nm);
+  }
+}
+
 template <int DK, int DV, typename IO, typename OUT>
 __global__ __launch_bounds__(256) void decode_kernel(int H, const float* S_in, float* S_out, const IO* cache_in,
                                                      IO* cache_out, const IO* q_t, const IO* k_t, const IO* v_t,
@@ -105,48 +158,80 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, const float* S_in, f
   }
   __syncthreads();
 
-  // partial column sums over this wave's rows
-  float pa[CPL], pc[CPL];
+  decode_update<DK, DV, OUT>(m, sk, sq, sv, sred, al, be, bh, o_t, Mout, wave, lane);
+}
+
+// One decode step of the static-conv block, the one JetBlock replaces
+// (Jet-Nemotron csdn translation, section 2.4: earlier linear-attention
+// blocks convolve with fixed kernels).  Read here as a causal depthwise conv
+// of size 4 with fixed weights on each of q, k and v, no activation, q and k
+// normalised after it.  Wave 0 convolves q and k from their caches and
+// normalises them, wave 1 forms v'; both shift their caches.  The rest is the
+// update above.  Each cache element is read before it is written by the
+// same thread, so a cache may be updated in place.
+template <int DK, int DV, typename IO, typename OUT>
+__global__ __launch_bounds__(256) void decode_static_kernel(int H, const float* S_in, float* S_out, const IO* cq_in,
+                                                            const IO* ck_in, const IO* cv_in, IO* cq_out, IO* ck_out,
+                                                            IO* cv_out, const IO* q_t, const IO* k_t, const IO* v_t,
+                                                            const float* alpha_t, const float* beta_t, const float* wq,
+                                                            const float* wk, const float* wv, OUT* o_t) {
+  constexpr int RPW = DK / 4;
+  constexpr int CPL = DV / 64;
+  __shared__ float sk[DK], sq[DK], sv[DV];
+  __shared__ float sred[2][4][DV];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t bh = (int64_t)b * H + h;
+  const float* Min = S_in + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+  float* Mout = S_out + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+
+  float m[RPW][CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) { pa[i] = 0.f; pc[i] = 0.f; }
+  for (int r = 0; r < RPW; ++r) ld<CPL>(Min + (int64_t)r * DV, m[r]);
+
+  const float al = alpha_t[bh], be = beta_t[bh];
+  if (wave == 0) {
+    float kx[2], qx[2];
+    float sk2 = 0.f, sq2 = 0.f;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float kr = sk[wave * RPW + r], qr = sq[wave * RPW + r];
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      kx[e] = qx[e] = 0.f;
+      if (d < DK) {
+        const int64_t r0 = (int64_t)b * 3 * H * DK + (int64_t)h * DK + d, rs = (int64_t)H * DK;
+        const IO k0 = ck_in[r0], k1 = ck_in[r0 + rs], k2 = ck_in[r0 + 2 * rs], kt = k_t[bh * DK + d];
+        const IO q0 = cq_in[r0], q1 = cq_in[r0 + rs], q2 = cq_in[r0 + 2 * rs], qt = q_t[bh * DK + d];
+        const float4 wkd = *reinterpret_cast<const float4*>(wk + ((int64_t)h * DK + d) * 4);
+        const float4 wqd = *reinterpret_cast<const float4*>(wq + ((int64_t)h * DK + d) * 4);
+        kx[e] = wkd.x * to_f32<IO>(k0) + wkd.y * to_f32<IO>(k1) + wkd.z * to_f32<IO>(k2) + wkd.w * to_f32<IO>(kt);
+        qx[e] = wqd.x * to_f32<IO>(q0) + wqd.y * to_f32<IO>(q1) + wqd.z * to_f32<IO>(q2) + wqd.w * to_f32<IO>(qt);
+        ck_out[r0] = k1; ck_out[r0 + rs] = k2; ck_out[r0 + 2 * rs] = kt;
+        cq_out[r0] = q1; cq_out[r0 + rs] = q2; cq_out[r0 + 2 * rs] = qt;
+      }
+      sk2 += kx[e] * kx[e];
+      sq2 += qx[e] * qx[e];
+    }
+    const float rk = l2_scale(wave_sum(sk2)), rq = l2_scale(wave_sum(sq2));
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) { pa[i] += m[r][i] * kr; pc[i] += m[r][i] * qr; }
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < DK) { sk[d] = kx[e] * rk; sq[d] = qx[e] * rq; }
+    }
+  } else if (wave == 1) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane * CPL + i;
+      const int64_t r0 = (int64_t)b * 3 * H * DV + (int64_t)h * DV + c, rs = (int64_t)H * DV;
+      const IO c0 = cv_in[r0], c1 = cv_in[r0 + rs], c2 = cv_in[r0 + 2 * rs], vt = v_t[bh * DV + c];
+      const float4 w = *reinterpret_cast<const float4*>(wv + ((int64_t)h * DV + c) * 4);
+      sv[c] = w.x * to_f32<IO>(c0) + w.y * to_f32<IO>(c1) + w.z * to_f32<IO>(c2) + w.w * to_f32<IO>(vt);
+      cv_out[r0] = c1; cv_out[r0 + rs] = c2; cv_out[r0 + 2 * rs] = vt;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    sred[0][wave][lane * CPL + i] = pa[i];
-    sred[1][wave][lane * CPL + i] = pc[i];
-  }
-  // k.q for the output term (every wave computes it from LDS)
-  float kq = 0.f;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int d = lane + 64 * e;
-    if (d < DK) kq += sk[d] * sq[d];
-  }
-  kq = wave_sum(kq);
   __syncthreads();
 
-  float u[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane * CPL + i;
-    const float av = sred[0][0][c] + sred[0][1][c] + sred[0][2][c] + sred[0][3][c];
-    const float cv = sred[1][0][c] + sred[1][1][c] + sred[1][2][c] + sred[1][3][c];
-    u[i] = be * (sv[c] - al * av);
-    if (wave == 0) o_t[bh * DV + c] = from_f32<OUT>(al * cv + kq * u[i]);
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float kr = sk[wave * RPW + r];
-    float nm[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) nm[i] = al * m[r][i] + kr * u[i];
-    st<CPL>(Mout + (int64_t)r * DV, nm);
-  }
+  decode_update<DK, DV, OUT>(m, sk, sq, sv, sred, al, be, bh, o_t, Mout, wave, lane);
 }
 
 // ------------------------------------------------------- fused decode step
@@ -552,6 +637,43 @@ hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const fl
                                           beta_t, taps, o_t, stream);                                         \
     return run_decode<DK_, DV_, float>(out, B, H, S_in, S_out, cache_in, cache_out, q_t, k_t, v_t, alpha_t,    \
                                        beta_t, taps, o_t, stream);                                            \
+  }
+  JB_DECODE_CASES(CASE)
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t run_decode_static(int out, int B, int H, const float* S_in, float* S_out, const void* cq_in,
+                                    const void* ck_in, const void* cv_in, void* cq_out, void* ck_out, void* cv_out,
+                                    const void* q_t, const void* k_t, const void* v_t, const float* alpha_t,
+                                    const float* beta_t, const float* wq, const float* wk, const float* wv, void* o_t,
+                                    hipStream_t stream) {
+  const dim3 grid(H, B);
+#define JB_STATIC_ARGS(OUT_)                                                                                    \
+  H, S_in, S_out, (const IO*)cq_in, (const IO*)ck_in, (const IO*)cv_in, (IO*)cq_out, (IO*)ck_out, (IO*)cv_out, \
+      (const IO*)q_t, (const IO*)k_t, (const IO*)v_t, alpha_t, beta_t, wq, wk, wv, (OUT_*)o_t
+  if (out == IO_F32)
+    decode_static_kernel<DK, DV, IO, float><<<grid, 256, 0, stream>>>(JB_STATIC_ARGS(float));
+  else
+    decode_static_kernel<DK, DV, IO, bf16_t><<<grid, 256, 0, stream>>>(JB_STATIC_ARGS(bf16_t));
+#undef JB_STATIC_ARGS
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_static(int io, int out, int B, int H, int dk, int dv, const float* S_in, float* S_out,
+                                const void* cq_in, const void* ck_in, const void* cv_in, void* cq_out, void* ck_out,
+                                void* cv_out, const void* q_t, const void* k_t, const void* v_t,
+                                const float* alpha_t, const float* beta_t, const float* wq, const float* wk,
+                                const float* wv, void* o_t, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+#define CASE(DK_, DV_)                                                                                          \
+  if (dk == DK_ && dv == DV_) {                                                                                 \
+    if (io == IO_BF16)                                                                                          \
+      return run_decode_static<DK_, DV_, bf16_t>(out, B, H, S_in, S_out, cq_in, ck_in, cv_in, cq_out, ck_out,   \
+                                                 cv_out, q_t, k_t, v_t, alpha_t, beta_t, wq, wk, wv, o_t, stream); \
+    return run_decode_static<DK_, DV_, float>(out, B, H, S_in, S_out, cq_in, ck_in, cv_in, cq_out, ck_out,      \
+                                              cv_out, q_t, k_t, v_t, alpha_t, beta_t, wq, wk, wv, o_t, stream);    \
   }
   JB_DECODE_CASES(CASE)
 #undef CASE

@@ -46,12 +46,32 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
                           const void* conv_in, const float* S0, void* o, float* S_final,
                           void* workspace, hipStream_t stream);
 
+// The static-conv variant: q, k, v each pass a causal conv with fixed
+// per-channel weights wq, wk [H*dk][4], wv [H*dv][4] (f32) instead of the
+// dynamic conv on v; caches cq/ck/cv [B][3][H][d] (NULL: zeros) hold the raw
+// rows before the sequence.  bf16 inputs; workspace of
+// prefill_static_workspace_bytes (segment buffers only).
+size_t prefill_static_workspace_bytes(const PrefillPlan& p);
+bool prefill_static_supported(const PrefillPlan& p);
+hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* wq, const float* wk,
+                                 const float* wv, const void* cq_in, const void* ck_in, const void* cv_in,
+                                 const float* S0, void* o, float* S_final, void* workspace, hipStream_t stream);
+
 // One decode step's state update (taps precomputed).
 bool decode_supported(int dk, int dv);
 hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const float* S_in,
                          float* S_out, const void* cache_in, void* cache_out, const void* q_t,
                          const void* k_t, const void* v_t, const float* alpha_t,
                          const float* beta_t, const float* taps, void* o_t, hipStream_t stream);
+
+// One decode step of the static-conv block: caches cq/ck/cv [B][3][H][d]
+// (updated in place when out == in), weights as for launch_prefill_static.
+hipError_t launch_decode_static(int io, int out, int B, int H, int dk, int dv, const float* S_in, float* S_out,
+                                const void* cq_in, const void* ck_in, const void* cv_in, void* cq_out, void* ck_out,
+                                void* cv_out, const void* q_t, const void* k_t, const void* v_t,
+                                const float* alpha_t, const float* beta_t, const float* wq, const float* wk,
+                                const float* wv, void* o_t, hipStream_t stream);
 
 // One whole decode step in one launch (generator taps, conv and state update
 // for B tokens); no workspace.

@@ -57,6 +57,12 @@ struct ChunkArgs {
   const float* beta;
   const float* taps;
   const void* conv_in;
+  // static-conv mode: fixed per-channel weights [H*d][4] and the q / k caches
+  const float* wq;
+  const float* wk;
+  const float* wv;
+  const void* cq_in;
+  const void* ck_in;
   const float* S0;      // output kernel with one segment only
   const float* Mstart;  // [B][H][nseg][DK][DV] start states (several segments)
   float* Dsum;          // [B][H][nseg][DK][DV]
@@ -73,7 +79,7 @@ struct ChunkArgs {
 // row stride is 2 (mod 4) dwords for fp16 and 4 (mod 8) dwords for fp32
 // tiles, so the lanes of a group spread over distinct banks.
 
-template <int DK, int DV, typename IO, typename OP, int MODE>
+template <int DK, int DV, typename IO, typename OP, int MODE, bool SC>
 struct Lds {
   static constexpr int LDK = DK + 4;                     // [C][DK] tiles
   static constexpr int LC = C + 4;                       // [*][C] tiles
@@ -84,20 +90,23 @@ struct Lds {
   static constexpr int szKt = DK * LC * (int)sizeof(OP);
   static constexpr int szQh = MODE == MODE_OUTPUT ? C * LDK * (int)sizeof(OP) : 0;
   static constexpr int szV = (C + 3) * LVB;
-  static constexpr int szTap = C * 4 * 4;
+  static constexpr int szTap = SC ? 0 : C * 4 * 4;
   static constexpr int szScal = 4 * C * 4;
   static constexpr int szW = C * LDK * (int)sizeof(OP);
   static constexpr int szAn = C * LC * (int)sizeof(OP);
   static constexpr int szAd = C * LAD * 4;
   static constexpr int szLi = C * LLI * (int)sizeof(OP);
   static constexpr int szP = MODE == MODE_OUTPUT ? C * LC * (int)sizeof(OP) : 0;
-  static constexpr int szRaw = C * DK * (int)sizeof(IO);                   // raw q or k rows of a chunk
+  // raw q or k rows of a chunk (static conv: with the 3-row halo in front, like the values)
+  static constexpr int szRaw = (SC ? C + 3 : C) * DK * (int)sizeof(IO);
   static constexpr int szQraw = MODE == MODE_OUTPUT ? szRaw : 0;
-  static constexpr int szGraw = C * 4 * 2 + C * 16;                        // raw alpha, beta, taps
+  static constexpr int szGraw = C * 4 * 2 + (SC ? 0 : C * 16);             // raw alpha, beta, taps
   // bf16 inputs: the band T of the right-hand side diag(b) V' = T V_ext, as
   // [hi, lo][row tile][16 rows][LT] bf16 (32 columns used)
   static constexpr int LT = 32 + 8;
-  static constexpr int szT = sizeof(IO) == 2 ? 2 * 4 * 16 * LT * 2 : 0;
+  static constexpr int szT = sizeof(IO) == 2 && !SC ? 2 * 4 * 16 * LT * 2 : 0;
+  // static conv: the head's weights, q and k tap-major [4][DK] f32 each, v as one float4 per column [DV]
+  static constexpr int szCw = SC ? (2 * DK + DV) * 16 : 0;
 
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   // small per-row arrays first, then the raw q / k staging (the -A region
@@ -118,7 +127,8 @@ struct Lds {
   static constexpr int oKh = a16(oQh + szQh);
   static constexpr int oV = a16(oKh + szKh);
   static constexpr int oT = a16(oV + szV);
-  static constexpr int total = a16(oT + szT);
+  static constexpr int oCw = a16(oT + szT);
+  static constexpr int total = a16(oCw + szCw);
   // raw k rows of the next chunk land in the -A / diagonal-block region, dead
   // while a chunk's column phase runs and rewritten only after the prologue
   static constexpr int oKraw = oAn;
@@ -192,6 +202,26 @@ struct Prologue {
   }
 };
 
+// Static-conv prologue: four channels d0 .. d0+3 of row `row` of the
+// convolved q or k, from raw staged rows [C+3][DK] where row r + j holds
+// token t0 + r - 3 + j, and tap-major weights w [4][DK]:
+// x[i] = sum_j w[j][d0 + i] raw[row + j][d0 + i].
+template <int DK, typename IO>
+__device__ __forceinline__ void conv4(const IO* raw, const float* w, int row, int d0, bool valid, float (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4 wj = *reinterpret_cast<const float4*>(w + j * DK + d0);
+    float r[4];
+    load_row_part<IO>(raw + (row + j) * DK + d0, r, 4, valid);
+    x[0] += wj.x * r[0];
+    x[1] += wj.y * r[1];
+    x[2] += wj.z * r[2];
+    x[3] += wj.w * r[3];
+  }
+}
+
 // g2 = inclusive cumsum of log2(alpha) over the chunk, lane = row (one wave).
 // The chunk kernels keep the gates in base 2: e^{g_i - g_j} = 2^{g2_i - g2_j}.
 __device__ __forceinline__ float chunk_gate_scan(float alpha_or_one) {
@@ -241,9 +271,9 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
 
 // ------------------------------------------------------------ chunk kernel
 
-template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE>
+template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE, bool SC>
 __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
-  using L = Lds<DK, DV, IO, OP, MODE>;
+  using L = Lds<DK, DV, IO, OP, MODE, SC>;
   constexpr int LDK = L::LDK, LC = L::LC, LVB = L::LVB, LAD = L::LAD, LLI = L::LLI;
   constexpr int NCT = MODE == MODE_SUMMARY ? (DV + DK) / 16 : DV / 16;  // column tiles
   constexpr int CPW = (NCT + NWAVE - 1) / NWAVE;                        // tiles per wave (max)
@@ -272,6 +302,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   char* sQraw = smem + L::oQraw;                            // [C][DK] raw q of the next chunk
   char* sGraw = smem + L::oGraw;                            // raw alpha [C], beta [C], taps [C][4]
   bf16_t* sT = reinterpret_cast<bf16_t*>(smem + L::oT);     // bf16 inputs: band T, hi then lo
+  float* sCwq = reinterpret_cast<float*>(smem + L::oCw);    // static conv weights: q [4][DK], k [4][DK],
+  float* sCwk = sCwq + 4 * DK;                              // v [DV] float4
+  const float4* sCwv = reinterpret_cast<const float4*>(sCwk + 4 * DK);
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
@@ -314,6 +347,22 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       const int r = e / C, c = e % C;
       if ((c >> 4) > (r >> 4)) sP[r * LC + c] = from_f32<OP>(0.f);
     }
+  // static conv: the head's weights stay in LDS for the whole segment
+  if constexpr (SC)
+    for (int e = tid; e < 2 * DK + DV; e += NTHR) {
+      if (e < 2 * DK) {
+        const int d = e % DK;
+        const float4 w = *reinterpret_cast<const float4*>((e < DK ? a.wq : a.wk) + ((int64_t)h * DK + d) * 4);
+        float* dst = e < DK ? sCwq : sCwk;
+        dst[d] = w.x;
+        dst[DK + d] = w.y;
+        dst[2 * DK + d] = w.z;
+        dst[3 * DK + d] = w.w;
+      } else {
+        const_cast<float4*>(sCwv)[e - 2 * DK] =
+            *reinterpret_cast<const float4*>(a.wv + ((int64_t)h * DV + e - 2 * DK) * 4);
+      }
+    }
 
   const int c_begin = s * a.seg_len;
   const int c_end = min(a.nchunks, c_begin + a.seg_len);
@@ -340,20 +389,48 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
     constexpr int PPK = DK / EP;                        // pieces per q or k row
-    for (int j = wave; j * 64 < C * PPK; j += NWAVE) {
-      const int p = j * 64 + lane;
-      const int r = p / PPK, pc = p % PPK;
-      if (p < C * PPK && r < nc) {
-        const int64_t off = (((int64_t)b * T + t0c + r) * H + h) * DK + pc * EP;
-        dma16(k + off, sKraw + j * 64 * 16);
-        if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+    if constexpr (!SC) {
+      for (int j = wave; j * 64 < C * PPK; j += NWAVE) {
+        const int p = j * 64 + lane;
+        const int r = p / PPK, pc = p % PPK;
+        if (p < C * PPK && r < nc) {
+          const int64_t off = (((int64_t)b * T + t0c + r) * H + h) * DK + pc * EP;
+          dma16(k + off, sKraw + j * 64 * 16);
+          if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+        }
+      }
+    } else {
+      // static conv: q and k rows t0-3 .. t0+63 like the values; rows past
+      // the sequence end are left as they are (the prologue never reads them)
+      const IO* cq = reinterpret_cast<const IO*>(a.cq_in);
+      const IO* ck = reinterpret_cast<const IO*>(a.ck_in);
+      constexpr int NPK = (C + 3) * PPK;
+      for (int j = wave; j * 64 < NPK; j += NWAVE) {
+        const int p = j * 64 + lane;
+        if (p < NPK) {
+          const int r = p / PPK, pc = p % PPK, t = t0c - 3 + r;
+          if (t >= 0) {
+            if (r - 3 < nc) {
+              const int64_t off = (((int64_t)b * T + t) * H + h) * DK + pc * EP;
+              dma16(k + off, sKraw + j * 64 * 16);
+              if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+            }
+          } else if (ck) {
+            const int64_t off = (((int64_t)b * 3 + (3 + t)) * H + h) * DK + pc * EP;
+            dma16(ck + off, sKraw + j * 64 * 16);
+            if (MODE == MODE_OUTPUT) dma16(cq + off, sQraw + j * 64 * 16);
+          } else {
+            *reinterpret_cast<uint4*>(sKraw + p * 16) = make_uint4(0u, 0u, 0u, 0u);
+            if (MODE == MODE_OUTPUT) *reinterpret_cast<uint4*>(sQraw + p * 16) = make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
       }
     }
     if (wave == GATE_WAVE && lane < nc) {
       const int64_t gidx = ((int64_t)b * T + t0c + lane) * H + h;
       dma4(a.alpha + gidx, sGraw);
       dma4(a.beta + gidx, sGraw + C * 4);
-      dma16(a.taps + gidx * 4, sGraw + C * 8);
+      if constexpr (!SC) dma16(a.taps + gidx * 4, sGraw + C * 8);
     }
   };
 
@@ -383,7 +460,51 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA transfers have landed
     __syncthreads();                // ... and every other wave's
     {
-      if (tid < PRO_THR) {
+      if (SC && tid < PRO_THR) {
+        // static conv: thread (row, part) as in Prologue; the convolved rows
+        // are formed twice, once for their norms and once to be scaled and
+        // stored, so that no thread holds a whole row part at a time
+        constexpr int E = DK / 8;
+        const int row = tid >> 3, d0 = (tid & 7) * E;
+        const bool valid = row < n;
+        const IO* kraw = reinterpret_cast<const IO*>(sKraw);
+        const IO* qraw = reinterpret_cast<const IO*>(sQraw);
+        float sk = 0.f, sq = 0.f;
+        // rolled loops: unrolled, the addresses of every group would be
+        // hoisted out of the chunk loop and spilled
+#pragma unroll 1
+        for (int e0 = 0; e0 < E; e0 += 4) {
+          const int dd = d0 + e0;
+          float x[4];
+          conv4<DK, IO>(kraw, sCwk, row, dd, valid, x);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sk += x[i] * x[i];
+          if (MODE == MODE_OUTPUT) {
+            conv4<DK, IO>(qraw, sCwq, row, dd, valid, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sq += x[i] * x[i];
+          }
+        }
+        const float rk = l2_scale(group_sum<8>(sk));
+        const float rq = MODE == MODE_OUTPUT ? l2_scale(group_sum<8>(sq)) : 0.f;
+#pragma unroll 1
+        for (int e0 = 0; e0 < E; e0 += 4) {
+          const int dd = d0 + e0;
+          float x[4];
+          conv4<DK, IO>(kraw, sCwk, row, dd, valid, x);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const OP kh = from_f32<OP>(x[i] * rk);
+            sKh[row * LDK + dd + i] = kh;
+            sKt[(dd + i) * LC + row] = kh;
+          }
+          if (MODE == MODE_OUTPUT) {
+            conv4<DK, IO>(qraw, sCwq, row, dd, valid, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sQh[row * LDK + dd + i] = from_f32<OP>(x[i] * rq);
+          }
+        }
+      } else if (tid < PRO_THR) {
         Prologue<DK, IO> pr;
         pr.load(reinterpret_cast<const IO*>(sQraw), reinterpret_cast<const IO*>(sKraw), 0, 1, n,
                 MODE == MODE_OUTPUT);
@@ -401,15 +522,16 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         const bool valid = lane < n;
         const float al = valid ? reinterpret_cast<const float*>(sGraw)[lane] : 1.f;
         const float be = valid ? reinterpret_cast<const float*>(sGraw + C * 4)[lane] : 0.f;
-        const float4 tp = valid ? reinterpret_cast<const float4*>(sGraw + C * 8)[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 tp = valid && !SC ? reinterpret_cast<const float4*>(sGraw + C * 8)[lane]
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
         const float g = chunk_gate_scan(al);
         const float gC = __shfl(g, C - 1, WAVE);
         sG[lane] = g;
         sGam[lane] = fast_exp2(g);
         sBeta[lane] = be;
         sDec[lane] = fast_exp2(gC - g);
-        *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
-        if constexpr (sizeof(IO) == 2) {
+        if constexpr (!SC) *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
+        if constexpr (sizeof(IO) == 2 && !SC) {
           // row `lane` of the band T with T[r][r + j] = b_r tap_r[j], so that the
           // right-hand side diag(b) V' = T V_ext runs on the matrix cores; row
           // tile rt multiplies the 32 staged value rows from 16 rt (from 35 for
@@ -512,7 +634,24 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       if (ct >= NCT || !(MODE == MODE_OUTPUT || ct < VCT)) continue;
       // right-hand side diag(b) V', V'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
       const int col = ct * 16 + m16;
-      if constexpr (sizeof(IO) == 2) {
+      if constexpr (SC) {
+        // static conv, per-column weights: V'[r][col] = sum_j w[col].j v[t0 + r - 3 + j][col],
+        // staged rows r .. r+3; the four rows of a lane share seven staged values
+        int wc = col;
+        asm volatile("" : "+v"(wc));  // read per chunk, not held across the loop
+        const float4 w = sCwv[wc];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          float vr[7];
+#pragma unroll
+          for (int m = 0; m < 7; ++m)
+            vr[m] = to_f32<IO>(reinterpret_cast<const IO*>(sV + (rb * 16 + 4 * g4 + m) * LVB)[col]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            U[cw][rb][i] = sBeta[rb * 16 + 4 * g4 + i] *
+                           (w.x * vr[i] + w.y * vr[i + 1] + w.z * vr[i + 2] + w.w * vr[i + 3]);
+        }
+      } else if constexpr (sizeof(IO) == 2) {
         // on the matrix cores: U0 tile rt = (T_hi + T_lo) V_ext[window rows][this column tile],
         // the value rows taken exactly as bf16 operands (K order 8g + j on both sides)
 #pragma unroll
@@ -843,33 +982,44 @@ PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, i
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t prefill_workspace_bytes(const PrefillPlan& p) {
-  // taps, then (several segments) Mstart, Dsum, Phi
-  size_t bytes = align256((size_t)p.B * p.T * p.H * 4 * sizeof(float));
-  if (p.nseg > 1) {
-    const size_t st = (size_t)p.B * p.H * p.nseg;
-    bytes += 2 * align256(st * p.dk * p.dv * sizeof(float));
-    bytes += align256(st * p.dk * p.dk * sizeof(float));
-  }
-  return bytes;
+static size_t taps_bytes(const PrefillPlan& p) { return align256((size_t)p.B * p.T * p.H * 4 * sizeof(float)); }
+
+// (several segments) Mstart, Dsum, Phi
+static size_t segment_bytes(const PrefillPlan& p) {
+  if (p.nseg <= 1) return 0;
+  const size_t st = (size_t)p.B * p.H * p.nseg;
+  return 2 * align256(st * p.dk * p.dv * sizeof(float)) + align256(st * p.dk * p.dk * sizeof(float));
 }
 
-template <int DK, int DV, typename IO, typename OP, typename OUT>
+size_t prefill_workspace_bytes(const PrefillPlan& p) { return taps_bytes(p) + segment_bytes(p); }
+size_t prefill_static_workspace_bytes(const PrefillPlan& p) { return segment_bytes(p); }
+
+template <int DK, int DV, typename IO, typename OP, typename OUT, bool SC>
 static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
   const dim3 blk(NTHR);
   if (p.nseg > 1) {
-    chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
+    chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY, SC><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
     scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(p.H, p.nseg, a.S0, a.Dsum, a.Phi,
                                                                                const_cast<float*>(a.Mstart));
   }
-  chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
+  chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT, SC><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int DK, int DV, typename IO, typename OP>
+template <int DK, int DV, typename IO, typename OP, bool SC = false>
 static hipError_t run_prefill_out(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
-  return p.out == IO_F32 ? run_prefill<DK, DV, IO, OP, float>(p, a, stream)
-                         : run_prefill<DK, DV, IO, OP, bf16_t>(p, a, stream);
+  return p.out == IO_F32 ? run_prefill<DK, DV, IO, OP, float, SC>(p, a, stream)
+                         : run_prefill<DK, DV, IO, OP, bf16_t, SC>(p, a, stream);
+}
+
+static void set_segment_buffers(const PrefillPlan& p, ChunkArgs& a, char* ws) {
+  if (p.nseg <= 1) return;
+  const size_t st = (size_t)p.B * p.H * p.nseg;
+  a.Mstart = reinterpret_cast<float*>(ws);
+  ws += align256(st * p.dk * p.dv * sizeof(float));
+  a.Dsum = reinterpret_cast<float*>(ws);
+  ws += align256(st * p.dk * p.dv * sizeof(float));
+  a.Phi = reinterpret_cast<float*>(ws);
 }
 
 #define JB_PREFILL_BF16_CASES(X) \
@@ -894,15 +1044,7 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;
-  if (p.nseg > 1) {
-    char* ws = static_cast<char*>(workspace) + align256((size_t)p.B * p.T * p.H * 4 * sizeof(float));
-    const size_t st = (size_t)p.B * p.H * p.nseg;
-    a.Mstart = reinterpret_cast<float*>(ws);
-    ws += align256(st * p.dk * p.dv * sizeof(float));
-    a.Dsum = reinterpret_cast<float*>(ws);
-    ws += align256(st * p.dk * p.dv * sizeof(float));
-    a.Phi = reinterpret_cast<float*>(ws);
-  }
+  set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16>(p, a, stream);
   if (p.io == IO_BF16) { JB_PREFILL_BF16_CASES(CASE) }
@@ -910,6 +1052,33 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, float, float>(p, a, stream);
   if (p.io == IO_F32) { JB_PREFILL_F32_CASES(CASE) }
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+#define JB_PREFILL_STATIC_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
+
+bool prefill_static_supported(const PrefillPlan& p) {
+#define CASE(DK_, DV_) if (p.dk == DK_ && p.dv == DV_) return true;
+  if (p.io == IO_BF16) { JB_PREFILL_STATIC_CASES(CASE) }
+#undef CASE
+  return false;
+}
+
+hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, const float* wq, const float* wk,
+                                 const float* wv, const void* cq_in, const void* ck_in, const void* cv_in,
+                                 const float* S0, void* o, float* S_final, void* workspace, hipStream_t stream) {
+  if (p.nchunks == 0) return hipSuccess;
+  ChunkArgs a{};
+  a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.conv_in = cv_in;
+  a.wq = wq; a.wk = wk; a.wv = wv; a.cq_in = cq_in; a.ck_in = ck_in;
+  a.S0 = S0; a.o = o; a.S_final = S_final;
+  set_segment_buffers(p, a, static_cast<char*>(workspace));
+#define CASE(DK_, DV_) \
+  if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16, true>(p, a, stream);
+  if (p.io == IO_BF16) { JB_PREFILL_STATIC_CASES(CASE) }
 #undef CASE
   return hipErrorInvalidValue;
 }

@@ -18,6 +18,9 @@ one torch generator seeded per workload:
     W1 ~ N(0,0.02); W2 ~ N(0,0.02)   (no biases)
 and for decode workloads, after those: the state S ~ N(0,0.1) and the conv
 cache ~ N(0,1), then every step's (x, q, k, v, alpha, beta) in step order.
+The static-conv block's weights (static_conv_inputs) are drawn from a generator
+of their own: wq, wk, wv ~ U(-1/2, 1/2), the usual default initialisation of a
+depthwise conv of size 4 (bound 1/sqrt(fan-in)), and caches ~ N(0,1).
 q and k are handed to the block raw: normalising them is the block's job.
 Tensors of the I/O dtype are drawn in float32 and rounded to nearest-even when
 the I/O dtype is bfloat16; alpha, beta and the state are always float32.
@@ -168,4 +171,21 @@ def projection_inputs(shape: Shape, seed: int = 0, device="cpu", alpha_mean: flo
         W1=_normal(g, (s.gen_hidden, s.d_model), 0.0, 0.02, device, io),
         W2=_normal(g, (s.H * s.taps, s.gen_hidden), 0.0, 0.02, device, io),
     )
+    return out
+
+
+def static_conv_inputs(shape: Shape, seed: int = 0, device="cpu"):
+    """Weights of the static-conv block, wq, wk [H*dk, 4] and wv [H*dv, 4] f32 ~ U(-1/2, 1/2),
+    and raw-row caches cache_q, cache_k [B,3,H,dk], cache_v [B,3,H,dv] ~ N(0,1) (I/O dtype)."""
+    s = shape
+    io = torch_dtype(s.io_dtype)
+    g = _gen(seed + 104729, device)
+
+    def unif(rows):
+        return torch.rand((rows, s.taps), generator=g, device=device, dtype=torch.float32) - 0.5
+
+    out = dict(wq=unif(s.H * s.dk), wk=unif(s.H * s.dk), wv=unif(s.H * s.dv))
+    out["cache_q"] = _normal(g, (s.B, s.taps - 1, s.H, s.dk), 0.0, 1.0, device, io)
+    out["cache_k"] = _normal(g, (s.B, s.taps - 1, s.H, s.dk), 0.0, 1.0, device, io)
+    out["cache_v"] = _normal(g, (s.B, s.taps - 1, s.H, s.dv), 0.0, 1.0, device, io)
     return out

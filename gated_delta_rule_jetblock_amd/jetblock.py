@@ -69,10 +69,14 @@ _lib.jb_project.argtypes = [_S] + [_P] * 18 + [_P, _SZ, _P]
 _lib.jb_prefill_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 _lib.jb_decode_step_from_x_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_decode_step_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
+_lib.jb_prefill_static_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
+_lib.jb_prefill_static.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
+_lib.jb_decode_step_static.argtypes = [_S] + [_P] * 17 + [_P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
            "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x",
-           "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x"):
+           "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x", "jb_prefill_static_workspace_size",
+           "jb_prefill_static", "jb_decode_step_static"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -346,3 +350,58 @@ def decode_step_from_x(S, cache, x_t, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=No
                                       _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(o), _ptr(ws),
                                       ws.numel(), _stream(stream)))
     return dict(o=o, S=S_out, cache=cache_out)
+
+
+def prefill_static_workspace_size(shape: Shape) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_prefill_static_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def prefill_static(q, k, v, alpha, beta, wq, wk, wv, S0=None, cache_q=None, cache_k=None, cache_v=None, *,
+                   out_dtype=torch.float32, seg_len: int | None = None, o=None, S_final=None,
+                   want_cache_out=True, ws=None, stream=None, d_model: int = 128):
+    """jb_prefill_static: the static-conv block.  q,k [B,T,H,dk], v [B,T,H,dv] (bf16), alpha,beta
+    [B,T,H] f32, weights wq,wk [H*dk,4], wv [H*dv,4] f32, caches [B,3,H,d] (all three or none).
+    Returns dict(o, S_final, cache_q, cache_k, cache_v)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    shape = make_shape(B, T, H, dk, dv, d_model, _io_code(q), _DT[out_dtype],
+                       flag_segment(seg_len) if seg_len else 0)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    outs = [None, None, None]
+    if want_cache_out:
+        outs = [torch.empty((B, 3, H, d), dtype=q.dtype, device=dev) for d in (dk, dk, dv)]
+    need = prefill_static_workspace_size(shape)
+    if ws is None and need > 0:
+        ws = workspace(need, dev)
+    _check(_lib.jb_prefill_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(wq), _ptr(wk), _ptr(wv), _ptr(S0), _ptr(cache_q), _ptr(cache_k),
+                                  _ptr(cache_v), _ptr(o), _ptr(S_final), _ptr(outs[0]), _ptr(outs[1]),
+                                  _ptr(outs[2]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return dict(o=o, S_final=S_final, cache_q=outs[0], cache_k=outs[1], cache_v=outs[2])
+
+
+def decode_step_static(S, cache_q, cache_k, cache_v, q_t, k_t, v_t, alpha_t, beta_t, wq, wk, wv, *,
+                       out_dtype=torch.float32, S_out=None, cache_q_out=None, cache_k_out=None,
+                       cache_v_out=None, o=None, stream=None, d_model: int = 128):
+    """jb_decode_step_static: one decode step of the static-conv block.  In place on S and the
+    caches unless the *_out tensors are given.  Returns dict(o, S, cache_q, cache_k, cache_v)."""
+    B, H, dk = q_t.shape
+    dv = v_t.shape[2]
+    shape = make_shape(B, 1, H, dk, dv, d_model, _io_code(q_t), _DT[out_dtype])
+    S_out = S if S_out is None else S_out
+    cq = cache_q if cache_q_out is None else cache_q_out
+    ck = cache_k if cache_k_out is None else cache_k_out
+    cv = cache_v if cache_v_out is None else cache_v_out
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype, device=q_t.device)
+    _check(_lib.jb_decode_step_static(ctypes.byref(shape), _ptr(S), _ptr(S_out), _ptr(cache_q), _ptr(cache_k),
+                                      _ptr(cache_v), _ptr(cq), _ptr(ck), _ptr(cv), _ptr(q_t), _ptr(k_t),
+                                      _ptr(v_t), _ptr(alpha_t), _ptr(beta_t), _ptr(wq), _ptr(wk), _ptr(wv),
+                                      _ptr(o), _stream(stream)))
+    return dict(o=o, S=S_out, cache_q=cq, cache_k=ck, cache_v=cv)

@@ -223,6 +223,55 @@ jb_status jb_decode_step_from_x(const jb_shape* shape, const float* S_in, float*
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The static-conv Gated DeltaNet block, the block JetBlock replaces (csdn
+ * translation, section 2.4: earlier linear-attention blocks convolve with
+ * fixed kernels; JetBlock makes the V kernel dynamic and drops the Q and K
+ * convs), kept for measuring the two side by side.  The pages give no
+ * detail; read here as a causal depthwise conv of size 4 with fixed weights
+ * on each of q, k and v (tap j multiplies token t-3+j, no activation), then
+ * L2 normalisation of q and k and the same gated delta rule:
+ *   q'_t[c] = sum_j wq[c][j] q_{t-3+j}[c]   (likewise k' with wk, v' with wv)
+ *
+ * Weights (fp32, row-major, 16-byte aligned): wq, wk [H*dk][4]; wv [H*dv][4],
+ * row h*d + c for channel c of head h.  Caches of raw rows, oldest first:
+ * cache_q, cache_k [B][3][H][dk]; cache_v [B][3][H][dv] (I/O dtype).
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of jb_prefill_static for `shape` (0 with one segment). */
+jb_status jb_prefill_static_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_prefill_static -- the static-conv block over B sequences of T tokens.
+ * q, k, v, alpha, beta, S0, o, S_final and shape.flags as in jb_prefill.
+ * cache_q_in, cache_k_in, cache_v_in: all three or none (NULL: zero rows
+ * before the sequence).  cache_*_out: each nullable; written after the
+ * recurrence has read the incoming caches, so an out cache may alias its in
+ * cache.  Built for bf16 inputs and (dk, dv) in {(32, 64), (64, 128),
+ * (96, 256), (128, 256)}; other shapes return JB_ERR_UNSUPPORTED.
+ */
+jb_status jb_prefill_static(const jb_shape* shape, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const float* wq, const float* wk,
+                            const float* wv, const float* S0, const void* cache_q_in,
+                            const void* cache_k_in, const void* cache_v_in, void* o, float* S_final,
+                            void* cache_q_out, void* cache_k_out, void* cache_v_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * jb_decode_step_static -- one decode step of the static-conv block for B
+ * sequences (shape.T == 1): q_t, k_t [B][H][dk], v_t [B][H][dv], alpha_t,
+ * beta_t [B][H]; S_in, S_out, o_t as in jb_decode_step.  All six caches are
+ * required; each out cache may alias its in cache (updated in place).  Both
+ * I/O dtypes, every (dk, dv) of jb_decode_step.  No workspace.
+ */
+jb_status jb_decode_step_static(const jb_shape* shape, const float* S_in, float* S_out,
+                                const void* cache_q_in, const void* cache_k_in,
+                                const void* cache_v_in, void* cache_q_out, void* cache_k_out,
+                                void* cache_v_out, const void* q_t, const void* k_t,
+                                const void* v_t, const float* alpha_t, const float* beta_t,
+                                const float* wq, const float* wk, const float* wv, void* o_t,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single-stage entry points.  Each runs one stage of the path by itself so
  * that it can be checked on its own; the two calls above fuse these stages.
  * ------------------------------------------------------------------------- */

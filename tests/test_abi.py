@@ -138,3 +138,40 @@ def test_projection_entries_reject_before_launch(jb):
     pargs = [fake] * 17
     assert lib.jb_prefill_from_x(ctypes.byref(s), *pargs, fake, 16, None) == 3
     assert lib.jb_prefill_from_x(ctypes.byref(s32), *pargs, fake, 1 << 30, None) == 2
+
+
+def test_static_entries_reject_before_launch(jb):
+    """jb_prefill_static / jb_decode_step_static: unsupported shapes, mixed caches, bad
+    pointers and small workspaces come back as status codes before any launch."""
+    lib = jb.library()
+    n = ctypes.c_size_t(0)
+    s = jb.make_shape(1, 64, 2, 32, 64, 128)
+    assert lib.jb_prefill_static_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == 0  # one segment: no workspace
+    sseg = jb.make_shape(1, 4096, 2, 32, 64, 128, flags=jb.flag_segment(8))
+    assert lib.jb_prefill_static_workspace_size(ctypes.byref(sseg), ctypes.byref(n)) == 0
+    assert n.value >= 8 * 2 * (2 * 32 * 64 + 32 * 32) * 4  # Mstart, Dsum, Phi of 8 segments
+    s_bad = jb.make_shape(1, 64, 2, 32, 128, 128)  # (32, 128) is not built for the static block
+    assert lib.jb_prefill_static_workspace_size(ctypes.byref(s_bad), ctypes.byref(n)) == 2
+    s32 = jb.make_shape(1, 64, 2, 32, 64, 128, io_dtype=jb.JB_F32)
+    assert lib.jb_prefill_static_workspace_size(ctypes.byref(s32), ctypes.byref(n)) == 2
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 17
+    a = list(args); a[0] = None  # q
+    assert lib.jb_prefill_static(ctypes.byref(s), *a, None, 0, None) == 1
+    assert "q is NULL" in jb.last_error()
+    a = list(args); a[5] = ctypes.c_void_p(0x10004)  # wq misaligned
+    assert lib.jb_prefill_static(ctypes.byref(s), *a, None, 0, None) == 1
+    a = list(args); a[10] = None  # cache_k_in NULL but the other two set
+    assert lib.jb_prefill_static(ctypes.byref(s), *a, None, 0, None) == 1
+    assert "all set or all NULL" in jb.last_error()
+    assert lib.jb_prefill_static(ctypes.byref(sseg), *args, fake, 16, None) == 3
+    d = jb.make_shape(8, 1, 2, 32, 64, 128)
+    dargs = [fake] * 17
+    a = list(dargs); a[4] = None  # cache_v_in
+    assert lib.jb_decode_step_static(ctypes.byref(d), *a, None) == 1
+    assert "cache_v_in is NULL" in jb.last_error()
+    a = list(dargs); a[14] = None  # wk
+    assert lib.jb_decode_step_static(ctypes.byref(d), *a, None) == 1
+    d.T = 3
+    assert lib.jb_decode_step_static(ctypes.byref(d), *dargs, None) == 1
