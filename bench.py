@@ -57,6 +57,15 @@ def decode_step_bytes(s, out_bytes: int) -> float:
     return s.B * s.H * per_unit + s.B * s.d_model * 2 + (32 * s.d_model + 4 * s.H * 32) * 2
 
 
+def decode_static_bytes(s, out_bytes: int) -> float:
+    """Compulsory HBM bytes of one jb_decode_step_static launch: per (sequence, head) the fp32
+    state read and written once, q, k, v_t (bf16), the three 3-row caches read and written,
+    alpha, beta (f32) and o; once, the conv weights (f32, 4 per channel)."""
+    per_unit = (2 * s.dk * s.dv * 4 + 2 * s.dk * 2 + s.dv * 2 + 2 * 3 * (2 * s.dk + s.dv) * 2 + 8
+                + s.dv * out_bytes)
+    return s.B * s.H * per_unit + s.H * (2 * s.dk + s.dv) * 16
+
+
 def measured_traffic(profile: str, sources: list[str]):
     """HBM bytes per launch of a kernel, from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain-copy calibration), or None when the
@@ -130,6 +139,51 @@ def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
                              flops_per_call=projection_flops_per_token(sp) * tok))
 
 
+def measure_static(jb, inputs, torch, sp, sd, p, d, out_dt, reps: int = 3):
+    """The static-conv block, the one JetBlock replaces, on the same inputs (outside the timed
+    step): jb_prefill_static at the prefill shape and jb_decode_step_static at the decode shape,
+    each averaged over `reps` calls bracketed by HIP events on the launching stream."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    w = inputs.static_conv_inputs(sp, seed=5, device=dev)
+    o = torch.empty((sp.B, sp.T, sp.H, sp.dv), dtype=out_dt, device=dev)
+    S = torch.empty((sp.B, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+    pshape = jb.make_shape(sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.d_model, jb.JB_BF16,
+                           jb.JB_BF16 if out_dt == torch.bfloat16 else jb.JB_F32)
+    need = jb.prefill_static_workspace_size(pshape)
+    ws = jb.workspace(need, dev) if need else None
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_pre = timed(lambda: jb.prefill_static(p["q"], p["k"], p["v"], p["alpha"], p["beta"], w["wq"], w["wk"], w["wv"],
+                                             out_dtype=out_dt, o=o, S_final=S, want_cache_out=False, ws=ws,
+                                             stream=stream))
+    wd = inputs.static_conv_inputs(sd, seed=6, device=dev)
+    Sd = d["S"].clone()
+    od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
+    us_dec = 1e3 * timed(lambda: jb.decode_step_static(Sd, wd["cache_q"], wd["cache_k"], wd["cache_v"], d["q"][0],
+                                                       d["k"][0], d["v"][0], d["alpha"][0], d["beta"][0], wd["wq"],
+                                                       wd["wk"], wd["wv"], out_dtype=out_dt, o=od, stream=stream))
+    out_bytes = 2 if out_dt == torch.bfloat16 else 4
+    dec_gbs = decode_static_bytes(sd, out_bytes) / (us_dec * 1e-6) / 1e9
+    tok = sp.B * sp.T
+    return dict(prefill=dict(call="jb_prefill_static", ms=round(ms_pre, 4), tokens_per_s=round(tok / (ms_pre * 1e-3), 1)),
+                decode=dict(call="jb_decode_step_static (decode_seq_static_kernel)", B=sd.B, us=round(us_dec, 2),
+                            tokens_per_s=round(sd.B / (us_dec * 1e-6), 1), hbm_GBs=round(dec_gbs, 1),
+                            hbm_frac=round(dec_gbs / HBM_PEAK_GBS, 4),
+                            bytes_per_launch=decode_static_bytes(sd, out_bytes)))
+
+
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
     """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
     import oracle
@@ -176,6 +230,7 @@ def main():
                     help="bracket every N-th decode state-update launch with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-from-x", action="store_true", help="skip the measurement of the block from x")
+    ap.add_argument("--no-static", action="store_true", help="skip the static-conv block measurement")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run three plain 256 MiB device-to-device copies, whose counter "
@@ -288,6 +343,14 @@ def main():
         log(f"from x: {from_x['ms']:.3f} ms per prefill, projections {from_x['project']['ms']:.3f} ms "
             f"({from_x['project']['frac'] * 100:.1f}% of the MFMA peak), decode step from x "
             f"{from_x['decode_step_from_x']['us']:.1f} us")
+    static = None
+    if not args.no_static:
+        log("timing the static-conv block ...")
+        static = measure_static(jb, inputs, torch, sp, sd, p, d, out_dt)
+        static["prefill"]["jetblock_over_static"] = round(pre_ms / static["prefill"]["ms"], 3)
+        static["decode"]["jetblock_over_static"] = round(dec_ms * 1e3 / static["decode"]["us"], 3)
+        log(f"static conv: prefill {static['prefill']['ms']:.3f} ms (JetBlock {pre_ms:.3f} ms), decode step "
+            f"{static['decode']['us']:.1f} us (JetBlock {dec_ms * 1e3:.1f} us)")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -321,6 +384,7 @@ def main():
         "roofline_prefill": roof_pre,
         "cpu_baseline": cpu,
         "from_x": from_x,
+        "static_conv": static,
     }
     print(json.dumps(line), flush=True)
 

@@ -161,79 +161,6 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, const float* S_in, f
   decode_update<DK, DV, OUT>(m, sk, sq, sv, sred, al, be, bh, o_t, Mout, wave, lane);
 }
 
-// One decode step of the static-conv block, the one JetBlock replaces
-// (Jet-Nemotron csdn translation, section 2.4: earlier linear-attention
-// blocks convolve with fixed kernels).  Read here as a causal depthwise conv
-// of size 4 with fixed weights on each of q, k and v, no activation, q and k
-// normalised after it.  Wave 0 convolves q and k from their caches and
-// normalises them, wave 1 forms v'; both shift their caches.  The rest is the
-// update above.  Each cache element is read before it is written by the
-// same thread, so a cache may be updated in place.
-template <int DK, int DV, typename IO, typename OUT>
-__global__ __launch_bounds__(256) void decode_static_kernel(int H, const float* S_in, float* S_out, const IO* cq_in,
-                                                            const IO* ck_in, const IO* cv_in, IO* cq_out, IO* ck_out,
-                                                            IO* cv_out, const IO* q_t, const IO* k_t, const IO* v_t,
-                                                            const float* alpha_t, const float* beta_t, const float* wq,
-                                                            const float* wk, const float* wv, OUT* o_t) {
-  constexpr int RPW = DK / 4;
-  constexpr int CPL = DV / 64;
-  __shared__ float sk[DK], sq[DK], sv[DV];
-  __shared__ float sred[2][4][DV];
-
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t bh = (int64_t)b * H + h;
-  const float* Min = S_in + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
-  float* Mout = S_out + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
-
-  float m[RPW][CPL];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) ld<CPL>(Min + (int64_t)r * DV, m[r]);
-
-  const float al = alpha_t[bh], be = beta_t[bh];
-  if (wave == 0) {
-    float kx[2], qx[2];
-    float sk2 = 0.f, sq2 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int d = lane + 64 * e;
-      kx[e] = qx[e] = 0.f;
-      if (d < DK) {
-        const int64_t r0 = (int64_t)b * 3 * H * DK + (int64_t)h * DK + d, rs = (int64_t)H * DK;
-        const IO k0 = ck_in[r0], k1 = ck_in[r0 + rs], k2 = ck_in[r0 + 2 * rs], kt = k_t[bh * DK + d];
-        const IO q0 = cq_in[r0], q1 = cq_in[r0 + rs], q2 = cq_in[r0 + 2 * rs], qt = q_t[bh * DK + d];
-        const float4 wkd = *reinterpret_cast<const float4*>(wk + ((int64_t)h * DK + d) * 4);
-        const float4 wqd = *reinterpret_cast<const float4*>(wq + ((int64_t)h * DK + d) * 4);
-        kx[e] = wkd.x * to_f32<IO>(k0) + wkd.y * to_f32<IO>(k1) + wkd.z * to_f32<IO>(k2) + wkd.w * to_f32<IO>(kt);
-        qx[e] = wqd.x * to_f32<IO>(q0) + wqd.y * to_f32<IO>(q1) + wqd.z * to_f32<IO>(q2) + wqd.w * to_f32<IO>(qt);
-        ck_out[r0] = k1; ck_out[r0 + rs] = k2; ck_out[r0 + 2 * rs] = kt;
-        cq_out[r0] = q1; cq_out[r0 + rs] = q2; cq_out[r0 + 2 * rs] = qt;
-      }
-      sk2 += kx[e] * kx[e];
-      sq2 += qx[e] * qx[e];
-    }
-    const float rk = l2_scale(wave_sum(sk2)), rq = l2_scale(wave_sum(sq2));
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int d = lane + 64 * e;
-      if (d < DK) { sk[d] = kx[e] * rk; sq[d] = qx[e] * rq; }
-    }
-  } else if (wave == 1) {
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = lane * CPL + i;
-      const int64_t r0 = (int64_t)b * 3 * H * DV + (int64_t)h * DV + c, rs = (int64_t)H * DV;
-      const IO c0 = cv_in[r0], c1 = cv_in[r0 + rs], c2 = cv_in[r0 + 2 * rs], vt = v_t[bh * DV + c];
-      const float4 w = *reinterpret_cast<const float4*>(wv + ((int64_t)h * DV + c) * 4);
-      sv[c] = w.x * to_f32<IO>(c0) + w.y * to_f32<IO>(c1) + w.z * to_f32<IO>(c2) + w.w * to_f32<IO>(vt);
-      cv_out[r0] = c1; cv_out[r0 + rs] = c2; cv_out[r0 + 2 * rs] = vt;
-    }
-  }
-  __syncthreads();
-
-  decode_update<DK, DV, OUT>(m, sk, sq, sv, sred, al, be, bh, o_t, Mout, wave, lane);
-}
-
 // ------------------------------------------------------- fused decode step
 //
 // jb_decode_step in one launch, with no communication between workgroups.
@@ -298,6 +225,67 @@ template <> struct Two<float> {
   __device__ __forceinline__ float lo() const { return v.x; }
   __device__ __forceinline__ float hi() const { return v.y; }
 };
+
+// The state updates of a workgroup's HPG heads (decode_seq_kernel and its
+// static-conv twin): sk, sq, skq, sv, sal, sbe of every head are in LDS
+// behind a barrier, head 0's tile is in ma and head 1's in (or on its way to)
+// mb.  Head j+2's tile is loaded into the registers head j has just
+// finished with, so one tile is always in flight.
+template <int DK, int DV, typename OUT, int NW, typename LoadTile>
+__device__ __forceinline__ void seq_update_heads(SeqSmem<DK, DV, NW>& sm, float (&ma)[DK / NW][DV / 64],
+                                                 float (&mb)[DK / NW][DV / 64], int HPG, int64_t bh0, float* S_out,
+                                                 OUT* o_t, int tid, int wave, int lane, LoadTile load_tile) {
+  constexpr int RPW = DK / NW;
+  constexpr int CPL = DV / 64;
+  auto process = [&](float (&m)[RPW][CPL], int j) {
+    const int64_t bh = bh0 + j;
+    float pa[CPL], pc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) { pa[i] = 0.f; pc[i] = 0.f; }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float kr = sm.sk[j][wave * RPW + r], qr = sm.sq[j][wave * RPW + r];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { pa[i] += m[r][i] * kr; pc[i] += m[r][i] * qr; }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      sm.sred[0][wave][lane * CPL + i] = pa[i];
+      sm.sred[1][wave][lane * CPL + i] = pc[i];
+    }
+    lds_barrier();
+    const float al = sm.sal[j];
+    if (tid < DV) {
+      float av = 0.f, cv = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { av += sm.sred[0][w][tid]; cv += sm.sred[1][w][tid]; }
+      const float u = sm.sbe[j] * (sm.sv[j][tid] - al * av);
+      sm.su[tid] = u;
+      o_t[bh * DV + tid] = from_f32<OUT>(al * cv + sm.skq[j] * u);
+    }
+    lds_barrier();
+    float* Mo = S_out + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+    float uu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) uu[i] = sm.su[lane * CPL + i];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const float kr = sm.sk[j][wave * RPW + r];
+      float nm[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) nm[i] = al * m[r][i] + kr * uu[i];
+      st<CPL>(Mo + (int64_t)r * DV, nm);
+    }
+  };
+  for (int j = 0; j < HPG; j += 2) {
+    process(ma, j);
+    if (j + 2 < HPG) load_tile(ma, j + 2);
+    if (j + 1 < HPG) {
+      process(mb, j + 1);
+      if (j + 3 < HPG) load_tile(mb, j + 3);
+    }
+  }
+}
 
 // GX: the gates come from x as well, alpha = sigmoid(Wa x + ba) and
 // beta = sigmoid(Wb x + bb) (the step from the layer input), instead of from
@@ -507,58 +495,144 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
   lds_barrier();
 
   // ---- the heads' state updates
-  auto process = [&](float (&m)[RPW][CPL], int j) {
-    const int64_t bh = bh0 + j;
-    float pa[CPL], pc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) { pa[i] = 0.f; pc[i] = 0.f; }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float kr = sm.sk[j][wave * RPW + r], qr = sm.sq[j][wave * RPW + r];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) { pa[i] += m[r][i] * kr; pc[i] += m[r][i] * qr; }
-    }
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      sm.sred[0][wave][lane * CPL + i] = pa[i];
-      sm.sred[1][wave][lane * CPL + i] = pc[i];
-    }
-    lds_barrier();
-    const float al = sm.sal[j];
-    if (tid < DV) {
-      float av = 0.f, cv = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) { av += sm.sred[0][w][tid]; cv += sm.sred[1][w][tid]; }
-      const float u = sm.sbe[j] * (sm.sv[j][tid] - al * av);
-      sm.su[tid] = u;
-      o_t[bh * DV + tid] = from_f32<OUT>(al * cv + sm.skq[j] * u);
-    }
-    lds_barrier();
-    float* Mo = S_out + bh * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
-    float uu[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) uu[i] = sm.su[lane * CPL + i];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float kr = sm.sk[j][wave * RPW + r];
-      float nm[CPL];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) nm[i] = al * m[r][i] + kr * uu[i];
-      st<CPL>(Mo + (int64_t)r * DV, nm);
-    }
-  };
-  for (int j = 0; j < HPG; j += 2) {
-    process(ma, j);
-    if (j + 2 < HPG) load_tile(ma, j + 2);
-    if (j + 1 < HPG) {
-      process(mb, j + 1);
-      if (j + 3 < HPG) load_tile(mb, j + 3);
-    }
-  }
+  seq_update_heads<DK, DV, OUT, NW>(sm, ma, mb, HPG, bh0, S_out, o_t, tid, wave, lane, load_tile);
 }
 
 // heads per workgroup: the fewest groups per sequence that give every CU
 // 16 waves (256 CUs) with at most SEQ_MAXHPG heads each (a divisor of H)
+// One decode step of the static-conv block, the one JetBlock replaces
+// (Jet-Nemotron csdn translation, section 2.4: earlier linear-attention
+// blocks convolve with fixed kernels).  Read here as a causal depthwise conv
+// of size 4 with fixed weights on each of q, k and v, no activation, q and k
+// normalised after it.  Same workgroup layout as decode_seq_kernel, with the
+// generator replaced by the three convs: wave w convolves q and k of heads
+// w, w + NW, .. from their caches, every thread the v columns it owns; each
+// cache element is written by the thread that read it, so the caches may be
+// updated in place.  Issue order: the first heads' q / k rows and weights,
+// the v rows and weights, then the state tiles.
+template <int DK, int DV, typename IO, typename OUT, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_seq_static_kernel(
+    int H, int HPG, const float* S_in, float* S_out, const IO* cq_in, const IO* ck_in, const IO* cv_in, IO* cq_out,
+    IO* ck_out, IO* cv_out, const IO* q_t, const IO* k_t, const IO* v_t, const float* alpha_t, const float* beta_t,
+    const float* wq, const float* wk, const float* wv, OUT* o_t) {
+  constexpr int NT = NW * 64;
+  constexpr int RPW = DK / NW;
+  constexpr int CPL = DV / 64;
+  constexpr int NPAIR = (SEQ_MAXHPG * DV / 2 + NT - 1) / NT;
+  constexpr bool EARLY_B = 2 * RPW * CPL <= 48;
+  __shared__ SeqSmem<DK, DV, NW> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.y, h0 = blockIdx.x * HPG;
+  const int64_t bh0 = (int64_t)b * H + h0;
+
+  auto load_tile = [&](float (&m)[RPW][CPL], int j) {
+    const float* p = S_in + (bh0 + j) * DK * DV + (int64_t)(wave * RPW) * DV + lane * CPL;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) ld<CPL>(p + (int64_t)r * DV, m[r]);
+  };
+
+  // raw q / k rows (three cached, the current one) and weights of head jw, up
+  // to two elements per lane
+  IO qr[2][4], kr[2][4];
+  float4 wqd[2], wkd[2];
+  auto load_qk = [&](int jw) {
+    const int h = h0 + jw;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < DK) {
+        const int64_t r0 = (int64_t)b * 3 * H * DK + (int64_t)h * DK + d, rs = (int64_t)H * DK;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          qr[e][t] = cq_in[r0 + t * rs];
+          kr[e][t] = ck_in[r0 + t * rs];
+        }
+        qr[e][3] = q_t[(bh0 + jw) * DK + d];
+        kr[e][3] = k_t[(bh0 + jw) * DK + d];
+        wqd[e] = *reinterpret_cast<const float4*>(wq + ((int64_t)h * DK + d) * 4);
+        wkd[e] = *reinterpret_cast<const float4*>(wk + ((int64_t)h * DK + d) * 4);
+      }
+    }
+  };
+  if (wave < HPG) load_qk(wave);
+  Two<IO> raw[NPAIR][4];  // columns c, c+1 of the three cached v rows and v_t
+  float4 wvc[NPAIR][2];   // their weights
+#pragma unroll
+  for (int i = 0; i < NPAIR; ++i) {
+    const int pr = tid + i * NT, j = pr / (DV / 2), c = 2 * (pr % (DV / 2));
+    if (j < HPG) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        raw[i][t] = *reinterpret_cast<const Two<IO>*>(cv_in + ((int64_t)b * 3 + t) * H * DV + (int64_t)(h0 + j) * DV + c);
+      raw[i][3] = *reinterpret_cast<const Two<IO>*>(v_t + (bh0 + j) * DV + c);
+      wvc[i][0] = *reinterpret_cast<const float4*>(wv + ((int64_t)(h0 + j) * DV + c) * 4);
+      wvc[i][1] = *reinterpret_cast<const float4*>(wv + ((int64_t)(h0 + j) * DV + c + 1) * 4);
+    }
+  }
+  float ma[RPW][CPL], mb[RPW][CPL];
+  load_tile(ma, 0);
+  if (EARLY_B && HPG > 1) load_tile(mb, 1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- q / k convs, normalisation and cache shift, per head of this wave
+  for (int jw = wave; jw < HPG; jw += NW) {
+    if (jw != wave) load_qk(jw);
+    float kx[2] = {0.f, 0.f}, qx[2] = {0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (lane + 64 * e < DK) {
+        kx[e] = wkd[e].x * to_f32<IO>(kr[e][0]) + wkd[e].y * to_f32<IO>(kr[e][1]) + wkd[e].z * to_f32<IO>(kr[e][2]) +
+                wkd[e].w * to_f32<IO>(kr[e][3]);
+        qx[e] = wqd[e].x * to_f32<IO>(qr[e][0]) + wqd[e].y * to_f32<IO>(qr[e][1]) + wqd[e].z * to_f32<IO>(qr[e][2]) +
+                wqd[e].w * to_f32<IO>(qr[e][3]);
+      }
+    float sk2 = kx[0] * kx[0] + kx[1] * kx[1], sq2 = qx[0] * qx[0] + qx[1] * qx[1];
+    const float rk = l2_scale(wave_sum(sk2)), rq = l2_scale(wave_sum(sq2));
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      if (d < DK) {
+        sm.sk[jw][d] = kx[e] * rk;
+        sm.sq[jw][d] = qx[e] * rq;
+        kq += kx[e] * rk * qx[e] * rq;
+        const int64_t r0 = (int64_t)b * 3 * H * DK + (int64_t)(h0 + jw) * DK + d, rs = (int64_t)H * DK;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          cq_out[r0 + t * rs] = qr[e][t + 1];
+          ck_out[r0 + t * rs] = kr[e][t + 1];
+        }
+      }
+    }
+    kq = wave_sum(kq);
+    if (lane == 0) {
+      sm.skq[jw] = kq;
+      sm.sal[jw] = alpha_t[bh0 + jw];
+      sm.sbe[jw] = beta_t[bh0 + jw];
+    }
+  }
+  // ---- v conv and cache shift
+#pragma unroll
+  for (int i = 0; i < NPAIR; ++i) {
+    const int pr = tid + i * NT, j = pr / (DV / 2), c = 2 * (pr % (DV / 2));
+    if (j < HPG) {
+      const float4 w0 = wvc[i][0], w1 = wvc[i][1];
+      sm.sv[j][c] = w0.x * raw[i][0].lo() + w0.y * raw[i][1].lo() + w0.z * raw[i][2].lo() + w0.w * raw[i][3].lo();
+      sm.sv[j][c + 1] = w1.x * raw[i][0].hi() + w1.y * raw[i][1].hi() + w1.z * raw[i][2].hi() + w1.w * raw[i][3].hi();
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        *reinterpret_cast<Two<IO>*>(cv_out + ((int64_t)b * 3 + t) * H * DV + (int64_t)(h0 + j) * DV + c) = raw[i][t + 1];
+    }
+  }
+  if (!EARLY_B && HPG > 1) load_tile(mb, 1);
+  lds_barrier();
+
+  // ---- the heads' state updates
+  seq_update_heads<DK, DV, OUT, NW>(sm, ma, mb, HPG, bh0, S_out, o_t, tid, wave, lane, load_tile);
+}
+
 int decode_seq_heads_per_group(int B, int H, int nw) {
   const int64_t want = 256 * (16 / nw);
   for (int ng = 1; ng <= H; ++ng)
@@ -649,14 +723,16 @@ static hipError_t run_decode_static(int out, int B, int H, const float* S_in, fl
                                     const void* q_t, const void* k_t, const void* v_t, const float* alpha_t,
                                     const float* beta_t, const float* wq, const float* wk, const float* wv, void* o_t,
                                     hipStream_t stream) {
-  const dim3 grid(H, B);
+  constexpr int NW = SEQ_NW;
+  const int hpg = decode_seq_heads_per_group(B, H, NW);
+  const dim3 grid(H / hpg, B);
 #define JB_STATIC_ARGS(OUT_)                                                                                    \
-  H, S_in, S_out, (const IO*)cq_in, (const IO*)ck_in, (const IO*)cv_in, (IO*)cq_out, (IO*)ck_out, (IO*)cv_out, \
-      (const IO*)q_t, (const IO*)k_t, (const IO*)v_t, alpha_t, beta_t, wq, wk, wv, (OUT_*)o_t
+  H, hpg, S_in, S_out, (const IO*)cq_in, (const IO*)ck_in, (const IO*)cv_in, (IO*)cq_out, (IO*)ck_out,         \
+      (IO*)cv_out, (const IO*)q_t, (const IO*)k_t, (const IO*)v_t, alpha_t, beta_t, wq, wk, wv, (OUT_*)o_t
   if (out == IO_F32)
-    decode_static_kernel<DK, DV, IO, float><<<grid, 256, 0, stream>>>(JB_STATIC_ARGS(float));
+    decode_seq_static_kernel<DK, DV, IO, float, NW><<<grid, NW * 64, 0, stream>>>(JB_STATIC_ARGS(float));
   else
-    decode_static_kernel<DK, DV, IO, bf16_t><<<grid, 256, 0, stream>>>(JB_STATIC_ARGS(bf16_t));
+    decode_seq_static_kernel<DK, DV, IO, bf16_t, NW><<<grid, NW * 64, 0, stream>>>(JB_STATIC_ARGS(bf16_t));
 #undef JB_STATIC_ARGS
   return hipGetLastError();
 }
