@@ -184,6 +184,60 @@ def measure_static(jb, inputs, torch, sp, sd, p, d, out_dt, reps: int = 3):
                             bytes_per_launch=decode_static_bytes(sd, out_bytes)))
 
 
+def measure_serving(jb, inputs, torch, sp, sd, out_dt, n_req: int, lo: int, hi: int, steps: int = 16, reps: int = 2):
+    """A serving batch (outside the timed step): n_req requests of lo..hi tokens at the
+    prefill shape's heads, prefilled as one packed batch (jb_prefill_varlen), then `steps`
+    decode steps of the whole batch from the prefill's states and caches (jb_decode_step).
+    Each part averaged over HIP events on the launching stream."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    lengths = inputs.request_lengths(n_req, lo, hi, seed=1)
+    total = sum(lengths)
+    p = inputs.packed_prefill_inputs(lengths, sp.H, sp.dk, sp.dv, sp.d_model, seed=4, device=dev)
+    cu = p["cu_seqlens"]
+    o = torch.empty((total, sp.H, sp.dv), dtype=out_dt, device=dev)
+    S = torch.empty((n_req, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+    cache = torch.empty((n_req, 3, sp.H, sp.dv), dtype=torch.bfloat16, device=dev)
+    shape = jb.make_shape(n_req, max(lengths), sp.H, sp.dk, sp.dv, sp.d_model)
+    ws = jb.workspace(jb.prefill_varlen_workspace_size(shape, total), dev)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_pre = timed(lambda: jb.prefill_varlen(cu, p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"],
+                                             p["W2"], max_seqlen=max(lengths), out_dtype=out_dt, o=o, S_final=S,
+                                             conv_out=cache, ws=ws, stream=stream), reps)
+    del p, o
+    d = inputs.decode_inputs(inputs.Shape(B=n_req, T=1, H=sd.H, dk=sd.dk, dv=sd.dv, d_model=sd.d_model),
+                             steps=steps, seed=8, device=dev, with_state=False)
+    od = torch.empty((n_req, sd.H, sd.dv), dtype=out_dt, device=dev)
+    state = dict(t=0)
+
+    def step():
+        t = state["t"] % steps
+        state["t"] += 1
+        jb.decode_step(S, cache, d["x"][t], d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t], d["W1"],
+                       d["W2"], out_dtype=out_dt, o=od, stream=stream)
+
+    us_dec = 1e3 * timed(step, steps)
+    flops = prefill_flops_per_token(sp) * total
+    tf = flops / (ms_pre * 1e-3) / 1e12
+    return dict(requests=n_req, lengths=f"uniform {lo}..{hi} (seeded)", tokens=total,
+                prefill=dict(call="jb_prefill_varlen", ms=round(ms_pre, 3), tokens_per_s=round(total / (ms_pre * 1e-3), 1),
+                             mfma_frac=round(tf / MFMA_PEAK_TFLOPS, 4)),
+                decode=dict(call="jb_decode_step (states handed over from the prefill)", B=n_req,
+                            us=round(us_dec, 2), tokens_per_s=round(n_req / (us_dec * 1e-6), 1)))
+
+
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
     """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
     import oracle
@@ -231,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-from-x", action="store_true", help="skip the measurement of the block from x")
     ap.add_argument("--no-static", action="store_true", help="skip the static-conv block measurement")
+    ap.add_argument("--no-serving", action="store_true", help="skip the packed serving-batch measurement")
+    ap.add_argument("--serving-requests", type=int, default=256)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run three plain 256 MiB device-to-device copies, whose counter "
@@ -351,6 +407,13 @@ def main():
         static["decode"]["jetblock_over_static"] = round(dec_ms * 1e3 / static["decode"]["us"], 3)
         log(f"static conv: prefill {static['prefill']['ms']:.3f} ms (JetBlock {pre_ms:.3f} ms), decode step "
             f"{static['decode']['us']:.1f} us (JetBlock {dec_ms * 1e3:.1f} us)")
+    serving = None
+    if not args.no_serving:
+        log(f"timing a serving batch of {args.serving_requests} requests ...")
+        serving = measure_serving(jb, inputs, torch, sp, sd, out_dt, args.serving_requests, 2048, 8192)
+        log(f"serving: {serving['tokens']} prompt tokens prefilled in {serving['prefill']['ms']:.2f} ms "
+            f"({serving['prefill']['tokens_per_s'] / 1e6:.1f} M tokens/s), decode step of the batch "
+            f"{serving['decode']['us']:.1f} us")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -385,6 +448,7 @@ def main():
         "cpu_baseline": cpu,
         "from_x": from_x,
         "static_conv": static,
+        "serving": serving,
     }
     print(json.dumps(line), flush=True)
 

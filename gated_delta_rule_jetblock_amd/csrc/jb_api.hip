@@ -159,6 +159,80 @@ jb_status jb_prefill(const jb_shape* s, const void* x, const void* q, const void
   return hip_status(fn, e);
 }
 
+namespace {
+
+jb_status check_varlen(const char* fn, const jb_shape* s, int64_t total_tokens, jb::PrefillPlan* p) {
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (total_tokens < 0 || total_tokens > (int64_t)s->B * s->T)
+    return fail(JB_ERR_INVALID_ARG, "%s: total_tokens = %lld not in [0, B*T] (B = %d, T = %d the longest sequence)", fn,
+                (long long)total_tokens, s->B, s->T);
+  if (total_tokens > 0x7fffffffLL) return fail(JB_ERR_UNSUPPORTED, "%s: total_tokens exceeds 2^31 - 1", fn);
+  *p = plan_of(s);
+  if (!jb::prefill_supported(*p))
+    return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built for io_dtype %d", fn, s->dk, s->dv, s->io_dtype);
+  if (seg_flag(s) < 0) return fail(JB_ERR_INVALID_ARG, "%s: bad segment flag", fn);
+  p->tokens = total_tokens;
+  return JB_OK;
+}
+
+}  // namespace
+
+jb_status jb_prefill_varlen_workspace_size(const jb_shape* s, int64_t total_tokens, size_t* bytes) {
+  const char* fn = "jb_prefill_varlen_workspace_size";
+  jb::PrefillPlan p;
+  jb_status st = check_varlen(fn, s, total_tokens, &p);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = jb::prefill_workspace_bytes(p);
+  return ok();
+}
+
+jb_status jb_prefill_varlen(const jb_shape* s, int64_t total_tokens, const int32_t* cu_seqlens, const void* x,
+                            const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                            const void* W1, const void* b1, const void* W2, const void* b2, const float* S0,
+                            const void* conv_in, void* o, float* S_final, void* conv_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_prefill_varlen";
+  jb::PrefillPlan p;
+  jb_status st = check_varlen(fn, s, total_tokens, &p);
+  if (st) return st;
+  JB_REQUIRE_SCALARS(cu_seqlens);
+  if (total_tokens > 0) {
+    JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v);
+    JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta); JB_REQUIRE_PTR(o);
+  }
+  JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_REQUIRE_PTR(S_final);
+  JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2); JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(conv_in);
+  JB_OPTIONAL_PTR(conv_out);
+  const size_t need = jb::prefill_workspace_bytes(p);
+  if (need && !workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if (workspace && ((uintptr_t)workspace & 255u))
+    return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
+  p.cu_seqlens = cu_seqlens;
+  hipError_t e = hipSuccess;
+  if (s->T == 0 || total_tokens == 0) {
+    // every sequence is empty: the state and cache pass through
+    if (S0 && S0 != S_final)
+      e = hipMemcpyAsync(S_final, S0, (size_t)s->B * s->H * s->dk * s->dv * sizeof(float), hipMemcpyDeviceToDevice, hs);
+    else if (!S0)
+      e = jb::launch_fill_zero(S_final, (size_t)s->B * s->H * s->dk * s->dv, hs);
+    if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(io, s->B, 0, s->H, s->dv, v, conv_in, conv_out, hs);
+    return hip_status(fn, e);
+  }
+  float* taps = static_cast<float*>(workspace);
+  e = jb::launch_gen_taps(io, total_tokens, s->d_model, s->H, x, W1, b1, W2, b2, taps, hs);
+  if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, workspace, hs);
+  if (e == hipSuccess && conv_out)
+    e = jb::launch_conv_tail(io, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs, cu_seqlens);
+  return hip_status(fn, e);
+}
+
 jb_status jb_decode_workspace_size(const jb_shape* s, size_t* bytes) {
   const char* fn = "jb_decode_workspace_size";
   jb_status st = check_shape(fn, s, true);

@@ -153,4 +153,19 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // L2 normalisation factor (sum x^2 + 1e-6)^(-1/2)
 __device__ __forceinline__ float l2_scale(float sumsq) { return 1.0f / sqrtf(sumsq + 1e-6f); }
 
+// First row and length of sequence b of a batch: rows b T .. b T + T - 1 of
+// the token-major tensors, or (packed sequences of different lengths) the
+// span cu_seqlens gives, its length clamped to [0, Tmax] so that a sequence
+// longer than the planned maximum stays inside the planned grid.
+__device__ __forceinline__ void seq_span(const int* cu_seqlens, int Tmax, int b, int64_t& tok0, int& T) {
+  if (!cu_seqlens) {
+    tok0 = (int64_t)b * Tmax;
+    T = Tmax;
+    return;
+  }
+  const int c0 = cu_seqlens[b], c1 = cu_seqlens[b + 1];
+  tok0 = c0;
+  T = min(max(c1 - c0, 0), Tmax);
+}
+
 }  // namespace jb

@@ -215,21 +215,26 @@ hipError_t launch_conv(int io, int B, int T, int H, int dv, const float* taps, c
 
 // ------------------------------------------------------- conv cache tail
 
-// conv_out[b][s] = row T-3+s of [conv_in; v]; one thread per (b, h, c) reads
-// all three sources before writing, so conv_out may alias conv_in.
+// conv_out[b][s] = row T_b-3+s of [conv_in; v] for sequence b; one thread
+// per (b, h, c) reads all three sources before writing, so conv_out may alias
+// conv_in.
 template <typename IO>
-__global__ void conv_tail_kernel(int B, int T, int H, int dv, const IO* v, const IO* conv_in, IO* conv_out) {
+__global__ void conv_tail_kernel(int B, int Tmax, int H, int dv, const IO* v, const IO* conv_in, IO* conv_out,
+                                 const int* cu_seqlens) {
   const int64_t total = (int64_t)B * H * dv;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total) return;
   const int c = (int)(e % dv);
   const int h = (int)((e / dv) % H);
   const int b = (int)(e / ((int64_t)dv * H));
+  int64_t tok0;
+  int T;
+  seq_span(cu_seqlens, Tmax, b, tok0, T);
   IO vals[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     const int t = T - 3 + s;
-    if (t >= 0) vals[s] = v[(((int64_t)b * T + t) * H + h) * dv + c];
+    if (t >= 0) vals[s] = v[((tok0 + t) * H + h) * dv + c];
     else if (conv_in) vals[s] = conv_in[(((int64_t)b * 3 + (3 + t)) * H + h) * dv + c];
     else vals[s] = from_f32<IO>(0.f);
   }
@@ -238,16 +243,16 @@ __global__ void conv_tail_kernel(int B, int T, int H, int dv, const IO* v, const
 }
 
 hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v, const void* conv_in, void* conv_out,
-                            hipStream_t stream) {
+                            hipStream_t stream, const int* cu_seqlens) {
   const int64_t total = (int64_t)B * H * dv;
   if (total == 0) return hipSuccess;
   const int blocks = (int)((total + 255) / 256);
   if (io == IO_BF16)
     conv_tail_kernel<bf16_t><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const bf16_t*)v, (const bf16_t*)conv_in,
-                                                         (bf16_t*)conv_out);
+                                                         (bf16_t*)conv_out, cu_seqlens);
   else
     conv_tail_kernel<float><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const float*)v, (const float*)conv_in,
-                                                        (float*)conv_out);
+                                                        (float*)conv_out, cu_seqlens);
   return hipGetLastError();
 }
 

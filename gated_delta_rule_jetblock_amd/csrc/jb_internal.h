@@ -26,9 +26,11 @@ hipError_t launch_prologue(int io, int B, int T, int H, int dk, const void* q, c
                            const float* alpha, float* qhat, float* khat, float* g,
                            hipStream_t stream);
 
-// Copy of the last 3 raw value rows of [conv_in; v] into conv_out.
+// Copy of the last 3 raw value rows of [conv_in; v] into conv_out, per
+// sequence (cu_seqlens: packed sequences of at most T rows, else dense).
 hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v,
-                            const void* conv_in, void* conv_out, hipStream_t stream);
+                            const void* conv_in, void* conv_out, hipStream_t stream,
+                            const int* cu_seqlens = nullptr);
 
 // Chunked prefill (segment summaries, scan, outputs).
 struct PrefillPlan {
@@ -36,7 +38,9 @@ struct PrefillPlan {
   int io, out;       // IoType of inputs and of o
   int nchunks;       // ceil(T / 64)
   int seg_len;       // chunks per segment
-  int nseg;          // number of segments
+  int nseg;          // number of segments (per sequence, at most)
+  int64_t tokens;    // rows of the token-major tensors (B T, or the packed total)
+  const int* cu_seqlens;  // packed batch: B + 1 row offsets on the device, T the longest; NULL: dense
 };
 PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, int seg_len);
 size_t prefill_workspace_bytes(const PrefillPlan& p);

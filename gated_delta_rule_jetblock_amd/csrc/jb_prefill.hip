@@ -50,6 +50,10 @@ enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1 };
 
 struct ChunkArgs {
   int T, H, nchunks, seg_len, nseg;
+  // packed sequences of different lengths: sequence b is rows cu_seqlens[b] ..
+  // cu_seqlens[b+1] - 1 of the token-major tensors, at most T of them (NULL:
+  // every sequence has T tokens, rows b T .. b T + T - 1)
+  const int* cu_seqlens;
   const void* q;
   const void* k;
   const void* v;
@@ -271,6 +275,13 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
 
 // ------------------------------------------------------------ chunk kernel
 
+// Segments sequence b is cut into (at least one, which carries the state
+// through an empty sequence).
+__device__ __forceinline__ int seq_segments(int T, int seg_len) {
+  const int nch = (T + 63) / 64;
+  return max(1, (nch + seg_len - 1) / seg_len);
+}
+
 template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE, bool SC>
 __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   using L = Lds<DK, DV, IO, OP, MODE, SC>;
@@ -307,7 +318,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   const float4* sCwv = reinterpret_cast<const float4*>(sCwk + 4 * DK);
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int T = a.T, H = a.H;
+  const int H = a.H;
+  int64_t tok0;
+  int T;
+  seq_span(a.cu_seqlens, a.T, b, tok0, T);
+  const int nseg_b = seq_segments(T, a.seg_len);
+  // a packed batch plans its grid for the longest sequence: shorter ones
+  // leave the extra segments' workgroups idle (the summary kernel has one
+  // workgroup per segment but the last)
+  if (s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
   // the wave index is uniform across a wave: keep it (and what derives from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
@@ -365,7 +384,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     }
 
   const int c_begin = s * a.seg_len;
-  const int c_end = min(a.nchunks, c_begin + a.seg_len);
+  const int c_end = min((T + C - 1) / C, c_begin + a.seg_len);
 
   // Raw inputs of chunk cc straight into LDS: value rows t0-3 .. t0+63 into
   // sV (zeros where neither v nor the conv cache has a row), raw k (and q)
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       if (p < NPV) {
         const int r = p / PPR, pc = p % PPR, t = t0c - 3 + r;
         if (t >= 0 && r - 3 < nc)
-          dma16(v + (((int64_t)b * T + t) * H + h) * DV + pc * EP, sV + j * 64 * 16);
+          dma16(v + ((tok0 + t) * H + h) * DV + pc * EP, sV + j * 64 * 16);
         else if (t < 0 && cin)
           dma16(cin + (((int64_t)b * 3 + (3 + t)) * H + h) * DV + pc * EP, sV + j * 64 * 16);
         else
@@ -394,7 +413,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         const int p = j * 64 + lane;
         const int r = p / PPK, pc = p % PPK;
         if (p < C * PPK && r < nc) {
-          const int64_t off = (((int64_t)b * T + t0c + r) * H + h) * DK + pc * EP;
+          const int64_t off = ((tok0 + t0c + r) * H + h) * DK + pc * EP;
           dma16(k + off, sKraw + j * 64 * 16);
           if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
         }
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
           const int r = p / PPK, pc = p % PPK, t = t0c - 3 + r;
           if (t >= 0) {
             if (r - 3 < nc) {
-              const int64_t off = (((int64_t)b * T + t) * H + h) * DK + pc * EP;
+              const int64_t off = ((tok0 + t) * H + h) * DK + pc * EP;
               dma16(k + off, sKraw + j * 64 * 16);
               if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
             }
@@ -427,7 +446,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
     if (wave == GATE_WAVE && lane < nc) {
-      const int64_t gidx = ((int64_t)b * T + t0c + lane) * H + h;
+      const int64_t gidx = (tok0 + t0c + lane) * H + h;
       dma4(a.alpha + gidx, sGraw);
       dma4(a.beta + gidx, sGraw + C * 4);
       if constexpr (!SC) dma16(a.taps + gidx * 4, sGraw + C * 8);
@@ -438,7 +457,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n) {
     const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
     const __amdgpu_buffer_rsrc_t orsrc =
-        make_rsrc(reinterpret_cast<OUT*>(a.o) + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
+        make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0) * H + h) * DV, (uint32_t)n * rowb);
     const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -450,7 +469,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 
   // T is zero outside its band; the band is rewritten every chunk
   for (int e = tid; e < L::szT / 16; e += NTHR) reinterpret_cast<uint4*>(smem + L::oT)[e] = make_uint4(0u, 0u, 0u, 0u);
-  issue_chunk(c_begin);
+  if (c_begin < c_end) issue_chunk(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
@@ -852,7 +871,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * g4 + i;
         if (MODE == MODE_OUTPUT) {
-          if (s == a.nseg - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+          if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else if (ct < VCT) {
           a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else {
@@ -887,12 +906,19 @@ __device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const floa
   mma(acc, af, bf);
 }
 
-// grid (DV/16, H, B), one wavefront: M_0 = S0 (or 0); M_{s+1} = Phi_s M_s + D_s.
+// grid (DV/16, H, B), one wavefront: M_0 = S0 (or 0); M_{s+1} = Phi_s M_s + D_s
+// over the segments of sequence b (nseg is the per-sequence stride of the
+// segment buffers; a packed batch's shorter sequences use fewer).
 template <int DK, int DV, typename OP>
-__global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const float* S0, const float* Dsum,
-                                                    const float* Phi, float* Mstart) {
+__global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const int* cu_seqlens, int Tmax, int seg_len,
+                                                    const float* S0, const float* Dsum, const float* Phi,
+                                                    float* Mstart) {
   constexpr int RT = DK / 16, KB = DK / 32;
   const int ct = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int64_t tok0;
+  int T;
+  seq_span(cu_seqlens, Tmax, b, tok0, T);
+  const int nseg_b = seq_segments(T, seg_len);
   const int lane = threadIdx.x, m16 = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * H + h;
   const int col = ct * 16 + m16;
@@ -901,13 +927,13 @@ __global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const float
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) M[rt][i] = S0 ? S0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
-  for (int s = 0; s < nseg; ++s) {
+  for (int s = 0; s < nseg_b; ++s) {
     float* dst = Mstart + (bh * nseg + s) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[rt][i];
-    if (s == nseg - 1) break;
+    if (s == nseg_b - 1) break;
     const float* D = Dsum + (bh * nseg + s) * DK * DV;
     const float* P = Phi + (bh * nseg + s) * DK * DK;
     float bv[KB][8];
@@ -966,6 +992,8 @@ __global__ __launch_bounds__(PRO_THR) void prologue_kernel(int T, int H, const I
 PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, int seg_len) {
   PrefillPlan p{};
   p.B = B; p.T = T; p.H = H; p.dk = dk; p.dv = dv; p.io = io; p.out = out;
+  p.tokens = (int64_t)B * T;
+  p.cu_seqlens = nullptr;
   p.nchunks = (T + C - 1) / C;
   if (p.nchunks == 0) { p.seg_len = 1; p.nseg = 0; return p; }
   if (seg_len <= 0) {
@@ -982,7 +1010,7 @@ PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, i
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static size_t taps_bytes(const PrefillPlan& p) { return align256((size_t)p.B * p.T * p.H * 4 * sizeof(float)); }
+static size_t taps_bytes(const PrefillPlan& p) { return align256((size_t)p.tokens * p.H * 4 * sizeof(float)); }
 
 // (several segments) Mstart, Dsum, Phi
 static size_t segment_bytes(const PrefillPlan& p) {
@@ -999,8 +1027,8 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
   const dim3 blk(NTHR);
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY, SC><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
-    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(p.H, p.nseg, a.S0, a.Dsum, a.Phi,
-                                                                               const_cast<float*>(a.Mstart));
+    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+        p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
   }
   chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT, SC><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
   return hipGetLastError();
@@ -1042,6 +1070,7 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
   if (p.nchunks == 0) return hipSuccess;
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.cu_seqlens = p.cu_seqlens;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;
   set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
@@ -1072,6 +1101,7 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
   if (p.nchunks == 0) return hipSuccess;
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.cu_seqlens = p.cu_seqlens;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.conv_in = cv_in;
   a.wq = wq; a.wk = wk; a.wv = wv; a.cq_in = cq_in; a.ck_in = ck_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;

@@ -18,6 +18,9 @@ one torch generator seeded per workload:
     W1 ~ N(0,0.02); W2 ~ N(0,0.02)   (no biases)
 and for decode workloads, after those: the state S ~ N(0,0.1) and the conv
 cache ~ N(0,1), then every step's (x, q, k, v, alpha, beta) in step order.
+Packed batches (packed_prefill_inputs) draw one sequence of the total length
+with the recipe above and cut it at the given lengths; serving mixes draw the
+lengths uniformly from a range (request_lengths).
 The static-conv block's weights (static_conv_inputs) are drawn from a generator
 of their own: wq, wk, wv ~ U(-1/2, 1/2), the usual default initialisation of a
 depthwise conv of size 4 (bound 1/sqrt(fan-in)), and caches ~ N(0,1).
@@ -188,4 +191,26 @@ def static_conv_inputs(shape: Shape, seed: int = 0, device="cpu"):
     out["cache_q"] = _normal(g, (s.B, s.taps - 1, s.H, s.dk), 0.0, 1.0, device, io)
     out["cache_k"] = _normal(g, (s.B, s.taps - 1, s.H, s.dk), 0.0, 1.0, device, io)
     out["cache_v"] = _normal(g, (s.B, s.taps - 1, s.H, s.dv), 0.0, 1.0, device, io)
+    return out
+
+
+def request_lengths(n: int, lo: int, hi: int, seed: int = 0) -> list[int]:
+    """n sequence lengths drawn uniformly from [lo, hi] (a serving batch's length mix)."""
+    g = _gen(seed + 31337, "cpu")
+    return [int(t) for t in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
+def packed_prefill_inputs(lengths, H: int, dk: int, dv: int, d_model: int, seed: int = 0, device="cpu",
+                          io_dtype: str = "bf16"):
+    """Inputs of a packed batch: sequences of the given lengths back to back.  Returns the
+    prefill_inputs tensors without the batch axis (x [total,D], q,k [total,H,dk], v [total,H,dv],
+    alpha,beta [total,H], W1, W2) and cu_seqlens int32 [len(lengths)+1]."""
+    total = int(sum(lengths))
+    shape = Shape(B=1, T=total, H=H, dk=dk, dv=dv, d_model=d_model, io_dtype=io_dtype)
+    p = prefill_inputs(shape, seed=seed, device=device)
+    out = {k: (v[0] if k not in ("W1", "W2") else v) for k, v in p.items()}
+    cu = [0]
+    for t in lengths:
+        cu.append(cu[-1] + int(t))
+    out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=device)
     return out

@@ -72,11 +72,14 @@ _lib.jb_decode_step_from_x.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 _lib.jb_prefill_static_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_prefill_static.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 _lib.jb_decode_step_static.argtypes = [_S] + [_P] * 17 + [_P]
+_lib.jb_prefill_varlen_workspace_size.argtypes = [_S, ctypes.c_int64, ctypes.POINTER(_SZ)]
+_lib.jb_prefill_varlen.argtypes = [_S, ctypes.c_int64] + [_P] * 16 + [_P, _SZ, _P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
            "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x",
            "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x", "jb_prefill_static_workspace_size",
-           "jb_prefill_static", "jb_decode_step_static"):
+           "jb_prefill_static", "jb_decode_step_static", "jb_prefill_varlen_workspace_size",
+           "jb_prefill_varlen"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -405,3 +408,44 @@ def decode_step_static(S, cache_q, cache_k, cache_v, q_t, k_t, v_t, alpha_t, bet
                                       _ptr(v_t), _ptr(alpha_t), _ptr(beta_t), _ptr(wq), _ptr(wk), _ptr(wv),
                                       _ptr(o), _stream(stream)))
     return dict(o=o, S=S_out, cache_q=cq, cache_k=ck, cache_v=cv)
+
+
+def prefill_varlen_workspace_size(shape: Shape, total_tokens: int) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_prefill_varlen_workspace_size(ctypes.byref(shape), int(total_tokens), ctypes.byref(n)))
+    return n.value
+
+
+def prefill_varlen(cu_seqlens, x, q, k, v, alpha, beta, W1, W2, b1=None, b2=None, S0=None, conv_in=None, *,
+                   max_seqlen: int | None = None, out_dtype=torch.float32, seg_len: int | None = None, o=None,
+                   S_final=None, conv_out=None, want_conv_out=True, ws=None, stream=None):
+    """jb_prefill_varlen: B packed sequences.  cu_seqlens int32 [B+1] (device; its host copy is
+    read once for the longest length unless max_seqlen is given), x [total,D], q,k [total,H,dk],
+    v [total,H,dv], alpha,beta [total,H].  Returns dict(o, S_final, conv_out) with per-sequence
+    S_final [B,H,dk,dv] and conv_out [B,3,H,dv]."""
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    B = cu_seqlens.numel() - 1
+    total, D = x.shape
+    H, dk = q.shape[1], q.shape[2]
+    dv = v.shape[2]
+    if max_seqlen is None:
+        lens = cu_seqlens.cpu().diff()
+        max_seqlen = int(lens.max()) if B > 0 else 0
+    shape = make_shape(B, max_seqlen, H, dk, dv, D, _io_code(x), _DT[out_dtype],
+                       flag_segment(seg_len) if seg_len else 0)
+    dev = x.device
+    if o is None:
+        o = torch.empty((total, H, dv), dtype=out_dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv_out:
+        conv_out = torch.empty((B, 3, H, dv), dtype=x.dtype, device=dev)
+    need = prefill_varlen_workspace_size(shape, total)
+    if ws is None:
+        ws = workspace(need, dev)
+    _check(_lib.jb_prefill_varlen(ctypes.byref(shape), total, _ptr(cu_seqlens), _ptr(x), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(alpha), _ptr(beta), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(S0),
+                                  _ptr(conv_in), _ptr(o), _ptr(S_final), _ptr(conv_out), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return dict(o=o, S_final=S_final, conv_out=conv_out)

@@ -161,6 +161,43 @@ jb_status jb_decode_step(const jb_shape* shape, const float* S_in, float* S_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Packed batches of sequences of different lengths: the serving side of the
+ * pages' throughput method (Jet-Nemotron csdn translation, section 3.1 on the
+ * throughput test bed, and appendix A.3: chunked prefill, the decode batch
+ * made as large as memory allows).
+ * The token-major tensors hold the sequences back to back: sequence b is rows
+ * cu_seqlens[b] .. cu_seqlens[b+1] - 1.  S0, S_final [B][H][dk][dv] and
+ * conv_in, conv_out [B][3][H][dv] are per sequence, in the layouts
+ * jb_decode_step takes, so a prefill's outputs are a decode batch's inputs.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of jb_prefill_varlen for `shape` and `total_tokens` rows. */
+jb_status jb_prefill_varlen_workspace_size(const jb_shape* shape, int64_t total_tokens,
+                                           size_t* bytes);
+
+/*
+ * jb_prefill_varlen -- jb_prefill over B packed sequences.
+ *   shape.B      number of sequences; shape.T the longest sequence's length
+ *                (the grid is planned for it: a longer sequence is cut to its
+ *                first shape.T tokens)
+ *   total_tokens rows of the packed tensors, = cu_seqlens[B] (<= B * T)
+ *   cu_seqlens   int32 [B+1] in device memory: 0, then non-decreasing row
+ *                offsets up to total_tokens (the library cannot check device
+ *                memory on the host: other values make it read and write
+ *                outside the tensors); an empty sequence passes its state and
+ *                cache through
+ *   x [total][d_model], q, k [total][H][dk], v [total][H][dv],
+ *   alpha, beta [total][H], o [total][H][dv]; the rest as in jb_prefill.
+ */
+jb_status jb_prefill_varlen(const jb_shape* shape, int64_t total_tokens,
+                            const int32_t* cu_seqlens, const void* x, const void* q,
+                            const void* k, const void* v, const float* alpha,
+                            const float* beta, const void* W1, const void* b1,
+                            const void* W2, const void* b2, const float* S0,
+                            const void* conv_in, void* o, float* S_final, void* conv_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * The block from its layer input x.  The kernel generator takes the same
  * input as the Q/K/V projection layers (csdn translation, section 2.4), so the
  * projections and the generator's first layer share one pass over x:

@@ -175,3 +175,24 @@ def test_static_entries_reject_before_launch(jb):
     assert lib.jb_decode_step_static(ctypes.byref(d), *a, None) == 1
     d.T = 3
     assert lib.jb_decode_step_static(ctypes.byref(d), *dargs, None) == 1
+
+
+def test_varlen_entries_reject_before_launch(jb):
+    lib = jb.library()
+    n = ctypes.c_size_t(0)
+    s = jb.make_shape(4, 1000, 2, 32, 64, 128)   # 4 sequences, the longest 1000 tokens
+    assert lib.jb_prefill_varlen_workspace_size(ctypes.byref(s), 2500, ctypes.byref(n)) == 0
+    assert n.value >= 2500 * 2 * 16              # the taps of the packed rows
+    assert lib.jb_prefill_varlen_workspace_size(ctypes.byref(s), 4001, ctypes.byref(n)) == 1  # > B * T
+    assert "total_tokens" in jb.last_error()
+    assert lib.jb_prefill_varlen_workspace_size(ctypes.byref(s), -1, ctypes.byref(n)) == 1
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 16
+    a = list(args); a[0] = None  # cu_seqlens
+    assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *a, fake, 1 << 30, None) == 1
+    assert "cu_seqlens is NULL" in jb.last_error()
+    a = list(args); a[0] = ctypes.c_void_p(0x10002)  # cu_seqlens not 4-byte aligned
+    assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *a, fake, 1 << 30, None) == 1
+    a = list(args); a[2] = None  # q
+    assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *a, fake, 1 << 30, None) == 1
+    assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *args, fake, 16, None) == 3  # workspace too small
