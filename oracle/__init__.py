@@ -56,6 +56,8 @@ def _load():
         _lib.jbo_prefill_static.argtypes = [I] * 6 + [P] * 17 + [I]
         _lib.jbo_prefill_static.restype = I
         _lib.jbo_project.restype = I
+        _lib.jbo_backward.argtypes = [I] * 8 + [P] * 27 + [I]
+        _lib.jbo_backward.restype = I
         _lib.jbo_bf16_round.argtypes = [ctypes.c_double]
         _lib.jbo_bf16_round.restype = ctypes.c_double
     return _lib
@@ -260,3 +262,30 @@ def decode_step_static(S, cache_q, cache_k, cache_v, q_t, k_t, v_t, alpha_t, bet
                        np.asarray(alpha_t)[:, None], np.asarray(beta_t)[:, None], wq, wk, wv, S0=S,
                        cache_q=cache_q, cache_k=cache_k, cache_v=cache_v, nthreads=nthreads)
     return dict(o=r["o"][:, 0], S=r["S_final"], cache_q=r["cache_q"], cache_k=r["cache_k"], cache_v=r["cache_v"])
+
+
+def backward(x, q, k, v, alpha, beta, W1, W2, dout, b1=None, b2=None, S0=None, conv_in=None, dS_final=None,
+             dconv_out=None, nthreads: int | None = None):
+    """Reverse-mode gradient of prefill (jbo_backward) for the output gradients dout [B,T,H,dv],
+    dS_final [B,H,dk,dv] and dconv_out [B,K-1,H,dv] (both nullable).  Returns a dict of f64
+    arrays: dx, dq, dk, dv, dalpha, dbeta, dW1, db1, dW2, db2, dS0, dconv_in (the last two are
+    gradients with respect to the zeros used when S0 / conv_in are None)."""
+    x, q, k, v, alpha, beta = _f32(x), _f32(q), _f32(k), _f32(v), _f32(alpha), _f32(beta)
+    W1, W2, b1, b2 = _f32(W1), _f32(W2), _f32(b1), _f32(b2)
+    S0, conv_in, dout, dS_final, dconv_out = _f32(S0), _f32(conv_in), _f32(dout), _f32(dS_final), _f32(dconv_out)
+    B, T, D = x.shape
+    H, dk = q.shape[2], q.shape[3]
+    dv = v.shape[3]
+    G = W1.shape[0]
+    K = W2.shape[0] // H
+    out = dict(dx=np.empty((B, T, D)), dq=np.empty((B, T, H, dk)), dk=np.empty((B, T, H, dk)),
+               dv=np.empty((B, T, H, dv)), dalpha=np.empty((B, T, H)), dbeta=np.empty((B, T, H)),
+               dW1=np.empty((G, D)), db1=np.empty(G), dW2=np.empty((H * K, G)), db2=np.empty(H * K),
+               dS0=np.empty((B, H, dk, dv)), dconv_in=np.empty((B, K - 1, H, dv)))
+    rc = _load().jbo_backward(B, T, H, dk, dv, D, G, K, _p(x), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(W1),
+                              _p(b1), _p(W2), _p(b2), _p(S0), _p(conv_in), _p(dout), _p(dS_final), _p(dconv_out),
+                              *[_p(out[n]) for n in ("dx", "dq", "dk", "dv", "dalpha", "dbeta", "dW1", "db1", "dW2",
+                                                     "db2", "dS0", "dconv_in")], nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("jbo_backward rejected its arguments")
+    return out

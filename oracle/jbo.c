@@ -503,3 +503,255 @@ int jbo_prefill_static(int B, int T, int H, int dk, int dv, int K, const float* 
   if (cv_out) tail_rows(B, T, H, dv, K, v, cv_in, cv_out);
   return 0;
 }
+
+/* ----------------------------------------------------------------- backward */
+/*
+ * Reverse-mode gradient of the block (what training it needs: the pages
+ * train JetBlock inside the model, csdn translation, sections 2.2 and 3.1).
+ * Given the gradients of the outputs -- dout [B][T][H][dv] of o, dS_final
+ * [B][H][dk][dv] of S_final and dconv_out [B][K-1][H][dv] of conv_out, the
+ * latter two nullable (zero) -- it returns, all in double:
+ *   dx [B][T][D], dq, dk [B][T][H][dk], dv [B][T][H][dv],
+ *   dalpha, dbeta [B][T][H], dW1 [G][D], db1 [G], dW2 [H*K][G], db2 [H*K],
+ *   dS0 [B][H][dk][dv], dconv_in [B][K-1][H][dv]
+ * (gradients with respect to S0 and conv_in are returned even when those are
+ * NULL, i.e. with respect to the zeros used in their place).
+ *
+ * Token by token in reverse, with M = S^T and N the state before token t:
+ *   forward  a = N^T k,  M_t = alpha (N - beta k a^T) + beta k v'^T,  o = M_t^T q
+ *   reverse  dM += q do^T;  dq^ = M_t do;  e = dM^T k;
+ *            dv' = beta e;  dbeta = e . (v' - alpha a);
+ *            dalpha = sum(dM . N) - beta e . a;
+ *            dk^ = beta dM v' - alpha beta (dM a + N e);
+ *            dM <- alpha (dM - beta k e^T)          (the gradient of N)
+ * then through the L2 norms (q^ = q / n, n = sqrt(sum q^2 + eps):
+ * dq = dq^ / n - q (q . dq^) / n^3), the conv (dv'_t spread over the raw rows
+ * it read, dtaps_t[j] = dv'_t . raw_{t-3+j}) and the generator
+ * (taps = W2 h + b2, h = SiLU(p), p = W1 x + b1,
+ * SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p)).
+ * States are recomputed from checkpoints taken every 64 tokens.
+ */
+#define JBO_CKPT 64
+
+typedef struct {
+  int B, T, H, dk, dv, K;
+  const float *q, *k, *v, *alpha, *beta, *S0, *conv_in, *dout, *dS_final, *dconv_out;
+  const double* taps;
+  double *dq, *dk_, *dv_, *dalpha, *dbeta, *dS0, *dconv_in, *dtaps;
+  int unit0, unit1;
+} bwd_job;
+
+/* the raw-row gradient slot of token t (t < 0: the conv cache) */
+static double* draw_row(int t, int b, int h, int T, int H, int dv, int K, double* dv_, double* dconv_in) {
+  if (t >= 0) return dv_ + (((int64_t)b * T + t) * H + h) * dv;
+  return dconv_in + (((int64_t)b * (K - 1) + (K - 1) + t) * H + h) * dv;
+}
+
+static void* bwd_worker(void* p) {
+  bwd_job* J = (bwd_job*)p;
+  const int T = J->T, H = J->H, dk = J->dk, dv = J->dv, K = J->K;
+  const int64_t md = (int64_t)dk * dv;
+  const int nblk = (T + JBO_CKPT - 1) / JBO_CKPT;
+  double* ck = (double*)malloc(sizeof(double) * (size_t)(md * (nblk > 0 ? nblk : 1)));
+  double* Ms = (double*)malloc(sizeof(double) * (size_t)(md * JBO_CKPT));
+  double* M = (double*)malloc(sizeof(double) * (size_t)md);
+  double* dM = (double*)malloc(sizeof(double) * (size_t)md);
+  double *qh = (double*)malloc(sizeof(double) * dk), *kh = (double*)malloc(sizeof(double) * dk);
+  double *qr = (double*)malloc(sizeof(double) * dk), *kr = (double*)malloc(sizeof(double) * dk);
+  double *dqh = (double*)malloc(sizeof(double) * dk), *dkh = (double*)malloc(sizeof(double) * dk);
+  double *vc = (double*)malloc(sizeof(double) * dv), *a = (double*)malloc(sizeof(double) * dv);
+  double *e = (double*)malloc(sizeof(double) * dv), *dvc = (double*)malloc(sizeof(double) * dv);
+  double* otmp = (double*)malloc(sizeof(double) * dv);
+  for (int u = J->unit0; u < J->unit1; ++u) {
+    const int b = u / H, h = u % H;
+    const int64_t sbase = ((int64_t)b * H + h) * md;
+    /* forward to the checkpoints */
+    for (int64_t i = 0; i < md; ++i) M[i] = J->S0 ? (double)J->S0[sbase + i] : 0.0;
+    for (int t = 0; t < T; ++t) {
+      if (t % JBO_CKPT == 0) memcpy(ck + (int64_t)(t / JBO_CKPT) * md, M, sizeof(double) * (size_t)md);
+      const int64_t bth = ((int64_t)b * T + t) * H + h;
+      conv_one(b, t, h, T, H, dv, K, J->taps + bth * K, J->v, J->conv_in, vc);
+      for (int i = 0; i < dk; ++i) { qh[i] = J->q[bth * dk + i]; kh[i] = J->k[bth * dk + i]; }
+      l2n_row(qh, dk, qh);
+      l2n_row(kh, dk, kh);
+      rec_step(M, qh, kh, vc, J->alpha[bth], J->beta[bth], dk, dv, a, otmp);
+    }
+    /* reverse */
+    for (int64_t i = 0; i < md; ++i) dM[i] = J->dS_final ? (double)J->dS_final[sbase + i] : 0.0;
+    if (J->dconv_out)
+      for (int s = 0; s < K - 1; ++s) {
+        double* dst = draw_row(T - (K - 1) + s, b, h, T, H, dv, K, J->dv_, J->dconv_in);
+        const float* src = J->dconv_out + (((int64_t)b * (K - 1) + s) * H + h) * dv;
+        for (int c = 0; c < dv; ++c) dst[c] += src[c];
+      }
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+      const int t0 = blk * JBO_CKPT, t1 = t0 + JBO_CKPT < T ? t0 + JBO_CKPT : T;
+      /* states after each token of the block */
+      memcpy(M, ck + (int64_t)blk * md, sizeof(double) * (size_t)md);
+      for (int t = t0; t < t1; ++t) {
+        const int64_t bth = ((int64_t)b * T + t) * H + h;
+        conv_one(b, t, h, T, H, dv, K, J->taps + bth * K, J->v, J->conv_in, vc);
+        for (int i = 0; i < dk; ++i) { qh[i] = J->q[bth * dk + i]; kh[i] = J->k[bth * dk + i]; }
+        l2n_row(qh, dk, qh);
+        l2n_row(kh, dk, kh);
+        rec_step(M, qh, kh, vc, J->alpha[bth], J->beta[bth], dk, dv, a, otmp);
+        memcpy(Ms + (int64_t)(t - t0) * md, M, sizeof(double) * (size_t)md);
+      }
+      for (int t = t1 - 1; t >= t0; --t) {
+        const int64_t bth = ((int64_t)b * T + t) * H + h;
+        const double* Mt = Ms + (int64_t)(t - t0) * md;
+        const double* N = t > t0 ? Ms + (int64_t)(t - 1 - t0) * md : ck + (int64_t)blk * md;
+        const double al = J->alpha[bth], be = J->beta[bth];
+        const float* dot = J->dout + bth * dv;
+        conv_one(b, t, h, T, H, dv, K, J->taps + bth * K, J->v, J->conv_in, vc);
+        for (int i = 0; i < dk; ++i) { qr[i] = J->q[bth * dk + i]; kr[i] = J->k[bth * dk + i]; }
+        l2n_row(qr, dk, qh);
+        l2n_row(kr, dk, kh);
+        /* output: o = M_t^T q^ */
+        for (int i = 0; i < dk; ++i) {
+          double s = 0.0;
+          for (int c = 0; c < dv; ++c) {
+            dM[(int64_t)i * dv + c] += qh[i] * (double)dot[c];
+            s += Mt[(int64_t)i * dv + c] * (double)dot[c];
+          }
+          dqh[i] = s;
+        }
+        /* the update */
+        for (int c = 0; c < dv; ++c) {
+          double sa = 0.0, se = 0.0;
+          for (int i = 0; i < dk; ++i) {
+            sa += N[(int64_t)i * dv + c] * kh[i];
+            se += dM[(int64_t)i * dv + c] * kh[i];
+          }
+          a[c] = sa;
+          e[c] = se;
+        }
+        double dbe = 0.0, dal = 0.0, ea = 0.0;
+        for (int c = 0; c < dv; ++c) {
+          dvc[c] = be * e[c];
+          dbe += e[c] * (vc[c] - al * a[c]);
+          ea += e[c] * a[c];
+        }
+        for (int64_t i = 0; i < md; ++i) dal += dM[i] * N[i];
+        dal -= be * ea;
+        for (int i = 0; i < dk; ++i) {
+          double s1 = 0.0, s2 = 0.0, s3 = 0.0;
+          for (int c = 0; c < dv; ++c) {
+            s1 += dM[(int64_t)i * dv + c] * vc[c];
+            s2 += dM[(int64_t)i * dv + c] * a[c];
+            s3 += N[(int64_t)i * dv + c] * e[c];
+          }
+          dkh[i] = be * s1 - al * be * (s2 + s3);
+        }
+        for (int i = 0; i < dk; ++i)
+          for (int c = 0; c < dv; ++c) {
+            double* m = &dM[(int64_t)i * dv + c];
+            *m = al * (*m - be * kh[i] * e[c]);
+          }
+        J->dalpha[bth] = dal;
+        J->dbeta[bth] = dbe;
+        /* the L2 norms */
+        double sq = 0.0, sk = 0.0, qd = 0.0, kd = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          sq += qr[i] * qr[i]; sk += kr[i] * kr[i];
+          qd += qr[i] * dqh[i]; kd += kr[i] * dkh[i];
+        }
+        const double nq = sqrt(sq + JBO_EPS), nk = sqrt(sk + JBO_EPS);
+        for (int i = 0; i < dk; ++i) {
+          J->dq[bth * dk + i] = dqh[i] / nq - qr[i] * qd / (nq * nq * nq);
+          J->dk_[bth * dk + i] = dkh[i] / nk - kr[i] * kd / (nk * nk * nk);
+        }
+        /* the conv: v'_t = sum_j taps[j] raw_{t-3+j} */
+        for (int j = 0; j < K; ++j) {
+          const int tr = t - (K - 1) + j;
+          const float* row = v_row(tr, b, h, T, H, dv, K, J->v, J->conv_in);
+          double* drow = draw_row(tr, b, h, T, H, dv, K, J->dv_, J->dconv_in);
+          double dt = 0.0;
+          for (int c = 0; c < dv; ++c) {
+            if (row) dt += dvc[c] * (double)row[c];
+            drow[c] += J->taps[bth * K + j] * dvc[c];
+          }
+          J->dtaps[bth * K + j] = dt;
+        }
+      }
+    }
+    for (int64_t i = 0; i < md; ++i) J->dS0[sbase + i] = dM[i];
+  }
+  free(ck); free(Ms); free(M); free(dM); free(qh); free(kh); free(qr); free(kr); free(dqh); free(dkh);
+  free(vc); free(a); free(e); free(dvc); free(otmp);
+  return NULL;
+}
+
+int jbo_backward(int B, int T, int H, int dk, int dv, int D, int G, int K, const float* x, const float* q,
+                 const float* k, const float* v, const float* alpha, const float* beta, const float* W1,
+                 const float* b1, const float* W2, const float* b2, const float* S0, const float* conv_in,
+                 const float* dout, const float* dS_final, const float* dconv_out, double* dx, double* dq,
+                 double* dk_, double* dv_, double* dalpha, double* dbeta, double* dW1, double* db1, double* dW2,
+                 double* db2, double* dS0, double* dconv_in, int nthreads) {
+  if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || D <= 0 || G <= 0 || K < 1) return 1;
+  if (!x || !q || !k || !v || !alpha || !beta || !W1 || !W2 || !dout) return 1;
+  if (!dx || !dq || !dk_ || !dv_ || !dalpha || !dbeta || !dW1 || !db1 || !dW2 || !db2 || !dS0 || !dconv_in)
+    return 1;
+  const int64_t n_tok = (int64_t)B * T;
+  const int HK = H * K;
+  double* taps = (double*)malloc(sizeof(double) * (size_t)(n_tok * HK + 1));
+  double* dtaps = (double*)calloc((size_t)(n_tok * HK + 1), sizeof(double));
+  if (jbo_gen_taps(n_tok, D, G, H, K, x, W1, b1, W2, b2, taps, nthreads)) { free(taps); free(dtaps); return 1; }
+  memset(dv_, 0, sizeof(double) * (size_t)(n_tok * H * dv));
+  memset(dconv_in, 0, sizeof(double) * (size_t)B * (K - 1) * H * dv);
+  const int units = B * H;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > units) nthreads = units > 0 ? units : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  bwd_job* jobs = (bwd_job*)malloc(sizeof(bwd_job) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (bwd_job){B, T, H, dk, dv, K, q, k, v, alpha, beta, S0, conv_in, dout, dS_final, dconv_out, taps,
+                        dq, dk_, dv_, dalpha, dbeta, dS0, dconv_in, dtaps,
+                        (int)((int64_t)units * i / nthreads), (int)((int64_t)units * (i + 1) / nthreads)};
+    if (nthreads == 1) bwd_worker(&jobs[i]);
+    else pthread_create(&th[i], NULL, bwd_worker, &jobs[i]);
+  }
+  if (nthreads > 1)
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  /* the generator, token by token */
+  memset(dW1, 0, sizeof(double) * (size_t)G * D);
+  memset(db1, 0, sizeof(double) * (size_t)G);
+  memset(dW2, 0, sizeof(double) * (size_t)HK * G);
+  memset(db2, 0, sizeof(double) * (size_t)HK);
+  double* pre = (double*)malloc(sizeof(double) * (size_t)G);
+  double* hid = (double*)malloc(sizeof(double) * (size_t)G);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)G);
+  for (int64_t n = 0; n < n_tok; ++n) {
+    const float* xr = x + n * D;
+    for (int g = 0; g < G; ++g) {
+      double acc = b1 ? (double)b1[g] : 0.0;
+      for (int d = 0; d < D; ++d) acc += (double)W1[(int64_t)g * D + d] * (double)xr[d];
+      pre[g] = acc;
+      hid[g] = acc / (1.0 + exp(-acc));
+    }
+    const double* dt = dtaps + n * HK;
+    for (int g = 0; g < G; ++g) {
+      double dh = 0.0;
+      for (int r = 0; r < HK; ++r) dh += (double)W2[(int64_t)r * G + g] * dt[r];
+      const double s = 1.0 / (1.0 + exp(-pre[g]));
+      dp[g] = dh * s * (1.0 + pre[g] * (1.0 - s));
+    }
+    for (int r = 0; r < HK; ++r) {
+      db2[r] += dt[r];
+      for (int g = 0; g < G; ++g) dW2[(int64_t)r * G + g] += dt[r] * hid[g];
+    }
+    for (int g = 0; g < G; ++g) {
+      db1[g] += dp[g];
+      for (int d = 0; d < D; ++d) dW1[(int64_t)g * D + d] += dp[g] * (double)xr[d];
+    }
+    for (int d = 0; d < D; ++d) {
+      double s = 0.0;
+      for (int g = 0; g < G; ++g) s += (double)W1[(int64_t)g * D + d] * dp[g];
+      dx[n * D + d] = s;
+    }
+  }
+  free(pre); free(hid); free(dp); free(taps); free(dtaps);
+  return 0;
+}
