@@ -548,6 +548,74 @@ jb_status jb_decode_step_static(const jb_shape* s, const float* S_in, float* S_o
                                                  static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+jb_status check_backward(const char* fn, const jb_shape* s) {
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the backward pass takes bf16 inputs only", fn);
+  if (!jb::backward_supported(jb::IO_BF16, s->dk, s->dv))
+    return fail(JB_ERR_UNSUPPORTED, "%s: (dk, dv) = (%d, %d) not built (built: (32,64), (64,128), (96,256), (128,256))",
+                fn, s->dk, s->dv);
+  if (s->flags) return fail(JB_ERR_INVALID_ARG, "%s: flags must be 0", fn);
+  return JB_OK;
+}
+
+}  // namespace
+
+jb_status jb_backward_workspace_size(const jb_shape* s, size_t* bytes) {
+  const char* fn = "jb_backward_workspace_size";
+  jb_status st = check_backward(fn, s);
+  if (st) return st;
+  if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  *bytes = jb::backward_workspace_bytes(s->B, s->T, s->H, s->dk, s->dv, s->d_model);
+  return ok();
+}
+
+jb_status jb_backward(const jb_shape* s, const void* x, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const void* W1, const void* b1, const void* W2,
+                      const void* b2, const float* S0, const void* conv_in, const float* dout, const float* dS_final,
+                      const float* dconv_out, float* dx, float* dq, float* dk, float* dv, float* dalpha,
+                      float* dbeta, float* dW1, float* db1, float* dW2, float* db2, float* dS0, float* dconv_in,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "jb_backward";
+  jb_status st = check_backward(fn, s);
+  if (st) return st;
+  if (s->T > 0) {
+    JB_REQUIRE_PTR(x); JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v);
+    JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta); JB_REQUIRE_PTR(dout);
+    JB_REQUIRE_PTR(dx); JB_REQUIRE_PTR(dq); JB_REQUIRE_PTR(dk); JB_REQUIRE_PTR(dv);
+    JB_REQUIRE_SCALARS(dalpha); JB_REQUIRE_SCALARS(dbeta);
+  }
+  JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2);
+  JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(conv_in); JB_OPTIONAL_PTR(dS_final); JB_OPTIONAL_PTR(dconv_out);
+  JB_REQUIRE_PTR(dW1); JB_REQUIRE_SCALARS(db1); JB_REQUIRE_PTR(dW2); JB_REQUIRE_SCALARS(db2);
+  JB_REQUIRE_PTR(dS0); JB_REQUIRE_PTR(dconv_in);
+  const size_t need = jb::backward_workspace_bytes(s->B, s->T, s->H, s->dk, s->dv, s->d_model);
+  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (s->T == 0) {
+    // nothing was computed: the state and cache gradients pass through, the weights get none
+    const size_t ns = (size_t)s->B * s->H * s->dk * s->dv, nc = (size_t)s->B * 3 * s->H * s->dv;
+    e = dS_final ? hipMemcpyAsync(dS0, dS_final, ns * 4, hipMemcpyDeviceToDevice, hs) : jb::launch_fill_zero(dS0, ns, hs);
+    if (e == hipSuccess)
+      e = dconv_out ? hipMemcpyAsync(dconv_in, dconv_out, nc * 4, hipMemcpyDeviceToDevice, hs)
+                    : jb::launch_fill_zero(dconv_in, nc, hs);
+    if (e == hipSuccess) e = jb::launch_fill_zero(dW1, (size_t)32 * s->d_model, hs);
+    if (e == hipSuccess) e = jb::launch_fill_zero(db1, 32, hs);
+    if (e == hipSuccess) e = jb::launch_fill_zero(dW2, (size_t)4 * s->H * 32, hs);
+    if (e == hipSuccess) e = jb::launch_fill_zero(db2, (size_t)4 * s->H, hs);
+    return hip_status(fn, e);
+  }
+  return hip_status(fn, jb::launch_backward(s->B, s->T, s->H, s->dk, s->dv, s->d_model, x, q, k, v, alpha, beta, W1,
+                                            b1, W2, b2, S0, conv_in, dout, dS_final, dconv_out, dx, dq, dk, dv,
+                                            dalpha, dbeta, dW1, db1, dW2, db2, dS0, dconv_in, workspace, hs));
+}
+
 jb_status jb_gen_taps(const jb_shape* s, const void* x, const void* W1, const void* b1, const void* W2, const void* b2,
                       float* taps, void* stream) {
   const char* fn = "jb_gen_taps";

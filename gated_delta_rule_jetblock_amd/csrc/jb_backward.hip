@@ -1,0 +1,1070 @@
+// jb_backward.hip -- the gradient of the block (training; the pages train
+// JetBlock inside the model: Jet-Nemotron csdn translation, sections 2.2 and
+// 3.1), chunked like the forward pass.
+//
+// Per chunk of C = 64 tokens entering with state M0 and leaving with M_C
+// (notation of jb_prefill.hip: A, T = (I + A)^{-1}, W = T diag(b gamma) K,
+// U0 = T diag(b) V', U = U0 - W M0, P, gamma, D = e^{g_C - g}), given dO and
+// the gradient dM of M_C:
+//   chain (sequential, backwards over chunks):
+//     dU = P^T dO + D K dM,   dM <- gamma_C dM + Q^T Gamma dO - W^T dU
+//   per chunk (parallel):
+//     dP = lower(dO U^T),  dQ = (dP.E) K + Gamma dO M0^T
+//     dW = -dU M0^T,  dB_w = T^T dW,  dB_u = T^T dU,  dV' = diag(b) dB_u
+//     dA = strictLower(-(dB_w W^T + dB_u U0^T)),  dS = dA . b_i E_ij
+//     dK = (dP.E)^T Q + D (U dM^T) + diag(b gamma) dB_w + (dS + dS^T) K
+//     db_i = gamma_i dB_w,i.k_i + dB_u,i.v'_i + sum_j dA_ij E_ij k_i.k_j
+//     dg from P, from Gamma in O, from A, from gamma in W, from gamma_C and D
+//     d ln a = reverse cumulative sum of dg within the chunk
+// then through the L2 norms, the conv and the generator.  The gradients of o
+// and S_final are scaled by a power of two (their largest magnitude brought
+// to [0.5, 1)) before they meet fp16 matrix-core operands, and every result
+// is scaled back, so the fp16 range never clips a gradient.
+#include "jb_chunk.h"
+#include "jb_device.h"
+#include "jb_internal.h"
+
+namespace jb {
+
+struct BwdArgs {
+  int T, H, nchunks;
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* conv_in;
+  const float* alpha;
+  const float* beta;
+  const float* taps;      // [B][T][H][4]
+  const float* dout;      // [B][T][H][DV]
+  const float* dS_final;  // [B][H][DK][DV] or NULL
+  const float* scale;     // [0] = s, [1] = 1/s
+  const float* Mck;       // [B][H][nchunks][DK][DV]: the state entering each chunk
+  float* dMck;            // [B][H][nchunks][DK][DV]: s x the gradient of the state leaving each chunk
+  float* dU;              // [B][T][H][DV]: s x dU
+  float* dS0;             // [B][H][DK][DV]
+  float* dq;              // [B][T][H][DK]
+  float* dk;
+  float* dalpha;          // [B][T][H]
+  float* dbeta;
+  float* dvc;             // [B][T][H][DV]: dV'
+};
+
+// ------------------------------------------------------------ gradient scale
+
+// scale[0] = 2^-e with max(|dout|, |dS_final|) 2^-e in [0.5, 1) (1 when all
+// are zero); scale[1] = 2^e.  One workgroup.
+__global__ __launch_bounds__(1024) void grad_scale_kernel(const float* dout, int64_t n_out, const float* dS,
+                                                          int64_t n_s, float* scale) {
+  __shared__ float sm[16];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < n_out; i += blockDim.x) m = fmaxf(m, fabsf(dout[i]));
+  if (dS)
+    for (int64_t i = threadIdx.x; i < n_s; i += blockDim.x) m = fmaxf(m, fabsf(dS[i]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mm = fmaxf(mm, sm[w]);
+    int e = 0;
+    if (mm > 0.f && isfinite(mm)) frexpf(mm, &e);  // mm = f 2^e, f in [0.5, 1)
+    scale[0] = ldexpf(1.f, -e);
+    scale[1] = ldexpf(1.f, e);
+  }
+}
+
+// ------------------------------------------------------------ chain kernel
+
+// grid (H, B), 8 waves; wave w owns dv column tiles w, w + 8, .. of dM, kept
+// in accumulator registers while the chunks are walked backwards.
+template <int DK, int DV>
+__global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
+  using OP = _Float16;
+  constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36;
+  constexpr int NCT = DV / 16, CPW = (NCT + NWAVE - 1) / NWAVE, RT = DK / 16, KB = DK / 32;
+  constexpr int oKh = 0;
+  constexpr int oQh = oKh + C * LDK * 2;
+  constexpr int oQt = oQh + C * LDK * 2;
+  constexpr int oWt = oQt + DK * LC * 2;
+  constexpr int oPt = oWt + DK * LC * 2;
+  constexpr int oAn = oPt + C * LC * 2;
+  constexpr int oAd = oAn + C * LC * 2;
+  constexpr int oLi = oAd + C * LAD * 4;
+  constexpr int oScal = oLi + C * LLI * 2;
+  constexpr int total = oScal + 4 * C * 4;
+  static_assert(total <= 160 * 1024, "LDS budget");
+  static_assert(RT <= NWAVE, "one wave per W column tile");
+  __shared__ __attribute__((aligned(16))) char smem[total];
+  OP* sKh = reinterpret_cast<OP*>(smem + oKh);   // [C][LDK]  normalised k
+  OP* sQh = reinterpret_cast<OP*>(smem + oQh);   // [C][LDK]  normalised q
+  OP* sQt = reinterpret_cast<OP*>(smem + oQt);   // [DK][LC]  its transpose
+  OP* sWt = reinterpret_cast<OP*>(smem + oWt);   // [DK][LC]  -W^T
+  OP* sPt = reinterpret_cast<OP*>(smem + oPt);   // [C][LC]   P^T
+  OP* sAn = reinterpret_cast<OP*>(smem + oAn);   // [C][LC]   -A
+  float* sAd = reinterpret_cast<float*>(smem + oAd);
+  OP* sLi = reinterpret_cast<OP*>(smem + oLi);
+  float* sG = reinterpret_cast<float*>(smem + oScal);
+  float* sGam = sG + C;
+  float* sBeta = sG + 2 * C;
+  float* sDec = sG + 3 * C;
+
+  const int h = blockIdx.x, b = blockIdx.y, H = a.H, T = a.T;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int64_t bh = (int64_t)b * H + h;
+  const float s = a.scale[0];
+  const int64_t rowld = (int64_t)H * DV;
+
+  for (int e = tid; e < C * C; e += NTHR) {
+    const int r = e / C, cc = e % C;
+    if ((r >> 4) > (cc >> 4)) sPt[r * LC + cc] = (OP)0.f;  // below the block diagonal: never written
+  }
+  f4_t dM[CPW][RT];
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        dM[cw][rt][i] = (ct < NCT && a.dS_final) ? s * a.dS_final[(bh * DK + row) * DV + ct * 16 + m16] : 0.f;
+      }
+  }
+
+  for (int c = a.nchunks - 1; c >= 0; --c) {
+    const int t0 = c * C, n = min(C, T - t0);
+    const float* dO = a.dout + (((int64_t)b * T + t0) * H + h) * DV;
+    // this chunk's dO tiles, issued first (accumulator layout)
+    f4_t dOr[CPW][4];
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) {
+      const int ct = wave + cw * NWAVE;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rt * 16 + 4 * g4 + i;
+          dOr[cw][rt][i] = (ct < NCT && row < n) ? s * dO[row * rowld + ct * 16 + m16] : 0.f;
+        }
+    }
+    __syncthreads();  // the previous chunk's column phase is done with the tiles
+
+    if (tid < PRO_THR) {
+      Prologue<DK, bf16_t> pr;
+      pr.load(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n, true);
+      pr.finish(true);
+#pragma unroll
+      for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
+        const int d = pr.part * Prologue<DK, bf16_t>::E + e;
+        const OP kh = (OP)pr.kv[e], qh = (OP)pr.qv[e];
+        sKh[pr.row * LDK + d] = kh;
+        sQh[pr.row * LDK + d] = qh;
+        sQt[d * LC + pr.row] = qh;
+      }
+    }
+    if (wave == GATE_WAVE) {
+      const bool valid = lane < n;
+      const int64_t gidx = ((int64_t)b * T + t0 + lane) * H + h;
+      const float al = valid ? a.alpha[gidx] : 1.f;
+      const float be = valid ? a.beta[gidx] : 0.f;
+      const float g = chunk_gate_scan(al);
+      const float gC = __shfl(g, C - 1, WAVE);
+      sG[lane] = g;
+      sGam[lane] = fast_exp2(g);
+      sBeta[lane] = be;
+      sDec[lane] = fast_exp2(gC - g);
+    }
+    __syncthreads();
+
+    // -A and its diagonal blocks (lower tiles), P^T (upper tiles)
+    for (int job = wave; job < 20; job += NWAVE) {
+      const int which = job >= 10, t = job - 10 * which;
+      const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+      f4_t acc = zero4();
+      if (which == 0) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mma(acc, lds_frag<OP>(sKh, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+          const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
+          sAn[r * LC + cc] = (OP)(-av);
+          if (ti == tj) sAd[r * LAD + m16] = av;
+        }
+      } else {
+        // P^T block (tj, ti): keys of block tj against queries of block ti
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mma(acc, lds_frag<OP>(sKh, LDK, tj * 16, kb * 32), lds_frag<OP>(sQh, LDK, ti * 16, kb * 32));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = tj * 16 + 4 * g4 + i, cc = ti * 16 + m16;
+          sPt[r * LC + cc] = (OP)(cc >= r ? fast_exp2(sG[cc] - sG[r]) * acc[i] : 0.f);
+        }
+      }
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+      // diagonal-block inverses, one column per lane (as in the forward pass)
+      const int base = (lane >> 4) * 16, jc = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == jc) ? 1.f : 0.f;
+        const float* arow = sAd + (base + i) * LAD;
+#pragma unroll
+        for (int k4 = 0; k4 < i; k4 += 4) {
+          const float4 av = *reinterpret_cast<const float4*>(arow + k4);
+          acc -= av.x * x[k4];
+          if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
+          if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
+          if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
+        }
+        x[i] = acc;
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sLi[(base + i) * LLI + jc] = (OP)x[i];
+        sLi[(base + i) * LLI + 16 + jc] = (OP)0.f;
+      }
+    }
+    __syncthreads();
+
+    if (wave < RT) {
+      // W column tile `wave`, stored as -W^T
+      f4_t Y[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rb * 16 + 4 * g4 + i;
+          Y[rb][i] = sBeta[r] * sGam[r] * (float)sKh[r * LDK + wave * 16 + m16];
+        }
+      block_solve<OP, LC, LLI>(Y, sAn, sLi);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sWt[(wave * 16 + m16) * LC + rb * 16 + 4 * g4 + i] = (OP)(-Y[rb][i]);
+    }
+    __syncthreads();
+
+    const float gamC = sGam[C - 1];
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) {
+      const int ct = wave + cw * NWAVE;
+      if (ct >= NCT) continue;
+      const int col = ct * 16 + m16;
+      // dU = P^T dO + D (K dM)
+      f4_t dU[4], tk[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) { dU[rt] = zero4(); tk[rt] = zero4(); }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<OP> fo = acc_frag<OP>(dOr[cw][2 * kb], dOr[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          if (kb * 32 + 31 >= rt * 16) mma(dU[rt], lds_frag<OP>(sPt, LC, rt * 16, kb * 32), fo);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag<OP> fm = acc_frag<OP>(dM[cw][2 * kb], dM[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mma(tk[rt], lds_frag<OP>(sKh, LDK, rt * 16, kb * 32), fm);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dU[rt][i] += sDec[rt * 16 + 4 * g4 + i] * tk[rt][i];
+      // the gradient of the chunk-end state and dU, for the per-chunk pass
+      float* dMo = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dMo[(rt * 16 + 4 * g4 + i) * DV + col] = dM[cw][rt][i];
+      float* dUo = a.dU + (((int64_t)b * T + t0) * H + h) * DV;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = rt * 16 + 4 * g4 + i;
+          if (row < n) dUo[row * rowld + col] = dU[rt][i];
+        }
+      // dM <- gamma_C dM + Q^T Gamma dO - W^T dU
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dM[cw][rt][i] *= gamC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<OP> fo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fo.v[j] = (OP)(dOr[cw][2 * kb][j] * sGam[kb * 32 + 4 * g4 + j]);
+          fo.v[4 + j] = (OP)(dOr[cw][2 * kb + 1][j] * sGam[kb * 32 + 16 + 4 * g4 + j]);
+        }
+        const Frag<OP> fu = acc_frag<OP>(dU[2 * kb], dU[2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          mma(dM[cw][rt], lds_frag<OP>(sQt, LC, rt * 16, kb * 32), fo);
+          mma(dM[cw][rt], lds_frag<OP>(sWt, LC, rt * 16, kb * 32), fu);
+        }
+      }
+    }
+  }
+
+  const float inv = a.scale[1];
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+    if (ct >= NCT) continue;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.dS0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + ct * 16 + m16] = dM[cw][rt][i] * inv;
+  }
+}
+
+// ------------------------------------------------------------ per-chunk gradients
+
+// sum of v over the 16 lanes of a lane group (all of them receive it)
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+// sum of v over the 4 lane groups at the same lane position
+__device__ __forceinline__ float sum_groups(float v) {
+  v += __shfl_xor(v, 16, WAVE);
+  v += __shfl_xor(v, 32, WAVE);
+  return v;
+}
+
+// Y = (I + A)^{-T} R for a 64 x 16 right-hand side in accumulator layout:
+// backward substitution over the transposed blocks; sAnT holds -A^T and sLiT
+// the transposed diagonal-block inverses (columns 16..31 zero).
+template <int LC, int LLI>
+__device__ __forceinline__ void block_solve_t(f4_t (&Y)[4], const _Float16* sAnT, const _Float16* sLiT) {
+  using OP = _Float16;
+  const f4_t z = zero4();
+  f4_t t = zero4();
+  mma(t, lds_frag<OP>(sLiT, LLI, 48, 0), acc_frag<OP>(Y[3], z));
+  Y[3] = t;
+  mma(Y[2], lds_frag<OP>(sAnT, LC, 32, 32), acc_frag<OP>(z, Y[3]));
+  t = zero4();
+  mma(t, lds_frag<OP>(sLiT, LLI, 32, 0), acc_frag<OP>(Y[2], z));
+  Y[2] = t;
+  const Frag<OP> f23 = acc_frag<OP>(Y[2], Y[3]);
+  mma(Y[1], lds_frag<OP>(sAnT, LC, 16, 32), f23);
+  mma(Y[0], lds_frag<OP>(sAnT, LC, 0, 32), f23);
+  t = zero4();
+  mma(t, lds_frag<OP>(sLiT, LLI, 16, 0), acc_frag<OP>(Y[1], z));
+  Y[1] = t;
+  mma(Y[0], lds_frag<OP>(sAnT, LC, 0, 0), acc_frag<OP>(z, Y[1]));
+  t = zero4();
+  mma(t, lds_frag<OP>(sLiT, LLI, 0, 0), acc_frag<OP>(Y[0], z));
+  Y[0] = t;
+}
+
+// grid (nchunks, H, B), 8 waves.  The dv columns are taken 32 at a time: two
+// waves form that block's U0, U and dB_u (accumulator layout, staged in LDS
+// as fp16), then every wave adds the block's share of the dv-reduced
+// products it owns: C x C tiles of dP and dB_u U0^T (jobs spread over the
+// waves), and for wave w < DK/16 column tile w of dO M0^T, U dM^T, dU M0^T.
+template <int DK, int DV>
+__global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
+  using OP = _Float16;
+  constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36, KW = 32, LKW = KW + 8;
+  constexpr int RT = DK / 16, KB = DK / 32, NKB = DV / KW;
+  constexpr int oKh = 0;
+  constexpr int oQh = oKh + C * LDK * 2;
+  constexpr int oW = oQh + C * LDK * 2;
+  constexpr int oAn = oW + C * LDK * 2;
+  constexpr int oAnT = oAn + C * LC * 2;
+  constexpr int oAd = oAnT + C * LC * 2;
+  constexpr int oLi = oAd + C * LAD * 4;
+  constexpr int oLiT = oLi + C * LLI * 2;
+  constexpr int oScal = oLiT + C * LLI * 2;           // g, gamma, beta, D, taps [C][4], norms, sums
+  constexpr int nScal = 4 * C + 4 * C + 2 * C + 6 * C + 4;
+  constexpr int oU = oScal + nScal * 4;               // union: staging during the dv loop, then dP.E, dS, dB_w
+  constexpr int szStage = 3 * C * LKW * 2;
+  constexpr int szPost = 2 * C * LC * 2 + C * LDK * 2;
+  constexpr int total = oU + (szStage > szPost ? szStage : szPost);
+  static_assert(total <= 160 * 1024, "LDS budget");
+  static_assert(RT <= NWAVE, "one wave per dk column tile");
+  __shared__ __attribute__((aligned(16))) char smem[total];
+  OP* sKh = reinterpret_cast<OP*>(smem + oKh);
+  OP* sQh = reinterpret_cast<OP*>(smem + oQh);
+  OP* sW = reinterpret_cast<OP*>(smem + oW);      // [C][LDK] W
+  OP* sAn = reinterpret_cast<OP*>(smem + oAn);    // [C][LC] -A
+  OP* sAnT = reinterpret_cast<OP*>(smem + oAnT);  // [C][LC] -A^T
+  float* sAd = reinterpret_cast<float*>(smem + oAd);
+  OP* sLi = reinterpret_cast<OP*>(smem + oLi);
+  OP* sLiT = reinterpret_cast<OP*>(smem + oLiT);
+  float* sG = reinterpret_cast<float*>(smem + oScal);
+  float* sGam = sG + C;
+  float* sBeta = sG + 2 * C;
+  float* sDec = sG + 3 * C;
+  float* sTap = sG + 4 * C;        // [C][4]
+  float* sNq = sTap + 4 * C;       // norms of the raw q, k rows
+  float* sNk = sNq + C;
+  float* sDg = sNk + C;            // d g (before the reverse cumsum)
+  float* sDb = sDg + C;            // d beta
+  float* sDD = sDb + C;            // k_i . (U dM^T)_i (the D term)
+  float* sQd = sDD + C;            // q_i . dq^_i and k_i . dk^_i (norm backward)
+  float* sKd = sQd + C;
+  float* sMisc = sKd + C;          // [0]: sum(dM . M0)
+  OP* sUb = reinterpret_cast<OP*>(smem + oU);        // [C][LKW] U of the current dv block
+  OP* sU0b = sUb + C * LKW;                          // U0
+  OP* sBub = sU0b + C * LKW;                         // dB_u
+  OP* sdPE = reinterpret_cast<OP*>(smem + oU);       // after the loop: [C][LC] dP . E
+  OP* sdS = sdPE + C * LC;                           // [C][LC] dS
+  OP* sdBw = sdS + C * LC;                           // [C][LDK] dB_w
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = a.H, T = a.T;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int64_t bh = (int64_t)b * H + h;
+  const int t0 = c * C, n = min(C, T - t0);
+  const float s = a.scale[0], inv = a.scale[1];
+  const int64_t rowld = (int64_t)H * DV;
+  const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
+  const float* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+  const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
+  const float* dO = a.dout + tokbase * DV;
+  const float* dUg = a.dU + tokbase * DV;
+
+  // ---- prologue: normalised q, k, gates, taps, norms
+  if (tid < PRO_THR) {
+    Prologue<DK, bf16_t> pr;
+    pr.load(a.q, a.k, tokbase, H, n, true);
+    // raw norms for the backward of the normalisation
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) { sk += pr.kv[e] * pr.kv[e]; sq += pr.qv[e] * pr.qv[e]; }
+    sk = group_sum<8>(sk);
+    sq = group_sum<8>(sq);
+    if (pr.part == 0) {
+      sNk[pr.row] = sqrtf(sk + 1e-6f);
+      sNq[pr.row] = sqrtf(sq + 1e-6f);
+    }
+    pr.finish(true);
+#pragma unroll
+    for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
+      const int d = pr.part * Prologue<DK, bf16_t>::E + e;
+      sKh[pr.row * LDK + d] = (OP)pr.kv[e];
+      sQh[pr.row * LDK + d] = (OP)pr.qv[e];
+    }
+  }
+  if (wave == GATE_WAVE) {
+    const bool valid = lane < n;
+    const float al = valid ? a.alpha[tokbase + (int64_t)lane * H] : 1.f;
+    const float be = valid ? a.beta[tokbase + (int64_t)lane * H] : 0.f;
+    const float4 tp = valid ? *reinterpret_cast<const float4*>(a.taps + (tokbase + (int64_t)lane * H) * 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float g = chunk_gate_scan(al);
+    const float gC = __shfl(g, C - 1, WAVE);
+    sG[lane] = g;
+    sGam[lane] = fast_exp2(g);
+    sBeta[lane] = be;
+    sDec[lane] = fast_exp2(gC - g);
+    *reinterpret_cast<float4*>(sTap + lane * 4) = tp;
+    sDg[lane] = 0.f;
+    sDb[lane] = 0.f;
+    sDD[lane] = 0.f;
+    sQd[lane] = 0.f;
+    sKd[lane] = 0.f;
+    if (lane == 0) sMisc[0] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- -A, its transpose and diagonal blocks
+  for (int t = wave; t < 10; t += NWAVE) {
+    const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+    f4_t acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      mma(acc, lds_frag<OP>(sKh, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+      const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
+      sAn[r * LC + cc] = (OP)(-av);
+      sAnT[cc * LC + r] = (OP)(-av);
+      if (ti != tj) sAnT[r * LC + cc] = (OP)0.f;  // the mirror tile of -A^T is zero
+      if (ti == tj) sAd[r * LAD + m16] = av;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int base = (lane >> 4) * 16, jc = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == jc) ? 1.f : 0.f;
+      const float* arow = sAd + (base + i) * LAD;
+#pragma unroll
+      for (int k4 = 0; k4 < i; k4 += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(arow + k4);
+        acc -= av.x * x[k4];
+        if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
+        if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
+        if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
+      }
+      x[i] = acc;
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sLi[(base + i) * LLI + jc] = (OP)x[i];
+      sLi[(base + i) * LLI + 16 + jc] = (OP)0.f;
+      sLiT[(base + jc) * LLI + i] = (OP)x[i];
+      sLiT[(base + i) * LLI + 16 + jc] = (OP)0.f;
+    }
+  }
+  __syncthreads();
+  if (wave < RT) {
+    f4_t Y[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * g4 + i;
+        Y[rb][i] = sBeta[r] * sGam[r] * (float)sKh[r * LDK + wave * 16 + m16];
+      }
+    block_solve<OP, LC, LLI>(Y, sAn, sLi);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sW[(rb * 16 + 4 * g4 + i) * LDK + wave * 16 + m16] = (OP)Y[rb][i];
+  }
+  __syncthreads();
+
+  // ---- the dv-reduced products, 32 columns at a time
+  f4_t accCC[3];                       // C x C jobs: wave, wave + 8, wave + 16 of {dP tiles, dB_u U0^T tiles}
+  f4_t aQO[4], aKM[4], aW[4];          // column tile `wave` of dO M0^T, U dM^T, dU M0^T
+#pragma unroll
+  for (int i = 0; i < 3; ++i) accCC[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { aQO[i] = zero4(); aKM[i] = zero4(); aW[i] = zero4(); }
+  float dgC_part = 0.f;
+  for (int kb = 0; kb < NKB; ++kb) {
+    if (wave < 2) {
+      const int col = kb * KW + wave * 16 + m16;
+      // V' (the conv of the raw value rows with the chunk's taps)
+      f4_t Vp[4], Y[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * g4 + i;
+          float acc = 0.f;
+          if (r < n) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int t = t0 + r - 3 + j;
+              float x = 0.f;
+              if (t >= 0) x = bf16_to_f32(a.v[(((int64_t)b * T + t) * H + h) * DV + col]);
+              else if (a.conv_in) x = bf16_to_f32(a.conv_in[(((int64_t)b * 3 + 3 + t) * H + h) * DV + col]);
+              acc += sTap[r * 4 + j] * x;
+            }
+          }
+          Vp[rt][i] = acc;
+          Y[rt][i] = sBeta[r] * acc;
+        }
+      block_solve<OP, LC, LLI>(Y, sAn, sLi);  // U0
+      // U = U0 - W M0 (M0 tile in accumulator layout)
+      f4_t m0[RT], tw[4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m0[rt][i] = M0[(rt * 16 + 4 * g4 + i) * DV + col];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) tw[rt] = zero4();
+#pragma unroll
+      for (int k2 = 0; k2 < KB; ++k2) {
+        const Frag<OP> fm = acc_frag<OP>(m0[2 * k2], m0[2 * k2 + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mma(tw[rt], lds_frag<OP>(sW, LDK, rt * 16, k2 * 32), fm);
+      }
+      // the chunk-end gate term sum(dM . M0) over this column
+      float pm = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm += m0[rt][i] * dMC[(rt * 16 + 4 * g4 + i) * DV + col];
+      dgC_part += pm;
+      // dB_u = T^T dU
+      f4_t dB[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * g4 + i;
+          dB[rt][i] = r < n ? dUg[r * rowld + col] : 0.f;
+        }
+      block_solve_t<LC, LLI>(dB, sAnT, sLiT);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * g4 + i;
+          const float u = Y[rt][i] - tw[rt][i];
+          sUb[r * LKW + wave * 16 + m16] = (OP)u;
+          sU0b[r * LKW + wave * 16 + m16] = (OP)Y[rt][i];
+          sBub[r * LKW + wave * 16 + m16] = (OP)dB[rt][i];
+          // dV' = b dB_u (unscaled), and b's share dB_u . V'
+          if (r < n) a.dvc[(tokbase + (int64_t)r * H) * DV + col] = sBeta[r] * dB[rt][i] * inv;
+          const float db = sum16(dB[rt][i] * Vp[rt][i]);
+          if (m16 == 0) atomicAdd(&sDb[r], db);
+        }
+    }
+    __syncthreads();
+    // C x C jobs: 0..9 dP tiles, 10..19 dB_u U0^T tiles
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const int job = wave + jj * NWAVE;
+      if (job < 20) {
+        const int which = job >= 10, t = job - 10 * which;
+        const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+        if (which == 0)
+          mma(accCC[jj], glb_frag<OP>(dO, rowld, ti * 16, kb * KW, s, n), lds_frag<OP>(sUb, LKW, tj * 16, 0));
+        else
+          mma(accCC[jj], lds_frag<OP>(sBub, LKW, ti * 16, 0), lds_frag<OP>(sU0b, LKW, tj * 16, 0));
+      }
+    }
+    if (wave < RT) {
+      const Frag<OP> fm0 = glb_frag<OP>(M0, DV, wave * 16, kb * KW, 1.f, DK);
+      const Frag<OP> fdm = glb_frag<OP>(dMC, DV, wave * 16, kb * KW, 1.f, DK);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        mma(aQO[rt], glb_frag<OP>(dO, rowld, rt * 16, kb * KW, s, n), fm0);
+        mma(aKM[rt], lds_frag<OP>(sUb, LKW, rt * 16, 0), fdm);
+        mma(aW[rt], glb_frag<OP>(dUg, rowld, rt * 16, kb * KW, 1.f, n), fm0);
+      }
+    }
+    __syncthreads();
+  }
+  if (wave < 2) {
+    const float t = wave_sum(dgC_part);
+    if (lane == 0) atomicAdd(&sMisc[0], t);
+  }
+
+  // ---- dP: the P and gate terms, dP . E to LDS; zero the upper tiles of dP.E and dS
+  for (int e = tid; e < C * C; e += NTHR) {
+    const int r = e / C, cc = e % C;
+    if ((r >> 4) < (cc >> 4)) { sdPE[r * LC + cc] = (OP)0.f; sdS[r * LC + cc] = (OP)0.f; }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    const int job = wave + jj * NWAVE;
+    if (job < 10) {
+      const int ti = (kLowI >> (2 * job)) & 3, tj = (kLowJ >> (2 * job)) & 3;
+      f4_t qk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma(qk, lds_frag<OP>(sQh, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+        const bool on = cc <= r;
+        const float E = fast_exp2(sG[r] - sG[cc]);
+        const float dp = on ? accCC[jj][i] : 0.f;
+        const float x = dp * E * qk[i];  // dP_ij P_ij
+        sdPE[r * LC + cc] = (OP)(dp * E);
+        const float rs = sum16(x);
+        if (m16 == 0) atomicAdd(&sDg[r], rs);
+        csum += x;
+      }
+      csum = sum_groups(csum);
+      if (g4 == 0) atomicAdd(&sDg[tj * 16 + m16], -csum);
+    }
+  }
+  // ---- dk column owners: dB_w = T^T dW, the W-gate, O-gate and D terms
+  f4_t dBw[4];
+  if (wave < RT) {
+    const int col = wave * 16 + m16;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dBw[rt][i] = -aW[rt][i];
+    block_solve_t<LC, LLI>(dBw, sAnT, sLiT);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + 4 * g4 + i;
+        sdBw[r * LDK + col] = (OP)dBw[rt][i];
+        const float kh = (float)sKh[r * LDK + col], qh = (float)sQh[r * LDK + col];
+        const float xw = sum16(dBw[rt][i] * kh);    // dB_w,i . k_i (this tile's share)
+        const float xo = sum16(aQO[rt][i] * qh);    // q_i . (dO M0^T)_i
+        const float xd = sum16(aKM[rt][i] * kh);    // k_i . (U dM^T)_i
+        if (m16 == 0) {
+          atomicAdd(&sDb[r], sGam[r] * xw);
+          atomicAdd(&sDg[r], sBeta[r] * sGam[r] * xw + sGam[r] * xo);
+          atomicAdd(&sDD[r], xd);
+        }
+      }
+  }
+  __syncthreads();
+  // ---- dA = strictLower(-(dB_w W^T + dB_u U0^T)): dS, the A gate and beta terms
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    const int job = wave + jj * NWAVE;
+    if (job >= 10 && job < 20) {
+      const int t = job - 10;
+      const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+      f4_t bw = zero4(), kk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        mma(bw, lds_frag<OP>(sdBw, LDK, ti * 16, kb * 32), lds_frag<OP>(sW, LDK, tj * 16, kb * 32));
+        mma(kk, lds_frag<OP>(sKh, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
+      }
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+        const bool on = cc < r;
+        const float E = fast_exp2(sG[r] - sG[cc]);
+        const float dA = on ? -(bw[i] + accCC[jj][i]) : 0.f;
+        sdS[r * LC + cc] = (OP)(dA * sBeta[r] * E);
+        const float xb = sum16(dA * E * kk[i]);              // sum_j dA_ij E_ij S_ij
+        const float xa = dA * sBeta[r] * E * kk[i];          // dA_ij A_ij
+        const float rs = sum16(xa);
+        if (m16 == 0) {
+          atomicAdd(&sDb[r], xb);
+          atomicAdd(&sDg[r], rs);
+        }
+        csum += xa;
+      }
+      csum = sum_groups(csum);
+      if (g4 == 0) atomicAdd(&sDg[tj * 16 + m16], -csum);
+    }
+  }
+  __syncthreads();
+  // ---- dq^, dk^ column tiles, and the row dots for the normalisation
+  f4_t dQh[4], dKh[4];
+  if (wave < RT) {
+    const int col = wave * 16 + m16;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      dQh[rt] = zero4();
+      dKh[rt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<OP> fk = lds_fragT<OP>(sKh, LDK, wave * 16, kb * 32);
+        mma(dQh[rt], lds_frag<OP>(sdPE, LC, rt * 16, kb * 32), fk);
+        mma(dKh[rt], lds_fragT<OP>(sdPE, LC, rt * 16, kb * 32), lds_fragT<OP>(sQh, LDK, wave * 16, kb * 32));
+        mma(dKh[rt], lds_frag<OP>(sdS, LC, rt * 16, kb * 32), fk);
+        mma(dKh[rt], lds_fragT<OP>(sdS, LC, rt * 16, kb * 32), fk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + 4 * g4 + i;
+        dQh[rt][i] += sGam[r] * aQO[rt][i];
+        dKh[rt][i] += sDec[r] * aKM[rt][i] + sBeta[r] * sGam[r] * dBw[rt][i];
+        const bool ok = r < n;
+        const float qv = ok ? bf16_to_f32(a.q[(tokbase + (int64_t)r * H) * DK + col]) : 0.f;
+        const float kv = ok ? bf16_to_f32(a.k[(tokbase + (int64_t)r * H) * DK + col]) : 0.f;
+        const float xq = sum16(qv * dQh[rt][i]), xk = sum16(kv * dKh[rt][i]);
+        if (m16 == 0) {
+          atomicAdd(&sQd[r], xq);
+          atomicAdd(&sKd[r], xk);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < RT) {
+    const int col = wave * 16 + m16;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + 4 * g4 + i;
+        if (r < n) {
+          const int64_t o = (tokbase + (int64_t)r * H) * DK + col;
+          const float qv = bf16_to_f32(a.q[o]), kv = bf16_to_f32(a.k[o]);
+          const float nq = sNq[r], nk = sNk[r];
+          a.dq[o] = (dQh[rt][i] / nq - qv * sQd[r] / (nq * nq * nq)) * inv;
+          a.dk[o] = (dKh[rt][i] / nk - kv * sKd[r] / (nk * nk * nk)) * inv;
+        }
+      }
+  }
+  // ---- the gates: D and gamma_C terms, reverse cumulative sum, d alpha and d beta
+  if (wave == GATE_WAVE) {
+    const float D = sDec[lane], dd = sDD[lane];
+    float dg = sDg[lane] - D * dd;
+    const float tot = wave_sum(D * dd) + sGam[C - 1] * sMisc[0];
+    if (lane == C - 1) dg += tot;
+    // reverse inclusive cumulative sum over the chunk
+    float r = dg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(r, o, WAVE);
+      if (lane + o < 64) r += y;
+    }
+    if (lane < n) {
+      const int64_t gi = tokbase + (int64_t)lane * H;
+      a.dalpha[gi] = r / a.alpha[gi] * inv;
+      a.dbeta[gi] = sDb[lane] * inv;
+    }
+  }
+}
+
+// ------------------------------------------------------------ conv backward
+
+// grid (ceil((T + 3) / 4), H, B), 4 waves: wave w handles token t = 4 x + w - 3
+// (t < 0: a conv-cache row).  dv_raw[t] = sum_j taps_{t+3-j}[j] dV'_{t+3-j}
+// over the tokens that read row t, plus the gradient of conv_out; dtaps_t[j]
+// = dV'_t . raw_{t-3+j} for t >= 0.
+template <int DV>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_t* v, const bf16_t* conv_in,
+                                                       const float* taps, const float* dvc, const float* dconv_out,
+                                                       float* dv, float* dconv_in, float* dtaps) {
+  constexpr int CPL = DV / 64;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6) - 3, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  float acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = t + 3 - j;  // the token whose tap j read row t
+    if (u >= 0 && u < T) {
+      const int64_t bu = ((int64_t)b * T + u) * H + h;
+      const float tp = taps[bu * 4 + j];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] += tp * dvc[bu * DV + lane * CPL + i];
+    }
+  }
+  if (dconv_out && t >= T - 3) {
+    const int sl = t - (T - 3);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] += dconv_out[(((int64_t)b * 3 + sl) * H + h) * DV + lane * CPL + i];
+  }
+  float* dst = t >= 0 ? dv + (((int64_t)b * T + t) * H + h) * DV : dconv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) dst[lane * CPL + i] = acc[i];
+  if (t >= 0) {
+    const int64_t bt = ((int64_t)b * T + t) * H + h;
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = t - 3 + j;
+      const bf16_t* row = r >= 0 ? v + (((int64_t)b * T + r) * H + h) * DV
+                                 : (conv_in ? conv_in + (((int64_t)b * 3 + 3 + r) * H + h) * DV : nullptr);
+      if (row)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) d[j] += dvc[bt * DV + lane * CPL + i] * bf16_to_f32(row[lane * CPL + i]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sj = wave_sum(d[j]);
+      if (lane == 0) dtaps[bt * 4 + j] = sj;
+    }
+  }
+}
+
+// ------------------------------------------------------------ generator backward
+
+// Per token (one wave each, 4 per workgroup): pre = W1 x + b1, hid = SiLU(pre),
+// dhid = W2^T dtaps, dp = dhid SiLU'(pre); writes dp and hid [n][32] and
+// dx = W1^T dp.
+__global__ __launch_bounds__(256) void gen_bwd_token_kernel(int64_t n_tok, int D, int H, const bf16_t* x,
+                                                            const bf16_t* W1, const bf16_t* b1, const bf16_t* W2,
+                                                            const float* dtaps, float* dp_out, float* hid_out,
+                                                            float* dx) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= n_tok) return;
+  const bf16_t* xr = x + t * D;
+  float pre[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) pre[u] = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    const float xv = bf16_to_f32(xr[d]);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) pre[u] += bf16_to_f32(W1[(int64_t)u * D + d]) * xv;
+  }
+  float dp = 0.f, hv = 0.f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const float p = wave_sum(pre[u]) + (b1 ? bf16_to_f32(b1[u]) : 0.f);
+    if (lane == u) {
+      const float sg = 1.f / (1.f + expf(-p));
+      hv = p * sg;
+      float dh = 0.f;
+      for (int r = 0; r < 4 * H; ++r) dh += bf16_to_f32(W2[(int64_t)r * 32 + u]) * dtaps[t * 4 * H + r];
+      dp = dh * sg * (1.f + p * (1.f - sg));
+    }
+  }
+  if (lane < 32) {
+    dp_out[t * 32 + lane] = dp;
+    hid_out[t * 32 + lane] = hv;
+  }
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc += bf16_to_f32(W1[(int64_t)u * D + d]) * __shfl(dp, u, WAVE);
+    dx[t * D + d] = acc;
+  }
+}
+
+// Partial weight gradients over a token range: grid (ceil(D / 256), NSPLIT);
+// thread d accumulates dW1[u][d] = sum_t dp[t][u] x[t][d] for its split; the
+// first column block also forms the split's dW2 = dtaps^T hid, db1, db2.
+__global__ __launch_bounds__(256) void gen_bwd_weight_kernel(int64_t n_tok, int D, int H, const bf16_t* x,
+                                                             const float* dp, const float* hid, const float* dtaps,
+                                                             float* part_w1, float* part_small) {
+  const int d = blockIdx.x * 256 + threadIdx.x, sp = blockIdx.y, nsp = gridDim.y;
+  const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
+  if (d < D) {
+    float acc[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc[u] = 0.f;
+    for (int64_t t = t0; t < t1; ++t) {
+      const float xv = bf16_to_f32(x[t * D + d]);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) acc[u] += dp[t * 32 + u] * xv;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) part_w1[((int64_t)sp * 32 + u) * D + d] = acc[u];
+  }
+  if (blockIdx.x == 0) {
+    // small parts: dW2 [4H][32], db2 [4H], db1 [32]
+    const int HK = 4 * H, nsmall = HK * 32 + HK + 32;
+    float* ps = part_small + (int64_t)sp * nsmall;
+    for (int e = threadIdx.x; e < nsmall; e += 256) {
+      float acc = 0.f;
+      if (e < HK * 32) {
+        const int r = e / 32, u = e % 32;
+        for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r] * hid[t * 32 + u];
+      } else if (e < HK * 32 + HK) {
+        const int r = e - HK * 32;
+        for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r];
+      } else {
+        const int u = e - HK * 32 - HK;
+        for (int64_t t = t0; t < t1; ++t) acc += dp[t * 32 + u];
+      }
+      ps[e] = acc;
+    }
+  }
+}
+
+// Sum of the NSPLIT partials in a fixed order: out[e] = sum_s part[s][e].
+__global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < nsp; ++s) acc += part[(int64_t)s * n + e];
+  out[e] = acc;
+}
+
+// ------------------------------------------------------------ host side
+
+// the (dk, dv) pairs built (backward_supported, in jb_prefill.hip, lists the same)
+#define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr int GEN_NSPLIT = 64;
+
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
+  const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
+  const size_t n = (size_t)B * T;
+  const size_t nch = (size_t)p.nchunks;
+  size_t bytes = al256(prefill_workspace_bytes(p));           // taps, segment buffers (the forward pass)
+  bytes += 2 * al256((size_t)B * H * nch * dk * dv * 4);       // Mck, dMck
+  bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
+  bytes += al256(n * H * 4 * 4);                               // dtaps
+  bytes += 2 * al256(n * 32 * 4);                              // dp, hid
+  bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
+  bytes += al256((size_t)GEN_NSPLIT * (4 * H * 32 + 4 * H + 32) * 4);
+  bytes += al256(16);                                          // scale
+  return bytes;
+}
+
+hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const void* x, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
+                           const void* W2, const void* b2, const float* S0, const void* conv_in, const float* dout,
+                           const float* dS_final, const float* dconv_out, float* dx, float* dq, float* dk_,
+                           float* dv_, float* dalpha, float* dbeta, float* dW1, float* db1, float* dW2, float* db2,
+                           float* dS0, float* dconv_in, void* workspace, hipStream_t stream) {
+  const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
+  const int64_t n = (int64_t)B * T;
+  const int nch = p.nchunks;
+  char* ws = static_cast<char*>(workspace);
+  char* fws = ws;                                   // taps first, then the segment buffers
+  float* taps = reinterpret_cast<float*>(ws);
+  ws += al256(prefill_workspace_bytes(p));
+  float* Mck = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)B * H * nch * dk * dv * 4);
+  float* dMck = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)B * H * nch * dk * dv * 4);
+  float* dU = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * H * dv * 4);
+  float* dvc = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * H * dv * 4);
+  float* dtaps = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * H * 4 * 4);
+  float* dp = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * 32 * 4);
+  float* hid = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * 32 * 4);
+  float* pw1 = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)GEN_NSPLIT * 32 * D * 4);
+  float* psm = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)GEN_NSPLIT * (4 * H * 32 + 4 * H + 32) * 4);
+  float* scale = reinterpret_cast<float*>(ws);
+
+  hipError_t e = hipSuccess;
+  grad_scale_kernel<<<1, 1024, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // forward: taps and the state entering every chunk
+  e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream);
+  if (e == hipSuccess) e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, fws, stream);
+  if (e != hipSuccess) return e;
+  BwdArgs a{};
+  a.T = T; a.H = H; a.nchunks = nch;
+  a.q = (const bf16_t*)q; a.k = (const bf16_t*)k; a.v = (const bf16_t*)v; a.conv_in = (const bf16_t*)conv_in;
+  a.alpha = alpha; a.beta = beta; a.taps = taps; a.dout = dout; a.dS_final = dS_final; a.scale = scale;
+  a.Mck = Mck; a.dMck = dMck; a.dU = dU; a.dS0 = dS0; a.dq = dq; a.dk = dk_; a.dalpha = dalpha; a.dbeta = dbeta;
+  a.dvc = dvc;
+  bool launched = false;
+#define CASE(DK_, DV_)                                                                              \
+  if (dk == DK_ && dv == DV_) {                                                                     \
+    bwd_chain_kernel<DK_, DV_><<<dim3(H, B), NTHR, 0, stream>>>(a);                                 \
+    bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
+    conv_bwd_kernel<DV_><<<dim3((T + 3 + 3) / 4, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v,   \
+        (const bf16_t*)conv_in, taps, dvc, dconv_out, dv_, dconv_in, dtaps);                        \
+    launched = true;                                                                                \
+  }
+  JB_BACKWARD_KERNEL_CASES(CASE)
+#undef CASE
+  if (!launched) return hipErrorInvalidValue;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the generator
+  gen_bwd_token_kernel<<<dim3((unsigned)((n + 3) / 4)), 256, 0, stream>>>(n, D, H, (const bf16_t*)x,
+                                                                        (const bf16_t*)W1, (const bf16_t*)b1,
+                                                                        (const bf16_t*)W2, dtaps, dp, hid, dx);
+  gen_bwd_weight_kernel<<<dim3((D + 255) / 256, GEN_NSPLIT), 256, 0, stream>>>(n, D, H, (const bf16_t*)x, dp, hid,
+                                                                              dtaps, pw1, psm);
+  const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
+  sum_parts_kernel<<<dim3((unsigned)((nw1 + 255) / 256)), 256, 0, stream>>>(nw1, GEN_NSPLIT, pw1, dW1);
+  // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout)
+  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256)), 256, 0, stream>>>(nsm, GEN_NSPLIT, psm, psm);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = hipMemcpyAsync(dW2, psm, (size_t)4 * H * 32 * 4, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(db2, psm + 4 * H * 32, (size_t)4 * H * 4, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(db1, psm + 4 * H * 32 + 4 * H, (size_t)32 * 4, hipMemcpyDeviceToDevice, stream);
+  return e;
+}
+
+}  // namespace jb

@@ -62,6 +62,23 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
                                  const float* wv, const void* cq_in, const void* ck_in, const void* cv_in,
                                  const float* S0, void* o, float* S_final, void* workspace, hipStream_t stream);
 
+// The forward pass storing the state entering every chunk, Mck
+// [B][H][nchunks][dk][dv] (bf16 inputs; workspace as launch_prefill's).
+hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* taps, const void* conv_in, const float* S0,
+                               float* Mck, void* workspace, hipStream_t stream);
+
+// The gradient of jb_prefill (bf16 inputs, fp32 gradients; one segment per
+// sequence).  Shapes built: (dk, dv) in {(32,64), (64,128), (96,256), (128,256)}.
+bool backward_supported(int io, int dk, int dv);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D);
+hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const void* x, const void* q, const void* k,
+                           const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
+                           const void* W2, const void* b2, const float* S0, const void* conv_in, const float* dout,
+                           const float* dS_final, const float* dconv_out, float* dx, float* dq, float* dk_,
+                           float* dv_, float* dalpha, float* dbeta, float* dW1, float* db1, float* dW2, float* db2,
+                           float* dS0, float* dconv_in, void* workspace, hipStream_t stream);
+
 // One decode step's state update (taps precomputed).
 bool decode_supported(int dk, int dv);
 hipError_t launch_decode(int io, int out, int B, int H, int dk, int dv, const float* S_in,

@@ -25,7 +25,7 @@
 // the normal range), fp32 operands in the all-fp32 mode.  The state and every
 // accumulator stay fp32; scalars (norms, gates) are applied in fp32.
 //
-// Workgroup: 16 wavefronts.  Chunk-shared tiles (K, K^T, Q, -A, the diagonal
+// Workgroup: 8 wavefronts.  Chunk-shared tiles (K, K^T, Q, -A, the diagonal
 // blocks of A and their inverses, -W, P, the value rows with their 3-row conv
 // halo) live in LDS; each wave owns whole 16-column tiles of the state and
 // keeps them in accumulator registers for the whole segment, so the state
@@ -34,19 +34,15 @@
 // wave applies a blocked forward substitution on the matrix cores to its own
 // right-hand sides (its columns of diag(b) V', and one column tile of
 // diag(b gamma) K for the W tiles).
+#include "jb_chunk.h"
 #include "jb_device.h"
 #include "jb_internal.h"
 
 namespace jb {
 
-constexpr int C = 64;        // chunk length
-constexpr int NWAVE = 8;     // wavefronts per chunk workgroup
-constexpr int NTHR = NWAVE * WAVE;
-constexpr int PRO_THR = 512; // threads of the prologue mapping: 64 rows x 8 parts
-constexpr int GATE_WAVE = 7; // the wave that loads and scans the gates
-constexpr int NCU = 256;     // compute units of one MI355X
-
-enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1 };
+// MODE_CKPT runs the output pass's state recurrence without q, P and o and
+// stores the state entering every chunk (the backward pass starts from them)
+enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1, MODE_CKPT = 2 };
 
 struct ChunkArgs {
   int T, H, nchunks, seg_len, nseg;
@@ -73,6 +69,7 @@ struct ChunkArgs {
   float* Phi;           // [B][H][nseg][DK][DK]
   void* o;
   float* S_final;
+  float* Mck;           // MODE_CKPT: [B][H][nchunks][DK][DV], the state entering every chunk
 };
 
 // ------------------------------------------------------------ LDS layout
@@ -138,140 +135,6 @@ struct Lds {
   static constexpr int oKraw = oAn;
   static_assert(oLi + szLi - oAn >= szRaw, "raw k staging does not fit");
 };
-
-// the lower-triangular tiles (i, j), j <= i, of a chunk's 4 x 4 tile grid in
-// row order, two bits per coordinate: tile t is ((kLowI >> 2t) & 3, (kLowJ >> 2t) & 3)
-constexpr uint32_t kLowI = 0xffa94u;  // rows    0 1 1 2 2 2 3 3 3 3
-constexpr uint32_t kLowJ = 0xe4910u;  // columns 0 0 1 0 1 2 0 1 2 3
-
-template <typename IO>
-__device__ __forceinline__ void load_row_part(const IO* src, float* dst, int n, bool valid);
-
-template <>
-__device__ __forceinline__ void load_row_part<bf16_t>(const bf16_t* src, float* dst, int n, bool valid) {
-  // n is a multiple of 4: 8-byte loads
-  for (int e = 0; e < n; e += 4) {
-    uint2 u = valid ? *reinterpret_cast<const uint2*>(src + e) : make_uint2(0u, 0u);
-    dst[e + 0] = __uint_as_float(u.x << 16);
-    dst[e + 1] = __uint_as_float(u.x & 0xffff0000u);
-    dst[e + 2] = __uint_as_float(u.y << 16);
-    dst[e + 3] = __uint_as_float(u.y & 0xffff0000u);
-  }
-}
-
-template <>
-__device__ __forceinline__ void load_row_part<float>(const float* src, float* dst, int n, bool valid) {
-  for (int e = 0; e < n; e += 4) {
-    float4 u = valid ? *reinterpret_cast<const float4*>(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    dst[e + 0] = u.x;
-    dst[e + 1] = u.y;
-    dst[e + 2] = u.z;
-    dst[e + 3] = u.w;
-  }
-}
-
-// The normalisation part of the prologue for one chunk, as the first 512
-// threads of a workgroup execute it: thread (row = tid/8, part = tid%8)
-// handles DK/8 elements of q and k for token t0 + row.  Rows at or beyond
-// `n` (ragged tail) are neutral tokens: q = k = 0 (and a = 1, b = 0).
-// load() only issues the global loads; finish() reduces and scales.
-template <int DK, typename IO>
-struct Prologue {
-  static constexpr int E = DK / 8;
-  float kv[E], qv[E];
-  int row, part;
-
-  __device__ __forceinline__ void load(const IO* q, const IO* k, int64_t row_base, int H, int n, bool want_q) {
-    row = threadIdx.x >> 3;
-    part = threadIdx.x & 7;
-    const bool valid = row < n;
-    const int64_t off = (row_base + (int64_t)row * H) * DK + part * E;
-    load_row_part<IO>(k + off, kv, E, valid);
-    if (want_q) load_row_part<IO>(q + off, qv, E, valid);
-  }
-  __device__ __forceinline__ void finish(bool want_q) {
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) sk += kv[e] * kv[e];
-    const float rk = l2_scale(group_sum<8>(sk));
-#pragma unroll
-    for (int e = 0; e < E; ++e) kv[e] *= rk;
-    if (want_q) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) sq += qv[e] * qv[e];
-      const float rq = l2_scale(group_sum<8>(sq));
-#pragma unroll
-      for (int e = 0; e < E; ++e) qv[e] *= rq;
-    }
-  }
-};
-
-// Static-conv prologue: four channels d0 .. d0+3 of row `row` of the
-// convolved q or k, from raw staged rows [C+3][DK] where row r + j holds
-// token t0 + r - 3 + j, and tap-major weights w [4][DK]:
-// x[i] = sum_j w[j][d0 + i] raw[row + j][d0 + i].
-template <int DK, typename IO>
-__device__ __forceinline__ void conv4(const IO* raw, const float* w, int row, int d0, bool valid, float (&x)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float4 wj = *reinterpret_cast<const float4*>(w + j * DK + d0);
-    float r[4];
-    load_row_part<IO>(raw + (row + j) * DK + d0, r, 4, valid);
-    x[0] += wj.x * r[0];
-    x[1] += wj.y * r[1];
-    x[2] += wj.z * r[2];
-    x[3] += wj.w * r[3];
-  }
-}
-
-// g2 = inclusive cumsum of log2(alpha) over the chunk, lane = row (one wave).
-// The chunk kernels keep the gates in base 2: e^{g_i - g_j} = 2^{g2_i - g2_j}.
-__device__ __forceinline__ float chunk_gate_scan(float alpha_or_one) {
-  return wave_inclusive_scan(fast_log2(alpha_or_one));
-}
-
-// Y = (I + A)^{-1} R for a 64 x 16 right-hand side in accumulator layout
-// (Y[b] holds rows 16b..16b+15 of R on entry and of the solution on exit).
-// Blocked forward substitution: Y_b = Linv_b (R_b - sum_{k<b} A_bk Y_k), on
-// the matrix cores; sAn holds -A (row stride LC) and sLi the four diagonal
-// block inverses (row stride LLI, columns 16..31 zero).
-template <typename OP, int LC, int LLI>
-__device__ __forceinline__ void block_solve(f4_t (&Y)[4], const OP* sAn, const OP* sLi) {
-  const f4_t z = zero4();
-  f4_t t = zero4();
-  mma(t, lds_frag<OP>(sLi, LLI, 0, 0), acc_frag<OP>(Y[0], z));
-  Y[0] = t;
-  mma(Y[1], lds_frag<OP>(sAn, LC, 16, 0), acc_frag<OP>(Y[0], z));
-  t = zero4();
-  mma(t, lds_frag<OP>(sLi, LLI, 16, 0), acc_frag<OP>(Y[1], z));
-  Y[1] = t;
-  const Frag<OP> f01 = acc_frag<OP>(Y[0], Y[1]);
-  mma(Y[2], lds_frag<OP>(sAn, LC, 32, 0), f01);
-  mma(Y[3], lds_frag<OP>(sAn, LC, 48, 0), f01);
-  t = zero4();
-  mma(t, lds_frag<OP>(sLi, LLI, 32, 0), acc_frag<OP>(Y[2], z));
-  Y[2] = t;
-  mma(Y[3], lds_frag<OP>(sAn, LC, 48, 32), acc_frag<OP>(Y[2], z));
-  t = zero4();
-  mma(t, lds_frag<OP>(sLi, LLI, 48, 0), acc_frag<OP>(Y[3], z));
-  Y[3] = t;
-}
-
-// ------------------------------------------------------------ LDS DMA
-
-// Direct global -> LDS loads (gfx950): one wave instruction moves a 16-byte
-// (or 4-byte) piece per active lane into consecutive LDS slots starting at the
-// wave-uniform address `lds`; lanes that skip the call write nothing.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
-}
 
 // ------------------------------------------------------------ chunk kernel
 
@@ -474,6 +337,19 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
+    if constexpr (MODE == MODE_CKPT) {
+      // the state entering chunk c, for the backward pass
+      float* dst = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw) {
+        const int ct = wave + cw * NWAVE;
+        if (ct < NCT)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+      }
+    }
 
     // ================= prefetched inputs -> prologue =================
     __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA transfers have landed
@@ -872,6 +748,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         const int row = rt * 16 + 4 * g4 + i;
         if (MODE == MODE_OUTPUT) {
           if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+        } else if (MODE == MODE_CKPT) {
         } else if (ct < VCT) {
           a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else {
@@ -1109,6 +986,43 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16, true>(p, a, stream);
   if (p.io == IO_BF16) { JB_PREFILL_STATIC_CASES(CASE) }
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int DV>
+static hipError_t run_ckpt(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
+  const dim3 blk(NTHR);
+  if (p.nseg > 1) {
+    chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_SUMMARY, false><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
+    scan_kernel<DK, DV, _Float16><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+        p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
+  }
+  chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_CKPT, false><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+#define JB_BACKWARD_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
+
+bool backward_supported(int io, int dk, int dv) {
+#define CASE(DK_, DV_) if (dk == DK_ && dv == DV_) return true;
+  if (io == IO_BF16) { JB_BACKWARD_CASES(CASE) }
+#undef CASE
+  return false;
+}
+
+hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* taps, const void* conv_in, const float* S0,
+                               float* Mck, void* workspace, hipStream_t stream) {
+  if (p.nchunks == 0) return hipSuccess;
+  ChunkArgs a{};
+  a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
+  a.S0 = S0; a.Mck = Mck;
+  set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
+#define CASE(DK_, DV_) \
+  if (p.dk == DK_ && p.dv == DV_) return run_ckpt<DK_, DV_>(p, a, stream);
+  if (p.io == IO_BF16) { JB_BACKWARD_CASES(CASE) }
 #undef CASE
   return hipErrorInvalidValue;
 }

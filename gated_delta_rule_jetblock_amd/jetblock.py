@@ -74,12 +74,14 @@ _lib.jb_prefill_static.argtypes = [_S] + [_P] * 17 + [_P, _SZ, _P]
 _lib.jb_decode_step_static.argtypes = [_S] + [_P] * 17 + [_P]
 _lib.jb_prefill_varlen_workspace_size.argtypes = [_S, ctypes.c_int64, ctypes.POINTER(_SZ)]
 _lib.jb_prefill_varlen.argtypes = [_S, ctypes.c_int64] + [_P] * 16 + [_P, _SZ, _P]
+_lib.jb_backward_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
+_lib.jb_backward.argtypes = [_S] + [_P] * 27 + [_P, _SZ, _P]
 for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
            "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x",
            "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x", "jb_prefill_static_workspace_size",
            "jb_prefill_static", "jb_decode_step_static", "jb_prefill_varlen_workspace_size",
-           "jb_prefill_varlen"):
+           "jb_prefill_varlen", "jb_backward_workspace_size", "jb_backward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -449,3 +451,33 @@ def prefill_varlen(cu_seqlens, x, q, k, v, alpha, beta, W1, W2, b1=None, b2=None
                                   _ptr(conv_in), _ptr(o), _ptr(S_final), _ptr(conv_out), _ptr(ws), ws.numel(),
                                   _stream(stream)))
     return dict(o=o, S_final=S_final, conv_out=conv_out)
+
+
+def backward_workspace_size(shape: Shape) -> int:
+    n = _SZ(0)
+    _check(_lib.jb_backward_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def backward(x, q, k, v, alpha, beta, W1, W2, dout, b1=None, b2=None, S0=None, conv_in=None, dS_final=None,
+             dconv_out=None, *, ws=None, stream=None):
+    """jb_backward: gradients of jb_prefill.  Returns a dict of float32 tensors dx, dq, dk, dv,
+    dalpha, dbeta, dW1, db1, dW2, db2, dS0, dconv_in."""
+    B, T, D = x.shape
+    H, dk = q.shape[2], q.shape[3]
+    dv = v.shape[3]
+    shape = make_shape(B, T, H, dk, dv, D, _io_code(x), JB_F32)
+    dev = x.device
+    f = lambda *sz: torch.empty(sz, dtype=torch.float32, device=dev)
+    out = dict(dx=f(B, T, D), dq=f(B, T, H, dk), dk=f(B, T, H, dk), dv=f(B, T, H, dv), dalpha=f(B, T, H),
+               dbeta=f(B, T, H), dW1=f(32, D), db1=f(32), dW2=f(4 * H, 32), db2=f(4 * H), dS0=f(B, H, dk, dv),
+               dconv_in=f(B, 3, H, dv))
+    if ws is None:
+        ws = workspace(backward_workspace_size(shape), dev)
+    _check(_lib.jb_backward(ctypes.byref(shape), _ptr(x), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                            _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(S0), _ptr(conv_in), _ptr(dout),
+                            _ptr(dS_final), _ptr(dconv_out),
+                            *[_ptr(out[n]) for n in ("dx", "dq", "dk", "dv", "dalpha", "dbeta", "dW1", "db1", "dW2",
+                                                     "db2", "dS0", "dconv_in")],
+                            _ptr(ws), ws.numel(), _stream(stream)))
+    return out

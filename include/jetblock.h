@@ -309,6 +309,40 @@ jb_status jb_decode_step_static(const jb_shape* shape, const float* S_in, float*
                                 void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The gradient of jb_prefill, for training the block (the pages train
+ * JetBlock inside the model: csdn translation, sections 2.2 and 3.1).
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes of jb_backward for `shape`. */
+jb_status jb_backward_workspace_size(const jb_shape* shape, size_t* bytes);
+
+/*
+ * jb_backward -- reverse-mode gradient of jb_prefill over B sequences of T
+ * tokens.  Inputs as in jb_prefill (bf16 I/O only, shape.flags == 0); dout
+ * [B][T][H][dv] is the gradient of o, dS_final [B][H][dk][dv] and dconv_out
+ * [B][K-1][H][dv] those of S_final and conv_out (both nullable: zero), all
+ * float32.  Outputs, all float32 and required:
+ *   dx [B][T][d_model]; dq, dk [B][T][H][dk]; dv [B][T][H][dv];
+ *   dalpha, dbeta [B][T][H]; dW1 [32][d_model], db1 [32]; dW2 [4H][32],
+ *   db2 [4H]; dS0 [B][H][dk][dv]; dconv_in [B][K-1][H][dv]
+ * (dS0 and dconv_in are returned also when S0 / conv_in are NULL: the
+ * gradient with respect to the zeros used in their place).  The pass
+ * recomputes the forward states chunk by chunk; the gradients of o and
+ * S_final are scaled internally by a power of two so that the fp16
+ * matrix-core operands cannot overflow.  Built for (dk, dv) in {(32, 64),
+ * (64, 128), (96, 256), (128, 256)}.  workspace: jb_backward_workspace_size()
+ * bytes, 256-byte aligned.
+ */
+jb_status jb_backward(const jb_shape* shape, const void* x, const void* q, const void* k,
+                      const void* v, const float* alpha, const float* beta, const void* W1,
+                      const void* b1, const void* W2, const void* b2, const float* S0,
+                      const void* conv_in, const float* dout, const float* dS_final,
+                      const float* dconv_out, float* dx, float* dq, float* dk, float* dv,
+                      float* dalpha, float* dbeta, float* dW1, float* db1, float* dW2, float* db2,
+                      float* dS0, float* dconv_in, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single-stage entry points.  Each runs one stage of the path by itself so
  * that it can be checked on its own; the two calls above fuse these stages.
  * ------------------------------------------------------------------------- */

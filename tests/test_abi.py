@@ -196,3 +196,24 @@ def test_varlen_entries_reject_before_launch(jb):
     a = list(args); a[2] = None  # q
     assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *a, fake, 1 << 30, None) == 1
     assert lib.jb_prefill_varlen(ctypes.byref(s), 2500, *args, fake, 16, None) == 3  # workspace too small
+
+
+def test_backward_entries_reject_before_launch(jb):
+    lib = jb.library()
+    n = ctypes.c_size_t(0)
+    s = jb.make_shape(2, 200, 2, 32, 64, 128)
+    assert lib.jb_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0 and n.value > 2 * 200 * 2 * 64 * 8
+    s_bad = jb.make_shape(2, 200, 2, 32, 128, 128)   # (32, 128) not built for the backward pass
+    assert lib.jb_backward_workspace_size(ctypes.byref(s_bad), ctypes.byref(n)) == 2
+    s32 = jb.make_shape(2, 200, 2, 32, 64, 128, io_dtype=jb.JB_F32)
+    assert lib.jb_backward_workspace_size(ctypes.byref(s32), ctypes.byref(n)) == 2
+    sflag = jb.make_shape(2, 200, 2, 32, 64, 128, flags=jb.flag_segment(2))
+    assert lib.jb_backward_workspace_size(ctypes.byref(sflag), ctypes.byref(n)) == 1
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 27
+    a = list(args); a[12] = None  # dout
+    assert lib.jb_backward(ctypes.byref(s), *a, fake, 1 << 34, None) == 1
+    assert "dout is NULL" in jb.last_error()
+    a = list(args); a[25] = None  # dS0
+    assert lib.jb_backward(ctypes.byref(s), *a, fake, 1 << 34, None) == 1
+    assert lib.jb_backward(ctypes.byref(s), *args, fake, 16, None) == 3   # workspace too small
