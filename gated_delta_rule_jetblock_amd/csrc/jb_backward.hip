@@ -51,26 +51,35 @@ struct BwdArgs {
 
 // ------------------------------------------------------------ gradient scale
 
-// scale[0] = 2^-e with max(|dout|, |dS_final|) 2^-e in [0.5, 1) (1 when all
-// are zero); scale[1] = 2^e.  One workgroup.
-__global__ __launch_bounds__(1024) void grad_scale_kernel(const float* dout, int64_t n_out, const float* dS,
-                                                          int64_t n_s, float* scale) {
-  __shared__ float sm[16];
+// The largest |dout| and |dS_final| as float bits (non-negative floats order
+// like their bit patterns): a grid-stride pass, one atomic max per workgroup
+// into word[0], which grad_scale_finish turns into scale[0] = 2^-e with
+// max 2^-e in [0.5, 1) (1 when all are zero) and scale[1] = 2^e.
+__global__ __launch_bounds__(256) void grad_absmax_kernel(const float* dout, int64_t n_out, const float* dS,
+                                                          int64_t n_s, unsigned int* word) {
+  __shared__ float sm[4];
   float m = 0.f;
-  for (int64_t i = threadIdx.x; i < n_out; i += blockDim.x) m = fmaxf(m, fabsf(dout[i]));
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += stride) m = fmaxf(m, fabsf(dout[i]));
   if (dS)
-    for (int64_t i = threadIdx.x; i < n_s; i += blockDim.x) m = fmaxf(m, fabsf(dS[i]));
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_s; i += stride) m = fmaxf(m, fabsf(dS[i]));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
   if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float mm = 0.f;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) mm = fmaxf(mm, sm[w]);
-    int e = 0;
-    if (mm > 0.f && isfinite(mm)) frexpf(mm, &e);  // mm = f 2^e, f in [0.5, 1)
-    scale[0] = ldexpf(1.f, -e);
-    scale[1] = ldexpf(1.f, e);
+    const float mm = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    atomicMax(word, __float_as_uint(mm));
   }
+}
+
+__global__ void grad_scale_start_kernel(unsigned int* word) { word[0] = 0u; }
+
+__global__ void grad_scale_finish_kernel(const unsigned int* word, float* scale) {
+  const float mm = __uint_as_float(word[0]);
+  int e = 0;
+  if (mm > 0.f && isfinite(mm)) frexpf(mm, &e);  // mm = f 2^e, f in [0.5, 1)
+  scale[0] = ldexpf(1.f, -e);
+  scale[1] = ldexpf(1.f, e);
 }
 
 // ------------------------------------------------------------ chain kernel
@@ -82,7 +91,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
   using OP = _Float16;
   constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36;
   constexpr int NCT = DV / 16, CPW = (NCT + NWAVE - 1) / NWAVE, RT = DK / 16, KB = DK / 32;
-  constexpr int oKh = 0;
+  // the per-row scalars first: below 64 KB every LDS address is one register
+  // plus an immediate offset
+  constexpr int oScal = 0;
+  constexpr int oKh = oScal + 4 * C * 4;
   constexpr int oQh = oKh + C * LDK * 2;
   constexpr int oQt = oQh + C * LDK * 2;
   constexpr int oWt = oQt + DK * LC * 2;
@@ -90,8 +102,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
   constexpr int oAn = oPt + C * LC * 2;
   constexpr int oAd = oAn + C * LC * 2;
   constexpr int oLi = oAd + C * LAD * 4;
-  constexpr int oScal = oLi + C * LLI * 2;
-  constexpr int total = oScal + 4 * C * 4;
+  constexpr int total = oLi + C * LLI * 2;
   static_assert(total <= 160 * 1024, "LDS budget");
   static_assert(RT <= NWAVE, "one wave per W column tile");
   __shared__ __attribute__((aligned(16))) char smem[total];
@@ -370,17 +381,22 @@ __device__ __forceinline__ void block_solve_t(f4_t (&Y)[4], const _Float16* sAnT
   Y[0] = t;
 }
 
-// grid (nchunks, H, B), 8 waves.  The dv columns are taken 32 at a time: two
-// waves form that block's U0, U and dB_u (accumulator layout, staged in LDS
-// as fp16), then every wave adds the block's share of the dv-reduced
-// products it owns: C x C tiles of dP and dB_u U0^T (jobs spread over the
-// waves), and for wave w < DK/16 column tile w of dO M0^T, U dM^T, dU M0^T.
+// grid (nchunks, H, B), 8 waves.  The dv columns are taken 128 at a time:
+// each wave forms one 16-column tile of that block's U0, U and dB_u
+// (accumulator layout, staged in LDS as fp16), then every wave adds the
+// block's share of the dv-reduced products it owns: C x C tiles of dP and
+// dB_u U0^T (jobs spread over the waves), and for wave w < DK/16 column tile
+// w of dO M0^T, U dM^T and dU M0^T.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   using OP = _Float16;
-  constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36, KW = 32, LKW = KW + 8;
-  constexpr int RT = DK / 16, KB = DK / 32, NKB = DV / KW;
-  constexpr int oKh = 0;
+  constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36, KW = DV >= 128 ? 128 : DV, LKW = KW + 8;
+  constexpr int RT = DK / 16, KB = DK / 32, NKB = DV / KW, KS = KW / 32;
+  // the per-row scalars first: below 64 KB every LDS address is one register
+  // plus an immediate offset
+  constexpr int oScal = 0;                            // g, gamma, beta, D, taps [C][4], norms, sums
+  constexpr int nScal = 4 * C + 4 * C + 2 * C + 6 * C + 4;
+  constexpr int oKh = oScal + nScal * 4;
   constexpr int oQh = oKh + C * LDK * 2;
   constexpr int oW = oQh + C * LDK * 2;
   constexpr int oAn = oW + C * LDK * 2;
@@ -388,9 +404,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   constexpr int oAd = oAnT + C * LC * 2;
   constexpr int oLi = oAd + C * LAD * 4;
   constexpr int oLiT = oLi + C * LLI * 2;
-  constexpr int oScal = oLiT + C * LLI * 2;           // g, gamma, beta, D, taps [C][4], norms, sums
-  constexpr int nScal = 4 * C + 4 * C + 2 * C + 6 * C + 4;
-  constexpr int oU = oScal + nScal * 4;               // union: staging during the dv loop, then dP.E, dS, dB_w
+  constexpr int oU = oLiT + C * LLI * 2;              // union: staging during the dv loop, then dP.E, dS, dB_w
   constexpr int szStage = 3 * C * LKW * 2;
   constexpr int szPost = 2 * C * LC * 2 + C * LDK * 2;
   constexpr int total = oU + (szStage > szPost ? szStage : szPost);
@@ -544,7 +558,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- the dv-reduced products, 32 columns at a time
+  // ---- the dv-reduced products, KW columns at a time
   f4_t accCC[3];                       // C x C jobs: wave, wave + 8, wave + 16 of {dP tiles, dB_u U0^T tiles}
   f4_t aQO[4], aKM[4], aW[4];          // column tile `wave` of dO M0^T, U dM^T, dU M0^T
 #pragma unroll
@@ -552,8 +566,13 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { aQO[i] = zero4(); aKM[i] = zero4(); aW[i] = zero4(); }
   float dgC_part = 0.f;
+#pragma unroll 1
   for (int kb = 0; kb < NKB; ++kb) {
-    if (wave < 2) {
+    if (wave < KW / 16) {
+      // an opaque copy of the row origin: the 64 row addresses of the value
+      // loads below would otherwise be hoisted out of this loop and spilled
+      int tb = t0;
+      asm volatile("" : "+s"(tb));
       const int col = kb * KW + wave * 16 + m16;
       // V' (the conv of the raw value rows with the chunk's taps)
       f4_t Vp[4], Y[4];
@@ -566,7 +585,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
           if (r < n) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int t = t0 + r - 3 + j;
+              const int t = tb + r - 3 + j;
               float x = 0.f;
               if (t >= 0) x = bf16_to_f32(a.v[(((int64_t)b * T + t) * H + h) * DV + col]);
               else if (a.conv_in) x = bf16_to_f32(a.conv_in[(((int64_t)b * 3 + 3 + t) * H + h) * DV + col]);
@@ -625,31 +644,43 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
     // C x C jobs: 0..9 dP tiles, 10..19 dB_u U0^T tiles
+#pragma unroll 1
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k0 = kb * KW + ks * 32;
 #pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const int job = wave + jj * NWAVE;
-      if (job < 20) {
-        const int which = job >= 10, t = job - 10 * which;
-        const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
-        if (which == 0)
-          mma(accCC[jj], glb_frag<OP>(dO, rowld, ti * 16, kb * KW, s, n), lds_frag<OP>(sUb, LKW, tj * 16, 0));
-        else
-          mma(accCC[jj], lds_frag<OP>(sBub, LKW, ti * 16, 0), lds_frag<OP>(sU0b, LKW, tj * 16, 0));
+      for (int jj = 0; jj < 3; ++jj) {
+        const int job = wave + jj * NWAVE;
+        if (job < 20) {
+          const int which = job >= 10, t = job - 10 * which;
+          const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+          if (which == 0)
+            mma(accCC[jj], glb_frag<OP>(dO, rowld, ti * 16, k0, s, n), lds_frag<OP>(sUb, LKW, tj * 16, ks * 32));
+          else
+            mma(accCC[jj], lds_frag<OP>(sBub, LKW, ti * 16, ks * 32), lds_frag<OP>(sU0b, LKW, tj * 16, ks * 32));
+        }
       }
-    }
-    if (wave < RT) {
-      const Frag<OP> fm0 = glb_frag<OP>(M0, DV, wave * 16, kb * KW, 1.f, DK);
-      const Frag<OP> fdm = glb_frag<OP>(dMC, DV, wave * 16, kb * KW, 1.f, DK);
+      if (wave < RT) {
+        const Frag<OP> fdm = glb_frag<OP>(dMC, DV, wave * 16, k0, 1.f, DK);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        mma(aQO[rt], glb_frag<OP>(dO, rowld, rt * 16, kb * KW, s, n), fm0);
-        mma(aKM[rt], lds_frag<OP>(sUb, LKW, rt * 16, 0), fdm);
-        mma(aW[rt], glb_frag<OP>(dUg, rowld, rt * 16, kb * KW, 1.f, n), fm0);
+        for (int rt = 0; rt < 4; ++rt) mma(aKM[rt], lds_frag<OP>(sUb, LKW, rt * 16, ks * 32), fdm);
       }
     }
     __syncthreads();
   }
-  if (wave < 2) {
+  // dO M0^T and dU M0^T take their operands from global memory only: a pass of
+  // their own keeps their accumulators out of the column work above
+  if (wave < RT) {
+#pragma unroll 1
+    for (int k0 = 0; k0 < DV; k0 += 32) {
+      const Frag<OP> fm0 = glb_frag<OP>(M0, DV, wave * 16, k0, 1.f, DK);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        mma(aQO[rt], glb_frag<OP>(dO, rowld, rt * 16, k0, s, n), fm0);
+        mma(aW[rt], glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n), fm0);
+      }
+    }
+  }
+  if (wave < KW / 16) {
     const float t = wave_sum(dgC_part);
     if (lane == 0) atomicAdd(&sMisc[0], t);
   }
@@ -1024,7 +1055,10 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   float* scale = reinterpret_cast<float*>(ws);
 
   hipError_t e = hipSuccess;
-  grad_scale_kernel<<<1, 1024, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, scale);
+  unsigned int* word = reinterpret_cast<unsigned int*>(scale + 2);
+  grad_scale_start_kernel<<<1, 1, 0, stream>>>(word);
+  grad_absmax_kernel<<<1024, 256, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, word);
+  grad_scale_finish_kernel<<<1, 1, 0, stream>>>(word, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // forward: taps and the state entering every chunk
   e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream);
