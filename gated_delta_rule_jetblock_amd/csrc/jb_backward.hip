@@ -565,7 +565,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   for (int i = 0; i < 3; ++i) accCC[i] = zero4();
 #pragma unroll
   for (int i = 0; i < 4; ++i) { aQO[i] = zero4(); aKM[i] = zero4(); aW[i] = zero4(); }
-  float dgC_part = 0.f;
 #pragma unroll 1
   for (int kb = 0; kb < NKB; ++kb) {
     if (wave < KW / 16) {
@@ -574,27 +573,32 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
       int tb = t0;
       asm volatile("" : "+s"(tb));
       const int col = kb * KW + wave * 16 + m16;
-      // V' (the conv of the raw value rows with the chunk's taps)
+      // V' (the conv of the raw value rows with the chunk's taps): a lane's
+      // four rows 4g..4g+3 of a row tile read the seven value rows 4g-3..4g+3
       f4_t Vp[4], Y[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt) {
+        float xr[7];
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+          const int r = rt * 16 + 4 * g4 + m - 3;  // chunk row of the value (t = t0 + r)
+          const int t = tb + r;
+          float x = 0.f;
+          if (r < n) {
+            if (t >= 0) x = bf16_to_f32(a.v[(((int64_t)b * T + t) * H + h) * DV + col]);
+            else if (a.conv_in) x = bf16_to_f32(a.conv_in[(((int64_t)b * 3 + 3 + t) * H + h) * DV + col]);
+          }
+          xr[m] = x;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * g4 + i;
-          float acc = 0.f;
-          if (r < n) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int t = tb + r - 3 + j;
-              float x = 0.f;
-              if (t >= 0) x = bf16_to_f32(a.v[(((int64_t)b * T + t) * H + h) * DV + col]);
-              else if (a.conv_in) x = bf16_to_f32(a.conv_in[(((int64_t)b * 3 + 3 + t) * H + h) * DV + col]);
-              acc += sTap[r * 4 + j] * x;
-            }
-          }
+          const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
+          const float acc = r < n ? tp.x * xr[i] + tp.y * xr[i + 1] + tp.z * xr[i + 2] + tp.w * xr[i + 3] : 0.f;
           Vp[rt][i] = acc;
           Y[rt][i] = sBeta[r] * acc;
         }
+      }
       block_solve<OP, LC, LLI>(Y, sAn, sLi);  // U0
       // U = U0 - W M0 (M0 tile in accumulator layout)
       f4_t m0[RT], tw[4];
@@ -610,13 +614,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) mma(tw[rt], lds_frag<OP>(sW, LDK, rt * 16, k2 * 32), fm);
       }
-      // the chunk-end gate term sum(dM . M0) over this column
-      float pm = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pm += m0[rt][i] * dMC[(rt * 16 + 4 * g4 + i) * DV + col];
-      dgC_part += pm;
       // dB_u = T^T dU
       f4_t dB[4];
 #pragma unroll
@@ -668,22 +665,37 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
     __syncthreads();
   }
   // dO M0^T and dU M0^T take their operands from global memory only: a pass of
-  // their own keeps their accumulators out of the column work above
+  // their own keeps their accumulators out of the column work above.  The
+  // same M0 rows give the chunk-end gate term sum(dM . M0) (in fp32).
   if (wave < RT) {
-#pragma unroll 1
+    float dgC_part = 0.f;
+    const float* m0p = M0 + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
+    const float* dmp = dMC + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
+#pragma unroll 2
     for (int k0 = 0; k0 < DV; k0 += 32) {
-      const Frag<OP> fm0 = glb_frag<OP>(M0, DV, wave * 16, k0, 1.f, DK);
+      const float4 ma = *reinterpret_cast<const float4*>(m0p + k0), mb = *reinterpret_cast<const float4*>(m0p + k0 + 16);
+      const float4 da = *reinterpret_cast<const float4*>(dmp + k0), db = *reinterpret_cast<const float4*>(dmp + k0 + 16);
+      dgC_part += ma.x * da.x + ma.y * da.y + ma.z * da.z + ma.w * da.w + mb.x * db.x + mb.y * db.y + mb.z * db.z +
+                  mb.w * db.w;
+      Frag<OP> fm0;
+      fm0.v[0] = (OP)ma.x; fm0.v[1] = (OP)ma.y; fm0.v[2] = (OP)ma.z; fm0.v[3] = (OP)ma.w;
+      fm0.v[4] = (OP)mb.x; fm0.v[5] = (OP)mb.y; fm0.v[6] = (OP)mb.z; fm0.v[7] = (OP)mb.w;
+      Frag<OP> fo[4], fu[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        mma(aQO[rt], glb_frag<OP>(dO, rowld, rt * 16, k0, s, n), fm0);
-        mma(aW[rt], glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n), fm0);
+        fo[rt] = glb_frag<OP>(dO, rowld, rt * 16, k0, s, n);
+        fu[rt] = glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        mma(aQO[rt], fo[rt], fm0);
+        mma(aW[rt], fu[rt], fm0);
       }
     }
-  }
-  if (wave < KW / 16) {
     const float t = wave_sum(dgC_part);
     if (lane == 0) atomicAdd(&sMisc[0], t);
   }
+
 
   // ---- dP: the P and gate terms, dP . E to LDS; zero the upper tiles of dP.E and dS
   for (int e = tid; e < C * C; e += NTHR) {
@@ -905,91 +917,84 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_
 
 // ------------------------------------------------------------ generator backward
 
-// Per token (one wave each, 4 per workgroup): pre = W1 x + b1, hid = SiLU(pre),
-// dhid = W2^T dtaps, dp = dhid SiLU'(pre); writes dp and hid [n][32] and
-// dx = W1^T dp.
-__global__ __launch_bounds__(256) void gen_bwd_token_kernel(int64_t n_tok, int D, int H, const bf16_t* x,
-                                                            const bf16_t* W1, const bf16_t* b1, const bf16_t* W2,
-                                                            const float* dtaps, float* dp_out, float* hid_out,
-                                                            float* dx) {
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= n_tok) return;
-  const bf16_t* xr = x + t * D;
-  float pre[32];
-#pragma unroll
-  for (int u = 0; u < 32; ++u) pre[u] = 0.f;
-  for (int d = lane; d < D; d += 64) {
-    const float xv = bf16_to_f32(xr[d]);
-#pragma unroll
-    for (int u = 0; u < 32; ++u) pre[u] += bf16_to_f32(W1[(int64_t)u * D + d]) * xv;
-  }
-  float dp = 0.f, hv = 0.f;
-#pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    const float p = wave_sum(pre[u]) + (b1 ? bf16_to_f32(b1[u]) : 0.f);
-    if (lane == u) {
-      const float sg = 1.f / (1.f + expf(-p));
-      hv = p * sg;
-      float dh = 0.f;
-      for (int r = 0; r < 4 * H; ++r) dh += bf16_to_f32(W2[(int64_t)r * 32 + u]) * dtaps[t * 4 * H + r];
-      dp = dh * sg * (1.f + p * (1.f - sg));
-    }
-  }
-  if (lane < 32) {
-    dp_out[t * 32 + lane] = dp;
-    hid_out[t * 32 + lane] = hv;
-  }
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) acc += bf16_to_f32(W1[(int64_t)u * D + d]) * __shfl(dp, u, WAVE);
-    dx[t * D + d] = acc;
-  }
+// One thread per (token, hidden unit): hid = SiLU(pre), dhid = W2^T dtaps,
+// dp = dhid SiLU'(pre), SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p).
+__global__ __launch_bounds__(256) void gen_bwd_dp_kernel(int64_t n_tok, int H, const bf16_t* W2, const float* pre,
+                                                         const float* dtaps, float* dp, float* hid) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_tok * 32) return;
+  const int64_t t = e >> 5;
+  const int u = (int)(e & 31);
+  const float p = pre[e], sg = 1.f / (1.f + expf(-p));
+  float dh = 0.f;
+  for (int r = 0; r < 4 * H; ++r) dh += bf16_to_f32(W2[r * 32 + u]) * dtaps[t * 4 * H + r];
+  dp[e] = dh * sg * (1.f + p * (1.f - sg));
+  hid[e] = p * sg;
 }
 
-// Partial weight gradients over a token range: grid (ceil(D / 256), NSPLIT);
-// thread d accumulates dW1[u][d] = sum_t dp[t][u] x[t][d] for its split; the
-// first column block also forms the split's dW2 = dtaps^T hid, db1, db2.
-__global__ __launch_bounds__(256) void gen_bwd_weight_kernel(int64_t n_tok, int D, int H, const bf16_t* x,
-                                                             const float* dp, const float* hid, const float* dtaps,
-                                                             float* part_w1, float* part_small) {
+// dx = dp W1 and the partial dW1 = dp^T x of one token range: grid
+// (ceil(D / 256), NSPLIT), thread d holds column d of W1 (32 values) and
+// its 32 dW1 sums; the range's dp rows are staged in LDS 64 at a time.
+__global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, const bf16_t* x, const bf16_t* W1,
+                                                        const float* dp, float* dx, float* part_w1) {
+  __shared__ float sdp[64][33];
   const int d = blockIdx.x * 256 + threadIdx.x, sp = blockIdx.y, nsp = gridDim.y;
   const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
-  if (d < D) {
-    float acc[32];
+  const bool ok = d < D;
+  float w[32], acc[32];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) acc[u] = 0.f;
-    for (int64_t t = t0; t < t1; ++t) {
-      const float xv = bf16_to_f32(x[t * D + d]);
+  for (int u = 0; u < 32; ++u) {
+    w[u] = ok ? bf16_to_f32(W1[(int64_t)u * D + d]) : 0.f;
+    acc[u] = 0.f;
+  }
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    const int nt = (int)(t1 - tb < 64 ? t1 - tb : 64);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nt * 32; e += 256) sdp[e >> 5][e & 31] = dp[(tb + (e >> 5)) * 32 + (e & 31)];
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+      const float xv = ok ? bf16_to_f32(x[(tb + i) * D + d]) : 0.f;
+      float s = 0.f;
 #pragma unroll
-      for (int u = 0; u < 32; ++u) acc[u] += dp[t * 32 + u] * xv;
+      for (int u = 0; u < 32; ++u) {
+        const float g = sdp[i][u];
+        s += w[u] * g;
+        acc[u] += g * xv;
+      }
+      if (ok) dx[(tb + i) * D + d] = s;
     }
+  }
+  if (ok)
 #pragma unroll
     for (int u = 0; u < 32; ++u) part_w1[((int64_t)sp * 32 + u) * D + d] = acc[u];
-  }
-  if (blockIdx.x == 0) {
-    // small parts: dW2 [4H][32], db2 [4H], db1 [32]
-    const int HK = 4 * H, nsmall = HK * 32 + HK + 32;
-    float* ps = part_small + (int64_t)sp * nsmall;
-    for (int e = threadIdx.x; e < nsmall; e += 256) {
-      float acc = 0.f;
-      if (e < HK * 32) {
-        const int r = e / 32, u = e % 32;
-        for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r] * hid[t * 32 + u];
-      } else if (e < HK * 32 + HK) {
-        const int r = e - HK * 32;
-        for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r];
-      } else {
-        const int u = e - HK * 32 - HK;
-        for (int64_t t = t0; t < t1; ++t) acc += dp[t * 32 + u];
-      }
-      ps[e] = acc;
+}
+
+// Partial dW2 = dtaps^T hid [4H][32], db2 = sum dtaps, db1 = sum dp over one
+// token range: grid NSPLIT, one entry per thread step.
+__global__ __launch_bounds__(256) void gen_bwd_small_kernel(int64_t n_tok, int H, const float* dp, const float* hid,
+                                                            const float* dtaps, float* part_small) {
+  const int sp = blockIdx.x, nsp = gridDim.x;
+  const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
+  const int HK = 4 * H, nsmall = HK * 32 + HK + 32;
+  float* ps = part_small + (int64_t)sp * nsmall;
+  for (int e = threadIdx.x; e < nsmall; e += 256) {
+    float acc = 0.f;
+    if (e < HK * 32) {
+      const int r = e / 32, u = e % 32;
+      for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r] * hid[t * 32 + u];
+    } else if (e < HK * 32 + HK) {
+      const int r = e - HK * 32;
+      for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r];
+    } else {
+      const int u = e - HK * 32 - HK;
+      for (int64_t t = t0; t < t1; ++t) acc += dp[t * 32 + u];
     }
+    ps[e] = acc;
   }
 }
 
-// Sum of the NSPLIT partials in a fixed order: out[e] = sum_s part[s][e].
+// Sum of the NSPLIT partials in a fixed order: out[e] = sum_s part[s][e]
+// (out may alias part: each thread reads its column before writing it).
 __global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* out) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
@@ -1004,7 +1009,7 @@ __global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr int GEN_NSPLIT = 64;
+constexpr int GEN_NSPLIT = 128;
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
@@ -1014,7 +1019,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += 2 * al256((size_t)B * H * nch * dk * dv * 4);       // Mck, dMck
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
   bytes += al256(n * H * 4 * 4);                               // dtaps
-  bytes += 2 * al256(n * 32 * 4);                              // dp, hid
+  bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
   bytes += al256((size_t)GEN_NSPLIT * (4 * H * 32 + 4 * H + 32) * 4);
   bytes += al256(16);                                          // scale
@@ -1044,6 +1049,8 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   ws += al256((size_t)n * H * dv * 4);
   float* dtaps = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * H * 4 * 4);
+  float* pre = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)n * 32 * 4);
   float* dp = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * 32 * 4);
   float* hid = reinterpret_cast<float*>(ws);
@@ -1061,7 +1068,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   grad_scale_finish_kernel<<<1, 1, 0, stream>>>(word, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // forward: taps and the state entering every chunk
-  e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream);
+  e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream, pre);
   if (e == hipSuccess) e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, fws, stream);
   if (e != hipSuccess) return e;
   BwdArgs a{};
@@ -1084,11 +1091,11 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   if (!launched) return hipErrorInvalidValue;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the generator
-  gen_bwd_token_kernel<<<dim3((unsigned)((n + 3) / 4)), 256, 0, stream>>>(n, D, H, (const bf16_t*)x,
-                                                                        (const bf16_t*)W1, (const bf16_t*)b1,
-                                                                        (const bf16_t*)W2, dtaps, dp, hid, dx);
-  gen_bwd_weight_kernel<<<dim3((D + 255) / 256, GEN_NSPLIT), 256, 0, stream>>>(n, D, H, (const bf16_t*)x, dp, hid,
-                                                                              dtaps, pw1, psm);
+  gen_bwd_dp_kernel<<<dim3((unsigned)((n * 32 + 255) / 256)), 256, 0, stream>>>(n, H, (const bf16_t*)W2, pre,
+                                                                                dtaps, dp, hid);
+  gen_bwd_x_kernel<<<dim3((D + 255) / 256, GEN_NSPLIT), 256, 0, stream>>>(n, D, (const bf16_t*)x,
+                                                                         (const bf16_t*)W1, dp, dx, pw1);
+  gen_bwd_small_kernel<<<dim3(GEN_NSPLIT), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
   const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
   sum_parts_kernel<<<dim3((unsigned)((nw1 + 255) / 256)), 256, 0, stream>>>(nw1, GEN_NSPLIT, pw1, dW1);
   // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout)

@@ -53,7 +53,8 @@ template <> struct GenFrag<float> {
 // so that each wave's chain of dependent loads stays short.
 template <typename IO, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, const IO* x, const IO* W1,
-                                                      const IO* b1, const IO* W2, const IO* b2, float* taps) {
+                                                      const IO* b1, const IO* W2, const IO* b2, float* taps,
+                                                      float* pre_out) {
   constexpr int NTOK = 16 * NT;
   constexpr int NTHREADS = NW * 64;
   __shared__ float red[NW][G][NTOK];
@@ -130,6 +131,7 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
 #pragma unroll
     for (int w = 0; w < NW; ++w) hsum += red[w][u][t];
     hid[t][u] = hsum / (1.0f + expf(-hsum));  // SiLU
+    if (pre_out && n0 + t < n) pre_out[(n0 + t) * G + u] = hsum;  // for the backward pass
   }
   __syncthreads();
   for (int e = tid; e < NTOK * HK; e += NTHREADS) {
@@ -145,31 +147,31 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
 
 template <typename IO, int NT, int NW>
 static void gen_launch(int64_t n, int D, int HK, const void* x, const void* W1, const void* b1, const void* W2,
-                       const void* b2, float* taps, hipStream_t stream) {
+                       const void* b2, float* taps, float* pre_out, hipStream_t stream) {
   const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)));
   gen_kernel<IO, NT, NW><<<grid, NW * 64, 0, stream>>>(n, D, HK, (const IO*)x, (const IO*)W1, (const IO*)b1,
-                                                      (const IO*)W2, (const IO*)b2, taps);
+                                                      (const IO*)W2, (const IO*)b2, taps, pre_out);
 }
 
 template <typename IO>
 static void gen_dispatch(int64_t n, int D, int HK, const void* x, const void* W1, const void* b1, const void* W2,
-                         const void* b2, float* taps, hipStream_t stream) {
+                         const void* b2, float* taps, float* pre_out, hipStream_t stream) {
   // few rows (decode): 16 tokens per workgroup over as many waves as d_model
   // allows, to spread the rows; many rows: 64 tokens per workgroup, 4 waves
   if (n <= 4096) {
-    if ((D / 32) % 16 == 0) gen_launch<IO, 1, 16>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
-    else if ((D / 32) % 8 == 0) gen_launch<IO, 1, 8>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
-    else gen_launch<IO, 1, 4>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+    if ((D / 32) % 16 == 0) gen_launch<IO, 1, 16>(n, D, HK, x, W1, b1, W2, b2, taps, pre_out, stream);
+    else if ((D / 32) % 8 == 0) gen_launch<IO, 1, 8>(n, D, HK, x, W1, b1, W2, b2, taps, pre_out, stream);
+    else gen_launch<IO, 1, 4>(n, D, HK, x, W1, b1, W2, b2, taps, pre_out, stream);
   } else {
-    gen_launch<IO, 4, 4>(n, D, HK, x, W1, b1, W2, b2, taps, stream);
+    gen_launch<IO, 4, 4>(n, D, HK, x, W1, b1, W2, b2, taps, pre_out, stream);
   }
 }
 
 hipError_t launch_gen_taps(int io, int64_t n, int D, int H, const void* x, const void* W1, const void* b1,
-                           const void* W2, const void* b2, float* taps, hipStream_t stream) {
+                           const void* W2, const void* b2, float* taps, hipStream_t stream, float* pre_out) {
   if (n == 0) return hipSuccess;
-  if (io == IO_BF16) gen_dispatch<bf16_t>(n, D, 4 * H, x, W1, b1, W2, b2, taps, stream);
-  else gen_dispatch<float>(n, D, 4 * H, x, W1, b1, W2, b2, taps, stream);
+  if (io == IO_BF16) gen_dispatch<bf16_t>(n, D, 4 * H, x, W1, b1, W2, b2, taps, pre_out, stream);
+  else gen_dispatch<float>(n, D, 4 * H, x, W1, b1, W2, b2, taps, pre_out, stream);
   return hipGetLastError();
 }
 

@@ -12,10 +12,11 @@ namespace jb {
 
 enum IoType { IO_BF16 = 0, IO_F32 = 1 };
 
-// Kernel generator over n rows of x [n][D] -> taps [n][H*4] f32.
+// Kernel generator over n rows of x [n][D] -> taps [n][H*4] f32 (and, when
+// pre_out is given, the hidden layer before SiLU [n][32] f32).
 hipError_t launch_gen_taps(int io, int64_t n, int D, int H, const void* x, const void* W1,
                            const void* b1, const void* W2, const void* b2, float* taps,
-                           hipStream_t stream);
+                           hipStream_t stream, float* pre_out = nullptr);
 
 // Dynamic causal conv: vconv [B][T][H][dv] f32 from taps [B][T][H][4].
 hipError_t launch_conv(int io, int B, int T, int H, int dv, const float* taps, const void* v,
