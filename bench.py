@@ -238,6 +238,46 @@ def measure_serving(jb, inputs, torch, sp, sd, out_dt, n_req: int, lo: int, hi: 
                             us=round(us_dec, 2), tokens_per_s=round(n_req / (us_dec * 1e-6), 1)))
 
 
+def measure_training(jb, inputs, torch, sp, B: int, T: int, reps: int = 3):
+    """Training at the prefill shape's heads (outside the timed step): B sequences of T tokens,
+    jb_prefill (the forward pass, fp32 o) and jb_backward (every gradient, from a random dO),
+    each averaged over `reps` calls bracketed by HIP events on the launching stream."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = inputs.Shape(B=B, T=T, H=sp.H, dk=sp.dk, dv=sp.dv, d_model=sp.d_model)
+    p = inputs.prefill_inputs(sh, seed=9, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(10)
+    dout = torch.randn((B, T, sh.H, sh.dv), generator=g, device=dev)
+    shape = jb.make_shape(B, T, sh.H, sh.dk, sh.dv, sh.d_model)
+    fws = jb.workspace(jb.prefill_workspace_size(shape), dev)
+    bws = jb.workspace(jb.backward_workspace_size(shape), dev)
+    o = torch.empty((B, T, sh.H, sh.dv), dtype=torch.float32, device=dev)
+    S = torch.empty((B, sh.H, sh.dk, sh.dv), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_f = timed(lambda: jb.prefill(p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"], p["W2"],
+                                    o=o, S_final=S, want_conv_out=False, ws=fws, stream=stream))
+    ms_b = timed(lambda: jb.backward(p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"], p["W2"], dout,
+                                     ws=bws, stream=stream))
+    tok = B * T
+    return dict(B=B, T=T, tokens=tok, forward=dict(call="jb_prefill (fp32 o)", ms=round(ms_f, 3)),
+                backward=dict(call="jb_backward (all gradients)", ms=round(ms_b, 3),
+                              tokens_per_s=round(tok / (ms_b * 1e-3), 1)),
+                tokens_per_s=round(tok / ((ms_f + ms_b) * 1e-3), 1), backward_over_forward=round(ms_b / ms_f, 2))
+
+
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
     """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
     import oracle
@@ -286,6 +326,7 @@ def main():
     ap.add_argument("--no-from-x", action="store_true", help="skip the measurement of the block from x")
     ap.add_argument("--no-static", action="store_true", help="skip the static-conv block measurement")
     ap.add_argument("--no-serving", action="store_true", help="skip the packed serving-batch measurement")
+    ap.add_argument("--no-training", action="store_true", help="skip the forward + backward measurement")
     ap.add_argument("--serving-requests", type=int, default=256)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -414,6 +455,12 @@ def main():
         log(f"serving: {serving['tokens']} prompt tokens prefilled in {serving['prefill']['ms']:.2f} ms "
             f"({serving['prefill']['tokens_per_s'] / 1e6:.1f} M tokens/s), decode step of the batch "
             f"{serving['decode']['us']:.1f} us")
+    training = None
+    if not args.no_training:
+        log("timing forward + backward (16 x 4096 tokens) ...")
+        training = measure_training(jb, inputs, torch, sp, 16, 4096)
+        log(f"training: forward {training['forward']['ms']:.2f} ms, backward {training['backward']['ms']:.2f} ms "
+            f"({training['tokens_per_s'] / 1e6:.2f} M tokens/s forward + backward)")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -449,6 +496,7 @@ def main():
         "from_x": from_x,
         "static_conv": static,
         "serving": serving,
+        "training": training,
     }
     print(json.dumps(line), flush=True)
 
