@@ -8,6 +8,39 @@
 
 namespace jb {
 
+// A fragment (kperm order) of the transpose of a row-major LDS tile: lane
+// reads column c0 + l%16 at rows k0 + kperm(g, j).  As an A operand it is
+// tile^T (rows c0..); as a B operand it is the tile itself (K = its rows).
+template <typename OP>
+__device__ __forceinline__ Frag<OP> lds_fragT(const OP* base, int ld, int c0, int k0) {
+  const int l = lane_id(), m = l & 15, g = l >> 4;
+  const OP* p = base + (k0 + 4 * g) * ld + c0 + m;
+  Frag<OP> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { f.v[j] = p[j * ld]; f.v[4 + j] = p[(16 + j) * ld]; }
+  return f;
+}
+
+// A fragment (kperm order) from a row-major fp32 matrix in global memory,
+// scaled: rows r0 + l%16, K offset k0 (two 16-byte loads per lane); rows at
+// or beyond nrows read as zero and are not touched.
+template <typename OP>
+__device__ __forceinline__ Frag<OP> glb_frag(const float* base, int64_t ld, int r0, int k0, float scale,
+                                             int nrows) {
+  const int l = lane_id(), m = l & 15, g = l >> 4;
+  const float* p = base + (int64_t)(r0 + m) * ld + k0 + 4 * g;
+  const bool ok = r0 + m < nrows;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 lo = ok ? *reinterpret_cast<const float4*>(p) : z;
+  const float4 hi = ok ? *reinterpret_cast<const float4*>(p + 16) : z;
+  Frag<OP> f;
+  f.v[0] = from_f32<OP>(lo.x * scale); f.v[1] = from_f32<OP>(lo.y * scale);
+  f.v[2] = from_f32<OP>(lo.z * scale); f.v[3] = from_f32<OP>(lo.w * scale);
+  f.v[4] = from_f32<OP>(hi.x * scale); f.v[5] = from_f32<OP>(hi.y * scale);
+  f.v[6] = from_f32<OP>(hi.z * scale); f.v[7] = from_f32<OP>(hi.w * scale);
+  return f;
+}
+
 constexpr int C = 64;        // chunk length
 constexpr int NWAVE = 8;     // wavefronts per chunk workgroup
 constexpr int NTHR = NWAVE * WAVE;
