@@ -156,14 +156,16 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = rt * 16 + 4 * g4 + i;
-          dOr[cw][rt][i] = (ct < NCT && row < n) ? s * dO[row * rowld + ct * 16 + m16] : 0.f;
+          // clamped row and column, then masked: the loads issue without branches
+          const float x = dO[min(row, n - 1) * rowld + min(ct, NCT - 1) * 16 + m16];
+          dOr[cw][rt][i] = (ct < NCT && row < n) ? s * x : 0.f;
         }
     }
     __syncthreads();  // the previous chunk's column phase is done with the tiles
 
     if (tid < PRO_THR) {
       Prologue<DK, bf16_t> pr;
-      pr.load(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n, true);
+      pr.load_global(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n);
       pr.finish(true);
 #pragma unroll
       for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
@@ -176,9 +178,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
     }
     if (wave == GATE_WAVE) {
       const bool valid = lane < n;
-      const int64_t gidx = ((int64_t)b * T + t0 + lane) * H + h;
-      const float al = valid ? a.alpha[gidx] : 1.f;
-      const float be = valid ? a.beta[gidx] : 0.f;
+      const int64_t gidx = ((int64_t)b * T + t0 + min(lane, n - 1)) * H + h;  // clamped, then masked
+      const float al0 = a.alpha[gidx], be0 = a.beta[gidx];
+      const float al = valid ? al0 : 1.f;
+      const float be = valid ? be0 : 0.f;
       const float g = chunk_gate_scan(al);
       const float gC = __shfl(g, C - 1, WAVE);
       sG[lane] = g;
@@ -455,7 +458,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   // ---- prologue: normalised q, k, gates, taps, norms
   if (tid < PRO_THR) {
     Prologue<DK, bf16_t> pr;
-    pr.load(a.q, a.k, tokbase, H, n, true);
+    pr.load_global(a.q, a.k, tokbase, H, n);
     // raw norms for the backward of the normalisation
     float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -476,10 +479,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   }
   if (wave == GATE_WAVE) {
     const bool valid = lane < n;
-    const float al = valid ? a.alpha[tokbase + (int64_t)lane * H] : 1.f;
-    const float be = valid ? a.beta[tokbase + (int64_t)lane * H] : 0.f;
-    const float4 tp = valid ? *reinterpret_cast<const float4*>(a.taps + (tokbase + (int64_t)lane * H) * 4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t gi = tokbase + (int64_t)min(lane, n - 1) * H;  // clamped, then masked
+    const float al0 = a.alpha[gi], be0 = a.beta[gi];
+    const float4 tp0 = *reinterpret_cast<const float4*>(a.taps + gi * 4);
+    const float al = valid ? al0 : 1.f;
+    const float be = valid ? be0 : 0.f;
+    const float4 tp = valid ? tp0 : make_float4(0.f, 0.f, 0.f, 0.f);
     const float g = chunk_gate_scan(al);
     const float gC = __shfl(g, C - 1, WAVE);
     sG[lane] = g;
@@ -581,14 +586,17 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
         float xr[7];
 #pragma unroll
         for (int m = 0; m < 7; ++m) {
+          // branch-free: every lane loads from a valid address (the first value
+          // row when the row has no data) and masks the value, so the seven
+          // loads go out together instead of one wait each
           const int r = rt * 16 + 4 * g4 + m - 3;  // chunk row of the value (t = t0 + r)
           const int t = tb + r;
-          float x = 0.f;
-          if (r < n) {
-            if (t >= 0) x = bf16_to_f32(a.v[(((int64_t)b * T + t) * H + h) * DV + col]);
-            else if (a.conv_in) x = bf16_to_f32(a.conv_in[(((int64_t)b * 3 + 3 + t) * H + h) * DV + col]);
-          }
-          xr[m] = x;
+          const bool inv = t >= 0 && r < n, inc = t < 0 && a.conv_in != nullptr;
+          const bf16_t* src = inv ? a.v + (((int64_t)b * T + t) * H + h) * DV + col
+                            : inc ? a.conv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV + col
+                                  : a.v;
+          const float x = bf16_to_f32(*src);
+          xr[m] = (inv || inc) ? x : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -621,7 +629,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * g4 + i;
-          dB[rt][i] = r < n ? dUg[r * rowld + col] : 0.f;
+          const float x = dUg[min(r, n - 1) * rowld + col];  // clamped row, then masked: no branch
+          dB[rt][i] = r < n ? x : 0.f;
         }
       block_solve_t<LC, LLI>(dB, sAnT, sLiT);
 #pragma unroll
@@ -812,8 +821,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
         dQh[rt][i] += sGam[r] * aQO[rt][i];
         dKh[rt][i] += sDec[r] * aKM[rt][i] + sBeta[r] * sGam[r] * dBw[rt][i];
         const bool ok = r < n;
-        const float qv = ok ? bf16_to_f32(a.q[(tokbase + (int64_t)r * H) * DK + col]) : 0.f;
-        const float kv = ok ? bf16_to_f32(a.k[(tokbase + (int64_t)r * H) * DK + col]) : 0.f;
+        const int64_t o = (tokbase + (int64_t)min(r, n - 1) * H) * DK + col;  // clamped, then masked
+        const float q0 = bf16_to_f32(a.q[o]), k0 = bf16_to_f32(a.k[o]);
+        const float qv = ok ? q0 : 0.f;
+        const float kv = ok ? k0 : 0.f;
         const float xq = sum16(qv * dQh[rt][i]), xk = sum16(kv * dKh[rt][i]);
         if (m16 == 0) {
           atomicAdd(&sQd[r], xq);
@@ -830,12 +841,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * g4 + i;
+        const int64_t o = (tokbase + (int64_t)min(r, n - 1) * H) * DK + col;  // clamped: loads without a branch
+        const float qv = bf16_to_f32(a.q[o]), kv = bf16_to_f32(a.k[o]);
+        const float nq = sNq[r], nk = sNk[r];
+        const float gq = (dQh[rt][i] / nq - qv * sQd[r] / (nq * nq * nq)) * inv;
+        const float gk = (dKh[rt][i] / nk - kv * sKd[r] / (nk * nk * nk)) * inv;
         if (r < n) {
-          const int64_t o = (tokbase + (int64_t)r * H) * DK + col;
-          const float qv = bf16_to_f32(a.q[o]), kv = bf16_to_f32(a.k[o]);
-          const float nq = sNq[r], nk = sNk[r];
-          a.dq[o] = (dQh[rt][i] / nq - qv * sQd[r] / (nq * nq * nq)) * inv;
-          a.dk[o] = (dKh[rt][i] / nk - kv * sKd[r] / (nk * nk * nk)) * inv;
+          a.dq[o] = gq;
+          a.dk[o] = gk;
         }
       }
   }

@@ -23,21 +23,21 @@ __device__ __forceinline__ Frag<OP> lds_fragT(const OP* base, int ld, int c0, in
 
 // A fragment (kperm order) from a row-major fp32 matrix in global memory,
 // scaled: rows r0 + l%16, K offset k0 (two 16-byte loads per lane); rows at
-// or beyond nrows read as zero and are not touched.
+// or beyond nrows (at least 1) read as zero.
 template <typename OP>
 __device__ __forceinline__ Frag<OP> glb_frag(const float* base, int64_t ld, int r0, int k0, float scale,
                                              int nrows) {
   const int l = lane_id(), m = l & 15, g = l >> 4;
-  const float* p = base + (int64_t)(r0 + m) * ld + k0 + 4 * g;
+  // the row is clamped and the values masked, so the loads issue without a branch
   const bool ok = r0 + m < nrows;
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4 lo = ok ? *reinterpret_cast<const float4*>(p) : z;
-  const float4 hi = ok ? *reinterpret_cast<const float4*>(p + 16) : z;
+  const float* p = base + (int64_t)min(r0 + m, nrows - 1) * ld + k0 + 4 * g;
+  const float sc = ok ? scale : 0.f;
+  const float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 16);
   Frag<OP> f;
-  f.v[0] = from_f32<OP>(lo.x * scale); f.v[1] = from_f32<OP>(lo.y * scale);
-  f.v[2] = from_f32<OP>(lo.z * scale); f.v[3] = from_f32<OP>(lo.w * scale);
-  f.v[4] = from_f32<OP>(hi.x * scale); f.v[5] = from_f32<OP>(hi.y * scale);
-  f.v[6] = from_f32<OP>(hi.z * scale); f.v[7] = from_f32<OP>(hi.w * scale);
+  f.v[0] = from_f32<OP>(lo.x * sc); f.v[1] = from_f32<OP>(lo.y * sc);
+  f.v[2] = from_f32<OP>(lo.z * sc); f.v[3] = from_f32<OP>(lo.w * sc);
+  f.v[4] = from_f32<OP>(hi.x * sc); f.v[5] = from_f32<OP>(hi.y * sc);
+  f.v[6] = from_f32<OP>(hi.z * sc); f.v[7] = from_f32<OP>(hi.w * sc);
   return f;
 }
 
@@ -98,6 +98,21 @@ struct Prologue {
     const int64_t off = (row_base + (int64_t)row * H) * DK + part * E;
     load_row_part<IO>(k + off, kv, E, valid);
     if (want_q) load_row_part<IO>(q + off, qv, E, valid);
+  }
+  // load() from global memory without branches: rows at or beyond n read
+  // row n - 1 (n >= 1) and are zeroed, so every load issues at once
+  __device__ __forceinline__ void load_global(const IO* q, const IO* k, int64_t row_base, int H, int n) {
+    row = threadIdx.x >> 3;
+    part = threadIdx.x & 7;
+    const bool valid = row < n;
+    const int64_t off = (row_base + (int64_t)min(row, n - 1) * H) * DK + part * E;
+    load_row_part<IO>(k + off, kv, E, true);
+    load_row_part<IO>(q + off, qv, E, true);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kv[e] = valid ? kv[e] : 0.f;
+      qv[e] = valid ? qv[e] : 0.f;
+    }
   }
   __device__ __forceinline__ void finish(bool want_q) {
     float sk = 0.f, sq = 0.f;
