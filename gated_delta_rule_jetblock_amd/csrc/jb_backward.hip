@@ -60,7 +60,12 @@ __global__ __launch_bounds__(256) void grad_absmax_kernel(const float* dout, int
   __shared__ float sm[4];
   float m = 0.f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_out; i += stride) m = fmaxf(m, fabsf(dout[i]));
+  // dout in 16-byte pieces (its element count is a multiple of dv), dS_final by elements
+  const float4* d4 = reinterpret_cast<const float4*>(dout);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_out / 4; i += stride) {
+    const float4 x = d4[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+  }
   if (dS)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_s; i += stride) m = fmaxf(m, fabsf(dS[i]));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
@@ -875,55 +880,89 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ conv backward
 
-// grid (ceil((T + 3) / 4), H, B), 4 waves: wave w handles token t = 4 x + w - 3
-// (t < 0: a conv-cache row).  dv_raw[t] = sum_j taps_{t+3-j}[j] dV'_{t+3-j}
-// over the tokens that read row t, plus the gradient of conv_out; dtaps_t[j]
-// = dV'_t . raw_{t-3+j} for t >= 0.
+// grid (ceil((T + 3) / 32), H, B), 4 waves: wave w walks 8 consecutive rows
+// t = 8 (4 x + w) - 3 + k (t < 0: a conv-cache row) with sliding windows of
+// the rows it reads, so each dV' row and each value row is loaded once per
+// strip.  dv_raw[t] = sum_j taps_{t+3-j}[j] dV'_{t+3-j} over the tokens that
+// read row t, plus the gradient of conv_out; dtaps_t[j] = dV'_t . raw_{t-3+j}.
 template <int DV>
 __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_t* v, const bf16_t* conv_in,
                                                        const float* taps, const float* dvc, const float* dconv_out,
                                                        float* dv, float* dconv_in, float* dtaps) {
-  constexpr int CPL = DV / 64;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6) - 3, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  float acc[CPL];
+  constexpr int CPL = DV / 64, STRIP = 8;
+  const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  const int tw0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * STRIP - 3;
+  if (tw0 >= T) return;
+  auto dvc_row = [&](int u, float (&o)[CPL], float (&tp)[4]) {  // dV'_u and taps_u (zero outside [0, T))
+    const bool ok = u >= 0 && u < T;
+    const int64_t bu = ((int64_t)b * T + (ok ? u : 0)) * H + h;
+    const float4 t4 = *reinterpret_cast<const float4*>(taps + bu * 4);
+    tp[0] = ok ? t4.x : 0.f; tp[1] = ok ? t4.y : 0.f; tp[2] = ok ? t4.z : 0.f; tp[3] = ok ? t4.w : 0.f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int u = t + 3 - j;  // the token whose tap j read row t
-    if (u >= 0 && u < T) {
-      const int64_t bu = ((int64_t)b * T + u) * H + h;
-      const float tp = taps[bu * 4 + j];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] += tp * dvc[bu * DV + lane * CPL + i];
+    for (int i = 0; i < CPL; ++i) {
+      const float x = dvc[bu * DV + lane * CPL + i];
+      o[i] = ok ? x : 0.f;
     }
-  }
-  if (dconv_out && t >= T - 3) {
-    const int sl = t - (T - 3);
+  };
+  auto raw_row = [&](int r, float (&o)[CPL]) {  // value row r (r < 0: the conv cache; zero without one)
+    const bool inv = r >= 0 && r < T, inc = r < 0 && r >= -3 && conv_in != nullptr;
+    const bf16_t* src = inv ? v + (((int64_t)b * T + r) * H + h) * DV
+                      : inc ? conv_in + (((int64_t)b * 3 + 3 + r) * H + h) * DV : v;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] += dconv_out[(((int64_t)b * 3 + sl) * H + h) * DV + lane * CPL + i];
-  }
-  float* dst = t >= 0 ? dv + (((int64_t)b * T + t) * H + h) * DV : dconv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) dst[lane * CPL + i] = acc[i];
-  if (t >= 0) {
-    const int64_t bt = ((int64_t)b * T + t) * H + h;
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = t - 3 + j;
-      const bf16_t* row = r >= 0 ? v + (((int64_t)b * T + r) * H + h) * DV
-                                 : (conv_in ? conv_in + (((int64_t)b * 3 + 3 + r) * H + h) * DV : nullptr);
-      if (row)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) d[j] += dvc[bt * DV + lane * CPL + i] * bf16_to_f32(row[lane * CPL + i]);
+    for (int i = 0; i < CPL; ++i) {
+      const float x = bf16_to_f32(src[lane * CPL + i]);
+      o[i] = (inv || inc) ? x : 0.f;
     }
+  };
+  float dwin[4][CPL], twin[4][4], rwin[4][CPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sj = wave_sum(d[j]);
-      if (lane == 0) dtaps[bt * 4 + j] = sj;
+  for (int j = 0; j < 3; ++j) {
+    dvc_row(tw0 + j, dwin[j + 1], twin[j + 1]);  // rows t .. t+2 of the first step sit in slots 1..3
+    raw_row(tw0 - 3 + j, rwin[j + 1]);           // rows t-3 .. t-1
+  }
+#pragma unroll
+  for (int k = 0; k < STRIP; ++k) {
+    const int t = tw0 + k;
+    if (t >= T) break;
+    // shift the windows: slot j holds dV' row t + j (j = 0..3) and raw row t - 3 + j
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) { dwin[j][i] = dwin[j + 1][i]; rwin[j][i] = rwin[j + 1][i]; }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) twin[j][q] = twin[j + 1][q];
+    }
+    dvc_row(t + 3, dwin[3], twin[3]);
+    raw_row(t, rwin[3]);
+    float acc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // token u = t + 3 - j read row t with its tap j
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] += twin[3 - j][j] * dwin[3 - j][i];
+    if (dconv_out && t >= T - 3) {
+      const int sl = t - (T - 3);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc[i] += dconv_out[(((int64_t)b * 3 + sl) * H + h) * DV + lane * CPL + i];
+    }
+    float* dst = t >= 0 ? dv + (((int64_t)b * T + t) * H + h) * DV : dconv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) dst[lane * CPL + i] = acc[i];
+    if (t >= 0) {
+      // dtaps_t[j] = dV'_t . raw_{t-3+j}; dV'_t sits in slot 0, raw row t-3+j in slot j
+      float d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) d[j] += dwin[0][i] * rwin[j][i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sj = wave_sum(d[j]);
+        if (lane == 0) dtaps[(((int64_t)b * T + t) * H + h) * 4 + j] = sj;
+      }
     }
   }
 }
@@ -1022,7 +1061,8 @@ __global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr int GEN_NSPLIT = 128;
+constexpr int GEN_NSPLIT = 128;       // token ranges of the dx / dW1 kernel
+constexpr int GEN_NSPLIT_SMALL = 2048; // token ranges of the dW2, db1, db2 partials
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
@@ -1034,7 +1074,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += al256(n * H * 4 * 4);                               // dtaps
   bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
-  bytes += al256((size_t)GEN_NSPLIT * (4 * H * 32 + 4 * H + 32) * 4);
+  bytes += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
   bytes += al256(16);                                          // scale
   return bytes;
 }
@@ -1071,13 +1111,13 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   float* pw1 = reinterpret_cast<float*>(ws);
   ws += al256((size_t)GEN_NSPLIT * 32 * D * 4);
   float* psm = reinterpret_cast<float*>(ws);
-  ws += al256((size_t)GEN_NSPLIT * (4 * H * 32 + 4 * H + 32) * 4);
+  ws += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
   float* scale = reinterpret_cast<float*>(ws);
 
   hipError_t e = hipSuccess;
   unsigned int* word = reinterpret_cast<unsigned int*>(scale + 2);
   grad_scale_start_kernel<<<1, 1, 0, stream>>>(word);
-  grad_absmax_kernel<<<1024, 256, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, word);
+  grad_absmax_kernel<<<4096, 256, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, word);
   grad_scale_finish_kernel<<<1, 1, 0, stream>>>(word, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // forward: taps and the state entering every chunk
@@ -1095,7 +1135,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   if (dk == DK_ && dv == DV_) {                                                                     \
     bwd_chain_kernel<DK_, DV_><<<dim3(H, B), NTHR, 0, stream>>>(a);                                 \
     bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
-    conv_bwd_kernel<DV_><<<dim3((T + 3 + 3) / 4, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v,   \
+    conv_bwd_kernel<DV_><<<dim3((T + 3 + 31) / 32, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v, \
         (const bf16_t*)conv_in, taps, dvc, dconv_out, dv_, dconv_in, dtaps);                        \
     launched = true;                                                                                \
   }
@@ -1108,11 +1148,11 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
                                                                                 dtaps, dp, hid);
   gen_bwd_x_kernel<<<dim3((D + 255) / 256, GEN_NSPLIT), 256, 0, stream>>>(n, D, (const bf16_t*)x,
                                                                          (const bf16_t*)W1, dp, dx, pw1);
-  gen_bwd_small_kernel<<<dim3(GEN_NSPLIT), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
+  gen_bwd_small_kernel<<<dim3(GEN_NSPLIT_SMALL), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
   const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
   sum_parts_kernel<<<dim3((unsigned)((nw1 + 255) / 256)), 256, 0, stream>>>(nw1, GEN_NSPLIT, pw1, dW1);
   // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout)
-  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256)), 256, 0, stream>>>(nsm, GEN_NSPLIT, psm, psm);
+  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256)), 256, 0, stream>>>(nsm, GEN_NSPLIT_SMALL, psm, psm);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = hipMemcpyAsync(dW2, psm, (size_t)4 * H * 32 * 4, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(db2, psm + 4 * H * 32, (size_t)4 * H * 4, hipMemcpyDeviceToDevice, stream);
