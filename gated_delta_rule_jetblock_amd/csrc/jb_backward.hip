@@ -89,13 +89,21 @@ __global__ void grad_scale_finish_kernel(const unsigned int* word, float* scale)
 
 // ------------------------------------------------------------ chain kernel
 
-// grid (H, B), 8 waves; wave w owns dv column tiles w, w + 8, .. of dM, kept
-// in accumulator registers while the chunks are walked backwards.
+// The dv columns of dM are independent, so they are split over CSPLIT
+// workgroups per (sequence, head) when there are more column tiles than
+// waves: each recomputes the chunk-shared tiles and carries its own columns.
+template <int DV>
+constexpr int chain_split() { return DV / 16 > NWAVE ? DV / 16 / NWAVE : 1; }
+
+// grid (H, B, CSPLIT), 8 waves; wave w of split s owns dv column tiles
+// s NCT/CSPLIT + w, + 8, .. of dM, kept in accumulator registers while the
+// chunks are walked backwards.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
   using OP = _Float16;
   constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36;
-  constexpr int NCT = DV / 16, CPW = (NCT + NWAVE - 1) / NWAVE, RT = DK / 16, KB = DK / 32;
+  constexpr int NCT = DV / 16, CSPLIT = chain_split<DV>(), NCTS = NCT / CSPLIT;
+  constexpr int CPW = (NCTS + NWAVE - 1) / NWAVE, RT = DK / 16, KB = DK / 32;
   // the per-row scalars first: below 64 KB every LDS address is one register
   // plus an immediate offset
   constexpr int oScal = 0;
@@ -138,13 +146,13 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
   f4_t dM[CPW][RT];
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = wave + cw * NWAVE;
+    const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * g4 + i;
-        dM[cw][rt][i] = (ct < NCT && a.dS_final) ? s * a.dS_final[(bh * DK + row) * DV + ct * 16 + m16] : 0.f;
+        dM[cw][rt][i] = (ct < (int)(blockIdx.z + 1) * NCTS && a.dS_final) ? s * a.dS_final[(bh * DK + row) * DV + ct * 16 + m16] : 0.f;
       }
   }
 
@@ -155,15 +163,16 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
     f4_t dOr[CPW][4];
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = wave + cw * NWAVE;
+      const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = rt * 16 + 4 * g4 + i;
           // clamped row and column, then masked: the loads issue without branches
-          const float x = dO[min(row, n - 1) * rowld + min(ct, NCT - 1) * 16 + m16];
-          dOr[cw][rt][i] = (ct < NCT && row < n) ? s * x : 0.f;
+          const int ctl = (int)(blockIdx.z + 1) * NCTS;
+          const float x = dO[min(row, n - 1) * rowld + min(ct, ctl - 1) * 16 + m16];
+          dOr[cw][rt][i] = (ct < ctl && row < n) ? s * x : 0.f;
         }
     }
     __syncthreads();  // the previous chunk's column phase is done with the tiles
@@ -274,8 +283,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
     const float gamC = sGam[C - 1];
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = wave + cw * NWAVE;
-      if (ct >= NCT) continue;
+      const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
+      if (ct >= (int)(blockIdx.z + 1) * NCTS) continue;
       const int col = ct * 16 + m16;
       // dU = P^T dO + D (K dM)
       f4_t dU[4], tk[4];
@@ -338,8 +347,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
   const float inv = a.scale[1];
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = wave + cw * NWAVE;
-    if (ct >= NCT) continue;
+    const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
+    if (ct >= (int)(blockIdx.z + 1) * NCTS) continue;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1133,7 +1142,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   bool launched = false;
 #define CASE(DK_, DV_)                                                                              \
   if (dk == DK_ && dv == DV_) {                                                                     \
-    bwd_chain_kernel<DK_, DV_><<<dim3(H, B), NTHR, 0, stream>>>(a);                                 \
+    bwd_chain_kernel<DK_, DV_><<<dim3(H, B, chain_split<DV_>()), NTHR, 0, stream>>>(a);             \
     bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
     conv_bwd_kernel<DV_><<<dim3((T + 3 + 31) / 32, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v, \
         (const bf16_t*)conv_in, taps, dvc, dconv_out, dv_, dconv_in, dtaps);                        \
