@@ -47,6 +47,9 @@ struct BwdArgs {
   float* dalpha;          // [B][T][H]
   float* dbeta;
   float* dvc;             // [B][T][H][DV]: dV'
+  float* QO;              // [B][H][nchunks][C][DK]: s x dO M0^T per chunk
+  float* WO;              // [B][H][nchunks][C][DK]: s x dU M0^T per chunk
+  float* dgC;             // [B][H][nchunks]: s x sum(dM . M0) per chunk
 };
 
 // ------------------------------------------------------------ gradient scale
@@ -360,10 +363,27 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
 // ------------------------------------------------------------ per-chunk gradients
 
 // sum of v over the 16 lanes of a lane group (all of them receive it)
+// one DPP-moved copy of v: CTRL is a row rotation (0x12r) or a quad permutation
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a DPP row, in every lane of the row: rotations by 8
+// and 4 within the row, then the two quad swaps
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, WAVE);
+  v += dpp_mov<0x128>(v);
+  v += dpp_mov<0x124>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0xB1>(v);
   return v;
+}
+
+// raw buffer loads: a wave-uniform resource and a per-lane byte offset; an
+// offset at or beyond the resource's size reads as zero
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ float buf_load_bf16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0));
 }
 // sum of v over the 4 lane groups at the same lane position
 __device__ __forceinline__ float sum_groups(float v) {
@@ -398,12 +418,78 @@ __device__ __forceinline__ void block_solve_t(f4_t (&Y)[4], const _Float16* sAnT
   Y[0] = t;
 }
 
+// dO M0^T and dU M0^T of every chunk (C x DK each, reduced over dv) and the
+// chunk-end gate term sum(dM . M0): operands from global memory only, so a
+// kernel of its own with no LDS runs many workgroups per compute unit and
+// hides the load latency.  grid (nchunks, H, B), one wave per dk column tile.
+template <int DK, int DV>
+__global__ __launch_bounds__(DK / 16 * 64) void bwd_dvred_kernel(BwdArgs a) {
+  using OP = _Float16;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = a.H, T = a.T;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int64_t bh = (int64_t)b * H + h;
+  const int t0 = c * C, n = min(C, T - t0);
+  const float s = a.scale[0];
+  const int64_t rowld = (int64_t)H * DV;
+  const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
+  const float* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+  const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
+  const float* dO = a.dout + tokbase * DV;
+  const float* dUg = a.dU + tokbase * DV;
+  f4_t aQO[4], aW[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) { aQO[rt] = zero4(); aW[rt] = zero4(); }
+  float dgC_part = 0.f;
+  const float* m0p = M0 + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
+  const float* dmp = dMC + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
+#pragma unroll 2
+  for (int k0 = 0; k0 < DV; k0 += 32) {
+    const float4 ma = *reinterpret_cast<const float4*>(m0p + k0), mb = *reinterpret_cast<const float4*>(m0p + k0 + 16);
+    const float4 da = *reinterpret_cast<const float4*>(dmp + k0), db = *reinterpret_cast<const float4*>(dmp + k0 + 16);
+    dgC_part += ma.x * da.x + ma.y * da.y + ma.z * da.z + ma.w * da.w + mb.x * db.x + mb.y * db.y + mb.z * db.z +
+                mb.w * db.w;
+    Frag<OP> fm0;
+    fm0.v[0] = (OP)ma.x; fm0.v[1] = (OP)ma.y; fm0.v[2] = (OP)ma.z; fm0.v[3] = (OP)ma.w;
+    fm0.v[4] = (OP)mb.x; fm0.v[5] = (OP)mb.y; fm0.v[6] = (OP)mb.z; fm0.v[7] = (OP)mb.w;
+    Frag<OP> fo[4], fu[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      fo[rt] = glb_frag<OP>(dO, rowld, rt * 16, k0, s, n);
+      fu[rt] = glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      mma(aQO[rt], fo[rt], fm0);
+      mma(aW[rt], fu[rt], fm0);
+    }
+  }
+  float* qo = a.QO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
+  float* wo = a.WO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qo[(rt * 16 + 4 * g4 + i) * DK] = aQO[rt][i];
+      wo[(rt * 16 + 4 * g4 + i) * DK] = aW[rt][i];
+    }
+  const float t = wave_sum(dgC_part);
+  __shared__ float sg[DK / 16];
+  if (lane == 0) sg[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < DK / 16; ++w) tot += sg[w];
+    a.dgC[bh * a.nchunks + c] = tot;
+  }
+}
+
 // grid (nchunks, H, B), 8 waves.  The dv columns are taken 128 at a time:
 // each wave forms one 16-column tile of that block's U0, U and dB_u
 // (accumulator layout, staged in LDS as fp16), then every wave adds the
 // block's share of the dv-reduced products it owns: C x C tiles of dP and
 // dB_u U0^T (jobs spread over the waves), and for wave w < DK/16 column tile
-// w of dO M0^T, U dM^T and dU M0^T.
+// w of U dM^T.  dO M0^T and dU M0^T come from bwd_dvred_kernel.
 template <int DK, int DV>
 __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   using OP = _Float16;
@@ -448,7 +534,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   float* sDD = sDb + C;            // k_i . (U dM^T)_i (the D term)
   float* sQd = sDD + C;            // q_i . dq^_i and k_i . dk^_i (norm backward)
   float* sKd = sQd + C;
-  float* sMisc = sKd + C;          // [0]: sum(dM . M0)
   OP* sUb = reinterpret_cast<OP*>(smem + oU);        // [C][LKW] U of the current dv block
   OP* sU0b = sUb + C * LKW;                          // U0
   OP* sBub = sU0b + C * LKW;                         // dB_u
@@ -511,7 +596,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
     sDD[lane] = 0.f;
     sQd[lane] = 0.f;
     sKd[lane] = 0.f;
-    if (lane == 0) sMisc[0] = 0.f;
   }
   __syncthreads();
 
@@ -584,39 +668,47 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   for (int i = 0; i < 3; ++i) accCC[i] = zero4();
 #pragma unroll
   for (int i = 0; i < 4; ++i) { aQO[i] = zero4(); aKM[i] = zero4(); aW[i] = zero4(); }
+  // Byte-addressed resources over the chunk's rows (row r at r * row stride):
+  // rows at or beyond n fall outside them, so loads read zero and stores are
+  // dropped without a branch.  The three value rows before the chunk come
+  // from the previous chunk, or for the first chunk from the conv cache
+  // (laid out [B][3][H][DV]: the same row stride), else read as zero.
+  const uint32_t rowv = (uint32_t)(H * DV * 2), rowf = (uint32_t)(H * DV * 4);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(a.v + tokbase * DV, (uint32_t)(n - 1) * rowv + DV * 2);
+  const bf16_t* halo = c > 0 ? a.v + (tokbase - 3 * (int64_t)H) * DV
+                     : a.conv_in ? a.conv_in + ((int64_t)b * 3 * H + h) * DV : a.v;
+  const __amdgpu_buffer_rsrc_t rVh = make_rsrc(halo, (c > 0 || a.conv_in) ? 2 * rowv + DV * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rdU = make_rsrc(dUg, (uint32_t)(n - 1) * rowf + DV * 4);
+  const __amdgpu_buffer_rsrc_t rdvc = make_rsrc(a.dvc + tokbase * DV, (uint32_t)(n - 1) * rowf + DV * 4);
+  const __amdgpu_buffer_rsrc_t rM0 = make_rsrc(M0, (uint32_t)(DK * DV * 4));
 #pragma unroll 1
   for (int kb = 0; kb < NKB; ++kb) {
     if (wave < KW / 16) {
-      // an opaque copy of the row origin: the 64 row addresses of the value
-      // loads below would otherwise be hoisted out of this loop and spilled
-      int tb = t0;
-      asm volatile("" : "+s"(tb));
       const int col = kb * KW + wave * 16 + m16;
+      // the lane's row 4g of the chunk as byte offsets; an opaque copy, so that
+      // the offsets derived from it are formed here and not kept in registers
+      // across the loop
+      uint32_t ov = 4 * g4 * rowv + col * 2, of = 4 * g4 * rowf + col * 4;
+      asm volatile("" : "+v"(ov), "+v"(of));
       // V' (the conv of the raw value rows with the chunk's taps): a lane's
-      // four rows 4g..4g+3 of a row tile read the seven value rows 4g-3..4g+3
+      // four rows 4g..4g+3 of a row tile read the seven value rows 4g-3..4g+3;
+      // a row before the chunk has a negative offset in rV (out of range, so
+      // zero) and its own in the halo resource
       f4_t Vp[4], Y[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         float xr[7];
 #pragma unroll
         for (int m = 0; m < 7; ++m) {
-          // branch-free: every lane loads from a valid address (the first value
-          // row when the row has no data) and masks the value, so the seven
-          // loads go out together instead of one wait each
-          const int r = rt * 16 + 4 * g4 + m - 3;  // chunk row of the value (t = t0 + r)
-          const int t = tb + r;
-          const bool inv = t >= 0 && r < n, inc = t < 0 && a.conv_in != nullptr;
-          const bf16_t* src = inv ? a.v + (((int64_t)b * T + t) * H + h) * DV + col
-                            : inc ? a.conv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV + col
-                                  : a.v;
-          const float x = bf16_to_f32(*src);
-          xr[m] = (inv || inc) ? x : 0.f;
+          const int dr = rt * 16 + m - 3;  // row offset from 4g
+          xr[m] = buf_load_bf16(rV, ov + (uint32_t)dr * rowv);
+          if (rt == 0 && m < 3) xr[m] += buf_load_bf16(rVh, ov + (uint32_t)(m * rowv));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * g4 + i;
           const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
-          const float acc = r < n ? tp.x * xr[i] + tp.y * xr[i + 1] + tp.z * xr[i + 2] + tp.w * xr[i + 3] : 0.f;
+          const float acc = tp.x * xr[i] + tp.y * xr[i + 1] + tp.z * xr[i + 2] + tp.w * xr[i + 3];
           Vp[rt][i] = acc;
           Y[rt][i] = sBeta[r] * acc;
         }
@@ -627,7 +719,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m0[rt][i] = M0[(rt * 16 + 4 * g4 + i) * DV + col];
+        for (int i = 0; i < 4; ++i) m0[rt][i] = buf_load_f32(rM0, (uint32_t)(((rt * 16 + 4 * g4 + i) * DV + col) * 4));
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) tw[rt] = zero4();
 #pragma unroll
@@ -641,11 +733,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rt * 16 + 4 * g4 + i;
-          const float x = dUg[min(r, n - 1) * rowld + col];  // clamped row, then masked: no branch
-          dB[rt][i] = r < n ? x : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) dB[rt][i] = buf_load_f32(rdU, of + (uint32_t)(rt * 16 + i) * rowf);
       block_solve_t<LC, LLI>(dB, sAnT, sLiT);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -657,7 +745,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
           sU0b[r * LKW + wave * 16 + m16] = (OP)Y[rt][i];
           sBub[r * LKW + wave * 16 + m16] = (OP)dB[rt][i];
           // dV' = b dB_u (unscaled), and b's share dB_u . V'
-          if (r < n) a.dvc[(tokbase + (int64_t)r * H) * DV + col] = sBeta[r] * dB[rt][i] * inv;
+          buf_store(rdvc, sBeta[r] * dB[rt][i] * inv, (int)(of + (uint32_t)(rt * 16 + i) * rowf), 0);
           const float db = sum16(dB[rt][i] * Vp[rt][i]);
           if (m16 == 0) atomicAdd(&sDb[r], db);
         }
@@ -687,38 +775,18 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
-  // dO M0^T and dU M0^T take their operands from global memory only: a pass of
-  // their own keeps their accumulators out of the column work above.  The
-  // same M0 rows give the chunk-end gate term sum(dM . M0) (in fp32).
+  // dO M0^T and dU M0^T (bwd_dvred_kernel): column tile `wave` into registers
   if (wave < RT) {
-    float dgC_part = 0.f;
-    const float* m0p = M0 + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
-    const float* dmp = dMC + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
-#pragma unroll 2
-    for (int k0 = 0; k0 < DV; k0 += 32) {
-      const float4 ma = *reinterpret_cast<const float4*>(m0p + k0), mb = *reinterpret_cast<const float4*>(m0p + k0 + 16);
-      const float4 da = *reinterpret_cast<const float4*>(dmp + k0), db = *reinterpret_cast<const float4*>(dmp + k0 + 16);
-      dgC_part += ma.x * da.x + ma.y * da.y + ma.z * da.z + ma.w * da.w + mb.x * db.x + mb.y * db.y + mb.z * db.z +
-                  mb.w * db.w;
-      Frag<OP> fm0;
-      fm0.v[0] = (OP)ma.x; fm0.v[1] = (OP)ma.y; fm0.v[2] = (OP)ma.z; fm0.v[3] = (OP)ma.w;
-      fm0.v[4] = (OP)mb.x; fm0.v[5] = (OP)mb.y; fm0.v[6] = (OP)mb.z; fm0.v[7] = (OP)mb.w;
-      Frag<OP> fo[4], fu[4];
+    const float* qo = a.QO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
+    const float* wo = a.WO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        fo[rt] = glb_frag<OP>(dO, rowld, rt * 16, k0, s, n);
-        fu[rt] = glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n);
-      }
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        mma(aQO[rt], fo[rt], fm0);
-        mma(aW[rt], fu[rt], fm0);
+      for (int i = 0; i < 4; ++i) {
+        aQO[rt][i] = qo[(rt * 16 + 4 * g4 + i) * DK];
+        aW[rt][i] = wo[(rt * 16 + 4 * g4 + i) * DK];
       }
-    }
-    const float t = wave_sum(dgC_part);
-    if (lane == 0) atomicAdd(&sMisc[0], t);
   }
-
 
   // ---- dP: the P and gate terms, dP . E to LDS; zero the upper tiles of dP.E and dS
   for (int e = tid; e < C * C; e += NTHR) {
@@ -834,11 +902,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
         const int r = rt * 16 + 4 * g4 + i;
         dQh[rt][i] += sGam[r] * aQO[rt][i];
         dKh[rt][i] += sDec[r] * aKM[rt][i] + sBeta[r] * sGam[r] * dBw[rt][i];
-        const bool ok = r < n;
-        const int64_t o = (tokbase + (int64_t)min(r, n - 1) * H) * DK + col;  // clamped, then masked
-        const float q0 = bf16_to_f32(a.q[o]), k0 = bf16_to_f32(a.k[o]);
-        const float qv = ok ? q0 : 0.f;
-        const float kv = ok ? k0 : 0.f;
+        // the normalisation's backward, dq = (dq^ - q^ (q^ . dq^)) / n, with q^ from LDS
+        const float qv = (float)sQh[r * LDK + col], kv = (float)sKh[r * LDK + col];
         const float xq = sum16(qv * dQh[rt][i]), xk = sum16(kv * dKh[rt][i]);
         if (m16 == 0) {
           atomicAdd(&sQd[r], xq);
@@ -855,11 +920,10 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * g4 + i;
-        const int64_t o = (tokbase + (int64_t)min(r, n - 1) * H) * DK + col;  // clamped: loads without a branch
-        const float qv = bf16_to_f32(a.q[o]), kv = bf16_to_f32(a.k[o]);
-        const float nq = sNq[r], nk = sNk[r];
-        const float gq = (dQh[rt][i] / nq - qv * sQd[r] / (nq * nq * nq)) * inv;
-        const float gk = (dKh[rt][i] / nk - kv * sKd[r] / (nk * nk * nk)) * inv;
+        const int64_t o = (tokbase + (int64_t)r * H) * DK + col;
+        const float qv = (float)sQh[r * LDK + col], kv = (float)sKh[r * LDK + col];
+        const float gq = (dQh[rt][i] - qv * sQd[r]) / sNq[r] * inv;
+        const float gk = (dKh[rt][i] - kv * sKd[r]) / sNk[r] * inv;
         if (r < n) {
           a.dq[o] = gq;
           a.dk[o] = gk;
@@ -870,7 +934,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   if (wave == GATE_WAVE) {
     const float D = sDec[lane], dd = sDD[lane];
     float dg = sDg[lane] - D * dd;
-    const float tot = wave_sum(D * dd) + sGam[C - 1] * sMisc[0];
+    const float tot = wave_sum(D * dd) + sGam[C - 1] * a.dgC[bh * a.nchunks + c];
     if (lane == C - 1) dg += tot;
     // reverse inclusive cumulative sum over the chunk
     float r = dg;
@@ -1080,6 +1144,8 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   size_t bytes = al256(prefill_workspace_bytes(p));           // taps, segment buffers (the forward pass)
   bytes += 2 * al256((size_t)B * H * nch * dk * dv * 4);       // Mck, dMck
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
+  bytes += 2 * al256((size_t)B * H * nch * C * dk * 4);        // dO M0^T, dU M0^T per chunk
+  bytes += al256((size_t)B * H * nch * 4);                     // the chunk-end gate term
   bytes += al256(n * H * 4 * 4);                               // dtaps
   bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
@@ -1109,6 +1175,12 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   ws += al256((size_t)n * H * dv * 4);
   float* dvc = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * H * dv * 4);
+  float* QO = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)B * H * nch * C * dk * 4);
+  float* WO = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)B * H * nch * C * dk * 4);
+  float* dgC = reinterpret_cast<float*>(ws);
+  ws += al256((size_t)B * H * nch * 4);
   float* dtaps = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * H * 4 * 4);
   float* pre = reinterpret_cast<float*>(ws);
@@ -1138,11 +1210,12 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   a.q = (const bf16_t*)q; a.k = (const bf16_t*)k; a.v = (const bf16_t*)v; a.conv_in = (const bf16_t*)conv_in;
   a.alpha = alpha; a.beta = beta; a.taps = taps; a.dout = dout; a.dS_final = dS_final; a.scale = scale;
   a.Mck = Mck; a.dMck = dMck; a.dU = dU; a.dS0 = dS0; a.dq = dq; a.dk = dk_; a.dalpha = dalpha; a.dbeta = dbeta;
-  a.dvc = dvc;
+  a.dvc = dvc; a.QO = QO; a.WO = WO; a.dgC = dgC;
   bool launched = false;
 #define CASE(DK_, DV_)                                                                              \
   if (dk == DK_ && dv == DV_) {                                                                     \
     bwd_chain_kernel<DK_, DV_><<<dim3(H, B, chain_split<DV_>()), NTHR, 0, stream>>>(a);             \
+    bwd_dvred_kernel<DK_, DV_><<<dim3(nch, H, B), DK_ / 16 * 64, 0, stream>>>(a);                   \
     bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
     conv_bwd_kernel<DV_><<<dim3((T + 3 + 31) / 32, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v, \
         (const bf16_t*)conv_in, taps, dvc, dconv_out, dv_, dconv_in, dtaps);                        \

@@ -210,3 +210,21 @@ def test_edge_values(jb, oracle_mod, case):
     ref = oracle_prefill(oracle_mod, p)
     r = _run(jb, p)
     _check(r, ref, TOL_BF16, case)
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_output_rows_stay_in_bounds(jb, out):
+    """A ragged last chunk (T = 200: 8 rows in chunk 3) writes its rows and nothing after
+    them: o is the head of a larger buffer whose tail of 64 rows must keep its fill."""
+    from gated_delta_rule_jetblock_amd import inputs
+    s = inputs.Shape(B=1, T=200, H=2, dk=32, dv=64, d_model=128)
+    p = inputs.prefill_inputs(s, seed=31)
+    n_o = s.B * s.T * s.H * s.dv
+    guard = 64 * s.H * s.dv
+    buf = torch.full((n_o + guard,), float("nan"), dtype=out, device="cuda")
+    o = buf[:n_o].view(s.B, s.T, s.H, s.dv)
+    r = _run(jb, p, out_dtype=out, o=o)
+    ref = _run(jb, p, out_dtype=out)
+    assert torch.equal(o, ref["o"])
+    tail = buf[n_o:]
+    assert torch.isnan(tail).all(), int((~torch.isnan(tail)).sum())
