@@ -419,69 +419,90 @@ __device__ __forceinline__ void block_solve_t(f4_t (&Y)[4], const _Float16* sAnT
 }
 
 // dO M0^T and dU M0^T of every chunk (C x DK each, reduced over dv) and the
-// chunk-end gate term sum(dM . M0): operands from global memory only, so a
-// kernel of its own with no LDS runs many workgroups per compute unit and
-// hides the load latency.  grid (nchunks, H, B), one wave per dk column tile.
+// chunk-end gate term sum(dM . M0).  grid (nchunks, H, B), 8 waves: M0 is
+// read once into LDS as fp16 (its rows are the B operand of both products),
+// dM alongside it for the gate term; wave w then forms row tile w % 4 of
+// dO M0^T (w < 4) or of dU M0^T, all DK columns, its A operand streamed from
+// global memory.  No operand is read twice, and two workgroups share a
+// compute unit.
 template <int DK, int DV>
-__global__ __launch_bounds__(DK / 16 * 64) void bwd_dvred_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
   using OP = _Float16;
+  constexpr int LDM = DV + 8;              // fp16 row stride of the staged M0
+  constexpr int CT = DK / 16;              // column tiles
+  constexpr int KSTEP = DV / 32;           // 32-deep steps over dv
+  constexpr int NV4 = DK * DV / 4 / NTHR;  // float4s of M0 per thread
+  constexpr int R = NV4 % 6 == 0 ? 6 : NV4 % 4 == 0 ? 4 : 1;  // float4s per staging round
+  static_assert(DK * DV % (4 * NTHR) == 0 && NV4 % R == 0, "whole float4s per thread");
+  __shared__ __attribute__((aligned(16))) OP sM0[DK * LDM];
+  __shared__ float sg[NWAVE];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = a.H, T = a.T;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * H + h;
   const int t0 = c * C, n = min(C, T - t0);
-  const float s = a.scale[0];
-  const int64_t rowld = (int64_t)H * DV;
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
-  const float* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
-  const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
-  const float* dO = a.dout + tokbase * DV;
-  const float* dUg = a.dU + tokbase * DV;
-  f4_t aQO[4], aW[4];
+  const float4* M0 = reinterpret_cast<const float4*>(a.Mck + ((bh * a.nchunks + c) * DK) * DV);
+  const float4* dMC = reinterpret_cast<const float4*>(a.dMck + ((bh * a.nchunks + c) * DK) * DV);
+
+  // this wave's A operand, 16 rows of dO (scaled) or of dU, issued first so
+  // that its loads are in flight while M0 is staged
+  const bool isU = wave >= 4;
+  const int rt = wave & 3;
+  const int row = rt * 16 + m16;
+  const float* A = (isU ? a.dU : a.dout) + (tokbase + (int64_t)min(row, n - 1) * H) * DV + 4 * g4;
+  const float sc = row < n ? (isU ? 1.f : a.scale[0]) : 0.f;  // clamped row, masked value
+  float4 ra[KSTEP][2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) { aQO[rt] = zero4(); aW[rt] = zero4(); }
-  float dgC_part = 0.f;
-  const float* m0p = M0 + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
-  const float* dmp = dMC + (int64_t)(wave * 16 + m16) * DV + 4 * g4;
-#pragma unroll 2
-  for (int k0 = 0; k0 < DV; k0 += 32) {
-    const float4 ma = *reinterpret_cast<const float4*>(m0p + k0), mb = *reinterpret_cast<const float4*>(m0p + k0 + 16);
-    const float4 da = *reinterpret_cast<const float4*>(dmp + k0), db = *reinterpret_cast<const float4*>(dmp + k0 + 16);
-    dgC_part += ma.x * da.x + ma.y * da.y + ma.z * da.z + ma.w * da.w + mb.x * db.x + mb.y * db.y + mb.z * db.z +
-                mb.w * db.w;
-    Frag<OP> fm0;
-    fm0.v[0] = (OP)ma.x; fm0.v[1] = (OP)ma.y; fm0.v[2] = (OP)ma.z; fm0.v[3] = (OP)ma.w;
-    fm0.v[4] = (OP)mb.x; fm0.v[5] = (OP)mb.y; fm0.v[6] = (OP)mb.z; fm0.v[7] = (OP)mb.w;
-    Frag<OP> fo[4], fu[4];
+  for (int ks = 0; ks < KSTEP; ++ks) {
+    ra[ks][0] = *reinterpret_cast<const float4*>(A + ks * 32);
+    ra[ks][1] = *reinterpret_cast<const float4*>(A + ks * 32 + 16);
+  }
+
+  float part = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      fo[rt] = glb_frag<OP>(dO, rowld, rt * 16, k0, s, n);
-      fu[rt] = glb_frag<OP>(dUg, rowld, rt * 16, k0, 1.f, n);
+  for (int j0 = 0; j0 < NV4; j0 += R) {
+    float4 m[R], d[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      m[j] = M0[(j0 + j) * NTHR + tid];
+      d[j] = dMC[(j0 + j) * NTHR + tid];
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      mma(aQO[rt], fo[rt], fm0);
-      mma(aW[rt], fu[rt], fm0);
+    for (int j = 0; j < R; ++j) {
+      const int e = (j0 + j) * NTHR + tid;
+      part += m[j].x * d[j].x + m[j].y * d[j].y + m[j].z * d[j].z + m[j].w * d[j].w;
+      const half4_t hv = {(OP)m[j].x, (OP)m[j].y, (OP)m[j].z, (OP)m[j].w};
+      *reinterpret_cast<half4_t*>(sM0 + (e / (DV / 4)) * LDM + (e % (DV / 4)) * 4) = hv;
     }
   }
-  float* qo = a.QO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
-  float* wo = a.WO + ((bh * a.nchunks + c) * C) * DK + wave * 16 + m16;
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qo[(rt * 16 + 4 * g4 + i) * DK] = aQO[rt][i];
-      wo[(rt * 16 + 4 * g4 + i) * DK] = aW[rt][i];
-    }
-  const float t = wave_sum(dgC_part);
-  __shared__ float sg[DK / 16];
-  if (lane == 0) sg[wave] = t;
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  part = wave_sum(part);
+  if (lane == 0) sg[wave] = part;
+  lds_barrier();  // the A loads stay in flight
+  if (tid == 0) {
     float tot = 0.f;
-    for (int w = 0; w < DK / 16; ++w) tot += sg[w];
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) tot += sg[w];
     a.dgC[bh * a.nchunks + c] = tot;
   }
+
+  f4_t acc[CT];
+#pragma unroll
+  for (int j = 0; j < CT; ++j) acc[j] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < KSTEP; ++ks) {
+    Frag<OP> fa;
+    const float4 lo = ra[ks][0], hi = ra[ks][1];
+    fa.v[0] = (OP)(lo.x * sc); fa.v[1] = (OP)(lo.y * sc); fa.v[2] = (OP)(lo.z * sc); fa.v[3] = (OP)(lo.w * sc);
+    fa.v[4] = (OP)(hi.x * sc); fa.v[5] = (OP)(hi.y * sc); fa.v[6] = (OP)(hi.z * sc); fa.v[7] = (OP)(hi.w * sc);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) mma(acc[j], fa, lds_frag<OP>(sM0, LDM, j * 16, ks * 32));
+  }
+  float* out = (isU ? a.WO : a.QO) + ((bh * a.nchunks + c) * C + rt * 16 + 4 * g4) * DK + m16;
+#pragma unroll
+  for (int j = 0; j < CT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i * DK + j * 16] = acc[j][i];
 }
 
 // grid (nchunks, H, B), 8 waves.  The dv columns are taken 128 at a time:
@@ -1215,7 +1236,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
 #define CASE(DK_, DV_)                                                                              \
   if (dk == DK_ && dv == DV_) {                                                                     \
     bwd_chain_kernel<DK_, DV_><<<dim3(H, B, chain_split<DV_>()), NTHR, 0, stream>>>(a);             \
-    bwd_dvred_kernel<DK_, DV_><<<dim3(nch, H, B), DK_ / 16 * 64, 0, stream>>>(a);                   \
+    bwd_dvred_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                            \
     bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
     conv_bwd_kernel<DV_><<<dim3((T + 3 + 31) / 32, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v, \
         (const bf16_t*)conv_in, taps, dvc, dconv_out, dv_, dconv_in, dtaps);                        \
