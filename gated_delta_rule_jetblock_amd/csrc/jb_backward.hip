@@ -1098,16 +1098,27 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
     __syncthreads();
     for (int e = threadIdx.x; e < nt * 32; e += 256) sdp[e >> 5][e & 31] = dp[(tb + (e >> 5)) * 32 + (e & 31)];
     __syncthreads();
-    for (int i = 0; i < nt; ++i) {
-      const float xv = ok ? bf16_to_f32(x[(tb + i) * D + d]) : 0.f;
-      float s = 0.f;
+    // four tokens at a time: their x loads go out together (rows past nt
+    // read row 0 of the block and weigh zero: sdp rows past nt are not used)
+    for (int i0 = 0; i0 < nt; i0 += 4) {
+      float xv[4];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const float g = sdp[i][u];
-        s += w[u] * g;
-        acc[u] += g * xv;
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j < nt ? i0 + j : 0;
+        xv[j] = ok ? bf16_to_f32(x[(tb + i) * D + d]) : 0.f;
       }
-      if (ok) dx[(tb + i) * D + d] = s;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j >= nt) break;
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const float g = sdp[i0 + j][u];
+          s += w[u] * g;
+          acc[u] += g * xv[j];
+        }
+        if (ok) dx[(tb + i0 + j) * D + d] = s;
+      }
     }
   }
   if (ok)
@@ -1139,14 +1150,22 @@ __global__ __launch_bounds__(256) void gen_bwd_small_kernel(int64_t n_tok, int H
   }
 }
 
-// Sum of the NSPLIT partials in a fixed order: out[e] = sum_s part[s][e]
-// (out may alias part: each thread reads its column before writing it).
-__global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* out) {
+// Sums of partials in a fixed order, `per` partials (a multiple of 4) per
+// range: out[y][e] = sum over s in [y per, (y + 1) per) of part[s][e], with
+// grid.y ranges.  Four running sums keep four loads in flight.
+__global__ void sum_parts_kernel(int64_t n, int per, const float* part, float* out) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n) return;
-  float acc = 0.f;
-  for (int s = 0; s < nsp; ++s) acc += part[(int64_t)s * n + e];
-  out[e] = acc;
+  const float* p = part + (int64_t)blockIdx.y * per * n + e;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < per; s += 4) {
+    a0 += p[(int64_t)s * n];
+    a1 += p[(int64_t)(s + 1) * n];
+    a2 += p[(int64_t)(s + 2) * n];
+    a3 += p[(int64_t)(s + 3) * n];
+  }
+  out[(int64_t)blockIdx.y * n + e] = (a0 + a1) + (a2 + a3);
 }
 
 // ------------------------------------------------------------ host side
@@ -1155,8 +1174,11 @@ __global__ void sum_parts_kernel(int64_t n, int nsp, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr int GEN_NSPLIT = 128;       // token ranges of the dx / dW1 kernel
+constexpr int GEN_NSPLIT = 512;       // token ranges of the dx / dW1 kernel
 constexpr int GEN_NSPLIT_SMALL = 2048; // token ranges of the dW2, db1, db2 partials
+constexpr int GEN_SMALL_PER = 64;      // partials per range in the first of their two sums
+static_assert(GEN_NSPLIT % 4 == 0 && GEN_SMALL_PER % 4 == 0 && (GEN_NSPLIT_SMALL / GEN_SMALL_PER) % 4 == 0,
+              "sum_parts_kernel takes partials four at a time");
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
@@ -1171,6 +1193,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
   bytes += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
+  bytes += al256((size_t)(GEN_NSPLIT_SMALL / GEN_SMALL_PER) * (4 * H * 32 + 4 * H + 32) * 4);
   bytes += al256(16);                                          // scale
   return bytes;
 }
@@ -1214,6 +1237,8 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   ws += al256((size_t)GEN_NSPLIT * 32 * D * 4);
   float* psm = reinterpret_cast<float*>(ws);
   ws += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
+  float* psm2 = reinterpret_cast<float*>(ws);   // range sums of the small partials
+  ws += al256((size_t)(GEN_NSPLIT_SMALL / GEN_SMALL_PER) * (4 * H * 32 + 4 * H + 32) * 4);
   float* scale = reinterpret_cast<float*>(ws);
 
   hipError_t e = hipSuccess;
@@ -1254,8 +1279,12 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   gen_bwd_small_kernel<<<dim3(GEN_NSPLIT_SMALL), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
   const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
   sum_parts_kernel<<<dim3((unsigned)((nw1 + 255) / 256)), 256, 0, stream>>>(nw1, GEN_NSPLIT, pw1, dW1);
-  // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout)
-  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256)), 256, 0, stream>>>(nsm, GEN_NSPLIT_SMALL, psm, psm);
+  // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout),
+  // summed in two steps: ranges of GEN_SMALL_PER partials, then the ranges
+  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256), GEN_NSPLIT_SMALL / GEN_SMALL_PER), 256, 0, stream>>>(
+      nsm, GEN_SMALL_PER, psm, psm2);
+  sum_parts_kernel<<<dim3((unsigned)((nsm + 255) / 256)), 256, 0, stream>>>(nsm, GEN_NSPLIT_SMALL / GEN_SMALL_PER,
+                                                                             psm2, psm);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = hipMemcpyAsync(dW2, psm, (size_t)4 * H * 32 * 4, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(db2, psm + 4 * H * 32, (size_t)4 * H * 4, hipMemcpyDeviceToDevice, stream);
