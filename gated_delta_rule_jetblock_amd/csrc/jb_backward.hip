@@ -734,6 +734,9 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
           Y[rt][i] = sBeta[r] * acc;
         }
       }
+      // the value loads and the conv stay ahead of the solve: interleaved with
+      // it by the scheduler, the whole column pass takes half again as long
+      __builtin_amdgcn_sched_barrier(0);
       block_solve<OP, LC, LLI>(Y, sAn, sLi);  // U0
       // U = U0 - W M0 (M0 tile in accumulator layout)
       f4_t m0[RT], tw[4];
@@ -1083,7 +1086,7 @@ __global__ __launch_bounds__(256) void gen_bwd_dp_kernel(int64_t n_tok, int H, c
 // its 32 dW1 sums; the range's dp rows are staged in LDS 64 at a time.
 __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, const bf16_t* x, const bf16_t* W1,
                                                         const float* dp, float* dx, float* part_w1) {
-  __shared__ float sdp[64][33];
+  __shared__ __attribute__((aligned(16))) float sdp[64][32];  // read as row broadcasts, 16 bytes at a time
   const int d = blockIdx.x * 256 + threadIdx.x, sp = blockIdx.y, nsp = gridDim.y;
   const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
   const bool ok = d < D;
@@ -1112,10 +1115,13 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
         if (i0 + j >= nt) break;
         float s = 0.f;
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const float g = sdp[i0 + j][u];
-          s += w[u] * g;
-          acc[u] += g * xv[j];
+        for (int u = 0; u < 32; u += 4) {
+          const float4 g = *reinterpret_cast<const float4*>(&sdp[i0 + j][u]);
+          s += w[u] * g.x + w[u + 1] * g.y + w[u + 2] * g.z + w[u + 3] * g.w;
+          acc[u] += g.x * xv[j];
+          acc[u + 1] += g.y * xv[j];
+          acc[u + 2] += g.z * xv[j];
+          acc[u + 3] += g.w * xv[j];
         }
         if (ok) dx[(tb + i0 + j) * D + d] = s;
       }
