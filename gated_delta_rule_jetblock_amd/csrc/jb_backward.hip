@@ -529,7 +529,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   constexpr int oLi = oAd + C * LAD * 4;
   constexpr int oLiT = oLi + C * LLI * 2;
   constexpr int oU = oLiT + C * LLI * 2;              // union: staging during the dv loop, then dP.E, dS, dB_w
-  constexpr int szStage = 3 * C * LKW * 2;
+  constexpr int szStage = 4 * C * LKW * 2;
   constexpr int szPost = 2 * C * LC * 2 + C * LDK * 2;
   constexpr int total = oU + (szStage > szPost ? szStage : szPost);
   static_assert(total <= 160 * 1024, "LDS budget");
@@ -558,6 +558,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   OP* sUb = reinterpret_cast<OP*>(smem + oU);        // [C][LKW] U of the current dv block
   OP* sU0b = sUb + C * LKW;                          // U0
   OP* sBub = sU0b + C * LKW;                         // dB_u
+  OP* sdOb = sBub + C * LKW;                         // s dO
   OP* sdPE = reinterpret_cast<OP*>(smem + oU);       // after the loop: [C][LC] dP . E
   OP* sdS = sdPE + C * LC;                           // [C][LC] dS
   OP* sdBw = sdS + C * LC;                           // [C][LDK] dB_w
@@ -700,6 +701,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
                      : a.conv_in ? a.conv_in + ((int64_t)b * 3 * H + h) * DV : a.v;
   const __amdgpu_buffer_rsrc_t rVh = make_rsrc(halo, (c > 0 || a.conv_in) ? 2 * rowv + DV * 2 : 0u);
   const __amdgpu_buffer_rsrc_t rdU = make_rsrc(dUg, (uint32_t)(n - 1) * rowf + DV * 4);
+  const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dO, (uint32_t)(n - 1) * rowf + DV * 4);
   const __amdgpu_buffer_rsrc_t rdvc = make_rsrc(a.dvc + tokbase * DV, (uint32_t)(n - 1) * rowf + DV * 4);
   const __amdgpu_buffer_rsrc_t rM0 = make_rsrc(M0, (uint32_t)(DK * DV * 4));
 #pragma unroll 1
@@ -759,6 +761,12 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dB[rt][i] = buf_load_f32(rdU, of + (uint32_t)(rt * 16 + i) * rowf);
       block_solve_t<LC, LLI>(dB, sAnT, sLiT);
+      // this column of dO, staged in LDS for the dP jobs
+      float xo[4][4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xo[rt][i] = buf_load_f32(rdO, of + (uint32_t)(rt * 16 + i) * rowf);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -768,6 +776,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
           sUb[r * LKW + wave * 16 + m16] = (OP)u;
           sU0b[r * LKW + wave * 16 + m16] = (OP)Y[rt][i];
           sBub[r * LKW + wave * 16 + m16] = (OP)dB[rt][i];
+          sdOb[r * LKW + wave * 16 + m16] = (OP)(s * xo[rt][i]);
           // dV' = b dB_u (unscaled), and b's share dB_u . V'
           buf_store(rdvc, sBeta[r] * dB[rt][i] * inv, (int)(of + (uint32_t)(rt * 16 + i) * rowf), 0);
           const float db = sum16(dB[rt][i] * Vp[rt][i]);
@@ -786,7 +795,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
           const int which = job >= 10, t = job - 10 * which;
           const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
           if (which == 0)
-            mma(accCC[jj], glb_frag<OP>(dO, rowld, ti * 16, k0, s, n), lds_frag<OP>(sUb, LKW, tj * 16, ks * 32));
+            mma(accCC[jj], lds_frag<OP>(sdOb, LKW, ti * 16, ks * 32), lds_frag<OP>(sUb, LKW, tj * 16, ks * 32));
           else
             mma(accCC[jj], lds_frag<OP>(sBub, LKW, ti * 16, ks * 32), lds_frag<OP>(sU0b, LKW, tj * 16, ks * 32));
         }
