@@ -804,15 +804,33 @@ __global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const int* 
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) M[rt][i] = S0 ? S0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
-  for (int s = 0; s < nseg_b; ++s) {
+  // D_s and Phi_s do not depend on M: with dk <= 96 two register sets take
+  // turns, the loads of step s + 1 in flight while step s multiplies, so the
+  // chain pays about one memory latency instead of one per segment (with
+  // dk = 128 two sets do not fit the registers and each step loads its own)
+  auto load_step = [&](int s, float (&d)[RT][4], float (&pm)[RT][KB][8]) {
+    const float* D = Dsum + (bh * nseg + s) * DK * DV;
+    const float* P = Phi + (bh * nseg + s) * DK * DK;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[rt][i] = D[(rt * 16 + 4 * g4 + i) * DV + col];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float* prow = P + (rt * 16 + m16) * DK + kb * 32 + 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { pm[rt][kb][j] = prow[j]; pm[rt][kb][4 + j] = prow[16 + j]; }
+      }
+    }
+  };
+  auto store_m = [&](int s) {
     float* dst = Mstart + (bh * nseg + s) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[rt][i];
-    if (s == nseg_b - 1) break;
-    const float* D = Dsum + (bh * nseg + s) * DK * DV;
-    const float* P = Phi + (bh * nseg + s) * DK * DK;
+  };
+  auto step = [&](const float (&d)[RT][4], const float (&pm)[RT][KB][8]) {
     float bv[KB][8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -822,16 +840,33 @@ __global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const int* 
     for (int rt = 0; rt < RT; ++rt) {
       f4_t acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = D[(rt * 16 + 4 * g4 + i) * DV + col];
+      for (int i = 0; i < 4; ++i) acc[i] = d[rt][i];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        float av[8];
-        const float* prow = P + (rt * 16 + m16) * DK + kb * 32 + 4 * g4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { av[j] = prow[j]; av[4 + j] = prow[16 + j]; }
-        split_mma(acc, av, bv[kb], OP());
-      }
+      for (int kb = 0; kb < KB; ++kb) split_mma(acc, pm[rt][kb], bv[kb], OP());
       M[rt] = acc;
+    }
+  };
+  const int last = nseg_b - 1;  // M_last is stored, not advanced
+  if constexpr (DK <= 96) {
+    float dA[RT][4], pA[RT][KB][8], dB[RT][4], pB[RT][KB][8];
+    if (last > 0) load_step(0, dA, pA);
+    for (int s = 0;; s += 2) {
+      store_m(s);
+      if (s == last) break;
+      if (s + 1 < last) load_step(s + 1, dB, pB);
+      step(dA, pA);
+      store_m(s + 1);
+      if (s + 1 == last) break;
+      if (s + 2 < last) load_step(s + 2, dA, pA);
+      step(dB, pB);
+    }
+  } else {
+    float d[RT][4], pm[RT][KB][8];
+    for (int s = 0;; ++s) {
+      store_m(s);
+      if (s == last) break;
+      load_step(s, d, pm);
+      step(d, pm);
     }
   }
 }
