@@ -37,10 +37,12 @@ template <> struct GenFrag<bf16_t> {
   __device__ __forceinline__ void mma(f4_t& acc, const GenFrag& b) const {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b.v, acc, 0, 0, 0);
   }
+  __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
 };
 template <> struct GenFrag<float> {
   float v[8];
   __device__ __forceinline__ void load(const float* p, bool valid) { load8(p, valid, v); }
+  __device__ __forceinline__ float get(int j) const { return v[j]; }
   __device__ __forceinline__ void mma(f4_t& acc, const GenFrag& b) const {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], b.v[j], acc, 0, 0, 0);
@@ -50,33 +52,24 @@ template <> struct GenFrag<float> {
 // One workgroup: 16*NT tokens, NW wavefronts.  hidden^T (32 x tokens) =
 // W1 (32 x D) x^T; wave w accumulates the K range [w D/NW, (w+1) D/NW) and
 // the partials meet in LDS.  Few tokens per workgroup (decode) use many waves
-// so that each wave's chain of dependent loads stays short.
+// so that each wave's chain of dependent loads stays short.  The second
+// layer, taps (tokens x 4H) = SiLU(hidden) W2^T, runs on the fp32 matrix
+// cores, 16 x 16 tiles with the 32 hidden units as K.
 template <typename IO, int NT, int NW>
-__global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, const IO* x, const IO* W1,
-                                                      const IO* b1, const IO* W2, const IO* b2, float* taps,
-                                                      float* pre_out) {
+__global__ __launch_bounds__(NW * 64, NT == 4 && sizeof(IO) == 2 ? 4 : 1) void gen_kernel(int64_t n, int D, int HK, const IO* x,
+                                                                      const IO* W1, const IO* b1, const IO* W2,
+                                                                      const IO* b2, float* taps, float* pre_out) {
   constexpr int NTOK = 16 * NT;
   constexpr int NTHREADS = NW * 64;
-  __shared__ float red[NW][G][NTOK];
+  constexpr int HALF = NW / 2;
+  static_assert(NW % 2 == 0, "the cross-wave sum pairs the waves");
+  __shared__ float red[HALF][G][NTOK];
   __shared__ float hid[NTOK][G + 1];
-  __shared__ float w2s[MAX_HK][G + 1];
-  __shared__ float b2s[MAX_HK];
   __shared__ float b1s[G];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * NTOK;
-
-  // second-layer weights and the biases first, so that their loads overlap
-  // the first layer's instead of forming a second round of memory latency
-  constexpr int WPT = (MAX_HK * G + NTHREADS - 1) / NTHREADS;
-  float w2r[WPT];
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int e = tid + i * NTHREADS;
-    w2r[i] = e < HK * G ? to_f32<IO>(W2[e]) : 0.f;
-  }
-  const float b2r = (tid < HK && b2) ? to_f32<IO>(b2[tid]) : 0.f;
   const float b1r = (tid < G && b1) ? to_f32<IO>(b1[tid]) : 0.f;
 
   f4_t acc[2][NT];
@@ -110,38 +103,62 @@ __global__ __launch_bounds__(NW * 64) void gen_kernel(int64_t n, int D, int HK, 
 #pragma unroll
         for (int t = 0; t < NT; ++t) A[s][u].mma(acc[u][t], Bt[s][t]);  // zero fragments past kend add nothing
   }
-  // lane holds hidden^T[u*16 + 4g + i][t*16 + m16]
+  // lane holds hidden^T[u*16 + 4g + i][t*16 + m16].  Cross-wave sum in a
+  // fixed order: waves HALF.. store, waves 0..HALF-1 add theirs, then the
+  // HALF slots are summed.
+  if (wave >= HALF) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][u * 16 + 4 * g4 + i][t * 16 + m16] = acc[u][t][i];
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int e = tid + i * NTHREADS;
-    if (e < HK * G) w2s[e / G][e % G] = w2r[i];
+        for (int i = 0; i < 4; ++i) red[wave - HALF][u * 16 + 4 * g4 + i][t * 16 + m16] = acc[u][t][i];
   }
-  if (tid < HK) b2s[tid] = b2r;
   if (tid < G) b1s[tid] = b1r;
+  __syncthreads();
+  if (wave < HALF) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][u * 16 + 4 * g4 + i][t * 16 + m16] += acc[u][t][i];
+  }
   __syncthreads();
   for (int e = tid; e < G * NTOK; e += NTHREADS) {
     const int u = e / NTOK, t = e % NTOK;
     float hsum = b1s[u];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) hsum += red[w][u][t];
+    for (int w = 0; w < HALF; ++w) hsum += red[w][u][t];
     hid[t][u] = hsum / (1.0f + expf(-hsum));  // SiLU
     if (pre_out && n0 + t < n) pre_out[(n0 + t) * G + u] = hsum;  // for the backward pass
   }
   __syncthreads();
-  for (int e = tid; e < NTOK * HK; e += NTHREADS) {
-    const int t = e / HK, r = e % HK;
-    const int64_t tok = n0 + t;
-    if (tok >= n) continue;
-    float s = b2s[r];
+  // taps tile (rt, ct): rows n0 + 16 rt.., taps 16 ct..; lane supplies
+  // hidden row 16 rt + m16 and W2 row 16 ct + m16 at K = 8g .. 8g + 7
+  const int nct = (HK + 15) / 16;
+  for (int tile = wave; tile < NT * nct; tile += NW) {
+    const int rt = tile / nct, ct = tile % nct;
+    const int r = ct * 16 + m16;
+    const bool rv = r < HK;
+    GenFrag<IO> w2f;
+    w2f.load(W2 + (int64_t)min(r, HK - 1) * G + 8 * g4, rv);
+    GenFrag<float> hf;
 #pragma unroll
-    for (int u = 0; u < G; ++u) s += w2s[r][u] * hid[t][u];
-    taps[tok * HK + r] = s;
+    for (int j = 0; j < 8; ++j) hf.v[j] = hid[rt * 16 + m16][8 * g4 + j];
+    float wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = w2f.get(j);
+    f4_t tp = zero4();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tp = __builtin_amdgcn_mfma_f32_16x16x4f32(hf.v[j], wv[j], tp, 0, 0, 0);
+    // lane holds taps[n0 + 16 rt + 4g + i][16 ct + m16]
+    const float bias = (rv && b2) ? to_f32<IO>(b2[r]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tok = n0 + rt * 16 + 4 * g4 + i;
+      if (tok < n && rv) taps[tok * HK + r] = tp[i] + bias;
+    }
   }
 }
 
