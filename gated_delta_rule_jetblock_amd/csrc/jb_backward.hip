@@ -38,7 +38,8 @@ struct BwdArgs {
   const float* dout;      // [B][T][H][DV]
   const float* dS_final;  // [B][H][DK][DV] or NULL
   const float* scale;     // [0] = s, [1] = 1/s
-  const float* Mck;       // [B][H][nchunks][DK][DV]: the state entering each chunk
+  const _Float16* Mck;    // [B][H][nchunks][DV/16][DK/16][64][4] fp16: the state entering each chunk, in
+                          // accumulator tiles (lane l: rows 4 (l / 16) .. + 3 of column l % 16)
   float* dMck;            // [B][H][nchunks][DK][DV]: s x the gradient of the state leaving each chunk
   float* dU;              // [B][T][H][DV]: s x dU
   float* dS0;             // [B][H][DK][DV]
@@ -419,8 +420,8 @@ __device__ __forceinline__ void block_solve_t(f4_t (&Y)[4], const _Float16* sAnT
 }
 
 // dO M0^T and dU M0^T of every chunk (C x DK each, reduced over dv) and the
-// chunk-end gate term sum(dM . M0).  grid (nchunks, H, B), 8 waves: M0 is
-// read once into LDS as fp16 (its rows are the B operand of both products),
+// chunk-end gate term sum(dM . M0).  grid (nchunks, H, B), 8 waves: M0 (kept
+// in fp16) is read once into LDS (its rows are the B operand of both products),
 // dM alongside it for the gate term; wave w then forms row tile w % 4 of
 // dO M0^T (w < 4) or of dU M0^T, all DK columns, its A operand streamed from
 // global memory.  No operand is read twice, and two workgroups share a
@@ -431,8 +432,8 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
   constexpr int LDM = DV + 8;              // fp16 row stride of the staged M0
   constexpr int CT = DK / 16;              // column tiles
   constexpr int KSTEP = DV / 32;           // 32-deep steps over dv
-  constexpr int NV4 = DK * DV / 4 / NTHR;  // float4s of M0 per thread
-  constexpr int R = NV4 % 6 == 0 ? 6 : NV4 % 4 == 0 ? 4 : 1;  // float4s per staging round
+  constexpr int NV4 = DK * DV / 4 / NTHR;  // groups of four M0 (and dM) elements per thread
+  constexpr int R = NV4 % 6 == 0 ? 6 : NV4 % 4 == 0 ? 4 : 1;  // groups per staging round
   static_assert(DK * DV % (4 * NTHR) == 0 && NV4 % R == 0, "whole float4s per thread");
   __shared__ __attribute__((aligned(16))) OP sM0[DK * LDM];
   __shared__ float sg[NWAVE];
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
   const int64_t bh = (int64_t)b * H + h;
   const int t0 = c * C, n = min(C, T - t0);
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
-  const float4* M0 = reinterpret_cast<const float4*>(a.Mck + ((bh * a.nchunks + c) * DK) * DV);
+  const uint2* M0 = reinterpret_cast<const uint2*>(a.Mck + ((bh * a.nchunks + c) * DK) * DV);  // a lane's 4 fp16
   const float4* dMC = reinterpret_cast<const float4*>(a.dMck + ((bh * a.nchunks + c) * DK) * DV);
 
   // this wave's A operand, 16 rows of dO (scaled) or of dU, issued first so
@@ -459,32 +460,38 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
     ra[ks][1] = *reinterpret_cast<const float4*>(A + ks * 32 + 16);
   }
 
+  // M0 tiles (lane groups of 4 rows) into LDS rows
+#pragma unroll
+  for (int j0 = 0; j0 < NV4; j0 += R) {
+    uint2 m[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) m[j] = M0[(j0 + j) * NTHR + tid];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int e = (j0 + j) * NTHR + tid, tile = e >> 6, ln = e & 63;
+      const int row = (tile % (DK / 16)) * 16 + 4 * (ln >> 4), col = (tile / (DK / 16)) * 16 + (ln & 15);
+      const half4_t hv = __builtin_bit_cast(half4_t, m[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sM0[(row + i) * LDM + col] = hv[i];
+    }
+  }
+  lds_barrier();  // the A loads stay in flight
+  // the gate term: dM rows (fp32, row-major) against the staged M0
   float part = 0.f;
 #pragma unroll
   for (int j0 = 0; j0 < NV4; j0 += R) {
-    float4 m[R], d[R];
+    float4 d[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      m[j] = M0[(j0 + j) * NTHR + tid];
-      d[j] = dMC[(j0 + j) * NTHR + tid];
-    }
+    for (int j = 0; j < R; ++j) d[j] = dMC[(j0 + j) * NTHR + tid];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int e = (j0 + j) * NTHR + tid;
-      part += m[j].x * d[j].x + m[j].y * d[j].y + m[j].z * d[j].z + m[j].w * d[j].w;
-      const half4_t hv = {(OP)m[j].x, (OP)m[j].y, (OP)m[j].z, (OP)m[j].w};
-      *reinterpret_cast<half4_t*>(sM0 + (e / (DV / 4)) * LDM + (e % (DV / 4)) * 4) = hv;
+      const half4_t hv = *reinterpret_cast<const half4_t*>(sM0 + (e / (DV / 4)) * LDM + (e % (DV / 4)) * 4);
+      part += (float)hv[0] * d[j].x + (float)hv[1] * d[j].y + (float)hv[2] * d[j].z + (float)hv[3] * d[j].w;
     }
   }
   part = wave_sum(part);
   if (lane == 0) sg[wave] = part;
-  lds_barrier();  // the A loads stay in flight
-  if (tid == 0) {
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) tot += sg[w];
-    a.dgC[bh * a.nchunks + c] = tot;
-  }
 
   f4_t acc[CT];
 #pragma unroll
@@ -503,6 +510,13 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
   for (int j = 0; j < CT; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i * DK + j * 16] = acc[j][i];
+  lds_barrier();  // sg
+  if (tid == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) tot += sg[w];
+    a.dgC[bh * a.nchunks + c] = tot;
+  }
 }
 
 // grid (nchunks, H, B), 8 waves.  The dv columns are taken 128 at a time:
@@ -569,9 +583,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   const int64_t bh = (int64_t)b * H + h;
   const int t0 = c * C, n = min(C, T - t0);
   const float s = a.scale[0], inv = a.scale[1];
-  const int64_t rowld = (int64_t)H * DV;
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
-  const float* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+  const _Float16* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
   const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
   const float* dO = a.dout + tokbase * DV;
   const float* dUg = a.dU + tokbase * DV;
@@ -703,7 +716,6 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rdU = make_rsrc(dUg, (uint32_t)(n - 1) * rowf + DV * 4);
   const __amdgpu_buffer_rsrc_t rdO = make_rsrc(dO, (uint32_t)(n - 1) * rowf + DV * 4);
   const __amdgpu_buffer_rsrc_t rdvc = make_rsrc(a.dvc + tokbase * DV, (uint32_t)(n - 1) * rowf + DV * 4);
-  const __amdgpu_buffer_rsrc_t rM0 = make_rsrc(M0, (uint32_t)(DK * DV * 4));
 #pragma unroll 1
   for (int kb = 0; kb < NKB; ++kb) {
     if (wave < KW / 16) {
@@ -742,10 +754,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
       block_solve<OP, LC, LLI>(Y, sAn, sLi);  // U0
       // U = U0 - W M0 (M0 tile in accumulator layout)
       f4_t m0[RT], tw[4];
+      // M0 tiles of this column tile: one 8-byte load per row tile
+      const half4_t* m0t = reinterpret_cast<const half4_t*>(M0) + (kb * (KW / 16) + wave) * RT * 64 + lane;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt) {
+        const half4_t hv = m0t[rt * 64];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m0[rt][i] = buf_load_f32(rM0, (uint32_t)(((rt * 16 + 4 * g4 + i) * DV + col) * 4));
+        for (int i = 0; i < 4; ++i) m0[rt][i] = (float)hv[i];
+      }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) tw[rt] = zero4();
 #pragma unroll
@@ -1200,7 +1216,8 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const size_t n = (size_t)B * T;
   const size_t nch = (size_t)p.nchunks;
   size_t bytes = al256(prefill_workspace_bytes(p));           // taps, segment buffers (the forward pass)
-  bytes += 2 * al256((size_t)B * H * nch * dk * dv * 4);       // Mck, dMck
+  bytes += al256((size_t)B * H * nch * dk * dv * 2);           // Mck (fp16)
+  bytes += al256((size_t)B * H * nch * dk * dv * 4);           // dMck
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
   bytes += 2 * al256((size_t)B * H * nch * C * dk * 4);        // dO M0^T, dU M0^T per chunk
   bytes += al256((size_t)B * H * nch * 4);                     // the chunk-end gate term
@@ -1226,8 +1243,8 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   char* fws = ws;                                   // taps first, then the segment buffers
   float* taps = reinterpret_cast<float*>(ws);
   ws += al256(prefill_workspace_bytes(p));
-  float* Mck = reinterpret_cast<float*>(ws);
-  ws += al256((size_t)B * H * nch * dk * dv * 4);
+  _Float16* Mck = reinterpret_cast<_Float16*>(ws);
+  ws += al256((size_t)B * H * nch * dk * dv * 2);
   float* dMck = reinterpret_cast<float*>(ws);
   ws += al256((size_t)B * H * nch * dk * dv * 4);
   float* dU = reinterpret_cast<float*>(ws);

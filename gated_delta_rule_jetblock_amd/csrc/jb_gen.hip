@@ -16,7 +16,6 @@
 namespace jb {
 
 constexpr int G = 32;        // generator hidden width
-constexpr int MAX_HK = 128;  // up to 32 heads
 
 // Fragment of 8 contiguous K values (order 8g + j) straight from memory.
 __device__ __forceinline__ void load8(const bf16_t* p, bool valid, bf16x8_t& out) {

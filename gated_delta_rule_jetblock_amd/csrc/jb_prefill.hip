@@ -69,7 +69,7 @@ struct ChunkArgs {
   float* Phi;           // [B][H][nseg][DK][DK]
   void* o;
   float* S_final;
-  float* Mck;           // MODE_CKPT: [B][H][nchunks][DK][DV], the state entering every chunk
+  _Float16* Mck;        // MODE_CKPT: the state entering every chunk, fp16 16x16 tiles (below)
 };
 
 // ------------------------------------------------------------ LDS layout
@@ -338,16 +338,21 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
     if constexpr (MODE == MODE_CKPT) {
-      // the state entering chunk c, for the backward pass
-      float* dst = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+      // the state entering chunk c, for the backward pass, in the fp16 its
+      // products there take as an operand and in accumulator tiles: per chunk
+      // [DV/16][DK/16][64 lanes][4], lane l of tile (ct, rt) holding rows
+      // 16 rt + 4 (l / 16) .. + 3 of column 16 ct + l % 16 (one 8-byte store)
+      _Float16* dst = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
 #pragma unroll
       for (int cw = 0; cw < CPW; ++cw) {
         const int ct = wave + cw * NWAVE;
         if (ct < NCT)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+          for (int rt = 0; rt < RT; ++rt) {
+            const half4_t hv = {(_Float16)Macc[cw][rt][0], (_Float16)Macc[cw][rt][1], (_Float16)Macc[cw][rt][2],
+                                (_Float16)Macc[cw][rt][3]};
+            *reinterpret_cast<half4_t*>(dst + ((ct * RT + rt) * 64 + lane) * 4) = hv;
+          }
       }
     }
 
@@ -1048,7 +1053,7 @@ bool backward_supported(int io, int dk, int dv) {
 
 hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, const float* taps, const void* conv_in, const float* S0,
-                               float* Mck, void* workspace, hipStream_t stream) {
+                               _Float16* Mck, void* workspace, hipStream_t stream) {
   if (p.nchunks == 0) return hipSuccess;
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
