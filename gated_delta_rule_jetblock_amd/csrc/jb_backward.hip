@@ -1106,55 +1106,93 @@ __global__ __launch_bounds__(256) void gen_bwd_dp_kernel(int64_t n_tok, int H, c
   hid[e] = p * sg;
 }
 
-// dx = dp W1 and the partial dW1 = dp^T x of one token range: grid
-// (ceil(D / 256), NSPLIT), thread d holds column d of W1 (32 values) and
-// its 32 dW1 sums; the range's dp rows are staged in LDS 64 at a time.
+// dx = dp W1 and the partial dW1 = dp^T x of one token range, on the fp32
+// matrix cores (16x16x4 products, exact fp32 operands): grid
+// (ceil(D / 128), NSPLIT), 4 waves; wave w owns the two 16-column tiles
+// from d0 = 128 blockIdx.x + 32 w.  The range's dp rows are staged in LDS
+// 64 at a time and read there in both orientations.
 __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, const bf16_t* x, const bf16_t* W1,
                                                         const float* dp, float* dx, float* part_w1) {
-  __shared__ __attribute__((aligned(16))) float sdp[64][32];  // read as row broadcasts, 16 bytes at a time
-  const int d = blockIdx.x * 256 + threadIdx.x, sp = blockIdx.y, nsp = gridDim.y;
+  __shared__ float sdp[64][33];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m16 = lane & 15, g4 = lane >> 4;
+  const int sp = blockIdx.y, nsp = gridDim.y;
   const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
-  const bool ok = d < D;
-  float w[32], acc[32];
+  const int d0 = blockIdx.x * 128 + wave * 32;
+  int dcol[2];
+  bool dok[2];
+  // W1 as the B operand of dx (K index = hidden unit 8g + s), held for the whole range
+  float wb[2][8];
 #pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    w[u] = ok ? bf16_to_f32(W1[(int64_t)u * D + d]) : 0.f;
-    acc[u] = 0.f;
+  for (int dt = 0; dt < 2; ++dt) {
+    dcol[dt] = d0 + dt * 16 + m16;
+    dok[dt] = dcol[dt] < D;
+    const int dc = dok[dt] ? dcol[dt] : 0;  // clamped, then masked
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float w = bf16_to_f32(W1[(int64_t)(8 * g4 + s) * D + dc]);
+      wb[dt][s] = dok[dt] ? w : 0.f;
+    }
   }
+  f4_t aw[2][2];  // dW1 tiles [unit tile][column tile]
+#pragma unroll
+  for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) aw[ut][dt] = zero4();
   for (int64_t tb = t0; tb < t1; tb += 64) {
     const int nt = (int)(t1 - tb < 64 ? t1 - tb : 64);
     __syncthreads();
-    for (int e = threadIdx.x; e < nt * 32; e += 256) sdp[e >> 5][e & 31] = dp[(tb + (e >> 5)) * 32 + (e & 31)];
+    for (int e = tid; e < 64 * 32; e += 256) sdp[e >> 5][e & 31] = (e >> 5) < nt ? dp[(tb + (e >> 5)) * 32 + (e & 31)] : 0.f;
     __syncthreads();
-    // four tokens at a time: their x loads go out together (rows past nt
-    // read row 0 of the block and weigh zero: sdp rows past nt are not used)
-    for (int i0 = 0; i0 < nt; i0 += 4) {
-      float xv[4];
+    for (int b16 = 0; b16 < nt; b16 += 16) {
+      // x rows tb + b16 + 4g + s (the B operand of dW1, K index = token 4g + s)
+      float xv[2][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + j < nt ? i0 + j : 0;
-        xv[j] = ok ? bf16_to_f32(x[(tb + i) * D + d]) : 0.f;
-      }
+      for (int s = 0; s < 4; ++s) {
+        const int64_t tok = tb + b16 + 4 * g4 + s;
+        const int64_t tr = tok < t1 ? tok : t1 - 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (i0 + j >= nt) break;
-        float s = 0.f;
-#pragma unroll
-        for (int u = 0; u < 32; u += 4) {
-          const float4 g = *reinterpret_cast<const float4*>(&sdp[i0 + j][u]);
-          s += w[u] * g.x + w[u + 1] * g.y + w[u + 2] * g.z + w[u + 3] * g.w;
-          acc[u] += g.x * xv[j];
-          acc[u + 1] += g.y * xv[j];
-          acc[u + 2] += g.z * xv[j];
-          acc[u + 3] += g.w * xv[j];
+        for (int dt = 0; dt < 2; ++dt) {
+          const float xx = bf16_to_f32(x[tr * D + (dok[dt] ? dcol[dt] : 0)]);
+          xv[dt][s] = (tok < t1 && dok[dt]) ? xx : 0.f;
         }
-        if (ok) dx[(tb + i0 + j) * D + d] = s;
+      }
+      // dx tiles: A = dp rows b16 + m16 at K = 8g + s
+      float da[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) da[s] = sdp[b16 + m16][8 * g4 + s];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        f4_t o = zero4();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(da[s], wb[dt][s], o, 0, 0, 0);
+        // lane holds dx[tb + b16 + 4g + i][dcol]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t tok = tb + b16 + 4 * g4 + i;
+          if (tok < t1 && dok[dt]) dx[tok * D + dcol[dt]] = o[i];
+        }
+      }
+      // dW1 tiles: A = dp^T rows 16 ut + m16 at K = token 4g + s
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut) {
+        float pa[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) pa[s] = sdp[b16 + 4 * g4 + s][ut * 16 + m16];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s], xv[dt][s], aw[ut][dt], 0, 0, 0);
       }
     }
   }
-  if (ok)
+  // lane holds dW1[16 ut + 4g + i][dcol]
 #pragma unroll
-    for (int u = 0; u < 32; ++u) part_w1[((int64_t)sp * 32 + u) * D + d] = acc[u];
+  for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      if (dok[dt])
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part_w1[((int64_t)sp * 32 + ut * 16 + 4 * g4 + i) * D + dcol[dt]] = aw[ut][dt][i];
 }
 
 // Partial dW2 = dtaps^T hid [4H][32], db2 = sum dtaps, db1 = sum dp over one
@@ -1306,7 +1344,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   // the generator
   gen_bwd_dp_kernel<<<dim3((unsigned)((n * 32 + 255) / 256)), 256, 0, stream>>>(n, H, (const bf16_t*)W2, pre,
                                                                                 dtaps, dp, hid);
-  gen_bwd_x_kernel<<<dim3((D + 255) / 256, GEN_NSPLIT), 256, 0, stream>>>(n, D, (const bf16_t*)x,
+  gen_bwd_x_kernel<<<dim3((D + 127) / 128, GEN_NSPLIT), 256, 0, stream>>>(n, D, (const bf16_t*)x,
                                                                          (const bf16_t*)W1, dp, dx, pw1);
   gen_bwd_small_kernel<<<dim3(GEN_NSPLIT_SMALL), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
   const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
