@@ -51,6 +51,7 @@ struct BwdArgs {
   float* QO;              // [B][H][nchunks][C][DK]: s x dO M0^T per chunk
   float* WO;              // [B][H][nchunks][C][DK]: s x dU M0^T per chunk
   float* dgC;             // [B][H][nchunks]: s x sum(dM . M0) per chunk
+  char* img;              // [B][H][nchunks] chain tiles (ChainImg)
 };
 
 // ------------------------------------------------------------ gradient scale
@@ -91,279 +92,319 @@ __global__ void grad_scale_finish_kernel(const unsigned int* word, float* scale)
   scale[1] = ldexpf(1.f, e);
 }
 
+// raw buffer loads: a wave-uniform resource and a per-lane byte offset; an
+// offset at or beyond the resource's size reads as zero
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ float buf_load_bf16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0));
+}
+
 // ------------------------------------------------------------ chain kernel
 
-// The dv columns of dM are independent, so they are split over CSPLIT
-// workgroups per (sequence, head) when there are more column tiles than
-// waves: each recomputes the chunk-shared tiles and carries its own columns.
-template <int DV>
-constexpr int chain_split() { return DV / 16 > NWAVE ? DV / 16 / NWAVE : 1; }
+// The state-independent tiles the chain needs of every chunk, in the padded
+// LDS layout the chain reads them in (so that they move as one contiguous
+// block): normalised K [C][DK], Q^T [DK][C], -W^T [DK][C], P^T [C][C] (fp16)
+// and gamma, e^{g_C - g} [C] (fp32).  Row strides are padded by 8 elements:
+// 16-byte multiples whose 16 rows of a fragment read fall in distinct banks.
+template <int DK>
+struct ChainImg {
+  static constexpr int LK = DK + 8, LT = C + 8;
+  static constexpr int oKh = 0;
+  static constexpr int oQt = oKh + C * LK * 2;
+  static constexpr int oWt = oQt + DK * LT * 2;
+  static constexpr int oPt = oWt + DK * LT * 2;
+  static constexpr int oGam = oPt + C * LT * 2;
+  static constexpr int oDec = oGam + C * 4;
+  static constexpr int bytes = oDec + C * 4;
+  static_assert(bytes % 16 == 0 && (LK * 2) % 16 == 0 && (LT * 2) % 16 == 0, "16-byte pieces");
+};
 
-// grid (H, B, CSPLIT), 8 waves; wave w of split s owns dv column tiles
-// s NCT/CSPLIT + w, + 8, .. of dM, kept in accumulator registers while the
-// chunks are walked backwards.
-template <int DK, int DV>
-__global__ __launch_bounds__(NTHR, 1) void bwd_chain_kernel(BwdArgs a) {
+// grid (nchunks, H, B), 8 waves: the chain tiles of one chunk, formed in LDS
+// (normalised q and k, the gates, -A and its diagonal-block inverses, W by
+// the blocked solve, the gated causal Q K^T) and written out whole.  Every
+// chunk is independent, so this runs at full occupancy ahead of the chain.
+template <int DK>
+__global__ __launch_bounds__(NTHR) void bwd_tiles_kernel(BwdArgs a) {
   using OP = _Float16;
+  using I = ChainImg<DK>;
   constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36;
-  constexpr int NCT = DV / 16, CSPLIT = chain_split<DV>(), NCTS = NCT / CSPLIT;
-  constexpr int CPW = (NCTS + NWAVE - 1) / NWAVE, RT = DK / 16, KB = DK / 32;
-  // the per-row scalars first: below 64 KB every LDS address is one register
-  // plus an immediate offset
-  constexpr int oScal = 0;
-  constexpr int oKh = oScal + 4 * C * 4;
-  constexpr int oQh = oKh + C * LDK * 2;
-  constexpr int oQt = oQh + C * LDK * 2;
-  constexpr int oWt = oQt + DK * LC * 2;
-  constexpr int oPt = oWt + DK * LC * 2;
-  constexpr int oAn = oPt + C * LC * 2;
+  constexpr int RT = DK / 16, KB = DK / 32;
+  constexpr int oImg = 0;
+  constexpr int oQh = oImg + I::bytes;
+  constexpr int oAn = oQh + C * LDK * 2;
   constexpr int oAd = oAn + C * LC * 2;
   constexpr int oLi = oAd + C * LAD * 4;
-  constexpr int total = oLi + C * LLI * 2;
-  static_assert(total <= 160 * 1024, "LDS budget");
+  constexpr int oScal = oLi + C * LLI * 2;
+  constexpr int total = oScal + 2 * C * 4;
   static_assert(RT <= NWAVE, "one wave per W column tile");
   __shared__ __attribute__((aligned(16))) char smem[total];
-  OP* sKh = reinterpret_cast<OP*>(smem + oKh);   // [C][LDK]  normalised k
-  OP* sQh = reinterpret_cast<OP*>(smem + oQh);   // [C][LDK]  normalised q
-  OP* sQt = reinterpret_cast<OP*>(smem + oQt);   // [DK][LC]  its transpose
-  OP* sWt = reinterpret_cast<OP*>(smem + oWt);   // [DK][LC]  -W^T
-  OP* sPt = reinterpret_cast<OP*>(smem + oPt);   // [C][LC]   P^T
-  OP* sAn = reinterpret_cast<OP*>(smem + oAn);   // [C][LC]   -A
+  char* img = smem + oImg;
+  OP* sKh = reinterpret_cast<OP*>(img + I::oKh);   // [C][LK]
+  OP* sQt = reinterpret_cast<OP*>(img + I::oQt);   // [DK][LT]
+  OP* sWt = reinterpret_cast<OP*>(img + I::oWt);   // [DK][LT]
+  OP* sPt = reinterpret_cast<OP*>(img + I::oPt);   // [C][LT]
+  float* sGam = reinterpret_cast<float*>(img + I::oGam);
+  float* sDec = reinterpret_cast<float*>(img + I::oDec);
+  OP* sQh = reinterpret_cast<OP*>(smem + oQh);     // [C][LDK]
+  OP* sAn = reinterpret_cast<OP*>(smem + oAn);     // [C][LC] -A
   float* sAd = reinterpret_cast<float*>(smem + oAd);
   OP* sLi = reinterpret_cast<OP*>(smem + oLi);
   float* sG = reinterpret_cast<float*>(smem + oScal);
-  float* sGam = sG + C;
-  float* sBeta = sG + 2 * C;
-  float* sDec = sG + 3 * C;
+  float* sBeta = sG + C;
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = a.H, T = a.T;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int t0 = c * C, n = min(C, T - t0);
+  const int64_t bh = (int64_t)b * H + h;
+
+  // P^T below the block diagonal stays zero
+  for (int e = tid; e < C * C; e += NTHR) {
+    const int r = e / C, cc = e % C;
+    if ((r >> 4) > (cc >> 4)) sPt[r * I::LT + cc] = (OP)0.f;
+  }
+  if (tid < PRO_THR) {
+    Prologue<DK, bf16_t> pr;
+    pr.load_global(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n);
+    pr.finish(true);
+#pragma unroll
+    for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
+      const int d = pr.part * Prologue<DK, bf16_t>::E + e;
+      const OP qh = (OP)pr.qv[e];
+      sKh[pr.row * I::LK + d] = (OP)pr.kv[e];
+      sQh[pr.row * LDK + d] = qh;
+      sQt[d * I::LT + pr.row] = qh;
+    }
+  }
+  if (wave == GATE_WAVE) {
+    const bool valid = lane < n;
+    const int64_t gidx = ((int64_t)b * T + t0 + min(lane, n - 1)) * H + h;  // clamped, then masked
+    const float al0 = a.alpha[gidx], be0 = a.beta[gidx];
+    const float al = valid ? al0 : 1.f;
+    const float be = valid ? be0 : 0.f;
+    const float g = chunk_gate_scan(al);
+    const float gC = __shfl(g, C - 1, WAVE);
+    sG[lane] = g;
+    sGam[lane] = fast_exp2(g);
+    sBeta[lane] = be;
+    sDec[lane] = fast_exp2(gC - g);
+  }
+  __syncthreads();
+
+  // -A and its diagonal blocks (lower tiles), P^T (upper tiles)
+  for (int job = wave; job < 20; job += NWAVE) {
+    const int which = job >= 10, t = job - 10 * which;
+    const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
+    f4_t acc = zero4();
+    if (which == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma(acc, lds_frag<OP>(sKh, I::LK, ti * 16, kb * 32), lds_frag<OP>(sKh, I::LK, tj * 16, kb * 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
+        const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
+        sAn[r * LC + cc] = (OP)(-av);
+        if (ti == tj) sAd[r * LAD + m16] = av;
+      }
+    } else {
+      // P^T block (tj, ti): keys of block tj against queries of block ti
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        mma(acc, lds_frag<OP>(sKh, I::LK, tj * 16, kb * 32), lds_frag<OP>(sQh, LDK, ti * 16, kb * 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tj * 16 + 4 * g4 + i, cc = ti * 16 + m16;
+        sPt[r * I::LT + cc] = (OP)(cc >= r ? fast_exp2(sG[cc] - sG[r]) * acc[i] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // diagonal-block inverses, one column per lane (as in the forward pass)
+    const int base = (lane >> 4) * 16, jc = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == jc) ? 1.f : 0.f;
+      const float* arow = sAd + (base + i) * LAD;
+#pragma unroll
+      for (int k4 = 0; k4 < i; k4 += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(arow + k4);
+        acc -= av.x * x[k4];
+        if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
+        if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
+        if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
+      }
+      x[i] = acc;
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sLi[(base + i) * LLI + jc] = (OP)x[i];
+      sLi[(base + i) * LLI + 16 + jc] = (OP)0.f;
+    }
+  }
+  __syncthreads();
+
+  if (wave < RT) {
+    // W column tile `wave`, stored as -W^T
+    f4_t Y[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * g4 + i;
+        Y[rb][i] = sBeta[r] * sGam[r] * (float)sKh[r * I::LK + wave * 16 + m16];
+      }
+    block_solve<OP, LC, LLI>(Y, sAn, sLi);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sWt[(wave * 16 + m16) * I::LT + rb * 16 + 4 * g4 + i] = (OP)(-Y[rb][i]);
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(a.img + (bh * a.nchunks + c) * I::bytes);
+  for (int e = tid; e < I::bytes / 16; e += NTHR) dst[e] = reinterpret_cast<const uint4*>(img)[e];
+}
+
+// grid (H, B), one wave per dv column tile (DV / 16 waves); wave w owns
+// column tile w of dM, kept in accumulator registers while the chunks are
+// walked backwards.  A chunk's tiles (bwd_tiles_kernel) stream into one of
+// two LDS buffers while the previous chunk is worked, and its dO tile into
+// registers, so a chunk costs one barrier and its products.
+template <int DK, int DV>
+__global__ __launch_bounds__(DV / 16 * 64, 1) void bwd_chain_kernel(BwdArgs a) {
+  using OP = _Float16;
+  using I = ChainImg<DK>;
+  constexpr int NW = DV / 16, RT = DK / 16, KB = DK / 32;
+  static_assert(NW <= 16, "one wave per column tile");
+  __shared__ __attribute__((aligned(16))) char smem[2 * I::bytes];
 
   const int h = blockIdx.x, b = blockIdx.y, H = a.H, T = a.T;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * H + h;
   const float s = a.scale[0];
-  const int64_t rowld = (int64_t)H * DV;
+  const int col = wave * 16 + m16;
 
-  for (int e = tid; e < C * C; e += NTHR) {
-    const int r = e / C, cc = e % C;
-    if ((r >> 4) > (cc >> 4)) sPt[r * LC + cc] = (OP)0.f;  // below the block diagonal: never written
-  }
-  f4_t dM[CPW][RT];
+  f4_t dM[RT];
 #pragma unroll
-  for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int i = 0; i < 4; ++i)
+      dM[rt][i] = a.dS_final ? s * a.dS_final[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
+
+  // dO, dU and dM rows through buffer resources: byte offsets are a 32-bit
+  // lane part (row 4g, this column) plus a wave-uniform row part, and rows
+  // past the chunk read zero / drop their stores
+  const uint32_t rowb = (uint32_t)(H * DV * 4);
+  const int ov = (int)(4 * g4 * rowb) + col * 4, om = (4 * g4 * DV + col) * 4;
+  // chunk cc's tiles into LDS buffer cc & 1, its dO tile (accumulator layout, scaled) into dOn
+  f4_t dOn[4];
+  auto issue = [&](int cc) {
+    const char* src = a.img + (bh * a.nchunks + cc) * I::bytes;
+    char* dstl = smem + (cc & 1) * I::bytes;
+    for (int j = wave; j * 64 < I::bytes / 16; j += NW) {
+      const int p = j * 64 + lane;
+      if (p < I::bytes / 16) dma16(src + p * 16, dstl + j * 64 * 16);
+    }
+    const int t0 = cc * C, n = min(C, T - t0);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.dout + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rt * 16 + 4 * g4 + i;
-        dM[cw][rt][i] = (ct < (int)(blockIdx.z + 1) * NCTS && a.dS_final) ? s * a.dS_final[(bh * DK + row) * DV + ct * 16 + m16] : 0.f;
-      }
-  }
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dOn[rt][i] = s * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rO, ov, (int)((rt * 16 + i) * rowb), 0));
+  };
+  if (a.nchunks > 0) issue(a.nchunks - 1);
 
   for (int c = a.nchunks - 1; c >= 0; --c) {
     const int t0 = c * C, n = min(C, T - t0);
-    const float* dO = a.dout + (((int64_t)b * T + t0) * H + h) * DV;
-    // this chunk's dO tiles, issued first (accumulator layout)
-    f4_t dOr[CPW][4];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile transfers and dO loads have landed
+    __syncthreads();                // ... and every other wave's; the other buffer is free
+    f4_t dOr[4];
 #pragma unroll
-    for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rt * 16 + 4 * g4 + i;
-          // clamped row and column, then masked: the loads issue without branches
-          const int ctl = (int)(blockIdx.z + 1) * NCTS;
-          const float x = dO[min(row, n - 1) * rowld + min(ct, ctl - 1) * 16 + m16];
-          dOr[cw][rt][i] = (ct < ctl && row < n) ? s * x : 0.f;
-        }
-    }
-    __syncthreads();  // the previous chunk's column phase is done with the tiles
-
-    if (tid < PRO_THR) {
-      Prologue<DK, bf16_t> pr;
-      pr.load_global(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n);
-      pr.finish(true);
-#pragma unroll
-      for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
-        const int d = pr.part * Prologue<DK, bf16_t>::E + e;
-        const OP kh = (OP)pr.kv[e], qh = (OP)pr.qv[e];
-        sKh[pr.row * LDK + d] = kh;
-        sQh[pr.row * LDK + d] = qh;
-        sQt[d * LC + pr.row] = qh;
-      }
-    }
-    if (wave == GATE_WAVE) {
-      const bool valid = lane < n;
-      const int64_t gidx = ((int64_t)b * T + t0 + min(lane, n - 1)) * H + h;  // clamped, then masked
-      const float al0 = a.alpha[gidx], be0 = a.beta[gidx];
-      const float al = valid ? al0 : 1.f;
-      const float be = valid ? be0 : 0.f;
-      const float g = chunk_gate_scan(al);
-      const float gC = __shfl(g, C - 1, WAVE);
-      sG[lane] = g;
-      sGam[lane] = fast_exp2(g);
-      sBeta[lane] = be;
-      sDec[lane] = fast_exp2(gC - g);
-    }
-    __syncthreads();
-
-    // -A and its diagonal blocks (lower tiles), P^T (upper tiles)
-    for (int job = wave; job < 20; job += NWAVE) {
-      const int which = job >= 10, t = job - 10 * which;
-      const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
-      f4_t acc = zero4();
-      if (which == 0) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          mma(acc, lds_frag<OP>(sKh, LDK, ti * 16, kb * 32), lds_frag<OP>(sKh, LDK, tj * 16, kb * 32));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
-          const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
-          sAn[r * LC + cc] = (OP)(-av);
-          if (ti == tj) sAd[r * LAD + m16] = av;
-        }
-      } else {
-        // P^T block (tj, ti): keys of block tj against queries of block ti
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          mma(acc, lds_frag<OP>(sKh, LDK, tj * 16, kb * 32), lds_frag<OP>(sQh, LDK, ti * 16, kb * 32));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = tj * 16 + 4 * g4 + i, cc = ti * 16 + m16;
-          sPt[r * LC + cc] = (OP)(cc >= r ? fast_exp2(sG[cc] - sG[r]) * acc[i] : 0.f);
-        }
-      }
-    }
-    __syncthreads();
-
-    if (wave == 0) {
-      // diagonal-block inverses, one column per lane (as in the forward pass)
-      const int base = (lane >> 4) * 16, jc = lane & 15;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == jc) ? 1.f : 0.f;
-        const float* arow = sAd + (base + i) * LAD;
-#pragma unroll
-        for (int k4 = 0; k4 < i; k4 += 4) {
-          const float4 av = *reinterpret_cast<const float4*>(arow + k4);
-          acc -= av.x * x[k4];
-          if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
-          if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
-          if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
-        }
-        x[i] = acc;
-        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sLi[(base + i) * LLI + jc] = (OP)x[i];
-        sLi[(base + i) * LLI + 16 + jc] = (OP)0.f;
-      }
-    }
-    __syncthreads();
-
-    if (wave < RT) {
-      // W column tile `wave`, stored as -W^T
-      f4_t Y[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rb * 16 + 4 * g4 + i;
-          Y[rb][i] = sBeta[r] * sGam[r] * (float)sKh[r * LDK + wave * 16 + m16];
-        }
-      block_solve<OP, LC, LLI>(Y, sAn, sLi);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sWt[(wave * 16 + m16) * LC + rb * 16 + 4 * g4 + i] = (OP)(-Y[rb][i]);
-    }
-    __syncthreads();
-
+    for (int rt = 0; rt < 4; ++rt) dOr[rt] = dOn[rt];
+    if (c > 0) issue(c - 1);
+    // an opaque buffer offset: the LDS addresses of both buffers would
+    // otherwise be formed once, outside the loop, and held in registers
+    int boff = (c & 1) * I::bytes;
+    asm volatile("" : "+s"(boff));
+    const char* img = smem + boff;
+    const OP* sKh = reinterpret_cast<const OP*>(img + I::oKh);
+    const OP* sQt = reinterpret_cast<const OP*>(img + I::oQt);
+    const OP* sWt = reinterpret_cast<const OP*>(img + I::oWt);
+    const OP* sPt = reinterpret_cast<const OP*>(img + I::oPt);
+    const float* sGam = reinterpret_cast<const float*>(img + I::oGam);
+    const float* sDec = reinterpret_cast<const float*>(img + I::oDec);
     const float gamC = sGam[C - 1];
+    // dU = P^T dO + D (K dM)
+    f4_t dU[4], tk[4];
 #pragma unroll
-    for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
-      if (ct >= (int)(blockIdx.z + 1) * NCTS) continue;
-      const int col = ct * 16 + m16;
-      // dU = P^T dO + D (K dM)
-      f4_t dU[4], tk[4];
+    for (int rt = 0; rt < 4; ++rt) { dU[rt] = zero4(); tk[rt] = zero4(); }
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) { dU[rt] = zero4(); tk[rt] = zero4(); }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const Frag<OP> fo = acc_frag<OP>(dOr[cw][2 * kb], dOr[cw][2 * kb + 1]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          if (kb * 32 + 31 >= rt * 16) mma(dU[rt], lds_frag<OP>(sPt, LC, rt * 16, kb * 32), fo);
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const Frag<OP> fm = acc_frag<OP>(dM[cw][2 * kb], dM[cw][2 * kb + 1]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mma(tk[rt], lds_frag<OP>(sKh, LDK, rt * 16, kb * 32), fm);
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const Frag<OP> fo = acc_frag<OP>(dOr[2 * kb], dOr[2 * kb + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
+        if (kb * 32 + 31 >= rt * 16) mma(dU[rt], lds_frag<OP>(sPt, I::LT, rt * 16, kb * 32), fo);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dU[rt][i] += sDec[rt * 16 + 4 * g4 + i] * tk[rt][i];
-      // the gradient of the chunk-end state and dU, for the per-chunk pass
-      float* dMo = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
+    for (int kb = 0; kb < KB; ++kb) {
+      const Frag<OP> fm = acc_frag<OP>(dM[2 * kb], dM[2 * kb + 1]);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < 4; ++rt) mma(tk[rt], lds_frag<OP>(sKh, I::LK, rt * 16, kb * 32), fm);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dMo[(rt * 16 + 4 * g4 + i) * DV + col] = dM[cw][rt][i];
-      float* dUo = a.dU + (((int64_t)b * T + t0) * H + h) * DV;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int i = 0; i < 4; ++i) dU[rt][i] += sDec[rt * 16 + 4 * g4 + i] * tk[rt][i];
+    // the gradient of the chunk-end state and dU, for the per-chunk pass
+    const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.dMck + ((bh * a.nchunks + c) * DK) * DV, (uint32_t)(DK * DV * 4));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = rt * 16 + 4 * g4 + i;
-          if (row < n) dUo[row * rowld + col] = dU[rt][i];
-        }
-      // dM <- gamma_C dM + Q^T Gamma dO - W^T dU
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int i = 0; i < 4; ++i) buf_store(rM, dM[rt][i], om, (rt * 16 + i) * DV * 4);
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(a.dU + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dM[cw][rt][i] *= gamC;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<OP> fo;
+      for (int i = 0; i < 4; ++i) buf_store(rU, dU[rt][i], ov, (int)((rt * 16 + i) * rowb));  // rows past n dropped
+    // dM <- gamma_C dM + Q^T Gamma dO - W^T dU
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          fo.v[j] = (OP)(dOr[cw][2 * kb][j] * sGam[kb * 32 + 4 * g4 + j]);
-          fo.v[4 + j] = (OP)(dOr[cw][2 * kb + 1][j] * sGam[kb * 32 + 16 + 4 * g4 + j]);
-        }
-        const Frag<OP> fu = acc_frag<OP>(dU[2 * kb], dU[2 * kb + 1]);
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          mma(dM[cw][rt], lds_frag<OP>(sQt, LC, rt * 16, kb * 32), fo);
-          mma(dM[cw][rt], lds_frag<OP>(sWt, LC, rt * 16, kb * 32), fu);
-        }
+      for (int i = 0; i < 4; ++i) dM[rt][i] *= gamC;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<OP> fo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fo.v[j] = (OP)(dOr[2 * kb][j] * sGam[kb * 32 + 4 * g4 + j]);
+        fo.v[4 + j] = (OP)(dOr[2 * kb + 1][j] * sGam[kb * 32 + 16 + 4 * g4 + j]);
+      }
+      const Frag<OP> fu = acc_frag<OP>(dU[2 * kb], dU[2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        mma(dM[rt], lds_frag<OP>(sQt, I::LT, rt * 16, kb * 32), fo);
+        mma(dM[rt], lds_frag<OP>(sWt, I::LT, rt * 16, kb * 32), fu);
       }
     }
   }
 
   const float inv = a.scale[1];
 #pragma unroll
-  for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = blockIdx.z * NCTS + wave + cw * NWAVE;
-    if (ct >= (int)(blockIdx.z + 1) * NCTS) continue;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a.dS0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + ct * 16 + m16] = dM[cw][rt][i] * inv;
-  }
+    for (int i = 0; i < 4; ++i) a.dS0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] = dM[rt][i] * inv;
 }
 
 // ------------------------------------------------------------ per-chunk gradients
 
-// sum of v over the 16 lanes of a lane group (all of them receive it)
 // one DPP-moved copy of v: CTRL is a row rotation (0x12r) or a quad permutation
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -378,14 +419,6 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// raw buffer loads: a wave-uniform resource and a per-lane byte offset; an
-// offset at or beyond the resource's size reads as zero
-__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ float buf_load_bf16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0));
-}
 // sum of v over the 4 lane groups at the same lane position
 __device__ __forceinline__ float sum_groups(float v) {
   v += __shfl_xor(v, 16, WAVE);
@@ -1243,6 +1276,10 @@ __global__ void sum_parts_kernel(int64_t n, int per, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+// bytes of one chunk's chain tiles (ChainImg<dk>::bytes)
+constexpr size_t chain_img_bytes(int dk) {
+  return (size_t)C * (dk + 8) * 2 + 2 * (size_t)dk * (C + 8) * 2 + (size_t)C * (C + 8) * 2 + 2 * (size_t)C * 4;
+}
 constexpr int GEN_NSPLIT = 512;       // token ranges of the dx / dW1 kernel
 constexpr int GEN_NSPLIT_SMALL = 2048; // token ranges of the dW2, db1, db2 partials
 constexpr int GEN_SMALL_PER = 64;      // partials per range in the first of their two sums
@@ -1258,6 +1295,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += al256((size_t)B * H * nch * dk * dv * 4);           // dMck
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
   bytes += 2 * al256((size_t)B * H * nch * C * dk * 4);        // dO M0^T, dU M0^T per chunk
+  bytes += al256((size_t)B * H * nch * chain_img_bytes(dk));   // the chain's tiles per chunk
   bytes += al256((size_t)B * H * nch * 4);                     // the chunk-end gate term
   bytes += al256(n * H * 4 * 4);                               // dtaps
   bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
@@ -1295,6 +1333,8 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   ws += al256((size_t)B * H * nch * C * dk * 4);
   float* dgC = reinterpret_cast<float*>(ws);
   ws += al256((size_t)B * H * nch * 4);
+  char* img = ws;
+  ws += al256((size_t)B * H * nch * chain_img_bytes(dk));
   float* dtaps = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * H * 4 * 4);
   float* pre = reinterpret_cast<float*>(ws);
@@ -1326,11 +1366,13 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   a.q = (const bf16_t*)q; a.k = (const bf16_t*)k; a.v = (const bf16_t*)v; a.conv_in = (const bf16_t*)conv_in;
   a.alpha = alpha; a.beta = beta; a.taps = taps; a.dout = dout; a.dS_final = dS_final; a.scale = scale;
   a.Mck = Mck; a.dMck = dMck; a.dU = dU; a.dS0 = dS0; a.dq = dq; a.dk = dk_; a.dalpha = dalpha; a.dbeta = dbeta;
-  a.dvc = dvc; a.QO = QO; a.WO = WO; a.dgC = dgC;
+  a.dvc = dvc; a.QO = QO; a.WO = WO; a.dgC = dgC; a.img = img;
   bool launched = false;
 #define CASE(DK_, DV_)                                                                              \
   if (dk == DK_ && dv == DV_) {                                                                     \
-    bwd_chain_kernel<DK_, DV_><<<dim3(H, B, chain_split<DV_>()), NTHR, 0, stream>>>(a);             \
+    static_assert(ChainImg<DK_>::bytes == chain_img_bytes(DK_), "chain tile layout");               \
+    bwd_tiles_kernel<DK_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                                 \
+    bwd_chain_kernel<DK_, DV_><<<dim3(H, B), DV_ / 16 * 64, 0, stream>>>(a);                        \
     bwd_dvred_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                            \
     bwd_grad_kernel<DK_, DV_><<<dim3(nch, H, B), NTHR, 0, stream>>>(a);                             \
     conv_bwd_kernel<DV_><<<dim3((T + 3 + 31) / 32, H, B), 256, 0, stream>>>(T, H, (const bf16_t*)v, \
