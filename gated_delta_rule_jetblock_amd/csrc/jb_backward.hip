@@ -103,63 +103,37 @@ __device__ __forceinline__ float buf_load_bf16(__amdgpu_buffer_rsrc_t r, uint32_
 
 // ------------------------------------------------------------ chain kernel
 
-// The state-independent tiles the chain needs of every chunk, in the padded
-// LDS layout the chain reads them in (so that they move as one contiguous
-// block): normalised K [C][DK], Q^T [DK][C], -W^T [DK][C], P^T [C][C] (fp16)
-// and gamma, e^{g_C - g} [C] (fp32).  Row strides are padded by 8 elements:
-// 16-byte multiples whose 16 rows of a fragment read fall in distinct banks.
-template <int DK>
-struct ChainImg {
-  static constexpr int LK = DK + 8, LT = C + 8;
-  static constexpr int oKh = 0;
-  static constexpr int oQt = oKh + C * LK * 2;
-  static constexpr int oWt = oQt + DK * LT * 2;
-  static constexpr int oPt = oWt + DK * LT * 2;
-  static constexpr int oGam = oPt + C * LT * 2;
-  static constexpr int oDec = oGam + C * 4;
-  static constexpr int bytes = oDec + C * 4;
-  static_assert(bytes % 16 == 0 && (LK * 2) % 16 == 0 && (LT * 2) % 16 == 0, "16-byte pieces");
-};
-
-// grid (nchunks, H, B), 8 waves: the chain tiles of one chunk, formed in LDS
-// (normalised q and k, the gates, -A and its diagonal-block inverses, W by
-// the blocked solve, the gated causal Q K^T) and written out whole.  Every
+// grid (nchunks, H, B), 8 waves: the Q^T and P^T chain tiles of one chunk
+// (the checkpointing forward pass wrote its K, -W^T and gates): normalised q
+// into LDS, the gated causal Q K^T blocks as P^T, both written out.  Every
 // chunk is independent, so this runs at full occupancy ahead of the chain.
 template <int DK>
 __global__ __launch_bounds__(NTHR) void bwd_tiles_kernel(BwdArgs a) {
   using OP = _Float16;
   using I = ChainImg<DK>;
-  constexpr int LDK = DK + 4, LC = C + 4, LAD = 20, LLI = 36;
-  constexpr int RT = DK / 16, KB = DK / 32;
-  constexpr int oImg = 0;
-  constexpr int oQh = oImg + I::bytes;
-  constexpr int oAn = oQh + C * LDK * 2;
-  constexpr int oAd = oAn + C * LC * 2;
-  constexpr int oLi = oAd + C * LAD * 4;
-  constexpr int oScal = oLi + C * LLI * 2;
-  constexpr int total = oScal + 2 * C * 4;
-  static_assert(RT <= NWAVE, "one wave per W column tile");
+  constexpr int LDK = DK + 4, KB = DK / 32;
+  constexpr int oKh = 0;                       // [C][LK] from the forward pass
+  constexpr int oQh = oKh + C * I::LK * 2;     // [C][LDK]
+  constexpr int oPt = oQh + C * LDK * 2;       // [C][LT]
+  constexpr int oG = oPt + C * I::LT * 2;      // [C]
+  constexpr int total = oG + C * 4;
   __shared__ __attribute__((aligned(16))) char smem[total];
-  char* img = smem + oImg;
-  OP* sKh = reinterpret_cast<OP*>(img + I::oKh);   // [C][LK]
-  OP* sQt = reinterpret_cast<OP*>(img + I::oQt);   // [DK][LT]
-  OP* sWt = reinterpret_cast<OP*>(img + I::oWt);   // [DK][LT]
-  OP* sPt = reinterpret_cast<OP*>(img + I::oPt);   // [C][LT]
-  float* sGam = reinterpret_cast<float*>(img + I::oGam);
-  float* sDec = reinterpret_cast<float*>(img + I::oDec);
-  OP* sQh = reinterpret_cast<OP*>(smem + oQh);     // [C][LDK]
-  OP* sAn = reinterpret_cast<OP*>(smem + oAn);     // [C][LC] -A
-  float* sAd = reinterpret_cast<float*>(smem + oAd);
-  OP* sLi = reinterpret_cast<OP*>(smem + oLi);
-  float* sG = reinterpret_cast<float*>(smem + oScal);
-  float* sBeta = sG + C;
+  OP* sKh = reinterpret_cast<OP*>(smem + oKh);
+  OP* sQh = reinterpret_cast<OP*>(smem + oQh);
+  OP* sPt = reinterpret_cast<OP*>(smem + oPt);
+  float* sG = reinterpret_cast<float*>(smem + oG);
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = a.H, T = a.T;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
   const int t0 = c * C, n = min(C, T - t0);
   const int64_t bh = (int64_t)b * H + h;
+  char* im = a.img + (bh * a.nchunks + c) * I::bytes;
 
+  // K and g from the forward pass
+  for (int e = tid; e < C * I::LK * 2 / 16; e += NTHR)
+    reinterpret_cast<uint4*>(sKh)[e] = reinterpret_cast<const uint4*>(im + I::oKh)[e];
+  if (tid < C) sG[tid] = reinterpret_cast<const float*>(im + I::oG)[tid];
   // P^T below the block diagonal stays zero
   for (int e = tid; e < C * C; e += NTHR) {
     const int r = e / C, cc = e % C;
@@ -169,106 +143,32 @@ __global__ __launch_bounds__(NTHR) void bwd_tiles_kernel(BwdArgs a) {
     Prologue<DK, bf16_t> pr;
     pr.load_global(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n);
     pr.finish(true);
+    OP* qt = reinterpret_cast<OP*>(im + I::oQt);
 #pragma unroll
     for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
       const int d = pr.part * Prologue<DK, bf16_t>::E + e;
       const OP qh = (OP)pr.qv[e];
-      sKh[pr.row * I::LK + d] = (OP)pr.kv[e];
       sQh[pr.row * LDK + d] = qh;
-      sQt[d * I::LT + pr.row] = qh;
+      qt[d * I::LT + pr.row] = qh;  // Q^T straight to the image
     }
   }
-  if (wave == GATE_WAVE) {
-    const bool valid = lane < n;
-    const int64_t gidx = ((int64_t)b * T + t0 + min(lane, n - 1)) * H + h;  // clamped, then masked
-    const float al0 = a.alpha[gidx], be0 = a.beta[gidx];
-    const float al = valid ? al0 : 1.f;
-    const float be = valid ? be0 : 0.f;
-    const float g = chunk_gate_scan(al);
-    const float gC = __shfl(g, C - 1, WAVE);
-    sG[lane] = g;
-    sGam[lane] = fast_exp2(g);
-    sBeta[lane] = be;
-    sDec[lane] = fast_exp2(gC - g);
-  }
   __syncthreads();
-
-  // -A and its diagonal blocks (lower tiles), P^T (upper tiles)
-  for (int job = wave; job < 20; job += NWAVE) {
-    const int which = job >= 10, t = job - 10 * which;
+  // P^T block (tj, ti): keys of block tj against queries of block ti
+  for (int t = wave; t < 10; t += NWAVE) {
     const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
     f4_t acc = zero4();
-    if (which == 0) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        mma(acc, lds_frag<OP>(sKh, I::LK, ti * 16, kb * 32), lds_frag<OP>(sKh, I::LK, tj * 16, kb * 32));
+    for (int kb = 0; kb < KB; ++kb)
+      mma(acc, lds_frag<OP>(sKh, I::LK, tj * 16, kb * 32), lds_frag<OP>(sQh, LDK, ti * 16, kb * 32));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = ti * 16 + 4 * g4 + i, cc = tj * 16 + m16;
-        const float av = cc < r ? sBeta[r] * fast_exp2(sG[r] - sG[cc]) * acc[i] : 0.f;
-        sAn[r * LC + cc] = (OP)(-av);
-        if (ti == tj) sAd[r * LAD + m16] = av;
-      }
-    } else {
-      // P^T block (tj, ti): keys of block tj against queries of block ti
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        mma(acc, lds_frag<OP>(sKh, I::LK, tj * 16, kb * 32), lds_frag<OP>(sQh, LDK, ti * 16, kb * 32));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = tj * 16 + 4 * g4 + i, cc = ti * 16 + m16;
-        sPt[r * I::LT + cc] = (OP)(cc >= r ? fast_exp2(sG[cc] - sG[r]) * acc[i] : 0.f);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = tj * 16 + 4 * g4 + i, cc = ti * 16 + m16;
+      sPt[r * I::LT + cc] = (OP)(cc >= r ? fast_exp2(sG[cc] - sG[r]) * acc[i] : 0.f);
     }
   }
   __syncthreads();
-
-  if (wave == 0) {
-    // diagonal-block inverses, one column per lane (as in the forward pass)
-    const int base = (lane >> 4) * 16, jc = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == jc) ? 1.f : 0.f;
-      const float* arow = sAd + (base + i) * LAD;
-#pragma unroll
-      for (int k4 = 0; k4 < i; k4 += 4) {
-        const float4 av = *reinterpret_cast<const float4*>(arow + k4);
-        acc -= av.x * x[k4];
-        if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
-        if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
-        if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
-      }
-      x[i] = acc;
-      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sLi[(base + i) * LLI + jc] = (OP)x[i];
-      sLi[(base + i) * LLI + 16 + jc] = (OP)0.f;
-    }
-  }
-  __syncthreads();
-
-  if (wave < RT) {
-    // W column tile `wave`, stored as -W^T
-    f4_t Y[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + 4 * g4 + i;
-        Y[rb][i] = sBeta[r] * sGam[r] * (float)sKh[r * I::LK + wave * 16 + m16];
-      }
-    block_solve<OP, LC, LLI>(Y, sAn, sLi);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sWt[(wave * 16 + m16) * I::LT + rb * 16 + 4 * g4 + i] = (OP)(-Y[rb][i]);
-  }
-  __syncthreads();
-  uint4* dst = reinterpret_cast<uint4*>(a.img + (bh * a.nchunks + c) * I::bytes);
-  for (int e = tid; e < I::bytes / 16; e += NTHR) dst[e] = reinterpret_cast<const uint4*>(img)[e];
+  for (int e = tid; e < C * I::LT * 2 / 16; e += NTHR)
+    reinterpret_cast<uint4*>(im + I::oPt)[e] = reinterpret_cast<const uint4*>(sPt)[e];
 }
 
 // grid (H, B), one wave per dv column tile (DV / 16 waves); wave w owns
@@ -1276,10 +1176,6 @@ __global__ void sum_parts_kernel(int64_t n, int per, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-// bytes of one chunk's chain tiles (ChainImg<dk>::bytes)
-constexpr size_t chain_img_bytes(int dk) {
-  return (size_t)C * (dk + 8) * 2 + 2 * (size_t)dk * (C + 8) * 2 + (size_t)C * (C + 8) * 2 + 2 * (size_t)C * 4;
-}
 constexpr int GEN_NSPLIT = 512;       // token ranges of the dx / dW1 kernel
 constexpr int GEN_NSPLIT_SMALL = 2048; // token ranges of the dW2, db1, db2 partials
 constexpr int GEN_SMALL_PER = 64;      // partials per range in the first of their two sums
@@ -1359,7 +1255,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // forward: taps and the state entering every chunk
   e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream, pre);
-  if (e == hipSuccess) e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, fws, stream);
+  if (e == hipSuccess) e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, img, fws, stream);
   if (e != hipSuccess) return e;
   BwdArgs a{};
   a.T = T; a.H = H; a.nchunks = nch;

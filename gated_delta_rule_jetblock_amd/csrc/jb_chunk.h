@@ -184,6 +184,33 @@ __device__ __forceinline__ void block_solve(f4_t (&Y)[4], const OP* sAn, const O
   Y[3] = t;
 }
 
+// ------------------------------------------------------------ chain tiles
+
+// The state-independent tiles the backward chain needs of every chunk, in the
+// padded LDS layout it reads them in (so that they move as one contiguous
+// block): normalised K [C][DK], Q^T [DK][C], -W^T [DK][C], P^T [C][C] (fp16)
+// and gamma, e^{g_C - g}, g [C] (fp32).  Row strides are padded by 8
+// elements: 16-byte multiples whose 16 rows of a fragment read fall in
+// distinct banks.  The checkpointing forward pass writes K, -W^T and the
+// gates; the backward's tile kernel adds Q^T and P^T.
+template <int DK>
+struct ChainImg {
+  static constexpr int LK = DK + 8, LT = C + 8;
+  static constexpr int oKh = 0;
+  static constexpr int oQt = oKh + C * LK * 2;
+  static constexpr int oWt = oQt + DK * LT * 2;
+  static constexpr int oPt = oWt + DK * LT * 2;
+  static constexpr int oGam = oPt + C * LT * 2;
+  static constexpr int oDec = oGam + C * 4;
+  static constexpr int oG = oDec + C * 4;
+  static constexpr int bytes = oG + C * 4;
+  static_assert(bytes % 16 == 0 && (LK * 2) % 16 == 0 && (LT * 2) % 16 == 0, "16-byte pieces");
+};
+// bytes of one chunk's chain tiles (ChainImg<dk>::bytes)
+constexpr size_t chain_img_bytes(int dk) {
+  return (size_t)C * (dk + 8) * 2 + 2 * (size_t)dk * (C + 8) * 2 + (size_t)C * (C + 8) * 2 + 3 * (size_t)C * 4;
+}
+
 // ------------------------------------------------------------ LDS DMA
 
 // Direct global -> LDS loads (gfx950): one wave instruction moves a 16-byte

@@ -67,7 +67,7 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
 // [B][H][nchunks][dk][dv] (bf16 inputs; workspace as launch_prefill's).
 hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, const float* taps, const void* conv_in, const float* S0,
-                               _Float16* Mck, void* workspace, hipStream_t stream);
+                               _Float16* Mck, char* img, void* workspace, hipStream_t stream);
 
 // The gradient of jb_prefill (bf16 inputs, fp32 gradients; one segment per
 // sequence).  Shapes built: (dk, dv) in {(32,64), (64,128), (96,256), (128,256)}.

@@ -70,6 +70,7 @@ struct ChunkArgs {
   void* o;
   float* S_final;
   _Float16* Mck;        // MODE_CKPT: the state entering every chunk, fp16 16x16 tiles (below)
+  char* img;            // MODE_CKPT: per chunk, the K, -W^T and gate parts of ChainImg
 };
 
 // ------------------------------------------------------------ LDS layout
@@ -588,6 +589,27 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     // the value rows, -A, its diagonal blocks and inverses, and the taps are
     // dead from here on: the next chunk's raw inputs can stream in now
     if (c + 1 < c_end) issue_chunk(c + 1);
+    if constexpr (MODE == MODE_CKPT) {
+      // the backward chain's K, -W^T and gate tiles of this chunk
+      using I = ChainImg<DK>;
+      char* im = a.img + (bh * a.nchunks + c) * I::bytes;
+      for (int e = tid; e < C * (DK / 4); e += NTHR) {  // K rows, 8 bytes at a time
+        const int r = e / (DK / 4), p = e % (DK / 4);
+        *reinterpret_cast<uint2*>(im + I::oKh + (r * I::LK + p * 4) * 2) =
+            *reinterpret_cast<const uint2*>(sKh + r * LDK + p * 4);
+      }
+      for (int e = tid; e < DK * (C / 2); e += NTHR) {  // -W^T, two rows of -W per 4-byte store
+        const int d = e / (C / 2), r = (e % (C / 2)) * 2;
+        const OP w0 = sW[r * LDK + d], w1 = sW[(r + 1) * LDK + d];
+        *reinterpret_cast<uint32_t*>(im + I::oWt + (d * I::LT + r) * 2) =
+            (uint32_t)__builtin_bit_cast(uint16_t, w0) | ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+      }
+      if (tid < C) {
+        reinterpret_cast<float*>(im + I::oGam)[tid] = sGam[tid];
+        reinterpret_cast<float*>(im + I::oDec)[tid] = sDec[tid];
+        reinterpret_cast<float*>(im + I::oG)[tid] = sG[tid];
+      }
+    }
     const float gamC = sGam[C - 1];
     if constexpr (CPW == 1) {
       // one column tile per wave
@@ -1053,12 +1075,12 @@ bool backward_supported(int io, int dk, int dv) {
 
 hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, const float* taps, const void* conv_in, const float* S0,
-                               _Float16* Mck, void* workspace, hipStream_t stream) {
+                               _Float16* Mck, char* img, void* workspace, hipStream_t stream) {
   if (p.nchunks == 0) return hipSuccess;
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
-  a.S0 = S0; a.Mck = Mck;
+  a.S0 = S0; a.Mck = Mck; a.img = img;
   set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_ckpt<DK_, DV_>(p, a, stream);
