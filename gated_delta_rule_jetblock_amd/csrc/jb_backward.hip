@@ -935,89 +935,81 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ conv backward
 
-// grid (ceil((T + 3) / 32), H, B), 4 waves: wave w walks 8 consecutive rows
-// t = 8 (4 x + w) - 3 + k (t < 0: a conv-cache row) with sliding windows of
-// the rows it reads, so each dV' row and each value row is loaded once per
-// strip.  dv_raw[t] = sum_j taps_{t+3-j}[j] dV'_{t+3-j} over the tokens that
-// read row t, plus the gradient of conv_out; dtaps_t[j] = dV'_t . raw_{t-3+j}.
+// grid (ceil((T + 3) / 32), H, B), 4 waves: wave w takes the 8 consecutive
+// rows t = 8 (4 x + w) - 3 + k (t < 0: a conv-cache row).  The dV' rows
+// t .. t + 3 and value rows t - 3 .. t the strip reads (11 of each) are
+// loaded together up front, each lane taking DV / 64 adjacent columns.
+// dv_raw[t] = sum_j taps_{t+3-j}[j] dV'_{t+3-j} over the tokens that read
+// row t, plus the gradient of conv_out; dtaps_t[j] = dV'_t . raw_{t-3+j}.
+template <int N> struct FVec;
+template <> struct FVec<1> { typedef float F; typedef uint16_t B; };
+template <> struct FVec<2> { typedef float2 F; typedef uint32_t B; };
+template <> struct FVec<4> { typedef float4 F; typedef uint2 B; };
+
 template <int DV>
 __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_t* v, const bf16_t* conv_in,
                                                        const float* taps, const float* dvc, const float* dconv_out,
                                                        float* dv, float* dconv_in, float* dtaps) {
-  constexpr int CPL = DV / 64, STRIP = 8;
+  constexpr int CPL = DV / 64, STRIP = 8, NR = STRIP + 3;
+  using FV = typename FVec<CPL>::F;
+  using BV = typename FVec<CPL>::B;
   const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
   const int tw0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * STRIP - 3;
   if (tw0 >= T) return;
-  auto dvc_row = [&](int u, float (&o)[CPL], float (&tp)[4]) {  // dV'_u and taps_u (zero outside [0, T))
+  float dw[NR][CPL], rw[NR][CPL], tp[NR][4];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    // dV' row u = tw0 + k and its taps (zero outside [0, T))
+    const int u = tw0 + k;
     const bool ok = u >= 0 && u < T;
     const int64_t bu = ((int64_t)b * T + (ok ? u : 0)) * H + h;
     const float4 t4 = *reinterpret_cast<const float4*>(taps + bu * 4);
-    tp[0] = ok ? t4.x : 0.f; tp[1] = ok ? t4.y : 0.f; tp[2] = ok ? t4.z : 0.f; tp[3] = ok ? t4.w : 0.f;
+    tp[k][0] = ok ? t4.x : 0.f; tp[k][1] = ok ? t4.y : 0.f; tp[k][2] = ok ? t4.z : 0.f; tp[k][3] = ok ? t4.w : 0.f;
+    const FV x = *reinterpret_cast<const FV*>(dvc + bu * DV + lane * CPL);
+    const float* xf = reinterpret_cast<const float*>(&x);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float x = dvc[bu * DV + lane * CPL + i];
-      o[i] = ok ? x : 0.f;
-    }
-  };
-  auto raw_row = [&](int r, float (&o)[CPL]) {  // value row r (r < 0: the conv cache; zero without one)
+    for (int i = 0; i < CPL; ++i) dw[k][i] = ok ? xf[i] : 0.f;
+    // value row r = tw0 - 3 + k (r < 0: the conv cache; zero without one)
+    const int r = tw0 - 3 + k;
     const bool inv = r >= 0 && r < T, inc = r < 0 && r >= -3 && conv_in != nullptr;
     const bf16_t* src = inv ? v + (((int64_t)b * T + r) * H + h) * DV
                       : inc ? conv_in + (((int64_t)b * 3 + 3 + r) * H + h) * DV : v;
+    const BV rb = *reinterpret_cast<const BV*>(src + lane * CPL);
+    const bf16_t* rbh = reinterpret_cast<const bf16_t*>(&rb);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float x = bf16_to_f32(src[lane * CPL + i]);
-      o[i] = (inv || inc) ? x : 0.f;
-    }
-  };
-  float dwin[4][CPL], twin[4][4], rwin[4][CPL];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    dvc_row(tw0 + j, dwin[j + 1], twin[j + 1]);  // rows t .. t+2 of the first step sit in slots 1..3
-    raw_row(tw0 - 3 + j, rwin[j + 1]);           // rows t-3 .. t-1
+    for (int i = 0; i < CPL; ++i) rw[k][i] = (inv || inc) ? bf16_to_f32(rbh[i]) : 0.f;
   }
 #pragma unroll
   for (int k = 0; k < STRIP; ++k) {
     const int t = tw0 + k;
     if (t >= T) break;
-    // shift the windows: slot j holds dV' row t + j (j = 0..3) and raw row t - 3 + j
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) { dwin[j][i] = dwin[j + 1][i]; rwin[j][i] = rwin[j + 1][i]; }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) twin[j][q] = twin[j + 1][q];
-    }
-    dvc_row(t + 3, dwin[3], twin[3]);
-    raw_row(t, rwin[3]);
+    // token u = t + 3 - j (slot k + 3 - j) read row t with its tap j
     float acc[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)  // token u = t + 3 - j read row t with its tap j
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] += twin[3 - j][j] * dwin[3 - j][i];
+      for (int i = 0; i < CPL; ++i) acc[i] += tp[k + 3 - j][j] * dw[k + 3 - j][i];
     if (dconv_out && t >= T - 3) {
       const int sl = t - (T - 3);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[i] += dconv_out[(((int64_t)b * 3 + sl) * H + h) * DV + lane * CPL + i];
     }
     float* dst = t >= 0 ? dv + (((int64_t)b * T + t) * H + h) * DV : dconv_in + (((int64_t)b * 3 + 3 + t) * H + h) * DV;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) dst[lane * CPL + i] = acc[i];
+    *reinterpret_cast<FV*>(dst + lane * CPL) = *reinterpret_cast<const FV*>(acc);
     if (t >= 0) {
-      // dtaps_t[j] = dV'_t . raw_{t-3+j}; dV'_t sits in slot 0, raw row t-3+j in slot j
+      // dtaps_t[j] = dV'_t . raw_{t-3+j}: dV'_t in slot k, raw row t-3+j in slot k + j
       float d[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         d[j] = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) d[j] += dwin[0][i] * rwin[j][i];
+        for (int i = 0; i < CPL; ++i) d[j] += dw[k][i] * rw[k + j][i];
+        d[j] = sum_groups(sum16(d[j]));
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float sj = wave_sum(d[j]);
-        if (lane == 0) dtaps[(((int64_t)b * T + t) * H + h) * 4 + j] = sj;
-      }
+      if (lane == 0)
+        *reinterpret_cast<float4*>(dtaps + (((int64_t)b * T + t) * H + h) * 4) = make_float4(d[0], d[1], d[2], d[3]);
     }
   }
 }
