@@ -1178,7 +1178,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
   const size_t n = (size_t)B * T;
   const size_t nch = (size_t)p.nchunks;
-  size_t bytes = al256(prefill_workspace_bytes(p));           // taps, segment buffers (the forward pass)
+  size_t bytes = al256(prefill_base_bytes(p));                // taps, segment buffers (the forward pass)
   bytes += al256((size_t)B * H * nch * dk * dv * 2);           // Mck (fp16)
   bytes += al256((size_t)B * H * nch * dk * dv * 4);           // dMck
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
@@ -1206,7 +1206,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   char* ws = static_cast<char*>(workspace);
   char* fws = ws;                                   // taps first, then the segment buffers
   float* taps = reinterpret_cast<float*>(ws);
-  ws += al256(prefill_workspace_bytes(p));
+  ws += al256(prefill_base_bytes(p));
   _Float16* Mck = reinterpret_cast<_Float16*>(ws);
   ws += al256((size_t)B * H * nch * dk * dv * 2);
   float* dMck = reinterpret_cast<float*>(ws);

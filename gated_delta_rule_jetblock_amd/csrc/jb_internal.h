@@ -45,6 +45,8 @@ struct PrefillPlan {
 };
 PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, int seg_len);
 size_t prefill_workspace_bytes(const PrefillPlan& p);
+// taps and segment buffers only (the checkpointing forward pass of the backward)
+size_t prefill_base_bytes(const PrefillPlan& p);
 bool prefill_supported(const PrefillPlan& p);
 hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, const float* taps,

@@ -41,8 +41,14 @@
 namespace jb {
 
 // MODE_CKPT runs the output pass's state recurrence without q, P and o and
-// stores the state entering every chunk (the backward pass starts from them)
-enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1, MODE_CKPT = 2 };
+// stores the state entering every chunk (the backward pass starts from them).
+// MODE_PREP runs the state-independent phases of one chunk per workgroup and
+// writes their results (StreamImg, U0) for the streaming passes.
+enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1, MODE_CKPT = 2, MODE_PREP = 3 };
+constexpr int PREP_CHUNKS = 8;  // chunks per MODE_PREP workgroup (the next one's inputs stream in meanwhile)
+
+// the chunk kernel also forms Q^T-side tiles (normalised q, P): output and prep modes
+__host__ __device__ constexpr bool with_q(int mode) { return mode == MODE_OUTPUT || mode == MODE_PREP; }
 
 struct ChunkArgs {
   int T, H, nchunks, seg_len, nseg;
@@ -70,7 +76,10 @@ struct ChunkArgs {
   void* o;
   float* S_final;
   _Float16* Mck;        // MODE_CKPT: the state entering every chunk, fp16 16x16 tiles (below)
-  char* img;            // MODE_CKPT: per chunk, the K, -W^T and gate parts of ChainImg
+  char* img;            // MODE_CKPT: per chunk, the K, -W^T and gate parts of ChainImg;
+                        // MODE_PREP / streaming passes: per chunk, StreamImg
+  _Float16* u0;         // MODE_PREP / streaming passes: per chunk, U0 in fp16 accumulator tiles
+                        // [DV/16][4][64 lanes][4]
 };
 
 // ------------------------------------------------------------ LDS layout
@@ -90,7 +99,7 @@ struct Lds {
   static constexpr int LLI = 32 + 4;                     // diagonal-block inverses (cols 16..31 zero)
   static constexpr int szKh = C * LDK * (int)sizeof(OP);
   static constexpr int szKt = DK * LC * (int)sizeof(OP);
-  static constexpr int szQh = MODE == MODE_OUTPUT ? C * LDK * (int)sizeof(OP) : 0;
+  static constexpr int szQh = with_q(MODE) ? C * LDK * (int)sizeof(OP) : 0;
   static constexpr int szV = (C + 3) * LVB;
   static constexpr int szTap = SC ? 0 : C * 4 * 4;
   static constexpr int szScal = 4 * C * 4;
@@ -98,10 +107,10 @@ struct Lds {
   static constexpr int szAn = C * LC * (int)sizeof(OP);
   static constexpr int szAd = C * LAD * 4;
   static constexpr int szLi = C * LLI * (int)sizeof(OP);
-  static constexpr int szP = MODE == MODE_OUTPUT ? C * LC * (int)sizeof(OP) : 0;
+  static constexpr int szP = with_q(MODE) ? C * LC * (int)sizeof(OP) : 0;
   // raw q or k rows of a chunk (static conv: with the 3-row halo in front, like the values)
   static constexpr int szRaw = (SC ? C + 3 : C) * DK * (int)sizeof(IO);
-  static constexpr int szQraw = MODE == MODE_OUTPUT ? szRaw : 0;
+  static constexpr int szQraw = with_q(MODE) ? szRaw : 0;
   static constexpr int szGraw = C * 4 * 2 + (SC ? 0 : C * 16);             // raw alpha, beta, taps
   // bf16 inputs: the band T of the right-hand side diag(b) V' = T V_ext, as
   // [hi, lo][row tile][16 rows][LT] bf16 (32 columns used)
@@ -130,11 +139,34 @@ struct Lds {
   static constexpr int oV = a16(oKh + szKh);
   static constexpr int oT = a16(oV + szV);
   static constexpr int oCw = a16(oT + szT);
-  static constexpr int total = a16(oCw + szCw);
+  // MODE_PREP: raw k of the next chunk in a region of its own where it fits,
+  // so that the next chunk can be issued while -A is in use
+  static constexpr int oKr2 = a16(oCw + szCw);
+  static constexpr bool SEPK = MODE == MODE_PREP && oKr2 + szRaw <= 160 * 1024;
+  static constexpr int total = a16(oKr2 + (SEPK ? szRaw : 0));
   // raw k rows of the next chunk land in the -A / diagonal-block region, dead
   // while a chunk's column phase runs and rewritten only after the prologue
-  static constexpr int oKraw = oAn;
+  static constexpr int oKraw = SEPK ? oKr2 : oAn;
   static_assert(oLi + szLi - oAn >= szRaw, "raw k staging does not fit");
+};
+
+// One chunk's state-independent tiles for the streaming passes: the bytes
+// [oKt, oQh + szQh) of the output-mode LDS layout (K^T, P, -W, Q with their
+// paddings, fp16), then gamma and e^{g_C - g} (fp32).  MODE_PREP writes them;
+// stream_kernel moves them into LDS as one block.
+template <int DK>
+struct StreamImg {
+  static constexpr int LDK = DK + 4, LC = C + 4;
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int oKt = 0;
+  static constexpr int oP = a16(DK * LC * 2);
+  static constexpr int oW = oP + a16(C * LC * 2);
+  static constexpr int oQh = oW + a16(C * LDK * 2);
+  static constexpr int region = oQh + C * LDK * 2;
+  static constexpr int oGam = a16(region);
+  static constexpr int oDec = oGam + C * 4;
+  static constexpr int bytes = oDec + C * 4;
+  static_assert(region % 16 == 0 && bytes % 16 == 0, "16-byte pieces");
 };
 
 // ------------------------------------------------------------ chunk kernel
@@ -190,7 +222,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   // a packed batch plans its grid for the longest sequence: shorter ones
   // leave the extra segments' workgroups idle (the summary kernel has one
   // workgroup per segment but the last)
-  if (s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
+  if (MODE == MODE_PREP ? s * PREP_CHUNKS * C >= T : s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
   // the wave index is uniform across a wave: keep it (and what derives from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
@@ -214,7 +246,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         const int row = rt * 16 + 4 * g4 + i;
         if (MODE == MODE_SUMMARY) {
           if (ct >= VCT) Macc[cw][rt][i] = (row == (ct - VCT) * 16 + m16) ? 1.f : 0.f;
-        } else {
+        } else if (MODE != MODE_PREP) {
           const int col = ct * 16 + m16;
           const float* src = a.nseg > 1 ? a.Mstart + ((bh * a.nseg + s) * DK) * DV
                                         : (a.S0 ? a.S0 + bh * DK * DV : nullptr);
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   }
 
   // P above its block diagonal is never written by the chunk loop
-  if (MODE == MODE_OUTPUT)
+  if (with_q(MODE))
     for (int e = tid; e < C * C; e += NTHR) {
       const int r = e / C, c = e % C;
       if ((c >> 4) > (r >> 4)) sP[r * LC + c] = from_f32<OP>(0.f);
@@ -247,8 +279,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
 
-  const int c_begin = s * a.seg_len;
-  const int c_end = min((T + C - 1) / C, c_begin + a.seg_len);
+  const int c_begin = s * (MODE == MODE_PREP ? PREP_CHUNKS : a.seg_len);
+  const int c_end = min((T + C - 1) / C, c_begin + (MODE == MODE_PREP ? PREP_CHUNKS : a.seg_len));
 
   // Raw inputs of chunk cc straight into LDS: value rows t0-3 .. t0+63 into
   // sV (zeros where neither v nor the conv cache has a row), raw k (and q)
@@ -279,7 +311,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         if (p < C * PPK && r < nc) {
           const int64_t off = ((tok0 + t0c + r) * H + h) * DK + pc * EP;
           dma16(k + off, sKraw + j * 64 * 16);
-          if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+          if (with_q(MODE)) dma16(q + off, sQraw + j * 64 * 16);
         }
       }
     } else {
@@ -296,15 +328,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
             if (r - 3 < nc) {
               const int64_t off = ((tok0 + t) * H + h) * DK + pc * EP;
               dma16(k + off, sKraw + j * 64 * 16);
-              if (MODE == MODE_OUTPUT) dma16(q + off, sQraw + j * 64 * 16);
+              if (with_q(MODE)) dma16(q + off, sQraw + j * 64 * 16);
             }
           } else if (ck) {
             const int64_t off = (((int64_t)b * 3 + (3 + t)) * H + h) * DK + pc * EP;
             dma16(ck + off, sKraw + j * 64 * 16);
-            if (MODE == MODE_OUTPUT) dma16(cq + off, sQraw + j * 64 * 16);
+            if (with_q(MODE)) dma16(cq + off, sQraw + j * 64 * 16);
           } else {
             *reinterpret_cast<uint4*>(sKraw + p * 16) = make_uint4(0u, 0u, 0u, 0u);
-            if (MODE == MODE_OUTPUT) *reinterpret_cast<uint4*>(sQraw + p * 16) = make_uint4(0u, 0u, 0u, 0u);
+            if (with_q(MODE)) *reinterpret_cast<uint4*>(sQraw + p * 16) = make_uint4(0u, 0u, 0u, 0u);
           }
         }
       }
@@ -334,6 +366,10 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   // T is zero outside its band; the band is rewritten every chunk
   for (int e = tid; e < L::szT / 16; e += NTHR) reinterpret_cast<uint4*>(smem + L::oT)[e] = make_uint4(0u, 0u, 0u, 0u);
   if (c_begin < c_end) issue_chunk(c_begin);
+
+  using SI = StreamImg<DK>;
+  static_assert(MODE != MODE_PREP || (sizeof(OP) == 2 && L::oP - L::oKt == SI::oP && L::oW - L::oKt == SI::oW &&
+                                      L::oQh - L::oKt == SI::oQh && L::oKt % 16 == 0), "stream image layout");
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
@@ -380,14 +416,14 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
           conv4<DK, IO>(kraw, sCwk, row, dd, valid, x);
 #pragma unroll
           for (int i = 0; i < 4; ++i) sk += x[i] * x[i];
-          if (MODE == MODE_OUTPUT) {
+          if (with_q(MODE)) {
             conv4<DK, IO>(qraw, sCwq, row, dd, valid, x);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sq += x[i] * x[i];
           }
         }
         const float rk = l2_scale(group_sum<8>(sk));
-        const float rq = MODE == MODE_OUTPUT ? l2_scale(group_sum<8>(sq)) : 0.f;
+        const float rq = with_q(MODE) ? l2_scale(group_sum<8>(sq)) : 0.f;
 #pragma unroll 1
         for (int e0 = 0; e0 < E; e0 += 4) {
           const int dd = d0 + e0;
@@ -399,7 +435,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
             sKh[row * LDK + dd + i] = kh;
             sKt[(dd + i) * LC + row] = kh;
           }
-          if (MODE == MODE_OUTPUT) {
+          if (with_q(MODE)) {
             conv4<DK, IO>(qraw, sCwq, row, dd, valid, x);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sQh[row * LDK + dd + i] = from_f32<OP>(x[i] * rq);
@@ -408,15 +444,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       } else if (tid < PRO_THR) {
         Prologue<DK, IO> pr;
         pr.load(reinterpret_cast<const IO*>(sQraw), reinterpret_cast<const IO*>(sKraw), 0, 1, n,
-                MODE == MODE_OUTPUT);
-        pr.finish(MODE == MODE_OUTPUT);
+                with_q(MODE));
+        pr.finish(with_q(MODE));
 #pragma unroll
         for (int e = 0; e < Prologue<DK, IO>::E; ++e) {
           const int d = pr.part * Prologue<DK, IO>::E + e;
           const OP kh = from_f32<OP>(pr.kv[e]);
           sKh[pr.row * LDK + d] = kh;
           sKt[d * LC + pr.row] = kh;
-          if (MODE == MODE_OUTPUT) sQh[pr.row * LDK + d] = from_f32<OP>(pr.qv[e]);
+          if (with_q(MODE)) sQh[pr.row * LDK + d] = from_f32<OP>(pr.qv[e]);
         }
       }
       if (wave == GATE_WAVE) {
@@ -453,9 +489,35 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
+    f4_t U[CPW][4];
+    if constexpr (MODE == MODE_PREP) {
+      // the right-hand sides diag(b) V' = T V_ext of U0 now, on the matrix cores
+      // (as below), so that the value rows are free for the next chunk early
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw) {
+        const int ct = wave + cw * NWAVE;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) U[cw][rb] = zero4();
+        if (ct >= NCT) continue;
+        const int col = ct * 16 + m16;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
+          const bf16_t* vcol = reinterpret_cast<const bf16_t*>(sV + (s0 + 8 * g4) * L::LVB) + col;
+          bf16x8_t vb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vb[j] = __builtin_bit_cast(__bf16, vcol[j * (L::LVB / 2)]);
+          const bf16x8_t th = *reinterpret_cast<const bf16x8_t*>(sT + (rt * 16 + m16) * L::LT + 8 * g4);
+          const bf16x8_t tl = *reinterpret_cast<const bf16x8_t*>(sT + ((4 + rt) * 16 + m16) * L::LT + 8 * g4);
+          const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
+          U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
+        }
+      }
+    }
+
     // ================= K K^T -> -A (and its diagonal blocks), Q K^T -> P =================
     {
-      constexpr int NJOB = MODE == MODE_OUTPUT ? 20 : 10;
+      constexpr int NJOB = with_q(MODE) ? 20 : 10;
       for (int job = wave; job < NJOB; job += NWAVE) {
         const int which = job >= 10, t = job - 10 * which;
         const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
@@ -478,6 +540,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
+
 
     // ================= diagonal-block inverses (wave 0) =================
     if (wave == 0) {
@@ -509,6 +572,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
+    if (L::SEPK && c + 1 < c_end) issue_chunk(c + 1);
     // ================= per-wave solves: W tiles and U0 = (I+A)^{-1} diag(b) V' =================
     if (wave < RT) {
       // W = (I+A)^{-1} diag(b gamma) K, column tile `wave`; stored negated
@@ -526,10 +590,13 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sW[(rb * 16 + 4 * g4 + i) * LDK + wave * 16 + m16] = from_f32<OP>(-Y[rb][i]);
     }
-    f4_t U[CPW][4];
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
       const int ct = wave + cw * NWAVE;
+      if constexpr (MODE == MODE_PREP) {
+        if (ct < NCT) block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
+        continue;
+      }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) U[cw][rb] = zero4();
       if (ct >= NCT || !(MODE == MODE_OUTPUT || ct < VCT)) continue;
@@ -584,6 +651,31 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
     }
     __syncthreads();
+
+    if constexpr (MODE == MODE_PREP) {
+      // the streaming passes' tiles of this chunk and U0 (fp16 accumulator tiles)
+      if (!L::SEPK && c + 1 < c_end) issue_chunk(c + 1);  // raw k lands on -A: only now
+      char* im = a.img + (bh * a.nchunks + c) * SI::bytes;
+      for (int e = tid; e < SI::region / 16; e += NTHR)
+        reinterpret_cast<uint4*>(im)[e] = reinterpret_cast<const uint4*>(smem + L::oKt)[e];
+      if (tid < C) {
+        reinterpret_cast<float*>(im + SI::oGam)[tid] = sGam[tid];
+        reinterpret_cast<float*>(im + SI::oDec)[tid] = sDec[tid];
+      }
+      uint2* u0 = reinterpret_cast<uint2*>(a.u0 + (bh * a.nchunks + c) * (DV * C));
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw) {
+        const int ct = wave + cw * NWAVE;
+        if (ct < NCT)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const half4_t hv = {(_Float16)U[cw][rt][0], (_Float16)U[cw][rt][1], (_Float16)U[cw][rt][2],
+                                (_Float16)U[cw][rt][3]};
+            u0[(ct * 4 + rt) * 64 + lane] = __builtin_bit_cast(uint2, hv);
+          }
+      }
+      continue;
+    }
 
     // ================= state-dependent part, per column tile =================
     // the value rows, -A, its diagonal blocks and inverses, and the taps are
@@ -764,6 +856,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   }
 
   // ---- results
+  if constexpr (MODE == MODE_PREP) return;
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
     const int ct = wave + cw * NWAVE;
@@ -776,6 +869,241 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         if (MODE == MODE_OUTPUT) {
           if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else if (MODE == MODE_CKPT) {
+        } else if (ct < VCT) {
+          a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+        } else {
+          a.Phi[((bh * a.nseg + s) * DK + row) * DK + (ct - VCT) * 16 + m16] = Macc[cw][rt][i];
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------ streaming passes
+
+// The summary (MODE_SUMMARY) and output (MODE_OUTPUT) passes over one
+// segment with the state-independent phases taken from MODE_PREP: each
+// chunk's StreamImg streams by LDS DMA into one of two buffers, and its U0
+// tiles into registers, while the previous chunk runs, so a chunk costs one
+// barrier and its state-dependent products (the same code as chunk_kernel's
+// column phase).  grid (segments, H, B), 8 waves.
+template <int DK, int DV, typename OUT, int MODE>
+__global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
+  using OP = _Float16;
+  using SI = StreamImg<DK>;
+  constexpr int LDK = SI::LDK, LC = SI::LC;
+  constexpr int NCT = MODE == MODE_SUMMARY ? (DV + DK) / 16 : DV / 16;  // column tiles
+  constexpr int CPW = (NCT + NWAVE - 1) / NWAVE;                        // tiles per wave (max)
+  constexpr int RT = DK / 16;                                           // row tiles of M
+  constexpr int KB = DK / 32;                                           // 32-deep blocks of dk
+  constexpr int VCT = DV / 16;                                          // value column tiles
+  __shared__ __attribute__((aligned(16))) char smem[2 * SI::bytes];
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int H = a.H;
+  int64_t tok0;
+  int T;
+  seq_span(a.cu_seqlens, a.T, b, tok0, T);
+  const int nseg_b = seq_segments(T, a.seg_len);
+  if (s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const int64_t bh = (int64_t)b * H + h;
+
+  // ---- initial state (accumulator layout: lane holds M[rt*16+4g+i][ct*16+m16])
+  f4_t Macc[CPW][RT];
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      Macc[cw][rt] = zero4();
+      if (ct >= NCT) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        if (MODE == MODE_SUMMARY) {
+          if (ct >= VCT) Macc[cw][rt][i] = (row == (ct - VCT) * 16 + m16) ? 1.f : 0.f;
+        } else {
+          const int col = ct * 16 + m16;
+          const float* src = a.nseg > 1 ? a.Mstart + ((bh * a.nseg + s) * DK) * DV
+                                        : (a.S0 ? a.S0 + bh * DK * DV : nullptr);
+          Macc[cw][rt][i] = src ? src[row * DV + col] : 0.f;
+        }
+      }
+    }
+  }
+
+  const int c_begin = s * a.seg_len;
+  const int c_end = min((T + C - 1) / C, c_begin + a.seg_len);
+
+  // a column tile of outputs, rows t0 .. t0+n-1, straight from registers
+  auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n) {
+    const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0) * H + h) * DV, (uint32_t)n * rowb);
+    const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        // rows at or beyond n fall outside the resource and are dropped
+        buf_store(orsrc, from_f32<OUT>(Ot[rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
+  };
+
+  // chunk cc's image into buffer cc & 1 (the summary pass skips P and Q) and
+  // its U0 tiles into Un
+  uint2 Un[CPW][4];
+  auto issue = [&](int cc) {
+    const char* src = a.img + (bh * a.nchunks + cc) * SI::bytes;
+    char* dst = smem + (cc & 1) * SI::bytes;
+    constexpr int NP = SI::bytes / 16;
+    for (int j = wave; j * 64 < NP; j += NWAVE) {
+      const int p = j * 64 + lane;
+      const int off = p * 16;
+      const bool skip = MODE == MODE_SUMMARY && ((off >= SI::oP && off < SI::oW) || (off >= SI::oQh && off < SI::oGam));
+      if (p < NP && !skip) dma16(src + off, dst + j * 64 * 16);
+    }
+    const uint2* u0 = reinterpret_cast<const uint2*>(a.u0 + (bh * a.nchunks + cc) * (DV * C));
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) {
+      const int ct = wave + cw * NWAVE;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Un[cw][rt] = ct < VCT ? u0[(ct * 4 + rt) * 64 + lane] : make_uint2(0u, 0u);
+    }
+  };
+  if (c_begin < c_end) issue(c_begin);
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's image transfers and U0 loads have landed
+    __syncthreads();                // ... and every other wave's; the other buffer is free
+    f4_t U[CPW][4];
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const half4_t hv = __builtin_bit_cast(half4_t, Un[cw][rt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[cw][rt][i] = (float)hv[i];
+      }
+    if (c + 1 < c_end) issue(c + 1);
+    // an opaque buffer offset: the LDS addresses of both buffers would
+    // otherwise be formed once, outside the loop, and held in registers
+    int boff = (c & 1) * SI::bytes;
+    asm volatile("" : "+s"(boff));
+    const char* im = smem + boff;
+    const OP* sKt = reinterpret_cast<const OP*>(im + SI::oKt);
+    const OP* sP = reinterpret_cast<const OP*>(im + SI::oP);
+    const OP* sW = reinterpret_cast<const OP*>(im + SI::oW);
+    const OP* sQh = reinterpret_cast<const OP*>(im + SI::oQh);
+    const float* sGam = reinterpret_cast<const float*>(im + SI::oGam);
+    const float* sDec = reinterpret_cast<const float*>(im + SI::oDec);
+    const float gamC = sGam[C - 1];
+    {
+    // Each A fragment (rows of W, Q, P, K^T) is read from LDS once and applied
+    // to all of the wave's column tiles.
+    bool has[CPW];  // the wave owns column tile wave + cw * NWAVE
+#pragma unroll
+    for (int cw = 0; cw < CPW; ++cw) has[cw] = wave + cw * NWAVE < NCT;
+    // V_new = U0 - W M0 and (outputs) Q M0
+    f4_t O[MODE == MODE_OUTPUT ? CPW : 1][4];
+#pragma unroll
+    for (int cw = 0; cw < (MODE == MODE_OUTPUT ? CPW : 1); ++cw)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      Frag<OP> mf[CPW];
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw) mf[cw] = acc_frag<OP>(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const Frag<OP> aw = lds_frag<OP>(sW, LDK, rt * 16, kb * 32);
+#pragma unroll
+        for (int cw = 0; cw < CPW; ++cw)
+          if (has[cw]) mma(U[cw][rt], aw, mf[cw]);
+        if (MODE == MODE_OUTPUT) {
+          const Frag<OP> aq = lds_frag<OP>(sQh, LDK, rt * 16, kb * 32);
+#pragma unroll
+          for (int cw = 0; cw < CPW; ++cw)
+            if (has[cw]) mma(O[cw][rt], aq, mf[cw]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MODE == MODE_OUTPUT) {
+      // O = diag(gamma) Q M0 + P V_new
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gm = sGam[rt * 16 + 4 * g4 + i];
+#pragma unroll
+          for (int cw = 0; cw < CPW; ++cw) O[cw][rt][i] *= gm;
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<OP> vn[CPW];
+#pragma unroll
+        for (int cw = 0; cw < CPW; ++cw) vn[cw] = acc_frag<OP>(U[cw][2 * kb], U[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          if (kb * 32 <= rt * 16 + 15) {
+            const Frag<OP> ap = lds_frag<OP>(sP, LC, rt * 16, kb * 32);
+#pragma unroll
+            for (int cw = 0; cw < CPW; ++cw)
+              if (has[cw]) mma(O[cw][rt], ap, vn[cw]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int cw = 0; cw < CPW; ++cw)
+        if (has[cw]) store_o(O[cw], wave + cw * NWAVE, t0, n);
+    }
+    // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<OP> vd[CPW];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = sDec[kb * 32 + 4 * g4 + j], d1 = sDec[kb * 32 + 16 + 4 * g4 + j];
+#pragma unroll
+        for (int cw = 0; cw < CPW; ++cw) {
+          vd[cw].v[j] = from_f32<OP>(U[cw][2 * kb][j] * d0);
+          vd[cw].v[4 + j] = from_f32<OP>(U[cw][2 * kb + 1][j] * d1);
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const Frag<OP> ak = lds_frag<OP>(sKt, LC, rt * 16, kb * 32);
+#pragma unroll
+        for (int cw = 0; cw < CPW; ++cw)
+          if (has[cw]) {
+            if (kb == 0) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+            }
+            mma(Macc[cw][rt], ak, vd[cw]);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    }
+  }
+
+  // ---- results
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) {
+    const int ct = wave + cw * NWAVE;
+    if (ct >= NCT) continue;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        if (MODE == MODE_OUTPUT) {
+          if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else if (ct < VCT) {
           a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
         } else {
@@ -958,12 +1286,46 @@ static size_t segment_bytes(const PrefillPlan& p) {
   return 2 * align256(st * p.dk * p.dv * sizeof(float)) + align256(st * p.dk * p.dk * sizeof(float));
 }
 
-size_t prefill_workspace_bytes(const PrefillPlan& p) { return taps_bytes(p) + segment_bytes(p); }
+// bytes of one chunk's StreamImg<dk>
+constexpr size_t stream_img_bytes(int dk) {
+  const size_t oW = (size_t)(dk * (C + 4) * 2 + 15) / 16 * 16 + (size_t)(C * (C + 4) * 2 + 15) / 16 * 16;
+  const size_t region = oW + (size_t)(C * (dk + 4) * 2 + 15) / 16 * 16 + (size_t)C * (dk + 4) * 2;
+  return (region + 15) / 16 * 16 + 2 * (size_t)C * 4;
+}
+
+// the streaming passes (bf16 inputs, several segments per sequence): per
+// (sequence, head, chunk) a StreamImg and U0.  With one segment there is no
+// summary pass to share the state-independent phases with, and the fused
+// output pass is faster.
+static bool use_stream(const PrefillPlan& p) { return p.io == IO_BF16 && p.nseg > 1; }
+static size_t stream_bytes(const PrefillPlan& p) {
+  if (!use_stream(p)) return 0;
+  const size_t units = (size_t)p.B * p.H * p.nchunks;
+  return align256(units * stream_img_bytes(p.dk)) + align256(units * p.dv * C * 2);
+}
+
+size_t prefill_base_bytes(const PrefillPlan& p) { return taps_bytes(p) + segment_bytes(p); }
+size_t prefill_workspace_bytes(const PrefillPlan& p) { return prefill_base_bytes(p) + stream_bytes(p); }
 size_t prefill_static_workspace_bytes(const PrefillPlan& p) { return segment_bytes(p); }
 
 template <int DK, int DV, typename IO, typename OP, typename OUT, bool SC>
 static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t stream) {
   const dim3 blk(NTHR);
+  if constexpr (sizeof(IO) == 2 && !SC) {
+    // several segments: the state-independent phases of every chunk at once,
+    // then the summary and output passes stream them
+    static_assert(StreamImg<DK>::bytes == stream_img_bytes(DK), "stream image size");
+    if (use_stream(p)) {
+      if (!a.img || !a.u0) return hipErrorInvalidValue;
+      chunk_kernel<DK, DV, IO, OP, float, MODE_PREP, false>
+          <<<dim3((p.nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS, p.H, p.B), blk, 0, stream>>>(a);
+      stream_kernel<DK, DV, OUT, MODE_SUMMARY><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
+      scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+          p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
+      stream_kernel<DK, DV, OUT, MODE_OUTPUT><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY, SC><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
     scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
@@ -1013,6 +1375,12 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;
   set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
+  if (use_stream(p)) {
+    char* sw = static_cast<char*>(workspace) + prefill_base_bytes(p);
+    const size_t units = (size_t)p.B * p.H * p.nchunks;
+    a.img = sw;
+    a.u0 = reinterpret_cast<_Float16*>(sw + align256(units * stream_img_bytes(p.dk)));
+  }
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16>(p, a, stream);
   if (p.io == IO_BF16) { JB_PREFILL_BF16_CASES(CASE) }

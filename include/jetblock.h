@@ -98,7 +98,10 @@ int32_t jb_version(void);
 /*
  * Workspace bytes jb_prefill needs for `shape` (device memory, 256-byte
  * aligned, contents ignored on entry).  Writes *bytes; returns JB_OK or a
- * validation error.
+ * validation error.  It holds the per-token conv taps, the segment maps
+ * when the sequence is cut into segments and, with bf16 inputs, every
+ * chunk's state-independent tiles (about 80 KB per (sequence, head, chunk)
+ * at dk = 96, dv = 256).
  */
 jb_status jb_prefill_workspace_size(const jb_shape* shape, size_t* bytes);
 
