@@ -428,7 +428,7 @@ def main():
     pre_flops = prefill_flops_per_token(sp) * tok_pre
     pre_tf = pre_flops / (pre_ms * 1e-3) / 1e12
     pre_gbs = prefill_bytes_per_token(sp, out_bytes) * tok_pre / (pre_ms * 1e-3) / 1e9
-    roof_pre = dict(call="jb_prefill (generator, summary, scan, output kernels)", bound="mfma",
+    roof_pre = dict(call="jb_prefill (generator, per-chunk tiles, summary, scan, output kernels)", bound="mfma",
                     achieved=round(pre_tf, 2), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4), hbm_GBs=round(pre_gbs, 1),
                     hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4), flops_per_call=pre_flops,
