@@ -34,6 +34,8 @@
 // wave applies a blocked forward substitution on the matrix cores to its own
 // right-hand sides (its columns of diag(b) V', and one column tile of
 // diag(b gamma) K for the W tiles).
+#include <algorithm>
+
 #include "jb_chunk.h"
 #include "jb_device.h"
 #include "jb_internal.h"
@@ -45,7 +47,6 @@ namespace jb {
 // MODE_PREP runs the state-independent phases of one chunk per workgroup and
 // writes their results (StreamImg, U0) for the streaming passes.
 enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1, MODE_CKPT = 2, MODE_PREP = 3 };
-constexpr int PREP_CHUNKS = 8;  // chunks per MODE_PREP workgroup (the next one's inputs stream in meanwhile)
 
 // the chunk kernel also forms Q^T-side tiles (normalised q, P): output and prep modes
 __host__ __device__ constexpr bool with_q(int mode) { return mode == MODE_OUTPUT || mode == MODE_PREP; }
@@ -78,6 +79,7 @@ struct ChunkArgs {
   _Float16* Mck;        // MODE_CKPT: the state entering every chunk, fp16 16x16 tiles (below)
   char* img;            // MODE_CKPT: per chunk, the K, -W^T and gate parts of ChainImg;
                         // MODE_PREP / streaming passes: per chunk, StreamImg
+  int prep_chunks;      // MODE_PREP: chunks per workgroup (the next one's inputs stream in meanwhile)
   _Float16* u0;         // MODE_PREP / streaming passes: per chunk, U0 in fp16 accumulator tiles
                         // [DV/16][4][64 lanes][4]
 };
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   // a packed batch plans its grid for the longest sequence: shorter ones
   // leave the extra segments' workgroups idle (the summary kernel has one
   // workgroup per segment but the last)
-  if (MODE == MODE_PREP ? s * PREP_CHUNKS * C >= T : s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
+  if (MODE == MODE_PREP ? s * a.prep_chunks * C >= T : s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
   // the wave index is uniform across a wave: keep it (and what derives from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
@@ -279,8 +281,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
 
-  const int c_begin = s * (MODE == MODE_PREP ? PREP_CHUNKS : a.seg_len);
-  const int c_end = min((T + C - 1) / C, c_begin + (MODE == MODE_PREP ? PREP_CHUNKS : a.seg_len));
+  const int span = MODE == MODE_PREP ? a.prep_chunks : a.seg_len;
+  const int c_begin = s * span;
+  const int c_end = min((T + C - 1) / C, c_begin + span);
 
   // Raw inputs of chunk cc straight into LDS: value rows t0-3 .. t0+63 into
   // sV (zeros where neither v nor the conv cache has a row), raw k (and q)
@@ -1317,8 +1320,11 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
     static_assert(StreamImg<DK>::bytes == stream_img_bytes(DK), "stream image size");
     if (use_stream(p)) {
       if (!a.img || !a.u0) return hipErrorInvalidValue;
+      // chunks per workgroup: up to 16, keeping about three workgroups per CU
+      const int64_t units = (int64_t)p.nchunks * p.H * p.B;
+      a.prep_chunks = (int)std::max<int64_t>(1, std::min<int64_t>(16, units / (3 * NCU)));
       chunk_kernel<DK, DV, IO, OP, float, MODE_PREP, false>
-          <<<dim3((p.nchunks + PREP_CHUNKS - 1) / PREP_CHUNKS, p.H, p.B), blk, 0, stream>>>(a);
+          <<<dim3((p.nchunks + a.prep_chunks - 1) / a.prep_chunks, p.H, p.B), blk, 0, stream>>>(a);
       stream_kernel<DK, DV, OUT, MODE_SUMMARY><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
       scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
           p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
