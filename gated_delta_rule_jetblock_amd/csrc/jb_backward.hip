@@ -897,19 +897,21 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   if (wave < RT) {
     const int col = wave * 16 + m16;
+    // rows past the chunk fall outside the resources and are dropped
+    const uint32_t rowq = (uint32_t)(H * DK * 4);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.dq + tokbase * DK, (uint32_t)(n - 1) * rowq + DK * 4);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.dk + tokbase * DK, (uint32_t)(n - 1) * rowq + DK * 4);
+    const int oq = (int)(4 * g4 * rowq) + col * 4;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * g4 + i;
-        const int64_t o = (tokbase + (int64_t)r * H) * DK + col;
         const float qv = (float)sQh[r * LDK + col], kv = (float)sKh[r * LDK + col];
         const float gq = (dQh[rt][i] - qv * sQd[r]) / sNq[r] * inv;
         const float gk = (dKh[rt][i] - kv * sKd[r]) / sNk[r] * inv;
-        if (r < n) {
-          a.dq[o] = gq;
-          a.dk[o] = gk;
-        }
+        buf_store(rq, gq, oq, (int)((rt * 16 + i) * rowq));
+        buf_store(rk, gk, oq, (int)((rt * 16 + i) * rowq));
       }
   }
   // ---- the gates: D and gamma_C terms, reverse cumulative sum, d alpha and d beta
