@@ -44,8 +44,8 @@ namespace jb {
 
 // MODE_CKPT runs the output pass's state recurrence without q, P and o and
 // stores the state entering every chunk (the backward pass starts from them).
-// MODE_PREP runs the state-independent phases of one chunk per workgroup and
-// writes their results (StreamImg, U0) for the streaming passes.
+// MODE_PREP runs the state-independent phases of a run of chunks per
+// workgroup and writes their results (StreamImg, U0) for the streaming passes.
 enum { MODE_SUMMARY = 0, MODE_OUTPUT = 1, MODE_CKPT = 2, MODE_PREP = 3 };
 
 // the chunk kernel also forms Q^T-side tiles (normalised q, P): output and prep modes
@@ -146,8 +146,9 @@ struct Lds {
   static constexpr int oKr2 = a16(oCw + szCw);
   static constexpr bool SEPK = MODE == MODE_PREP && oKr2 + szRaw <= 160 * 1024;
   static constexpr int total = a16(oKr2 + (SEPK ? szRaw : 0));
-  // raw k rows of the next chunk land in the -A / diagonal-block region, dead
-  // while a chunk's column phase runs and rewritten only after the prologue
+  // otherwise raw k rows of the next chunk land in the -A / diagonal-block
+  // region, dead while a chunk's column phase runs and rewritten only after
+  // the prologue
   static constexpr int oKraw = SEPK ? oKr2 : oAn;
   static_assert(oLi + szLi - oAn >= szRaw, "raw k staging does not fit");
 };
