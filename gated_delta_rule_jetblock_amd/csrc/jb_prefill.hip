@@ -494,9 +494,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
 
     f4_t U[CPW][4];
-    if constexpr (MODE == MODE_PREP) {
-      // the right-hand sides diag(b) V' = T V_ext of U0 now, on the matrix cores
-      // (as below), so that the value rows are free for the next chunk early
+    // MODE_PREP: the right-hand sides diag(b) V' = T V_ext of U0 on the matrix
+    // cores (as below): wave 0 here, the other waves while wave 0 inverts
+    auto prep_rhs = [&]() {
 #pragma unroll
       for (int cw = 0; cw < CPW; ++cw) {
         const int ct = wave + cw * NWAVE;
@@ -517,12 +517,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
           U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
         }
       }
-    }
+    };
+    if constexpr (MODE == MODE_PREP)
+      if (wave == 0) prep_rhs();
 
     // ================= K K^T -> -A (and its diagonal blocks), Q K^T -> P =================
     {
       constexpr int NJOB = with_q(MODE) ? 20 : 10;
-      for (int job = wave; job < NJOB; job += NWAVE) {
+      constexpr int J0 = MODE == MODE_PREP ? 1 : 0;  // MODE_PREP: waves 1..7
+      for (int job = wave - J0; job >= 0 && job < NJOB; job += NWAVE - J0) {
         const int which = job >= 10, t = job - 10 * which;
         const int ti = (kLowI >> (2 * t)) & 3, tj = (kLowJ >> (2 * t)) & 3;
         const OP* Asrc = which ? sQh : sKh;
@@ -547,6 +550,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 
 
     // ================= diagonal-block inverses (wave 0) =================
+    if constexpr (MODE == MODE_PREP)
+      if (wave != 0) prep_rhs();
     if (wave == 0) {
       // four 16x16 blocks by forward substitution, one column per lane; rows
       // are read as float4 and the scheduling fences keep the compiler from
