@@ -519,7 +519,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     };
     if constexpr (MODE == MODE_PREP)
-      if (wave == 0) prep_rhs();
+      if (wave == 0) {
+        prep_rhs();
+        // K^T and Q are final: wave 0 writes them to the image meanwhile
+        char* im = a.img + (bh * a.nchunks + c) * SI::bytes;
+        for (int e = lane; e < SI::oP / 16; e += WAVE)
+          reinterpret_cast<uint4*>(im)[e] = reinterpret_cast<const uint4*>(smem + L::oKt)[e];
+        for (int e = SI::oQh / 16 + lane; e < SI::region / 16; e += WAVE)
+          reinterpret_cast<uint4*>(im)[e] = reinterpret_cast<const uint4*>(smem + L::oKt)[e];
+      }
 
     // ================= K K^T -> -A (and its diagonal blocks), Q K^T -> P =================
     {
@@ -665,7 +673,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       // the streaming passes' tiles of this chunk and U0 (fp16 accumulator tiles)
       if (!L::SEPK && c + 1 < c_end) issue_chunk(c + 1);  // raw k lands on -A: only now
       char* im = a.img + (bh * a.nchunks + c) * SI::bytes;
-      for (int e = tid; e < SI::region / 16; e += NTHR)
+      for (int e = SI::oP / 16 + tid; e < SI::oQh / 16; e += NTHR)  // P and -W
         reinterpret_cast<uint4*>(im)[e] = reinterpret_cast<const uint4*>(smem + L::oKt)[e];
       if (tid < C) {
         reinterpret_cast<float*>(im + SI::oGam)[tid] = sGam[tid];
