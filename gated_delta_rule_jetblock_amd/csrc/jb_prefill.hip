@@ -902,14 +902,14 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 // chunk's StreamImg streams by LDS DMA into one of two buffers, and its U0
 // tiles into registers, while the previous chunk runs, so a chunk costs one
 // barrier and its state-dependent products (the same code as chunk_kernel's
-// column phase).  grid (segments, H, B), 8 waves.
-template <int DK, int DV, typename OUT, int MODE>
-__global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
+// column phase).  grid (segments, H, B), SNW waves.
+template <int DK, int DV, typename OUT, int MODE, int SNW>
+__global__ __launch_bounds__(SNW * 64, 1) void stream_kernel(ChunkArgs a) {
   using OP = _Float16;
   using SI = StreamImg<DK>;
   constexpr int LDK = SI::LDK, LC = SI::LC;
   constexpr int NCT = MODE == MODE_SUMMARY ? (DV + DK) / 16 : DV / 16;  // column tiles
-  constexpr int CPW = (NCT + NWAVE - 1) / NWAVE;                        // tiles per wave (max)
+  constexpr int CPW = (NCT + SNW - 1) / SNW;                        // tiles per wave (max)
   constexpr int RT = DK / 16;                                           // row tiles of M
   constexpr int KB = DK / 32;                                           // 32-deep blocks of dk
   constexpr int VCT = DV / 16;                                          // value column tiles
@@ -930,7 +930,7 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
   f4_t Macc[CPW][RT];
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = wave + cw * NWAVE;
+    const int ct = wave + cw * SNW;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       Macc[cw][rt] = zero4();
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
     const char* src = a.img + (bh * a.nchunks + cc) * SI::bytes;
     char* dst = smem + (cc & 1) * SI::bytes;
     constexpr int NP = SI::bytes / 16;
-    for (int j = wave; j * 64 < NP; j += NWAVE) {
+    for (int j = wave; j * 64 < NP; j += SNW) {
       const int p = j * 64 + lane;
       const int off = p * 16;
       const bool skip = MODE == MODE_SUMMARY && ((off >= SI::oP && off < SI::oW) || (off >= SI::oQh && off < SI::oGam));
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
     const uint2* u0 = reinterpret_cast<const uint2*>(a.u0 + (bh * a.nchunks + cc) * (DV * C));
 #pragma unroll
     for (int cw = 0; cw < CPW; ++cw) {
-      const int ct = wave + cw * NWAVE;
+      const int ct = wave + cw * SNW;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Un[cw][rt] = ct < VCT ? u0[(ct * 4 + rt) * 64 + lane] : make_uint2(0u, 0u);
     }
@@ -1020,9 +1020,9 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
     {
     // Each A fragment (rows of W, Q, P, K^T) is read from LDS once and applied
     // to all of the wave's column tiles.
-    bool has[CPW];  // the wave owns column tile wave + cw * NWAVE
+    bool has[CPW];  // the wave owns column tile wave + cw * SNW
 #pragma unroll
-    for (int cw = 0; cw < CPW; ++cw) has[cw] = wave + cw * NWAVE < NCT;
+    for (int cw = 0; cw < CPW; ++cw) has[cw] = wave + cw * SNW < NCT;
     // V_new = U0 - W M0 and (outputs) Q M0
     f4_t O[MODE == MODE_OUTPUT ? CPW : 1][4];
 #pragma unroll
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int cw = 0; cw < CPW; ++cw)
-        if (has[cw]) store_o(O[cw], wave + cw * NWAVE, t0, n);
+        if (has[cw]) store_o(O[cw], wave + cw * SNW, t0, n);
     }
     // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
 #pragma unroll
@@ -1112,7 +1112,7 @@ __global__ __launch_bounds__(NTHR, 1) void stream_kernel(ChunkArgs a) {
   // ---- results
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
-    const int ct = wave + cw * NWAVE;
+    const int ct = wave + cw * SNW;
     if (ct >= NCT) continue;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -1339,10 +1339,12 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
       a.prep_chunks = (int)std::max<int64_t>(1, std::min<int64_t>(16, units / (3 * NCU)));
       chunk_kernel<DK, DV, IO, OP, float, MODE_PREP, false>
           <<<dim3((p.nchunks + a.prep_chunks - 1) / a.prep_chunks, p.H, p.B), blk, 0, stream>>>(a);
-      stream_kernel<DK, DV, OUT, MODE_SUMMARY><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
+      // the summary pass carries dk more columns (Phi): waves of two column tiles each
+      constexpr int SUMW = ((DV + DK) / 16 + 1) / 2 > NWAVE ? ((DV + DK) / 16 + 1) / 2 : NWAVE;
+      stream_kernel<DK, DV, OUT, MODE_SUMMARY, SUMW><<<dim3(p.nseg - 1, p.H, p.B), dim3(SUMW * 64), 0, stream>>>(a);
       scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
           p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
-      stream_kernel<DK, DV, OUT, MODE_OUTPUT><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
+      stream_kernel<DK, DV, OUT, MODE_OUTPUT, NWAVE><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
       return hipGetLastError();
     }
   }
