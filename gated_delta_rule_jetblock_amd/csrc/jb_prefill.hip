@@ -1155,91 +1155,75 @@ __device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const floa
   mma(acc, af, bf);
 }
 
-// grid (DV/16, H, B), one wavefront: M_0 = S0 (or 0); M_{s+1} = Phi_s M_s + D_s
-// over the segments of sequence b (nseg is the per-sequence stride of the
-// segment buffers; a packed batch's shorter sequences use fewer).
+// grid (DV/16, H, B), one wave per row tile of M (DK/16 waves): M_0 = S0 (or
+// 0); M_{s+1} = Phi_s M_s + D_s over the segments of sequence b (nseg is the
+// per-sequence stride of the segment buffers; a packed batch's shorter
+// sequences use fewer).  Wave w forms row tile w of each M from the whole
+// previous M, which the waves share through LDS; each wave's D_s and Phi_s
+// rows for the next segment load while it multiplies.
 template <int DK, int DV, typename OP>
-__global__ __launch_bounds__(WAVE) void scan_kernel(int H, int nseg, const int* cu_seqlens, int Tmax, int seg_len,
-                                                    const float* S0, const float* Dsum, const float* Phi,
-                                                    float* Mstart) {
-  constexpr int RT = DK / 16, KB = DK / 32;
+__global__ __launch_bounds__(DK / 16 * WAVE) void scan_kernel(int H, int nseg, const int* cu_seqlens, int Tmax,
+                                                              int seg_len, const float* S0, const float* Dsum,
+                                                              const float* Phi, float* Mstart) {
+  constexpr int KB = DK / 32, LM = 16 + 1;
+  __shared__ float sM[DK * LM];  // M, [DK][16] (+1 pad)
   const int ct = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int64_t tok0;
   int T;
   seq_span(cu_seqlens, Tmax, b, tok0, T);
   const int nseg_b = seq_segments(T, seg_len);
-  const int lane = threadIdx.x, m16 = lane & 15, g4 = lane >> 4;
+  const int rt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * H + h;
   const int col = ct * 16 + m16;
-  f4_t M[RT];
+  f4_t M;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) M[rt][i] = S0 ? S0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
-  // D_s and Phi_s do not depend on M: with dk <= 96 two register sets take
-  // turns, the loads of step s + 1 in flight while step s multiplies, so the
-  // chain pays about one memory latency instead of one per segment (with
-  // dk = 128 two sets do not fit the registers and each step loads its own)
-  auto load_step = [&](int s, float (&d)[RT][4], float (&pm)[RT][KB][8]) {
+  for (int i = 0; i < 4; ++i) M[i] = S0 ? S0[(bh * DK + rt * 16 + 4 * g4 + i) * DV + col] : 0.f;
+  auto load_step = [&](int s, float (&d)[4], float (&pm)[KB][8]) {
     const float* D = Dsum + (bh * nseg + s) * DK * DV;
     const float* P = Phi + (bh * nseg + s) * DK * DK;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int i = 0; i < 4; ++i) d[i] = D[(rt * 16 + 4 * g4 + i) * DV + col];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[rt][i] = D[(rt * 16 + 4 * g4 + i) * DV + col];
+    for (int kb = 0; kb < KB; ++kb) {
+      const float* prow = P + (rt * 16 + m16) * DK + kb * 32 + 4 * g4;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const float* prow = P + (rt * 16 + m16) * DK + kb * 32 + 4 * g4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { pm[rt][kb][j] = prow[j]; pm[rt][kb][4 + j] = prow[16 + j]; }
-      }
-    }
-  };
-  auto store_m = [&](int s) {
-    float* dst = Mstart + (bh * nseg + s) * DK * DV;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[rt][i];
-  };
-  auto step = [&](const float (&d)[RT][4], const float (&pm)[RT][KB][8]) {
-    float bv[KB][8];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { bv[kb][j] = M[2 * kb][j]; bv[kb][4 + j] = M[2 * kb + 1][j]; }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f4_t acc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = d[rt][i];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) split_mma(acc, pm[rt][kb], bv[kb], OP());
-      M[rt] = acc;
+      for (int j = 0; j < 4; ++j) { pm[kb][j] = prow[j]; pm[kb][4 + j] = prow[16 + j]; }
     }
   };
   const int last = nseg_b - 1;  // M_last is stored, not advanced
-  if constexpr (DK <= 96) {
-    float dA[RT][4], pA[RT][KB][8], dB[RT][4], pB[RT][KB][8];
-    if (last > 0) load_step(0, dA, pA);
-    for (int s = 0;; s += 2) {
-      store_m(s);
-      if (s == last) break;
-      if (s + 1 < last) load_step(s + 1, dB, pB);
-      step(dA, pA);
-      store_m(s + 1);
-      if (s + 1 == last) break;
-      if (s + 2 < last) load_step(s + 2, dA, pA);
-      step(dB, pB);
+  float dn[4], pn[KB][8];
+  if (last > 0) load_step(0, dn, pn);
+  for (int s = 0;; ++s) {
+    float* dst = Mstart + (bh * nseg + s) * DK * DV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[i];
+      sM[(rt * 16 + 4 * g4 + i) * LM + m16] = M[i];
     }
-  } else {
-    float d[RT][4], pm[RT][KB][8];
-    for (int s = 0;; ++s) {
-      store_m(s);
-      if (s == last) break;
-      load_step(s, d, pm);
-      step(d, pm);
+    if (s == last) break;
+    float dc[4], pc[KB][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dc[i] = dn[i];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pc[kb][j] = pn[kb][j];
+    if (s + 1 < last) load_step(s + 1, dn, pn);
+    __syncthreads();  // every row tile of M_s is in LDS
+    // B fragments: rows kb*32 + kperm(g, j) of M_s, this lane's column
+    f4_t acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = dc[i];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      float bv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = sM[(kb * 32 + kperm(g4, j)) * LM + m16];
+      split_mma(acc, pc[kb], bv, OP());
     }
+    M = acc;
+    __syncthreads();  // every wave has read M_s before it is overwritten
   }
 }
 
@@ -1342,7 +1326,7 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
       // the summary pass carries dk more columns (Phi): waves of two column tiles each
       constexpr int SUMW = ((DV + DK) / 16 + 1) / 2 > NWAVE ? ((DV + DK) / 16 + 1) / 2 : NWAVE;
       stream_kernel<DK, DV, OUT, MODE_SUMMARY, SUMW><<<dim3(p.nseg - 1, p.H, p.B), dim3(SUMW * 64), 0, stream>>>(a);
-      scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+      scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
           p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
       stream_kernel<DK, DV, OUT, MODE_OUTPUT, NWAVE><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
       return hipGetLastError();
@@ -1350,7 +1334,7 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
   }
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY, SC><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
-    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
         p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
   }
   chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT, SC><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
@@ -1447,7 +1431,7 @@ static hipError_t run_ckpt(const PrefillPlan& p, ChunkArgs a, hipStream_t stream
   const dim3 blk(NTHR);
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_SUMMARY, false><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
-    scan_kernel<DK, DV, _Float16><<<dim3(DV / 16, p.H, p.B), dim3(WAVE), 0, stream>>>(
+    scan_kernel<DK, DV, _Float16><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
         p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
   }
   chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_CKPT, false><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
