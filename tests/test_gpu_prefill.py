@@ -59,16 +59,19 @@ def test_ragged_lengths_with_state(jb, oracle_mod, io, T):
     np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
 
 
+@pytest.mark.parametrize("seg", [None, 2])
 @pytest.mark.parametrize("dk,dv", [(32, 64), (64, 128), (96, 256), (128, 256), (128, 64), (96, 128)])
-def test_head_shapes_bf16(jb, oracle_mod, dk, dv):
+def test_head_shapes_bf16(jb, oracle_mod, dk, dv, seg):
+    """Every head shape, in one segment (the fused chunk loop) and in segments of two
+    chunks (per-chunk tiles, summaries, scan and output passes)."""
     from gated_delta_rule_jetblock_amd import inputs
-    print(f"shape dk={dk} dv={dv}", flush=True)
+    print(f"shape dk={dk} dv={dv} seg={seg}", flush=True)
     s = inputs.Shape(B=1, T=300, H=3, dk=dk, dv=dv, d_model=256)
     p = inputs.prefill_inputs(s, seed=dk + dv)
     st = inputs.state_inputs(s, seed=1)
     ref = oracle_prefill(oracle_mod, p, st["S"], st["cache"])
-    r = _run(jb, p, st["S"], st["cache"])
-    _check(r, ref, TOL_BF16, f"dk={dk} dv={dv}")
+    r = _run(jb, p, st["S"], st["cache"], seg_len=seg)
+    _check(r, ref, TOL_BF16, f"dk={dk} dv={dv} seg={seg}")
 
 
 def test_jetblock2b_T4096(jb, oracle_mod):
