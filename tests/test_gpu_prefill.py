@@ -59,11 +59,12 @@ def test_ragged_lengths_with_state(jb, oracle_mod, io, T):
     np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
 
 
-@pytest.mark.parametrize("seg", [None, 2])
+@pytest.mark.parametrize("seg", [None, 2, 64])
 @pytest.mark.parametrize("dk,dv", [(32, 64), (64, 128), (96, 256), (128, 256), (128, 64), (96, 128)])
 def test_head_shapes_bf16(jb, oracle_mod, dk, dv, seg):
-    """Every head shape, in one segment (the fused chunk loop) and in segments of two
-    chunks (per-chunk tiles, summaries, scan and output passes)."""
+    """Every head shape under the default segment plan (three heads: one chunk per
+    segment), in segments of two chunks (both through the per-chunk tiles, summaries, scan
+    and output passes) and in one segment (the fused chunk loop)."""
     from gated_delta_rule_jetblock_amd import inputs
     print(f"shape dk={dk} dv={dv} seg={seg}", flush=True)
     s = inputs.Shape(B=1, T=300, H=3, dk=dk, dv=dv, d_model=256)
