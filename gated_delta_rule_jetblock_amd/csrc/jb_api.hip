@@ -229,7 +229,7 @@ jb_status jb_prefill_varlen(const jb_shape* s, int64_t total_tokens, const int32
   e = jb::launch_gen_taps(io, total_tokens, s->d_model, s->H, x, W1, b1, W2, b2, taps, hs);
   if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, workspace, hs);
   if (e == hipSuccess && conv_out)
-    e = jb::launch_conv_tail(io, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs, cu_seqlens);
+    e = jb::launch_conv_tail(io, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs, cu_seqlens, total_tokens);
   return hip_status(fn, e);
 }
 

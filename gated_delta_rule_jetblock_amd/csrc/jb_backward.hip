@@ -19,7 +19,12 @@
 // then through the L2 norms, the conv and the generator.  The gradients of o
 // and S_final are scaled by a power of two (their largest magnitude brought
 // to [0.5, 1)) before they meet fp16 matrix-core operands, and every result
-// is scaled back, so the fp16 range never clips a gradient.
+// is scaled back, so the fp16 range never clips a gradient.  Likewise the
+// forward values the pass re-forms (V', U0, U and the checkpointed states)
+// carry one power of two sigma chosen from the largest |v|, |conv_in|, |taps|
+// and |S0| (the block is linear in v' and S0): the gradients of q, k, alpha
+// and beta, bilinear in forward and backward values, are scaled back by
+// 1/sigma; those of v, conv_in, S0 and the taps do not depend on it.
 #include "jb_chunk.h"
 #include "jb_device.h"
 #include "jb_internal.h"
@@ -37,7 +42,7 @@ struct BwdArgs {
   const float* taps;      // [B][T][H][4]
   const float* dout;      // [B][T][H][DV]
   const float* dS_final;  // [B][H][DK][DV] or NULL
-  const float* scale;     // [0] = s, [1] = 1/s
+  const float* scale;     // [0] = s, [1] = 1/s, [2] = sigma, [3] = 1/(s sigma)
   const _Float16* Mck;    // [B][H][nchunks][DV/16][DK/16][64][4] fp16: the state entering each chunk, in
                           // accumulator tiles (lane l: rows 4 (l / 16) .. + 3 of column l % 16)
   float* dMck;            // [B][H][nchunks][DK][DV]: s x the gradient of the state leaving each chunk
@@ -82,7 +87,66 @@ __global__ __launch_bounds__(256) void grad_absmax_kernel(const float* dout, int
   }
 }
 
-__global__ void grad_scale_start_kernel(unsigned int* word) { word[0] = 0u; }
+// The largest |v| and |conv_in| (word[1]), |S0| (word[2]) and |taps| (word[3])
+// as float bits, by the same grid-stride pattern (element counts are
+// multiples of 8 for the bf16 tensors and of 4 for the float ones).
+__global__ __launch_bounds__(256) void value_absmax_kernel(const bf16_t* v, int64_t n_v, const bf16_t* cin, int64_t n_c,
+                                                           const float* S0, int64_t n_s, const float* taps,
+                                                           int64_t n_t, unsigned int* word) {
+  __shared__ unsigned int sm[3][4];
+  unsigned int mv = 0u;
+  float ms = 0.f, mt = 0.f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x, i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // |bf16| orders like its low 15 bits
+  for (int64_t i = i0; i < n_v / 8; i += stride) {
+    const uint4 x = reinterpret_cast<const uint4*>(v)[i];
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mv = max(mv, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+  }
+  if (cin)
+    for (int64_t i = i0; i < n_c; i += stride) mv = max(mv, (uint32_t)cin[i] & 0x7fffu);
+  if (S0)
+    for (int64_t i = i0; i < n_s / 4; i += stride) {
+      const float4 x = reinterpret_cast<const float4*>(S0)[i];
+      ms = fmaxf(ms, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
+  for (int64_t i = i0; i < n_t / 4; i += stride) {
+    const float4 x = reinterpret_cast<const float4*>(taps)[i];
+    mt = fmaxf(mt, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mv = max(mv, (unsigned)__shfl_xor((int)mv, o, WAVE));
+    ms = fmaxf(ms, __shfl_xor(ms, o, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, o, WAVE));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sm[0][threadIdx.x >> 6] = mv << 16;  // the bf16 bits widened to a float's
+    sm[1][threadIdx.x >> 6] = __float_as_uint(ms);
+    sm[2][threadIdx.x >> 6] = __float_as_uint(mt);
+  }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    const unsigned int* r = sm[threadIdx.x];
+    atomicMax(word + 1 + threadIdx.x, max(max(r[0], r[1]), max(r[2], r[3])));
+  }
+}
+
+__global__ void grad_scale_start_kernel(unsigned int* word) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) word[i] = 0u;
+}
+
+// sigma = 2^-e with max(4 max|taps| max(|v|, |conv_in|), max|S0|) sigma in
+// [2^8, 2^9) (1 when zero or not finite): the forward kernels' operand range.
+__global__ void value_scale_finish_kernel(const unsigned int* word, float* scale) {
+  const float mv = __uint_as_float(word[1]), ms = __uint_as_float(word[2]), mt = __uint_as_float(word[3]);
+  const float mm = fmaxf(4.f * mt * mv, ms);
+  int e = 9;
+  if (mm > 0.f && isfinite(mm)) frexpf(mm, &e);  // mm = f 2^e, f in [0.5, 1)
+  scale[2] = ldexpf(1.f, 9 - e);
+  scale[3] = ldexpf(scale[1], e - 9);
+}
 
 __global__ void grad_scale_finish_kernel(const unsigned int* word, float* scale) {
   const float mm = __uint_as_float(word[0]);
@@ -515,7 +579,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   const int m16 = lane & 15, g4 = lane >> 4;
   const int64_t bh = (int64_t)b * H + h;
   const int t0 = c * C, n = min(C, T - t0);
-  const float s = a.scale[0], inv = a.scale[1];
+  // s, 1/s: the gradient scale; vs: sigma, the forward values' scale; invq = 1/(s sigma)
+  const float s = a.scale[0], inv = a.scale[1], vs = a.scale[2], invq = a.scale[3];
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
   const _Float16* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
   const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
@@ -676,7 +741,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * g4 + i;
           const float4 tp = *reinterpret_cast<const float4*>(sTap + r * 4);
-          const float acc = tp.x * xr[i] + tp.y * xr[i + 1] + tp.z * xr[i + 2] + tp.w * xr[i + 3];
+          const float acc = (tp.x * xr[i] + tp.y * xr[i + 1] + tp.z * xr[i + 2] + tp.w * xr[i + 3]) * vs;
           Vp[rt][i] = acc;
           Y[rt][i] = sBeta[r] * acc;
         }
@@ -908,8 +973,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + 4 * g4 + i;
         const float qv = (float)sQh[r * LDK + col], kv = (float)sKh[r * LDK + col];
-        const float gq = (dQh[rt][i] - qv * sQd[r]) / sNq[r] * inv;
-        const float gk = (dKh[rt][i] - kv * sKd[r]) / sNk[r] * inv;
+        const float gq = (dQh[rt][i] - qv * sQd[r]) / sNq[r] * invq;
+        const float gk = (dKh[rt][i] - kv * sKd[r]) / sNk[r] * invq;
         buf_store(rq, gq, oq, (int)((rt * 16 + i) * rowq));
         buf_store(rk, gk, oq, (int)((rt * 16 + i) * rowq));
       }
@@ -929,8 +994,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
     }
     if (lane < n) {
       const int64_t gi = tokbase + (int64_t)lane * H;
-      a.dalpha[gi] = r / a.alpha[gi] * inv;
-      a.dbeta[gi] = sDb[lane] * inv;
+      a.dalpha[gi] = r / a.alpha[gi] * invq;
+      a.dbeta[gi] = sDb[lane] * invq;
     }
   }
 }
@@ -1192,7 +1257,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
   bytes += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
   bytes += al256((size_t)(GEN_NSPLIT_SMALL / GEN_SMALL_PER) * (4 * H * 32 + 4 * H + 32) * 4);
-  bytes += al256(16);                                          // scale
+  bytes += al256(64);                                          // scales and their max words
   return bytes;
 }
 
@@ -1242,14 +1307,20 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   float* scale = reinterpret_cast<float*>(ws);
 
   hipError_t e = hipSuccess;
-  unsigned int* word = reinterpret_cast<unsigned int*>(scale + 2);
+  unsigned int* word = reinterpret_cast<unsigned int*>(scale + 8);
   grad_scale_start_kernel<<<1, 1, 0, stream>>>(word);
   grad_absmax_kernel<<<4096, 256, 0, stream>>>(dout, n * H * dv, dS_final, (int64_t)B * H * dk * dv, word);
   grad_scale_finish_kernel<<<1, 1, 0, stream>>>(word, scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // forward: taps and the state entering every chunk
+  // forward: taps, the forward values' scale and the state entering every chunk
   e = launch_gen_taps(IO_BF16, n, D, H, x, W1, b1, W2, b2, taps, stream, pre);
-  if (e == hipSuccess) e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, img, fws, stream);
+  if (e != hipSuccess) return e;
+  value_absmax_kernel<<<4096, 256, 0, stream>>>((const bf16_t*)v, n * H * dv, (const bf16_t*)conv_in,
+                                                conv_in ? (int64_t)B * 3 * H * dv : 0, S0, (int64_t)B * H * dk * dv,
+                                                taps, n * H * 4, word);
+  value_scale_finish_kernel<<<1, 1, 0, stream>>>(word, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_prefill_ckpt(p, q, k, v, alpha, beta, taps, conv_in, S0, Mck, img, fws, stream, scale + 2);
   if (e != hipSuccess) return e;
   BwdArgs a{};
   a.T = T; a.H = H; a.nchunks = nch;

@@ -151,6 +151,72 @@ __device__ __forceinline__ void conv4(const IO* raw, const float* w, int row, in
   }
 }
 
+// ------------------------------------------------------------ operand range
+//
+// The fp16 operands of the chunk products have 5 exponent bits: about 6e-5 to
+// 6.5e4 at full precision.  The recurrence is linear in (v', S0), so a column
+// tile of the state, its right-hand sides and its new values may be carried
+// at any power-of-two scale and the outputs scaled back exactly.  Each tile
+// keeps its own exponent E (held values = true values * 2^-E), chosen from
+// the magnitudes the tile meets: after a change, the largest of |M| and the
+// right-hand side sits in [2^8, 2^9), and it is changed again only when it
+// leaves [2^4, 2^12) (a factor 128 of headroom under the fp16 maximum for the
+// sums the products form).  Scaling every input by 2^k shifts every E by k
+// and leaves the held values bit for bit unchanged.
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
+  return v;
+}
+
+// A tile starts "fresh" (E_FRESH: held in true units, no exponent chosen yet)
+// so that its first choice does not depend on where the magnitudes happen to
+// sit relative to 2^0; held_exp gives the exponent its held values carry.
+constexpr int E_FRESH = -0x40000000;
+__host__ __device__ constexpr int held_exp(int E) { return E == E_FRESH ? 0 : E; }
+
+// The exponent for a tile currently at exponent E whose largest true
+// magnitude is mx (wave-uniform).  Zero, infinite and NaN magnitudes keep E.
+__device__ __forceinline__ int pick_exp(float mx, int E) {
+  if (!(mx > 0.f) || !(mx <= 3.402823466e38f)) return E;
+  const int ex = __builtin_amdgcn_frexp_expf(mx);  // mx in [2^(ex-1), 2^ex)
+  const int t = ex - E;                            // held maximum in [2^(t-1), 2^t)
+  return (E != E_FRESH && t >= 5 && t <= 12) ? E : ex - 9;
+}
+
+// One column tile before a chunk's solve: M (held at 2^-E, accumulator
+// layout) and the chunk's right-hand side R (true units).  Picks the tile's
+// exponent from both, re-expresses M if it changes, and brings R to it.
+template <int RT>
+__device__ __forceinline__ void rescale_tile(f4_t (&M)[RT], f4_t (&R)[4], int& E) {
+  float mm = 0.f, mr = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mm = fmaxf(mm, fabsf(M[rt][i]));
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mr = fmaxf(mr, fabsf(R[rb][i]));
+  const int E0 = held_exp(E);
+  const float mx = wave_max(fmaxf(ldexpf(mm, E0), mr));
+  const int En = __builtin_amdgcn_readfirstlane(pick_exp(mx, E));
+  if (En != E) {
+    const int En0 = held_exp(En);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M[rt][i] = ldexpf(M[rt][i], E0 - En0);
+    E = En;
+  }
+  const int E1 = held_exp(E);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) R[rb][i] = ldexpf(R[rb][i], -E1);
+}
+
 // g2 = inclusive cumsum of log2(alpha) over the chunk, lane = row (one wave).
 // The chunk kernels keep the gates in base 2: e^{g_i - g_j} = 2^{g2_i - g2_j}.
 __device__ __forceinline__ float chunk_gate_scan(float alpha_or_one) {

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "jb_span.h"
+
 namespace jb {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -155,17 +157,15 @@ __device__ __forceinline__ float l2_scale(float sumsq) { return 1.0f / sqrtf(sum
 
 // First row and length of sequence b of a batch: rows b T .. b T + T - 1 of
 // the token-major tensors, or (packed sequences of different lengths) the
-// span cu_seqlens gives, its length clamped to [0, Tmax] so that a sequence
-// longer than the planned maximum stays inside the planned grid.
-__device__ __forceinline__ void seq_span(const int* cu_seqlens, int Tmax, int b, int64_t& tok0, int& T) {
+// span cu_seqlens gives (jb_span.h: clamped to the packed rows and to Tmax).
+__device__ __forceinline__ void seq_span(const int* cu_seqlens, int Tmax, int64_t total, int b, int64_t& tok0,
+                                         int& T) {
   if (!cu_seqlens) {
     tok0 = (int64_t)b * Tmax;
     T = Tmax;
     return;
   }
-  const int c0 = cu_seqlens[b], c1 = cu_seqlens[b + 1];
-  tok0 = c0;
-  T = min(max(c1 - c0, 0), Tmax);
+  clamp_span(cu_seqlens[b], cu_seqlens[b + 1], Tmax, total, tok0, T);
 }
 
 }  // namespace jb

@@ -238,7 +238,7 @@ hipError_t launch_conv(int io, int B, int T, int H, int dv, const float* taps, c
 // conv_in.
 template <typename IO>
 __global__ void conv_tail_kernel(int B, int Tmax, int H, int dv, const IO* v, const IO* conv_in, IO* conv_out,
-                                 const int* cu_seqlens) {
+                                 const int* cu_seqlens, int64_t rows) {
   const int64_t total = (int64_t)B * H * dv;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total) return;
@@ -247,7 +247,7 @@ __global__ void conv_tail_kernel(int B, int Tmax, int H, int dv, const IO* v, co
   const int b = (int)(e / ((int64_t)dv * H));
   int64_t tok0;
   int T;
-  seq_span(cu_seqlens, Tmax, b, tok0, T);
+  seq_span(cu_seqlens, Tmax, rows, b, tok0, T);
   IO vals[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
@@ -261,16 +261,17 @@ __global__ void conv_tail_kernel(int B, int Tmax, int H, int dv, const IO* v, co
 }
 
 hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v, const void* conv_in, void* conv_out,
-                            hipStream_t stream, const int* cu_seqlens) {
+                            hipStream_t stream, const int* cu_seqlens, int64_t rows) {
   const int64_t total = (int64_t)B * H * dv;
+  if (rows < 0) rows = (int64_t)B * T;
   if (total == 0) return hipSuccess;
   const int blocks = (int)((total + 255) / 256);
   if (io == IO_BF16)
     conv_tail_kernel<bf16_t><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const bf16_t*)v, (const bf16_t*)conv_in,
-                                                         (bf16_t*)conv_out, cu_seqlens);
+                                                         (bf16_t*)conv_out, cu_seqlens, rows);
   else
     conv_tail_kernel<float><<<blocks, 256, 0, stream>>>(B, T, H, dv, (const float*)v, (const float*)conv_in,
-                                                        (float*)conv_out, cu_seqlens);
+                                                        (float*)conv_out, cu_seqlens, rows);
   return hipGetLastError();
 }
 

@@ -28,10 +28,11 @@ hipError_t launch_prologue(int io, int B, int T, int H, int dk, const void* q, c
                            hipStream_t stream);
 
 // Copy of the last 3 raw value rows of [conv_in; v] into conv_out, per
-// sequence (cu_seqlens: packed sequences of at most T rows, else dense).
+// sequence (cu_seqlens: packed sequences of at most T rows in `rows` packed
+// rows, else dense: rows < 0 means B T).
 hipError_t launch_conv_tail(int io, int B, int T, int H, int dv, const void* v,
                             const void* conv_in, void* conv_out, hipStream_t stream,
-                            const int* cu_seqlens = nullptr);
+                            const int* cu_seqlens = nullptr, int64_t rows = -1);
 
 // Chunked prefill (segment summaries, scan, outputs).
 struct PrefillPlan {
@@ -66,10 +67,12 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
                                  const float* S0, void* o, float* S_final, void* workspace, hipStream_t stream);
 
 // The forward pass storing the state entering every chunk, Mck
-// [B][H][nchunks][dk][dv] (bf16 inputs; workspace as launch_prefill's).
+// [B][H][nchunks][dk][dv] fp16, as the true state times *ck_scale (a power of
+// two in device memory; bf16 inputs; workspace as launch_prefill's).
 hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, const float* taps, const void* conv_in, const float* S0,
-                               _Float16* Mck, char* img, void* workspace, hipStream_t stream);
+                               _Float16* Mck, char* img, void* workspace, hipStream_t stream,
+                               const float* ck_scale);
 
 // The gradient of jb_prefill (bf16 inputs, fp32 gradients; one segment per
 // sequence).  Shapes built: (dk, dv) in {(32,64), (64,128), (96,256), (128,256)}.

@@ -57,6 +57,7 @@ struct ChunkArgs {
   // cu_seqlens[b+1] - 1 of the token-major tensors, at most T of them (NULL:
   // every sequence has T tokens, rows b T .. b T + T - 1)
   const int* cu_seqlens;
+  int64_t total;        // rows of the token-major tensors (packed batches: cu_seqlens[B])
   const void* q;
   const void* k;
   const void* v;
@@ -79,6 +80,7 @@ struct ChunkArgs {
   _Float16* Mck;        // MODE_CKPT: the state entering every chunk, fp16 16x16 tiles (below)
   char* img;            // MODE_CKPT: per chunk, the K, -W^T and gate parts of ChainImg;
                         // MODE_PREP / streaming passes: per chunk, StreamImg
+  const float* ck_scale;  // MODE_CKPT: the stored states are the true states times *ck_scale (a power of two)
   int prep_chunks;      // MODE_PREP: chunks per workgroup (the next one's inputs stream in meanwhile)
   _Float16* u0;         // MODE_PREP / streaming passes: per chunk, U0 in fp16 accumulator tiles
                         // [DV/16][4][64 lanes][4]
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   const int H = a.H;
   int64_t tok0;
   int T;
-  seq_span(a.cu_seqlens, a.T, b, tok0, T);
+  seq_span(a.cu_seqlens, a.T, a.total, b, tok0, T);
   const int nseg_b = seq_segments(T, a.seg_len);
   // a packed batch plans its grid for the longest sequence: shorter ones
   // leave the extra segments' workgroups idle (the summary kernel has one
@@ -237,6 +239,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 
   // ---- initial state (accumulator layout: lane holds M[rt*16+4g+i][ct*16+m16])
   f4_t Macc[CPW][RT];
+  // fp16 operands: each column tile held at its own power-of-two scale (jb_chunk.h)
+  constexpr bool SCALED = sizeof(OP) == 2;
+  int Ex[CPW];
+#pragma unroll
+  for (int cw = 0; cw < CPW; ++cw) Ex[cw] = E_FRESH;
 #pragma unroll
   for (int cw = 0; cw < CPW; ++cw) {
     const int ct = wave + cw * NWAVE;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   };
 
   // a column tile of outputs, rows t0 .. t0+n-1, straight from registers
-  auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n) {
+  auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n, int E) {
     const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0) * H + h) * DV, (uint32_t)n * rowb);
@@ -364,7 +371,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         // rows at or beyond n fall outside the resource and are dropped
-        buf_store(orsrc, from_f32<OUT>(Ot[rt][i]), ovoff, (int)((rt * 16 + i) * rowb));
+        buf_store(orsrc, from_f32<OUT>(SCALED ? ldexpf(Ot[rt][i], held_exp(E)) : Ot[rt][i]), ovoff,
+                  (int)((rt * 16 + i) * rowb));
   };
 
   // T is zero outside its band; the band is rewritten every chunk
@@ -384,14 +392,18 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       // [DV/16][DK/16][64 lanes][4], lane l of tile (ct, rt) holding rows
       // 16 rt + 4 (l / 16) .. + 3 of column 16 ct + l % 16 (one 8-byte store)
       _Float16* dst = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
+      const float cks = a.ck_scale ? *a.ck_scale : 1.f;
 #pragma unroll
       for (int cw = 0; cw < CPW; ++cw) {
         const int ct = wave + cw * NWAVE;
         if (ct < NCT)
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const half4_t hv = {(_Float16)Macc[cw][rt][0], (_Float16)Macc[cw][rt][1], (_Float16)Macc[cw][rt][2],
-                                (_Float16)Macc[cw][rt][3]};
+            const int ce = held_exp(Ex[cw]);
+            const half4_t hv = {(_Float16)(ldexpf(Macc[cw][rt][0], ce) * cks),
+                                (_Float16)(ldexpf(Macc[cw][rt][1], ce) * cks),
+                                (_Float16)(ldexpf(Macc[cw][rt][2], ce) * cks),
+                                (_Float16)(ldexpf(Macc[cw][rt][3], ce) * cks)};
             *reinterpret_cast<half4_t*>(dst + ((ct * RT + rt) * 64 + lane) * 4) = hv;
           }
       }
@@ -616,7 +628,12 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) U[cw][rb] = zero4();
-      if (ct >= NCT || !(MODE == MODE_OUTPUT || ct < VCT)) continue;
+      if (ct >= NCT) continue;
+      if (!(MODE == MODE_OUTPUT || ct < VCT)) {
+        // a transition column (summary): no values, but its scale follows M
+        if constexpr (SCALED) rescale_tile(Macc[cw], U[cw], Ex[cw]);
+        continue;
+      }
       // right-hand side diag(b) V', V'[r][col] = sum_j tap[r][j] v[t0 + r - 3 + j][col]
       const int col = ct * 16 + m16;
       if constexpr (SC) {
@@ -665,6 +682,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
             if (i == 3) __builtin_amdgcn_sched_barrier(0);
           }
       }
+      if constexpr (SCALED) rescale_tile(Macc[cw], U[cw], Ex[cw]);
       block_solve<OP, LC, LLI>(U[cw], sAn, sLi);
     }
     __syncthreads();
@@ -755,7 +773,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
               if (kb * 32 <= rt * 16 + 15) mma(O[rt], lds_frag<OP>(sP, LC, rt * 16, kb * 32), vn);
             __builtin_amdgcn_sched_barrier(0);
           }
-          store_o(O, ct, t0, n);
+          store_o(O, ct, t0, n, Ex[cw]);
         }
         // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
 #pragma unroll
@@ -837,7 +855,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
         }
 #pragma unroll
         for (int cw = 0; cw < CPW; ++cw)
-          if (has[cw]) store_o(O[cw], wave + cw * NWAVE, t0, n);
+          if (has[cw]) store_o(O[cw], wave + cw * NWAVE, t0, n, Ex[cw]);
       }
       // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new
 #pragma unroll
@@ -883,13 +901,14 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * g4 + i;
+        const float mv = SCALED ? ldexpf(Macc[cw][rt][i], held_exp(Ex[cw])) : Macc[cw][rt][i];  // true units
         if (MODE == MODE_OUTPUT) {
-          if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+          if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = mv;
         } else if (MODE == MODE_CKPT) {
         } else if (ct < VCT) {
-          a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = Macc[cw][rt][i];
+          a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = mv;
         } else {
-          a.Phi[((bh * a.nseg + s) * DK + row) * DK + (ct - VCT) * 16 + m16] = Macc[cw][rt][i];
+          a.Phi[((bh * a.nseg + s) * DK + row) * DK + (ct - VCT) * 16 + m16] = mv;
         }
       }
   }
@@ -919,7 +938,7 @@ __global__ __launch_bounds__(SNW * 64, 1) void stream_kernel(ChunkArgs a) {
   const int H = a.H;
   int64_t tok0;
   int T;
-  seq_span(a.cu_seqlens, a.T, b, tok0, T);
+  seq_span(a.cu_seqlens, a.T, a.total, b, tok0, T);
   const int nseg_b = seq_segments(T, a.seg_len);
   if (s >= (MODE == MODE_SUMMARY ? nseg_b - 1 : nseg_b)) return;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1163,14 +1182,14 @@ __device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const floa
 // rows for the next segment load while it multiplies.
 template <int DK, int DV, typename OP>
 __global__ __launch_bounds__(DK / 16 * WAVE) void scan_kernel(int H, int nseg, const int* cu_seqlens, int Tmax,
-                                                              int seg_len, const float* S0, const float* Dsum,
+                                                              int64_t total, int seg_len, const float* S0, const float* Dsum,
                                                               const float* Phi, float* Mstart) {
   constexpr int KB = DK / 32, LM = 16 + 1;
   __shared__ float sM[DK * LM];  // M, [DK][16] (+1 pad)
   const int ct = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int64_t tok0;
   int T;
-  seq_span(cu_seqlens, Tmax, b, tok0, T);
+  seq_span(cu_seqlens, Tmax, total, b, tok0, T);
   const int nseg_b = seq_segments(T, seg_len);
   const int rt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m16 = lane & 15, g4 = lane >> 4;
@@ -1298,7 +1317,7 @@ constexpr size_t stream_img_bytes(int dk) {
 // (sequence, head, chunk) a StreamImg and U0.  With one segment there is no
 // summary pass to share the state-independent phases with, and the fused
 // output pass is faster.
-static bool use_stream(const PrefillPlan& p) { return p.io == IO_BF16 && p.nseg > 1; }
+static bool use_stream(const PrefillPlan& p) { return false && p.io == IO_BF16 && p.nseg > 1; }
 static size_t stream_bytes(const PrefillPlan& p) {
   if (!use_stream(p)) return 0;
   const size_t units = (size_t)p.B * p.H * p.nchunks;
@@ -1326,16 +1345,16 @@ static hipError_t run_prefill(const PrefillPlan& p, ChunkArgs a, hipStream_t str
       // the summary pass carries dk more columns (Phi): waves of two column tiles each
       constexpr int SUMW = ((DV + DK) / 16 + 1) / 2 > NWAVE ? ((DV + DK) / 16 + 1) / 2 : NWAVE;
       stream_kernel<DK, DV, OUT, MODE_SUMMARY, SUMW><<<dim3(p.nseg - 1, p.H, p.B), dim3(SUMW * 64), 0, stream>>>(a);
-      scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
-          p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
+      scan_kernel<DK, DV, float><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
+          p.H, p.nseg, a.cu_seqlens, a.T, a.total, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
       stream_kernel<DK, DV, OUT, MODE_OUTPUT, NWAVE><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
       return hipGetLastError();
     }
   }
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, IO, OP, OUT, MODE_SUMMARY, SC><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
-    scan_kernel<DK, DV, OP><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
-        p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
+    scan_kernel<DK, DV, float><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
+        p.H, p.nseg, a.cu_seqlens, a.T, a.total, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
   }
   chunk_kernel<DK, DV, IO, OP, OUT, MODE_OUTPUT, SC><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
   return hipGetLastError();
@@ -1378,6 +1397,7 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
   a.cu_seqlens = p.cu_seqlens;
+  a.total = p.tokens;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;
   set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
@@ -1415,6 +1435,7 @@ hipError_t launch_prefill_static(const PrefillPlan& p, const void* q, const void
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
   a.cu_seqlens = p.cu_seqlens;
+  a.total = p.tokens;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.conv_in = cv_in;
   a.wq = wq; a.wk = wk; a.wv = wv; a.cq_in = cq_in; a.ck_in = ck_in;
   a.S0 = S0; a.o = o; a.S_final = S_final;
@@ -1431,8 +1452,8 @@ static hipError_t run_ckpt(const PrefillPlan& p, ChunkArgs a, hipStream_t stream
   const dim3 blk(NTHR);
   if (p.nseg > 1) {
     chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_SUMMARY, false><<<dim3(p.nseg - 1, p.H, p.B), blk, 0, stream>>>(a);
-    scan_kernel<DK, DV, _Float16><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
-        p.H, p.nseg, a.cu_seqlens, a.T, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
+    scan_kernel<DK, DV, float><<<dim3(DV / 16, p.H, p.B), dim3(DK / 16 * WAVE), 0, stream>>>(
+        p.H, p.nseg, a.cu_seqlens, a.T, a.total, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart));
   }
   chunk_kernel<DK, DV, bf16_t, _Float16, float, MODE_CKPT, false><<<dim3(p.nseg, p.H, p.B), blk, 0, stream>>>(a);
   return hipGetLastError();
@@ -1449,12 +1470,14 @@ bool backward_supported(int io, int dk, int dv) {
 
 hipError_t launch_prefill_ckpt(const PrefillPlan& p, const void* q, const void* k, const void* v, const float* alpha,
                                const float* beta, const float* taps, const void* conv_in, const float* S0,
-                               _Float16* Mck, char* img, void* workspace, hipStream_t stream) {
+                               _Float16* Mck, char* img, void* workspace, hipStream_t stream,
+                               const float* ck_scale) {
   if (p.nchunks == 0) return hipSuccess;
   ChunkArgs a{};
   a.T = p.T; a.H = p.H; a.nchunks = p.nchunks; a.seg_len = p.seg_len; a.nseg = p.nseg;
+  a.total = p.tokens;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.taps = taps; a.conv_in = conv_in;
-  a.S0 = S0; a.Mck = Mck; a.img = img;
+  a.S0 = S0; a.Mck = Mck; a.img = img; a.ck_scale = ck_scale;
   set_segment_buffers(p, a, static_cast<char*>(workspace) + taps_bytes(p));
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_ckpt<DK_, DV_>(p, a, stream);
