@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libjetblock.so")
-SOURCES = ["jb_api.hip", "jb_gen.hip", "jb_prefill.hip", "jb_decode.hip", "jb_proj.hip", "jb_backward.hip"]
+SOURCES = ["jb_api.hip", "jb_gen.hip", "jb_prefill.hip", "jb_fwd.hip", "jb_decode.hip", "jb_proj.hip",
+           "jb_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

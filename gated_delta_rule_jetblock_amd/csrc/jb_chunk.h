@@ -49,6 +49,13 @@ constexpr int GATE_WAVE = 7; // the wave that loads and scans the gates
 constexpr int NCU = 256;     // compute units of one MI355X
 
 
+// Segments sequence b is cut into (at least one, which carries the state
+// through an empty sequence).
+__device__ __forceinline__ int seq_segments(int T, int seg_len) {
+  const int nch = (T + C - 1) / C;
+  return max(1, (nch + seg_len - 1) / seg_len);
+}
+
 // the lower-triangular tiles (i, j), j <= i, of a chunk's 4 x 4 tile grid in
 // row order, two bits per coordinate: tile t is ((kLowI >> 2t) & 3, (kLowJ >> 2t) & 3)
 constexpr uint32_t kLowI = 0xffa94u;  // rows    0 1 1 2 2 2 3 3 3 3

@@ -1,0 +1,720 @@
+// jb_fwd.hip -- the chunked JetBlock prefill for bf16 inputs, one fused pass
+// per segment.
+//
+// The recurrence and its chunked (WY/UT) form are those of jb_prefill.hip
+// (Gated DeltaNet time mixing: Jet-Nemotron csdn translation, section 2.4;
+// dynamic causal conv of the values, section 2.4 and the xugj520 blog,
+// section 2.2).  A long sequence is cut into segments; the summary pass runs
+// each segment but the last from the zero state on augmented columns [D | Phi]
+// (Phi starting at I), the scan chains the segment maps, and the output pass
+// reruns every segment from its true start state.  Each pass forms every
+// chunk's state-independent tiles from the raw q, k, v rows itself, so the only
+// HBM traffic is the compulsory inputs (read twice for all but the last
+// segment) and o.
+//
+// Workgroup: one per (segment, head, sequence); each wave owns two 16-column
+// tiles of the state (value columns, or transition columns in the summary),
+// held in fp32 accumulators at a per-tile power-of-two scale (jb_chunk.h).
+// Per chunk of C = 64 tokens, five barriers:
+//   A  normalise the staged q, k rows into K^, Q^ (fp16); the gate wave scans
+//      the gates and writes the conv band;
+//   B  Gram tiles K^K^T and Q^K^T -> -A, its fp32 diagonal blocks, P (written
+//      as whole rows: each product is formed transposed); every value-tile
+//      wave forms its right-hand side diag(b) V' = Band V_ext on the bf16
+//      matrix cores and picks its tiles' exponents;
+//   C  one wave inverts the four 16x16 diagonal blocks of I + A while the
+//      others form Q^ M (output pass);
+//   D  blocked forward substitution on the matrix cores: -W^T (six waves, one
+//      dk column tile each) and U0 for every value tile;
+//   E  V_new = U0 - W M, O = diag(gamma) Q^ M + P V_new (stored), and
+//      M <- gamma_C M + K^T diag(e^{g_C - g}) V_new.
+// The next chunk's q, k and gate rows move into LDS by DMA from phase B on and
+// its value rows from phase C on, so their HBM latency overlaps the chunk.
+//
+// Operands read down a column of a row-major tile (K^ as K^T, -W^T as W, the
+// value rows) come from ds_read_b64_tr_b16: within each group of 16 lanes,
+// lane 4a + b receives element b of the 8-byte pieces addressed by lanes
+// 4j + a (j = 0..3), so one instruction yields four K values of a fragment.
+#include <algorithm>
+
+#include "jb_chunk.h"
+#include "jb_device.h"
+#include "jb_internal.h"
+
+namespace jb {
+namespace fwd {
+
+enum { SUMMARY = 0, OUTPUT = 1 };
+
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) s4_t lds_s4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// ------------------------------------------------------------ fragments
+
+__device__ __forceinline__ half8_t cat8(h4_t lo, h4_t hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f4_t mfma(const half8_t& a, const half8_t& b, const f4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Fragment reads take this lane's base address in a tile, formed once, plus a
+// byte offset that is a compile-time constant after unrolling, so that the
+// constant lands in the LDS instruction's offset field instead of a register.
+
+// four 16-bit values down a column of a row-major 16-bit tile: this lane
+// supplies the address of its 8-byte piece (see the file header)
+__device__ __forceinline__ s4_t tr4(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p);
+}
+
+// Lane bases for reads down the columns of a row-major 16-bit tile (row stride
+// ld elements): the supplying lane 16g + 4j + a points at row r(g) + j,
+// column 4a, with r(g) = 4g (kperm halves at rows k0 and k0 + 16) or 8g
+// (contiguous halves at rows k0 and k0 + 4).
+__device__ __forceinline__ const lds_char* tr_base_kp(const lds_char* tile, int ld) {
+  const int l = lane_id();
+  return tile + ((4 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2;
+}
+__device__ __forceinline__ const lds_char* tr_base_ct(const lds_char* tile, int ld) {
+  const int l = lane_id();
+  return tile + ((8 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2;
+}
+// Fragment down the columns from a kperm base: lane 16g + n receives
+// tile[k0 + 4g + j][c0 + n], then tile[k0 + 16 + 4g + j][c0 + n]
+template <int LD>
+__device__ __forceinline__ half8_t tr_frag_kp(const lds_char* base, int k0, int c0) {
+  const s4_t lo = tr4(base + (k0 * LD + c0) * 2);
+  const s4_t hi = tr4(base + ((k0 + 16) * LD + c0) * 2);
+  return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// ... from a contiguous base: rows k0 + 8g + j, then k0 + 8g + 4 + j
+template <int LD>
+__device__ __forceinline__ half8_t tr_frag_ct(const lds_char* base, int k0, int c0) {
+  const s4_t lo = tr4(base + (k0 * LD + c0) * 2);
+  const s4_t hi = tr4(base + ((k0 + 4) * LD + c0) * 2);
+  return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lane bases for reads along the rows (lane 16g + m: row m, column 4g (kperm)
+// or 8g (contiguous)) of a row-major fp16 tile
+__device__ __forceinline__ const _Float16* row_base_kp(const _Float16* tile, int ld) {
+  const int l = lane_id();
+  return tile + (l & 15) * ld + 4 * (l >> 4);
+}
+__device__ __forceinline__ const _Float16* row_base_ct(const _Float16* tile, int ld) {
+  const int l = lane_id();
+  return tile + (l & 15) * ld + 8 * (l >> 4);
+}
+// Fragment along rows r0.. with K in the accumulator-chaining order (kperm:
+// columns k0 + 4g .. + 3 and k0 + 16 + 4g .. + 3)
+template <int LD>
+__device__ __forceinline__ half8_t row_frag_kp(const _Float16* base, int r0, int k0) {
+  const _Float16* p = base + r0 * LD + k0;
+  return cat8(*reinterpret_cast<const h4_t*>(p), *reinterpret_cast<const h4_t*>(p + 16));
+}
+// ... K contiguous (columns k0 + 8g .. + 7): one 16-byte read
+template <int LD>
+__device__ __forceinline__ half8_t row_frag_ct(const _Float16* base, int r0, int k0) {
+  return *reinterpret_cast<const half8_t*>(base + r0 * LD + k0);
+}
+
+// B fragment (kperm order) from two accumulator tiles: rows 0..15 and 16..31
+__device__ __forceinline__ half8_t acc_frag2(const f4_t& lo, const f4_t& hi) {
+  const h2_t a = __builtin_convertvector(f2_t{lo[0], lo[1]}, h2_t);
+  const h2_t b = __builtin_convertvector(f2_t{lo[2], lo[3]}, h2_t);
+  const h2_t c = __builtin_convertvector(f2_t{hi[0], hi[1]}, h2_t);
+  const h2_t d = __builtin_convertvector(f2_t{hi[2], hi[3]}, h2_t);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// the same with every row scaled first (rows of lo by s0, of hi by s1)
+__device__ __forceinline__ half8_t acc_frag2_scaled(const f4_t& lo, const f4_t& hi, const float4& s0,
+                                                    const float4& s1) {
+  return acc_frag2(f4_t{lo[0] * s0.x, lo[1] * s0.y, lo[2] * s0.z, lo[3] * s0.w},
+                   f4_t{hi[0] * s1.x, hi[1] * s1.y, hi[2] * s1.z, hi[3] * s1.w});
+}
+
+// the blocked triangular solve of jb_chunk.h on these fragments, Y = (I + A)^{-1} Y,
+// from the kperm row bases of -A (row stride LC) and of the diagonal-block
+// inverses (LLI, columns 16..31 zero)
+template <int LC, int LLI>
+__device__ __forceinline__ void solve(f4_t (&Y)[4], const _Float16* bAn, const _Float16* bLi) {
+  const f4_t z = zero4();
+  Y[0] = mfma(row_frag_kp<LLI>(bLi, 0, 0), acc_frag2(Y[0], z), z);
+  Y[1] = mfma(row_frag_kp<LC>(bAn, 16, 0), acc_frag2(Y[0], z), Y[1]);
+  Y[1] = mfma(row_frag_kp<LLI>(bLi, 16, 0), acc_frag2(Y[1], z), z);
+  const half8_t f01 = acc_frag2(Y[0], Y[1]);
+  Y[2] = mfma(row_frag_kp<LC>(bAn, 32, 0), f01, Y[2]);
+  Y[3] = mfma(row_frag_kp<LC>(bAn, 48, 0), f01, Y[3]);
+  Y[2] = mfma(row_frag_kp<LLI>(bLi, 32, 0), acc_frag2(Y[2], z), z);
+  Y[3] = mfma(row_frag_kp<LC>(bAn, 48, 32), acc_frag2(Y[2], z), Y[3]);
+  Y[3] = mfma(row_frag_kp<LLI>(bLi, 48, 0), acc_frag2(Y[3], z), z);
+}
+
+// Direct buffer -> LDS loads: a piece of `size` bytes at byte offset voff of
+// the resource for every active lane, landing at lds + size * lane (lds is
+// wave-uniform); offsets past the resource read as zero
+template <int SIZE>
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_char* lds) {
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, 0, 0, 0);
+}
+
+// Barrier for data exchanged through LDS: this wave's LDS accesses complete,
+// then s_barrier.  Outstanding global loads (the next chunk's LDS DMA) and
+// stores stay in flight.
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ------------------------------------------------------------ geometry
+
+template <int DK, int DV, int MODE>
+struct Geo {
+  static constexpr bool OUTM = MODE == OUTPUT;
+  static constexpr int NCT = OUTM ? DV / 16 : (DV + DK) / 16;  // column tiles
+  static constexpr int VCT = DV / 16;                          // value column tiles
+  static constexpr int RT = DK / 16, KB = DK / 32;
+  static constexpr int NW = 8;                                 // waves
+  static constexpr int TPW = (NCT + NW - 1) / NW;              // tiles per wave: wave w owns w, w + 8, ..
+  static constexpr int GW = NW - 1;                            // gate wave
+  static constexpr int IW = NW - 2;                            // inverse wave
+  static constexpr int LDK = DK + 8, LC = C + 8, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
+  static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
+  static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
+  static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
+  static constexpr int oKh = a16(oT + 2 * 4 * 16 * LT * 2);     // [C][LDK] K^
+  static constexpr int szQh = OUTM ? C * LDK * 2 : 0;
+  static constexpr int szWt = DK * LC * 2;
+  static constexpr int oQW = a16(oKh + C * LDK * 2);            // Q^ (output), then -W^T [DK][LC]
+  static constexpr int oAn = a16(oQW + (szQh > szWt ? szQh : szWt));  // [C][LC] -A
+  static constexpr int oAd = a16(oAn + C * LC * 2);             // [C][LAD] f32 diagonal blocks of A
+  static constexpr int oLi = a16(oAd + C * LAD * 4);            // [C][LLI] their inverses
+  static constexpr int oP = a16(oLi + C * LLI * 2);             // [C][LC] P (output)
+  static constexpr int WORK = a16(oP + (OUTM ? C * LC * 2 : 0));
+  static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + (C + 3) * LV * 2;
+  static_assert(WORK + STAGE <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(RT <= NW, "one wave per W column tile");
+  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0, "aligned rows");
+};
+
+// ------------------------------------------------------------ kernel
+
+template <int DK, int DV, typename OUT, int MODE>
+__global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
+  using G = Geo<DK, DV, MODE>;
+  constexpr bool OUTM = G::OUTM;
+  constexpr int NCT = G::NCT, VCT = G::VCT, RT = G::RT, KB = G::KB, NW = G::NW, TPW = G::TPW;
+  constexpr int LDK = G::LDK, LC = G::LC, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
+
+  // working tiles, and the DMA staging areas as arrays of their own (so the
+  // compiler can tell that reads of the tiles never wait on the DMA)
+  __shared__ __attribute__((aligned(16))) char work[G::WORK];
+  __shared__ __attribute__((aligned(16))) bf16_t sKr[C * DK];
+  __shared__ __attribute__((aligned(16))) bf16_t sQr[OUTM ? C * DK : 8];
+  __shared__ __attribute__((aligned(16))) float sGr[C * 6];  // alpha [C], beta [C], taps [C][4]
+  __shared__ __attribute__((aligned(16))) bf16_t sV[(C + 3) * LV];
+  float* sG = reinterpret_cast<float*>(work + G::oG);
+  float* sGam = sG + C;
+  float* sBeta = sG + 2 * C;
+  float* sDec = sG + 3 * C;
+  bf16_t* sT = reinterpret_cast<bf16_t*>(work + G::oT);
+  _Float16* sKh = reinterpret_cast<_Float16*>(work + G::oKh);
+  _Float16* sQh = reinterpret_cast<_Float16*>(work + G::oQW);
+  _Float16* sAn = reinterpret_cast<_Float16*>(work + G::oAn);
+  float* sAd = reinterpret_cast<float*>(work + G::oAd);
+  _Float16* sLi = reinterpret_cast<_Float16*>(work + G::oLi);
+  _Float16* sP = reinterpret_cast<_Float16*>(work + G::oP);
+  // the same tiles as LDS addresses, for the transposed reads and the DMA
+  const lds_char* lKh = (const lds_char*)work + G::oKh;
+  const lds_char* lWt = (const lds_char*)work + G::oQW;  // -W^T [DK][LC]
+  const lds_char* lV = (const lds_char*)sV;
+  lds_char* lKr = (lds_char*)sKr;
+  lds_char* lQr = (lds_char*)sQr;
+  lds_char* lGr = (lds_char*)sGr;
+  lds_char* lVw = (lds_char*)sV;
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int H = a.H;
+  int64_t tok0;
+  int T;
+  seq_span(a.cu_seqlens, a.T, a.total, b, tok0, T);
+  const int nseg_b = seq_segments(T, a.seg_len);
+  if (s >= (OUTM ? nseg_b : nseg_b - 1)) return;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int m16 = lane & 15, g4 = lane >> 4;
+  const bf16_t* q = a.q;
+  const bf16_t* k = a.k;
+  const bf16_t* v = a.v;
+  const bf16_t* cin = a.conv_in;
+  const int64_t bh = (int64_t)b * H + h;
+  // column tile cw of this wave: wave + 8 cw; value tiles have right-hand sides
+  auto tile = [&](int cw) { return wave + cw * NW; };
+  auto has = [&](int cw) { return wave + cw * NW < NCT; };
+  auto isval = [&](int cw) { return wave + cw * NW < VCT; };
+
+  // this lane's bases in the tiles
+  const lds_char* tKkp = tr_base_kp(lKh, LDK);   // K^ down its columns (K^T; the W right-hand side)
+  const lds_char* tWkp = tr_base_kp(lWt, LC);    // -W^T down its columns (-W)
+  const lds_char* tVct = tr_base_ct(lV, LV);     // value rows down their columns
+  const _Float16* rKct = row_base_ct(sKh, LDK);  // rows of K^, Q^ (Gram tiles)
+  const _Float16* rQct = row_base_ct(sQh, LDK);
+  const _Float16* rQkp = row_base_kp(sQh, LDK);  // rows of Q^ (Q^ M)
+  const _Float16* rPkp = row_base_kp(sP, LC);
+  const _Float16* rAkp = row_base_kp(sAn, LC);
+  const _Float16* rLkp = row_base_kp(sLi, LLI);
+
+  // ---- initial state, accumulator layout: lane holds M[16 rt + 4 g + i][16 ct + m16]
+  f4_t Macc[TPW][RT];
+  int Ex[TPW];
+#pragma unroll
+  for (int cw = 0; cw < TPW; ++cw) {
+    const int ct = tile(cw);
+    Ex[cw] = E_FRESH;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      Macc[cw][rt] = zero4();
+      if (!has(cw)) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        if (!OUTM) {
+          if (ct >= VCT) Macc[cw][rt][i] = (row == (ct - VCT) * 16 + m16) ? 1.f : 0.f;
+        } else {
+          const float* src = a.nseg > 1 ? a.Mstart + ((bh * a.nseg + s) * DK) * DV
+                                        : (a.S0 ? a.S0 + bh * DK * DV : nullptr);
+          Macc[cw][rt][i] = src ? src[row * DV + ct * 16 + m16] : 0.f;
+        }
+      }
+    }
+  }
+
+  // tiles never rewritten: the band outside its diagonals, P above its block diagonal
+  for (int e = tid; e < 2 * 4 * 16 * LT / 8; e += NW * 64)
+    reinterpret_cast<uint4*>(sT)[e] = make_uint4(0u, 0u, 0u, 0u);
+  if (OUTM)
+    for (int e = tid; e < C * C; e += NW * 64) {
+      const int r = e / C, c = e % C;
+      if ((c >> 4) > (r >> 4)) sP[r * LC + c] = (_Float16)0.f;
+    }
+
+  const int c_begin = s * a.seg_len;
+  const int c_end = min((T + C - 1) / C, c_begin + a.seg_len);
+
+  // ---- raw inputs of chunk cc into the staging areas by DMA (a buffer
+  // resource per chunk and stream, per-lane 32-bit byte offsets); rows past
+  // the sequence are left as they are (the prologue masks them) except the
+  // value rows, which are zeroed (the band multiplies them by zero
+  // coefficients, and stale values could be non-finite)
+  const uint32_t rowq = (uint32_t)(H * DK * 2), rowv = (uint32_t)(H * DV * 2);  // bytes between tokens
+  auto issue_qkg = [&](int cc) {
+    const int t0c = cc * C, nc = min(C, T - t0c);
+    constexpr int PPK = DK / 8;  // 16-byte pieces per q or k row
+    const int64_t e0 = (tok0 + t0c) * H * DK + (int64_t)h * DK;
+    const uint32_t bytes = (uint32_t)(nc - 1) * rowq + DK * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + e0, bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + e0, bytes);
+    for (int j = wave; j * 64 < C * PPK; j += NW) {
+      const int p = j * 64 + lane, r = p / PPK, pc = p % PPK;
+      const uint32_t off = (uint32_t)r * rowq + (uint32_t)pc * 16;
+      if (p < C * PPK && r < nc) {
+        dma_buf<16>(rk, off, lKr + j * 1024);
+        if (OUTM) dma_buf<16>(rq, off, lQr + j * 1024);
+      }
+    }
+    if (wave == G::GW && lane < nc) {
+      const int64_t gidx = (tok0 + t0c) * H + h;
+      const uint32_t gb = (uint32_t)(nc - 1) * H * 4 + 4;
+      const uint32_t off = (uint32_t)(lane * H) * 4;
+      dma_buf<4>(make_rsrc(a.alpha + gidx, gb), off, lGr);
+      dma_buf<4>(make_rsrc(a.beta + gidx, gb), off, lGr + C * 4);
+      dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, lGr + 2 * C * 4);
+    }
+  };
+  auto issue_v = [&](int cc) {
+    const int t0c = cc * C, nc = min(C, T - t0c);
+    constexpr int PPR = DV / 8;  // 16-byte pieces per value row
+    // rows from token rb0 (the halo's first row, or the chunk's when it starts the sequence)
+    const int rb0 = t0c >= 3 ? t0c - 3 : t0c;
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(v + ((tok0 + rb0) * H + h) * DV, (uint32_t)(t0c + nc - 1 - rb0) * rowv + DV * 2);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(cin ? cin + ((int64_t)b * 3 * H + h) * DV : v, cin ? 2 * rowv + DV * 2 : 0u);
+    for (int r = wave; r < C + 3; r += NW) {  // staged row r holds token t0c - 3 + r
+      const int t = t0c - 3 + r;
+      lds_char* dst = lVw + r * LV * 2;
+      if (lane < PPR) {
+        if (t >= 0 && r - 3 < nc)
+          dma_buf<16>(rv, (uint32_t)(t - rb0) * rowv + lane * 16, dst);
+        else if (t < 0 && cin)
+          dma_buf<16>(rc, (uint32_t)(3 + t) * rowv + lane * 16, dst);
+        else
+          *(__attribute__((address_space(3))) u4_t*)(dst + lane * 16) = u4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  // a column tile of outputs, rows t0 .. t0 + n - 1, straight from registers
+  auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n, int E) {
+    const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0) * H + h) * DV, (uint32_t)n * rowb);
+    const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
+    const int e = held_exp(E);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        // rows at or beyond n fall outside the resource and are dropped
+        buf_store(orsrc, from_f32<OUT>(ldexpf(Ot[rt][i], e)), ovoff, (int)((rt * 16 + i) * rowb));
+  };
+
+  if (c_begin < c_end) {
+    issue_qkg(c_begin);
+    issue_v(c_begin);
+  }
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * C;
+    const int n = min(C, T - t0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA transfers (and earlier stores) are done
+    bar();                          // ... and every other wave's; the previous chunk's reads are done
+
+    // ================= A: normalise q, k; gates and band =================
+    {
+      constexpr int E = DK / 8;
+      const int row = tid >> 3, part = tid & 7;
+      const bool valid = row < n;
+      float kv[E];
+      load_row_part<bf16_t>(sKr + row * DK + part * E, kv, E, valid);
+      float sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) sk += kv[e] * kv[e];
+      const float rk = l2_scale(group_sum<8>(sk));
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const h2_t x0 = __builtin_convertvector(f2_t{kv[e] * rk, kv[e + 1] * rk}, h2_t);
+        const h2_t x1 = __builtin_convertvector(f2_t{kv[e + 2] * rk, kv[e + 3] * rk}, h2_t);
+        *reinterpret_cast<h4_t*>(sKh + row * LDK + part * E + e) = h4_t{x0[0], x0[1], x1[0], x1[1]};
+      }
+      if (OUTM) {
+        float qv[E];
+        load_row_part<bf16_t>(sQr + row * DK + part * E, qv, E, valid);
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) sq += qv[e] * qv[e];
+        const float rq = l2_scale(group_sum<8>(sq));
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const h2_t x0 = __builtin_convertvector(f2_t{qv[e] * rq, qv[e + 1] * rq}, h2_t);
+          const h2_t x1 = __builtin_convertvector(f2_t{qv[e + 2] * rq, qv[e + 3] * rq}, h2_t);
+          *reinterpret_cast<h4_t*>(sQh + row * LDK + part * E + e) = h4_t{x0[0], x0[1], x1[0], x1[1]};
+        }
+      }
+    }
+    if (wave == G::GW) {
+      const bool valid = lane < n;
+      const float al = valid ? sGr[lane] : 1.f;
+      const float be = valid ? sGr[C + lane] : 0.f;
+      const float4 tp = valid ? reinterpret_cast<const float4*>(sGr + 2 * C)[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float g = chunk_gate_scan(al);
+      const float gC = __shfl(g, C - 1, WAVE);
+      sG[lane] = g;
+      sGam[lane] = fast_exp2(g);
+      sBeta[lane] = be;
+      sDec[lane] = fast_exp2(gC - g);
+      // row `lane` of the band with Band[r][r + j] = b_r tap_r[j], so that
+      // diag(b) V' = Band V_ext runs on the matrix cores: row tile rt takes the
+      // 32 staged value rows from 16 rt (from C + 3 - 32 for the last tile),
+      // each coefficient split into bf16 hi + lo
+      const int rt = lane >> 4, m = lane & 15, k0 = (rt < 3 ? 0 : 16 * rt - (C + 3 - 32)) + m;
+      const float cf[4] = {be * tp.x, be * tp.y, be * tp.z, be * tp.w};
+      bf16_t* th = sT + (rt * 16 + m) * LT + k0;
+      bf16_t* tl = th + 4 * 16 * LT;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16_t hi = f32_to_bf16(cf[j]);
+        th[j] = hi;
+        tl[j] = f32_to_bf16(cf[j] - bf16_to_f32(hi));
+      }
+    }
+    bar();
+    if (c + 1 < c_end) issue_qkg(c + 1);
+
+    // ================= B: Gram tiles; right-hand sides; tile exponents =================
+    for (int job = wave; job < 10; job += NW) {
+      const int ti = (kLowI >> (2 * job)) & 3, tj = (kLowJ >> (2 * job)) & 3;
+      // formed transposed: lane holds (Y K^T)[16 ti + m16][16 tj + 4 g4 + i], Y = K^ or Q^
+      f4_t kk = zero4(), qk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const half8_t ak = row_frag_ct<LDK>(rKct, tj * 16, kb * 32);
+        kk = mfma(ak, row_frag_ct<LDK>(rKct, ti * 16, kb * 32), kk);
+        if (OUTM) qk = mfma(ak, row_frag_ct<LDK>(rQct, ti * 16, kb * 32), qk);
+      }
+      const int r = ti * 16 + m16, c0 = tj * 16 + 4 * g4;
+      const float gr = sG[r], br = sBeta[r];
+      const float4 gc = *reinterpret_cast<const float4*>(sG + c0);
+      const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
+      float an[4], pp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float E = fast_exp2(gr - gcv[i]);
+        const int cc = c0 + i;
+        an[i] = cc < r ? br * E * kk[i] : 0.f;
+        pp[i] = cc <= r ? E * qk[i] : 0.f;
+      }
+      const h2_t a0 = __builtin_convertvector(f2_t{-an[0], -an[1]}, h2_t);
+      const h2_t a1 = __builtin_convertvector(f2_t{-an[2], -an[3]}, h2_t);
+      *reinterpret_cast<h4_t*>(sAn + r * LC + c0) = h4_t{a0[0], a0[1], a1[0], a1[1]};
+      if (ti == tj) *reinterpret_cast<float4*>(sAd + r * LAD + 4 * g4) = make_float4(an[0], an[1], an[2], an[3]);
+      if (OUTM) {
+        const h2_t p0 = __builtin_convertvector(f2_t{pp[0], pp[1]}, h2_t);
+        const h2_t p1 = __builtin_convertvector(f2_t{pp[2], pp[3]}, h2_t);
+        *reinterpret_cast<h4_t*>(sP + r * LC + c0) = h4_t{p0[0], p0[1], p1[0], p1[1]};
+      }
+    }
+    f4_t U[TPW][4];
+#pragma unroll
+    for (int cw = 0; cw < TPW; ++cw) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) U[cw][rt] = zero4();
+      if (!isval(cw)) continue;
+      // right-hand side diag(b) V': tile rt = (Band_hi + Band_lo) V_ext[window rows][column tile],
+      // the value rows taken exactly as bf16 operands (K order 8g + j on both sides)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
+        const bf16x8_t th = *reinterpret_cast<const bf16x8_t*>(sT + (rt * 16 + m16) * LT + 8 * g4);
+        const bf16x8_t tl = *reinterpret_cast<const bf16x8_t*>(sT + ((4 + rt) * 16 + m16) * LT + 8 * g4);
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, tr_frag_ct<LV>(tVct, s0, tile(cw) * 16));
+        const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
+        U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int cw = 0; cw < TPW; ++cw)
+      if (has(cw)) rescale_tile(Macc[cw], U[cw], Ex[cw]);
+    bar();
+    if (c + 1 < c_end) issue_v(c + 1);
+
+    // ================= C: diagonal-block inverses; Q^ M =================
+    if (wave == G::IW) {
+      // four 16x16 blocks of I + A by forward substitution, one column per lane
+      const int base = (lane >> 4) * 16;
+      int jc = lane & 15;
+      asm volatile("" : "+v"(jc));  // formed per chunk: the 16 identity values are not held across the loop
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == jc) ? 1.f : 0.f;
+        const float* arow = sAd + (base + i) * LAD;
+#pragma unroll
+        for (int k4 = 0; k4 < i; k4 += 4) {
+          const float4 av = *reinterpret_cast<const float4*>(arow + k4);
+          acc -= av.x * x[k4];
+          if (k4 + 1 < i) acc -= av.y * x[k4 + 1];
+          if (k4 + 2 < i) acc -= av.z * x[k4 + 2];
+          if (k4 + 3 < i) acc -= av.w * x[k4 + 3];
+        }
+        x[i] = acc;
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sLi[(base + i) * LLI + jc] = (_Float16)x[i];
+        sLi[(base + i) * LLI + 16 + jc] = (_Float16)0.f;  // the zero half a 32-deep fragment reads
+      }
+    }
+    f4_t O[OUTM ? TPW : 1][4];
+    if constexpr (OUTM) {
+#pragma unroll
+      for (int cw = 0; cw < TPW; ++cw)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        half8_t mk[TPW];  // this chunk's M as fp16 B fragments (kperm rows)
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw) mk[cw] = acc_frag2(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const half8_t aq = row_frag_kp<LDK>(rQkp, rt * 16, kb * 32);
+#pragma unroll
+          for (int cw = 0; cw < TPW; ++cw)
+            if (has(cw)) O[cw][rt] = mfma(aq, mk[cw], O[cw][rt]);
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 gm = *reinterpret_cast<const float4*>(sGam + rt * 16 + 4 * g4);
+        const float gmv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[cw][rt][i] *= gmv[i];
+      }
+    }
+    bar();
+
+    // ================= D: -W^T and U0 by blocked forward substitution =================
+    {
+      const int jw = NW - 1 - wave;  // W column tile of this wave
+      if (jw < RT) {
+        // right-hand side diag(b gamma) K^, column tile jw, read down the columns of K^
+        f4_t Y[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const h4_t kh = __builtin_bit_cast(h4_t, tr4(tKkp + (rb * 16 * LDK + jw * 16) * 2));
+          const float4 bt = *reinterpret_cast<const float4*>(sBeta + rb * 16 + 4 * g4);
+          const float4 gm = *reinterpret_cast<const float4*>(sGam + rb * 16 + 4 * g4);
+          Y[rb] = f4_t{bt.x * gm.x * (float)kh[0], bt.y * gm.y * (float)kh[1], bt.z * gm.z * (float)kh[2],
+                       bt.w * gm.w * (float)kh[3]};
+        }
+        solve<LC, LLI>(Y, rAkp, rLkp);
+        // -W^T: row jw*16 + m16, columns 16 rb + 4 g4 .. + 3
+        _Float16* sWt = reinterpret_cast<_Float16*>(work + G::oQW);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const h2_t w0 = __builtin_convertvector(f2_t{-Y[rb][0], -Y[rb][1]}, h2_t);
+          const h2_t w1 = __builtin_convertvector(f2_t{-Y[rb][2], -Y[rb][3]}, h2_t);
+          *reinterpret_cast<h4_t*>(sWt + (jw * 16 + m16) * LC + rb * 16 + 4 * g4) = h4_t{w0[0], w0[1], w1[0], w1[1]};
+        }
+      }
+#pragma unroll
+      for (int cw = 0; cw < TPW; ++cw)
+        if (isval(cw)) solve<LC, LLI>(U[cw], rAkp, rLkp);
+    }
+    bar();
+
+    // ================= E: state-dependent part of the chunk =================
+    // V_new = U0 - W M (W^T read down its columns; kperm rows of dk)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      half8_t mk[TPW];
+#pragma unroll
+      for (int cw = 0; cw < TPW; ++cw) mk[cw] = acc_frag2(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const half8_t aw = tr_frag_kp<LC>(tWkp, kb * 32, rt * 16);
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw)
+          if (has(cw)) U[cw][rt] = mfma(aw, mk[cw], U[cw][rt]);
+      }
+    }
+    if constexpr (OUTM) {
+      // O += P V_new, then the outputs
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        half8_t vn[TPW];
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw) vn[cw] = acc_frag2(U[cw][2 * kb], U[cw][2 * kb + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          if (kb * 32 <= rt * 16 + 15) {
+            const half8_t ap = row_frag_kp<LC>(rPkp, rt * 16, kb * 32);
+#pragma unroll
+            for (int cw = 0; cw < TPW; ++cw)
+              if (has(cw)) O[cw][rt] = mfma(ap, vn[cw], O[cw][rt]);
+          }
+      }
+#pragma unroll
+      for (int cw = 0; cw < TPW; ++cw)
+        if (has(cw)) store_o(O[cw], tile(cw), t0, n, Ex[cw]);
+    }
+    // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new (K^ read down its columns)
+    {
+      const float gamC = sGam[C - 1];
+#pragma unroll
+      for (int cw = 0; cw < TPW; ++cw)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Macc[cw][rt][i] *= gamC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 d0 = *reinterpret_cast<const float4*>(sDec + kb * 32 + 4 * g4);
+        const float4 d1 = *reinterpret_cast<const float4*>(sDec + kb * 32 + 16 + 4 * g4);
+        half8_t vd[TPW];
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw) vd[cw] = acc_frag2_scaled(U[cw][2 * kb], U[cw][2 * kb + 1], d0, d1);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const half8_t ak = tr_frag_kp<LDK>(tKkp, kb * 32, rt * 16);
+#pragma unroll
+          for (int cw = 0; cw < TPW; ++cw)
+            if (has(cw)) Macc[cw][rt] = mfma(ak, vd[cw], Macc[cw][rt]);
+        }
+      }
+    }
+  }
+
+  // ---- results (true units)
+#pragma unroll
+  for (int cw = 0; cw < TPW; ++cw) {
+    if (!has(cw)) continue;
+    const int ct = tile(cw);
+    const int e = held_exp(Ex[cw]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rt * 16 + 4 * g4 + i;
+        const float mv = ldexpf(Macc[cw][rt][i], e);
+        if (OUTM) {
+          if (s == nseg_b - 1) a.S_final[(bh * DK + row) * DV + ct * 16 + m16] = mv;
+        } else if (ct < VCT) {
+          a.Dsum[((bh * a.nseg + s) * DK + row) * DV + ct * 16 + m16] = mv;
+        } else {
+          a.Phi[((bh * a.nseg + s) * DK + row) * DK + (ct - VCT) * 16 + m16] = mv;
+        }
+      }
+  }
+}
+
+}  // namespace fwd
+
+// ------------------------------------------------------------ host side
+
+#define JB_FWD_CASES(X) \
+  X(32, 64) X(32, 128) X(32, 256) X(64, 64) X(64, 128) X(64, 256) \
+  X(96, 64) X(96, 128) X(96, 256) X(128, 64) X(128, 128) X(128, 256)
+
+bool fwd_supported(int dk, int dv) {
+#define CASE(DK_, DV_) if (dk == DK_ && dv == DV_) return true;
+  JB_FWD_CASES(CASE)
+#undef CASE
+  return false;
+}
+
+template <int DK, int DV, typename OUT>
+static hipError_t run_fwd(const FwdArgs& a, int passes, int nseg, int H, int B, hipStream_t stream) {
+  using GS = fwd::Geo<DK, DV, fwd::SUMMARY>;
+  using GO = fwd::Geo<DK, DV, fwd::OUTPUT>;
+  if (passes & 1)
+    fwd::fwd_kernel<DK, DV, OUT, fwd::SUMMARY><<<dim3(nseg - 1, H, B), dim3(GS::NW * 64), 0, stream>>>(a);
+  if (passes & 2)
+    fwd::fwd_kernel<DK, DV, OUT, fwd::OUTPUT><<<dim3(nseg, H, B), dim3(GO::NW * 64), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int passes, int dk, int dv, bool out_bf16, int nseg, int H, int B,
+                      hipStream_t stream) {
+#define CASE(DK_, DV_)                                                                  \
+  if (dk == DK_ && dv == DV_)                                                           \
+    return out_bf16 ? run_fwd<DK_, DV_, bf16_t>(a, passes, nseg, H, B, stream)          \
+                    : run_fwd<DK_, DV_, float>(a, passes, nseg, H, B, stream);
+  JB_FWD_CASES(CASE)
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace jb

@@ -54,6 +54,32 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
                           const void* conv_in, const float* S0, void* o, float* S_final,
                           void* workspace, hipStream_t stream);
 
+// The fused chunk passes for bf16 inputs (jb_fwd.hip): passes bit 0 runs the
+// segment summaries (segments 0 .. nseg-2: Dsum, Phi), bit 1 the output pass
+// (o, S_final) from S0 (one segment) or Mstart.  bf16 tensors are passed as
+// their 16-bit patterns.
+struct FwdArgs {
+  int T, H, seg_len, nseg;
+  const int* cu_seqlens;   // packed batch (NULL: dense, rows b T ..)
+  int64_t total;           // rows of the token-major tensors
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* conv_in;
+  const float* alpha;
+  const float* beta;
+  const float* taps;
+  const float* S0;
+  const float* Mstart;     // [B][H][nseg][dk][dv]
+  float* Dsum;             // [B][H][nseg][dk][dv]
+  float* Phi;              // [B][H][nseg][dk][dk]
+  void* o;
+  float* S_final;
+};
+bool fwd_supported(int dk, int dv);
+hipError_t launch_fwd(const FwdArgs& a, int passes, int dk, int dv, bool out_bf16, int nseg, int H, int B,
+                      hipStream_t stream);
+
 // The static-conv variant: q, k, v each pass a causal conv with fixed
 // per-channel weights wq, wk [H*dk][4], wv [H*dv][4] (f32) instead of the
 // dynamic conv on v; caches cq/ck/cv [B][3][H][d] (NULL: zeros) hold the raw

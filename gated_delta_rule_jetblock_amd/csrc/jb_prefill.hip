@@ -176,12 +176,6 @@ struct StreamImg {
 
 // ------------------------------------------------------------ chunk kernel
 
-// Segments sequence b is cut into (at least one, which carries the state
-// through an empty sequence).
-__device__ __forceinline__ int seq_segments(int T, int seg_len) {
-  const int nch = (T + 63) / 64;
-  return max(1, (nch + seg_len - 1) / seg_len);
-}
 
 template <int DK, int DV, typename IO, typename OP, typename OUT, int MODE, bool SC>
 __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
@@ -1381,6 +1375,19 @@ static void set_segment_buffers(const PrefillPlan& p, ChunkArgs& a, char* ws) {
   X(96, 64) X(96, 128) X(96, 256) X(128, 64) X(128, 128) X(128, 256)
 #define JB_PREFILL_F32_CASES(X) X(32, 64) X(64, 64)
 
+// the segment scan on its own (the fused passes' summaries feed it)
+static hipError_t launch_scan(const PrefillPlan& p, const ChunkArgs& a, hipStream_t stream) {
+#define CASE(DK_, DV_)                                                                                       \
+  if (p.dk == DK_ && p.dv == DV_) {                                                                          \
+    scan_kernel<DK_, DV_, float><<<dim3(DV_ / 16, p.H, p.B), dim3(DK_ / 16 * WAVE), 0, stream>>>(              \
+        p.H, p.nseg, a.cu_seqlens, a.T, a.total, a.seg_len, a.S0, a.Dsum, a.Phi, const_cast<float*>(a.Mstart)); \
+    return hipGetLastError();                                                                                \
+  }
+  JB_PREFILL_BF16_CASES(CASE)
+#undef CASE
+  return hipErrorInvalidValue;
+}
+
 bool prefill_supported(const PrefillPlan& p) {
 #define CASE(DK_, DV_) if (p.dk == DK_ && p.dv == DV_) return true;
   if (p.io == IO_BF16) { JB_PREFILL_BF16_CASES(CASE) }
@@ -1406,6 +1413,22 @@ hipError_t launch_prefill(const PrefillPlan& p, const void* q, const void* k, co
     const size_t units = (size_t)p.B * p.H * p.nchunks;
     a.img = sw;
     a.u0 = reinterpret_cast<_Float16*>(sw + align256(units * stream_img_bytes(p.dk)));
+  }
+  if (p.io == IO_BF16 && fwd_supported(p.dk, p.dv)) {
+    // the fused chunk passes: summaries, scan, outputs
+    FwdArgs f{};
+    f.T = p.T; f.H = p.H; f.seg_len = p.seg_len; f.nseg = p.nseg; f.cu_seqlens = p.cu_seqlens; f.total = p.tokens;
+    f.q = static_cast<const uint16_t*>(q); f.k = static_cast<const uint16_t*>(k);
+    f.v = static_cast<const uint16_t*>(v); f.conv_in = static_cast<const uint16_t*>(conv_in);
+    f.alpha = alpha; f.beta = beta; f.taps = taps; f.S0 = S0; f.Mstart = a.Mstart; f.Dsum = a.Dsum; f.Phi = a.Phi;
+    f.o = o; f.S_final = S_final;
+    hipError_t e = hipSuccess;
+    if (p.nseg > 1) {
+      e = launch_fwd(f, 1, p.dk, p.dv, p.out == IO_BF16, p.nseg, p.H, p.B, stream);
+      if (e == hipSuccess) e = launch_scan(p, a, stream);
+    }
+    if (e == hipSuccess) e = launch_fwd(f, 2, p.dk, p.dv, p.out == IO_BF16, p.nseg, p.H, p.B, stream);
+    return e;
   }
 #define CASE(DK_, DV_) \
   if (p.dk == DK_ && p.dv == DV_) return run_prefill_out<DK_, DV_, bf16_t, _Float16>(p, a, stream);

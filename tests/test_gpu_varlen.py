@@ -145,3 +145,30 @@ def test_varlen_serving_batch_jetblock2b(jb, oracle_mod):
         print(f"  seq {n} (T={lengths[n]}): o {e_o:.2e}  S {e_s:.2e}", flush=True)
         # bf16 o: one more rounding, at most 2^-9 of the largest element
         assert e_o < TOL_BF16 + 2.0 ** -9 and e_s < TOL_BF16, (n, e_o, e_s)
+
+
+def test_malformed_offsets_stay_in_bounds(jb):
+    """cu_seqlens lives in device memory, so the host cannot validate it: offsets past the
+    packed rows, negative and decreasing offsets give wrong rows but no access outside the
+    tensors.  o, S_final and conv_out sit inside NaN-filled buffers whose guard regions on
+    both sides must keep their fill."""
+    print("[malformed cu_seqlens]", flush=True)
+    H, dk, dv, D, total, Tmax = 2, 32, 64, 128, 300, 200
+    p = packed_prefill_inputs([100, 100, 100], H, dk, dv, D, seed=3)
+    g = {k: v.cuda() for k, v in p.items()}
+    bad = torch.tensor([0, 500, -40, 300], dtype=torch.int32, device="cuda")
+    guard = 4096
+
+    def guarded(n, dtype):
+        buf = torch.full((guard + n + guard,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[guard:guard + n]
+
+    ob, o = guarded(total * H * dv, torch.float32)
+    sb, s = guarded(3 * H * dk * dv, torch.float32)
+    cb, c = guarded(3 * 3 * H * dv, torch.bfloat16)
+    jb.prefill_varlen(bad, g["x"], g["q"], g["k"], g["v"], g["alpha"], g["beta"], g["W1"], g["W2"],
+                      max_seqlen=Tmax, o=o.view(total, H, dv), S_final=s.view(3, H, dk, dv),
+                      conv_out=c.view(3, 3, H, dv), seg_len=1)
+    torch.cuda.synchronize()
+    for buf in (ob, sb, cb):
+        assert torch.isnan(buf[:guard].float()).all() and torch.isnan(buf[-guard:].float()).all()
