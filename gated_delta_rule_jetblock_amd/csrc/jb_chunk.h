@@ -171,10 +171,16 @@ __device__ __forceinline__ void conv4(const IO* raw, const float* w, int row, in
 // sums the products form).  Scaling every input by 2^k shifts every E by k
 // and leaves the held values bit for bit unchanged.
 
+// maximum over the wave: within quads, half rows, rows, then across rows by
+// the row broadcasts (lane 63 ends with the total), read back from lane 63
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
-  return v;
+  v = fmaxf(v, dpp<0xb1>(v, v));        // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4e>(v, v));        // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v, v));       // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v, v));       // row_mirror
+  v = fmaxf(v, dpp<0x142, 0xa>(v, v));  // row_bcast:15 into rows 1, 3
+  v = fmaxf(v, dpp<0x143, 0xc>(v, v));  // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // A tile starts "fresh" (E_FRESH: held in true units, no exponent chosen yet)

@@ -119,22 +119,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// sum over aligned groups of `n` consecutive lanes (n power of two <= 64)
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = N / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
-  return v;
+// DPP lane exchange (data moves between lanes inside the VALU, no LDS round
+// trip): dpp_ctrl as in the GFX9 ISA; rows outside row_mask keep `old`, and
+// with bound_ctrl a lane whose source is outside its row reads zero
+template <int CTRL, int ROWMASK = 0xf, bool BOUND = false>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWMASK, 0xf, BOUND));
 }
 
-// inclusive prefix sum across the 64 lanes of a wave
-__device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int l = lane_id();
+// sum over aligned groups of `n` consecutive lanes (n power of two <= 64);
+// every lane of a group receives the same value
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N == 8) {
+    v += dpp<0xb1>(v, v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4e>(v, v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v, v);  // row_half_mirror: quad i of a half row meets quad 1 - i
+    return v;
+  } else {
 #pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    float u = __shfl_up(v, off, WAVE);
-    if (l >= off) v += u;
+    for (int off = N / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+    return v;
   }
+}
+
+// inclusive prefix sum across the 64 lanes of a wave: within rows of 16 by
+// shifts of 1, 2, 4, 8, then across rows by the row broadcasts
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  v += dpp<0x111, 0xf, true>(0.f, v);   // row_shr:1
+  v += dpp<0x112, 0xf, true>(0.f, v);   // row_shr:2
+  v += dpp<0x114, 0xf, true>(0.f, v);   // row_shr:4
+  v += dpp<0x118, 0xf, true>(0.f, v);   // row_shr:8
+  v += dpp<0x142, 0xa, false>(0.f, v);  // row_bcast:15 into rows 1, 3
+  v += dpp<0x143, 0xc, false>(0.f, v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 

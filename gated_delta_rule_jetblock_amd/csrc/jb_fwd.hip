@@ -170,6 +170,14 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, 0, 0, 0);
 }
 
+// A copy of x the compiler cannot see through: values derived from it inside
+// the chunk loop are formed there, not hoisted out of the loop and held (or
+// spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Barrier for data exchanged through LDS: this wave's LDS accesses complete,
 // then s_barrier.  Outstanding global loads (the next chunk's LDS DMA) and
 // stores stay in flight.
@@ -187,13 +195,13 @@ struct Geo {
   static constexpr int TPW = (NCT + NW - 1) / NW;              // tiles per wave: wave w owns w, w + 8, ..
   static constexpr int GW = NW - 1;                            // gate wave
   static constexpr int IW = NW - 2;                            // inverse wave
-  static constexpr int LDK = DK + 8, LC = C + 8, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
+  static constexpr int LDK = DK + 16, LC = C + 8, LWT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
   static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
   static constexpr int oKh = a16(oT + 2 * 4 * 16 * LT * 2);     // [C][LDK] K^
   static constexpr int szQh = OUTM ? C * LDK * 2 : 0;
-  static constexpr int szWt = DK * LC * 2;
+  static constexpr int szWt = DK * LWT * 2;
   static constexpr int oQW = a16(oKh + C * LDK * 2);            // Q^ (output), then -W^T [DK][LC]
   static constexpr int oAn = a16(oQW + (szQh > szWt ? szQh : szWt));  // [C][LC] -A
   static constexpr int oAd = a16(oAn + C * LC * 2);             // [C][LAD] f32 diagonal blocks of A
@@ -203,7 +211,7 @@ struct Geo {
   static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + (C + 3) * LV * 2;
   static_assert(WORK + STAGE <= 160 * 1024, "LDS budget of one CU exceeded");
   static_assert(RT <= NW, "one wave per W column tile");
-  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0, "aligned rows");
+  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0 && (LWT * 2) % 8 == 0, "aligned rows");
 };
 
 // ------------------------------------------------------------ kernel
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   using G = Geo<DK, DV, MODE>;
   constexpr bool OUTM = G::OUTM;
   constexpr int NCT = G::NCT, VCT = G::VCT, RT = G::RT, KB = G::KB, NW = G::NW, TPW = G::TPW;
-  constexpr int LDK = G::LDK, LC = G::LC, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
+  constexpr int LDK = G::LDK, LC = G::LC, LWT = G::LWT, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
 
   // working tiles, and the DMA staging areas as arrays of their own (so the
   // compiler can tell that reads of the tiles never wait on the DMA)
@@ -263,14 +271,15 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 
   // this lane's bases in the tiles
   const lds_char* tKkp = tr_base_kp(lKh, LDK);   // K^ down its columns (K^T; the W right-hand side)
-  const lds_char* tWkp = tr_base_kp(lWt, LC);    // -W^T down its columns (-W)
-  const lds_char* tVct = tr_base_ct(lV, LV);     // value rows down their columns
+  const lds_char* tWkp = tr_base_kp(lWt, LWT);   // -W^T down its columns (-W)
+  const lds_char* tVkp = tr_base_kp(lV, LV);     // value rows down their columns
   const _Float16* rKct = row_base_ct(sKh, LDK);  // rows of K^, Q^ (Gram tiles)
   const _Float16* rQct = row_base_ct(sQh, LDK);
   const _Float16* rQkp = row_base_kp(sQh, LDK);  // rows of Q^ (Q^ M)
   const _Float16* rPkp = row_base_kp(sP, LC);
   const _Float16* rAkp = row_base_kp(sAn, LC);
   const _Float16* rLkp = row_base_kp(sLi, LLI);
+  const _Float16* rTkp = row_base_kp(reinterpret_cast<const _Float16*>(sT), LT);  // band rows (bf16 bits)
 
   // ---- initial state, accumulator layout: lane holds M[16 rt + 4 g + i][16 ct + m16]
   f4_t Macc[TPW][RT];
@@ -322,18 +331,19 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     const uint32_t bytes = (uint32_t)(nc - 1) * rowq + DK * 2;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + e0, bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + e0, bytes);
+    const int ln = opaque(lane);
     for (int j = wave; j * 64 < C * PPK; j += NW) {
-      const int p = j * 64 + lane, r = p / PPK, pc = p % PPK;
+      const int p = j * 64 + ln, r = p / PPK, pc = p % PPK;
       const uint32_t off = (uint32_t)r * rowq + (uint32_t)pc * 16;
       if (p < C * PPK && r < nc) {
         dma_buf<16>(rk, off, lKr + j * 1024);
         if (OUTM) dma_buf<16>(rq, off, lQr + j * 1024);
       }
     }
-    if (wave == G::GW && lane < nc) {
+    if (wave == G::GW && ln < nc) {
       const int64_t gidx = (tok0 + t0c) * H + h;
       const uint32_t gb = (uint32_t)(nc - 1) * H * 4 + 4;
-      const uint32_t off = (uint32_t)(lane * H) * 4;
+      const uint32_t off = (uint32_t)(ln * H) * 4;
       dma_buf<4>(make_rsrc(a.alpha + gidx, gb), off, lGr);
       dma_buf<4>(make_rsrc(a.beta + gidx, gb), off, lGr + C * 4);
       dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, lGr + 2 * C * 4);
@@ -348,16 +358,17 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         make_rsrc(v + ((tok0 + rb0) * H + h) * DV, (uint32_t)(t0c + nc - 1 - rb0) * rowv + DV * 2);
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(cin ? cin + ((int64_t)b * 3 * H + h) * DV : v, cin ? 2 * rowv + DV * 2 : 0u);
+    const int l16 = opaque(lane) * 16;
     for (int r = wave; r < C + 3; r += NW) {  // staged row r holds token t0c - 3 + r
       const int t = t0c - 3 + r;
       lds_char* dst = lVw + r * LV * 2;
-      if (lane < PPR) {
+      if (l16 < PPR * 16) {
         if (t >= 0 && r - 3 < nc)
-          dma_buf<16>(rv, (uint32_t)(t - rb0) * rowv + lane * 16, dst);
+          dma_buf<16>(rv, (uint32_t)(t - rb0) * rowv + l16, dst);
         else if (t < 0 && cin)
-          dma_buf<16>(rc, (uint32_t)(3 + t) * rowv + lane * 16, dst);
+          dma_buf<16>(rc, (uint32_t)(3 + t) * rowv + l16, dst);
         else
-          *(__attribute__((address_space(3))) u4_t*)(dst + lane * 16) = u4_t{0u, 0u, 0u, 0u};
+          *(__attribute__((address_space(3))) u4_t*)(dst + l16) = u4_t{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -381,12 +392,26 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     issue_qkg(c_begin);
     issue_v(c_begin);
   }
+  // o stores this wave issues per chunk (one per row of each owned tile)
+  int nst = 0;
+#pragma unroll
+  for (int cw = 0; cw < TPW; ++cw) nst += has(cw) ? 16 : 0;
 
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA transfers (and earlier stores) are done
-    bar();                          // ... and every other wave's; the previous chunk's reads are done
+    // this wave's DMA transfers into the staging areas are done (they were
+    // issued before the previous chunk's o stores, which may stay in flight:
+    // vector memory operations complete in order), then every other wave's
+    if (OUTM && c > c_begin) {
+      if (nst == 32) __builtin_amdgcn_s_waitcnt(0x8070);       // vmcnt(32), lgkmcnt(0)
+      else if (nst == 48) __builtin_amdgcn_s_waitcnt(0xC070);  // vmcnt(48)
+      else if (nst == 16) __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16)
+      else __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    bar();
 
     // ================= A: normalise q, k; gates and band =================
     {
@@ -449,10 +474,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     bar();
     if (c + 1 < c_end) issue_qkg(c + 1);
 
-    // ================= B: Gram tiles; right-hand sides; tile exponents =================
-    for (int job = wave; job < 10; job += NW) {
-      const int ti = (kLowI >> (2 * job)) & 3, tj = (kLowJ >> (2 * job)) & 3;
-      // formed transposed: lane holds (Y K^T)[16 ti + m16][16 tj + 4 g4 + i], Y = K^ or Q^
+    // ================= B: Gram tiles and diagonal inverses; right-hand sides,
+    // tile exponents, Q^ M =================
+    // Gram tile (ti, tj), formed transposed: lane holds (Y K^T)[16 ti + m16][16 tj + 4 g4 + i]
+    // (Y = K^ or Q^), so -A, P and the diagonal blocks are written as whole rows
+    auto gram = [&](int ti, int tj) {
       f4_t kk = zero4(), qk = zero4();
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -460,7 +486,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         kk = mfma(ak, row_frag_ct<LDK>(rKct, ti * 16, kb * 32), kk);
         if (OUTM) qk = mfma(ak, row_frag_ct<LDK>(rQct, ti * 16, kb * 32), qk);
       }
-      const int r = ti * 16 + m16, c0 = tj * 16 + 4 * g4;
+      const int ln = opaque(lane);
+      const int r = ti * 16 + (ln & 15), c0 = tj * 16 + 4 * (ln >> 4);
       const float gr = sG[r], br = sBeta[r];
       const float4 gc = *reinterpret_cast<const float4*>(sG + c0);
       const float gcv[4] = {gc.x, gc.y, gc.z, gc.w};
@@ -475,41 +502,20 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       const h2_t a0 = __builtin_convertvector(f2_t{-an[0], -an[1]}, h2_t);
       const h2_t a1 = __builtin_convertvector(f2_t{-an[2], -an[3]}, h2_t);
       *reinterpret_cast<h4_t*>(sAn + r * LC + c0) = h4_t{a0[0], a0[1], a1[0], a1[1]};
-      if (ti == tj) *reinterpret_cast<float4*>(sAd + r * LAD + 4 * g4) = make_float4(an[0], an[1], an[2], an[3]);
+      if (ti == tj) *reinterpret_cast<float4*>(sAd + r * LAD + c0 - tj * 16) = make_float4(an[0], an[1], an[2], an[3]);
       if (OUTM) {
         const h2_t p0 = __builtin_convertvector(f2_t{pp[0], pp[1]}, h2_t);
         const h2_t p1 = __builtin_convertvector(f2_t{pp[2], pp[3]}, h2_t);
         *reinterpret_cast<h4_t*>(sP + r * LC + c0) = h4_t{p0[0], p0[1], p1[0], p1[1]};
       }
-    }
-    f4_t U[TPW][4];
-#pragma unroll
-    for (int cw = 0; cw < TPW; ++cw) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) U[cw][rt] = zero4();
-      if (!isval(cw)) continue;
-      // right-hand side diag(b) V': tile rt = (Band_hi + Band_lo) V_ext[window rows][column tile],
-      // the value rows taken exactly as bf16 operands (K order 8g + j on both sides)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
-        const bf16x8_t th = *reinterpret_cast<const bf16x8_t*>(sT + (rt * 16 + m16) * LT + 8 * g4);
-        const bf16x8_t tl = *reinterpret_cast<const bf16x8_t*>(sT + ((4 + rt) * 16 + m16) * LT + 8 * g4);
-        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, tr_frag_ct<LV>(tVct, s0, tile(cw) * 16));
-        const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
-        U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int cw = 0; cw < TPW; ++cw)
-      if (has(cw)) rescale_tile(Macc[cw], U[cw], Ex[cw]);
-    bar();
-    if (c + 1 < c_end) issue_v(c + 1);
-
-    // ================= C: diagonal-block inverses; Q^ M =================
-    if (wave == G::IW) {
-      // four 16x16 blocks of I + A by forward substitution, one column per lane
-      const int base = (lane >> 4) * 16;
+    };
+    if (wave >= 4) {
+      // diagonal tile d = wave - 4, then the inverse of I + A's diagonal block d
+      // by forward substitution (column jc = lane % 16; lanes 16.. repeat lanes 0..15)
+      const int d = wave - 4;
+      gram(d, d);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's block rows are in LDS
+      const int base = d * 16;
       int jc = lane & 15;
       asm volatile("" : "+v"(jc));  // formed per chunk: the 16 identity values are not held across the loop
       float x[16];
@@ -528,12 +534,43 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         x[i] = acc;
         if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
+      if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sLi[(base + i) * LLI + jc] = (_Float16)x[i];
-        sLi[(base + i) * LLI + 16 + jc] = (_Float16)0.f;  // the zero half a 32-deep fragment reads
+        for (int i = 0; i < 16; ++i) {
+          sLi[(base + i) * LLI + jc] = (_Float16)x[i];
+          sLi[(base + i) * LLI + 16 + jc] = (_Float16)0.f;  // the zero half a 32-deep fragment reads
+        }
+      }
+    } else {
+      // off-diagonal tiles (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): jobs wave and wave + 4
+      constexpr uint32_t kOffI = 0xfe9u, kOffJ = 0x910u;  // two bits per job
+      gram((kOffI >> (2 * wave)) & 3, (kOffJ >> (2 * wave)) & 3);
+      if (wave < 2) gram((kOffI >> (2 * wave + 8)) & 3, (kOffJ >> (2 * wave + 8)) & 3);
+    }
+    // the rest of the phase after the Gram work (waves 0..3 and 4..7 share the
+    // SIMDs pairwise, so the other wave fills a SIMD while one inverts)
+    __builtin_amdgcn_sched_barrier(0);
+    f4_t U[TPW][4];
+#pragma unroll
+    for (int cw = 0; cw < TPW; ++cw) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) U[cw][rt] = zero4();
+      if (!isval(cw)) continue;
+      // right-hand side diag(b) V': tile rt = (Band_hi + Band_lo) V_ext[window rows][column tile],
+      // the value rows taken exactly as bf16 operands (kperm K order on both sides)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
+        const bf16x8_t th = __builtin_bit_cast(bf16x8_t, row_frag_kp<LT>(rTkp, rt * 16, 0));
+        const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, row_frag_kp<LT>(rTkp, (4 + rt) * 16, 0));
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, tr_frag_kp<LV>(tVkp, s0, tile(cw) * 16));
+        const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
+        U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int cw = 0; cw < TPW; ++cw)
+      if (has(cw)) rescale_tile(Macc[cw], U[cw], Ex[cw]);
     f4_t O[OUTM ? TPW : 1][4];
     if constexpr (OUTM) {
 #pragma unroll
@@ -552,6 +589,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
           for (int cw = 0; cw < TPW; ++cw)
             if (has(cw)) O[cw][rt] = mfma(aq, mk[cw], O[cw][rt]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -564,6 +602,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
     }
     bar();
+    if (c + 1 < c_end) issue_v(c + 1);
 
     // ================= D: -W^T and U0 by blocked forward substitution =================
     {
@@ -586,7 +625,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         for (int rb = 0; rb < 4; ++rb) {
           const h2_t w0 = __builtin_convertvector(f2_t{-Y[rb][0], -Y[rb][1]}, h2_t);
           const h2_t w1 = __builtin_convertvector(f2_t{-Y[rb][2], -Y[rb][3]}, h2_t);
-          *reinterpret_cast<h4_t*>(sWt + (jw * 16 + m16) * LC + rb * 16 + 4 * g4) = h4_t{w0[0], w0[1], w1[0], w1[1]};
+          *reinterpret_cast<h4_t*>(sWt + (jw * 16 + m16) * LWT + rb * 16 + 4 * g4) = h4_t{w0[0], w0[1], w1[0], w1[1]};
         }
       }
 #pragma unroll
@@ -604,7 +643,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       for (int cw = 0; cw < TPW; ++cw) mk[cw] = acc_frag2(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const half8_t aw = tr_frag_kp<LC>(tWkp, kb * 32, rt * 16);
+        const half8_t aw = tr_frag_kp<LWT>(tWkp, kb * 32, rt * 16);
 #pragma unroll
         for (int cw = 0; cw < TPW; ++cw)
           if (has(cw)) U[cw][rt] = mfma(aw, mk[cw], U[cw][rt]);
@@ -625,6 +664,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
             for (int cw = 0; cw < TPW; ++cw)
               if (has(cw)) O[cw][rt] = mfma(ap, vn[cw], O[cw][rt]);
           }
+        __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
 #pragma unroll
       for (int cw = 0; cw < TPW; ++cw)
@@ -653,6 +693,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
           for (int cw = 0; cw < TPW; ++cw)
             if (has(cw)) Macc[cw][rt] = mfma(ak, vd[cw], Macc[cw][rt]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
     }
   }
