@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/jetblock.h"
 #include "jb_internal.h"
 
@@ -114,11 +116,11 @@ jb_status jb_prefill_workspace_size(const jb_shape* s, size_t* bytes) {
   return ok();
 }
 
-jb_status jb_prefill(const jb_shape* s, const void* x, const void* q, const void* k, const void* v,
-                     const float* alpha, const float* beta, const void* W1, const void* b1, const void* W2,
-                     const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
-                     void* conv_out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "jb_prefill";
+static jb_status prefill_impl(const char* fn, const jb_shape* s, const void* x, const void* q, const void* k,
+                              const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
+                              const void* W2, const void* b2, const float* S0, const void* conv_in, void* o,
+                              float* S_final, void* conv_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   jb_status st = check_shape(fn, s, false);
   if (st) return st;
   const jb::PrefillPlan p = plan_of(s);
@@ -157,6 +159,67 @@ jb_status jb_prefill(const jb_shape* s, const void* x, const void* q, const void
   if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, workspace, hs);
   if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(io, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs);
   return hip_status(fn, e);
+}
+
+jb_status jb_prefill(const jb_shape* s, const void* x, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const void* W1, const void* b1, const void* W2,
+                     const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
+                     void* conv_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl("jb_prefill", s, x, q, k, v, alpha, beta, W1, b1, W2, b2, S0, conv_in, o, S_final, conv_out,
+                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free prefill: jb_prefill's kernels on a workspace that
+// is a file-scope device array.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+static __device__ __align__(256) unsigned char scratch[JB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    // first call on this device: look the array up with the device current
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+jb_status jb_prefill_noalloc(const jb_shape* s, const void* x, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const void* W1, const void* b1, const void* W2,
+                             const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
+                             void* conv_out, void* stream) {
+  const char* fn = "jb_prefill_noalloc";
+  jb_status st = check_shape(fn, s, false);
+  if (st) return st;
+  const size_t need = jb::prefill_workspace_bytes(plan_of(s));
+  if (need > JB_NOALLOC_SCRATCH_BYTES)
+    return fail(JB_ERR_WORKSPACE, "%s: the shape needs %zu bytes of workspace, above the %zu this call holds; "
+                "use jb_prefill with a workspace (or fewer tokens per call)", fn, need,
+                (size_t)JB_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  const hipError_t e = scratch_address(&ptr);
+  if (e != hipSuccess) return hip_status(fn, e);
+  return prefill_impl(fn, s, x, q, k, v, alpha, beta, W1, b1, W2, b2, S0, conv_in, o, S_final, conv_out, ptr,
+                      JB_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 namespace {

@@ -58,6 +58,7 @@ _lib.jb_prefill_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_decode_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_prefill.argtypes = [_S] + [_P] * 15 + [_P, _SZ, _P]
 _lib.jb_decode_step.argtypes = [_S] + [_P] * 15 + [_P, _SZ, _P]
+_lib.jb_prefill_noalloc.argtypes = [_S] + [_P] * 15 + [_P]
 _lib.jb_gen_taps.argtypes = [_S] + [_P] * 6 + [_P]
 _lib.jb_gen_conv.argtypes = [_S] + [_P] * 9 + [_P]
 _lib.jb_prologue.argtypes = [_S] + [_P] * 6 + [_P]
@@ -76,7 +77,8 @@ _lib.jb_prefill_varlen_workspace_size.argtypes = [_S, ctypes.c_int64, ctypes.POI
 _lib.jb_prefill_varlen.argtypes = [_S, ctypes.c_int64] + [_P] * 16 + [_P, _SZ, _P]
 _lib.jb_backward_workspace_size.argtypes = [_S, ctypes.POINTER(_SZ)]
 _lib.jb_backward.argtypes = [_S] + [_P] * 27 + [_P, _SZ, _P]
-for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_decode_step",
+for _f in ("jb_prefill_workspace_size", "jb_decode_workspace_size", "jb_prefill", "jb_prefill_noalloc",
+           "jb_decode_step",
            "jb_gen_taps", "jb_gen_conv", "jb_prologue", "jb_probe_mfma", "jb_decode_update",
            "jb_project_workspace_size", "jb_prefill_from_x_workspace_size", "jb_project", "jb_prefill_from_x",
            "jb_decode_step_from_x_workspace_size", "jb_decode_step_from_x", "jb_prefill_static_workspace_size",
@@ -180,6 +182,33 @@ def prefill(x, q, k, v, alpha, beta, W1, W2, b1=None, b2=None, S0=None, conv_in=
                            _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(S0), _ptr(conv_in), _ptr(o),
                            _ptr(S_final), _ptr(conv_out), _ptr(ws), ws.numel(), _stream(stream)))
     return dict(o=o, S_final=S_final, conv_out=conv_out)
+
+
+def prefill_noalloc(x, q, k, v, alpha, beta, W1, W2, b1=None, b2=None, S0=None, conv_in=None, *,
+                    out_dtype=torch.float32, seg_len: int | None = None, o=None, S_final=None,
+                    conv_out=None, want_conv_out=True, stream=None):
+    """jb_prefill_noalloc: jb_prefill on the library's own per-device scratch array
+    (NOALLOC_SCRATCH_BYTES).  Same arguments as prefill() without ws; outputs are
+    allocated here unless given, so a caller that must not allocate passes o, S_final
+    and conv_out (or want_conv_out=False)."""
+    B, T, D = x.shape
+    H, dk = q.shape[2], q.shape[3]
+    dv = v.shape[3]
+    shape = make_shape(B, T, H, dk, dv, D, _io_code(x), _DT[out_dtype], flag_segment(seg_len) if seg_len else 0)
+    dev = x.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv_out:
+        conv_out = torch.empty((B, 3, H, dv), dtype=x.dtype, device=dev)
+    _check(_lib.jb_prefill_noalloc(ctypes.byref(shape), _ptr(x), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(S0), _ptr(conv_in),
+                                   _ptr(o), _ptr(S_final), _ptr(conv_out), _stream(stream)))
+    return dict(o=o, S_final=S_final, conv_out=conv_out)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def decode_step(S, cache, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, W2, b1=None, b2=None, *,

@@ -131,6 +131,34 @@ jb_status jb_prefill(const jb_shape* shape, const void* x, const void* q, const 
                      const void* conv_in, void* o, float* S_final, void* conv_out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device memory jb_prefill_noalloc holds per GPU (its workspace). */
+#define JB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * jb_prefill_noalloc -- jb_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, results and errors as
+ * jb_prefill, without the workspace: the call runs jb_prefill's kernels on a
+ * file-scope device array of JB_NOALLOC_SCRATCH_BYTES bytes (each GPU the
+ * library runs on holds its own copy until the process ends) and calls no
+ * hipMalloc, hipFree or allocating library routine.
+ *
+ * The array of the calling thread's current device is used, so `stream`
+ * must belong to that device; its address is looked up on the first call on
+ * each device.  Returns JB_ERR_WORKSPACE, launching nothing, when the shape
+ * needs more than JB_NOALLOC_SCRATCH_BYTES (jb_prefill_workspace_size tells).
+ * At dk = 96, dv = 256, H = 12: one sequence of T = 16384 needs 56 MiB,
+ * 64 sequences of 1024 tokens 12 MiB, one of T = 65536 68 MiB (rejected).
+ * Nothing in the array has to start at zero.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different streams
+ * or threads) race and must be serialised by the caller.
+ */
+jb_status jb_prefill_noalloc(const jb_shape* shape, const void* x, const void* q, const void* k,
+                             const void* v, const float* alpha, const float* beta, const void* W1,
+                             const void* b1, const void* W2, const void* b2, const float* S0,
+                             const void* conv_in, void* o, float* S_final, void* conv_out,
+                             void* stream);
+
 /* Workspace bytes jb_decode_step needs for `shape` (shape.T must be 1).
  * Currently 0: the step keeps its intermediates on chip. */
 jb_status jb_decode_workspace_size(const jb_shape* shape, size_t* bytes);
