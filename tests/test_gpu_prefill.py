@@ -97,21 +97,6 @@ def test_jetblock2b_T65536_full(jb, oracle_mod):
     _check(r, ref, TOL_BF16, "2B T=65536")
 
 
-def test_jetblock4b_T262144_heads(jb, oracle_mod):
-    """JetBlock 4B prefill at full size, B=1, T=262144, H=16, dk=128, dv=256,
-    d_model=2048, default segment plan; the oracle follows four of the sixteen heads over
-    the whole sequence (outputs at every token and the final states)."""
-    from gated_delta_rule_jetblock_amd import inputs
-    print("4B T=262144 full size, heads 0 5 11 15", flush=True)
-    heads = [0, 5, 11, 15]
-    p = inputs.prefill_inputs(inputs.B4_T262144, seed=0)
-    r = _run(jb, p)
-    sub = dict(o=r["o"][:, :, heads], S_final=r["S_final"][:, heads])
-    del r
-    ref = oracle_prefill(oracle_mod, p, heads=heads)
-    _check(sub, ref, TOL_BF16, "4B T=262144")
-
-
 @pytest.mark.parametrize("seg", [1, 2, 5, 64])
 def test_segmentation_invariance(jb, oracle_mod, seg):
     """Any split into segments (1 chunk .. whole sequence) gives the oracle's result."""
