@@ -51,11 +51,23 @@ typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) s4_t lds_s4;
 typedef __attribute__((address_space(3))) char lds_char;
 
 // ------------------------------------------------------------ fragments
+
+// A copy of x the compiler cannot see through.  Used for lane offsets, so that
+// an LDS address stays one short chain of additions from its array (the
+// compiler then still knows which array every access touches, and reads of the
+// working tiles never wait for the DMA into the staging areas), and for values
+// derived from the lane inside the chunk loop, which are then formed there
+// instead of being hoisted out of the loop and held (or spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ half8_t cat8(h4_t lo, h4_t hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -81,11 +93,11 @@ __device__ __forceinline__ s4_t tr4(const lds_char* p) {
 // (contiguous halves at rows k0 and k0 + 4).
 __device__ __forceinline__ const lds_char* tr_base_kp(const lds_char* tile, int ld) {
   const int l = lane_id();
-  return tile + ((4 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2;
+  return tile + opaque(((4 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2);
 }
 __device__ __forceinline__ const lds_char* tr_base_ct(const lds_char* tile, int ld) {
   const int l = lane_id();
-  return tile + ((8 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2;
+  return tile + opaque(((8 * (l >> 4) + ((l >> 2) & 3)) * ld + 4 * (l & 3)) * 2);
 }
 // Fragment down the columns from a kperm base: lane 16g + n receives
 // tile[k0 + 4g + j][c0 + n], then tile[k0 + 16 + 4g + j][c0 + n]
@@ -107,23 +119,23 @@ __device__ __forceinline__ half8_t tr_frag_ct(const lds_char* base, int k0, int 
 // or 8g (contiguous)) of a row-major fp16 tile
 __device__ __forceinline__ const _Float16* row_base_kp(const _Float16* tile, int ld) {
   const int l = lane_id();
-  return tile + (l & 15) * ld + 4 * (l >> 4);
+  return tile + opaque((l & 15) * ld + 4 * (l >> 4));
 }
 __device__ __forceinline__ const _Float16* row_base_ct(const _Float16* tile, int ld) {
   const int l = lane_id();
-  return tile + (l & 15) * ld + 8 * (l >> 4);
+  return tile + opaque((l & 15) * ld + 8 * (l >> 4));
 }
 // Fragment along rows r0.. with K in the accumulator-chaining order (kperm:
 // columns k0 + 4g .. + 3 and k0 + 16 + 4g .. + 3)
 template <int LD>
 __device__ __forceinline__ half8_t row_frag_kp(const _Float16* base, int r0, int k0) {
-  const _Float16* p = base + r0 * LD + k0;
-  return cat8(*reinterpret_cast<const h4_t*>(p), *reinterpret_cast<const h4_t*>(p + 16));
+  const int o = r0 * LD + k0;
+  return cat8(*reinterpret_cast<const h4_t*>(base + o), *reinterpret_cast<const h4_t*>(base + (o + 16)));
 }
 // ... K contiguous (columns k0 + 8g .. + 7): one 16-byte read
 template <int LD>
 __device__ __forceinline__ half8_t row_frag_ct(const _Float16* base, int r0, int k0) {
-  return *reinterpret_cast<const half8_t*>(base + r0 * LD + k0);
+  return *reinterpret_cast<const half8_t*>(base + (r0 * LD + k0));
 }
 
 // B fragment (kperm order) from two accumulator tiles: rows 0..15 and 16..31
@@ -168,14 +180,6 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, 0, 0, 0);
-}
-
-// A copy of x the compiler cannot see through: values derived from it inside
-// the chunk loop are formed there, not hoisted out of the loop and held (or
-// spilled) across it.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
 }
 
 // Barrier for data exchanged through LDS: this wave's LDS accesses complete,
@@ -258,6 +262,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   const int nseg_b = seq_segments(T, a.seg_len);
   if (s >= (OUTM ? nseg_b : nseg_b - 1)) return;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // (the block has NW waves: with this known, which tiles a wave owns and how
+  // many o stores it issues per chunk are compile-time facts, and the compiler
+  // can count the DMA transfers complete at the top wait; the summary pass
+  // stores nothing per chunk and waits for everything there)
+  if constexpr (OUTM) __builtin_assume(wave >= 0 && wave < NW);
   const int m16 = lane & 15, g4 = lane >> 4;
   const bf16_t* q = a.q;
   const bf16_t* k = a.k;
@@ -332,7 +341,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + e0, bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + e0, bytes);
     const int ln = opaque(lane);
-    for (int j = wave; j * 64 < C * PPK; j += NW) {
+    constexpr int NJ = (C * PPK + 64 * NW - 1) / (64 * NW);  // 64-piece rows per wave
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = wave + jj * NW;
       const int p = j * 64 + ln, r = p / PPK, pc = p % PPK;
       const uint32_t off = (uint32_t)r * rowq + (uint32_t)pc * 16;
       if (p < C * PPK && r < nc) {
@@ -373,44 +385,53 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // a column tile of outputs, rows t0 .. t0 + n - 1, straight from registers
+  // a column tile of outputs, rows t0 .. t0 + n - 1, straight from registers:
+  // the tile is held transposed (lane 16 g + m has row m of each 16-row block,
+  // columns 4 g .. 4 g + 3), so every lane stores four adjacent outputs at once
   auto store_o = [&](const f4_t (&Ot)[4], int ct, int t0, int n, int E) {
     const uint32_t rowb = (uint32_t)(H * DV * (int)sizeof(OUT));
     const __amdgpu_buffer_rsrc_t orsrc =
         make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0) * H + h) * DV, (uint32_t)n * rowb);
-    const int ovoff = (int)(4 * g4 * rowb) + (ct * 16 + m16) * (int)sizeof(OUT);
+    const int ovoff = (int)(m16 * rowb) + (ct * 16 + 4 * g4) * (int)sizeof(OUT);
     const int e = held_exp(E);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        // rows at or beyond n fall outside the resource and are dropped
-        buf_store(orsrc, from_f32<OUT>(ldexpf(Ot[rt][i], e)), ovoff, (int)((rt * 16 + i) * rowb));
+    for (int rt = 0; rt < 4; ++rt) {
+      const float x0 = ldexpf(Ot[rt][0], e), x1 = ldexpf(Ot[rt][1], e);
+      const float x2 = ldexpf(Ot[rt][2], e), x3 = ldexpf(Ot[rt][3], e);
+      // rows at or beyond n fall outside the resource and are dropped
+      if constexpr (sizeof(OUT) == 2) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(x2) | ((uint32_t)f32_to_bf16(x3) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(u2_t{w0, w1}, orsrc, ovoff, (int)(rt * 16 * rowb), 0);
+      } else {
+        // two 8-byte stores: a wider store's data registers may still be read
+        // after the next instruction has overwritten them (the compiler does not
+        // guard that case when the offset is in an SGPR)
+        __builtin_amdgcn_raw_buffer_store_b64(u2_t{__float_as_uint(x0), __float_as_uint(x1)}, orsrc, ovoff,
+                                              (int)(rt * 16 * rowb), 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u2_t{__float_as_uint(x2), __float_as_uint(x3)}, orsrc, ovoff + 8,
+                                              (int)(rt * 16 * rowb), 0);
+      }
+    }
   };
 
   if (c_begin < c_end) {
     issue_qkg(c_begin);
     issue_v(c_begin);
+    // the first chunk's rows land before the loop, so that at the top of every
+    // iteration the transfers still outstanding are those the previous chunk
+    // issued, followed by its o stores
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  // o stores this wave issues per chunk (one per row of each owned tile)
-  int nst = 0;
-#pragma unroll
-  for (int cw = 0; cw < TPW; ++cw) nst += has(cw) ? 16 : 0;
-
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
-    // this wave's DMA transfers into the staging areas are done (they were
-    // issued before the previous chunk's o stores, which may stay in flight:
-    // vector memory operations complete in order), then every other wave's
-    if (OUTM && c > c_begin) {
-      if (nst == 32) __builtin_amdgcn_s_waitcnt(0x8070);       // vmcnt(32), lgkmcnt(0)
-      else if (nst == 48) __builtin_amdgcn_s_waitcnt(0xC070);  // vmcnt(48)
-      else if (nst == 16) __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16)
-      else __builtin_amdgcn_s_waitcnt(0);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0);
-    }
+    // this wave's DMA transfers into the staging areas are done, then every
+    // other wave's.  (The wait covers the previous chunk's o stores as well:
+    // loads and stores share the vector memory counter and need not complete
+    // in order with respect to each other, so no count short of zero proves
+    // the transfers done.)
+    __builtin_amdgcn_s_waitcnt(0);
     bar();
 
     // ================= A: normalise q, k; gates and band =================
@@ -462,8 +483,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       // each coefficient split into bf16 hi + lo
       const int rt = lane >> 4, m = lane & 15, k0 = (rt < 3 ? 0 : 16 * rt - (C + 3 - 32)) + m;
       const float cf[4] = {be * tp.x, be * tp.y, be * tp.z, be * tp.w};
-      bf16_t* th = sT + (rt * 16 + m) * LT + k0;
-      bf16_t* tl = th + 4 * 16 * LT;
+      // (one opaque offset: the address stays a short chain from the LDS array,
+      // so the compiler can tell these stores from the DMA's)
+      const int to = opaque((rt * 16 + m) * LT + k0);
+      bf16_t* th = sT + to;
+      bf16_t* tl = sT + (to + 4 * 16 * LT);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bf16_t hi = f32_to_bf16(cf[j]);
@@ -472,7 +496,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
     }
     bar();
-    if (c + 1 < c_end) issue_qkg(c + 1);
 
     // ================= B: Gram tiles and diagonal inverses; right-hand sides,
     // tile exponents, Q^ M =================
@@ -587,22 +610,24 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
           const half8_t aq = row_frag_kp<LDK>(rQkp, rt * 16, kb * 32);
 #pragma unroll
           for (int cw = 0; cw < TPW; ++cw)
-            if (has(cw)) O[cw][rt] = mfma(aq, mk[cw], O[cw][rt]);
+            if (has(cw)) O[cw][rt] = mfma(mk[cw], aq, O[cw][rt]);
         }
         __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const float4 gm = *reinterpret_cast<const float4*>(sGam + rt * 16 + 4 * g4);
-        const float gmv[4] = {gm.x, gm.y, gm.z, gm.w};
+        const float gm = sGam[rt * 16 + m16];  // the row of O this lane holds
 #pragma unroll
         for (int cw = 0; cw < TPW; ++cw)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[cw][rt][i] *= gmv[i];
+          for (int i = 0; i < 4; ++i) O[cw][rt][i] *= gm;
       }
     }
     bar();
-    if (c + 1 < c_end) issue_v(c + 1);
+    if (c + 1 < c_end) {
+      issue_qkg(c + 1);
+      issue_v(c + 1);
+    }
 
     // ================= D: -W^T and U0 by blocked forward substitution =================
     {
@@ -662,7 +687,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
             const half8_t ap = row_frag_kp<LC>(rPkp, rt * 16, kb * 32);
 #pragma unroll
             for (int cw = 0; cw < TPW; ++cw)
-              if (has(cw)) O[cw][rt] = mfma(ap, vn[cw], O[cw][rt]);
+              if (has(cw)) O[cw][rt] = mfma(vn[cw], ap, O[cw][rt]);
           }
         __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
