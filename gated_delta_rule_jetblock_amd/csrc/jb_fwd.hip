@@ -199,23 +199,26 @@ struct Geo {
   static constexpr int TPW = (NCT + NW - 1) / NW;              // tiles per wave: wave w owns w, w + 8, ..
   static constexpr int GW = NW - 1;                            // gate wave
   static constexpr int IW = NW - 2;                            // inverse wave
-  static constexpr int LDK = DK + 16, LC = C + 8, LWT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
+  static constexpr int LDK = DK + 16, LC = C + 8, LTT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
   static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
   static constexpr int oKh = a16(oT + 2 * 4 * 16 * LT * 2);     // [C][LDK] K^
   static constexpr int szQh = OUTM ? C * LDK * 2 : 0;
-  static constexpr int szWt = DK * LWT * 2;
-  static constexpr int oQW = a16(oKh + C * LDK * 2);            // Q^ (output), then -W^T [DK][LC]
-  static constexpr int oAn = a16(oQW + (szQh > szWt ? szQh : szWt));  // [C][LC] -A
+  static constexpr int szT = C * LTT * 2;
+  static constexpr int oQW = a16(oKh + C * LDK * 2);            // Q^ (output), then T^T [C][LTT]
+  static constexpr int oAn = a16(oQW + (szQh > szT ? szQh : szT));  // [C][LC] -A
   static constexpr int oAd = a16(oAn + C * LC * 2);             // [C][LAD] f32 diagonal blocks of A
   static constexpr int oLi = a16(oAd + C * LAD * 4);            // [C][LLI] their inverses
   static constexpr int oP = a16(oLi + C * LLI * 2);             // [C][LC] P (output)
-  static constexpr int WORK = a16(oP + (OUTM ? C * LC * 2 : 0));
+  static constexpr int oSO = oAn;                               // (output) o rows of a chunk, bf16 [C][DV]
+  static constexpr int SO_END = oSO + (OUTM ? C * DV * 2 : 0);  // over -A .. P, dead once P V_new is done
+  static constexpr int WORK0 = a16(oP + (OUTM ? C * LC * 2 : 0));
+  static constexpr int WORK = WORK0 > SO_END ? WORK0 : a16(SO_END);
   static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + (C + 3) * LV * 2;
   static_assert(WORK + STAGE <= 160 * 1024, "LDS budget of one CU exceeded");
   static_assert(RT <= NW, "one wave per W column tile");
-  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0 && (LWT * 2) % 8 == 0, "aligned rows");
+  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0 && (LTT * 2) % 8 == 0, "aligned rows");
 };
 
 // ------------------------------------------------------------ kernel
@@ -224,8 +227,11 @@ template <int DK, int DV, typename OUT, int MODE>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   using G = Geo<DK, DV, MODE>;
   constexpr bool OUTM = G::OUTM;
+  // bf16 outputs leave through LDS as whole rows (one 16-byte piece per lane,
+  // a chunk row in contiguous lanes); f32 outputs straight from the registers
+  constexpr bool STAGE_O = OUTM && sizeof(OUT) == 2;
   constexpr int NCT = G::NCT, VCT = G::VCT, RT = G::RT, KB = G::KB, NW = G::NW, TPW = G::TPW;
-  constexpr int LDK = G::LDK, LC = G::LC, LWT = G::LWT, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
+  constexpr int LDK = G::LDK, LC = G::LC, LTT = G::LTT, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
 
   // working tiles, and the DMA staging areas as arrays of their own (so the
   // compiler can tell that reads of the tiles never wait on the DMA)
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   _Float16* sP = reinterpret_cast<_Float16*>(work + G::oP);
   // the same tiles as LDS addresses, for the transposed reads and the DMA
   const lds_char* lKh = (const lds_char*)work + G::oKh;
-  const lds_char* lWt = (const lds_char*)work + G::oQW;  // -W^T [DK][LC]
+  const lds_char* lTt = (const lds_char*)work + G::oQW;  // T^T [C][LTT]
   const lds_char* lV = (const lds_char*)sV;
   lds_char* lKr = (lds_char*)sKr;
   lds_char* lQr = (lds_char*)sQr;
@@ -279,12 +285,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   auto isval = [&](int cw) { return wave + cw * NW < VCT; };
 
   // this lane's bases in the tiles
-  const lds_char* tKkp = tr_base_kp(lKh, LDK);   // K^ down its columns (K^T; the W right-hand side)
-  const lds_char* tWkp = tr_base_kp(lWt, LWT);   // -W^T down its columns (-W)
+  const lds_char* tKkp = tr_base_kp(lKh, LDK);   // K^ down its columns (K^T, for the state update)
+  const lds_char* tTkp = tr_base_kp(lTt, LTT);   // T^T down its columns (T)
   const lds_char* tVkp = tr_base_kp(lV, LV);     // value rows down their columns
   const _Float16* rKct = row_base_ct(sKh, LDK);  // rows of K^, Q^ (Gram tiles)
   const _Float16* rQct = row_base_ct(sQh, LDK);
   const _Float16* rQkp = row_base_kp(sQh, LDK);  // rows of Q^ (Q^ M)
+  const _Float16* rKkp = row_base_kp(sKh, LDK);  // rows of K^ (K^ M)
   const _Float16* rPkp = row_base_kp(sP, LC);
   const _Float16* rAkp = row_base_kp(sAn, LC);
   const _Float16* rLkp = row_base_kp(sLi, LLI);
@@ -315,7 +322,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // tiles never rewritten: the band outside its diagonals, P above its block diagonal
+  // tiles not rewritten per chunk: the band outside its diagonals, P above its
+  // block diagonal (but see the o staging below)
   for (int e = tid; e < 2 * 4 * 16 * LT / 8; e += NW * 64)
     reinterpret_cast<uint4*>(sT)[e] = make_uint4(0u, 0u, 0u, 0u);
   if (OUTM)
@@ -333,7 +341,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   // value rows, which are zeroed (the band multiplies them by zero
   // coefficients, and stale values could be non-finite)
   const uint32_t rowq = (uint32_t)(H * DK * 2), rowv = (uint32_t)(H * DV * 2);  // bytes between tokens
-  auto issue_qkg = [&](int cc) {
+  constexpr int VR = (C + 3 + NW - 1) / NW;  // staged value rows per wave
+  // q, k and gate rows of chunk cc, shared by waves 0 .. nw - 1 (wave wv takes
+  // the 64-piece rows wv, wv + nw, ..; the last of them also the gates)
+  auto issue_qkg = [&](int cc, int wv, int nw) {
     const int t0c = cc * C, nc = min(C, T - t0c);
     constexpr int PPK = DK / 8;  // 16-byte pieces per q or k row
     const int64_t e0 = (tok0 + t0c) * H * DK + (int64_t)h * DK;
@@ -341,10 +352,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + e0, bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + e0, bytes);
     const int ln = opaque(lane);
-    constexpr int NJ = (C * PPK + 64 * NW - 1) / (64 * NW);  // 64-piece rows per wave
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int j = wave + jj * NW;
+    for (int j = wv; j * 64 < C * PPK; j += nw) {
       const int p = j * 64 + ln, r = p / PPK, pc = p % PPK;
       const uint32_t off = (uint32_t)r * rowq + (uint32_t)pc * 16;
       if (p < C * PPK && r < nc) {
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         if (OUTM) dma_buf<16>(rq, off, lQr + j * 1024);
       }
     }
-    if (wave == G::GW && ln < nc) {
+    if (wv == nw - 1 && ln < nc) {
       const int64_t gidx = (tok0 + t0c) * H + h;
       const uint32_t gb = (uint32_t)(nc - 1) * H * 4 + 4;
       const uint32_t off = (uint32_t)(ln * H) * 4;
@@ -361,7 +369,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, lGr + 2 * C * 4);
     }
   };
-  auto issue_v = [&](int cc) {
+  // value rows (with the conv halo) of chunk cc: this wave's rows wave + NW i
+  // for i0 <= i < i1
+  auto issue_v = [&](int cc, int i0, int i1) {
     const int t0c = cc * C, nc = min(C, T - t0c);
     constexpr int PPR = DV / 8;  // 16-byte pieces per value row
     // rows from token rb0 (the halo's first row, or the chunk's when it starts the sequence)
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(cin ? cin + ((int64_t)b * 3 * H + h) * DV : v, cin ? 2 * rowv + DV * 2 : 0u);
     const int l16 = opaque(lane) * 16;
-    for (int r = wave; r < C + 3; r += NW) {  // staged row r holds token t0c - 3 + r
+    for (int r = wave + i0 * NW; r < C + 3 && r < wave + i1 * NW; r += NW) {  // row r holds token t0c - 3 + r
       const int t = t0c - 3 + r;
       lds_char* dst = lVw + r * LV * 2;
       if (l16 < PPR * 16) {
@@ -415,9 +425,49 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
   };
 
+  // bf16 o rows of a chunk in LDS: row r at r * DV * 2 bytes, its 32-byte
+  // column blocks permuted by the row (block b sits at b ^ (r % NCT)) so that
+  // the tile writes below spread over the banks
+  lds_char* lSO = (lds_char*)work + G::oSO;
+  auto so_addr = [&](int row, int cbyte) {  // cbyte: byte offset in the row
+    return row * (DV * 2) + (cbyte ^ ((row & (NCT - 1)) << 5));
+  };
+  // a column tile of outputs (held transposed, as in store_o) into the staging rows
+  auto stage_o = [&](const f4_t (&Ot)[4], int ct, int E) {
+    const int e = held_exp(E);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const uint32_t w0 = (uint32_t)f32_to_bf16(ldexpf(Ot[rt][0], e)) |
+                          ((uint32_t)f32_to_bf16(ldexpf(Ot[rt][1], e)) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(ldexpf(Ot[rt][2], e)) |
+                          ((uint32_t)f32_to_bf16(ldexpf(Ot[rt][3], e)) << 16);
+      *(__attribute__((address_space(3))) u2_t*)(lSO + opaque(so_addr(rt * 16 + m16, ct * 32 + 8 * g4))) =
+          u2_t{w0, w1};
+    }
+  };
+  // the staged rows t0p .. t0p + np - 1 to o: whole rows, 16 bytes per lane
+  // (rows at or beyond np fall outside the resource and are dropped)
+  auto flush_o = [&](int t0p, int np) {
+    constexpr int LPR = DV * 2 / 16;  // lanes per row
+    constexpr int RPI = 64 / LPR;     // rows per store
+    const uint32_t rowb = (uint32_t)(H * DV * 2);
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(reinterpret_cast<OUT*>(a.o) + ((tok0 + t0p) * H + h) * DV, (uint32_t)np * rowb);
+    const int ln = opaque(lane);
+    const int cb = (ln % LPR) * 16;
+#pragma unroll
+    for (int i = 0; i < C / (NW * RPI); ++i) {
+      const int row = (wave * (C / (NW * RPI)) + i) * RPI + ln / LPR;
+      const u4_t val = *(const __attribute__((address_space(3))) u4_t*)(lSO + so_addr(row, cb));
+      // a zero soffset: the compiler then guards the store's data registers
+      __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(row * rowb) + cb, 0, 0);
+    }
+  };
+  int pend_t0 = 0, pend_n = 0;
+
   if (c_begin < c_end) {
-    issue_qkg(c_begin);
-    issue_v(c_begin);
+    issue_qkg(c_begin, wave, NW);
+    issue_v(c_begin, 0, VR);
     // the first chunk's rows land before the loop, so that at the top of every
     // iteration the transfers still outstanding are those the previous chunk
     // issued, followed by its o stores
@@ -433,6 +483,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     // the transfers done.)
     __builtin_amdgcn_s_waitcnt(0);
     bar();
+
+    // the previous chunk's outputs, staged in LDS, leave first (their region is
+    // next written in phase B)
+    if constexpr (STAGE_O)
+      if (c > c_begin) flush_o(pend_t0, pend_n);
 
     // ================= A: normalise q, k; gates and band =================
     {
@@ -569,6 +624,18 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       constexpr uint32_t kOffI = 0xfe9u, kOffJ = 0x910u;  // two bits per job
       gram((kOffI >> (2 * wave)) & 3, (kOffJ >> (2 * wave)) & 3);
       if (wave < 2) gram((kOffI >> (2 * wave + 8)) & 3, (kOffJ >> (2 * wave + 8)) & 3);
+      // these waves are done with the Gram work first: they move the next
+      // chunk's q, k and gate rows (the staging areas were last read in phase A)
+      if (c + 1 < c_end) issue_qkg(c + 1, wave, 4);
+      if constexpr (STAGE_O) {
+        // the two zero blocks above P's block diagonal that P V_new reads,
+        // rows 0..15 x columns 16..31 and rows 32..47 x columns 48..63 (the
+        // o staging rows of the previous chunk lay over them)
+        if (wave == 3) {
+          const int blk = lane >> 5, r = blk * 32 + ((lane & 31) >> 1), c0 = blk * 32 + 16 + 8 * (lane & 1);
+          *reinterpret_cast<u4_t*>(sP + opaque(r * LC + c0)) = u4_t{0u, 0u, 0u, 0u};
+        }
+      }
     }
     // the rest of the phase after the Gram work (waves 0..3 and 4..7 share the
     // SIMDs pairwise, so the other wave fills a SIMD while one inverts)
@@ -594,26 +661,43 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int cw = 0; cw < TPW; ++cw)
       if (has(cw)) rescale_tile(Macc[cw], U[cw], Ex[cw]);
+    // R = diag(b) V' - diag(b gamma) K^ M (both now at the tile's scale): the rows
+    // of K^ scaled by -b gamma of their token (the A fragment's row is the
+    // lane's), onto the band product; with the same fragments of M, the output
+    // pass forms Q^ M (transposed, as the o tiles are held)
     f4_t O[OUTM ? TPW : 1][4];
     if constexpr (OUTM) {
 #pragma unroll
       for (int cw = 0; cw < TPW; ++cw)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) O[cw][rt] = zero4();
+    }
+    {
+      _Float16 bg[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) bg[rt] = (_Float16)(-sBeta[rt * 16 + m16] * sGam[rt * 16 + m16]);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        half8_t mk[TPW];  // this chunk's M as fp16 B fragments (kperm rows)
+        half8_t mk[TPW];  // this chunk's M as fp16 fragments (kperm rows)
 #pragma unroll
         for (int cw = 0; cw < TPW; ++cw) mk[cw] = acc_frag2(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const half8_t aq = row_frag_kp<LDK>(rQkp, rt * 16, kb * 32);
+          const half8_t ak = row_frag_kp<LDK>(rKkp, rt * 16, kb * 32) * bg[rt];
 #pragma unroll
           for (int cw = 0; cw < TPW; ++cw)
-            if (has(cw)) O[cw][rt] = mfma(mk[cw], aq, O[cw][rt]);
+            if (has(cw)) U[cw][rt] = mfma(ak, mk[cw], U[cw][rt]);
+          if constexpr (OUTM) {
+            const half8_t aq = row_frag_kp<LDK>(rQkp, rt * 16, kb * 32);
+#pragma unroll
+            for (int cw = 0; cw < TPW; ++cw)
+              if (has(cw)) O[cw][rt] = mfma(mk[cw], aq, O[cw][rt]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
+    }
+    if constexpr (OUTM) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const float gm = sGam[rt * 16 + m16];  // the row of O this lane holds
@@ -624,56 +708,56 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
     }
     bar();
-    if (c + 1 < c_end) {
-      issue_qkg(c + 1);
-      issue_v(c + 1);
-    }
+    // the next chunk's value rows, in three portions spread over phases D and E
+    if (c + 1 < c_end) issue_v(c + 1, 0, VR / 3);
 
-    // ================= D: -W^T and U0 by blocked forward substitution =================
-    {
-      const int jw = NW - 1 - wave;  // W column tile of this wave
-      if (jw < RT) {
-        // right-hand side diag(b gamma) K^, column tile jw, read down the columns of K^
-        f4_t Y[4];
+    // ================= D: T = (I + A)^{-1} by blocked forward substitution,
+    // column block j on wave j (its columns of the identity as right-hand side)
+    if (wave < 4) {
+      const int j = wave, jm = opaque(m16 - 4 * g4);  // lane's identity entry: row 16 j + 4 g4 + i == 16 j + m16
+      f4_t Y[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const h4_t kh = __builtin_bit_cast(h4_t, tr4(tKkp + (rb * 16 * LDK + jw * 16) * 2));
-          const float4 bt = *reinterpret_cast<const float4*>(sBeta + rb * 16 + 4 * g4);
-          const float4 gm = *reinterpret_cast<const float4*>(sGam + rb * 16 + 4 * g4);
-          Y[rb] = f4_t{bt.x * gm.x * (float)kh[0], bt.y * gm.y * (float)kh[1], bt.z * gm.z * (float)kh[2],
-                       bt.w * gm.w * (float)kh[3]};
-        }
-        solve<LC, LLI>(Y, rAkp, rLkp);
-        // -W^T: row jw*16 + m16, columns 16 rb + 4 g4 .. + 3
-        _Float16* sWt = reinterpret_cast<_Float16*>(work + G::oQW);
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const h2_t w0 = __builtin_convertvector(f2_t{-Y[rb][0], -Y[rb][1]}, h2_t);
-          const h2_t w1 = __builtin_convertvector(f2_t{-Y[rb][2], -Y[rb][3]}, h2_t);
-          *reinterpret_cast<h4_t*>(sWt + (jw * 16 + m16) * LWT + rb * 16 + 4 * g4) = h4_t{w0[0], w0[1], w1[0], w1[1]};
-        }
+        for (int i = 0; i < 4; ++i) Y[rb][i] = (rb == j && i == jm) ? 1.f : 0.f;
+      solve<LC, LLI>(Y, rAkp, rLkp);
+      // T^T: row 16 j + m16, columns 16 rb + 4 g4 .. + 3 (zero above the diagonal blocks)
+      _Float16* sTt = reinterpret_cast<_Float16*>(work + G::oQW);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const h2_t w0 = __builtin_convertvector(f2_t{Y[rb][0], Y[rb][1]}, h2_t);
+        const h2_t w1 = __builtin_convertvector(f2_t{Y[rb][2], Y[rb][3]}, h2_t);
+        *reinterpret_cast<h4_t*>(sTt + opaque((j * 16 + m16) * LTT + rb * 16 + 4 * g4)) =
+            h4_t{w0[0], w0[1], w1[0], w1[1]};
       }
-#pragma unroll
-      for (int cw = 0; cw < TPW; ++cw)
-        if (isval(cw)) solve<LC, LLI>(U[cw], rAkp, rLkp);
     }
+    if (c + 1 < c_end) issue_v(c + 1, VR / 3, 2 * VR / 3);
     bar();
 
     // ================= E: state-dependent part of the chunk =================
-    // V_new = U0 - W M (W^T read down its columns; kperm rows of dk)
+    // V_new = T R (T read down the columns of T^T; row block rt takes K blocks
+    // kb <= rt / 2, T being lower triangular), over R in place
+    {
+      half8_t rf[TPW][2];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      half8_t mk[TPW];
+      for (int cw = 0; cw < TPW; ++cw)
 #pragma unroll
-      for (int cw = 0; cw < TPW; ++cw) mk[cw] = acc_frag2(Macc[cw][2 * kb], Macc[cw][2 * kb + 1]);
+        for (int kb = 0; kb < 2; ++kb) rf[cw][kb] = acc_frag2(U[cw][2 * kb], U[cw][2 * kb + 1]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const half8_t aw = tr_frag_kp<LWT>(tWkp, kb * 32, rt * 16);
+        const half8_t t0f = tr_frag_kp<LTT>(tTkp, 0, rt * 16);
 #pragma unroll
         for (int cw = 0; cw < TPW; ++cw)
-          if (has(cw)) U[cw][rt] = mfma(aw, mk[cw], U[cw][rt]);
+          if (has(cw)) U[cw][rt] = mfma(t0f, rf[cw][0], zero4());
+        if (rt >= 2) {
+          const half8_t t1f = tr_frag_kp<LTT>(tTkp, 32, rt * 16);
+#pragma unroll
+          for (int cw = 0; cw < TPW; ++cw)
+            if (has(cw)) U[cw][rt] = mfma(t1f, rf[cw][1], U[cw][rt]);
+        }
       }
     }
+    if (c + 1 < c_end) issue_v(c + 1, 2 * VR / 3, VR);
     if constexpr (OUTM) {
       // O += P V_new, then the outputs
 #pragma unroll
@@ -691,9 +775,18 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
           }
         __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
+      if constexpr (STAGE_O) {
+        bar();  // every wave is done with P (and -A, its diagonal blocks and their inverses)
 #pragma unroll
-      for (int cw = 0; cw < TPW; ++cw)
-        if (has(cw)) store_o(O[cw], tile(cw), t0, n, Ex[cw]);
+        for (int cw = 0; cw < TPW; ++cw)
+          if (has(cw)) stage_o(O[cw], tile(cw), Ex[cw]);
+        pend_t0 = t0;  // stored at the start of the next chunk
+        pend_n = n;
+      } else {
+#pragma unroll
+        for (int cw = 0; cw < TPW; ++cw)
+          if (has(cw)) store_o(O[cw], tile(cw), t0, n, Ex[cw]);
+      }
     }
     // M <- gamma_C M + K^T diag(e^{g_C - g}) V_new (K^ read down its columns)
     {
@@ -720,6 +813,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);  // one K block of fragments in registers at a time
       }
+    }
+  }
+
+  if constexpr (STAGE_O) {
+    if (c_begin < c_end) {
+      bar();
+      flush_o(pend_t0, pend_n);
     }
   }
 
