@@ -278,6 +278,80 @@ def measure_training(jb, inputs, torch, sp, B: int, T: int, reps: int = 3):
                 tokens_per_s=round(tok / ((ms_f + ms_b) * 1e-3), 1), backward_over_forward=round(ms_b / ms_f, 2))
 
 
+def measure_4b(jb, inputs, torch, out_dt, out_bytes: int, reps: int = 3, dsteps: int = 32):
+    """The JetBlock-4B-shape workload as one chain: jb_prefill of B=1, T=262144, H=16, dk=128,
+    dv=256, d_model=2048 (HIP events around each call), then jb_decode_step on a batch of 128
+    sequences started from the prefill's final state and conv cache (events around each
+    launch), with the layer's own generator weights."""
+    sp, sd = inputs.B4_T262144, inputs.B4_DECODE
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    p = inputs.prefill_inputs(sp, seed=0, device=dev)
+    o = torch.empty((sp.B, sp.T, sp.H, sp.dv), dtype=out_dt, device=dev)
+    S_fin = torch.empty((sp.B, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
+    conv_out = torch.empty((sp.B, 3, sp.H, sp.dv), dtype=torch.bfloat16, device=dev)
+    shp = jb.make_shape(sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.d_model, jb.JB_BF16,
+                        jb.JB_BF16 if out_dt == torch.bfloat16 else jb.JB_F32)
+    ws = jb.workspace(jb.prefill_workspace_size(shp), dev)
+
+    def pre():
+        jb.prefill(p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"], p["W2"], out_dtype=out_dt,
+                   o=o, S_final=S_fin, conv_out=conv_out, ws=ws, stream=stream)
+
+    pre()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pre()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    pre_ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+
+    d = inputs.decode_inputs(sd, steps=dsteps, seed=1, device=dev, with_state=False)
+    S = S_fin.expand(sd.B, -1, -1, -1).contiguous()
+    cache = conv_out.expand(sd.B, -1, -1, -1).contiguous()
+    od = torch.empty((sd.B, sd.H, sd.dv), dtype=out_dt, device=dev)
+
+    def dec(t):
+        jb.decode_step(S, cache, d["x"][t], d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["beta"][t],
+                       p["W1"], p["W2"], out_dtype=out_dt, o=od, stream=stream)
+
+    dec(0)
+    torch.cuda.synchronize()
+    ev = []
+    for t in range(1, dsteps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dec(t)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    dec_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    pre_flops = prefill_flops_per_token(sp) * sp.T
+    pre_tf = pre_flops / (pre_ms * 1e-3) / 1e12
+    pre_gbs = prefill_bytes_per_token(sp, out_bytes) * sp.T / (pre_ms * 1e-3) / 1e9
+    dec_bytes = decode_step_bytes(sd, out_bytes)
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    out = dict(
+        workload="JetBlock-4B shape: prefill B=1 T=262144 H=16 dk=128 dv=256 d_model=2048, then decode of "
+                 f"B=128 from its state ({dsteps - 1} timed steps)",
+        prefill=dict(ms=round(pre_ms, 4), tokens_per_s=round(sp.T / (pre_ms * 1e-3), 1),
+                     roofline=dict(call="jb_prefill", bound="mfma", achieved=round(pre_tf, 2),
+                                   peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s", frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4),
+                                   hbm_GBs=round(pre_gbs, 1), hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4),
+                                   flops_per_call=pre_flops)),
+        decode=dict(launch_us=round(dec_ms * 1e3, 2), tokens_per_s=round(sd.B / (dec_ms * 1e-3), 1),
+                    roofline=dict(kernel="decode_seq_kernel (jb_decode_step)", bound="hbm",
+                                  achieved=round(dec_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                  frac=round(dec_gbs / HBM_PEAK_GBS, 4), bytes_per_launch=dec_bytes)))
+    del p, o, ws, S, cache, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_step, budget_tokens):
     """Time the fp64 oracle on a bounded sample and scale to the step's token mix."""
     import oracle
@@ -305,11 +379,27 @@ def cpu_baseline(shape_p, shape_d, prefill_tokens_per_step, decode_tokens_per_st
     pre_rate = tp / t_pre
     dec_rate = shape_d.B * dsteps / t_dec
     step_s = prefill_tokens_per_step / pre_rate + decode_tokens_per_step / dec_rate
+    # the same oracle on one thread, on a smaller sample
+    tp1 = max(256, budget_tokens // 16)
+    args1 = [f(p[k][:, :tp1].contiguous()) if k in ("x", "q", "k", "v", "alpha", "beta") else f(p[k])
+             for k in ("x", "q", "k", "v", "alpha", "beta", "W1", "W2")]
+    t0 = time.perf_counter()
+    oracle.prefill(*args1, nthreads=1)
+    t_pre1 = time.perf_counter() - t0
+    S, c = f(d["S"]), f(d["cache"])
+    t0 = time.perf_counter()
+    oracle.decode_step(S, c, *(f(d[k][0]) for k in ("x", "q", "k", "v", "alpha", "beta")), f(d["W1"]), f(d["W2"]),
+                       nthreads=1)
+    t_dec1 = time.perf_counter() - t0
+    step1 = prefill_tokens_per_step * t_pre1 / tp1 + decode_tokens_per_step * t_dec1 / shape_d.B
     return dict(value=(prefill_tokens_per_step + decode_tokens_per_step) / step_s, unit="tokens/s", cores=threads,
                 kind="oracle",
                 sample=f"fp64 oracle: prefill of {tp} tokens (all {shape_p.H} heads) in {t_pre:.2f} s and "
                        f"{dsteps} decode steps x {shape_d.B} sequences in {t_dec:.2f} s, scaled to one step",
-                prefill_tokens_per_s=pre_rate, decode_tokens_per_s=dec_rate)
+                prefill_tokens_per_s=pre_rate, decode_tokens_per_s=dec_rate,
+                single_thread=dict(value=(prefill_tokens_per_step + decode_tokens_per_step) / step1, cores=1,
+                                   sample=f"prefill of {tp1} tokens in {t_pre1:.2f} s and one decode step x "
+                                          f"{shape_d.B} sequences in {t_dec1:.2f} s, scaled to one step"))
 
 
 def main():
@@ -327,6 +417,7 @@ def main():
     ap.add_argument("--no-static", action="store_true", help="skip the static-conv block measurement")
     ap.add_argument("--no-serving", action="store_true", help="skip the packed serving-batch measurement")
     ap.add_argument("--no-training", action="store_true", help="skip the forward + backward measurement")
+    ap.add_argument("--no-4b", action="store_true", help="skip the JetBlock-4B-shape chain (with --workload 2b)")
     ap.add_argument("--serving-requests", type=int, default=256)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="oracle prefill sample length")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -428,7 +519,15 @@ def main():
     pre_flops = prefill_flops_per_token(sp) * tok_pre
     pre_tf = pre_flops / (pre_ms * 1e-3) / 1e12
     pre_gbs = prefill_bytes_per_token(sp, out_bytes) * tok_pre / (pre_ms * 1e-3) / 1e9
-    roof_pre = dict(call="jb_prefill (generator, per-chunk tiles, summary, scan, output kernels)", bound="mfma",
+    pre_traffic = (measured_traffic("prefill_jetblock2b_T65536.md",
+                                    ["gated_delta_rule_jetblock_amd/csrc/jb_fwd.hip",
+                                     "gated_delta_rule_jetblock_amd/csrc/jb_chunk.h",
+                                     "gated_delta_rule_jetblock_amd/csrc/jb_device.h",
+                                     "gated_delta_rule_jetblock_amd/csrc/jb_gen.hip",
+                                     "gated_delta_rule_jetblock_amd/csrc/jb_prefill.hip"])
+                   if args.workload == "2b" and args.out_dtype == "bf16" else None)
+    roof_pre = dict(call="jb_prefill (generator, fused summary pass, segment scan, fused output pass)", bound="mfma",
+                    traffic=pre_traffic, compulsory_bytes=prefill_bytes_per_token(sp, out_bytes) * tok_pre,
                     achieved=round(pre_tf, 2), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(pre_tf / MFMA_PEAK_TFLOPS, 4), hbm_GBs=round(pre_gbs, 1),
                     hbm_frac=round(pre_gbs / HBM_PEAK_GBS, 4), flops_per_call=pre_flops,
@@ -461,6 +560,13 @@ def main():
         training = measure_training(jb, inputs, torch, sp, 16, 4096)
         log(f"training: forward {training['forward']['ms']:.2f} ms, backward {training['backward']['ms']:.2f} ms "
             f"({training['tokens_per_s'] / 1e6:.2f} M tokens/s forward + backward)")
+    jb4 = None
+    if args.workload == "2b" and not args.no_4b:
+        log("timing the JetBlock-4B-shape chain (prefill T=262144, decode B=128) ...")
+        jb4 = measure_4b(jb, inputs, torch, out_dt, out_bytes)
+        log(f"4B: prefill {jb4['prefill']['ms']:.3f} ms ({jb4['prefill']['roofline']['frac'] * 100:.1f}% of the "
+            f"MFMA peak), decode launch {jb4['decode']['launch_us']:.1f} us "
+            f"({jb4['decode']['roofline']['frac'] * 100:.1f}% of HBM)")
     if args.calibrate_copy:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
         dst = torch.empty_like(src)
@@ -497,6 +603,7 @@ def main():
         "static_conv": static,
         "serving": serving,
         "training": training,
+        "jetblock4b": jb4,
     }
     print(json.dumps(line), flush=True)
 

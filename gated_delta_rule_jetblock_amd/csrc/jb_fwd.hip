@@ -199,7 +199,7 @@ struct Geo {
   static constexpr int TPW = (NCT + NW - 1) / NW;              // tiles per wave: wave w owns w, w + 8, ..
   static constexpr int GW = NW - 1;                            // gate wave
   static constexpr int IW = NW - 2;                            // inverse wave
-  static constexpr int LDK = DK + 16, LC = C + 8, LTT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
+  static constexpr int LDK = DK + 8, LC = C + 8, LTT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
   static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
@@ -425,12 +425,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // bf16 o rows of a chunk in LDS: row r at r * DV * 2 bytes, its 32-byte
-  // column blocks permuted by the row (block b sits at b ^ (r % NCT)) so that
-  // the tile writes below spread over the banks
+  // bf16 o rows of a chunk in LDS: row r at r * DV * 2 bytes, its 16-byte
+  // pieces permuted by the row (piece p sits at p ^ (r % (DV / 8))) so that the
+  // tile writes below (16 rows, one 16-byte piece each per half wave) touch
+  // every bank once
   lds_char* lSO = (lds_char*)work + G::oSO;
   auto so_addr = [&](int row, int cbyte) {  // cbyte: byte offset in the row
-    return row * (DV * 2) + (cbyte ^ ((row & (NCT - 1)) << 5));
+    return row * (DV * 2) + (cbyte ^ ((row & (DV / 8 - 1)) << 4));
   };
   // a column tile of outputs (held transposed, as in store_o) into the staging rows
   auto stage_o = [&](const f4_t (&Ot)[4], int ct, int E) {
