@@ -79,3 +79,13 @@ def test_backward_jetblock2b_T1024(jb, oracle_mod):
     errs = _run(jb, oracle_mod, Shape(B=1, T=1024, H=12, dk=96, dv=256, d_model=1536), seed=5)
     bad = {n: e for n, e in errs.items() if not e < TOL}
     assert not bad, bad
+
+
+def test_backward_training_shape_B16_T4096(jb, oracle_mod):
+    """The training shape the bench times: B=16 sequences x T=4,096 tokens at the 2B head
+    shape (H=12, dk=96, dv=256, d_model=1536), 1,024 chunks per head in all, with initial
+    states and conv caches and every output gradient; every gradient tensor against the
+    oracle over all sixteen sequences and twelve heads."""
+    print("[backward B=16 T=4096 2B heads]", flush=True)
+    errs = _run(jb, oracle_mod, Shape(B=16, T=4096, H=12, dk=96, dv=256, d_model=1536), seed=31)
+    assert max(errs.values()) < TOL, errs
