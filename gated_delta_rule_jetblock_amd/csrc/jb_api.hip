@@ -52,6 +52,7 @@ jb_status check_shape(const char* fn, const jb_shape* s, bool decode) {
   if (s->B > 65535) return fail(JB_ERR_UNSUPPORTED, "%s: B = %d exceeds 65535 (one grid dimension)", fn, s->B);
   if (decode ? s->T != 1 : s->T < 0)
     return fail(JB_ERR_INVALID_ARG, "%s: T = %d (%s)", fn, s->T, decode ? "decode needs T == 1" : "must be >= 0");
+  if (s->T > (1 << 30)) return fail(JB_ERR_UNSUPPORTED, "%s: T = %d exceeds 2^30", fn, s->T);
   if (s->H < 1 || s->H > 32) return fail(JB_ERR_UNSUPPORTED, "%s: H = %d not in [1, 32]", fn, s->H);
   if (s->dk != 32 && s->dk != 64 && s->dk != 96 && s->dk != 128)
     return fail(JB_ERR_UNSUPPORTED, "%s: dk = %d not in {32, 64, 96, 128}", fn, s->dk);
@@ -93,7 +94,10 @@ jb_status hip_status(const char* fn, hipError_t e) {
 extern "C" {
 
 const char* jb_status_string(jb_status st) {
-  switch (st) {
+  // a C caller may pass any int: read the bits as an int, not as the enum
+  int v;
+  memcpy(&v, &st, sizeof v);
+  switch (v) {
     case JB_OK: return "JB_OK";
     case JB_ERR_INVALID_ARG: return "JB_ERR_INVALID_ARG";
     case JB_ERR_UNSUPPORTED: return "JB_ERR_UNSUPPORTED";
@@ -116,15 +120,14 @@ jb_status jb_prefill_workspace_size(const jb_shape* s, size_t* bytes) {
   return ok();
 }
 
-static jb_status prefill_impl(const char* fn, const jb_shape* s, const void* x, const void* q, const void* k,
-                              const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
-                              const void* W2, const void* b2, const float* S0, const void* conv_in, void* o,
-                              float* S_final, void* conv_out, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+// Shape and pointer checks of jb_prefill and jb_prefill_noalloc (everything but the workspace).
+static jb_status check_prefill(const char* fn, const jb_shape* s, const void* x, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
+                               const void* W2, const void* b2, const float* S0, const void* conv_in, const void* o,
+                               const float* S_final, const void* conv_out) {
   jb_status st = check_shape(fn, s, false);
   if (st) return st;
-  const jb::PrefillPlan p = plan_of(s);
-  if (!jb::prefill_supported(p))
+  if (!jb::prefill_supported(plan_of(s)))
     return fail(JB_ERR_UNSUPPORTED, "%s: dk=%d dv=%d not built for io_dtype %d (the all-fp32 mode needs dk*dv <= 4096)",
                 fn, s->dk, s->dv, s->io_dtype);
   if (seg_flag(s) < 0) return fail(JB_ERR_INVALID_ARG, "%s: bad segment flag", fn);
@@ -135,6 +138,17 @@ static jb_status prefill_impl(const char* fn, const jb_shape* s, const void* x, 
   JB_REQUIRE_PTR(W1); JB_REQUIRE_PTR(W2); JB_REQUIRE_PTR(S_final);
   JB_OPTIONAL_PTR(b1); JB_OPTIONAL_PTR(b2); JB_OPTIONAL_PTR(S0); JB_OPTIONAL_PTR(conv_in);
   JB_OPTIONAL_PTR(conv_out);
+  return JB_OK;
+}
+
+static jb_status prefill_impl(const char* fn, const jb_shape* s, const void* x, const void* q, const void* k,
+                              const void* v, const float* alpha, const float* beta, const void* W1, const void* b1,
+                              const void* W2, const void* b2, const float* S0, const void* conv_in, void* o,
+                              float* S_final, void* conv_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  jb_status st = check_prefill(fn, s, x, q, k, v, alpha, beta, W1, b1, W2, b2, S0, conv_in, o, S_final, conv_out);
+  if (st) return st;
+  const jb::PrefillPlan p = plan_of(s);
   const size_t need = jb::prefill_workspace_bytes(p);
   if (need && !workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
   if (workspace_bytes < need)
@@ -208,7 +222,7 @@ jb_status jb_prefill_noalloc(const jb_shape* s, const void* x, const void* q, co
                              const void* b2, const float* S0, const void* conv_in, void* o, float* S_final,
                              void* conv_out, void* stream) {
   const char* fn = "jb_prefill_noalloc";
-  jb_status st = check_shape(fn, s, false);
+  jb_status st = check_prefill(fn, s, x, q, k, v, alpha, beta, W1, b1, W2, b2, S0, conv_in, o, S_final, conv_out);
   if (st) return st;
   const size_t need = jb::prefill_workspace_bytes(plan_of(s));
   if (need > JB_NOALLOC_SCRATCH_BYTES)

@@ -937,7 +937,7 @@ PrefillPlan plan_prefill(int B, int T, int H, int dk, int dv, int io, int out, i
   p.B = B; p.T = T; p.H = H; p.dk = dk; p.dv = dv; p.io = io; p.out = out;
   p.tokens = (int64_t)B * T;
   p.cu_seqlens = nullptr;
-  p.nchunks = (T + C - 1) / C;
+  p.nchunks = (int)(((int64_t)T + C - 1) / C);
   if (p.nchunks == 0) { p.seg_len = 1; p.nseg = 0; return p; }
   if (seg_len <= 0) {
     const int64_t units = (int64_t)B * H;

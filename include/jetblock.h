@@ -45,8 +45,8 @@
  *
  * Supported shapes: dk in {32, 64, 96, 128}; dv in {64, 128, 256};
  * gen_hidden == 32; taps == 4; chunk == 64 (0 selects 64); d_model a
- * positive multiple of 128; 1 <= B <= 65535; H <= 32; T >= 0 for prefill,
- * T == 1 for decode.
+ * positive multiple of 128; 1 <= B <= 65535; H <= 32; 0 <= T <= 2^30 for
+ * prefill, T == 1 for decode; fewer than 2^40 elements in any tensor.
  * The all-fp32 mode of jb_prefill additionally needs dk*dv <= 64*64 (its
  * tiles must fit in the 160 KB of LDS of one compute unit).
  */
@@ -98,10 +98,9 @@ int32_t jb_version(void);
 /*
  * Workspace bytes jb_prefill needs for `shape` (device memory, 256-byte
  * aligned, contents ignored on entry).  Writes *bytes; returns JB_OK or a
- * validation error.  It holds the per-token conv taps, the segment maps
- * when the sequence is cut into segments and, with bf16 inputs, every
- * chunk's state-independent tiles (about 80 KB per (sequence, head, chunk)
- * at dk = 96, dv = 256).
+ * validation error.  It holds the per-token conv taps (B*T*H*4 floats)
+ * and, when a sequence is cut into segments, each segment's start state and
+ * its two summaries (2*dk*dv + dk*dk floats per (sequence, head, segment)).
  */
 jb_status jb_prefill_workspace_size(const jb_shape* shape, size_t* bytes);
 

@@ -57,10 +57,14 @@ def test_noalloc_matches_prefill_two_calls(jb):
 
 
 def test_noalloc_rejects_shapes_above_the_array(jb):
-    """B = 1, T = 65536, H = 12 needs 68 MiB: JB_ERR_WORKSPACE from the host check,
-    with every pointer NULL (nothing is read or launched)."""
+    """B = 1, T = 65536, H = 12 needs 68 MiB: JB_ERR_WORKSPACE from the host check.  The
+    pointers are aligned stand-ins that the library never dereferences: every check runs
+    on the host before the first HIP call, the pointers' first (a NULL x is named)."""
     s = jb.make_shape(1, 65536, 12, 96, 256, 1536, jb.JB_BF16, jb.JB_BF16)
     assert jb.prefill_workspace_size(s) > jb.NOALLOC_SCRATCH_BYTES
-    st = jb.library().jb_prefill_noalloc(ctypes.byref(s), *([None] * 15), None)
+    stand_in = ctypes.c_void_p(1 << 20)
+    st = jb.library().jb_prefill_noalloc(ctypes.byref(s), *([stand_in] * 15), None)
     assert st == jb.JB_ERR_WORKSPACE, (st, jb.last_error())
     assert "jb_prefill_noalloc" in jb.last_error() and "workspace" in jb.last_error()
+    st = jb.library().jb_prefill_noalloc(ctypes.byref(s), None, *([stand_in] * 14), None)
+    assert st == jb.JB_ERR_INVALID_ARG and "x is NULL" in jb.last_error(), (st, jb.last_error())
