@@ -46,7 +46,7 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
-                           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"])
+                           "-Wl,-rpath,/opt/rocm/lib"])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)

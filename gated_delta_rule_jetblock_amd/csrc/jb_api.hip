@@ -337,7 +337,7 @@ jb_status jb_decode_step(const jb_shape* s, const float* S_in, float* S_out, con
   const int io = s->io_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
   const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
   return hip_status(fn, jb::launch_decode_step(io, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
-                                               cache_out, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, b1, W2, b2, nullptr, nullptr, nullptr, nullptr, o_t,
+                                               cache_out, x_t, q_t, k_t, v_t, alpha_t, beta_t, W1, b1, W2, b2, o_t,
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -401,11 +401,8 @@ jb_status jb_project(const jb_shape* s, const void* x, const void* Wq, const voi
   JB_PROJECTION_PTRS();
   JB_REQUIRE_PTR(q); JB_REQUIRE_PTR(k); JB_REQUIRE_PTR(v); JB_REQUIRE_SCALARS(alpha); JB_REQUIRE_SCALARS(beta);
   JB_REQUIRE_PTR(taps);
-  const size_t need = jb::project_workspace_bytes((int64_t)s->B * s->T, s->H, s->d_model);
-  if (!workspace) return fail(JB_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
-  if (workspace_bytes < need)
-    return fail(JB_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
-  if ((uintptr_t)workspace & 255u) return fail(JB_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  (void)workspace;
+  (void)workspace_bytes;
   return hip_status(fn, jb::launch_project((int64_t)s->B * s->T, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa,
                                            ba, Wb, bb, W1, b1, W2, b2, q, k, v, alpha, beta, taps,
                                            workspace, static_cast<hipStream_t>(stream)));
@@ -416,8 +413,7 @@ jb_status jb_prefill_from_x_workspace_size(const jb_shape* s, size_t* bytes) {
   jb_status st = check_projection_args(fn, s);
   if (st) return st;
   if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
-  *bytes = a256(jb::prefill_workspace_bytes(plan_of(s))) + qkvab_bytes(s) +
-           jb::project_workspace_bytes((int64_t)s->B * s->T, s->H, s->d_model);
+  *bytes = a256(jb::prefill_workspace_bytes(plan_of(s))) + qkvab_bytes(s);
   return ok();
 }
 
@@ -471,9 +467,8 @@ jb_status jb_prefill_from_x(const jb_shape* s, const void* x, const void* Wq, co
   float* alpha = reinterpret_cast<float*>(ws);
   ws += a256(n * s->H * sizeof(float));
   float* beta = reinterpret_cast<float*>(ws);
-  ws += a256(n * s->H * sizeof(float));
   e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa, ba, Wb, bb, W1, b1, W2, b2, q,
-                         k, v, alpha, beta, taps, ws, hs);
+                         k, v, alpha, beta, taps, nullptr, hs);
   if (e == hipSuccess) e = jb::launch_prefill(p, q, k, v, alpha, beta, taps, conv_in, S0, o, S_final, pre_ws, hs);
   if (e == hipSuccess && conv_out) e = jb::launch_conv_tail(jb::IO_BF16, s->B, s->T, s->H, s->dv, v, conv_in, conv_out, hs);
   return hip_status(fn, e);
@@ -485,8 +480,8 @@ jb_status jb_decode_step_from_x_workspace_size(const jb_shape* s, size_t* bytes)
   if (st) return st;
   if (s->io_dtype != JB_BF16) return fail(JB_ERR_UNSUPPORTED, "%s: the projections take bf16 inputs only", fn);
   if (!bytes) return fail(JB_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
-  // q, k, v of the B tokens, then the projections' own
-  *bytes = qkvab_bytes(s) + jb::project_workspace_bytes(s->B, s->H, s->d_model);
+  // q, k, v and the gates of the B tokens
+  *bytes = qkvab_bytes(s);
   return ok();
 }
 
@@ -518,15 +513,17 @@ jb_status jb_decode_step_from_x(const jb_shape* s, const float* S_in, float* S_o
   ws += a256(n * s->H * s->dk * 2);
   void* v = ws;
   ws += a256(n * s->H * s->dv * 2);
+  float* alpha = reinterpret_cast<float*>(ws);
+  ws += a256(n * s->H * sizeof(float));
+  float* beta = reinterpret_cast<float*>(ws);
   const int out = s->out_dtype == JB_F32 ? jb::IO_F32 : jb::IO_BF16;
-  // q, k, v as GEMMs over the batch; the step itself forms the taps and the
-  // gates from x (its workgroups hold x_t of their sequence)
-  hipError_t e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, nullptr, nullptr,
-                                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, q, k, v, nullptr, nullptr,
-                                    nullptr, ws, hs);
+  // q, k, v and the gates of the batch from the projection kernel; the step
+  // forms the taps itself (its workgroups hold x_t of their sequence)
+  hipError_t e = jb::launch_project((int64_t)n, s->H, s->dk, s->dv, s->d_model, x, Wq, Wk, Wv, Wa, ba, Wb, bb, W1,
+                                    nullptr, nullptr, nullptr, q, k, v, alpha, beta, nullptr, nullptr, hs);
   if (e == hipSuccess)
     e = jb::launch_decode_step(jb::IO_BF16, out, s->B, s->H, s->dk, s->dv, s->d_model, S_in, S_out, cache_in,
-                               cache_out, x, q, k, v, nullptr, nullptr, W1, b1, W2, b2, Wa, ba, Wb, bb, o_t, hs);
+                               cache_out, x, q, k, v, alpha, beta, W1, b1, W2, b2, o_t, hs);
   return hip_status(fn, e);
 }
 

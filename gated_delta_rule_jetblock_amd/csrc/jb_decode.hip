@@ -287,18 +287,13 @@ __device__ __forceinline__ void seq_update_heads(SeqSmem<DK, DV, NW>& sm, float 
   }
 }
 
-// GX: the gates come from x as well, alpha = sigmoid(Wa x + ba) and
-// beta = sigmoid(Wb x + bb) (the step from the layer input), instead of from
-// alpha_t, beta_t.
-template <int DK, int DV, typename IO, typename OUT, int NW, bool GX>
+template <int DK, int DV, typename IO, typename OUT, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int D, const float* S_in,
                                                                  float* S_out, const IO* cache_in, IO* cache_out,
                                                                  const IO* x_t, const IO* q_t, const IO* k_t,
                                                                  const IO* v_t, const float* alpha_t,
                                                                  const float* beta_t, const IO* W1, const IO* b1,
-                                                                 const IO* W2, const IO* b2, const IO* Wa,
-                                                                 const IO* ba, const IO* Wb, const IO* bb,
-                                                                 OUT* o_t) {
+                                                                 const IO* W2, const IO* b2, OUT* o_t) {
   constexpr int NT = NW * 64;
   constexpr int RPW = DK / NW;                   // state rows per wave
   constexpr int UPW = 32 / NW;                   // generator hidden units per wave
@@ -307,7 +302,6 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
   constexpr int GU = (sizeof(IO) == 2 ? 8 : 4) / UPW;  // generator pieces per lane in flight
   constexpr int NPAIR = (SEQ_MAXHPG * DV / 2 + NT - 1) / NT;  // (head, column pair) conv items per thread, at most
   constexpr bool EARLY_B = 2 * RPW * CPL <= 48;  // second state tile in flight during the generator
-  constexpr int GR = GX ? 2 * SEQ_MAXHPG / NW : 1;  // gate rows per wave (GX), at most
   __shared__ SeqSmem<DK, DV, NW> sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -324,12 +318,7 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
   // ---- issue: generator pieces (wave w owns hidden units UPW w .. UPW w +
   // UPW-1, its lanes split d_model), the conv rows, then the state tiles
   const int npc = (D + 64 * EPC - 1) / (64 * EPC);  // pieces per lane over d_model
-  // gate row i of this wave (GX): row ri = wave + NW i of [Wa rows of the group's heads; Wb rows]
-  auto gate_row = [&](int i) -> const IO* {
-    const int ri = wave + NW * i;
-    return ri < HPG ? Wa + (int64_t)(h0 + ri) * D : Wb + (int64_t)(h0 + ri - HPG) * D;
-  };
-  uint4 gx[GU], gw[UPW][GU], gg[GR][GU];
+  uint4 gx[GU], gw[UPW][GU];
 #pragma unroll
   for (int g = 0; g < GU; ++g) {
     const int e = (g * 64 + lane) * EPC;
@@ -337,10 +326,6 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
     gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
 #pragma unroll
     for (int u = 0; u < UPW; ++u) gw[u][g] = ld16(W1 + (int64_t)(UPW * wave + u) * D + e, ok);
-    if constexpr (GX) {
-#pragma unroll
-      for (int i = 0; i < GR; ++i) gg[i][g] = ld16(gate_row(i) + e, ok && wave + NW * i < 2 * HPG);
-    }
   }
   // q and k of the wave's first head (each lane holds up to two elements)
   float kx[2] = {0.f, 0.f}, qx[2] = {0.f, 0.f};
@@ -372,19 +357,13 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- generator hidden layer (pre-activation), q / k normalisation, cache shift
-  float hacc[UPW], gacc[GR];
+  float hacc[UPW];
 #pragma unroll
   for (int u = 0; u < UPW; ++u) hacc[u] = 0.f;
-#pragma unroll
-  for (int i = 0; i < GR; ++i) gacc[i] = 0.f;
 #pragma unroll
   for (int g = 0; g < GU; ++g) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) hacc[u] = dot16(gw[u][g], gx[g], hacc[u], IO());
-    if constexpr (GX) {
-#pragma unroll
-      for (int i = 0; i < GR; ++i) gacc[i] = dot16(gg[i][g], gx[g], gacc[i], IO());
-    }
   }
   for (int p0 = GU; p0 < npc; p0 += GU) {  // d_model beyond one round of pieces
 #pragma unroll
@@ -394,42 +373,17 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
       gx[g] = ld16(x_t + (int64_t)b * D + e, ok);
 #pragma unroll
       for (int u = 0; u < UPW; ++u) gw[u][g] = ld16(W1 + (int64_t)(UPW * wave + u) * D + e, ok);
-      if constexpr (GX) {
-#pragma unroll
-        for (int i = 0; i < GR; ++i) gg[i][g] = ld16(gate_row(i) + e, ok && wave + NW * i < 2 * HPG);
-      }
     }
 #pragma unroll
     for (int g = 0; g < GU; ++g) {
 #pragma unroll
       for (int u = 0; u < UPW; ++u) hacc[u] = dot16(gw[u][g], gx[g], hacc[u], IO());
-      if constexpr (GX) {
-#pragma unroll
-        for (int i = 0; i < GR; ++i) gacc[i] = dot16(gg[i][g], gx[g], gacc[i], IO());
-      }
     }
   }
 #pragma unroll
   for (int u = 0; u < UPW; ++u) {
     const float hs = wave_sum(hacc[u]);
     if (lane == 0) sm.shraw[UPW * wave + u] = hs;
-  }
-  if constexpr (GX) {
-#pragma unroll
-    for (int i = 0; i < GR; ++i) {
-      const int ri = wave + NW * i;
-      if (ri < 2 * HPG) {
-        const float zs = wave_sum(gacc[i]);
-        if (lane == 0) {
-          const IO* bias = ri < HPG ? ba : bb;
-          const int j = ri < HPG ? ri : ri - HPG;
-          const float z = zs + (bias ? to_f32<IO>(bias[h0 + j]) : 0.f);
-          const float gv = 1.0f / (1.0f + expf(-z));
-          if (ri < HPG) sm.sal[j] = gv;
-          else sm.sbe[j] = gv;
-        }
-      }
-    }
   }
   for (int jw = wave; jw < HPG; jw += NW) {
     // normalise q and k of head jw (loaded above for the first)
@@ -449,10 +403,8 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_kernel(int H, int HPG, int
     kq = wave_sum(kq);
     if (lane == 0) {
       sm.skq[jw] = kq;
-      if constexpr (!GX) {
-        sm.sal[jw] = alpha_t[bh0 + jw];
-        sm.sbe[jw] = beta_t[bh0 + jw];
-      }
+      sm.sal[jw] = alpha_t[bh0 + jw];
+      sm.sbe[jw] = beta_t[bh0 + jw];
     }
   }
   for (int e = tid; e < HPG * 4 * 32; e += NT) sm.sw2[e / 32][e % 32] = to_f32<IO>(W2[(int64_t)h0 * 4 * 32 + e]);
@@ -644,30 +596,17 @@ template <int DK, int DV, typename IO>
 static hipError_t run_decode_seq(int out, int B, int H, int D, const float* S_in, float* S_out, const void* cache_in,
                                  void* cache_out, const void* x_t, const void* q_t, const void* k_t, const void* v_t,
                                  const float* alpha_t, const float* beta_t, const void* W1, const void* b1,
-                                 const void* W2, const void* b2, const void* Wa, const void* ba, const void* Wb,
-                                 const void* bb, void* o_t, hipStream_t stream) {
+                                 const void* W2, const void* b2, void* o_t, hipStream_t stream) {
   constexpr int NW = SEQ_NW;
   const int hpg = decode_seq_heads_per_group(B, H, NW);
   const dim3 grid(H / hpg, B);
 #define JB_SEQ_ARGS(OUT_)                                                                                       \
   H, hpg, D, S_in, S_out, (const IO*)cache_in, (IO*)cache_out, (const IO*)x_t, (const IO*)q_t, (const IO*)k_t, \
-      (const IO*)v_t, alpha_t, beta_t, (const IO*)W1, (const IO*)b1, (const IO*)W2, (const IO*)b2, (const IO*)Wa, \
-      (const IO*)ba, (const IO*)Wb, (const IO*)bb, (OUT_*)o_t
-  if (!alpha_t) {
-    // gates from x (bf16 inputs only)
-    if constexpr (sizeof(IO) == 2) {
-      if (out == IO_F32)
-        decode_seq_kernel<DK, DV, IO, float, NW, true><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
-      else
-        decode_seq_kernel<DK, DV, IO, bf16_t, NW, true><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
-      return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
-  }
+      (const IO*)v_t, alpha_t, beta_t, (const IO*)W1, (const IO*)b1, (const IO*)W2, (const IO*)b2, (OUT_*)o_t
   if (out == IO_F32)
-    decode_seq_kernel<DK, DV, IO, float, NW, false><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
+    decode_seq_kernel<DK, DV, IO, float, NW><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(float));
   else
-    decode_seq_kernel<DK, DV, IO, bf16_t, NW, false><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
+    decode_seq_kernel<DK, DV, IO, bf16_t, NW><<<grid, NW * 64, 0, stream>>>(JB_SEQ_ARGS(bf16_t));
 #undef JB_SEQ_ARGS
   return hipGetLastError();
 }
@@ -759,16 +698,16 @@ hipError_t launch_decode_static(int io, int out, int B, int H, int dk, int dv, c
 hipError_t launch_decode_step(int io, int out, int B, int H, int dk, int dv, int D, const float* S_in, float* S_out,
                               const void* cache_in, void* cache_out, const void* x_t, const void* q_t,
                               const void* k_t, const void* v_t, const float* alpha_t, const float* beta_t,
-                              const void* W1, const void* b1, const void* W2, const void* b2, const void* Wa,
-                              const void* ba, const void* Wb, const void* bb, void* o_t, hipStream_t stream) {
+                              const void* W1, const void* b1, const void* W2, const void* b2, void* o_t,
+                              hipStream_t stream) {
   if (B == 0) return hipSuccess;
 #define CASE(DK_, DV_)                                                                                         \
   if (dk == DK_ && dv == DV_) {                                                                                \
     if (io == IO_BF16)                                                                                         \
       return run_decode_seq<DK_, DV_, bf16_t>(out, B, H, D, S_in, S_out, cache_in, cache_out, x_t, q_t, k_t, v_t, \
-                                              alpha_t, beta_t, W1, b1, W2, b2, Wa, ba, Wb, bb, o_t, stream);   \
+                                              alpha_t, beta_t, W1, b1, W2, b2, o_t, stream);                   \
     return run_decode_seq<DK_, DV_, float>(out, B, H, D, S_in, S_out, cache_in, cache_out, x_t, q_t, k_t, v_t,    \
-                                           alpha_t, beta_t, W1, b1, W2, b2, Wa, ba, Wb, bb, o_t, stream);      \
+                                           alpha_t, beta_t, W1, b1, W2, b2, o_t, stream);                      \
   }
   JB_DECODE_CASES(CASE)
 #undef CASE

@@ -328,12 +328,11 @@ def project(x, Wq, Wk, Wv, Wa, Wb, W1, W2, ba=None, bb=None, b1=None, b2=None, *
     alpha = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     beta = torch.empty_like(alpha)
     taps = torch.empty((B, T, H, 4), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = workspace(project_workspace_size(shape), dev)
+    # the projection kernel takes no workspace (jb_project_workspace_size is 0)
     _check(_lib.jb_project(ctypes.byref(shape), _ptr(x), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wa), _ptr(ba),
                            _ptr(Wb), _ptr(bb), _ptr(W1), _ptr(b1), _ptr(W2),
                            _ptr(b2), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(taps), _ptr(ws),
-                           ws.numel(), _stream(stream)))
+                           0 if ws is None else ws.numel(), _stream(stream)))
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, taps=taps)
 
 

@@ -244,14 +244,18 @@ jb_status jb_prefill_varlen(const jb_shape* shape, int64_t total_tokens,
  * nullable (NULL means zero).  All pointers 16-byte aligned.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes of jb_project for `shape` (B*T tokens). */
+/* Workspace bytes of jb_project for `shape` (B*T tokens): always 0, kept so
+ * that callers size every entry point the same way. */
 jb_status jb_project_workspace_size(const jb_shape* shape, size_t* bytes);
 
 /*
  * jb_project -- the projections above for the B*T rows of x [B][T][d_model]:
  * writes q, k [B][T][H][dk] and v [B][T][H][dv] (bf16), alpha, beta
- * [B][T][H] and taps [B][T][H][4] (fp32).  The three large products run as
- * library GEMMs (bf16 operands, fp32 accumulation); W1, Wa, Wb form one more.
+ * [B][T][H] and taps [B][T][H][4] (fp32).  One kernel reads x once per
+ * token tile and forms every output on bf16 matrix cores with fp32
+ * accumulation (q, k, v rounded once; SiLU, the generator's second layer and
+ * the sigmoids in fp32).  workspace and workspace_bytes are not used (may be
+ * NULL and 0).
  */
 jb_status jb_project(const jb_shape* shape, const void* x, const void* Wq, const void* Wk,
                      const void* Wv, const void* Wa, const void* ba, const void* Wb, const void* bb,
@@ -278,9 +282,10 @@ jb_status jb_decode_step_from_x_workspace_size(const jb_shape* shape, size_t* by
 
 /*
  * jb_decode_step_from_x -- one decode step for B sequences from the layer
- * input x_t [B][d_model]: jb_project on the B tokens (q, k, v and the gates
- * into the workspace) and then jb_decode_step.  S_in, S_out, cache_in,
- * cache_out, o_t as in jb_decode_step.
+ * input x_t [B][d_model]: the projection kernel forms q, k, v of the B tokens
+ * in the workspace, then the decode step, which forms the taps and the gates
+ * from x_t itself.  S_in, S_out, cache_in, cache_out, o_t as in
+ * jb_decode_step.
  */
 jb_status jb_decode_step_from_x(const jb_shape* shape, const float* S_in, float* S_out,
                                 const void* cache_in, void* cache_out, const void* x_t,

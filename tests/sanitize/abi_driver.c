@@ -107,7 +107,7 @@ static const entry entries[] = {
   {"jb_prefill_noalloc", "RRRRSSROROOORRO", c_prefill_noalloc, 0, 0},
   {"jb_decode_step", "RRRRRRRRSSRORORN", c_decode_step, 1, 0},
   {"jb_prefill_varlen", "SRRRRSSROROOORROW", c_prefill_varlen, 0, 1},
-  {"jb_project", "RRRRRORORORORRRSSRW", c_project, 0, 1},
+  {"jb_project", "RRRRRORORORORRRSSRN", c_project, 0, 0},
   {"jb_prefill_from_x", "RRRRRORORORO" "OORROW", c_prefill_from_x, 0, 1},
   {"jb_decode_step_from_x", "RRRRRRRRRORORORORW", c_decode_step_from_x, 1, 1},
   {"jb_prefill_static", K_STATIC, c_prefill_static, 0, 1},

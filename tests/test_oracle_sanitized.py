@@ -67,7 +67,7 @@ def test_host_validation_under_asan_ubsan():
         _run(["/opt/rocm/llvm/bin/clang", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", *SAN,
               "-fno-sanitize-recover=all", "-c", os.path.join(ROOT, "tests", "sanitize", "abi_driver.c"), "-o", drv])
         exe = os.path.join(d, "abi_driver")
-        _run([*common, "-o", exe, drv, *objs, "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"])
+        _run([*common, "-o", exe, drv, *objs, "-Wl,-rpath,/opt/rocm/lib"])
         r = _run([exe], env=_env(), timeout=300)
         _clean(r)
         if r.stdout.startswith("skipped"):
