@@ -98,11 +98,14 @@ __device__ __forceinline__ void dma16(v4i_t desc, int voff, int soff, uint32_t l
 }
 
 // slot of 16-byte piece p in LDS row r: p ^ swz(r), with swz a function of
-// r mod 16 chosen so that 16 consecutive rows read at one piece cover all
-// banks in every 8- and 16-lane phase
+// r mod 16 (the same for every 16-row block a lane reads).  Chosen by
+// measurement (SQ_LDS_BANK_CONFLICT on the fragment reads: 16 rows, one
+// piece per lane group): r mod 8 for 128-byte rows and (r/2 ^ r/4) mod 4 for
+// 64-byte rows leave about 1% of LDS cycles in conflicts, where
+// (r mod 8) ^ (r/8 mod 2) leaves 49% and no permutation 74%.
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+  if constexpr (BK == 64) return r & 7;
   else return ((r >> 1) ^ (r >> 2)) & 3;
 }
 
