@@ -76,6 +76,28 @@ def test_project_vs_oracle(jb, oracle_mod, gen_bias, B, T, H, dk, dv, D):
     assert rel_err(r["taps"], taps) < 1e-5
 
 
+@pytest.mark.parametrize("B,T,H,dk,dv,D", [(1, 4133, 3, 64, 128, 256), (1, 4133, 16, 128, 256, 2048)])
+def test_project_large_tiles_vs_oracle(jb, oracle_mod, B, T, H, dk, dv, D):
+    """The 256 x 256 tile configuration (4096 tokens and more): a token tail of 37 rows, feature
+    tiles that straddle q / k / v (H dk = 192), and the 4B widths (d_model 2048, 8192 q/k/v
+    features); the generator tile with its biases."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"project (large tiles) B={B} T={T} H={H} dk={dk} dv={dv} D={D}", flush=True)
+    s = inputs.Shape(B=B, T=T, H=H, dk=dk, dv=dv, d_model=D)
+    p = inputs.projection_inputs(s, seed=T + D + H)
+    g = torch.Generator().manual_seed(H)
+    p["b1"] = (torch.randn(32, generator=g) * 0.3).to(torch.bfloat16)
+    p["b2"] = (torch.randn(4 * H, generator=g) * 0.3).to(torch.bfloat16)
+    d = {k: v.cuda() for k, v in p.items()}
+    r = jb.project(**d)
+    torch.cuda.synchronize()
+    a = _oracle_args(p)
+    ref = oracle_mod.project(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wa"], a["Wb"], ba=a["ba"], bb=a["bb"])
+    _check_projections(r, ref, p, f"T={T}")
+    taps = oracle_mod.gen_taps(a["x"], a["W1"], a["W2"], b1=to_np(p["b1"]), b2=to_np(p["b2"]), H=H)
+    assert rel_err(r["taps"], taps) < 1e-5
+
+
 @pytest.mark.parametrize("B,T,H,dk,dv,D,seg", [(2, 70, 3, 64, 128, 256, None), (1, 200, 2, 96, 256, 512, 1),
                                                (1, 4096, 12, 96, 256, 1536, None)])
 def test_prefill_from_x_vs_oracle(jb, oracle_mod, B, T, H, dk, dv, D, seg):
