@@ -835,7 +835,7 @@ __device__ __forceinline__ void split_mma(f4_t& acc, const float* av, const floa
 // per-sequence stride of the segment buffers; a packed batch's shorter
 // sequences use fewer).  Wave w forms row tile w of each M from the whole
 // previous M, which the waves share through LDS; each wave's D_s and Phi_s
-// rows for the next segment load while it multiplies.
+// rows of the next two segments load while it multiplies.
 template <int DK, int DV, typename OP>
 __global__ __launch_bounds__(DK / 16 * WAVE) void scan_kernel(int H, int nseg, const int* cu_seqlens, int Tmax,
                                                               int64_t total, int seg_len, const float* S0, const float* Dsum,
@@ -867,24 +867,23 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void scan_kernel(int H, int nseg, c
     }
   };
   const int last = nseg_b - 1;  // M_last is stored, not advanced
-  float dn[4], pn[KB][8];
-  if (last > 0) load_step(0, dn, pn);
-  for (int s = 0;; ++s) {
+  // the maps of the next two segments are in flight while one multiplies: three
+  // register buffers in rotation, the loop unrolled by three so that no buffer
+  // is copied (a copy would wait for its loads)
+  float d0[4], p0[KB][8], d1[4], p1[KB][8], d2[4], p2[KB][8];
+  if (last > 0) load_step(0, d0, p0);
+  if (last > 1) load_step(1, d1, p1);
+  // step s from the buffer (dc, pc), then the segment s + 2 into (dl, pl);
+  // returns false once M_last is stored
+  auto step = [&](int s, const float (&dc)[4], const float (&pc)[KB][8], float (&dl)[4], float (&pl)[KB][8]) {
     float* dst = Mstart + (bh * nseg + s) * DK * DV;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dst[(rt * 16 + 4 * g4 + i) * DV + col] = M[i];
       sM[(rt * 16 + 4 * g4 + i) * LM + m16] = M[i];
     }
-    if (s == last) break;
-    float dc[4], pc[KB][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dc[i] = dn[i];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pc[kb][j] = pn[kb][j];
-    if (s + 1 < last) load_step(s + 1, dn, pn);
+    if (s == last) return false;
+    if (s + 2 < last) load_step(s + 2, dl, pl);
     __syncthreads();  // every row tile of M_s is in LDS
     // B fragments: rows kb*32 + kperm(g, j) of M_s, this lane's column
     f4_t acc;
@@ -899,6 +898,12 @@ __global__ __launch_bounds__(DK / 16 * WAVE) void scan_kernel(int H, int nseg, c
     }
     M = acc;
     __syncthreads();  // every wave has read M_s before it is overwritten
+    return true;
+  };
+  for (int s = 0;; s += 3) {
+    if (!step(s, d0, p0, d2, p2)) break;
+    if (!step(s + 1, d1, p1, d0, p0)) break;
+    if (!step(s + 2, d2, p2, d1, p1)) break;
   }
 }
 
