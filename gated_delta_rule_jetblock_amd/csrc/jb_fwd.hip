@@ -199,7 +199,14 @@ struct Geo {
   static constexpr int TPW = (NCT + NW - 1) / NW;              // tiles per wave: wave w owns w, w + 8, ..
   static constexpr int GW = NW - 1;                            // gate wave
   static constexpr int IW = NW - 2;                            // inverse wave
-  static constexpr int LDK = DK + 8, LC = C + 8, LTT = C + 16, LAD = 20, LLI = 36, LT = 40, LV = DV + 16;
+  static constexpr int LDK = DK + 8, LC = C + 8, LTT = C + 16, LAD = 20, LLI = 36, LT = 40;
+  // value rows in groups of VRPG rows (1 KB, one full-wave DMA), 32 bytes of
+  // padding after each group; row r at vrow(r).  Within row j of a group the
+  // 16-column tiles are XOR-permuted by vsw(j) (< NW), so that the 8 rows one
+  // half-wave reads down a column tile fall in distinct 32-byte bank slots.
+  static constexpr int VRPG = 1024 / (DV * 2), VG = 1024 + 32, NVG = (C + 3 + VRPG - 1) / VRPG;
+  static constexpr int vrow(int r) { return (r / VRPG) * VG + (r % VRPG) * DV * 2; }
+  static constexpr int vsw(int j) { return DV == 256 ? 4 * j : DV == 128 ? 2 * j : j >> 1; }
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
   static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
   static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
@@ -215,10 +222,13 @@ struct Geo {
   static constexpr int SO_END = oSO + (OUTM ? C * DV * 2 : 0);  // over -A .. P, dead once P V_new is done
   static constexpr int WORK0 = a16(oP + (OUTM ? C * LC * 2 : 0));
   static constexpr int WORK = WORK0 > SO_END ? WORK0 : a16(SO_END);
-  static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + (C + 3) * LV * 2;
+  static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + NVG * VG;
   static_assert(WORK + STAGE <= 160 * 1024, "LDS budget of one CU exceeded");
   static_assert(RT <= NW, "one wave per W column tile");
-  static_assert((LDK * 2) % 16 == 0 && (LV * 2) % 16 == 0 && (LC * 2) % 8 == 0 && (LTT * 2) % 8 == 0, "aligned rows");
+  static_assert((LDK * 2) % 16 == 0 && VG % 16 == 0 && (LC * 2) % 8 == 0 && (LTT * 2) % 8 == 0, "aligned rows");
+  static_assert(16 % VRPG == 0 && VRPG * DV * 2 == 1024, "value row groups of 1 KB that tile 16-row windows");
+  static_assert(vsw(VRPG - 1) < NW && vsw(VRPG - 1) < VCT && (NW & (NW - 1)) == 0,
+                "tile swizzle within a row, commuting with the wave stride of column tiles");
 };
 
 // ------------------------------------------------------------ kernel
@@ -231,7 +241,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   // a chunk row in contiguous lanes); f32 outputs straight from the registers
   constexpr bool STAGE_O = OUTM && sizeof(OUT) == 2;
   constexpr int NCT = G::NCT, VCT = G::VCT, RT = G::RT, KB = G::KB, NW = G::NW, TPW = G::TPW;
-  constexpr int LDK = G::LDK, LC = G::LC, LTT = G::LTT, LAD = G::LAD, LLI = G::LLI, LT = G::LT, LV = G::LV;
+  constexpr int LDK = G::LDK, LC = G::LC, LTT = G::LTT, LAD = G::LAD, LLI = G::LLI, LT = G::LT;
+  constexpr int VRPG = G::VRPG, VG = G::VG, NVG = G::NVG;
 
   // working tiles, and the DMA staging areas as arrays of their own (so the
   // compiler can tell that reads of the tiles never wait on the DMA)
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sKr[C * DK];
   __shared__ __attribute__((aligned(16))) bf16_t sQr[OUTM ? C * DK : 8];
   __shared__ __attribute__((aligned(16))) float sGr[C * 6];  // alpha [C], beta [C], taps [C][4]
-  __shared__ __attribute__((aligned(16))) bf16_t sV[(C + 3) * LV];
+  __shared__ __attribute__((aligned(16))) char sV[NVG * VG];
   float* sG = reinterpret_cast<float*>(work + G::oG);
   float* sGam = sG + C;
   float* sBeta = sG + 2 * C;
@@ -287,7 +298,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   // this lane's bases in the tiles
   const lds_char* tKkp = tr_base_kp(lKh, LDK);   // K^ down its columns (K^T, for the state update)
   const lds_char* tTkp = tr_base_kp(lTt, LTT);   // T^T down its columns (T)
-  const lds_char* tVkp = tr_base_kp(lV, LV);     // value rows down their columns
+  // value rows down their columns (the kperm lane rows of tr_base_kp, in the
+  // grouped row layout): windows from a multiple of 16, and the last one from row C + 3 - 32
+  // (tile wave + NW cw of row r sits at tile (wave ^ vsw(r % VRPG)) + NW cw)
+  const int vx = 4 * (lane >> 4) + ((lane >> 2) & 3), va = 8 * (lane & 3);
+  const lds_char* tVa = lV + opaque(G::vrow(vx) + 32 * (wave ^ G::vsw(vx % VRPG)) + va);
+  const lds_char* tVb =
+      lV + opaque(G::vrow(C + 3 - 32 + vx) + 32 * (wave ^ G::vsw((C + 3 - 32 + vx) % VRPG)) + va);
   const _Float16* rKct = row_base_ct(sKh, LDK);  // rows of K^, Q^ (Gram tiles)
   const _Float16* rQct = row_base_ct(sQh, LDK);
   const _Float16* rQkp = row_base_kp(sQh, LDK);  // rows of Q^ (Q^ M)
@@ -341,7 +358,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   // value rows, which are zeroed (the band multiplies them by zero
   // coefficients, and stale values could be non-finite)
   const uint32_t rowq = (uint32_t)(H * DK * 2), rowv = (uint32_t)(H * DV * 2);  // bytes between tokens
-  constexpr int VR = (C + 3 + NW - 1) / NW;  // staged value rows per wave
   // q, k and gate rows of chunk cc, shared by waves 0 .. nw - 1 (wave wv takes
   // the 64-piece rows wv, wv + nw, ..; the last of them also the gates)
   auto issue_qkg = [&](int cc, int wv, int nw) {
@@ -369,28 +385,48 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, lGr + 2 * C * 4);
     }
   };
-  // value rows (with the conv halo) of chunk cc: this wave's rows wave + NW i
-  // for i0 <= i < i1
-  auto issue_v = [&](int cc, int i0, int i1) {
+  // value rows (with the conv halo) of chunk cc, portion part (0, 1, 2) of this
+  // wave's share.  Row r holds token t0c - 3 + r.  Past the sequence's first
+  // chunk all rows come from v: one full-wave DMA per 1 KB group of rows
+  // (groups wave + NW i), rows past the sequence end reading zero through the
+  // buffer range.  In the first chunk the halo rows come from the conv cache
+  // (or are zero): one DMA per row.
+  auto issue_v = [&](int cc, int part) {
     const int t0c = cc * C, nc = min(C, T - t0c);
     constexpr int PPR = DV / 8;  // 16-byte pieces per value row
     // rows from token rb0 (the halo's first row, or the chunk's when it starts the sequence)
     const int rb0 = t0c >= 3 ? t0c - 3 : t0c;
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(v + ((tok0 + rb0) * H + h) * DV, (uint32_t)(t0c + nc - 1 - rb0) * rowv + DV * 2);
+    const int ln = opaque(lane);
+    if (t0c >= 3) {
+      constexpr int GPW = (NVG + NW - 1) / NW;  // groups per wave
+      const int i0 = part * GPW / 3, i1 = (part + 1) * GPW / 3;
+      // lane ln fills slot ln % PPR of row ln / PPR of the group
+      const int j = ln / PPR;
+      const uint32_t lo = (uint32_t)j * rowv + (uint32_t)((ln % PPR) ^ (2 * G::vsw(j))) * 16;
+      for (int i = i0; i < i1; ++i) {
+        const int g = wave + i * NW;
+        if (g < NVG) dma_buf<16>(rv, (uint32_t)(g * VRPG) * rowv + lo, lVw + g * VG);
+      }
+      return;
+    }
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(cin ? cin + ((int64_t)b * 3 * H + h) * DV : v, cin ? 2 * rowv + DV * 2 : 0u);
-    const int l16 = opaque(lane) * 16;
-    for (int r = wave + i0 * NW; r < C + 3 && r < wave + i1 * NW; r += NW) {  // row r holds token t0c - 3 + r
+
+    constexpr int VR = (C + 3 + NW - 1) / NW;  // rows per wave
+    const int i0 = part * VR / 3, i1 = (part + 1) * VR / 3;
+    for (int r = wave + i0 * NW; r < C + 3 && r < wave + i1 * NW; r += NW) {
       const int t = t0c - 3 + r;
-      lds_char* dst = lVw + r * LV * 2;
-      if (l16 < PPR * 16) {
+      lds_char* dst = lVw + G::vrow(r);
+      const uint32_t pc = (uint32_t)(ln ^ (2 * G::vsw(r % VRPG))) * 16;  // piece for slot ln
+      if (ln < PPR) {
         if (t >= 0 && r - 3 < nc)
-          dma_buf<16>(rv, (uint32_t)(t - rb0) * rowv + l16, dst);
+          dma_buf<16>(rv, (uint32_t)(t - rb0) * rowv + pc, dst);
         else if (t < 0 && cin)
-          dma_buf<16>(rc, (uint32_t)(3 + t) * rowv + l16, dst);
+          dma_buf<16>(rc, (uint32_t)(3 + t) * rowv + pc, dst);
         else
-          *(__attribute__((address_space(3))) u4_t*)(dst + l16) = u4_t{0u, 0u, 0u, 0u};
+          *(__attribute__((address_space(3))) u4_t*)(dst + ln * 16) = u4_t{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -468,7 +504,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 
   if (c_begin < c_end) {
     issue_qkg(c_begin, wave, NW);
-    issue_v(c_begin, 0, VR);
+    issue_v(c_begin, 0);
+    issue_v(c_begin, 1);
+    issue_v(c_begin, 2);
     // the first chunk's rows land before the loop, so that at the top of every
     // iteration the transfers still outstanding are those the previous chunk
     // issued, followed by its o stores
@@ -651,10 +689,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       // the value rows taken exactly as bf16 operands (kperm K order on both sides)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int s0 = rt < 3 ? 16 * rt : C + 3 - 32;
         const bf16x8_t th = __builtin_bit_cast(bf16x8_t, row_frag_kp<LT>(rTkp, rt * 16, 0));
         const bf16x8_t tl = __builtin_bit_cast(bf16x8_t, row_frag_kp<LT>(rTkp, (4 + rt) * 16, 0));
-        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, tr_frag_kp<LV>(tVkp, s0, tile(cw) * 16));
+        // window rows 16 rt .. (rt < 3) or C + 3 - 32 .. (the last): two 16-row halves
+        const lds_char* vbase = rt < 3 ? tVa + G::vrow(16 * rt) : tVb;
+        const s4_t vlo = tr4(vbase + cw * NW * 32);
+        const s4_t vhi = tr4(vbase + (16 / VRPG) * VG + cw * NW * 32);
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
         const f4_t hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(th, vb, zero4(), 0, 0, 0);
         U[cw][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tl, vb, hi, 0, 0, 0);
       }
@@ -710,7 +751,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
     bar();
     // the next chunk's value rows, in three portions spread over phases D and E
-    if (c + 1 < c_end) issue_v(c + 1, 0, VR / 3);
+    if (c + 1 < c_end) issue_v(c + 1, 0);
 
     // ================= D: T = (I + A)^{-1} by blocked forward substitution,
     // column block j on wave j (its columns of the identity as right-hand side)
@@ -732,7 +773,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
             h4_t{w0[0], w0[1], w1[0], w1[1]};
       }
     }
-    if (c + 1 < c_end) issue_v(c + 1, VR / 3, 2 * VR / 3);
+    if (c + 1 < c_end) issue_v(c + 1, 1);
     bar();
 
     // ================= E: state-dependent part of the chunk =================
@@ -758,7 +799,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (c + 1 < c_end) issue_v(c + 1, 2 * VR / 3, VR);
+    if (c + 1 < c_end) issue_v(c + 1, 2);
     if constexpr (OUTM) {
       // O += P V_new, then the outputs
 #pragma unroll
