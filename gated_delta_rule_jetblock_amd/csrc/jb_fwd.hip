@@ -12,24 +12,25 @@
 // HBM traffic is the compulsory inputs (read twice for all but the last
 // segment) and o.
 //
-// Workgroup: one per (segment, head, sequence); each wave owns two 16-column
-// tiles of the state (value columns, or transition columns in the summary),
-// held in fp32 accumulators at a per-tile power-of-two scale (jb_chunk.h).
-// Per chunk of C = 64 tokens, five barriers:
-//   A  normalise the staged q, k rows into K^, Q^ (fp16); the gate wave scans
-//      the gates and writes the conv band;
+// Workgroup: one per (segment, head, sequence); wave w owns the 16-column
+// tiles w, w + 8, .. of the state (value columns, and in the summary the
+// transition columns after them), held in fp32 accumulators at a per-tile
+// power-of-two scale (jb_chunk.h).  Per chunk of C = 64 tokens:
+//   A  normalise the staged q, k rows into K^, Q^ (fp16);
 //   B  Gram tiles K^K^T and Q^K^T -> -A, its fp32 diagonal blocks, P (written
-//      as whole rows: each product is formed transposed); every value-tile
-//      wave forms its right-hand side diag(b) V' = Band V_ext on the bf16
-//      matrix cores and picks its tiles' exponents;
-//   C  one wave inverts the four 16x16 diagonal blocks of I + A while the
-//      others form Q^ M (output pass);
-//   D  blocked forward substitution on the matrix cores: -W^T (six waves, one
-//      dk column tile each) and U0 for every value tile;
-//   E  V_new = U0 - W M, O = diag(gamma) Q^ M + P V_new (stored), and
-//      M <- gamma_C M + K^T diag(e^{g_C - g}) V_new.
-// The next chunk's q, k and gate rows move into LDS by DMA from phase B on and
-// its value rows from phase C on, so their HBM latency overlaps the chunk.
+//      as whole rows: each product is formed transposed); waves 4..7 invert
+//      the four 16x16 diagonal blocks of I + A; every wave forms its
+//      right-hand sides diag(b) V' = Band V_ext on the bf16 matrix cores,
+//      picks its tiles' exponents and subtracts diag(b gamma) K^ M (output
+//      pass: also Q^ M);
+//   D  T = (I + A)^{-1} by blocked forward substitution on the matrix cores
+//      (waves 0..3, a column block each); the gate wave scans the next
+//      chunk's gates and writes its conv band;
+//   E  V_new = T R, O = diag(gamma) Q^ M + P V_new (staged in LDS, stored at
+//      the start of the next chunk), and M <- gamma_C M + K^T diag(e^{g_C - g}) V_new.
+// The next chunk's q and k rows move into LDS by DMA from phase B on, its
+// value rows from phase D on, and the gate rows two chunks ahead, so their
+// HBM latency overlaps the chunk.
 //
 // Operands read down a column of a row-major tile (K^ as K^T, -W^T as W, the
 // value rows) come from ds_read_b64_tr_b16: within each group of 16 lanes,
@@ -208,8 +209,8 @@ struct Geo {
   static constexpr int vrow(int r) { return (r / VRPG) * VG + (r % VRPG) * DV * 2; }
   static constexpr int vsw(int j) { return DV == 256 ? 4 * j : DV == 128 ? 2 * j : j >> 1; }
   static constexpr int a16(int x) { return (x + 15) / 16 * 16; }
-  static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [4][C] f32
-  static constexpr int oT = oG + 4 * C * 4;                     // band: [hi, lo][4][16][LT] bf16
+  static constexpr int oG = 0;                                  // g, gamma, beta, e^{g_C - g}: [2][4][C] f32
+  static constexpr int oT = oG + 2 * 4 * C * 4;                 // band: [hi, lo][4][16][LT] bf16
   static constexpr int oKh = a16(oT + 2 * 4 * 16 * LT * 2);     // [C][LDK] K^
   static constexpr int szQh = OUTM ? C * LDK * 2 : 0;
   static constexpr int szT = C * LTT * 2;
@@ -222,7 +223,7 @@ struct Geo {
   static constexpr int SO_END = oSO + (OUTM ? C * DV * 2 : 0);  // over -A .. P, dead once P V_new is done
   static constexpr int WORK0 = a16(oP + (OUTM ? C * LC * 2 : 0));
   static constexpr int WORK = WORK0 > SO_END ? WORK0 : a16(SO_END);
-  static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + C * 6 * 4 + NVG * VG;
+  static constexpr int STAGE = (OUTM ? 2 : 1) * C * DK * 2 + 2 * C * 6 * 4 + NVG * VG;
   static_assert(WORK + STAGE <= 160 * 1024, "LDS budget of one CU exceeded");
   static_assert(RT <= NW, "one wave per W column tile");
   static_assert((LDK * 2) % 16 == 0 && VG % 16 == 0 && (LC * 2) % 8 == 0 && (LTT * 2) % 8 == 0, "aligned rows");
@@ -249,12 +250,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char work[G::WORK];
   __shared__ __attribute__((aligned(16))) bf16_t sKr[C * DK];
   __shared__ __attribute__((aligned(16))) bf16_t sQr[OUTM ? C * DK : 8];
-  __shared__ __attribute__((aligned(16))) float sGr[C * 6];  // alpha [C], beta [C], taps [C][4]
+  __shared__ __attribute__((aligned(16))) float sGr[2 * C * 6];  // [chunk & 1]: alpha [C], beta [C], taps [C][4]
   __shared__ __attribute__((aligned(16))) char sV[NVG * VG];
-  float* sG = reinterpret_cast<float*>(work + G::oG);
-  float* sGam = sG + C;
-  float* sBeta = sG + 2 * C;
-  float* sDec = sG + 3 * C;
+  float* sG2 = reinterpret_cast<float*>(work + G::oG);  // [chunk & 1]: g, gamma, beta, e^{g_C - g}
   bf16_t* sT = reinterpret_cast<bf16_t*>(work + G::oT);
   _Float16* sKh = reinterpret_cast<_Float16*>(work + G::oKh);
   _Float16* sQh = reinterpret_cast<_Float16*>(work + G::oQW);
@@ -376,22 +374,63 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         if (OUTM) dma_buf<16>(rq, off, lQr + j * 1024);
       }
     }
-    if (wv == nw - 1 && ln < nc) {
+  };
+  // the gate rows of chunk cc (one wave), into raw gate buffer cc & 1
+  auto issue_g = [&](int cc) {
+    const int t0c = cc * C, nc = min(C, T - t0c);
+    const int ln = opaque(lane);
+    lds_char* dst = lGr + (cc & 1) * (C * 6 * 4);
+    if (ln < nc) {
       const int64_t gidx = (tok0 + t0c) * H + h;
       const uint32_t gb = (uint32_t)(nc - 1) * H * 4 + 4;
       const uint32_t off = (uint32_t)(ln * H) * 4;
-      dma_buf<4>(make_rsrc(a.alpha + gidx, gb), off, lGr);
-      dma_buf<4>(make_rsrc(a.beta + gidx, gb), off, lGr + C * 4);
-      dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, lGr + 2 * C * 4);
+      dma_buf<4>(make_rsrc(a.alpha + gidx, gb), off, dst);
+      dma_buf<4>(make_rsrc(a.beta + gidx, gb), off, dst + C * 4);
+      dma_buf<16>(make_rsrc(a.taps + gidx * 4, gb * 4), off * 4, dst + 2 * C * 4);
     }
   };
-  // value rows (with the conv halo) of chunk cc, portion part (0, 1, 2) of this
-  // wave's share.  Row r holds token t0c - 3 + r.  Past the sequence's first
-  // chunk all rows come from v: one full-wave DMA per 1 KB group of rows
-  // (groups wave + NW i), rows past the sequence end reading zero through the
-  // buffer range.  In the first chunk the halo rows come from the conv cache
-  // (or are zero): one DMA per row.
-  auto issue_v = [&](int cc, int part) {
+  // gates of chunk cc (wave GW, its raw gate rows in LDS): the cumulative log
+  // decay g (base 2), gamma = 2^g, beta and e^{g_C - g} into gate buffer cc & 1,
+  // and the chunk's band coefficients
+  auto gates = [&](int cc) {
+    const int nc = min(C, T - cc * C);
+    const float* gr = sGr + (cc & 1) * (C * 6);
+    float* gg = sG2 + (cc & 1) * (4 * C);
+    const bool valid = lane < nc;
+    const float al = valid ? gr[lane] : 1.f;
+    const float be = valid ? gr[C + lane] : 0.f;
+    const float4 tp = valid ? reinterpret_cast<const float4*>(gr + 2 * C)[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float g = chunk_gate_scan(al);
+    const float gC = __shfl(g, C - 1, WAVE);
+    gg[lane] = g;
+    gg[C + lane] = fast_exp2(g);
+    gg[2 * C + lane] = be;
+    gg[3 * C + lane] = fast_exp2(gC - g);
+    // row `lane` of the band with Band[r][r + j] = b_r tap_r[j], so that
+    // diag(b) V' = Band V_ext runs on the matrix cores: row tile rt takes the
+    // 32 staged value rows from 16 rt (from C + 3 - 32 for the last tile),
+    // each coefficient split into bf16 hi + lo
+    const int rt = lane >> 4, m = lane & 15, k0 = (rt < 3 ? 0 : 16 * rt - (C + 3 - 32)) + m;
+    const float cf[4] = {be * tp.x, be * tp.y, be * tp.z, be * tp.w};
+    // (one opaque offset: the address stays a short chain from the LDS array,
+    // so the compiler can tell these stores from the DMA's)
+    const int to = opaque((rt * 16 + m) * LT + k0);
+    bf16_t* th = sT + to;
+    bf16_t* tl = sT + (to + 4 * 16 * LT);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16_t hi = f32_to_bf16(cf[j]);
+      th[j] = hi;
+      tl[j] = f32_to_bf16(cf[j] - bf16_to_f32(hi));
+    }
+  };
+  // value rows (with the conv halo) of chunk cc, shared by waves w0 .. w0 + nw - 1.
+  // Row r holds token t0c - 3 + r.  Past the sequence's first chunk all rows
+  // come from v: one full-wave DMA per 1 KB group of rows (wave w takes groups
+  // w - w0, w - w0 + nw, ..), rows past the sequence end reading zero through
+  // the buffer range.  In the first chunk the halo rows come from
+  // the conv cache (or are zero): one DMA per row.
+  auto issue_v = [&](int cc, int w0, int nw) {
     const int t0c = cc * C, nc = min(C, T - t0c);
     constexpr int PPR = DV / 8;  // 16-byte pieces per value row
     // rows from token rb0 (the halo's first row, or the chunk's when it starts the sequence)
@@ -400,23 +439,17 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         make_rsrc(v + ((tok0 + rb0) * H + h) * DV, (uint32_t)(t0c + nc - 1 - rb0) * rowv + DV * 2);
     const int ln = opaque(lane);
     if (t0c >= 3) {
-      constexpr int GPW = (NVG + NW - 1) / NW;  // groups per wave
-      const int i0 = part * GPW / 3, i1 = (part + 1) * GPW / 3;
       // lane ln fills slot ln % PPR of row ln / PPR of the group
       const int j = ln / PPR;
       const uint32_t lo = (uint32_t)j * rowv + (uint32_t)((ln % PPR) ^ (2 * G::vsw(j))) * 16;
-      for (int i = i0; i < i1; ++i) {
-        const int g = wave + i * NW;
-        if (g < NVG) dma_buf<16>(rv, (uint32_t)(g * VRPG) * rowv + lo, lVw + g * VG);
-      }
+      for (int g = wave - w0; g < NVG; g += nw)
+        dma_buf<16>(rv, (uint32_t)(g * VRPG) * rowv + lo, lVw + g * VG);
       return;
     }
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(cin ? cin + ((int64_t)b * 3 * H + h) * DV : v, cin ? 2 * rowv + DV * 2 : 0u);
 
-    constexpr int VR = (C + 3 + NW - 1) / NW;  // rows per wave
-    const int i0 = part * VR / 3, i1 = (part + 1) * VR / 3;
-    for (int r = wave + i0 * NW; r < C + 3 && r < wave + i1 * NW; r += NW) {
+    for (int r = wave - w0; r < C + 3; r += nw) {
       const int t = t0c - 3 + r;
       lds_char* dst = lVw + G::vrow(r);
       const uint32_t pc = (uint32_t)(ln ^ (2 * G::vsw(r % VRPG))) * 16;  // piece for slot ln
@@ -504,17 +537,26 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 
   if (c_begin < c_end) {
     issue_qkg(c_begin, wave, NW);
-    issue_v(c_begin, 0);
-    issue_v(c_begin, 1);
-    issue_v(c_begin, 2);
+    issue_v(c_begin, 0, NW);
+    // the gate rows run two chunks ahead (those of chunk c + 2 move during
+    // chunk c; chunk c + 1's gates are formed in chunk c's phase D)
+    if (wave == G::GW) {
+      issue_g(c_begin);
+      if (c_begin + 1 < c_end) issue_g(c_begin + 1);
+    }
     // the first chunk's rows land before the loop, so that at the top of every
     // iteration the transfers still outstanding are those the previous chunk
     // issued, followed by its o stores
     __builtin_amdgcn_s_waitcnt(0);
+    if (wave == G::GW) gates(c_begin);
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
+    const float* sG = sG2 + (c & 1) * (4 * C);
+    const float* sGam = sG + C;
+    const float* sBeta = sG + 2 * C;
+    const float* sDec = sG + 3 * C;
     // this wave's DMA transfers into the staging areas are done, then every
     // other wave's.  (The wait covers the previous chunk's o stores as well:
     // loads and stores share the vector memory counter and need not complete
@@ -558,35 +600,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
           const h2_t x1 = __builtin_convertvector(f2_t{qv[e + 2] * rq, qv[e + 3] * rq}, h2_t);
           *reinterpret_cast<h4_t*>(sQh + row * LDK + part * E + e) = h4_t{x0[0], x0[1], x1[0], x1[1]};
         }
-      }
-    }
-    if (wave == G::GW) {
-      const bool valid = lane < n;
-      const float al = valid ? sGr[lane] : 1.f;
-      const float be = valid ? sGr[C + lane] : 0.f;
-      const float4 tp = valid ? reinterpret_cast<const float4*>(sGr + 2 * C)[lane] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float g = chunk_gate_scan(al);
-      const float gC = __shfl(g, C - 1, WAVE);
-      sG[lane] = g;
-      sGam[lane] = fast_exp2(g);
-      sBeta[lane] = be;
-      sDec[lane] = fast_exp2(gC - g);
-      // row `lane` of the band with Band[r][r + j] = b_r tap_r[j], so that
-      // diag(b) V' = Band V_ext runs on the matrix cores: row tile rt takes the
-      // 32 staged value rows from 16 rt (from C + 3 - 32 for the last tile),
-      // each coefficient split into bf16 hi + lo
-      const int rt = lane >> 4, m = lane & 15, k0 = (rt < 3 ? 0 : 16 * rt - (C + 3 - 32)) + m;
-      const float cf[4] = {be * tp.x, be * tp.y, be * tp.z, be * tp.w};
-      // (one opaque offset: the address stays a short chain from the LDS array,
-      // so the compiler can tell these stores from the DMA's)
-      const int to = opaque((rt * 16 + m) * LT + k0);
-      bf16_t* th = sT + to;
-      bf16_t* tl = sT + (to + 4 * 16 * LT);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16_t hi = f32_to_bf16(cf[j]);
-        th[j] = hi;
-        tl[j] = f32_to_bf16(cf[j] - bf16_to_f32(hi));
       }
     }
     bar();
@@ -666,6 +679,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       // these waves are done with the Gram work first: they move the next
       // chunk's q, k and gate rows (the staging areas were last read in phase A)
       if (c + 1 < c_end) issue_qkg(c + 1, wave, 4);
+      if (wave == 3 && c + 2 < c_end) issue_g(c + 2);
       if constexpr (STAGE_O) {
         // the two zero blocks above P's block diagonal that P V_new reads,
         // rows 0..15 x columns 16..31 and rows 32..47 x columns 48..63 (the
@@ -750,8 +764,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
     }
     bar();
-    // the next chunk's value rows, in three portions spread over phases D and E
-    if (c + 1 < c_end) issue_v(c + 1, 0);
+    // the next chunk's value rows (every wave is past its band product), moved
+    // by the waves that wait out the solve (the DMA issue stalls a wave while
+    // the CU's load path is busy)
+    if (c + 1 < c_end && wave >= 4 && wave < G::GW) issue_v(c + 1, 4, G::GW - 4);
 
     // ================= D: T = (I + A)^{-1} by blocked forward substitution,
     // column block j on wave j (its columns of the identity as right-hand side)
@@ -772,8 +788,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         *reinterpret_cast<h4_t*>(sTt + opaque((j * 16 + m16) * LTT + rb * 16 + 4 * g4)) =
             h4_t{w0[0], w0[1], w1[0], w1[1]};
       }
+    } else if (wave == G::GW && c + 1 < c_end) {
+      // the next chunk's gates (its raw rows landed by this chunk's top wait;
+      // the band was last read in phase B, the gate buffer in the previous chunk)
+      gates(c + 1);
     }
-    if (c + 1 < c_end) issue_v(c + 1, 1);
     bar();
 
     // ================= E: state-dependent part of the chunk =================
@@ -799,7 +818,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    if (c + 1 < c_end) issue_v(c + 1, 2);
     if constexpr (OUTM) {
       // O += P V_new, then the outputs
 #pragma unroll
