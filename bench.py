@@ -521,6 +521,7 @@ def main():
     pre_gbs = prefill_bytes_per_token(sp, out_bytes) * tok_pre / (pre_ms * 1e-3) / 1e9
     pre_traffic = (measured_traffic("prefill_jetblock2b_T65536.md",
                                     ["gated_delta_rule_jetblock_amd/csrc/jb_fwd.hip",
+                                     "gated_delta_rule_jetblock_amd/csrc/jb_frag.h",
                                      "gated_delta_rule_jetblock_amd/csrc/jb_chunk.h",
                                      "gated_delta_rule_jetblock_amd/csrc/jb_device.h",
                                      "gated_delta_rule_jetblock_amd/csrc/jb_gen.hip",

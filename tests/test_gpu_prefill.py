@@ -59,6 +59,26 @@ def test_ragged_lengths_with_state(jb, oracle_mod, io, T):
     np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
 
 
+@pytest.mark.parametrize("dk", [96, 128])
+@pytest.mark.parametrize("T", [1, 3, 31, 32, 33, 95, 200])
+def test_ragged_lengths_2b_4b_heads(jb, oracle_mod, dk, T):
+    """Ragged lengths at the 2B / 4B head shapes: partial chunks, the conv halo from
+    the cache in the first chunk, a carried state."""
+    from gated_delta_rule_jetblock_amd import inputs
+    print(f"ragged dk={dk} T={T}", flush=True)
+    s = inputs.Shape(B=2, T=T, H=2, dk=dk, dv=256, d_model=128)
+    p = inputs.prefill_inputs(s, seed=100 + T)
+    st = inputs.state_inputs(s, seed=100 + T)
+    ref = oracle_prefill(oracle_mod, p, st["S"], st["cache"])
+    r = _run(jb, p, st["S"], st["cache"])
+    _check(r, ref, TOL_BF16, f"T={T}")
+    np.testing.assert_array_equal(to_np(r["conv_out"]), ref["conv_out"])
+    # bf16 o (staged through LDS) is the fp32 o rounded to nearest even
+    rb = _run(jb, p, st["S"], st["cache"], out_dtype=torch.bfloat16)
+    assert torch.equal(rb["o"].cpu(), r["o"].to(torch.bfloat16).cpu())
+    assert torch.equal(rb["S_final"].cpu(), r["S_final"].cpu())
+
+
 @pytest.mark.parametrize("seg", [None, 2, 64])
 @pytest.mark.parametrize("dk,dv", [(32, 64), (64, 128), (96, 256), (128, 256), (128, 64), (96, 128)])
 def test_head_shapes_bf16(jb, oracle_mod, dk, dv, seg):
