@@ -87,10 +87,11 @@ def projection_flops_per_token(s) -> float:
     return 2.0 * s.d_model * (2 * s.H * s.dk + s.H * s.dv + 32 + 2 * s.H)
 
 
-def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
+def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 5, dec_reps: int = 30):
     """The block from its layer input x (outside the timed step): jb_project alone and
-    jb_prefill_from_x at the prefill shape, jb_decode_step_from_x at the decode shape, each
-    averaged over `reps` calls bracketed by HIP events on the launching stream."""
+    jb_prefill_from_x at the prefill shape (`reps` calls each), jb_decode_step_from_x at the
+    decode shape (`dec_reps` calls), each after 3 warm-up calls and bracketed by HIP events on
+    the launching stream."""
     dev = torch.device("cuda:0")
     p = inputs.projection_inputs(sp, seed=2, device=dev)
     stream = torch.cuda.current_stream()
@@ -101,17 +102,18 @@ def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
     o = torch.empty((sp.B, sp.T, sp.H, sp.dv), dtype=out_dt, device=dev)
     S = torch.empty((sp.B, sp.H, sp.dk, sp.dv), dtype=torch.float32, device=dev)
 
-    def timed(fn):
-        fn()
+    def timed(fn, n=reps):
+        for _ in range(3):
+            fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / n
 
     ms_proj = timed(lambda: jb.project(**p, ws=ws_p, stream=stream))
     # one decode step from x_t at the decode shape (projections over the batch + the step)
@@ -124,7 +126,7 @@ def measure_from_x(jb, inputs, torch, sp, out_dt, reps: int = 3):
     dshape = jb.make_shape(sd.B, 1, sd.H, sd.dk, sd.dv, sd.d_model)
     ws_d = jb.workspace(jb.decode_step_from_x_workspace_size(dshape), dev)
     us_dec = 1e3 * timed(lambda: jb.decode_step_from_x(st["S"], st["cache"], xt, **Wd, out_dtype=out_dt, o=od,
-                                                       ws=ws_d, stream=stream))
+                                                       ws=ws_d, stream=stream), dec_reps)
     ms_x = timed(lambda: jb.prefill_from_x(**p, out_dtype=out_dt, o=o, S_final=S, want_conv_out=False, ws=ws_x,
                                            stream=stream))
     tok = sp.B * sp.T
@@ -153,17 +155,18 @@ def measure_static(jb, inputs, torch, sp, sd, p, d, out_dt, reps: int = 3):
     need = jb.prefill_static_workspace_size(pshape)
     ws = jb.workspace(need, dev) if need else None
 
-    def timed(fn):
-        fn()
+    def timed(fn, n=reps):
+        for _ in range(3):
+            fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / n
 
     ms_pre = timed(lambda: jb.prefill_static(p["q"], p["k"], p["v"], p["alpha"], p["beta"], w["wq"], w["wk"], w["wv"],
                                              out_dtype=out_dt, o=o, S_final=S, want_cache_out=False, ws=ws,
@@ -255,17 +258,18 @@ def measure_training(jb, inputs, torch, sp, B: int, T: int, reps: int = 3):
     o = torch.empty((B, T, sh.H, sh.dv), dtype=torch.float32, device=dev)
     S = torch.empty((B, sh.H, sh.dk, sh.dv), dtype=torch.float32, device=dev)
 
-    def timed(fn):
-        fn()
+    def timed(fn, n=reps):
+        for _ in range(3):
+            fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(n):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / n
 
     ms_f = timed(lambda: jb.prefill(p["x"], p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["W1"], p["W2"],
                                     o=o, S_final=S, want_conv_out=False, ws=fws, stream=stream))
