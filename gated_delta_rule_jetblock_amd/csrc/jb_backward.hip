@@ -1101,22 +1101,29 @@ __global__ __launch_bounds__(256) void gen_bwd_dp_kernel(int64_t n_tok, int H, c
 // dx = dp W1 and the partial dW1 = dp^T x of one token range, on the fp32
 // matrix cores (16x16x4 products, exact fp32 operands): grid
 // (ceil(D / 128), NSPLIT), 4 waves; wave w owns the two 16-column tiles
-// from d0 = 128 blockIdx.x + 32 w.  The range's dp rows are staged in LDS
-// 64 at a time and read there in both orientations.
+// from d0 = 128 blockIdx.x + 32 w.  The range goes 64 tokens at a time: its
+// dp rows and its x rows (128 columns) are staged in LDS by whole-row 16-byte
+// loads and read there in the operand orientations, and the dx tile leaves
+// through LDS as whole-row 16-byte stores, so every HBM access is a full
+// row piece.
 __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, const bf16_t* x, const bf16_t* W1,
                                                         const float* dp, float* dx, float* part_w1) {
+  constexpr int LX = 128 + 8, LO = 128 + 4;  // row strides of the x (bf16) and dx (f32) tiles
   __shared__ float sdp[64][33];
+  __shared__ __attribute__((aligned(16))) bf16_t sx[64 * LX];
+  __shared__ __attribute__((aligned(16))) float sdx[64 * LO];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, m16 = lane & 15, g4 = lane >> 4;
   const int sp = blockIdx.y, nsp = gridDim.y;
   const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
-  const int d0 = blockIdx.x * 128 + wave * 32;
+  const int c0 = blockIdx.x * 128;                 // first column of the block
+  const int cw = wave * 32;                        // the wave's columns within the block
   int dcol[2];
   bool dok[2];
   // W1 as the B operand of dx (K index = hidden unit 8g + s), held for the whole range
   float wb[2][8];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
-    dcol[dt] = d0 + dt * 16 + m16;
+    dcol[dt] = c0 + cw + dt * 16 + m16;
     dok[dt] = dcol[dt] < D;
     const int dc = dok[dt] ? dcol[dt] : 0;  // clamped, then masked
 #pragma unroll
@@ -1132,22 +1139,28 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
     for (int dt = 0; dt < 2; ++dt) aw[ut][dt] = zero4();
   for (int64_t tb = t0; tb < t1; tb += 64) {
     const int nt = (int)(t1 - tb < 64 ? t1 - tb : 64);
-    __syncthreads();
-    for (int e = tid; e < 64 * 32; e += 256) sdp[e >> 5][e & 31] = (e >> 5) < nt ? dp[(tb + (e >> 5)) * 32 + (e & 31)] : 0.f;
+    __syncthreads();  // the previous block's tiles are read and its dx rows are out
+    // dp rows: 64 x 32 floats, one 16-byte piece per thread and pass
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = it * 256 + tid, r = e >> 3, q = e & 7;
+      const float4 v4 = r < nt ? *reinterpret_cast<const float4*>(dp + (tb + r) * 32 + 4 * q)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      sdp[r][4 * q] = v4.x;
+      sdp[r][4 * q + 1] = v4.y;
+      sdp[r][4 * q + 2] = v4.z;
+      sdp[r][4 * q + 3] = v4.w;
+    }
+    // x rows: 64 x 128 bf16, 16 pieces of 16 bytes per row
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int e = it * 256 + tid, r = e >> 4, q = e & 15, col = c0 + 8 * q;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nt && col < D) u = *reinterpret_cast<const uint4*>(x + (tb + r) * D + col);
+      *reinterpret_cast<uint4*>(sx + r * LX + 8 * q) = u;
+    }
     __syncthreads();
     for (int b16 = 0; b16 < nt; b16 += 16) {
-      // x rows tb + b16 + 4g + s (the B operand of dW1, K index = token 4g + s)
-      float xv[2][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t tok = tb + b16 + 4 * g4 + s;
-        const int64_t tr = tok < t1 ? tok : t1 - 1;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const float xx = bf16_to_f32(x[tr * D + (dok[dt] ? dcol[dt] : 0)]);
-          xv[dt][s] = (tok < t1 && dok[dt]) ? xx : 0.f;
-        }
-      }
       // dx tiles: A = dp rows b16 + m16 at K = 8g + s
       float da[8];
 #pragma unroll
@@ -1157,14 +1170,16 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
         f4_t o = zero4();
 #pragma unroll
         for (int s = 0; s < 8; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(da[s], wb[dt][s], o, 0, 0, 0);
-        // lane holds dx[tb + b16 + 4g + i][dcol]
+        // lane holds dx[b16 + 4g + i][cw + 16 dt + m16]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t tok = tb + b16 + 4 * g4 + i;
-          if (tok < t1 && dok[dt]) dx[tok * D + dcol[dt]] = o[i];
-        }
+        for (int i = 0; i < 4; ++i) sdx[(b16 + 4 * g4 + i) * LO + cw + dt * 16 + m16] = o[i];
       }
-      // dW1 tiles: A = dp^T rows 16 ut + m16 at K = token 4g + s
+      // dW1 tiles: A = dp^T rows 16 ut + m16 at K = token 4g + s; B = x rows 4g + s
+      float xv[2][4];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xv[dt][s] = bf16_to_f32(sx[(b16 + 4 * g4 + s) * LX + cw + dt * 16 + m16]);
 #pragma unroll
       for (int ut = 0; ut < 2; ++ut) {
         float pa[4];
@@ -1175,6 +1190,14 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
 #pragma unroll
           for (int s = 0; s < 4; ++s) aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s], xv[dt][s], aw[ut][dt], 0, 0, 0);
       }
+    }
+    __syncthreads();
+    // the dx tile out: 32 pieces of 16 bytes per row, 8 rows per pass
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 8 + (tid >> 5), q = tid & 31, col = c0 + 4 * q;
+      if (r < nt && col < D)
+        *reinterpret_cast<float4*>(dx + (tb + r) * D + col) = *reinterpret_cast<const float4*>(sdx + r * LO + 4 * q);
     }
   }
   // lane holds dW1[16 ut + 4g + i][dcol]
@@ -1235,7 +1258,7 @@ __global__ void sum_parts_kernel(int64_t n, int per, const float* part, float* o
 #define JB_BACKWARD_KERNEL_CASES(X) X(32, 64) X(64, 128) X(96, 256) X(128, 256)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr int GEN_NSPLIT = 512;       // token ranges of the dx / dW1 kernel
+constexpr int GEN_NSPLIT = 128;       // token ranges of the dx / dW1 kernel
 constexpr int GEN_NSPLIT_SMALL = 2048; // token ranges of the dW2, db1, db2 partials
 constexpr int GEN_SMALL_PER = 64;      // partials per range in the first of their two sums
 static_assert(GEN_NSPLIT % 4 == 0 && GEN_SMALL_PER % 4 == 0 && (GEN_NSPLIT_SMALL / GEN_SMALL_PER) % 4 == 0,
