@@ -45,7 +45,8 @@ struct BwdArgs {
   const float* scale;     // [0] = s, [1] = 1/s, [2] = sigma, [3] = 1/(s sigma)
   const _Float16* Mck;    // [B][H][nchunks][DV/16][DK/16][64][4] fp16: the state entering each chunk, in
                           // accumulator tiles (lane l: rows 4 (l / 16) .. + 3 of column l % 16)
-  float* dMck;            // [B][H][nchunks][DK][DV]: s x the gradient of the state leaving each chunk
+  _Float16* dMck;         // [B][H][nchunks][DK][DV]: s x the gradient of the state leaving each chunk (fp16: its
+                          // products take it as an fp16 operand, and s keeps it in range)
   float* dU;              // [B][T][H][DV]: s x dU
   float* dS0;             // [B][H][DK][DV]
   float* dq;              // [B][T][H][DK]
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(DV / 16 * 64, 1) void bwd_chain_kernel(BwdArgs a) {
   // lane part (row 4g, this column) plus a wave-uniform row part, and rows
   // past the chunk read zero / drop their stores
   const uint32_t rowb = (uint32_t)(H * DV * 4);
-  const int ov = (int)(4 * g4 * rowb) + col * 4, om = (4 * g4 * DV + col) * 4;
+  const int ov = (int)(4 * g4 * rowb) + col * 4, om = (4 * g4 * DV + col) * 2;
   // chunk cc's tiles into LDS buffer cc & 1, its dO tile (accumulator layout, scaled) into dOn
   f4_t dOn[4];
   auto issue = [&](int cc) {
@@ -328,11 +329,12 @@ __global__ __launch_bounds__(DV / 16 * 64, 1) void bwd_chain_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dU[rt][i] += sDec[rt * 16 + 4 * g4 + i] * tk[rt][i];
     // the gradient of the chunk-end state and dU, for the per-chunk pass
-    const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.dMck + ((bh * a.nchunks + c) * DK) * DV, (uint32_t)(DK * DV * 4));
+    const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.dMck + ((bh * a.nchunks + c) * DK) * DV, (uint32_t)(DK * DV * 2));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) buf_store(rM, dM[rt][i], om, (rt * 16 + i) * DV * 4);
+      for (int i = 0; i < 4; ++i)
+        buf_store(rM, __builtin_bit_cast(bf16_t, (_Float16)dM[rt][i]), om, (rt * 16 + i) * DV * 2);  // fp16 bits
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(a.dU + (((int64_t)b * T + t0) * H + h) * DV, (uint32_t)n * rowb);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
   const int t0 = c * C, n = min(C, T - t0);
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
   const uint2* M0 = reinterpret_cast<const uint2*>(a.Mck + ((bh * a.nchunks + c) * DK) * DV);  // a lane's 4 fp16
-  const float4* dMC = reinterpret_cast<const float4*>(a.dMck + ((bh * a.nchunks + c) * DK) * DV);
+  const uint2* dMC = reinterpret_cast<const uint2*>(a.dMck + ((bh * a.nchunks + c) * DK) * DV);  // a lane's 4 fp16
 
   // this wave's A operand, 16 rows of dO (scaled) or of dU, issued first so
   // that its loads are in flight while M0 is staged
@@ -473,18 +475,20 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dvred_kernel(BwdArgs a) {
     }
   }
   lds_barrier();  // the A loads stay in flight
-  // the gate term: dM rows (fp32, row-major) against the staged M0
+  // the gate term: dM rows (fp16, row-major) against the staged M0
   float part = 0.f;
 #pragma unroll
   for (int j0 = 0; j0 < NV4; j0 += R) {
-    float4 d[R];
+    uint2 d[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) d[j] = dMC[(j0 + j) * NTHR + tid];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int e = (j0 + j) * NTHR + tid;
       const half4_t hv = *reinterpret_cast<const half4_t*>(sM0 + (e / (DV / 4)) * LDM + (e % (DV / 4)) * 4);
-      part += (float)hv[0] * d[j].x + (float)hv[1] * d[j].y + (float)hv[2] * d[j].z + (float)hv[3] * d[j].w;
+      const half4_t dv4 = __builtin_bit_cast(half4_t, d[j]);
+      part += (float)hv[0] * (float)dv4[0] + (float)hv[1] * (float)dv4[1] + (float)hv[2] * (float)dv4[2] +
+              (float)hv[3] * (float)dv4[3];
     }
   }
   part = wave_sum(part);
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
   const float s = a.scale[0], inv = a.scale[1], vs = a.scale[2], invq = a.scale[3];
   const int64_t tokbase = ((int64_t)b * T + t0) * H + h;
   const _Float16* M0 = a.Mck + ((bh * a.nchunks + c) * DK) * DV;
-  const float* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
+  const _Float16* dMC = a.dMck + ((bh * a.nchunks + c) * DK) * DV;
   const float* dO = a.dout + tokbase * DV;
   const float* dUg = a.dU + tokbase * DV;
 
@@ -815,7 +819,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_grad_kernel(BwdArgs a) {
         }
       }
       if (wave < RT) {
-        const Frag<OP> fdm = glb_frag<OP>(dMC, DV, wave * 16, k0, 1.f, DK);
+        // dM rows 16 wave + m16 at K = k0 + 4 g4 .. + 3 and k0 + 16 + 4 g4 .. + 3 (fp16 as stored)
+        Frag<OP> fdm;
+        {
+          const _Float16* pr = dMC + (wave * 16 + m16) * DV + k0 + 4 * g4;
+          const half4_t lo = *reinterpret_cast<const half4_t*>(pr), hi = *reinterpret_cast<const half4_t*>(pr + 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { fdm.v[j] = lo[j]; fdm.v[4 + j] = hi[j]; }
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) mma(aKM[rt], lds_frag<OP>(sUb, LKW, rt * 16, ks * 32), fdm);
       }
@@ -1270,7 +1281,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   const size_t nch = (size_t)p.nchunks;
   size_t bytes = al256(prefill_base_bytes(p));                // taps, segment buffers (the forward pass)
   bytes += al256((size_t)B * H * nch * dk * dv * 2);           // Mck (fp16)
-  bytes += al256((size_t)B * H * nch * dk * dv * 4);           // dMck
+  bytes += al256((size_t)B * H * nch * dk * dv * 2);           // dMck (fp16)
   bytes += 2 * al256(n * H * dv * 4);                          // dU, dV'
   bytes += 2 * al256((size_t)B * H * nch * C * dk * 4);        // dO M0^T, dU M0^T per chunk
   bytes += al256((size_t)B * H * nch * chain_img_bytes(dk));   // the chain's tiles per chunk
@@ -1299,8 +1310,8 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   ws += al256(prefill_base_bytes(p));
   _Float16* Mck = reinterpret_cast<_Float16*>(ws);
   ws += al256((size_t)B * H * nch * dk * dv * 2);
-  float* dMck = reinterpret_cast<float*>(ws);
-  ws += al256((size_t)B * H * nch * dk * dv * 4);
+  _Float16* dMck = reinterpret_cast<_Float16*>(ws);
+  ws += al256((size_t)B * H * nch * dk * dv * 2);
   float* dU = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * H * dv * 4);
   float* dvc = reinterpret_cast<float*>(ws);
