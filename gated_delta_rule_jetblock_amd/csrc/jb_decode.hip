@@ -585,8 +585,13 @@ __global__ __launch_bounds__(NW * 64) void decode_seq_static_kernel(
   seq_update_heads<DK, DV, OUT, NW>(sm, ma, mb, HPG, bh0, S_out, o_t, tid, wave, lane, load_tile);
 }
 
-int decode_seq_heads_per_group(int B, int H, int nw) {
-  const int64_t want = 256 * (16 / nw);
+// Heads per workgroup: the fewest groups (each a divisor of H, at most
+// SEQ_MAXHPG heads) that give at least 512 workgroups of nw = 8 waves, or 1024
+// when a head's state is 128 rows or more.  Measured at B = 256, H = 12,
+// dk = 96: 6 heads per workgroup 104 us per step, 4 or 3 heads 106-108 us; at
+// B = 128, H = 16, dk = 128: 4 heads 96.7 us, 2 heads 93.0 us.
+int decode_seq_heads_per_group(int B, int H, int dk, int nw) {
+  const int64_t want = (int64_t)(dk >= 128 ? 1024 : 512) * 8 / nw;
   for (int ng = 1; ng <= H; ++ng)
     if (H % ng == 0 && H / ng <= SEQ_MAXHPG && (int64_t)B * ng >= want) return H / ng;
   return 1;
@@ -598,7 +603,7 @@ static hipError_t run_decode_seq(int out, int B, int H, int D, const float* S_in
                                  const float* alpha_t, const float* beta_t, const void* W1, const void* b1,
                                  const void* W2, const void* b2, void* o_t, hipStream_t stream) {
   constexpr int NW = SEQ_NW;
-  const int hpg = decode_seq_heads_per_group(B, H, NW);
+  const int hpg = decode_seq_heads_per_group(B, H, DK, NW);
   const dim3 grid(H / hpg, B);
 #define JB_SEQ_ARGS(OUT_)                                                                                       \
   H, hpg, D, S_in, S_out, (const IO*)cache_in, (IO*)cache_out, (const IO*)x_t, (const IO*)q_t, (const IO*)k_t, \
@@ -663,7 +668,7 @@ static hipError_t run_decode_static(int out, int B, int H, const float* S_in, fl
                                     const float* beta_t, const float* wq, const float* wk, const float* wv, void* o_t,
                                     hipStream_t stream) {
   constexpr int NW = SEQ_NW;
-  const int hpg = decode_seq_heads_per_group(B, H, NW);
+  const int hpg = decode_seq_heads_per_group(B, H, DK, NW);
   const dim3 grid(H / hpg, B);
 #define JB_STATIC_ARGS(OUT_)                                                                                    \
   H, hpg, S_in, S_out, (const IO*)cq_in, (const IO*)ck_in, (const IO*)cv_in, (IO*)cq_out, (IO*)ck_out,         \
