@@ -307,10 +307,21 @@ __global__ __launch_bounds__(DV / 16 * 64, 1) void bwd_chain_kernel(BwdArgs a) {
     const float* sGam = reinterpret_cast<const float*>(img + I::oGam);
     const float* sDec = reinterpret_cast<const float*>(img + I::oDec);
     const float gamC = sGam[C - 1];
-    // dU = P^T dO + D (K dM)
-    f4_t dU[4], tk[4];
+    // dU = D (K dM) + P^T dO: K dM first, scaled by D row by row, then the
+    // P^T dO products accumulate onto it (one accumulator set)
+    f4_t dU[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) { dU[rt] = zero4(); tk[rt] = zero4(); }
+    for (int rt = 0; rt < 4; ++rt) dU[rt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const Frag<OP> fm = acc_frag<OP>(dM[2 * kb], dM[2 * kb + 1]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) mma(dU[rt], lds_frag<OP>(sKh, I::LK, rt * 16, kb * 32), fm);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dU[rt][i] *= sDec[rt * 16 + 4 * g4 + i];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const Frag<OP> fo = acc_frag<OP>(dOr[2 * kb], dOr[2 * kb + 1]);
@@ -318,16 +329,6 @@ __global__ __launch_bounds__(DV / 16 * 64, 1) void bwd_chain_kernel(BwdArgs a) {
       for (int rt = 0; rt < 4; ++rt)
         if (kb * 32 + 31 >= rt * 16) mma(dU[rt], lds_frag<OP>(sPt, I::LT, rt * 16, kb * 32), fo);
     }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const Frag<OP> fm = acc_frag<OP>(dM[2 * kb], dM[2 * kb + 1]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) mma(tk[rt], lds_frag<OP>(sKh, I::LK, rt * 16, kb * 32), fm);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dU[rt][i] += sDec[rt * 16 + 4 * g4 + i] * tk[rt][i];
     // the gradient of the chunk-end state and dU, for the per-chunk pass
     const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.dMck + ((bh * a.nchunks + c) * DK) * DV, (uint32_t)(DK * DV * 2));
 #pragma unroll
