@@ -345,12 +345,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * C;
     const int n = min(C, T - t0);
-    // ================= prefetched inputs -> prologue =================
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA transfers have landed
-    __syncthreads();                // ... and every other wave's
     if constexpr (MODE == MODE_CKPT) {
-      // the state entering chunk c, for the backward pass (stored after the
-      // wait above, so that the stores complete while the chunk is worked), in the fp16 its
+      // the state entering chunk c, for the backward pass, in the fp16 its
       // products there take as an operand and in accumulator tiles: per chunk
       // [DV/16][DK/16][64 lanes][4], lane l of tile (ct, rt) holding rows
       // 16 rt + 4 (l / 16) .. + 3 of column 16 ct + l % 16 (one 8-byte store)
@@ -372,6 +368,9 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
 
+    // ================= prefetched inputs -> prologue =================
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS DMA transfers have landed
+    __syncthreads();                // ... and every other wave's
     {
       if (SC && tid < PRO_THR) {
         // static conv: thread (row, part) as in Prologue; the convolved rows
