@@ -1149,29 +1149,43 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
   for (int ut = 0; ut < 2; ++ut)
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) aw[ut][dt] = zero4();
-  for (int64_t tb = t0; tb < t1; tb += 64) {
+  // a block's dp rows (64 x 32 floats, one 16-byte piece per thread and pass)
+  // and x rows (64 x 128 bf16, 16 pieces per row) into registers: the next
+  // block's move while the current one is multiplied
+  float4 pdp[2];
+  uint4 px[4];
+  auto load_block = [&](int64_t tb) {
     const int nt = (int)(t1 - tb < 64 ? t1 - tb : 64);
-    __syncthreads();  // the previous block's tiles are read and its dx rows are out
-    // dp rows: 64 x 32 floats, one 16-byte piece per thread and pass
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int e = it * 256 + tid, r = e >> 3, q = e & 7;
-      const float4 v4 = r < nt ? *reinterpret_cast<const float4*>(dp + (tb + r) * 32 + 4 * q)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-      sdp[r][4 * q] = v4.x;
-      sdp[r][4 * q + 1] = v4.y;
-      sdp[r][4 * q + 2] = v4.z;
-      sdp[r][4 * q + 3] = v4.w;
+      pdp[it] = r < nt ? *reinterpret_cast<const float4*>(dp + (tb + r) * 32 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // x rows: 64 x 128 bf16, 16 pieces of 16 bytes per row
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int e = it * 256 + tid, r = e >> 4, q = e & 15, col = c0 + 8 * q;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nt && col < D) u = *reinterpret_cast<const uint4*>(x + (tb + r) * D + col);
-      *reinterpret_cast<uint4*>(sx + r * LX + 8 * q) = u;
+      px[it] = (r < nt && col < D) ? *reinterpret_cast<const uint4*>(x + (tb + r) * D + col) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  if (t0 < t1) load_block(t0);
+  for (int64_t tb = t0; tb < t1; tb += 64) {
+    const int nt = (int)(t1 - tb < 64 ? t1 - tb : 64);
+    __syncthreads();  // the previous block's tiles are read and its dx rows are out
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = it * 256 + tid, r = e >> 3, q = e & 7;
+      sdp[r][4 * q] = pdp[it].x;
+      sdp[r][4 * q + 1] = pdp[it].y;
+      sdp[r][4 * q + 2] = pdp[it].z;
+      sdp[r][4 * q + 3] = pdp[it].w;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int e = it * 256 + tid, r = e >> 4, q = e & 15;
+      *reinterpret_cast<uint4*>(sx + r * LX + 8 * q) = px[it];
     }
     __syncthreads();
+    if (tb + 64 < t1) load_block(tb + 64);
     for (int b16 = 0; b16 < nt; b16 += 16) {
       // dx tiles: A = dp rows b16 + m16 at K = 8g + s
       float da[8];
