@@ -1095,20 +1095,6 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_
 
 // ------------------------------------------------------------ generator backward
 
-// One thread per (token, hidden unit): hid = SiLU(pre), dhid = W2^T dtaps,
-// dp = dhid SiLU'(pre), SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p).
-__global__ __launch_bounds__(256) void gen_bwd_dp_kernel(int64_t n_tok, int H, const bf16_t* W2, const float* pre,
-                                                         const float* dtaps, float* dp, float* hid) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= n_tok * 32) return;
-  const int64_t t = e >> 5;
-  const int u = (int)(e & 31);
-  const float p = pre[e], sg = 1.f / (1.f + expf(-p));
-  float dh = 0.f;
-  for (int r = 0; r < 4 * H; ++r) dh += bf16_to_f32(W2[r * 32 + u]) * dtaps[t * 4 * H + r];
-  dp[e] = dh * sg * (1.f + p * (1.f - sg));
-  hid[e] = p * sg;
-}
 
 // dx = dp W1 and the partial dW1 = dp^T x of one token range, on the fp32
 // matrix cores (16x16x4 products, exact fp32 operands): grid
@@ -1236,28 +1222,67 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
         for (int i = 0; i < 4; ++i) part_w1[((int64_t)sp * 32 + ut * 16 + 4 * g4 + i) * D + dcol[dt]] = aw[ut][dt][i];
 }
 
-// Partial dW2 = dtaps^T hid [4H][32], db2 = sum dtaps, db1 = sum dp over one
-// token range: grid NSPLIT, one entry per thread step.
-__global__ __launch_bounds__(256) void gen_bwd_small_kernel(int64_t n_tok, int H, const float* dp, const float* hid,
-                                                            const float* dtaps, float* part_small) {
-  const int sp = blockIdx.x, nsp = gridDim.x;
+// The generator's first backward step and its small partials, per token range
+// (grid GEN_NSPLIT_SMALL ranges, 256 threads), in passes of 32 tokens whose
+// taps gradients sit in LDS beside W2:
+//   hid = SiLU(pre), dhid = W2^T dtaps, dp = dhid SiLU'(pre) with
+//   SiLU'(p) = s (1 + p (1 - s)), s = sigmoid(p)   (dp written: dx and dW1 take it);
+// then the range's partial dW2 = dtaps^T hid [4H][32], db2 = sum dtaps and
+// db1 = sum dp, each summed over the range's tokens in order.
+constexpr int GEN_SMALL_MAXH = 32;  // heads (4H taps) the LDS holds
+__global__ __launch_bounds__(256) void gen_bwd_head_kernel(int64_t n_tok, int H, const bf16_t* W2, const float* pre,
+                                                           const float* dtaps, float* dp, float* part_small) {
+  constexpr int TB = 32, MAXHK = 4 * GEN_SMALL_MAXH;
+  constexpr int NJ = (MAXHK * 32 + MAXHK + 32 + 255) / 256;  // outputs per thread, at most
+  __shared__ float sW2[MAXHK * 32];
+  __shared__ float sdt[TB][MAXHK + 1];
+  __shared__ float shid[TB][33];
+  __shared__ float sdp[TB][33];
+  const int tid = threadIdx.x, sp = blockIdx.x, nsp = gridDim.x;
   const int64_t t0 = n_tok * sp / nsp, t1 = n_tok * (sp + 1) / nsp;
   const int HK = 4 * H, nsmall = HK * 32 + HK + 32;
-  float* ps = part_small + (int64_t)sp * nsmall;
-  for (int e = threadIdx.x; e < nsmall; e += 256) {
-    float acc = 0.f;
-    if (e < HK * 32) {
-      const int r = e / 32, u = e % 32;
-      for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r] * hid[t * 32 + u];
-    } else if (e < HK * 32 + HK) {
-      const int r = e - HK * 32;
-      for (int64_t t = t0; t < t1; ++t) acc += dtaps[t * HK + r];
-    } else {
-      const int u = e - HK * 32 - HK;
-      for (int64_t t = t0; t < t1; ++t) acc += dp[t * 32 + u];
+  for (int e = tid; e < HK * 32; e += 256) sW2[e] = bf16_to_f32(W2[e]);
+  float acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
+  for (int64_t tb = t0; tb < t1; tb += TB) {
+    const int nt = (int)(t1 - tb < TB ? t1 - tb : TB);
+    __syncthreads();  // W2 is in; the previous pass's rows are read
+    for (int e = tid; e < nt * HK; e += 256) sdt[e / HK][e % HK] = dtaps[tb * HK + e];
+    __syncthreads();
+    for (int e = tid; e < nt * 32; e += 256) {
+      const int t = e >> 5, u = e & 31;
+      const float p = pre[(tb + t) * 32 + u], sg = 1.f / (1.f + expf(-p));
+      float dh = 0.f;
+      for (int r = 0; r < HK; ++r) dh += sW2[r * 32 + u] * sdt[t][r];
+      const float d = dh * sg * (1.f + p * (1.f - sg));
+      dp[(tb + t) * 32 + u] = d;
+      sdp[t][u] = d;
+      shid[t][u] = p * sg;
     }
-    ps[e] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = tid + 256 * j;
+      if (e >= nsmall) continue;
+      float a = acc[j];
+      if (e < HK * 32) {
+        const int r = e / 32, u = e % 32;
+        for (int t = 0; t < nt; ++t) a += sdt[t][r] * shid[t][u];
+      } else if (e < HK * 32 + HK) {
+        const int r = e - HK * 32;
+        for (int t = 0; t < nt; ++t) a += sdt[t][r];
+      } else {
+        const int u = e - HK * 32 - HK;
+        for (int t = 0; t < nt; ++t) a += sdp[t][u];
+      }
+      acc[j] = a;
+    }
   }
+  float* ps = part_small + (int64_t)sp * nsmall;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (tid + 256 * j < nsmall) ps[tid + 256 * j] = acc[j];
 }
 
 // Sums of partials in a fixed order, `per` partials (a multiple of 4) per
@@ -1302,7 +1327,7 @@ size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int D) {
   bytes += al256((size_t)B * H * nch * chain_img_bytes(dk));   // the chain's tiles per chunk
   bytes += al256((size_t)B * H * nch * 4);                     // the chunk-end gate term
   bytes += al256(n * H * 4 * 4);                               // dtaps
-  bytes += 3 * al256(n * 32 * 4);                              // pre, dp, hid
+  bytes += 2 * al256(n * 32 * 4);                              // pre, dp
   bytes += al256((size_t)GEN_NSPLIT * 32 * D * 4);             // dW1 partials
   bytes += al256((size_t)GEN_NSPLIT_SMALL * (4 * H * 32 + 4 * H + 32) * 4);
   bytes += al256((size_t)(GEN_NSPLIT_SMALL / GEN_SMALL_PER) * (4 * H * 32 + 4 * H + 32) * 4);
@@ -1316,6 +1341,7 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
                            const float* dS_final, const float* dconv_out, float* dx, float* dq, float* dk_,
                            float* dv_, float* dalpha, float* dbeta, float* dW1, float* db1, float* dW2, float* db2,
                            float* dS0, float* dconv_in, void* workspace, hipStream_t stream) {
+  if (H > GEN_SMALL_MAXH) return hipErrorInvalidValue;
   const PrefillPlan p = plan_prefill(B, T, H, dk, dv, IO_BF16, IO_F32, 0);
   const int64_t n = (int64_t)B * T;
   const int nch = p.nchunks;
@@ -1344,8 +1370,6 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   float* pre = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * 32 * 4);
   float* dp = reinterpret_cast<float*>(ws);
-  ws += al256((size_t)n * 32 * 4);
-  float* hid = reinterpret_cast<float*>(ws);
   ws += al256((size_t)n * 32 * 4);
   float* pw1 = reinterpret_cast<float*>(ws);
   ws += al256((size_t)GEN_NSPLIT * 32 * D * 4);
@@ -1394,11 +1418,9 @@ hipError_t launch_backward(int B, int T, int H, int dk, int dv, int D, const voi
   if (!launched) return hipErrorInvalidValue;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the generator
-  gen_bwd_dp_kernel<<<dim3((unsigned)((n * 32 + 255) / 256)), 256, 0, stream>>>(n, H, (const bf16_t*)W2, pre,
-                                                                                dtaps, dp, hid);
+  gen_bwd_head_kernel<<<dim3(GEN_NSPLIT_SMALL), 256, 0, stream>>>(n, H, (const bf16_t*)W2, pre, dtaps, dp, psm);
   gen_bwd_x_kernel<<<dim3((D + 127) / 128, GEN_NSPLIT), 256, 0, stream>>>(n, D, (const bf16_t*)x,
                                                                          (const bf16_t*)W1, dp, dx, pw1);
-  gen_bwd_small_kernel<<<dim3(GEN_NSPLIT_SMALL), 256, 0, stream>>>(n, H, dp, hid, dtaps, psm);
   const int64_t nw1 = (int64_t)32 * D, nsm = (int64_t)4 * H * 32 + 4 * H + 32;
   sum_parts_kernel<<<dim3((unsigned)((nw1 + 255) / 256)), 256, 0, stream>>>(nw1, GEN_NSPLIT, pw1, dW1);
   // the small parts land in dW2 [4H][32], db2 [4H], db1 [32] (three sums over the same partial layout),
