@@ -208,14 +208,9 @@ __global__ __launch_bounds__(NTHR) void bwd_tiles_kernel(BwdArgs a) {
     Prologue<DK, bf16_t> pr;
     pr.load_global(a.q, a.k, ((int64_t)b * T + t0) * H + h, H, n);
     pr.finish(true);
-    OP* qt = reinterpret_cast<OP*>(im + I::oQt);
 #pragma unroll
-    for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e) {
-      const int d = pr.part * Prologue<DK, bf16_t>::E + e;
-      const OP qh = (OP)pr.qv[e];
-      sQh[pr.row * LDK + d] = qh;
-      qt[d * I::LT + pr.row] = qh;  // Q^T straight to the image
-    }
+    for (int e = 0; e < Prologue<DK, bf16_t>::E; ++e)
+      sQh[pr.row * LDK + pr.part * Prologue<DK, bf16_t>::E + e] = (OP)pr.qv[e];
   }
   __syncthreads();
   // P^T block (tj, ti): keys of block tj against queries of block ti
@@ -234,6 +229,20 @@ __global__ __launch_bounds__(NTHR) void bwd_tiles_kernel(BwdArgs a) {
   __syncthreads();
   for (int e = tid; e < C * I::LT * 2 / 16; e += NTHR)
     reinterpret_cast<uint4*>(im + I::oPt)[e] = reinterpret_cast<const uint4*>(sPt)[e];
+  // Q^T from the row-major Q^ tile: 16-byte pieces of eight consecutive tokens
+  // of one feature (the padding columns past C written as zeros)
+  constexpr int PPT = I::LT / 8;  // pieces per Q^T row
+  for (int e = tid; e < DK * PPT; e += NTHR) {
+    const int d = e / PPT, r0 = (e % PPT) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + 2 * j;
+      const OP lo = r < C ? sQh[r * LDK + d] : (OP)0.f, hi = r + 1 < C ? sQh[(r + 1) * LDK + d] : (OP)0.f;
+      w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(im + I::oQt + (d * I::LT + r0) * 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // grid (H, B), one wave per dv column tile (DV / 16 waves); wave w owns
