@@ -1113,6 +1113,22 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_
 // loads and read there in the operand orientations, and the dx tile leaves
 // through LDS as whole-row 16-byte stores, so every HBM access is a full
 // row piece.
+// x = hi + mid + lo with each part bf16 (round to nearest even at each step):
+// the three parts keep x's 24 significant bits, so three bf16 matrix-core
+// products against an operand exact in bf16 give the fp32 product.
+__device__ __forceinline__ void split3(const float (&v)[8], bf16x8_t& h, bf16x8_t& m, bf16x8_t& l) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 hj = (__bf16)v[j];
+    const float r1 = v[j] - (float)hj;
+    const __bf16 mj = (__bf16)r1;
+    const float r2 = r1 - (float)mj;
+    h[j] = hj;
+    m[j] = mj;
+    l[j] = (__bf16)r2;
+  }
+}
+
 __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, const bf16_t* x, const bf16_t* W1,
                                                         const float* dp, float* dx, float* part_w1) {
   constexpr int LX = 128 + 8, LO = 128 + 4;  // row strides of the x (bf16) and dx (f32) tiles
@@ -1126,17 +1142,17 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
   const int cw = wave * 32;                        // the wave's columns within the block
   int dcol[2];
   bool dok[2];
-  // W1 as the B operand of dx (K index = hidden unit 8g + s), held for the whole range
-  float wb[2][8];
+  // W1 as the B operand of dx (K index = hidden unit 8g + j), held for the whole range
+  bf16x8_t wb16[2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt) {
     dcol[dt] = c0 + cw + dt * 16 + m16;
     dok[dt] = dcol[dt] < D;
     const int dc = dok[dt] ? dcol[dt] : 0;  // clamped, then masked
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const float w = bf16_to_f32(W1[(int64_t)(8 * g4 + s) * D + dc]);
-      wb[dt][s] = dok[dt] ? w : 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const bf16_t w = W1[(int64_t)(8 * g4 + j) * D + dc];
+      wb16[dt][j] = __builtin_bit_cast(__bf16, dok[dt] ? w : (bf16_t)0);
     }
   }
   f4_t aw[2][2];  // dW1 tiles [unit tile][column tile]
@@ -1181,35 +1197,48 @@ __global__ __launch_bounds__(256) void gen_bwd_x_kernel(int64_t n_tok, int D, co
     }
     __syncthreads();
     if (tb + 64 < t1) load_block(tb + 64);
-    for (int b16 = 0; b16 < nt; b16 += 16) {
-      // dx tiles: A = dp rows b16 + m16 at K = 8g + s
-      float da[8];
+    for (int b32 = 0; b32 < nt; b32 += 32) {
+      // dx tiles: A = dp rows b16 + m16 at K = hidden unit 8g + j, split into
+      // three bf16 parts (hi + mid + lo keeps dp's 24 bits); B = W1, exact in bf16
 #pragma unroll
-      for (int s = 0; s < 8; ++s) da[s] = sdp[b16 + m16][8 * g4 + s];
+      for (int hb = 0; hb < 2; ++hb) {
+        const int b16 = b32 + 16 * hb;
+        float da[8];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        f4_t o = zero4();
+        for (int j = 0; j < 8; ++j) da[j] = sdp[b16 + m16][8 * g4 + j];
+        bf16x8_t ah, am, al;
+        split3(da, ah, am, al);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(da[s], wb[dt][s], o, 0, 0, 0);
-        // lane holds dx[b16 + 4g + i][cw + 16 dt + m16]
+        for (int dt = 0; dt < 2; ++dt) {
+          f4_t o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb16[dt], zero4(), 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, wb16[dt], o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb16[dt], o, 0, 0, 0);
+          // lane holds dx[b16 + 4g + i][cw + 16 dt + m16]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sdx[(b16 + 4 * g4 + i) * LO + cw + dt * 16 + m16] = o[i];
+          for (int i = 0; i < 4; ++i) sdx[(b16 + 4 * g4 + i) * LO + cw + dt * 16 + m16] = o[i];
+        }
       }
-      // dW1 tiles: A = dp^T rows 16 ut + m16 at K = token 4g + s; B = x rows 4g + s
-      float xv[2][4];
+      // dW1 tiles: A = dp^T rows 16 ut + m16 at K = token b32 + 8g + j (split
+      // likewise); B = x rows b32 + 8g + j, exact in bf16
+      bf16x8_t xb[2];
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xv[dt][s] = bf16_to_f32(sx[(b16 + 4 * g4 + s) * LX + cw + dt * 16 + m16]);
+        for (int j = 0; j < 8; ++j)
+          xb[dt][j] = __builtin_bit_cast(__bf16, sx[(b32 + 8 * g4 + j) * LX + cw + dt * 16 + m16]);
 #pragma unroll
       for (int ut = 0; ut < 2; ++ut) {
-        float pa[4];
+        float pa[8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) pa[s] = sdp[b16 + 4 * g4 + s][ut * 16 + m16];
+        for (int j = 0; j < 8; ++j) pa[j] = sdp[b32 + 8 * g4 + j][ut * 16 + m16];
+        bf16x8_t ph, pm, pl;
+        split3(pa, ph, pm, pl);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[s], xv[dt][s], aw[ut][dt], 0, 0, 0);
+        for (int dt = 0; dt < 2; ++dt) {
+          aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, xb[dt], aw[ut][dt], 0, 0, 0);
+          aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pm, xb[dt], aw[ut][dt], 0, 0, 0);
+          aw[ut][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, xb[dt], aw[ut][dt], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
