@@ -1104,9 +1104,8 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(int T, int H, const bf16_
 
 // ------------------------------------------------------------ generator backward
 
-
-// dx = dp W1 and the partial dW1 = dp^T x of one token range, on the fp32
-// matrix cores (16x16x4 products, exact fp32 operands): grid
+// dx = dp W1 and the partial dW1 = dp^T x of one token range, on the bf16
+// matrix cores (dp in three bf16 parts, x and W1 exact; split3 below): grid
 // (ceil(D / 128), NSPLIT), 4 waves; wave w owns the two 16-column tiles
 // from d0 = 128 blockIdx.x + 32 w.  The range goes 64 tokens at a time: its
 // dp rows and its x rows (128 columns) are staged in LDS by whole-row 16-byte
